@@ -1,0 +1,168 @@
+"""Python access to the CPU oracle (``oracle.c``), built with gcc into ``liboracle.so``.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, the package's ``smoke()`` check
+and the CPU-baseline leg of ``bench.py``.  The GPU product path never imports it.
+It shares no code with that path; the only thing both sides use is the seeded
+input generator in ``workloads``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+# A test that plants a mistake in a copy of the oracle points this at the
+# mutant's library (tests/test_oracle_mutants.py); nothing else sets it.
+_LIB_OVERRIDE = os.environ.get("IDX_ORACLE_MUTANT_LIB")
+_lib = None
+
+Q_MXFP4 = 0
+Q_FP8 = 1
+
+
+def build() -> str:
+    """Compile oracle.c (plain C, -O2, no FP contraction) into liboracle.so."""
+    tmp = _LIB + ".tmp"
+    subprocess.check_call(["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fPIC", "-shared",
+                           "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if _LIB_OVERRIDE:
+            L = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+            L = ctypes.CDLL(_LIB)
+        d, i, i32p = ctypes.c_double, ctypes.c_int, ctypes.c_void_p
+        for name in ("orc_e2m1", "orc_ue8m0", "orc_e4m3fn"):
+            getattr(L, name).restype = d
+            getattr(L, name).argtypes = [i]
+        L.orc_candidate_tokens.restype = ctypes.c_int32
+        L.orc_candidate_tokens.argtypes = [i32p, i, i, ctypes.c_int32, ctypes.c_int32, i32p]
+        L.orc_expand_row.restype = ctypes.c_int32
+        L.orc_expand_row.argtypes = [i32p, i, i, i, ctypes.c_int32, ctypes.c_int32, i32p,
+                                     ctypes.c_int32, i32p]
+        L.orc_select_topk.restype = ctypes.c_int32
+        L.orc_select_topk.argtypes = [i32p, i32p, ctypes.c_int32, ctypes.c_int32, i32p]
+        p, i64 = ctypes.c_void_p, ctypes.c_int64
+        L.orc_indexer_rows.restype = i
+        L.orc_indexer_rows.argtypes = [i, i, i, i, i, i, i, p, p, p, p, p, p, i64, p, i64, p, i64,
+                                       p, p, p, p, i64, p, ctypes.c_int32, p, i64, p, p, i64, p]
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def e2m1(code: int) -> float:
+    return lib().orc_e2m1(int(code))
+
+
+def ue8m0(b: int) -> float:
+    return lib().orc_ue8m0(int(b))
+
+
+def e4m3fn(b: int) -> float:
+    return lib().orc_e4m3fn(int(b))
+
+
+def candidate_tokens(cand_row, cbs: int, ks: int, ke: int) -> np.ndarray:
+    cand_row = np.ascontiguousarray(cand_row, dtype=np.int32)
+    out = np.empty(max(1, cand_row.size * cbs), dtype=np.int32)
+    n = lib().orc_candidate_tokens(_ptr(cand_row), cand_row.size, cbs, ks, ke, _ptr(out))
+    return out[:n].copy()
+
+
+def expand_row(cand_row, cbs: int, sbk: int, ks: int, ke: int, nsb_cap: int):
+    """(sparse_indices[nsb_cap], listed count, end) of one row."""
+    cand_row = np.ascontiguousarray(cand_row, dtype=np.int32)
+    out = np.empty(max(1, nsb_cap), dtype=np.int32)
+    end = np.zeros(1, dtype=np.int32)
+    n = lib().orc_expand_row(_ptr(cand_row), cand_row.size, cbs, sbk, ks, ke, _ptr(out),
+                             nsb_cap, _ptr(end))
+    return out[:nsb_cap].copy(), int(n), int(end[0])
+
+
+def expand(case, sbk: int):
+    """Schedule of every row of a case: (sparse_indices [R, NSB], end [R])."""
+    s = case.spec
+    nsb = s.nb * (s.cbs // sbk)
+    si = np.empty((case.num_rows, nsb), dtype=np.int32)
+    end = np.empty(case.num_rows, dtype=np.int32)
+    for r in range(case.num_rows):
+        si[r], _, end[r] = expand_row(case.candidate_blocks[r], s.cbs, sbk,
+                                      int(case.row_ks[r]), int(case.row_ke[r]), nsb)
+    return si, end
+
+
+def select_topk(tokens, logits, topk: int) -> np.ndarray:
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    out = np.empty(max(1, topk), dtype=np.int32)
+    lib().orc_select_topk(_ptr(tokens), _ptr(logits), tokens.size, topk, _ptr(out))
+    return out[:topk].copy()
+
+
+class RowResult:
+    """Oracle output for a list of rows."""
+
+    def __init__(self, rows, indices, tokens, logits, count):
+        self.rows = rows          # int32 [n]
+        self.indices = indices    # int32 [n, topk]
+        self.tokens = tokens      # int32 [n, cap] (first count[i] valid)
+        self.logits = logits      # float32 [n, cap]
+        self.count = count        # int32 [n]
+
+    def row_tokens(self, i):
+        return self.tokens[i, :self.count[i]]
+
+    def row_logits(self, i):
+        return self.logits[i, :self.count[i]]
+
+
+def indexer_rows(case, layer: int = 0, rows=None, q_format: str = "mxfp4", pool=None,
+                 with_logits: bool = True) -> RowResult:
+    """Run the oracle over the given rows (default: all) of one layer of a case."""
+    s = case.spec
+    L = case.layers[layer]
+    if rows is None:
+        rows = np.arange(case.num_rows, dtype=np.int32)
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    if pool is None:
+        pool = L.host_pool(s.page_bytes)
+    pool = np.ascontiguousarray(pool)
+    vb = s.values_bytes
+    n = rows.size
+    cap = max(1, s.nb * s.cbs)
+    idx = np.empty((n, s.topk), dtype=np.int32)
+    toks = np.empty((n, cap), dtype=np.int32) if with_logits else None
+    lg = np.empty((n, cap), dtype=np.float32) if with_logits else None
+    cnt = np.empty(n, dtype=np.int32)
+    fmt = Q_MXFP4 if q_format == "mxfp4" else Q_FP8
+    cand = np.ascontiguousarray(case.candidate_blocks, dtype=np.int32)
+    bt = np.ascontiguousarray(case.block_table, dtype=np.int32)
+    lib().orc_indexer_rows(
+        s.num_heads, s.head_dim, s.page_size, s.cbs, s.nb, s.topk, fmt,
+        _ptr(L.q_values) if fmt == Q_MXFP4 else None,
+        _ptr(L.q_scales) if fmt == Q_MXFP4 else None,
+        _ptr(L.q_fp8) if fmt == Q_FP8 else None,
+        _ptr(L.q_rowscale) if fmt == Q_FP8 else None,
+        _ptr(np.ascontiguousarray(L.weights, dtype=np.float32)),
+        _ptr(pool), s.page_bytes, pool.ctypes.data + vb, s.page_bytes,
+        _ptr(bt), bt.shape[1],
+        _ptr(case.row_ks), _ptr(case.row_ke), _ptr(case.row_table),
+        _ptr(cand), cand.shape[1], _ptr(rows), n,
+        _ptr(idx), s.topk, _ptr(toks), _ptr(lg), cap, _ptr(cnt))
+    return RowResult(rows, idx, toks, lg, cnt)

@@ -1,0 +1,355 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+* element decodes against hand-derived tables and PyTorch's fp8 / e8m0 decodes;
+* closed-form logits (constant inputs, flipped heads, one-hot scale blocks,
+  the fp8-Q variant) whose values follow by hand from the definition;
+* a textbook special case (one head, unit weight, unit scales) that reduces to
+  an integer dot product and numpy's lexsort;
+* the independent dense-then-mask brute force on hundreds of tiny random cases;
+* invariants of the output and arithmetic-free special cases (k >= valid count,
+  all-equal logits).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from brute_force import row as brute_row
+from golden_io import e2m1_table, packed_examples, scale_fp8_examples
+
+pytestmark = []
+
+
+# ---------------------------------------------------------------- decodes ----
+
+def test_e2m1_matches_hand_table():
+    table = e2m1_table()
+    for code, v in table.items():
+        got = oracle.e2m1(code)
+        assert got == v and np.signbit(got) == np.signbit(v), (hex(code), got, v)
+
+
+def test_ue8m0_matches_torch_e8m0():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).to(torch.float64)
+    for b in range(255):
+        assert oracle.ue8m0(b) == ref[b].item(), b
+    assert np.isnan(oracle.ue8m0(255)) and torch.isnan(ref[255])
+
+
+def test_e4m3fn_matches_torch_e4m3fn():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64)
+    for b in range(256):
+        got, want = oracle.e4m3fn(b), ref[b].item()
+        if np.isnan(want):
+            assert np.isnan(got), hex(b)
+        else:
+            assert got == want and np.signbit(got) == np.signbit(want), (hex(b), got, want)
+
+
+def test_hand_worked_scale_and_fp8_examples():
+    for kind, b, v in scale_fp8_examples():
+        got = oracle.ue8m0(b) if kind == "ue8m0" else oracle.e4m3fn(b)
+        assert got == v and np.signbit(got) == np.signbit(v), (kind, b, got, v)
+
+
+# ------------------------------------------------------ hand-built cases ----
+
+def _one_row_case(H, D, ps=16, n_tokens=16, cbs=16, nb=1, topk=4, q_format="mxfp4"):
+    """A one-row decode case with every array set explicitly by the caller."""
+    spec = W.Spec(name="hand", num_rows=1, num_heads=H, head_dim=D, page_size=ps, cbs=cbs,
+                  nb=nb, topk=topk, q_formats=(q_format,))
+    n_pages = (n_tokens + ps - 1) // ps
+    L = W.LayerData(weights=np.zeros((1, H), np.float32), num_pages=n_pages + 2,
+                    filled_pages=np.arange(n_pages, dtype=np.int64) + 2,
+                    filled_data=np.zeros((n_pages, spec.page_bytes), np.uint8))
+    if q_format == "mxfp4":
+        L.q_values = np.zeros((1, H, D // 2), np.uint8)
+        L.q_scales = np.full((1, H, D // 32), 127, np.uint8)
+    else:
+        L.q_fp8 = np.zeros((1, H, D), np.uint8)
+        L.q_rowscale = np.ones(1, np.float32)
+    table = np.full((1, n_pages), -1, np.int32)
+    table[0] = np.arange(n_pages) + 2           # logical page p -> physical page p + 2
+    case = W.Case(spec=spec, seed=0, row_ks=np.zeros(1, np.int32),
+                  row_ke=np.array([n_tokens], np.int32), row_table=np.zeros(1, np.int32),
+                  block_table=table,
+                  candidate_blocks=np.arange(nb, dtype=np.int32)[None, :].copy(), layers=[L])
+    return case
+
+
+def _set_k(case, t, values_bytes, scale_bytes):
+    s = case.spec
+    L = case.layers[0]
+    page = t // s.page_size - 0   # logical page; filled_data row = logical page
+    j = t % s.page_size
+    D = s.head_dim
+    L.filled_data[page, j * (D // 2):(j + 1) * (D // 2)] = values_bytes
+    off = s.values_bytes + j * (D // 32)
+    L.filled_data[page, off:off + D // 32] = scale_bytes
+
+
+def test_closed_form_constant_inputs_give_1024():
+    # Q elements 1.0 (bytes 0x22, scale 2^0); K elements 0.5 (bytes 0x11, scale 2^1):
+    # every term is 1.0 * 0.5 * 2 = 1, every dot 128, logit = 64 * (1/8) * 128 = 1024.
+    case = _one_row_case(H=64, D=128, topk=16)
+    L = case.layers[0]
+    L.q_values[:] = 0x22
+    L.weights[:] = 1.0 / 8.0
+    for t in range(16):
+        _set_k(case, t, 0x11, 128)
+    res = oracle.indexer_rows(case)
+    assert res.count[0] == 16
+    assert np.all(res.row_logits(0) == 1024.0)
+    assert list(res.indices[0]) == list(range(16))
+    # Flipping head h's Q to -1.0 (0xAA) makes its dot -128, which ReLU removes:
+    # each flipped head takes away exactly (1/8) * 128 = 16.
+    for nflip in (1, 5, 64):
+        L.q_values[0, :nflip] = 0xAA
+        res = oracle.indexer_rows(case)
+        assert np.all(res.row_logits(0) == 1024.0 - 16.0 * nflip), nflip
+        L.q_values[:] = 0x22
+
+
+def test_closed_form_weights_are_per_head():
+    # Only head 3 is positive: logit = w[3] * 128 whatever the other weights are.
+    case = _one_row_case(H=8, D=128, topk=16)
+    L = case.layers[0]
+    L.q_values[:] = 0xAA
+    L.q_values[0, 3] = 0x22
+    L.weights[0] = np.arange(8, dtype=np.float32) + 1.0
+    for t in range(16):
+        _set_k(case, t, 0x11, 128)
+    res = oracle.indexer_rows(case)
+    assert np.all(res.row_logits(0) == 4.0 * 128.0)
+
+
+@pytest.mark.parametrize("d0", list(range(0, 128, 1)))
+def test_one_hot_element_and_scale_block(d0):
+    # Q: element d0 = 1.0 with its block scale 2^e1; K of token t: element d0 = code
+    # c_t with its block scale 2^e2.  dot = e2m1(c_t) * 2^(e1 + e2), logit = ReLU(dot).
+    D = 128
+    case = _one_row_case(H=1, D=D, topk=16)
+    L = case.layers[0]
+    L.weights[:] = 1.0
+    e1 = (d0 % 7) - 3
+    qv = np.zeros(D // 2, np.uint8)
+    qv[d0 // 2] = (0x2 << 4) if d0 & 1 else 0x2
+    L.q_values[0, 0] = qv
+    L.q_scales[0, 0] = 127
+    L.q_scales[0, 0, d0 // 32] = 127 + e1
+    table = e2m1_table()
+    expect = []
+    for t in range(16):
+        c = t                       # codes 0..15 over the 16 tokens
+        e2 = (t % 5) - 2
+        kv = np.full(D // 2, 0x77, np.uint8)          # every other element is 6.0 ...
+        kv[d0 // 2] = (c << 4) | 0x7 if d0 & 1 else (0x70 | c)
+        ks = np.full(D // 32, 127, np.uint8)
+        ks[d0 // 32] = 127 + e2
+        _set_k(case, t, kv, ks)
+        expect.append(max(table[c] * 2.0 ** (e1 + e2), 0.0))
+    # ... but Q is zero there, so only element d0 contributes.
+    res = oracle.indexer_rows(case)
+    np.testing.assert_array_equal(res.row_logits(0), np.array(expect, np.float32))
+
+
+def test_closed_form_fp8_q_with_row_scale():
+    # Q e4m3 1.0 (0x38) everywhere with row scale 0.5; K 0.5 with scale 2^1:
+    # dot = 128 * 1.0 * 1.0 = 128, times 0.5 = 64; logit = 64 heads * (1/8) * 64 = 512.
+    case = _one_row_case(H=64, D=128, topk=16, q_format="fp8")
+    L = case.layers[0]
+    L.q_fp8[:] = 0x38
+    L.q_rowscale[:] = 0.5
+    L.weights[:] = 1.0 / 8.0
+    for t in range(16):
+        _set_k(case, t, 0x11, 128)
+    res = oracle.indexer_rows(case, q_format="fp8")
+    assert np.all(res.row_logits(0) == 512.0)
+    # Negative row direction: Q -1.0 (0xB8) makes every dot negative -> all logits 0.
+    L.q_fp8[:] = 0xB8
+    res = oracle.indexer_rows(case, q_format="fp8")
+    assert np.all(res.row_logits(0) == 0.0)
+
+
+def test_packed_nibble_order_examples():
+    # Each golden byte as K element pair (0, 1) against one-hot Q picks its halves.
+    for byte, e0, e1 in packed_examples():
+        for d0, want in ((0, e0), (1, e1)):
+            case = _one_row_case(H=1, D=32, topk=1, n_tokens=16, cbs=16)
+            L = case.layers[0]
+            L.weights[:] = 1.0
+            qv = np.zeros(16, np.uint8)
+            qv[0] = 0x2 << 4 if d0 else 0x2        # Q element d0 = 1.0
+            L.q_values[0, 0] = qv
+            kv = np.zeros(16, np.uint8)
+            kv[0] = byte
+            _set_k(case, 0, kv, 127)
+            res = oracle.indexer_rows(case)
+            assert res.row_logits(0)[0] == max(want, 0.0), (hex(byte), d0)
+
+
+# ------------------------------------------------------ textbook case -------
+
+@pytest.mark.parametrize("seed", range(20))
+def test_textbook_single_head_integer_dot(seed):
+    # H = 1, w = 1, all scales 2^0: logit = ReLU(sum_d q_d k_d) with e2m1 values, i.e.
+    # an integer dot product of doubled codes divided by 4; top-k = lexsort.
+    spec = W.Spec(name="tb", num_rows=2, num_heads=1, head_dim=64, page_size=8, cbs=8, nb=6,
+                  topk=9, ke_rule="uniform", ke_lo=20, ke_hi=60, scale_exp=(0, 0),
+                  cand_rule="messy", fill="all")
+    case = W.generate(spec, seed)
+    L = case.layers[0]
+    L.weights[:] = 1.0
+    twice = np.array([int(round(2 * e2m1_table()[c])) for c in range(16)], np.int64)
+    pool = L.host_pool(spec.page_bytes)
+    res = oracle.indexer_rows(case, pool=pool)
+    q2 = np.empty(64, np.int64)
+    for r in range(case.num_rows):
+        q2[0::2] = twice[L.q_values[r, 0] & 15]
+        q2[1::2] = twice[L.q_values[r, 0] >> 4]
+        toks = res.row_tokens(r)
+        want = []
+        for t in toks:
+            page = case.block_table[case.row_table[r], t // 8]
+            vals = pool[page, (t % 8) * 32:(t % 8 + 1) * 32]
+            k2 = np.empty(64, np.int64)
+            k2[0::2] = twice[vals & 15]
+            k2[1::2] = twice[vals >> 4]
+            want.append(max(int(q2 @ k2), 0) / 4.0)
+        want = np.array(want, np.float32)
+        np.testing.assert_array_equal(res.row_logits(r), want)
+        order = np.lexsort((toks, -want.astype(np.float64)))
+        count = min(spec.topk, toks.size)
+        exp = np.full(spec.topk, -1, np.int32)
+        exp[:count] = np.sort(toks[order[:count]])
+        np.testing.assert_array_equal(res.indices[r], exp)
+
+
+# ------------------------------------------------------ brute force ---------
+
+def _tiny_spec(rng, i):
+    H = int(rng.choice([1, 2, 4]))
+    D = int(rng.choice([32, 64, 128]))
+    ps = int(rng.choice([4, 8, 16]))
+    cbs = int(rng.choice([8, 16]))
+    mode = "prefill" if i % 4 == 3 else "decode"
+    R = int(rng.integers(1, 5))
+    ke_lo = int(rng.integers(1, 150))
+    ke_hi = int(rng.integers(ke_lo, 300))
+    return W.Spec(name=f"tiny{i}", num_rows=R, num_heads=H, head_dim=D, page_size=ps, cbs=cbs,
+                  nb=int(rng.integers(1, 12)), topk=int(rng.integers(1, 64)),
+                  mode=mode, ke_rule="uniform", ke_lo=ke_lo, ke_hi=ke_hi,
+                  context=ke_hi, ks_rule="random" if i % 3 else "zero",
+                  cand_rule=["messy", "distinct"][i % 2], fill="all",
+                  q_formats=("mxfp4", "fp8") if i % 5 == 0 else ("mxfp4",))
+
+
+@pytest.mark.parametrize("chunk", range(10))
+def test_oracle_matches_dense_then_mask_brute_force(chunk):
+    for i in range(chunk * 30, chunk * 30 + 30):
+        rng = np.random.default_rng(1000 + i)
+        spec = _tiny_spec(rng, i)
+        case = W.generate(spec, seed=i)
+        pool = case.layers[0].host_pool(spec.page_bytes)
+        for fmt in spec.q_formats:
+            res = oracle.indexer_rows(case, pool=pool, q_format=fmt)
+            for r in range(case.num_rows):
+                idx, toks, lg = brute_row(case, r, q_format=fmt, pool=pool)
+                np.testing.assert_array_equal(res.row_tokens(r), toks, err_msg=f"case {i} row {r}")
+                np.testing.assert_array_equal(res.row_logits(r), lg, err_msg=f"case {i} row {r}")
+                np.testing.assert_array_equal(res.indices[r], idx, err_msg=f"case {i} row {r}")
+
+
+# ------------------------------------------------------ invariants -----------
+
+def _check_invariants(case, res):
+    s = case.spec
+    for i, r in enumerate(res.rows):
+        ks, ke = int(case.row_ks[r]), int(case.row_ke[r])
+        blocks = set(int(b) for b in case.candidate_blocks[r] if b >= 0)
+        valid = sum(1 for b in blocks for t in range(b * s.cbs, (b + 1) * s.cbs) if ks <= t < ke)
+        count = min(s.topk, valid)
+        out = res.indices[i]
+        assert res.count[i] == valid
+        assert np.all(out[count:] == -1)
+        chosen = out[:count]
+        assert np.all(chosen >= ks) and np.all(chosen < ke)
+        assert all(int(t) // s.cbs in blocks for t in chosen)
+        assert np.all(np.diff(chosen) > 0)             # unique, ascending
+        # every chosen logit >= every unchosen one; ties resolved toward lower t
+        toks, lg = res.row_tokens(i), res.row_logits(i)
+        sel = np.isin(toks, chosen)
+        if count and (~sel).any():
+            lo = lg[sel].min()
+            hi = lg[~sel].max()
+            assert lo >= hi
+            if lo == hi:
+                assert toks[sel & (lg == lo)].max() < toks[~sel & (lg == hi)].min()
+
+
+@pytest.mark.parametrize("n", [1, 2])
+def test_invariants_on_workload_shapes(n):
+    case = W.generate(W.config(n), 0)
+    rows = np.arange(min(8, case.num_rows), dtype=np.int32)
+    res = oracle.indexer_rows(case, rows=rows)
+    _check_invariants(case, res)
+
+
+def test_invariants_on_messy_cases():
+    for i in range(40):
+        spec = W.Spec(name="m", num_rows=3, num_heads=4, head_dim=32, page_size=8, cbs=8, nb=10,
+                      topk=int(1 + i % 40), ke_rule="uniform", ke_lo=1, ke_hi=200,
+                      ks_rule="random", cand_rule="messy", fill="all")
+        case = W.generate(spec, i)
+        _check_invariants(case, oracle.indexer_rows(case))
+
+
+def test_k_at_least_valid_count_returns_all_valid_tokens():
+    # Causal prefill rows with i + 1 <= topk: the answer is 0..i then -1, whatever
+    # the logits are.
+    spec = W.Spec(name="c", num_rows=200, num_heads=2, head_dim=32, page_size=16, cbs=16,
+                  nb=16, topk=128, mode="prefill", ke_rule="causal", context=256,
+                  cand_rule="causal_all", fill="all")
+    case = W.generate(spec, 3)
+    res = oracle.indexer_rows(case)
+    for i in range(128):
+        want = np.full(128, -1, np.int32)
+        want[:i + 1] = np.arange(i + 1)
+        np.testing.assert_array_equal(res.indices[i], want)
+
+
+def test_all_equal_logits_take_lowest_tokens():
+    # K all zero -> every logit is 0 -> ties everywhere -> the lowest tokens win.
+    spec = W.Spec(name="z", num_rows=2, num_heads=2, head_dim=32, page_size=8, cbs=8, nb=5,
+                  topk=13, ke_rule="fixed", ke_lo=64, ke_hi=64, fill="all")
+    case = W.generate(spec, 1)
+    case.layers[0].filled_data[:] = 0
+    res = oracle.indexer_rows(case)
+    for i in range(2):
+        toks = res.row_tokens(i)
+        assert np.all(res.row_logits(i) == 0)
+        np.testing.assert_array_equal(res.indices[i], np.sort(toks)[:13])
+
+
+# ------------------------------------------------------ schedule -------------
+
+def test_expand_matches_token_set_definition():
+    for i in range(300):
+        rng = np.random.default_rng(i)
+        cbs = int(rng.choice([16, 32, 64, 128]))
+        sbk = int(rng.choice([s for s in (16, 32, 64) if cbs % s == 0]))
+        nb = int(rng.integers(1, 20))
+        ke = int(rng.integers(0, 3000))
+        ks = int(rng.integers(0, ke + 1)) if i % 2 else 0
+        cand = rng.integers(-3, (ke + cbs - 1) // cbs + 3, size=nb).astype(np.int32)
+        nsb = nb * (cbs // sbk)
+        si, n, end = oracle.expand_row(cand, cbs, sbk, ks, ke, nsb)
+        toks = set(t for b in set(int(x) for x in cand if x >= 0)
+                   for t in range(b * cbs, (b + 1) * cbs) if ks <= t < ke)
+        want = sorted(set(t // sbk for t in toks))
+        assert end == len(toks)
+        assert n == len(want)
+        np.testing.assert_array_equal(si[:n], want)
+        assert np.all(si[n:] == -1)
+        np.testing.assert_array_equal(oracle.candidate_tokens(cand, cbs, ks, ke), sorted(toks))
