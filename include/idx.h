@@ -1,0 +1,183 @@
+/*
+ * idx.h — C ABI of the candidate-consuming sparse MQA-logits indexer for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation (vLLM DeepSeek-V4.1 two-level selection; pages
+ * vllm.model_executor.layers.sparse_mqa_indexer, the DeepSeek-V4.1 sparse
+ * indexer backend source, and vllm.model_executor.layers.rocm_paged_mxfp4_indexer):
+ * a candidate-source layer publishes candidate blocks per query row; a consuming
+ * layer scores only the tokens inside those blocks, reading a paged MXFP4 K cache
+ * in place, and returns the row's top-k token indices.  For a row with query
+ * heads q_h (h < H), per-head weights w_h and candidate token set T:
+ *
+ *     logit[t] = sum_h w_h * max(q_h . k_t, 0)            (fp32 result)
+ *     out      = the min(topk, |T|) tokens of T with the largest logits,
+ *                ties toward the lower token, in ascending token order,
+ *                followed by -1 up to topk.
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers named in the structs and arguments are DEVICE pointers owned by
+ *    the caller unless a comment says "host".  Nothing is allocated per call.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *    asynchronously on it; the call returns once the launches are queued.
+ *  - Every argument check runs on the host before any launch.  On error the call
+ *    returns a negative idx_status, launches nothing, and idx_last_error() gives a
+ *    message (per calling thread).
+ *  - Device data is trusted as far as the stated preconditions go; page ids
+ *    outside [0, num_pages), table rows outside [0, num_tables) and logical pages
+ *    outside [0, pages_per_table) are never dereferenced: the affected sparse
+ *    blocks are dropped from the schedule instead (so a result computed from such
+ *    input is unspecified, but no read leaves the caller's buffers).
+ *  - Calls on one stream are ordered; concurrent calls that share a schedule or
+ *    workspace on different streams race.
+ */
+#ifndef IDX_H
+#define IDX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    IDX_OK = 0,
+    IDX_EINVAL = -1,         /* a null pointer, a negative size, an inconsistent shape */
+    IDX_EUNSUPPORTED = -2,   /* a configuration the kernels are not built for */
+    IDX_EWORKSPACE = -3,     /* a schedule or workspace buffer that is too small */
+    IDX_EHIP = -4            /* a HIP launch or runtime error */
+} idx_status;
+
+/* Query formats.  MXFP4: e2m1 values packed two per byte (element 2i in the low
+ * nibble) with one UE8M0 scale byte per 32 elements.  FP8: OCP e4m3fn codes with
+ * one fp32 scale per row applied to every dot product before the ReLU (the pages
+ * name the fp8 x fp4 kernel variant on the backend source page). */
+enum { IDX_Q_MXFP4 = 0, IDX_Q_FP8_E4M3_ROWSCALE = 1 };
+
+/* Per-model configuration, checked once (the backend builder's engine-start
+ * checks on the sparse indexer backend page).  Host struct. */
+typedef struct {
+    int32_t num_heads;             /* H; the kernels are built for 64 */
+    int32_t head_dim;              /* D; the kernels are built for 128 */
+    int32_t q_format;              /* IDX_Q_* */
+    int32_t page_size;             /* tokens per cache page; a multiple of sparse_block_kv */
+    int32_t candidate_block_size;  /* cbs: tokens per candidate block, > 0 */
+    int32_t sparse_block_kv;       /* sbk: tokens per sparse block; 0 = choose (filled in) */
+    int32_t num_candidate_blocks;  /* NB: candidate ids per row, > 0 */
+    int32_t topk;                  /* 1 <= topk <= NB * cbs, and <= IDX_MAX_TOPK */
+} idx_config;
+
+/* Kernel limits (sizes of the on-chip top-k working set). */
+#define IDX_MAX_ROW_COLS 8192      /* NB * cbs for the sparse path */
+#define IDX_MAX_DENSE_COLS 65536   /* max_ctx for the dense comparator */
+#define IDX_MAX_TOPK 8192
+
+/* Paged MXFP4 K cache of one layer.  A page holds page_size tokens; token slot j
+ * of page p has D/2 bytes of packed e2m1 values at values + p*values_page_stride
+ * + j*(D/2) and D/32 UE8M0 scale bytes at scales + p*scales_page_stride +
+ * j*(D/32), scale byte i covering elements [32i, 32i+32).  Logical page n of
+ * table row b is block_table[b*block_table_stride + n].  (The pages state only
+ * that the model writes the cache in the order the gfx950 kernel reads it; this
+ * two-pointer form covers both an interleaved and a split pool.) */
+typedef struct {
+    const uint8_t *values;
+    int64_t values_page_stride;    /* bytes between consecutive pages */
+    const uint8_t *scales;
+    int64_t scales_page_stride;    /* bytes between consecutive pages */
+    int64_t num_pages;             /* pages in the pool */
+    const int32_t *block_table;    /* int32 [num_tables][block_table_stride] */
+    int64_t block_table_stride;    /* int32 elements between table rows */
+    int32_t num_tables;
+    int32_t pages_per_table;       /* logical pages readable per table row */
+} idx_kcache;
+
+/* The rows of one call (SparseMQARowsMetadata on the backend page): decode rows
+ * (ks = 0, ke = the compressed context length, one table row each) or one prefill
+ * chunk (per-row [ks, ke), all rows on the request's table row). */
+typedef struct {
+    int32_t num_rows;              /* >= 0; 0 launches nothing */
+    const int32_t *row_ks;         /* [num_rows] K-range start, or NULL for all 0 */
+    const int32_t *row_ke;         /* [num_rows] exclusive K-range end */
+    const int32_t *row_table;      /* [num_rows] row -> table row, or NULL for row r -> r */
+} idx_rows;
+
+/* The shared sparse-column schedule of one step (built by idx_expand_candidates,
+ * read by every consuming layer of the step; the backend page's per-row
+ * sparse_indices / end scratch that the first consumer fills and later ones
+ * reuse).  Caller-owned device memory. */
+typedef struct {
+    int32_t *sparse_indices;       /* [num_rows][NSB] ascending sparse block ids, then -1 */
+    int32_t *end;                  /* [num_rows] valid token count |T| */
+    void *work;                    /* idx_schedule_work_bytes() bytes, opaque */
+    size_t work_bytes;
+} idx_schedule;
+
+/* Validate a configuration and fill in sparse_block_kv when it is 0: 64 if
+ * cbs % 64 == 0, else cbs when cbs is 16 or 32 (the backend's
+ * pick_sparse_block_kv, whose body the pages do not show).  Host only. */
+int idx_check_config(idx_config *cfg);
+
+/* NSB = NB * (cbs / sbk) sparse blocks per row, or a negative idx_status. Host. */
+int32_t idx_num_sparse_blocks(const idx_config *cfg);
+
+/* Bytes of idx_schedule.work for up to max_rows rows.  Host; 0 on a bad config. */
+size_t idx_schedule_work_bytes(const idx_config *cfg, int32_t max_rows);
+
+/* Bytes of scratch for up to max_rows rows: the sparse path needs
+ * max_rows * NB * cbs fp32 logits; the dense comparator max_rows * max_ctx
+ * (pass max_ctx = 0 when it is not used).  Host; 0 on a bad config. */
+size_t idx_workspace_bytes(const idx_config *cfg, int32_t max_rows, int32_t max_ctx);
+
+/* Message of the last failing call on this thread ("" if none).  Host. */
+const char *idx_last_error(void);
+
+/* Step a1: candidate expansion.  For each row, drop negative ids, count repeated
+ * ids once, sort ascending, split each candidate block into cbs/sbk sparse blocks,
+ * keep those holding a token of [ks, ke), pad with -1; end = number of valid
+ * tokens.  candidate_blocks is int32 [num_rows][cand_stride] (first NB used).
+ * Runs once per step; the schedule then serves every consuming layer whose K
+ * cache uses the same block table and pool size. */
+int idx_expand_candidates(const idx_config *cfg, const idx_rows *rows, const idx_kcache *k,
+                          const int32_t *candidate_blocks, int64_t cand_stride,
+                          const idx_schedule *sched, void *stream);
+
+/* Steps a2-a6 (and a8 with the fp8 format): paged gather, MX-scaled MFMA,
+ * ReLU + fp32 weighted head reduce, masking, per-row top-k.
+ *   q_values: MXFP4 u8 [num_rows][H][D/2]; FP8 u8 [num_rows][H][D]
+ *   q_scales: MXFP4 u8 [num_rows][H][D/32]; FP8 float [num_rows] (s_r > 0)
+ *   weights:  float [num_rows][H]
+ *   topk_indices: int32 rows of out_stride elements; slots [0, topk) written
+ *   logits_out: NULL, or float [num_rows][NB*cbs]: the logit of sparse column c
+ *     (token sparse_indices[c / sbk] * sbk + c % sbk), -inf where invalid
+ *   workspace: idx_workspace_bytes(cfg, num_rows, 0) bytes unless logits_out
+ *     is given (then it may be NULL).
+ * Serves decode rows and a prefill chunk alike; the schedule must come from
+ * idx_expand_candidates on the same rows. */
+int idx_sparse_mqa_logits_topk(const idx_config *cfg, const idx_rows *rows, const void *q_values,
+                               const void *q_scales, const float *weights, const idx_kcache *k,
+                               const idx_schedule *sched, int32_t *topk_indices,
+                               int64_t out_stride, float *logits_out, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/* Step a9, the comparator the sparse path replaces (the dense indexer scores the
+ * whole context and masks to the candidates: module summary of the
+ * sparse_mqa_indexer page): scores every token of [ks, ke) with the same
+ * per-column arithmetic as the sparse path, keeps the tokens whose sparse block is
+ * in the schedule, and selects the top-k with the same rule, so both return
+ * identical indices.  Needs the block table to map every page of [0, ke).
+ *   logits_out: NULL or float [num_rows][logits_stride] (token t at column t,
+ *     -inf outside [ks, ke)); workspace: idx_workspace_bytes(cfg, rows, max_ctx)
+ *     bytes when logits_out is NULL.  max_ctx bounds every ke. */
+int idx_dense_masked_logits_topk(const idx_config *cfg, const idx_rows *rows, int32_t max_ctx,
+                                 const void *q_values, const void *q_scales,
+                                 const float *weights, const idx_kcache *k,
+                                 const idx_schedule *sched, int32_t *topk_indices,
+                                 int64_t out_stride, float *logits_out, int64_t logits_stride,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IDX_H */

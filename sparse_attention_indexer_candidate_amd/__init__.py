@@ -1,0 +1,202 @@
+"""Python binding of libidx, the candidate-consuming sparse MQA-logits indexer for MI355X.
+
+Argument marshalling only: every step of the indexer runs in the HIP kernels of
+``libidx.so`` (built from ``csrc/`` by ``build.py``).  The functions carry the C
+names of ``include/idx.h`` and take either ctypes structs / raw device pointers, or
+torch tensors through the small helpers below (PyTorch supplies device memory and
+the stream, nothing else).  Importing this package fails loudly when the library
+has not been built; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libidx.so")
+
+IDX_OK = 0
+IDX_EINVAL = -1
+IDX_EUNSUPPORTED = -2
+IDX_EWORKSPACE = -3
+IDX_EHIP = -4
+IDX_Q_MXFP4 = 0
+IDX_Q_FP8_E4M3_ROWSCALE = 1
+IDX_MAX_ROW_COLS = 8192
+IDX_MAX_DENSE_COLS = 65536
+IDX_MAX_TOPK = 8192
+
+EXPORTED = ("idx_check_config", "idx_num_sparse_blocks", "idx_schedule_work_bytes",
+            "idx_workspace_bytes", "idx_last_error", "idx_expand_candidates",
+            "idx_sparse_mqa_logits_topk", "idx_dense_masked_logits_topk")
+
+
+class IdxError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{msg} (status {code})")
+        self.code = code
+
+
+class idx_config(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("q_format", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("candidate_block_size", ctypes.c_int32), ("sparse_block_kv", ctypes.c_int32),
+                ("num_candidate_blocks", ctypes.c_int32), ("topk", ctypes.c_int32)]
+
+
+class idx_kcache(ctypes.Structure):
+    _fields_ = [("values", ctypes.c_void_p), ("values_page_stride", ctypes.c_int64),
+                ("scales", ctypes.c_void_p), ("scales_page_stride", ctypes.c_int64),
+                ("num_pages", ctypes.c_int64), ("block_table", ctypes.c_void_p),
+                ("block_table_stride", ctypes.c_int64), ("num_tables", ctypes.c_int32),
+                ("pages_per_table", ctypes.c_int32)]
+
+
+class idx_rows(ctypes.Structure):
+    _fields_ = [("num_rows", ctypes.c_int32), ("row_ks", ctypes.c_void_p),
+                ("row_ke", ctypes.c_void_p), ("row_table", ctypes.c_void_p)]
+
+
+class idx_schedule(ctypes.Structure):
+    _fields_ = [("sparse_indices", ctypes.c_void_p), ("end", ctypes.c_void_p),
+                ("work", ctypes.c_void_p), ("work_bytes", ctypes.c_size_t)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python sparse_attention_indexer_candidate_amd/build.py` "
+                          "(there is no fallback implementation)")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    L.idx_check_config.argtypes = [P(idx_config)]
+    L.idx_check_config.restype = ctypes.c_int
+    L.idx_num_sparse_blocks.argtypes = [P(idx_config)]
+    L.idx_num_sparse_blocks.restype = i32
+    L.idx_schedule_work_bytes.argtypes = [P(idx_config), i32]
+    L.idx_schedule_work_bytes.restype = sz
+    L.idx_workspace_bytes.argtypes = [P(idx_config), i32, i32]
+    L.idx_workspace_bytes.restype = sz
+    L.idx_last_error.argtypes = []
+    L.idx_last_error.restype = ctypes.c_char_p
+    L.idx_expand_candidates.argtypes = [P(idx_config), P(idx_rows), P(idx_kcache), vp, i64,
+                                        P(idx_schedule), vp]
+    L.idx_expand_candidates.restype = ctypes.c_int
+    L.idx_sparse_mqa_logits_topk.argtypes = [P(idx_config), P(idx_rows), vp, vp, vp,
+                                             P(idx_kcache), P(idx_schedule), vp, i64, vp, vp, sz,
+                                             vp]
+    L.idx_sparse_mqa_logits_topk.restype = ctypes.c_int
+    L.idx_dense_masked_logits_topk.argtypes = [P(idx_config), P(idx_rows), i32, vp, vp, vp,
+                                               P(idx_kcache), P(idx_schedule), vp, i64, vp, i64,
+                                               vp, sz, vp]
+    L.idx_dense_masked_logits_topk.restype = ctypes.c_int
+    return L
+
+
+lib = _load()
+
+
+def idx_last_error() -> str:
+    return lib.idx_last_error().decode()
+
+
+def _check(rc: int) -> int:
+    if rc < 0:
+        raise IdxError(rc, idx_last_error())
+    return rc
+
+
+# ------------------------------------------------------------- raw C calls --
+
+def idx_check_config(cfg: idx_config) -> idx_config:
+    _check(lib.idx_check_config(ctypes.byref(cfg)))
+    return cfg
+
+
+def idx_num_sparse_blocks(cfg: idx_config) -> int:
+    return _check(lib.idx_num_sparse_blocks(ctypes.byref(cfg)))
+
+
+def idx_schedule_work_bytes(cfg: idx_config, max_rows: int) -> int:
+    return lib.idx_schedule_work_bytes(ctypes.byref(cfg), max_rows)
+
+
+def idx_workspace_bytes(cfg: idx_config, max_rows: int, max_ctx: int = 0) -> int:
+    return lib.idx_workspace_bytes(ctypes.byref(cfg), max_rows, max_ctx)
+
+
+def idx_expand_candidates(cfg, rows, k, candidate_blocks, cand_stride, sched, stream=None):
+    return _check(lib.idx_expand_candidates(ctypes.byref(cfg), ctypes.byref(rows),
+                                            ctypes.byref(k), _p(candidate_blocks), cand_stride,
+                                            ctypes.byref(sched), _p(stream)))
+
+
+def idx_sparse_mqa_logits_topk(cfg, rows, q_values, q_scales, weights, k, sched, topk_indices,
+                               out_stride, logits_out=None, workspace=None, workspace_bytes=0,
+                               stream=None):
+    return _check(lib.idx_sparse_mqa_logits_topk(
+        ctypes.byref(cfg), ctypes.byref(rows), _p(q_values), _p(q_scales), _p(weights),
+        ctypes.byref(k), ctypes.byref(sched), _p(topk_indices), out_stride, _p(logits_out),
+        _p(workspace), workspace_bytes, _p(stream)))
+
+
+def idx_dense_masked_logits_topk(cfg, rows, max_ctx, q_values, q_scales, weights, k, sched,
+                                 topk_indices, out_stride, logits_out=None, logits_stride=0,
+                                 workspace=None, workspace_bytes=0, stream=None):
+    return _check(lib.idx_dense_masked_logits_topk(
+        ctypes.byref(cfg), ctypes.byref(rows), max_ctx, _p(q_values), _p(q_scales), _p(weights),
+        ctypes.byref(k), ctypes.byref(sched), _p(topk_indices), out_stride, _p(logits_out),
+        logits_stride, _p(workspace), workspace_bytes, _p(stream)))
+
+
+# ------------------------------------------------------------- torch glue ---
+
+def _p(x):
+    """Raw pointer of a torch tensor / int / None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr() if x.numel() else None
+    if hasattr(x, "cuda_stream"):
+        return x.cuda_stream
+    raise TypeError(f"cannot take a pointer of {type(x)}")
+
+
+def make_config(num_heads=64, head_dim=128, q_format=IDX_Q_MXFP4, page_size=64,
+                candidate_block_size=64, sparse_block_kv=0, num_candidate_blocks=64,
+                topk=2048) -> idx_config:
+    return idx_check_config(idx_config(num_heads, head_dim, q_format, page_size,
+                                       candidate_block_size, sparse_block_kv,
+                                       num_candidate_blocks, topk))
+
+
+def make_kcache(pool, page_size, head_dim, block_table) -> idx_kcache:
+    """K cache over one uint8 pool tensor [num_pages, page_bytes] whose pages hold the
+    packed values [page_size][D/2] followed by the scales [page_size][D/32], and an
+    int32 block table [num_tables, pages_per_table]."""
+    page_bytes = pool.shape[1]
+    return idx_kcache(pool.data_ptr(), page_bytes, pool.data_ptr() + page_size * head_dim // 2,
+                      page_bytes, pool.shape[0], block_table.data_ptr(), block_table.stride(0),
+                      block_table.shape[0], block_table.shape[1])
+
+
+def make_rows(row_ke, row_ks=None, row_table=None) -> idx_rows:
+    return idx_rows(row_ke.shape[0], _p(row_ks), _p(row_ke), _p(row_table))
+
+
+class Schedule:
+    """Device buffers of one step's sparse-column schedule (owned by torch)."""
+
+    def __init__(self, cfg: idx_config, max_rows: int, device):
+        import torch
+
+        self.nsb = idx_num_sparse_blocks(cfg)
+        self.sparse_indices = torch.empty((max_rows, self.nsb), dtype=torch.int32, device=device)
+        self.end = torch.empty(max_rows, dtype=torch.int32, device=device)
+        nbytes = max(4, idx_schedule_work_bytes(cfg, max_rows))
+        self.work = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.struct = idx_schedule(self.sparse_indices.data_ptr(), self.end.data_ptr(),
+                                   self.work.data_ptr(), nbytes)

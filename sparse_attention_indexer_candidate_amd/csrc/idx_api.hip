@@ -1,0 +1,293 @@
+// C-ABI entry points of libidx (declared in include/idx.h): host-side validation,
+// then launches on the caller's stream.  Every check runs before the first HIP call,
+// so the error paths need no GPU.
+#include "idx.h"
+#include "idx_internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return IDX_OK;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// The engine-start checks of the sparse indexer backend builder, restated for
+// the gfx950 kernels.  Does not modify cfg.
+int check(const idx_config *cfg, int32_t *sbk_out) {
+    if (!cfg) return fail(IDX_EINVAL, "config is NULL");
+    if (cfg->num_heads != idx::kHeads || cfg->head_dim != idx::kHeadDim)
+        return fail(IDX_EUNSUPPORTED, "kernels are built for num_heads=%d head_dim=%d (got %d, %d)",
+                    idx::kHeads, idx::kHeadDim, cfg->num_heads, cfg->head_dim);
+    if (cfg->q_format != IDX_Q_MXFP4 && cfg->q_format != IDX_Q_FP8_E4M3_ROWSCALE)
+        return fail(IDX_EINVAL, "unknown q_format %d", cfg->q_format);
+    if (cfg->candidate_block_size <= 0 || cfg->num_candidate_blocks <= 0)
+        return fail(IDX_EINVAL, "candidate_block_size (%d) and num_candidate_blocks (%d) must be > 0",
+                    cfg->candidate_block_size, cfg->num_candidate_blocks);
+    const int32_t cbs = cfg->candidate_block_size;
+    int32_t sbk = cfg->sparse_block_kv;
+    if (sbk == 0) {
+        if (cbs % 64 == 0) sbk = 64;
+        else if (cbs == 16 || cbs == 32) sbk = cbs;
+        else return fail(IDX_EUNSUPPORTED, "no sparse block size for candidate_block_size %d "
+                         "(need a multiple of 64, or 16 or 32)", cbs);
+    } else if (!(sbk == 16 || sbk == 32 || sbk == 64) || cbs % sbk != 0) {
+        return fail(IDX_EUNSUPPORTED, "sparse_block_kv %d must be 16, 32 or 64 and divide "
+                    "candidate_block_size %d", sbk, cbs);
+    }
+    if (cfg->page_size <= 0 || cfg->page_size % sbk != 0)
+        return fail(IDX_EINVAL, "page_size %d must be a positive multiple of sparse_block_kv %d",
+                    cfg->page_size, sbk);
+    const int64_t cols = (int64_t)cfg->num_candidate_blocks * cbs;
+    if (cols > IDX_MAX_ROW_COLS)
+        return fail(IDX_EUNSUPPORTED, "num_candidate_blocks * candidate_block_size = %lld exceeds %d",
+                    (long long)cols, IDX_MAX_ROW_COLS);
+    if (cfg->topk < 1 || cfg->topk > cols || cfg->topk > IDX_MAX_TOPK)
+        return fail(IDX_EINVAL, "topk %d must be in [1, min(%lld, %d)]", cfg->topk,
+                    (long long)cols, IDX_MAX_TOPK);
+    if (sbk_out) *sbk_out = sbk;
+    return IDX_OK;
+}
+
+int check_filled(const idx_config *cfg, int32_t *sbk) {
+    int rc = check(cfg, sbk);
+    if (rc) return rc;
+    if (cfg->sparse_block_kv == 0)
+        return fail(IDX_EINVAL, "config not checked: call idx_check_config first");
+    return IDX_OK;
+}
+
+int check_rows(const idx_rows *rows) {
+    if (!rows) return fail(IDX_EINVAL, "rows is NULL");
+    if (rows->num_rows < 0) return fail(IDX_EINVAL, "num_rows %d < 0", rows->num_rows);
+    if (rows->num_rows > 0 && !rows->row_ke) return fail(IDX_EINVAL, "row_ke is NULL");
+    return IDX_OK;
+}
+
+int check_kcache(const idx_config *cfg, const idx_kcache *k) {
+    if (!k) return fail(IDX_EINVAL, "k cache is NULL");
+    if (!k->values || !k->scales || !k->block_table)
+        return fail(IDX_EINVAL, "k cache values, scales and block_table must be non-NULL");
+    if (k->num_pages <= 0 || k->num_tables <= 0 || k->pages_per_table <= 0)
+        return fail(IDX_EINVAL, "num_pages, num_tables and pages_per_table must be > 0");
+    if (k->block_table_stride < k->pages_per_table)
+        return fail(IDX_EINVAL, "block_table_stride %lld < pages_per_table %d",
+                    (long long)k->block_table_stride, k->pages_per_table);
+    const int64_t vrow = (int64_t)cfg->page_size * (idx::kHeadDim / 2);
+    const int64_t srow = (int64_t)cfg->page_size * (idx::kHeadDim / 32);
+    if (k->values_page_stride < vrow || k->scales_page_stride < srow)
+        return fail(IDX_EINVAL, "page strides (%lld, %lld) smaller than a page's values / scales "
+                    "(%lld, %lld bytes)", (long long)k->values_page_stride,
+                    (long long)k->scales_page_stride, (long long)vrow, (long long)srow);
+    if (!aligned(k->values, 16) || k->values_page_stride % 16 != 0)
+        return fail(IDX_EINVAL, "k values base and page stride must be 16-byte aligned");
+    if (!aligned(k->block_table, 4)) return fail(IDX_EINVAL, "block_table must be 4-byte aligned");
+    return IDX_OK;
+}
+
+int check_schedule(const idx_config *cfg, const idx_rows *rows, const idx_schedule *sched) {
+    if (!sched) return fail(IDX_EINVAL, "schedule is NULL");
+    if (!sched->sparse_indices || !sched->end || !sched->work)
+        return fail(IDX_EINVAL, "schedule sparse_indices, end and work must be non-NULL");
+    const size_t need = idx::schedule_work_bytes(rows->num_rows);
+    if (sched->work_bytes < need)
+        return fail(IDX_EWORKSPACE, "schedule work has %zu bytes, needs %zu", sched->work_bytes,
+                    need);
+    if (!aligned(sched->sparse_indices, 4) || !aligned(sched->end, 4) || !aligned(sched->work, 4))
+        return fail(IDX_EINVAL, "schedule buffers must be 4-byte aligned");
+    (void)cfg;
+    return IDX_OK;
+}
+
+int check_q(const idx_config *cfg, const void *qv, const void *qs, const float *w) {
+    if (!qv || !qs || !w) return fail(IDX_EINVAL, "q_values, q_scales and weights must be non-NULL");
+    if (!aligned(qv, 16)) return fail(IDX_EINVAL, "q_values must be 16-byte aligned");
+    if (!aligned(w, 4)) return fail(IDX_EINVAL, "weights must be 4-byte aligned");
+    if (cfg->q_format == IDX_Q_FP8_E4M3_ROWSCALE && !aligned(qs, 4))
+        return fail(IDX_EINVAL, "fp8 row scales must be 4-byte aligned");
+    return IDX_OK;
+}
+
+idx::KCache to_kcache(const idx_config *cfg, const idx_kcache *k) {
+    return idx::KCache{k->values, k->values_page_stride, k->scales, k->scales_page_stride,
+                       k->num_pages, k->block_table, k->block_table_stride, k->num_tables,
+                       k->pages_per_table, cfg->page_size};
+}
+
+idx::Rows to_rows(const idx_rows *r) {
+    return idx::Rows{r->num_rows, r->row_ks, r->row_ke, r->row_table};
+}
+
+idx::Schedule to_schedule(const idx_config *cfg, int32_t sbk, const idx_schedule *s) {
+    const int32_t nsb = cfg->num_candidate_blocks * (cfg->candidate_block_size / sbk);
+    return idx::Schedule{s->sparse_indices, s->end, (int32_t *)s->work, nsb, sbk};
+}
+
+int hip_status(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(IDX_EHIP, "%s: %s", what, hipGetErrorString(e));
+    return IDX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int idx_check_config(idx_config *cfg) {
+    int32_t sbk = 0;
+    int rc = check(cfg, &sbk);
+    if (rc) return rc;
+    cfg->sparse_block_kv = sbk;
+    return ok();
+}
+
+int32_t idx_num_sparse_blocks(const idx_config *cfg) {
+    int32_t sbk = 0;
+    int rc = check(cfg, &sbk);
+    if (rc) return rc;
+    ok();
+    return cfg->num_candidate_blocks * (cfg->candidate_block_size / sbk);
+}
+
+size_t idx_schedule_work_bytes(const idx_config *cfg, int32_t max_rows) {
+    if (check(cfg, nullptr)) return 0;
+    ok();
+    return idx::schedule_work_bytes(max_rows);
+}
+
+size_t idx_workspace_bytes(const idx_config *cfg, int32_t max_rows, int32_t max_ctx) {
+    if (check(cfg, nullptr)) return 0;
+    if (max_rows < 0 || max_ctx < 0) {
+        fail(IDX_EINVAL, "max_rows and max_ctx must be >= 0");
+        return 0;
+    }
+    ok();
+    const size_t sparse = (size_t)max_rows * cfg->num_candidate_blocks * cfg->candidate_block_size;
+    const size_t dense = (size_t)max_rows * (((size_t)max_ctx + 63) / 64 * 64);
+    return (sparse > dense ? sparse : dense) * sizeof(float);
+}
+
+const char *idx_last_error(void) { return g_err; }
+
+int idx_expand_candidates(const idx_config *cfg, const idx_rows *rows, const idx_kcache *k,
+                          const int32_t *candidate_blocks, int64_t cand_stride,
+                          const idx_schedule *sched, void *stream) {
+    int32_t sbk = 0;
+    int rc;
+    if ((rc = check_filled(cfg, &sbk)) || (rc = check_rows(rows)) || (rc = check_kcache(cfg, k)) ||
+        (rc = check_schedule(cfg, rows, sched)))
+        return rc;
+    if (rows->num_rows > 0 && !candidate_blocks) return fail(IDX_EINVAL, "candidate_blocks is NULL");
+    if (cand_stride < cfg->num_candidate_blocks)
+        return fail(IDX_EINVAL, "cand_stride %lld < num_candidate_blocks %d",
+                    (long long)cand_stride, cfg->num_candidate_blocks);
+    const idx::Schedule s = to_schedule(cfg, sbk, sched);
+    if ((rc = hip_status(idx::launch_expand(to_rows(rows), to_kcache(cfg, k), candidate_blocks,
+                                            cand_stride, cfg->num_candidate_blocks,
+                                            cfg->candidate_block_size, s, (hipStream_t)stream),
+                         "expand launch")))
+        return rc;
+    return ok();
+}
+
+int idx_sparse_mqa_logits_topk(const idx_config *cfg, const idx_rows *rows, const void *q_values,
+                               const void *q_scales, const float *weights, const idx_kcache *k,
+                               const idx_schedule *sched, int32_t *topk_indices,
+                               int64_t out_stride, float *logits_out, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+    int32_t sbk = 0;
+    int rc;
+    if ((rc = check_filled(cfg, &sbk)) || (rc = check_rows(rows)) || (rc = check_kcache(cfg, k)) ||
+        (rc = check_schedule(cfg, rows, sched)) || (rc = check_q(cfg, q_values, q_scales, weights)))
+        return rc;
+    if (!topk_indices || !aligned(topk_indices, 4))
+        return fail(IDX_EINVAL, "topk_indices must be non-NULL and 4-byte aligned");
+    if (out_stride < cfg->topk)
+        return fail(IDX_EINVAL, "out_stride %lld < topk %d", (long long)out_stride, cfg->topk);
+    const idx::Schedule s = to_schedule(cfg, sbk, sched);
+    const int32_t ncols = s.nsb * s.sbk;
+    float *logits = logits_out;
+    if (!logits) {
+        const size_t need = (size_t)rows->num_rows * ncols * sizeof(float);
+        if (!workspace && need) return fail(IDX_EWORKSPACE, "workspace is NULL (needs %zu bytes)", need);
+        if (workspace_bytes < need)
+            return fail(IDX_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+        logits = (float *)workspace;
+    }
+    if (!aligned(logits, 16)) return fail(IDX_EINVAL, "logits buffer must be 16-byte aligned");
+    const idx::Rows r = to_rows(rows);
+    const idx::KCache kc = to_kcache(cfg, k);
+    hipStream_t st = (hipStream_t)stream;
+    if ((rc = hip_status(idx::launch_score_sparse(cfg->q_format, r, q_values, q_scales, weights, kc,
+                                                  s, logits, st), "score launch")))
+        return rc;
+    if ((rc = hip_status(idx::launch_topk(false, r, s, logits, ncols, ncols, cfg->topk,
+                                          topk_indices, out_stride, st), "top-k launch")))
+        return rc;
+    return ok();
+}
+
+int idx_dense_masked_logits_topk(const idx_config *cfg, const idx_rows *rows, int32_t max_ctx,
+                                 const void *q_values, const void *q_scales,
+                                 const float *weights, const idx_kcache *k,
+                                 const idx_schedule *sched, int32_t *topk_indices,
+                                 int64_t out_stride, float *logits_out, int64_t logits_stride,
+                                 void *workspace, size_t workspace_bytes, void *stream) {
+    int32_t sbk = 0;
+    int rc;
+    if ((rc = check_filled(cfg, &sbk)) || (rc = check_rows(rows)) || (rc = check_kcache(cfg, k)) ||
+        (rc = check_schedule(cfg, rows, sched)) || (rc = check_q(cfg, q_values, q_scales, weights)))
+        return rc;
+    if (max_ctx <= 0 || max_ctx > IDX_MAX_DENSE_COLS)
+        return fail(IDX_EUNSUPPORTED, "max_ctx %d must be in [1, %d]", max_ctx, IDX_MAX_DENSE_COLS);
+    if (!topk_indices || !aligned(topk_indices, 4))
+        return fail(IDX_EINVAL, "topk_indices must be non-NULL and 4-byte aligned");
+    if (out_stride < cfg->topk)
+        return fail(IDX_EINVAL, "out_stride %lld < topk %d", (long long)out_stride, cfg->topk);
+    const int32_t ncols = (max_ctx + 63) / 64 * 64;
+    float *logits = logits_out;
+    int64_t lstride = logits_stride;
+    if (logits) {
+        if (lstride < ncols || lstride % 4 != 0)
+            return fail(IDX_EINVAL, "logits_stride %lld must be a multiple of 4 and >= %d",
+                        (long long)lstride, ncols);
+    } else {
+        lstride = ncols;
+        const size_t need = (size_t)rows->num_rows * ncols * sizeof(float);
+        if (!workspace && need) return fail(IDX_EWORKSPACE, "workspace is NULL (needs %zu bytes)", need);
+        if (workspace_bytes < need)
+            return fail(IDX_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+        logits = (float *)workspace;
+    }
+    if (!aligned(logits, 16)) return fail(IDX_EINVAL, "logits buffer must be 16-byte aligned");
+    const idx::Rows r = to_rows(rows);
+    const idx::KCache kc = to_kcache(cfg, k);
+    const idx::Schedule s = to_schedule(cfg, sbk, sched);
+    hipStream_t st = (hipStream_t)stream;
+    if ((rc = hip_status(idx::launch_score_dense(cfg->q_format, r, max_ctx, q_values, q_scales,
+                                                 weights, kc, logits, lstride, st),
+                         "dense score launch")))
+        return rc;
+    if ((rc = hip_status(idx::launch_topk(true, r, s, logits, lstride, ncols, cfg->topk,
+                                          topk_indices, out_stride, st), "dense top-k launch")))
+        return rc;
+    return ok();
+}
+
+}  // extern "C"

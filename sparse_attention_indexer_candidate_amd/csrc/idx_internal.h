@@ -1,0 +1,66 @@
+// Internal interface between the C-ABI entry points (idx_api.hip) and the kernel
+// launchers (idx_kernels.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace idx {
+
+constexpr int kHeads = 64;
+constexpr int kHeadDim = 128;
+
+// Layout of idx_schedule.work: int32 kept[max_rows] (sparse blocks listed per row).
+inline size_t schedule_work_bytes(int32_t max_rows) {
+    return (size_t)(max_rows > 0 ? max_rows : 0) * sizeof(int32_t);
+}
+
+struct KCache {
+    const uint8_t *values;
+    int64_t values_page_stride;
+    const uint8_t *scales;
+    int64_t scales_page_stride;
+    int64_t num_pages;
+    const int32_t *block_table;
+    int64_t block_table_stride;
+    int32_t num_tables;
+    int32_t pages_per_table;
+    int32_t page_size;
+};
+
+struct Rows {
+    int32_t num_rows;
+    const int32_t *ks;     // may be null (all 0)
+    const int32_t *ke;
+    const int32_t *table;  // may be null (row r -> r)
+};
+
+struct Schedule {
+    int32_t *sparse_indices;  // [rows][nsb]
+    int32_t *end;             // [rows]
+    int32_t *kept;            // [rows]
+    int32_t nsb;              // sparse blocks per row
+    int32_t sbk;              // tokens per sparse block
+};
+
+hipError_t launch_expand(const Rows &rows, const KCache &k, const int32_t *cand, int64_t cand_stride,
+                         int32_t nb, int32_t cbs, const Schedule &s, hipStream_t stream);
+
+// Scores every sparse column of every row into logits [rows][nsb*sbk].
+hipError_t launch_score_sparse(int q_format, const Rows &rows, const void *q_values,
+                               const void *q_scales, const float *weights, const KCache &k,
+                               const Schedule &s, float *logits, hipStream_t stream);
+
+// Scores every token t < max_ctx of every row into logits [rows][logits_stride]
+// (-inf outside [ks, ke)).
+hipError_t launch_score_dense(int q_format, const Rows &rows, int32_t max_ctx, const void *q_values,
+                              const void *q_scales, const float *weights, const KCache &k,
+                              float *logits, int64_t logits_stride, hipStream_t stream);
+
+// Per-row top-k over the logits written by one of the scoring launches.
+hipError_t launch_topk(bool dense, const Rows &rows, const Schedule &s, const float *logits,
+                       int64_t logits_stride, int32_t ncols, int32_t topk, int32_t *out,
+                       int64_t out_stride, hipStream_t stream);
+
+}  // namespace idx

@@ -1,0 +1,140 @@
+"""Helpers that run the HIP path through the C ABI and compare it with the oracle.
+
+Floating point: |gpu - oracle| <= 1e-6 + 1e-5 * |oracle| for every candidate token.
+Indices: with theta the oracle's count-th selected logit and tau = 1e-6 + 1e-5*|theta|,
+the GPU picks exactly count distinct valid tokens in ascending order, every token
+with oracle logit > theta + tau, none with oracle logit < theta - tau, -1 in the
+other slots, and exactly the oracle's set when no other oracle logit lies within
+tau of theta.  The GPU's selection is also checked bit-exactly against its own
+logits (an independent lexsort here), which pins the top-k kernel without any
+rounding slack.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+ATOL = 1e-6
+RTOL = 1e-5
+
+
+def gpu_row_tokens(si_row, kept, sbk, ks, ke, logits_row):
+    """(tokens, logits) of a row's valid sparse columns, ascending by token."""
+    cols = np.arange(kept * sbk)
+    toks = si_row[cols // sbk].astype(np.int64) * sbk + cols % sbk
+    ok = (toks >= ks) & (toks < ke)
+    return toks[ok].astype(np.int32), logits_row[cols[ok]]
+
+
+def exact_topk(tokens, logits, topk):
+    """Top-k of (tokens, fp32 logits): larger logit first, ties to the lower token."""
+    lg = logits.astype(np.float32) + np.float32(0.0)     # -0 -> +0
+    order = np.lexsort((tokens, -lg.astype(np.float64)))
+    count = min(topk, tokens.size)
+    out = np.full(topk, -1, np.int32)
+    out[:count] = np.sort(tokens[order[:count]])
+    return out
+
+
+def check_logits(o_tokens, o_logits, g_tokens, g_logits, what=""):
+    np.testing.assert_array_equal(g_tokens, o_tokens, err_msg=f"{what}: candidate tokens differ")
+    err = np.abs(g_logits.astype(np.float64) - o_logits.astype(np.float64))
+    lim = ATOL + RTOL * np.abs(o_logits.astype(np.float64))
+    bad = np.nonzero(err > lim)[0]
+    assert bad.size == 0, (f"{what}: {bad.size} logits outside tolerance, first token "
+                           f"{o_tokens[bad[0]]}: gpu {g_logits[bad[0]]!r} oracle {o_logits[bad[0]]!r}")
+
+
+def check_indices(o_tokens, o_logits, o_idx, g_idx, topk, what=""):
+    n = o_tokens.size
+    count = min(topk, n)
+    assert np.all(g_idx[count:] == -1), f"{what}: slots past count={count} are not -1"
+    chosen = g_idx[:count]
+    assert np.all(np.diff(chosen) > 0), f"{what}: chosen ids not strictly ascending"
+    if count == 0:
+        return
+    pos = np.searchsorted(o_tokens, chosen)
+    assert np.all(pos < n) and np.all(o_tokens[np.minimum(pos, n - 1)] == chosen), \
+        f"{what}: a chosen id is not a valid candidate token"
+    ol = o_logits.astype(np.float64)
+    o_sel = np.isin(o_tokens, o_idx[:count])
+    theta = ol[o_sel].min()
+    tau = ATOL + RTOL * abs(theta)
+    g_sel = np.zeros(n, bool)
+    g_sel[pos] = True
+    must = ol > theta + tau
+    assert np.all(g_sel[must]), f"{what}: missed {np.count_nonzero(must & ~g_sel)} clear winners"
+    forbid = ol < theta - tau
+    assert not np.any(g_sel & forbid), f"{what}: picked {np.count_nonzero(g_sel & forbid)} clear losers"
+    if np.count_nonzero(np.abs(ol - theta) <= tau) == 1:
+        np.testing.assert_array_equal(chosen, o_idx[:count], err_msg=f"{what}: set differs")
+
+
+def check_topk_exact_for_own_logits(g_tokens, g_logits, g_idx, topk, what=""):
+    np.testing.assert_array_equal(g_idx, exact_topk(g_tokens, g_logits, topk),
+                                  err_msg=f"{what}: GPU top-k is not exact for its own logits")
+
+
+class GpuRun:
+    """One configured indexer over a device case: schedule + per-layer calls."""
+
+    def __init__(self, case, dcase, sbk=0, q_format="mxfp4"):
+        import torch
+
+        import sparse_attention_indexer_candidate_amd as idx
+
+        self.idx = idx
+        s = case.spec
+        self.case, self.dcase, self.spec = case, dcase, s
+        self.q_format = q_format
+        self.cfg = idx.make_config(s.num_heads, s.head_dim,
+                                   idx.IDX_Q_MXFP4 if q_format == "mxfp4" else idx.IDX_Q_FP8_E4M3_ROWSCALE,
+                                   s.page_size, s.cbs, sbk, s.nb, s.topk)
+        self.sbk = self.cfg.sparse_block_kv
+        R = case.num_rows
+        dev = dcase.row_ke.device
+        self.rows = idx.make_rows(dcase.row_ke, dcase.row_ks, dcase.row_table)
+        self.sched = idx.Schedule(self.cfg, R, dev)
+        self.kcaches = [idx.make_kcache(L.pool, s.page_size, s.head_dim, dcase.block_table)
+                        for L in dcase.layers]
+        self.out = torch.full((R, s.topk), -7, dtype=torch.int32, device=dev)
+        self.logits = torch.empty((R, s.nb * s.cbs), dtype=torch.float32, device=dev)
+        ws = idx.idx_workspace_bytes(self.cfg, R, 0)
+        self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
+
+    def expand(self, layer=0):
+        self.idx.idx_expand_candidates(self.cfg, self.rows, self.kcaches[layer],
+                                       self.dcase.candidate_blocks,
+                                       self.dcase.candidate_blocks.stride(0), self.sched.struct)
+
+    def score(self, layer=0, with_logits=True):
+        L = self.dcase.layers[layer]
+        qv, qs = L.q(self.q_format)
+        self.idx.idx_sparse_mqa_logits_topk(
+            self.cfg, self.rows, qv, qs, L.weights, self.kcaches[layer], self.sched.struct,
+            self.out, self.out.stride(0), self.logits if with_logits else None,
+            None if with_logits else self.workspace,
+            0 if with_logits else self.workspace.numel())
+
+    def fetch(self):
+        import torch
+
+        torch.cuda.synchronize()
+        return dict(indices=self.out.cpu().numpy(), logits=self.logits.cpu().numpy(),
+                    sparse_indices=self.sched.sparse_indices.cpu().numpy(),
+                    end=self.sched.end.cpu().numpy(),
+                    kept=self.sched.work[:4 * self.case.num_rows].view(torch.int32).cpu().numpy())
+
+
+def compare_rows(case, res, ora, topk, sbk, what=""):
+    """Compare GPU results (dict from GpuRun.fetch) with an oracle RowResult."""
+    for i, r in enumerate(ora.rows):
+        r = int(r)
+        tag = f"{what} row {r}"
+        ks, ke = int(case.row_ks[r]), int(case.row_ke[r])
+        gt, gl = gpu_row_tokens(res["sparse_indices"][r], int(res["kept"][r]), sbk, ks, ke,
+                                res["logits"][r])
+        assert res["end"][r] == ora.count[i], f"{tag}: end {res['end'][r]} != {ora.count[i]}"
+        check_logits(ora.row_tokens(i), ora.row_logits(i), gt, gl, tag)
+        check_indices(ora.row_tokens(i), ora.row_logits(i), ora.indices[i], res["indices"][r],
+                      topk, tag)
+        check_topk_exact_for_own_logits(gt, gl, res["indices"][r], topk, tag)

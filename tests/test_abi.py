@@ -1,0 +1,178 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, applies the
+configuration rules, and rejects bad arguments on the host before any launch.
+
+No test here reaches a kernel launch: each call either fails a host check or has
+zero rows (which launches nothing), so fake pointers are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_indexer_candidate_amd as idx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x100000          # 16-byte aligned, never dereferenced
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "idx.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(idx_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert names == sorted(idx.EXPORTED), names
+    lib = ctypes.CDLL(idx.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def cfg(**kw):
+    base = dict(num_heads=64, head_dim=128, q_format=0, page_size=64, candidate_block_size=64,
+                sparse_block_kv=0, num_candidate_blocks=64, topk=2048)
+    base.update(kw)
+    return idx.idx_config(*[base[f] for f, _ in idx.idx_config._fields_])
+
+
+@pytest.mark.parametrize("cbs,want", [(64, 64), (128, 64), (192, 64), (16, 16), (32, 32)])
+def test_sparse_block_pick(cbs, want):
+    c = cfg(candidate_block_size=cbs, num_candidate_blocks=8, topk=8, page_size=128)
+    idx.idx_check_config(c)
+    assert c.sparse_block_kv == want
+    assert idx.idx_num_sparse_blocks(c) == 8 * cbs // want
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_heads=32), idx.IDX_EUNSUPPORTED),
+    (dict(head_dim=64), idx.IDX_EUNSUPPORTED),
+    (dict(q_format=7), idx.IDX_EINVAL),
+    (dict(candidate_block_size=0), idx.IDX_EINVAL),
+    (dict(num_candidate_blocks=0), idx.IDX_EINVAL),
+    (dict(candidate_block_size=48), idx.IDX_EUNSUPPORTED),
+    (dict(candidate_block_size=8), idx.IDX_EUNSUPPORTED),
+    (dict(sparse_block_kv=48), idx.IDX_EUNSUPPORTED),
+    (dict(sparse_block_kv=128, candidate_block_size=128), idx.IDX_EUNSUPPORTED),
+    (dict(page_size=96), idx.IDX_EINVAL),          # not a multiple of sbk = 64
+    (dict(page_size=0), idx.IDX_EINVAL),
+    (dict(topk=0), idx.IDX_EINVAL),
+    (dict(topk=4097), idx.IDX_EINVAL),             # > NB * cbs = 4096
+    (dict(num_candidate_blocks=129), idx.IDX_EUNSUPPORTED),  # 129 * 64 > 8192 columns
+])
+def test_config_errors(kw, code):
+    c = cfg(**kw)
+    with pytest.raises(idx.IdxError) as e:
+        idx.idx_check_config(c)
+    assert e.value.code == code
+    assert idx.idx_last_error()
+
+
+def test_explicit_sparse_block_kept():
+    c = cfg(candidate_block_size=64, sparse_block_kv=32, page_size=32)
+    idx.idx_check_config(c)
+    assert c.sparse_block_kv == 32 and idx.idx_num_sparse_blocks(c) == 128
+
+
+def test_sizes():
+    c = idx.idx_check_config(cfg())
+    assert idx.idx_workspace_bytes(c, 64, 0) == 64 * 4096 * 4
+    assert idx.idx_workspace_bytes(c, 128, 65536) == 128 * 65536 * 4
+    assert idx.idx_workspace_bytes(c, 2, 100) == 2 * 4096 * 4      # sparse need dominates
+    assert idx.idx_workspace_bytes(c, 2, 5000) == 2 * 5056 * 4     # dense rounds to 64
+    assert idx.idx_schedule_work_bytes(c, 64) >= 64 * 4
+    assert idx.idx_workspace_bytes(cfg(num_heads=1), 4, 0) == 0
+
+
+# ----------------------------------------------------------- call argument checks --
+
+def kcache(**kw):
+    base = dict(values=FAKE, values_page_stride=4352, scales=FAKE + 4096, scales_page_stride=4352,
+                num_pages=10, block_table=FAKE, block_table_stride=4, num_tables=2,
+                pages_per_table=4)
+    base.update(kw)
+    return idx.idx_kcache(*[base[f] for f, _ in idx.idx_kcache._fields_])
+
+
+def rows(n=2, **kw):
+    base = dict(num_rows=n, row_ks=None, row_ke=FAKE, row_table=None)
+    base.update(kw)
+    return idx.idx_rows(*[base[f] for f, _ in idx.idx_rows._fields_])
+
+
+def sched(work_bytes=1024, **kw):
+    base = dict(sparse_indices=FAKE, end=FAKE, work=FAKE, work_bytes=work_bytes)
+    base.update(kw)
+    return idx.idx_schedule(*[base[f] for f, _ in idx.idx_schedule._fields_])
+
+
+def sparse_call(c=None, r=None, k=None, s=None, qv=FAKE, qs=FAKE, w=FAKE, out=FAKE, ostride=2048,
+                logits=None, ws=None, wsb=0):
+    c = c or idx.idx_check_config(cfg())
+    return idx.lib.idx_sparse_mqa_logits_topk(
+        ctypes.byref(c), ctypes.byref(r or rows()), qv, qs, w, ctypes.byref(k or kcache()),
+        ctypes.byref(s or sched()), out, ostride, logits, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(qv=None), idx.IDX_EINVAL),
+    (dict(qv=FAKE + 4), idx.IDX_EINVAL),                 # q_values not 16-byte aligned
+    (dict(w=None), idx.IDX_EINVAL),
+    (dict(out=None), idx.IDX_EINVAL),
+    (dict(ostride=100), idx.IDX_EINVAL),                 # out_stride < topk
+    (dict(), idx.IDX_EWORKSPACE),                        # no logits buffer, no workspace
+    (dict(ws=FAKE, wsb=1000), idx.IDX_EWORKSPACE),        # workspace too small
+    (dict(s=sched(work_bytes=4)), idx.IDX_EWORKSPACE),   # schedule work too small for 2 rows
+    (dict(s=sched(end=None)), idx.IDX_EINVAL),
+    (dict(r=rows(-1)), idx.IDX_EINVAL),
+    (dict(r=rows(2, row_ke=None)), idx.IDX_EINVAL),
+    (dict(k=kcache(values=None)), idx.IDX_EINVAL),
+    (dict(k=kcache(num_pages=0)), idx.IDX_EINVAL),
+    (dict(k=kcache(block_table_stride=2)), idx.IDX_EINVAL),
+    (dict(k=kcache(values_page_stride=100)), idx.IDX_EINVAL),
+    (dict(k=kcache(values=FAKE + 8)), idx.IDX_EINVAL),
+])
+def test_sparse_call_rejects_bad_arguments(kw, code):
+    assert sparse_call(**kw) == code
+    assert idx.idx_last_error()
+
+
+def test_unchecked_config_is_rejected():
+    c = cfg()   # sparse_block_kv still 0
+    assert sparse_call(c=c, logits=FAKE) == idx.IDX_EINVAL
+    assert "idx_check_config" in idx.idx_last_error()
+
+
+def test_zero_rows_launch_nothing_and_succeed():
+    assert sparse_call(r=rows(0), logits=FAKE) == idx.IDX_OK
+    assert idx.idx_last_error() == ""
+    c = idx.idx_check_config(cfg())
+    rc = idx.lib.idx_expand_candidates(ctypes.byref(c), ctypes.byref(rows(0)),
+                                       ctypes.byref(kcache()), FAKE, 64, ctypes.byref(sched()),
+                                       None)
+    assert rc == idx.IDX_OK
+
+
+def test_expand_rejects_bad_arguments():
+    c = idx.idx_check_config(cfg())
+    call = lambda cand, stride, s=None: idx.lib.idx_expand_candidates(
+        ctypes.byref(c), ctypes.byref(rows()), ctypes.byref(kcache()), cand, stride,
+        ctypes.byref(s or sched()), None)
+    assert call(None, 64) == idx.IDX_EINVAL
+    assert call(FAKE, 10) == idx.IDX_EINVAL            # stride < NB
+    assert call(FAKE, 64, sched(sparse_indices=None)) == idx.IDX_EINVAL
+
+
+def test_dense_call_rejects_bad_arguments():
+    c = idx.idx_check_config(cfg())
+    def call(max_ctx=65536, logits=None, lstride=0, ws=None, wsb=0):
+        return idx.lib.idx_dense_masked_logits_topk(
+            ctypes.byref(c), ctypes.byref(rows()), max_ctx, FAKE, FAKE, FAKE,
+            ctypes.byref(kcache()), ctypes.byref(sched()), FAKE, 2048, logits, lstride, ws, wsb,
+            None)
+    assert call(max_ctx=0) == idx.IDX_EUNSUPPORTED
+    assert call(max_ctx=65537) == idx.IDX_EUNSUPPORTED
+    assert call() == idx.IDX_EWORKSPACE
+    assert call(logits=FAKE, lstride=1000) == idx.IDX_EINVAL
+    assert call(ws=FAKE, wsb=16) == idx.IDX_EWORKSPACE

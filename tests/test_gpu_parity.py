@@ -1,0 +1,212 @@
+"""GPU parity of the HIP path against the CPU oracle, called through the C ABI.
+
+Small cases span several 64-column groups, ragged tails, every sparse block size,
+ks > 0, duplicate / -1 / out-of-range candidates, empty rows and k above and below
+the valid count; they are compared on every row.  The five workloads run at their
+full sizes in the launch configuration the benchmark uses, compared on every row
+where the oracle finishes in seconds (workloads 1, 2, 5) and on sampled rows
+otherwise (3, 4), plus properties checked on every row at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from parity import GpuRun, compare_rows, exact_topk, gpu_row_tokens
+from workloads.device import to_device
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def run_and_compare(case, rows=None, layers=(0,), q_format="mxfp4", sbk=0, tag=""):
+    dcase = to_device(case, DEV)
+    g = GpuRun(case, dcase, sbk=sbk, q_format=q_format)
+    _say(f"[{tag}] expand rows={case.num_rows} sbk={g.sbk} fmt={q_format}")
+    g.expand()
+    si_o, end_o = oracle.expand(case, g.sbk)
+    res = None
+    for layer in layers:
+        _say(f"[{tag}] score layer {layer}")
+        g.score(layer, with_logits=True)
+        res = g.fetch()
+        np.testing.assert_array_equal(res["sparse_indices"], si_o, err_msg=f"{tag}: schedule")
+        np.testing.assert_array_equal(res["end"], end_o, err_msg=f"{tag}: end")
+        pool = case.layers[layer].host_pool(case.spec.page_bytes)
+        ora = oracle.indexer_rows(case, layer, rows, q_format, pool=pool)
+        compare_rows(case, res, ora, case.spec.topk, g.sbk, f"{tag} layer {layer}")
+        # the launch configuration of the benchmark (workspace, no logits output)
+        g.out.fill_(-7)
+        g.score(layer, with_logits=False)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(g.out.cpu().numpy(), res["indices"],
+                                      err_msg=f"{tag}: workspace launch differs")
+    return g, res
+
+
+SMALL = {
+    "ragged_sbk64_ks": W.Spec(name="s1", num_rows=37, num_heads=64, head_dim=128, page_size=128,
+                              cbs=128, nb=7, topk=100, ke_rule="uniform", ke_lo=1, ke_hi=3000,
+                              ks_rule="random", cand_rule="messy", fill="all"),
+    "sbk16": W.Spec(name="s2", num_rows=20, page_size=32, cbs=16, nb=40, topk=50,
+                    ke_rule="uniform", ke_lo=100, ke_hi=900, cand_rule="messy", fill="all"),
+    "sbk32_k_above_valid": W.Spec(name="s3", num_rows=13, page_size=64, cbs=32, nb=20, topk=300,
+                                  ke_rule="uniform", ke_lo=50, ke_hi=1500, ks_rule="random",
+                                  cand_rule="distinct", fill="all"),
+    "prefill_offset": W.Spec(name="s4", num_rows=300, page_size=64, cbs=64, nb=16, topk=128,
+                             mode="prefill", ke_rule="causal", row_offset=100, context=512,
+                             cand_rule="causal_all", fill="all"),
+    "empty_and_tiny_rows": W.Spec(name="s5", num_rows=9, page_size=64, cbs=64, nb=4, topk=64,
+                                  ke_rule="uniform", ke_lo=0, ke_hi=70, cand_rule="distinct",
+                                  fill="all"),
+    "cbs128_split_sbk32": W.Spec(name="s6", num_rows=11, page_size=128, cbs=128, nb=9, topk=200,
+                                 ke_rule="uniform", ke_lo=300, ke_hi=2000, ks_rule="random",
+                                 cand_rule="messy", fill="all"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_cases_all_rows(name):
+    spec = SMALL[name]
+    sbk = 32 if name == "cbs128_split_sbk32" else 0
+    run_and_compare(W.generate(spec, seed=11), sbk=sbk, tag=name)
+
+
+def test_small_case_fp8_query():
+    spec = W.Spec(name="f8", num_rows=21, page_size=64, cbs=64, nb=12, topk=150,
+                  ke_rule="uniform", ke_lo=10, ke_hi=2500, ks_rule="random", cand_rule="messy",
+                  fill="all", q_formats=("mxfp4", "fp8"))
+    case = W.generate(spec, seed=5)
+    run_and_compare(case, q_format="fp8", tag="fp8")
+
+
+def test_config1_tiny_decode_all_rows():
+    run_and_compare(W.generate(W.config(1), 0), tag="cfg1")
+
+
+def test_config2_decode_batch_all_rows():
+    run_and_compare(W.generate(W.config(2), 0), tag="cfg2")
+
+
+def test_config3_prefill_chunk_sampled_and_properties():
+    case = W.generate(W.config(3), 0)
+    rows = np.unique(np.r_[0, 1, 63, 64, 65, 1000, 2046, 2047, 2048, 2049, 3000, 4094, 4095,
+                           np.random.default_rng(3).integers(2048, 4096, 20)]).astype(np.int32)
+    g, res = run_and_compare(case, rows=rows, tag="cfg3")
+    # every row: rows with i + 1 <= k keep all tokens 0..i; the selection is exact for
+    # the GPU's own logits
+    k = case.spec.topk
+    for i in range(case.num_rows):
+        idx = res["indices"][i]
+        if i + 1 <= k:
+            want = np.full(k, -1, np.int32)
+            want[:i + 1] = np.arange(i + 1)
+            np.testing.assert_array_equal(idx, want, err_msg=f"cfg3 row {i}")
+        else:
+            gt, gl = gpu_row_tokens(res["sparse_indices"][i], int(res["kept"][i]), g.sbk, 0, i + 1,
+                                    res["logits"][i])
+            np.testing.assert_array_equal(gt, np.arange(i + 1))
+            np.testing.assert_array_equal(idx, exact_topk(gt, gl, k), err_msg=f"cfg3 row {i}")
+
+
+def test_config4_long_decode_four_layers_sampled():
+    case = W.generate(W.config(4), 0)
+    rows = np.r_[0, 1, 2, 127, 254, 255, np.random.default_rng(4).integers(3, 254, 6)].astype(np.int32)
+    g, res = run_and_compare(case, rows=np.unique(rows), layers=(0, 1, 2, 3), tag="cfg4")
+    k = case.spec.topk
+    for i in range(case.num_rows):     # last layer, every row
+        gt, gl = gpu_row_tokens(res["sparse_indices"][i], int(res["kept"][i]), g.sbk,
+                                int(case.row_ks[i]), int(case.row_ke[i]), res["logits"][i])
+        np.testing.assert_array_equal(res["indices"][i], exact_topk(gt, gl, k),
+                                      err_msg=f"cfg4 row {i}")
+
+
+@pytest.mark.parametrize("q_format", ["mxfp4", "fp8"])
+def test_config5_sparse_equals_dense_masked(q_format):
+    import sparse_attention_indexer_candidate_amd as idx
+
+    case = W.generate(W.config(5), 0)
+    g, res = run_and_compare(case, q_format=q_format, tag=f"cfg5-{q_format}")
+    # dense comparator on the same inputs: every token of [0, 65536) scored, masked to
+    # the candidates, same selection rule -> identical indices, identical logits
+    R, ctx = case.num_rows, 65536
+    dlog = torch.empty((R, ctx), dtype=torch.float32, device=DEV)
+    dout = torch.full((R, case.spec.topk), -7, dtype=torch.int32, device=DEV)
+    L = g.dcase.layers[0]
+    qv, qs = L.q(q_format)
+    _say(f"[cfg5-{q_format}] dense")
+    idx.idx_dense_masked_logits_topk(g.cfg, g.rows, ctx, qv, qs, L.weights, g.kcaches[0],
+                                     g.sched.struct, dout, dout.stride(0), dlog, dlog.stride(0))
+    torch.cuda.synchronize()
+    dout_np = dout.cpu().numpy()
+    np.testing.assert_array_equal(dout_np, res["indices"], err_msg="dense != sparse indices")
+    dl = dlog.cpu().numpy()
+    for i in range(R):
+        gt, gl = gpu_row_tokens(res["sparse_indices"][i], int(res["kept"][i]), g.sbk, 0, ctx,
+                                res["logits"][i])
+        np.testing.assert_array_equal(dl[i, gt].view(np.uint32), gl.view(np.uint32),
+                                      err_msg=f"dense logits differ bitwise row {i}")
+    # the workspace form of the dense call gives the same indices
+    ws = torch.empty(idx.idx_workspace_bytes(g.cfg, R, ctx), dtype=torch.uint8, device=DEV)
+    dout.fill_(-7)
+    idx.idx_dense_masked_logits_topk(g.cfg, g.rows, ctx, qv, qs, L.weights, g.kcaches[0],
+                                     g.sched.struct, dout, dout.stride(0), None, 0, ws, ws.numel())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(dout.cpu().numpy(), res["indices"])
+
+
+def test_repeat_calls_are_deterministic_and_reuse_schedule():
+    case = W.generate(W.config(2), 1)
+    dcase = to_device(case, DEV)
+    g = GpuRun(case, dcase)
+    g.expand()
+    g.score(0)
+    a = g.fetch()
+    for _ in range(3):
+        g.out.fill_(-7)
+        g.score(0)
+        b = g.fetch()
+        np.testing.assert_array_equal(a["indices"], b["indices"])
+        np.testing.assert_array_equal(a["logits"].view(np.uint32), b["logits"].view(np.uint32))
+
+
+def test_invariances_page_permutation_scale_and_weights():
+    spec = W.Spec(name="inv", num_rows=8, page_size=64, cbs=64, nb=16, topk=200,
+                  ke_rule="uniform", ke_lo=1500, ke_hi=4000, cand_rule="messy", fill="all")
+    case = W.generate(spec, seed=9)
+    g0, r0 = run_and_compare(case, tag="inv-base")
+    # permuting the physical pages (data and block table together) changes nothing
+    L = case.layers[0]
+    perm = np.random.default_rng(1).permutation(L.num_pages)
+    case_p = W.Case(spec, 9, case.row_ks, case.row_ke, case.row_table,
+                    np.where(case.block_table >= 0, perm[np.maximum(case.block_table, 0)], -1).astype(np.int32),
+                    case.candidate_blocks,
+                    [W.LayerData(L.weights, L.num_pages, perm[L.filled_pages], L.filled_data,
+                                 L.q_values, L.q_scales)])
+    g1, r1 = run_and_compare(case_p, tag="inv-perm")
+    np.testing.assert_array_equal(r0["indices"], r1["indices"])
+    np.testing.assert_array_equal(r0["logits"].view(np.uint32), r1["logits"].view(np.uint32))
+    # every K scale byte + 1 doubles every logit exactly and keeps the indices
+    data2 = L.filled_data.copy()
+    data2[:, spec.values_bytes:] += 1
+    case_s = W.Case(spec, 9, case.row_ks, case.row_ke, case.row_table, case.block_table,
+                    case.candidate_blocks,
+                    [W.LayerData(L.weights, L.num_pages, L.filled_pages, data2, L.q_values, L.q_scales)])
+    g2, r2 = run_and_compare(case_s, tag="inv-scale")
+    np.testing.assert_array_equal(r0["indices"], r2["indices"])
+    fin = np.isfinite(r0["logits"])
+    np.testing.assert_array_equal(r2["logits"][fin], 2 * r0["logits"][fin])
+    # shuffled candidate order gives the same schedule and result
+    cand = case.candidate_blocks.copy()
+    for r in range(cand.shape[0]):
+        cand[r] = np.random.default_rng(r).permutation(cand[r])
+    case_c = W.Case(spec, 9, case.row_ks, case.row_ke, case.row_table, case.block_table, cand,
+                    case.layers)
+    g3, r3 = run_and_compare(case_c, tag="inv-shuffle")
+    np.testing.assert_array_equal(r0["indices"], r3["indices"])
+    np.testing.assert_array_equal(r0["logits"].view(np.uint32), r3["logits"].view(np.uint32))
