@@ -1,0 +1,236 @@
+"""Throughput of the candidate-consuming sparse MQA-logits indexer on one MI355X.
+
+One step = the whole hot path over one batch: idx_expand_candidates (the shared
+sparse-column schedule) followed by idx_sparse_mqa_logits_topk for every consumer
+layer (paged gather, MX-scaled MFMA, ReLU + fp32 head reduce, per-row top-k).  The
+default workload is the decode batch (64 rows, contexts 8k-32k, 64 candidate blocks
+of 64 tokens, top-2048).  Inputs are seeded and synthetic and already resident in
+HBM when the timed region starts; the step rotates through enough copies of them
+(distinct device buffers) that no step finds its K pages in the 256 MB Infinity
+Cache.
+
+Prints one JSON line: candidate columns scored per second (and rows/s), the
+dominant kernel's roofline (algorithmic bytes per launch / average launch time,
+timed with HIP events on its stream), and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "candidate cols scored/s & rows/s incl. top-k; % of HBM / MXFP4-MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+MXFP4_PEAK_TFLOPS = 10066.0
+KERNEL_SOURCES = ["sparse_attention_indexer_candidate_amd/csrc/idx_kernels.hip",
+                  "sparse_attention_indexer_candidate_amd/csrc/idx_api.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(case, q_format: str, ends: np.ndarray) -> int:
+    """Bytes one launch must move: 68 B of K per valid column (64 B e2m1 + 4 B
+    UE8M0), and per row its query (4352 B MXFP4 / 8196 B fp8 with its row scale),
+    its 64 fp32 weights, ~12 B per candidate block (candidate id, schedule entry,
+    block-table entry) and the 4-byte top-k output slots."""
+    s = case.spec
+    per_col = s.head_dim // 2 + s.head_dim // 32
+    q = s.num_heads * (s.head_dim // 2 + s.head_dim // 32) if q_format == "mxfp4" \
+        else s.num_heads * s.head_dim + 4
+    per_row = q + 4 * s.num_heads + 12 * s.nb + 4 * s.topk
+    return int(ends.astype(np.int64).sum()) * per_col + case.num_rows * per_row
+
+
+def cpu_baseline(case, q_format: str, seconds: float):
+    """The oracle (unchanged, single-threaded) over whole passes of the workload's
+    rows, in order, until `seconds` have elapsed or every row has run once."""
+    import oracle
+
+    pool = case.layers[0].host_pool(case.spec.page_bytes)
+    rows_done, cols_done, t_total = 0, 0, 0.0
+    order = np.arange(case.num_rows, dtype=np.int32)
+    i = 0
+    while t_total < seconds and i < case.num_rows:
+        chunk = order[i:i + 4]
+        t0 = time.perf_counter()
+        res = oracle.indexer_rows(case, 0, chunk, q_format, pool=pool, with_logits=False)
+        t_total += time.perf_counter() - t0
+        rows_done += chunk.size
+        cols_done += int(res.count.sum())
+        i += chunk.size
+    return dict(value=cols_done / t_total, unit="cols/s", cores=1, kind="oracle",
+                rows_per_s=rows_done / t_total,
+                sample=f"{rows_done} of {case.num_rows} rows of layer 0 ({cols_done} candidate "
+                       f"cols), single-threaded C oracle, {t_total:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload 1-5 (default 2)")
+    ap.add_argument("--q-format", default="mxfp4", choices=["mxfp4", "fp8"])
+    ap.add_argument("--replicas", type=int, default=0, help="input copies (0 = auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(rows shard across GPUs with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_attention_indexer_candidate_amd as idx
+    import workloads as W
+    from workloads.device import to_device
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    spec = W.config(args.config)
+    if args.q_format == "fp8" and "fp8" not in spec.q_formats:
+        spec = W.config(args.config, q_formats=("mxfp4", "fp8"))
+    t0 = time.time()
+    case = W.generate(spec, args.seed)
+    gen_s = time.time() - t0
+
+    cfg = idx.make_config(spec.num_heads, spec.head_dim,
+                          idx.IDX_Q_MXFP4 if args.q_format == "mxfp4" else idx.IDX_Q_FP8_E4M3_ROWSCALE,
+                          spec.page_size, spec.cbs, 0, spec.nb, spec.topk)
+    R = case.num_rows
+
+    # Touched bytes per step decide how many copies defeat the Infinity Cache.
+    sched0 = idx.Schedule(cfg, R, dev)
+    base = to_device(case, dev)
+    kc0 = [idx.make_kcache(L.pool, spec.page_size, spec.head_dim, base.block_table)
+           for L in base.layers]
+    rows0 = idx.make_rows(base.row_ke, base.row_ks, base.row_table)
+    idx.idx_expand_candidates(cfg, rows0, kc0[0], base.candidate_blocks,
+                              base.candidate_blocks.stride(0), sched0.struct)
+    torch.cuda.synchronize()
+    ends = sched0.end.cpu().numpy()
+    step_bytes = algorithmic_bytes(case, args.q_format, ends) * spec.layers
+    pool_bytes = sum(L.pool.numel() for L in base.layers)
+    if args.replicas > 0:
+        nrep = args.replicas
+    else:
+        nrep = max(2, math.ceil(1.5e9 / step_bytes))
+        nrep = max(1, min(nrep, int(40e9 // max(pool_bytes, 1))))
+
+    reps = [base]
+    for _ in range(nrep - 1):
+        reps.append(type(base)(
+            row_ks=base.row_ks.clone(), row_ke=base.row_ke.clone(), row_table=base.row_table.clone(),
+            block_table=base.block_table.clone(), candidate_blocks=base.candidate_blocks.clone(),
+            layers=[type(L)(pool=L.pool.clone(), weights=L.weights.clone(),
+                            q_values=None if L.q_values is None else L.q_values.clone(),
+                            q_scales=None if L.q_scales is None else L.q_scales.clone(),
+                            q_fp8=None if L.q_fp8 is None else L.q_fp8.clone(),
+                            q_rowscale=None if L.q_rowscale is None else L.q_rowscale.clone())
+                    for L in base.layers]))
+
+    ws_bytes = idx.idx_workspace_bytes(cfg, R, 0)
+    plans = []
+    for d in reps:
+        plans.append(dict(
+            d=d, rows=idx.make_rows(d.row_ke, d.row_ks, d.row_table),
+            kc=[idx.make_kcache(L.pool, spec.page_size, spec.head_dim, d.block_table) for L in d.layers],
+            sched=idx.Schedule(cfg, R, dev),
+            out=torch.empty((R, spec.topk), dtype=torch.int32, device=dev),
+            ws=torch.empty(ws_bytes, dtype=torch.uint8, device=dev)))
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    n_events = args.steps * spec.layers
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_events)]
+
+    def step(i, timed):
+        p = plans[i % nrep]
+        d = p["d"]
+        idx.idx_expand_candidates(cfg, p["rows"], p["kc"][0], d.candidate_blocks,
+                                  d.candidate_blocks.stride(0), p["sched"].struct, stream=sh)
+        for layer, L in enumerate(d.layers):
+            qv, qs = L.q(args.q_format)
+            if timed:
+                ev[i * spec.layers + layer][0].record(stream)
+            idx.idx_sparse_mqa_logits_topk(cfg, p["rows"], qv, qs, L.weights, p["kc"][layer],
+                                           p["sched"].struct, p["out"], p["out"].stride(0), None,
+                                           p["ws"], p["ws"].numel(), stream=sh)
+            if timed:
+                ev[i * spec.layers + layer][1].record(stream)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    kernel_ms = [a.elapsed_time(b) for a, b in ev]
+    avg_kernel_s = float(np.mean(kernel_ms)) / 1e3
+    cols_per_step = int(ends.astype(np.int64).sum()) * spec.layers
+    launch_bytes = step_bytes / spec.layers
+    achieved = launch_bytes / avg_kernel_s / 1e9
+
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", f"traffic_sparse_fused_cfg{args.config}_{args.q_format}.json")
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            t = json.load(f)
+        if t.get("kernel_source_hash") == kernel_source_hash():
+            traffic = t.get("bytes_per_launch")
+
+    out = {
+        "metric": METRIC,
+        "value": cols_per_step * args.steps / elapsed,
+        "unit": "cols/s",
+        "rows_per_s": R * spec.layers * args.steps / elapsed,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4" if args.q_format == "mxfp4" else "fp8e4m3xmxfp4",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "rows": R, "candidate_blocks": spec.nb,
+                   "candidate_block_size": spec.cbs, "topk": spec.topk, "layers": spec.layers,
+                   "heads": spec.num_heads, "head_dim": spec.head_dim, "page_size": spec.page_size,
+                   "valid_cols_per_step": cols_per_step, "q_format": args.q_format,
+                   "input_copies": nrep, "seed": args.seed},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "sparse_fused_kernel", "avg_launch_us": avg_kernel_s * 1e6,
+                     "algorithmic_bytes_per_launch": launch_bytes,
+                     "mxfp4_tflops": 2 * spec.num_heads * spec.head_dim * cols_per_step
+                                     / spec.layers / avg_kernel_s / 1e12},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(case, args.q_format, args.cpu_seconds)
+    print(f"# generated inputs in {gen_s:.1f} s; {nrep} input copies", file=sys.stderr)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

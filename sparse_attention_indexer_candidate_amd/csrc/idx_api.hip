@@ -106,13 +106,15 @@ int check_schedule(const idx_config *cfg, const idx_rows *rows, const idx_schedu
     if (!sched) return fail(IDX_EINVAL, "schedule is NULL");
     if (!sched->sparse_indices || !sched->end || !sched->work)
         return fail(IDX_EINVAL, "schedule sparse_indices, end and work must be non-NULL");
-    const size_t need = idx::schedule_work_bytes(rows->num_rows);
+    int32_t sbk = 0;
+    check(cfg, &sbk);
+    const int32_t nsb = cfg->num_candidate_blocks * (cfg->candidate_block_size / sbk);
+    const size_t need = idx::schedule_work_bytes(rows->num_rows, nsb);
     if (sched->work_bytes < need)
         return fail(IDX_EWORKSPACE, "schedule work has %zu bytes, needs %zu", sched->work_bytes,
                     need);
     if (!aligned(sched->sparse_indices, 4) || !aligned(sched->end, 4) || !aligned(sched->work, 4))
         return fail(IDX_EINVAL, "schedule buffers must be 4-byte aligned");
-    (void)cfg;
     return IDX_OK;
 }
 
@@ -137,7 +139,12 @@ idx::Rows to_rows(const idx_rows *r) {
 
 idx::Schedule to_schedule(const idx_config *cfg, int32_t sbk, const idx_schedule *s) {
     const int32_t nsb = cfg->num_candidate_blocks * (cfg->candidate_block_size / sbk);
-    return idx::Schedule{s->sparse_indices, s->end, (int32_t *)s->work, nsb, sbk};
+    // capacity in rows of the work buffer; its layout depends only on work_bytes and
+    // nsb, so every call that passes the same schedule agrees on it
+    const size_t cap = s->work_bytes / ((1 + (size_t)nsb) * sizeof(int32_t));
+    int32_t *kept = (int32_t *)s->work;
+    const int32_t lsbk = sbk == 16 ? 4 : sbk == 32 ? 5 : 6;
+    return idx::Schedule{s->sparse_indices, s->end, kept, kept + cap, nsb, sbk, lsbk};
 }
 
 int hip_status(hipError_t e, const char *what) {
@@ -166,9 +173,11 @@ int32_t idx_num_sparse_blocks(const idx_config *cfg) {
 }
 
 size_t idx_schedule_work_bytes(const idx_config *cfg, int32_t max_rows) {
-    if (check(cfg, nullptr)) return 0;
+    int32_t sbk = 0;
+    if (check(cfg, &sbk)) return 0;
     ok();
-    return idx::schedule_work_bytes(max_rows);
+    return idx::schedule_work_bytes(max_rows,
+                                    cfg->num_candidate_blocks * (cfg->candidate_block_size / sbk));
 }
 
 size_t idx_workspace_bytes(const idx_config *cfg, int32_t max_rows, int32_t max_ctx) {
@@ -222,23 +231,22 @@ int idx_sparse_mqa_logits_topk(const idx_config *cfg, const idx_rows *rows, cons
         return fail(IDX_EINVAL, "out_stride %lld < topk %d", (long long)out_stride, cfg->topk);
     const idx::Schedule s = to_schedule(cfg, sbk, sched);
     const int32_t ncols = s.nsb * s.sbk;
-    float *logits = logits_out;
-    if (!logits) {
+    if (!logits_out) {
         const size_t need = (size_t)rows->num_rows * ncols * sizeof(float);
         if (!workspace && need) return fail(IDX_EWORKSPACE, "workspace is NULL (needs %zu bytes)", need);
         if (workspace_bytes < need)
             return fail(IDX_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
-        logits = (float *)workspace;
+        if (!aligned(workspace, 16)) return fail(IDX_EINVAL, "workspace must be 16-byte aligned");
+    } else if (!aligned(logits_out, 16)) {
+        return fail(IDX_EINVAL, "logits_out must be 16-byte aligned");
     }
-    if (!aligned(logits, 16)) return fail(IDX_EINVAL, "logits buffer must be 16-byte aligned");
     const idx::Rows r = to_rows(rows);
     const idx::KCache kc = to_kcache(cfg, k);
     hipStream_t st = (hipStream_t)stream;
-    if ((rc = hip_status(idx::launch_score_sparse(cfg->q_format, r, q_values, q_scales, weights, kc,
-                                                  s, logits, st), "score launch")))
-        return rc;
-    if ((rc = hip_status(idx::launch_topk(false, r, s, logits, ncols, ncols, cfg->topk,
-                                          topk_indices, out_stride, st), "top-k launch")))
+    if ((rc = hip_status(idx::launch_sparse(cfg->q_format, r, q_values, q_scales, weights, kc, s,
+                                            logits_out, (float *)workspace, cfg->topk,
+                                            topk_indices, out_stride, st),
+                         "sparse launch")))
         return rc;
     return ok();
 }
@@ -284,8 +292,9 @@ int idx_dense_masked_logits_topk(const idx_config *cfg, const idx_rows *rows, in
                                                  weights, kc, logits, lstride, st),
                          "dense score launch")))
         return rc;
-    if ((rc = hip_status(idx::launch_topk(true, r, s, logits, lstride, ncols, cfg->topk,
-                                          topk_indices, out_stride, st), "dense top-k launch")))
+    if ((rc = hip_status(idx::launch_dense_topk(r, kc, s, logits, lstride, ncols, cfg->topk,
+                                                topk_indices, out_stride, st),
+                         "dense top-k launch")))
         return rc;
     return ok();
 }

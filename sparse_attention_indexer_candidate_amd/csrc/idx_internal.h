@@ -11,9 +11,11 @@ namespace idx {
 constexpr int kHeads = 64;
 constexpr int kHeadDim = 128;
 
-// Layout of idx_schedule.work: int32 kept[max_rows] (sparse blocks listed per row).
-inline size_t schedule_work_bytes(int32_t max_rows) {
-    return (size_t)(max_rows > 0 ? max_rows : 0) * sizeof(int32_t);
+// Layout of idx_schedule.work for a capacity of R rows: int32 kept[R] (sparse blocks
+// listed per row), then int32 pages[R][nsb] (the page holding each listed sparse
+// block, resolved through the block table once per step).
+inline size_t schedule_work_bytes(int32_t max_rows, int32_t nsb) {
+    return (size_t)(max_rows > 0 ? max_rows : 0) * (1 + (size_t)nsb) * sizeof(int32_t);
 }
 
 struct KCache {
@@ -40,17 +42,24 @@ struct Schedule {
     int32_t *sparse_indices;  // [rows][nsb]
     int32_t *end;             // [rows]
     int32_t *kept;            // [rows]
+    int32_t *pages;           // [rows][nsb]
     int32_t nsb;              // sparse blocks per row
-    int32_t sbk;              // tokens per sparse block
+    int32_t sbk;              // tokens per sparse block (16, 32 or 64)
+    int32_t lsbk;             // log2(sbk)
 };
 
 hipError_t launch_expand(const Rows &rows, const KCache &k, const int32_t *cand, int64_t cand_stride,
                          int32_t nb, int32_t cbs, const Schedule &s, hipStream_t stream);
 
-// Scores every sparse column of every row into logits [rows][nsb*sbk].
-hipError_t launch_score_sparse(int q_format, const Rows &rows, const void *q_values,
-                               const void *q_scales, const float *weights, const KCache &k,
-                               const Schedule &s, float *logits, hipStream_t stream);
+// The sparse path: scores every sparse column of every row and writes each row's
+// top-k into out.  With at least as many rows as CUs one launch does both per row
+// (logits in LDS; copied to logits_out if given); otherwise a split scoring launch
+// writes logits [rows][nsb*sbk] to logits_out or workspace and a second launch
+// selects.
+hipError_t launch_sparse(int q_format, const Rows &rows, const void *q_values, const void *q_scales,
+                         const float *weights, const KCache &k, const Schedule &s, float *logits_out,
+                         float *workspace, int32_t topk, int32_t *out, int64_t out_stride,
+                         hipStream_t stream);
 
 // Scores every token t < max_ctx of every row into logits [rows][logits_stride]
 // (-inf outside [ks, ke)).
@@ -58,9 +67,9 @@ hipError_t launch_score_dense(int q_format, const Rows &rows, int32_t max_ctx, c
                               const void *q_scales, const float *weights, const KCache &k,
                               float *logits, int64_t logits_stride, hipStream_t stream);
 
-// Per-row top-k over the logits written by one of the scoring launches.
-hipError_t launch_topk(bool dense, const Rows &rows, const Schedule &s, const float *logits,
-                       int64_t logits_stride, int32_t ncols, int32_t topk, int32_t *out,
-                       int64_t out_stride, hipStream_t stream);
+// Per-row top-k over the dense logits (tokens masked to the schedule's blocks).
+hipError_t launch_dense_topk(const Rows &rows, const KCache &k, const Schedule &s,
+                             const float *logits, int64_t logits_stride, int32_t ncols,
+                             int32_t topk, int32_t *out, int64_t out_stride, hipStream_t stream);
 
 }  // namespace idx

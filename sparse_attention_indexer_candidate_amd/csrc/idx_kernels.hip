@@ -1,16 +1,26 @@
 // gfx950 kernels of the candidate-consuming sparse MQA-logits indexer.
 //
-//  expand_kernel       candidate expansion -> sparse-column schedule (one workgroup per row)
-//  score_*_kernel      paged gather of e2m1 K + UE8M0 scales, MX-scaled MFMA
-//                      [64 heads x 128] . [128 x 16 columns], ReLU, fp32 weighted
-//                      head reduce; one wave per 64-column group
-//  topk_kernel         per-row radix select on the fp32 logits with ties toward the
-//                      lower column, ascending output, -1 fill (one workgroup per row)
+//  expand_kernel        candidate expansion -> sparse-column schedule, one wave per row:
+//                       register/shuffle bitonic sort of the candidate ids, ballot
+//                       compaction, block-table lookups (page ids kept in the schedule)
+//  score core           paged gather of e2m1 K + UE8M0 scales, MX-scaled MFMA
+//                       [64 heads x 128] . [128 x 16 tokens], ReLU, fp32 weighted head
+//                       reduce; one wave per 64-column group, K loads batched
+//  select_topk          per-row radix select on fp32 logits, ties toward the lower
+//                       column, ascending output, -1 fill (one workgroup per row)
+//  fused_row_kernel     rows >= CUs: one workgroup scores a whole row into LDS and
+//                       selects from LDS (no global round trip, no cross-workgroup sync)
+//  score_split_kernel + topk_split_kernel
+//                       fewer rows than CUs: rows split over workgroups, logits in
+//                       global scratch, selection in a second launch
+//  score_dense_kernel + dense_topk_kernel
+//                       the comparator: every token of [ks, ke) with the same
+//                       per-tile code, masked to the candidates, same selection
 //
-// The operation follows the vLLM DeepSeek-V4.1 pages (sparse_mqa_indexer,
-// the sparse indexer backend source, rocm_paged_mxfp4_indexer): logits over the
-// candidate blocks only, fp32 weights and logits on gfx950, top-k token ids with
-// -1 past the valid count.
+// The operation follows the vLLM DeepSeek-V4.1 pages (sparse_mqa_indexer, the
+// sparse indexer backend source, rocm_paged_mxfp4_indexer): logits over the
+// candidate blocks only, fp32 weights and logits on gfx950, top-k token ids with -1
+// past the valid count.
 //
 // MFMA operand layout of v_mfma_scale_f32_16x16x128_f8f6f4 (measured on gfx950):
 //   A (16 x 128), e2m1: lane l holds row l%16, k = 32*(l/16) + j (j < 32), element
@@ -23,25 +33,61 @@
 // With A = 16 query heads of one row and B = 16 tokens of K, one 16-byte load per
 // lane delivers a token's packed values straight into the B operand, and the head
 // reduce is 16 in-register FMAs per lane plus a 4-way cross-lane exchange.
+//
+// fp8 (e4m3) queries use v_mfma_f32_16x16x32_bf16 instead: the MX fp8 x fp4 MFMA
+// adds each aligned group of 8 products in a narrow adder (measured: 448 + 2^-9
+// in one group returns 448), which misses the fp32 tolerance on real data, while
+// the bf16 MFMA keeps fp32-level sums.  e4m3 codes and scaled e2m1 values are
+// exact in bf16 (converted with v_cvt_scalef32_pk_bf16_fp8 / _fp4).  The bf16
+// MFMA's k slot (step s, lane group g, element j) carries dimension
+// 32*g + 8*s + j for both operands, so lane g again reads the 32 dimensions of
+// its scale block: the same 16-byte K load and scale byte as the fp4 path.
+//
+// No kernel here synchronises workgroups through memory: an agent-scope release /
+// acquire pair costs an L2 writeback and invalidate on this multi-XCD part
+// (measured: +29 us on a 64-row decode batch), so cross-workgroup hand-offs go
+// through kernel boundaries instead.
 #include "idx_internal.h"
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <climits>
 
 namespace idx {
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
-constexpr int kMaxNB = 512;    // NB * cbs <= 8192 with cbs >= 16
-constexpr int kMaxNSB = 512;   // NSB * sbk <= 8192 with sbk >= 16
-constexpr int kMaxDenseBlocks = 65536 / 16;
+constexpr int kMaxNB = 512;          // NB * cbs <= 8192 with cbs >= 16
+constexpr int kMaxNSB = 512;         // NSB * sbk <= 8192 with sbk >= 16
+constexpr int kMaxRowCols = 8192;    // NB * cbs
+constexpr int kMaxDenseCols = 65536;
+constexpr int kMaxDenseBlocks = kMaxDenseCols / 16;
+
+// Pointers rebuilt from integers (per-tile bases read back from lanes) are tagged
+// with the global address space so loads use the global (not flat) path.
+#define kGlobal __attribute__((address_space(1)))
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// ---------------------------------------------------------------- block scans --
+// 64-bit value from two 32-bit halves as returned by v_readlane (a signed int): both
+// halves are zero-extended, never sign-extended.
+__device__ __forceinline__ uint64_t join64(int hi, int lo) {
+    return ((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    const int lane = threadIdx.x & (kWave - 1);
+    return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// ---------------------------------------------------------------- reductions ---
 
 __device__ __forceinline__ int wave_incl_scan(int x) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -53,9 +99,16 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
     return x;
 }
 
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+    return x;
+}
+
 // Exclusive prefix sum over the workgroup (NT threads); *total gets the sum.
-// smem holds NT/64 + 1 ints.  Contains barriers: call from every thread.
-template <int NT>
+// smem holds NT/64 + 1 ints.  Contains barriers: call from every thread.  With
+// REUSE the call ends with a barrier so smem can be reused right away.
+template <int NT, bool REUSE = true>
 __device__ int block_excl_scan(int x, int *total, int *smem) {
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
     int incl = wave_incl_scan(x);
@@ -73,121 +126,219 @@ __device__ int block_excl_scan(int x, int *total, int *smem) {
     __syncthreads();
     int res = smem[wid] + incl - x;
     *total = smem[NT / kWave];
-    __syncthreads();
+    if (REUSE) __syncthreads();
     return res;
+}
+
+// Workgroup count / min / max of valid keys.  smem holds 3 * NT/64 words and is
+// not reused afterwards (no trailing barrier).
+template <int NT>
+__device__ void block_count_min_max(int n, uint32_t mn, uint32_t mx, int *count, uint32_t *bmin,
+                                    uint32_t *bmax, uint32_t *smem) {
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        n += __shfl_xor(n, o, kWave);
+        mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
+    }
+    constexpr int W = NT / kWave;
+    if (lane == 0) {
+        smem[wid] = (uint32_t)n;
+        smem[W + wid] = mn;
+        smem[2 * W + wid] = mx;
+    }
+    __syncthreads();
+    int c = 0;
+    uint32_t a = 0xFFFFFFFFu, b = 0u;
+    for (int w = 0; w < W; ++w) {
+        c += (int)smem[w];
+        a = min(a, smem[W + w]);
+        b = max(b, smem[2 * W + w]);
+    }
+    *count = c;
+    *bmin = a;
+    *bmax = b;
 }
 
 // ---------------------------------------------------------------- expansion ----
 
 constexpr int kExpandThreads = 256;
+constexpr int kExpandRows = kExpandThreads / kWave;
 
-// One workgroup per row.  kept[i] marks candidate ids that are >= 0, hold a token
-// of [ks, ke) and are the first occurrence of their id; a kept id's rank among
-// kept ids gives its sorted position; each kept block splits into cbs/sbk sparse
-// blocks at positions rank*per + j, of which those holding a token of [ks, ke)
-// (and whose page the table maps inside the pool) are compacted in order.
+// One wave per row; lane l holds candidate ids l, l + 64, ... (E per lane).  Ids that
+// are negative or hold no token of [ks, ke) become INT_MAX; a bitonic sort over the
+// 64*E register slots (shuffles across lanes, swaps within a lane) orders them; an id
+// is kept if it differs from its predecessor (so repeats count once); kept blocks
+// split into cbs/sbk sparse blocks, of which those holding a token of [ks, ke) and
+// mapped by the block table inside the pool are listed in order with their page.
+template <int E>
 __global__ __launch_bounds__(kExpandThreads) void expand_kernel(Rows rows, KCache k,
                                                                 const int32_t *cand,
                                                                 int64_t cand_stride, int32_t nb,
                                                                 int32_t cbs, Schedule s) {
-    __shared__ int32_t s_id[kMaxNB];
-    __shared__ int32_t s_keep[kMaxNB];
-    __shared__ int32_t s_sb[kMaxNSB];
-    __shared__ int32_t s_cnt[kMaxNSB];
-    __shared__ int s_scan[kExpandThreads / kWave + 1];
-    constexpr int NT = kExpandThreads;
-    const int r = blockIdx.x, tid = threadIdx.x;
+    __shared__ int32_t s_blk[kExpandRows][kMaxNB];
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int r = blockIdx.x * kExpandRows + wave;
+    if (r >= rows.num_rows) return;  // whole wave; no workgroup barriers below
     const int64_t ks = rows.ks ? rows.ks[r] : 0;
     const int64_t ke = rows.ke[r];
     const int tbl = rows.table ? rows.table[r] : r;
     const bool tbl_ok = tbl >= 0 && tbl < k.num_tables;
     const int sbk = s.sbk, nsb = s.nsb, per = cbs / sbk;
 
-    for (int i = tid; i < nb; i += NT) s_id[i] = cand[(int64_t)r * cand_stride + i];
-    for (int i = tid; i < nsb; i += NT) {
-        s_sb[i] = -1;
-        s_cnt[i] = 0;
+    int v[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int i = e * kWave + lane;
+        const int b = i < nb ? cand[(int64_t)r * cand_stride + i] : -1;
+        const bool ok = b >= 0 && (int64_t)b * cbs < ke && ((int64_t)b + 1) * cbs > ks;
+        v[e] = ok ? b : INT_MAX;
     }
-    __syncthreads();
-    for (int i = tid; i < nb; i += NT) {
-        const int b = s_id[i];
-        bool keep = b >= 0 && (int64_t)b * cbs < ke && ((int64_t)b + 1) * cbs > ks;
-        for (int j = 0; j < i && keep; ++j) keep = s_id[j] != b;
-        s_keep[i] = keep;
-    }
-    __syncthreads();
-    for (int i = tid; i < nb; i += NT) {
-        if (!s_keep[i]) continue;
-        const int b = s_id[i];
-        int rank = 0;
-        for (int j = 0; j < nb; ++j) rank += (s_keep[j] && s_id[j] < b);
-        for (int j = 0; j < per; ++j) {
-            const int64_t sb = (int64_t)b * per + j;
-            const int64_t lo = max(sb * sbk, ks), hi = min(sb * sbk + sbk, ke);
-            if (hi <= lo) continue;
-            const int64_t lp = sb * sbk / k.page_size;
-            if (!tbl_ok || lp >= k.pages_per_table) continue;
-            const int32_t page = k.block_table[(int64_t)tbl * k.block_table_stride + lp];
-            if (page < 0 || page >= k.num_pages) continue;
-            s_sb[rank * per + j] = (int32_t)sb;
-            s_cnt[rank * per + j] = (int32_t)(hi - lo);
+#pragma unroll
+    for (int kk = 2; kk <= kWave * E; kk <<= 1) {
+#pragma unroll
+        for (int j = kk >> 1; j > 0; j >>= 1) {
+            if (j >= kWave) {
+                const int je = j / kWave;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    if (e & je) continue;
+                    const int e2 = e | je;
+                    const bool asc = ((e * kWave + lane) & kk) == 0;
+                    const int a = v[e], b = v[e2];
+                    const bool sw = asc ? (a > b) : (a < b);
+                    v[e] = sw ? b : a;
+                    v[e2] = sw ? a : b;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const int x = e * kWave + lane;
+                    const int p = __shfl_xor(v[e], j, kWave);
+                    const bool lower = (x & j) == 0, asc = (x & kk) == 0;
+                    v[e] = (lower == asc) ? min(v[e], p) : max(v[e], p);
+                }
+            }
         }
     }
-    __syncthreads();
-    const int chunk = (nsb + NT - 1) / NT;
-    const int c0 = min(tid * chunk, nsb), c1 = min(c0 + chunk, nsb);
-    int mine = 0, toks = 0;
-    for (int i = c0; i < c1; ++i) {
-        mine += s_sb[i] >= 0;
-        toks += s_cnt[i];
+    int nkept = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        int prev = __shfl_up(v[e], 1, kWave);
+        if (lane == 0) prev = (e == 0) ? -1 : __builtin_amdgcn_readlane(v[e > 0 ? e - 1 : 0], kWave - 1);
+        const bool keep = v[e] != INT_MAX && v[e] != prev;
+        const uint64_t m = __ballot(keep);
+        if (keep) s_blk[wave][nkept + __popcll(m & lanemask_lt())] = v[e];
+        nkept += __popcll(m);
     }
-    int total = 0, tok_total = 0;
-    int pos = block_excl_scan<NT>(mine, &total, s_scan);
-    block_excl_scan<NT>(toks, &tok_total, s_scan);
-    int32_t *out = s.sparse_indices + (int64_t)r * nsb;
-    for (int i = c0; i < c1; ++i)
-        if (s_sb[i] >= 0) out[pos++] = s_sb[i];
-    for (int i = total + tid; i < nsb; i += NT) out[i] = -1;
-    if (tid == 0) {
-        s.end[r] = tok_total;
-        s.kept[r] = total;
+    __builtin_amdgcn_wave_barrier();
+
+    int32_t *out_si = s.sparse_indices + (int64_t)r * nsb;
+    int32_t *out_pg = s.pages + (int64_t)r * nsb;
+    const int total = nkept * per;
+    int nlist = 0, ntok = 0;
+    for (int base = 0; base < total; base += kWave) {
+        const int i = base + lane;
+        bool ok = false;
+        int32_t sb = 0, page = -1;
+        if (i < total) {
+            const int64_t sb64 = (int64_t)s_blk[wave][i / per] * per + i % per;
+            const int64_t lo = max(sb64 * sbk, ks), hi = min(sb64 * sbk + sbk, ke);
+            const int64_t lp = sb64 * sbk / k.page_size;
+            if (hi > lo && tbl_ok && lp < k.pages_per_table) {
+                page = k.block_table[(int64_t)tbl * k.block_table_stride + lp];
+                ok = page >= 0 && page < k.num_pages;
+                if (ok) ntok += (int)(hi - lo);
+            }
+            sb = (int32_t)sb64;
+        }
+        const uint64_t m = __ballot(ok);
+        if (ok) {
+            const int pos = nlist + __popcll(m & lanemask_lt());
+            out_si[pos] = sb;
+            out_pg[pos] = page;
+        }
+        nlist += __popcll(m);
+    }
+    for (int i = nlist + lane; i < nsb; i += kWave) {
+        out_si[i] = -1;
+        out_pg[i] = -1;
+    }
+    ntok = wave_sum(ntok);
+    if (lane == 0) {
+        s.end[r] = ntok;
+        s.kept[r] = nlist;
     }
 }
 
 // ---------------------------------------------------------------- scoring ------
 
-constexpr int kScoreThreads = 256;
+// Raw K data of one lane for a 16-token tile: 16 bytes of packed e2m1 (dimensions
+// [32g, 32g+32) of token tok0 + lane%16) and the UE8M0 byte scaling them.
+struct KTile {
+    uint4 v;
+    int sc;
+};
 
-// Per-lane query state of one row: the A operands of the four 16-head tiles, their
-// scale operands, and the weights of the heads whose accumulators the lane holds
-// (heads 16*ht + 4*(lane/16) + v).
+// Per-lane query state of one row.  MXFP4: the A operands of the four 16-head tiles
+// and their scale operands.  FP8: the same data converted to bf16, per head tile and
+// k step.  Both: the weights of the heads whose accumulators the lane holds (heads
+// 16*ht + 4*(lane/16) + v), times the row scale for fp8.
 template <int QF>
-struct QFrag {
+struct QFrag;
+
+template <>
+struct QFrag<0> {
     v8i a[4];
     int sc[4];
     float w[4][4];
 };
 
-template <int QF>
-__device__ __forceinline__ void load_q(QFrag<QF> &f, const void *qv, const void *qs,
-                                       const float *weights, int row, int lane) {
+template <>
+struct QFrag<1> {
+    v8bf a[4][4];
+    float w[4][4];
+};
+
+__device__ __forceinline__ v8bf cat4(v2bf a, v2bf b, v2bf c, v2bf d) {
+    return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+__device__ __forceinline__ void load_q(QFrag<0> &f, const void *qv, const void *qs, int row,
+                                       int lane) {
     const int n = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) {
         const int64_t h = (int64_t)row * kHeads + 16 * ht + n;
-        if (QF == 0) {
-            const uint4 x = *(const uint4 *)((const uint8_t *)qv + h * (kHeadDim / 2) + 16 * g);
-            f.a[ht] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-            f.sc[ht] = ((const uint8_t *)qs)[h * (kHeadDim / 32) + g];
-        } else {
-            const uint8_t *p = (const uint8_t *)qv + h * kHeadDim;
-            const uint4 x = *(const uint4 *)(p + 16 * g);
-            const uint4 y = *(const uint4 *)(p + 64 + 16 * g);
-            f.a[ht] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w,
-                          (int)y.x, (int)y.y, (int)y.z, (int)y.w};
-            f.sc[ht] = 127;  // 2^0: the fp8 row scale is folded into the weights
-        }
+        const uint4 x = *(const uint4 *)((const uint8_t *)qv + h * (kHeadDim / 2) + 16 * g);
+        f.a[ht] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+        f.sc[ht] = ((const uint8_t *)qs)[h * (kHeadDim / 32) + g];
     }
+}
+
+__device__ __forceinline__ void load_q(QFrag<1> &f, const void *qv, const void *qs, int row,
+                                       int lane) {
+    const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) {
+        const int64_t h = (int64_t)row * kHeads + 16 * ht + n;
+        const uint8_t *p = (const uint8_t *)qv + h * kHeadDim + 32 * g;
+        const uint4 x = *(const uint4 *)p, y = *(const uint4 *)(p + 16);
+        const uint32_t d[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+            f.a[ht][st] = cat4(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[2 * st], 1.0f, false),
+                               __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[2 * st], 1.0f, true),
+                               __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[2 * st + 1], 1.0f, false),
+                               __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[2 * st + 1], 1.0f, true));
+    }
+}
+
+template <int QF>
+__device__ __forceinline__ void load_q_weights(QFrag<QF> &f, const void *qs, const float *weights,
+                                               int row, int lane) {
+    const int g = lane >> 4;
     const float rs = (QF == 1) ? ((const float *)qs)[row] : 1.0f;
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht)
@@ -196,170 +347,221 @@ __device__ __forceinline__ void load_q(QFrag<QF> &f, const void *qv, const void 
             f.w[ht][v] = weights[(int64_t)row * kHeads + 16 * ht + 4 * g + v] * rs;
 }
 
+template <int QF>
+__device__ __forceinline__ void load_q(QFrag<QF> &f, const void *qv, const void *qs,
+                                       const float *weights, int row, int lane) {
+    load_q(f, qv, qs, row, lane);
+    load_q_weights(f, qs, weights, row, lane);
+}
+
+// ReLU as one integer max on the float's bits: negative values (and -0) have the
+// sign bit set, so they become +0; non-negative values pass unchanged.  (fmaxf would
+// cost a second instruction to quiet NaN inputs.)
+__device__ __forceinline__ float relu(float x) {
+    return __int_as_float(max(__float_as_int(x), 0));
+}
+
+// Weighted ReLU of one head tile's accumulators into the lane's partial sum.
+__device__ __forceinline__ float relu_weighted(const float (&w)[4], v4f acc, float p) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) p = __builtin_fmaf(w[v], relu(acc[v]), p);
+    return p;
+}
+
 // Partial weighted ReLU head sum of the lane's 16 heads for its column of one
 // 16-token tile.  The same code serves the sparse and the dense kernels, so a
 // token's logit does not depend on which path scored it.
-template <int QF>
-__device__ __forceinline__ float tile_partial(const QFrag<QF> &f, const v8i &kb, int ksc) {
+__device__ __forceinline__ float tile_partial(const QFrag<0> &f, const KTile &k) {
+    const v8i kb = v8i{(int)k.v.x, (int)k.v.y, (int)k.v.z, (int)k.v.w, 0, 0, 0, 0};
     float p = 0.0f;
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) {
         v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.a[ht], kb, acc, QF == 0 ? 4 : 0, 4,
-                                                               0, f.sc[ht], 0, ksc);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) p = __builtin_fmaf(f.w[ht][v], fmaxf(acc[v], 0.0f), p);
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.a[ht], kb, acc, 4, 4, 0, f.sc[ht],
+                                                               0, k.sc);
+        p = relu_weighted(f.w[ht], acc, p);
     }
     return p;
 }
 
-// Lanes of group g = lane/16 hold partial sums p[t] (their 16 heads) of column
-// lane%16 of tiles t = 0..3.  Returns, in lane l, the full sum of tile l/16's
-// column l%16, i.e. of column l of the 64-column group.  Every tile's sum is
-// ((p(g0) + p(g0^2)) + (p(g0^1) + p(g0^3))) up to the order of operands of each
-// addition, so the result does not depend on the column's position in the group.
-__device__ __forceinline__ float reduce_transpose4(float p0, float p1, float p2, float p3,
-                                                   int lane) {
-    const int g = lane >> 4;
-    const bool b1 = (g & 2) != 0, b0 = (g & 1) != 0;
-    const float a0 = b1 ? p2 : p0, a1 = b1 ? p3 : p1;
-    const float s0 = b1 ? p0 : p2, s1 = b1 ? p1 : p3;
-    const float q0 = a0 + __shfl_xor(s0, 32, kWave);
-    const float q1 = a1 + __shfl_xor(s1, 32, kWave);
-    const float keep = b0 ? q1 : q0, send = b0 ? q0 : q1;
-    return keep + __shfl_xor(send, 16, kWave);
+__device__ __forceinline__ float tile_partial(const QFrag<1> &f, const KTile &k) {
+    // 2^(sc - 127) as fp32 (sc = 0 is the subnormal 2^-127)
+    const float scale = __uint_as_float(k.sc == 0 ? 0x00400000u : (uint32_t)k.sc << 23);
+    const uint32_t d[4] = {k.v.x, k.v.y, k.v.z, k.v.w};
+    v8bf b[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+        b[st] = cat4(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[st], scale, 0),
+                     __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[st], scale, 1),
+                     __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[st], scale, 2),
+                     __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[st], scale, 3));
+    float p = 0.0f;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) {
+        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[ht][st], b[st], acc, 0, 0, 0);
+        p = relu_weighted(f.w[ht], acc, p);
+    }
+    return p;
 }
 
-// Tile of 16 consecutive tokens starting at tok0 (inside one page): the lane's
-// B operand (16 bytes of token tok0 + lane%16, k-block lane/16) and scale byte.
-__device__ __forceinline__ void load_k_tile(const KCache &k, int32_t page, int32_t j0, int lane,
-                                            v8i &kb, int &ksc) {
+// Lanes of row g = lane/16 hold partial sums p[t] (their 16 heads) of column
+// lane%16 of tiles t = 0..3.  Returns, in lane l, the full sum of tile l/16's column
+// l%16, i.e. of column l of the 64-column group.  v_permlane32_swap(a, b) moves b's
+// lanes 0-31 into a's lanes 32-63 and a's lanes 32-63 into b's lanes 0-31; the sum
+// of the two results therefore pairs rows (0,2) and (1,3); v_permlane16_swap then
+// pairs rows (0,1) and (2,3).  Every tile's column sum comes out as
+// (p(row0) + p(row2)) + (p(row1) + p(row3)) with the same operand order, so the
+// result does not depend on the column's position in the group.
+__device__ __forceinline__ float reduce_transpose4(float p0, float p1, float p2, float p3) {
+    const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p2),
+                                                    false, false);
+    const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(p1), __float_as_uint(p3),
+                                                    false, false);
+    const float q0 = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+    const float q1 = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+    const auto z = __builtin_amdgcn_permlane16_swap(__float_as_uint(q0), __float_as_uint(q1),
+                                                    false, false);
+    return __uint_as_float(z[0]) + __uint_as_float(z[1]);
+}
+
+
+
+// Scores the 64-column groups [g0, g1) of one row, in rounds of RG <= 16 groups.  Lane t
+// first resolves tile t of the round: desc gives its page (-1: nothing to score) and
+// first token, from which the lane forms the tile's value and scale base addresses,
+// so all descriptor loads and address arithmetic of a round cost one memory latency
+// and one pass of vector instructions.  A tile then costs scalar reads of those
+// addresses and two loads at a per-lane offset (token lane%16, scale block lane/16)
+// that never changes.
+//
+// The round runs as RG/U units of U groups, fully unrolled, loading unit u+1 while
+// unit u computes (two U-group buffers, 2*U*4 KB in flight per wave).  Loads are
+// never under a branch: a tile with nothing to score, or beyond the round's groups,
+// reads the pool's first bytes (in bounds, and an L2 hit after the first time) and
+// its result is dropped by a select.  Branch-free loads keep the compiler's
+// memory-counter waits exact (a load under an if makes it wait for everything).
+// sink(c, logit) receives every column of the groups, -inf where the column is not a
+// valid token of [ks, ke).
+template <int QF, int RG, int U, class Desc, class Sink>
+__device__ __forceinline__ void score_groups(const KCache &k, const QFrag<QF> &f, int ks, int ke,
+                                             int g0, int g1, Desc desc, Sink sink) {
+    static_assert(RG <= 16 && RG % U == 0, "units must tile a round of at most 16 groups");
+    constexpr int NU = RG / U;
+    const int lane = threadIdx.x & (kWave - 1);
     const int n = lane & 15, g = lane >> 4;
-    const int64_t slot = (int64_t)j0 + n;
-    const uint4 x = *(const uint4 *)(k.values + (int64_t)page * k.values_page_stride +
-                                     slot * (kHeadDim / 2) + 16 * g);
-    kb = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-    ksc = k.scales[(int64_t)page * k.scales_page_stride + slot * (kHeadDim / 32) + g];
-}
-
-// Sparse scoring.  grid = (rows, column chunks); each wave takes 64-column groups of
-// the row's sparse-column space round robin.  Column c maps to token
-// sparse_indices[c / sbk] * sbk + c % sbk; a 16-column tile never crosses a sparse
-// block (sbk is a multiple of 16) nor a page (page_size is a multiple of sbk).
-template <int QF>
-__global__ __launch_bounds__(kScoreThreads) void score_sparse_kernel(
-    Rows rows, const void *qv, const void *qs, const float *weights, KCache k, Schedule s,
-    float *logits, int groups_per_wg) {
-    const int row = blockIdx.x;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = uniform(threadIdx.x / kWave);
-    const int ncols = s.nsb * s.sbk;
-    const int ngroups = (ncols + 63) / 64;
-    const int gb = blockIdx.y * groups_per_wg;
-    const int ge = min(gb + groups_per_wg, ngroups);
-    const int kept = max(0, min(uniform(s.kept[row]), s.nsb));
-    const int valid_cols = kept * s.sbk;
-    const int ks = rows.ks ? rows.ks[row] : 0;
-    const int ke = rows.ke[row];
-    const int tbl = rows.table ? rows.table[row] : row;
-    const bool tbl_ok = tbl >= 0 && tbl < k.num_tables;
-    const int32_t *si = s.sparse_indices + (int64_t)row * s.nsb;
-    const int32_t *bt = k.block_table + (int64_t)(tbl_ok ? tbl : 0) * k.block_table_stride;
-    float *lrow = logits + (int64_t)row * ncols;
-
-    QFrag<QF> f;
-    if (gb * 64 < valid_cols && tbl_ok) load_q<QF>(f, qv, qs, weights, row, lane);
-
-    for (int grp = gb + wave; grp < ge; grp += kScoreThreads / kWave) {
-        const int c0 = grp * 64;
-        v8i kb[4];
-        int ksc[4];
-        bool tv[4];
-        int tok0[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int tc = c0 + 16 * t;
-            tv[t] = false;
-            tok0[t] = 0;
-            if (tc < valid_cols && tbl_ok) {
-                const int sb = uniform(si[tc / s.sbk]);
-                const int64_t tok = (int64_t)sb * s.sbk + tc % s.sbk;
-                const int64_t lp = tok / k.page_size;
-                const int32_t page =
-                    (sb >= 0 && lp < k.pages_per_table) ? uniform(bt[lp]) : -1;
-                if (page >= 0 && page < k.num_pages) {
-                    tv[t] = true;
-                    tok0[t] = (int)tok;
-                    load_k_tile(k, page, (int)(tok % k.page_size), lane, kb[t], ksc[t]);
-                }
-            }
+    const uint32_t voff = n * (kHeadDim / 2) + 16 * g;
+    const uint32_t soff = n * (kHeadDim / 32) + g;
+    for (int r0 = g0; r0 < g1; r0 += RG) {
+        const int ng = min(RG, g1 - r0);
+        int page = -1, ttok = 0;
+        if (lane < ng * 4) desc(r0 * 4 + lane, page, ttok);
+        const bool ok = page >= 0 && page < k.num_pages && ttok >= 0;
+        uint64_t vb = (uint64_t)k.values, sb = (uint64_t)k.scales;  // safe, never scored
+        if (ok) {
+            const int64_t j0 = ttok % k.page_size;
+            vb += (uint64_t)((int64_t)page * k.values_page_stride + j0 * (kHeadDim / 2));
+            sb += (uint64_t)((int64_t)page * k.scales_page_stride + j0 * (kHeadDim / 32));
         }
-        float p[4];
+        const uint32_t vlo = (uint32_t)vb, vhi = (uint32_t)(vb >> 32);
+        const uint32_t slo = (uint32_t)sb, shi = (uint32_t)(sb >> 32);
+        const uint64_t okmask = __ballot(ok);  // bit t: tile t has something to score
+        KTile kt[2][U][4];
+        auto load_unit = [&](int u, KTile(&b)[U][4]) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) p[t] = tv[t] ? tile_partial<QF>(f, kb[t], ksc[t]) : 0.0f;
-        const float lg = reduce_transpose4(p[0], p[1], p[2], p[3], lane);
-        const int g = lane >> 4;
-        const bool mine = g == 0 ? tv[0] : g == 1 ? tv[1] : g == 2 ? tv[2] : tv[3];
-        const int tk = (g == 0 ? tok0[0] : g == 1 ? tok0[1] : g == 2 ? tok0[2] : tok0[3]) + (lane & 15);
-        const int c = c0 + lane;
-        if (c < ncols) lrow[c] = (mine && tk >= ks && tk < ke) ? lg : -INFINITY;
+            for (int q = 0; q < U; ++q)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int src = (u * U + q) * 4 + t;
+                    const kGlobal uint8_t *vp = (const kGlobal uint8_t *)join64(
+                        __builtin_amdgcn_readlane(vhi, src), __builtin_amdgcn_readlane(vlo, src));
+                    const kGlobal uint8_t *sp = (const kGlobal uint8_t *)join64(
+                        __builtin_amdgcn_readlane(shi, src), __builtin_amdgcn_readlane(slo, src));
+                    const v4u x = *(const kGlobal v4u *)(vp + voff);
+                    b[q][t].v = make_uint4(x[0], x[1], x[2], x[3]);
+                    b[q][t].sc = sp[soff];
+                }
+        };
+        auto finish_unit = [&](int u, const KTile(&b)[U][4]) {
+#pragma unroll
+            for (int q = 0; q < U; ++q) {
+                const int grp = u * U + q;
+                if (grp >= ng) break;
+                float p[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const float v = tile_partial(f, b[q][t]);
+                    p[t] = ((okmask >> (grp * 4 + t)) & 1) ? v : 0.0f;
+                }
+                const float lg = reduce_transpose4(p[0], p[1], p[2], p[3]);
+                const int tok = __shfl(ttok, grp * 4 + g, kWave) + n;
+                const bool valid = ((okmask >> (grp * 4 + g)) & 1) && tok >= ks && tok < ke;
+                sink((r0 + grp) * 64 + lane, valid ? lg : -INFINITY);
+            }
+        };
+        load_unit(0, kt[0]);
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            if (u + 1 < NU) load_unit(u + 1, kt[(u + 1) & 1]);
+            if (u * U < ng) finish_unit(u, kt[u & 1]);
+        }
     }
 }
 
-// Dense scoring (the comparator): column t is token t, every token < max_ctx.
-template <int QF>
-__global__ __launch_bounds__(kScoreThreads) void score_dense_kernel(
-    Rows rows, int32_t max_ctx, const void *qv, const void *qs, const float *weights, KCache k,
-    float *logits, int64_t lstride, int groups_per_wg) {
-    const int row = blockIdx.x;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = uniform(threadIdx.x / kWave);
-    const int ngroups = (max_ctx + 63) / 64;
-    const int gb = blockIdx.y * groups_per_wg;
-    const int ge = min(gb + groups_per_wg, ngroups);
-    const int ks = rows.ks ? rows.ks[row] : 0;
-    const int ke = min(rows.ke[row], max_ctx);
-    const int tbl = rows.table ? rows.table[row] : row;
-    const bool tbl_ok = tbl >= 0 && tbl < k.num_tables;
-    const int32_t *bt = k.block_table + (int64_t)(tbl_ok ? tbl : 0) * k.block_table_stride;
-    float *lrow = logits + (int64_t)row * lstride;
-
-    QFrag<QF> f;
-    if (gb * 64 < ke && (gb + groups_per_wg) * 64 > ks && tbl_ok)
-        load_q<QF>(f, qv, qs, weights, row, lane);
-
-    for (int grp = gb + wave; grp < ge; grp += kScoreThreads / kWave) {
-        const int c0 = grp * 64;
-        v8i kb[4];
-        int ksc[4];
-        bool tv[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int tok = c0 + 16 * t;
-            tv[t] = false;
-            if (tok < ke && tok + 16 > ks && tbl_ok) {
-                const int lp = tok / k.page_size;
-                const int32_t page = lp < k.pages_per_table ? uniform(bt[lp]) : -1;
-                if (page >= 0 && page < k.num_pages) {
-                    tv[t] = true;
-                    load_k_tile(k, page, tok % k.page_size, lane, kb[t], ksc[t]);
-                }
-            }
+// Tile descriptor of a row's sparse column space: tile t covers columns [16t, 16t+16)
+// of sparse block slot 16t / sbk, tokens sparse_indices[slot] * sbk + 16t % sbk + i,
+// on the page the schedule resolved for that slot.
+struct SparseDesc {
+    const int32_t *si, *pg;
+    int valid_cols, sbk;
+    __device__ __forceinline__ void operator()(int tile, int &page, int &tok) const {
+        const int c = tile * 16;
+        if (c < valid_cols) {
+            const int slot = c / sbk;
+            page = pg[slot];
+            tok = si[slot] * sbk + c % sbk;
         }
-        float p[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) p[t] = tv[t] ? tile_partial<QF>(f, kb[t], ksc[t]) : 0.0f;
-        const float lg = reduce_transpose4(p[0], p[1], p[2], p[3], lane);
-        const int g = lane >> 4;
-        const bool mine = g == 0 ? tv[0] : g == 1 ? tv[1] : g == 2 ? tv[2] : tv[3];
-        const int t = c0 + lane;  // < ngroups * 64 <= lstride
-        lrow[t] = (mine && t >= ks && t < ke) ? lg : -INFINITY;
     }
+};
+
+// Tile descriptor of the dense comparator: tile t is tokens [16t, 16t+16).
+struct DenseDesc {
+    const int32_t *bt;
+    int ks, ke, page_size, pages_per_table;
+    __device__ __forceinline__ void operator()(int tile, int &page, int &tok) const {
+        const int t0 = tile * 16;
+        if (t0 < ke && t0 + 16 > ks) {
+            const int lp = t0 / page_size;
+            if (lp < pages_per_table) page = bt[lp];
+            tok = t0;
+        }
+    }
+};
+
+struct RowInfo {
+    int ks, ke, kept, valid_cols, ncols;
+    bool tbl_ok;
+    const int32_t *si, *pg;
+};
+
+__device__ __forceinline__ RowInfo row_info(const Rows &rows, const KCache &k, const Schedule &s,
+                                            int row) {
+    RowInfo ri;
+    ri.ks = rows.ks ? rows.ks[row] : 0;
+    ri.ke = rows.ke[row];
+    const int tbl = rows.table ? rows.table[row] : row;
+    ri.tbl_ok = tbl >= 0 && tbl < k.num_tables;
+    ri.kept = ri.tbl_ok ? max(0, min(uniform(s.kept[row]), s.nsb)) : 0;
+    ri.valid_cols = ri.kept * s.sbk;
+    ri.ncols = s.nsb * s.sbk;
+    ri.si = s.sparse_indices + (int64_t)row * s.nsb;
+    ri.pg = s.pages + (int64_t)row * s.nsb;
+    return ri;
 }
 
 // ---------------------------------------------------------------- top-k --------
-
-constexpr int kTopkThreads = 1024;
 
 // Order-preserving map of an fp32 logit to uint32 (larger float -> larger key);
 // -0 is first made +0 so the two compare equal.  Finite logits map above 0x007FFFFF,
@@ -369,158 +571,306 @@ __device__ __forceinline__ uint32_t ordered_key(float x) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// One workgroup per row.  Thread i owns columns [i*KPT, (i+1)*KPT), so column order
-// (= ascending token order) is thread order then register order.  The count-th
-// largest key is found MSB-first with 8-bit digits; a pass stops early once the
-// chosen digit's bucket is taken whole.  Selected: keys above the prefix, plus the
-// first k_rem keys equal to it in column order (ties toward the lower token).
-template <int KPT, bool DENSE>
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(Rows rows, Schedule s,
-                                                            const float *logits, int64_t lstride,
-                                                            int32_t ncols, int32_t topk,
-                                                            int32_t *out, int64_t ostride) {
-    __shared__ int32_t s_si[DENSE ? 1 : kMaxNSB];
-    __shared__ uint32_t s_bits[DENSE ? kMaxDenseBlocks / 32 : 1];
-    __shared__ int s_hist[256];
-    __shared__ int s_scan[kTopkThreads / kWave + 1];
-    __shared__ int s_w[4];
-    __shared__ int s_sel[3];
-    constexpr int NT = kTopkThreads;
-    const int row = blockIdx.x, tid = threadIdx.x;
-    const int ks = rows.ks ? rows.ks[row] : 0;
-    const int ke = rows.ke[row];
-    const int kept = max(0, min(s.kept[row], s.nsb));
-    const int sbk = s.sbk;
-    const int32_t *si = s.sparse_indices + (int64_t)row * s.nsb;
-    int32_t *orow = out + (int64_t)row * ostride;
+// Top-k of one row by one workgroup of NT threads.  Thread i holds the keys of
+// columns [i*KPT, (i+1)*KPT) (key 0: invalid column); column order is ascending
+// token order.  count = min(topk, valid).  The count-th largest key is searched
+// MSB-first: the bits above the highest bit where the row's smallest and largest
+// keys differ are common to every key, so the first digit (up to 8 bits) starts
+// right below them; the search stops once the chosen digit's bucket is taken whole.
+// Each digit costs two barriers: histogram (ping-pong buffers, the next one cleared
+// while the current one is scanned), then one wave scans the 256 buckets and
+// publishes the choice.  Selected: keys whose prefix is above the chosen prefix,
+// plus the first k_rem keys equal to it in column order (ties toward the lower
+// token).  Writes orow[0, topk): chosen tokens ascending, then -1.
+template <int NT, int KPT, class TokenOf>
+__device__ void select_topk(const uint32_t (&key)[KPT], int32_t topk, int32_t *orow,
+                            TokenOf token_of) {
+    __shared__ int s_hist[2][256];
+    __shared__ int s_scan[NT / kWave + 1];
+    __shared__ uint32_t s_red[3 * (NT / kWave)];
+    __shared__ int s_sel[2][3];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
 
-    if (!DENSE) {
-        for (int i = tid; i < kept; i += NT) s_si[i] = si[i];
-    } else {
-        const int nwords = (ncols / sbk + 31) / 32;
-        for (int i = tid; i < nwords; i += NT) s_bits[i] = 0u;
-        __syncthreads();
-        for (int i = tid; i < kept; i += NT) {
-            const int b = si[i];
-            if (b >= 0 && b < ncols / sbk) atomicOr(&s_bits[b >> 5], 1u << (b & 31));
-        }
-    }
-    __syncthreads();
-
-    auto token_of = [&](int c) -> int {
-        return DENSE ? c : s_si[c / sbk] * sbk + c % sbk;
-    };
-    auto valid_col = [&](int c) -> bool {
-        if (DENSE) {
-            if (c < ks || c >= ke || c >= ncols) return false;
-            const int b = c / sbk;
-            return (s_bits[b >> 5] >> (b & 31)) & 1u;
-        }
-        if (c >= kept * sbk) return false;
-        const int t = token_of(c);
-        return t >= ks && t < ke;
-    };
-
-    uint32_t key[KPT];
-    int nvalid = 0;
-    const int cbase = tid * KPT;
-    const float *lrow = logits + (int64_t)row * lstride;
+    for (int i = tid; i < 256; i += NT) s_hist[0][i] = 0;
+    int nv = 0;
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
-    for (int i = 0; i < KPT; i += 4) {
-        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (cbase + i < ncols) x = *(const float4 *)(lrow + cbase + i);
-        const float xs[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const bool v = valid_col(cbase + i + j);
-            key[i + j] = v ? ordered_key(xs[j]) : 0u;
-            nvalid += v;
+    for (int i = 0; i < KPT; ++i) {
+        if (key[i] != 0u) {
+            ++nv;
+            mn = min(mn, key[i]);
+            mx = max(mx, key[i]);
         }
     }
     int total_valid = 0;
-    block_excl_scan<NT>(nvalid, &total_valid, s_scan);
+    uint32_t kmin = 0, kmax = 0;
+    block_count_min_max<NT>(nv, mn, mx, &total_valid, &kmin, &kmax, s_red);
     const int count = min(topk, total_valid);
-
-    // Radix select of the count-th largest key (skipped when every valid key is taken).
     const bool take_all = count == total_valid;
-    uint32_t prefix = 0;
-    int depth = 0, k_rem = count;
+
+    int shift = 0, k_rem = count;
+    uint64_t prefix = 0;
     if (!take_all) {
-        for (int pass = 0; pass < 4; ++pass) {
-            const int shift = 24 - 8 * pass;
-            if (tid < 256) s_hist[tid] = 0;
-            __syncthreads();
+        const uint32_t diff = kmin ^ kmax;
+        shift = diff ? 32 - __clz((int)diff) : 0;
+        prefix = (uint64_t)kmin >> shift;
+        for (int pass = 0; shift > 0; ++pass) {
+            const int w = min(8, shift), ns = shift - w;
+            int *h = s_hist[pass & 1];
 #pragma unroll
             for (int i = 0; i < KPT; ++i) {
                 const uint32_t kk = key[i];
-                if (kk != 0u && (pass == 0 || (kk >> (shift + 8)) == prefix))
-                    atomicAdd(&s_hist[(kk >> shift) & 255u], 1);
+                if (kk != 0u && ((uint64_t)kk >> shift) == prefix)
+                    atomicAdd(&h[(kk >> ns) & ((1u << w) - 1u)], 1);
             }
             __syncthreads();
-            int c = 0, incl = 0;
-            if (tid < 256) {
-                c = s_hist[255 - tid];
-                incl = wave_incl_scan(c);
-                if ((tid & 63) == 63) s_w[tid >> 6] = incl;
-            }
-            __syncthreads();
-            if (tid < 256) {
-                for (int w = 0; w < (tid >> 6); ++w) incl += s_w[w];
-                const int before = incl - c;
+            if (tid < kWave) {
+                // lane l owns digits 255-4l .. 252-4l, scanned from the top
+                const int d0 = 255 - 4 * lane;
+                const int c0 = h[d0], c1 = h[d0 - 1], c2 = h[d0 - 2], c3 = h[d0 - 3];
+                const int sum = c0 + c1 + c2 + c3;
+                const int incl = wave_incl_scan(sum);
+                int before = incl - sum;
                 if (before < k_rem && incl >= k_rem) {
-                    s_sel[0] = 255 - tid;
-                    s_sel[1] = k_rem - before;
-                    s_sel[2] = c;
+                    int d = d0, c = c0;
+                    if (before + c < k_rem) { before += c; --d; c = c1;
+                        if (before + c < k_rem) { before += c; --d; c = c2;
+                            if (before + c < k_rem) { before += c; --d; c = c3; } } }
+                    s_sel[pass & 1][0] = d;
+                    s_sel[pass & 1][1] = k_rem - before;
+                    s_sel[pass & 1][2] = c;
                 }
+                int *hn = s_hist[(pass + 1) & 1];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) hn[lane + 64 * i] = 0;
             }
             __syncthreads();
-            prefix = (prefix << 8) | (uint32_t)s_sel[0];
-            k_rem = s_sel[1];
-            depth += 8;
-            const bool whole = s_sel[2] == k_rem;
-            __syncthreads();
-            if (whole) break;
+            prefix = (prefix << w) | (uint32_t)s_sel[pass & 1][0];
+            k_rem = s_sel[pass & 1][1];
+            shift = ns;
+            if (s_sel[pass & 1][2] == k_rem) break;
         }
     }
 
-    // Compaction in column order.
+    // Compaction in column order; gt and eq counts share one scan (each < 2^16).
     int ngt = 0, neq = 0;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
         const uint32_t kk = key[i];
         if (kk == 0u) continue;
-        if (take_all) {
-            ++ngt;
-        } else {
-            const uint32_t top = kk >> (32 - depth);
-            ngt += top > prefix;
-            neq += top == prefix;
-        }
+        const uint64_t top = (uint64_t)kk >> shift;
+        ngt += take_all || top > prefix;
+        neq += !take_all && top == prefix;
     }
-    int tot_gt = 0, tot_eq = 0;
-    int gpos = block_excl_scan<NT>(ngt, &tot_gt, s_scan);
-    int epos = block_excl_scan<NT>(neq, &tot_eq, s_scan);
+    int tot = 0;
+    const int excl = block_excl_scan<NT, false>(ngt | (neq << 16), &tot, s_scan);
+    int gpos = excl & 0xFFFF, epos = excl >> 16;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
         const uint32_t kk = key[i];
         if (kk == 0u) continue;
-        const int c = cbase + i;
-        if (take_all) {
-            if (gpos < count) orow[gpos] = token_of(c);
-            ++gpos;
-            continue;
-        }
-        const uint32_t top = kk >> (32 - depth);
-        if (top > prefix) {
+        const uint64_t top = (uint64_t)kk >> shift;
+        if (take_all || top > prefix) {
             const int pos = gpos + min(epos, k_rem);
-            if (pos < count) orow[pos] = token_of(c);
+            if (pos < count) orow[pos] = token_of(tid * KPT + i);
             ++gpos;
         } else if (top == prefix) {
-            if (epos < k_rem && gpos + epos < count) orow[gpos + epos] = token_of(c);
+            if (epos < k_rem && gpos + epos < count) orow[gpos + epos] = token_of(tid * KPT + i);
             ++epos;
         }
     }
     for (int i = count + tid; i < topk; i += NT) orow[i] = -1;
+}
+
+// ---------------------------------------------------------------- kernels ------
+
+constexpr int kScoreThreads = 256;
+constexpr int kTopkThreads = 512;
+constexpr int kDenseTopkThreads = 1024;
+
+// Rows split over workgroups: grid = (rows, chunks of groups_per_wg 64-column groups);
+// each wave scores a contiguous quarter of its workgroup's groups into logits.
+template <int QF, int PW>
+__global__ __launch_bounds__(kScoreThreads) void score_split_kernel(
+    Rows rows, const void *qv, const void *qs, const float *weights, KCache k, Schedule s,
+    float *logits, int groups_per_wg) {
+    const int row = blockIdx.x;
+    const int wave = uniform(threadIdx.x / kWave);
+    const RowInfo ri = row_info(rows, k, s, row);
+    const int ngroups = (ri.ncols + 63) / 64;
+    const int g0 = min(blockIdx.y * groups_per_wg + wave * PW, ngroups);
+    const int g1 = min(g0 + PW, ngroups);
+    float *lrow = logits + (int64_t)row * ri.ncols;
+    QFrag<QF> f;
+    if (g0 * 64 < ri.valid_cols) load_q<QF>(f, qv, qs, weights, row, threadIdx.x & (kWave - 1));
+    score_groups<QF, PW, PW>(k, f, ri.ks, ri.ke, g0, g1, SparseDesc{ri.si, ri.pg, ri.valid_cols, s.sbk},
+                        [&](int c, float v) { if (c < ri.ncols) lrow[c] = v; });
+}
+
+// Token of sparse column c (sbk = 1 << lsbk).
+__device__ __forceinline__ int sparse_token(const int32_t *si_lds, int lsbk, int c) {
+    return (si_lds[c >> lsbk] << lsbk) + (c & ((1 << lsbk) - 1));
+}
+
+// Key of a scored column: the scoring writes -inf where the column is not a valid
+// token, which becomes the invalid key 0.
+__device__ __forceinline__ uint32_t column_key(float x) {
+    return x == -INFINITY ? 0u : ordered_key(x);
+}
+
+// Selection for rows scored by score_split_kernel: keys from the global logits
+// (loaded before anything else so their latency overlaps the schedule load).
+__global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(Rows rows, KCache k, Schedule s,
+                                                                  const float *logits, int32_t topk,
+                                                                  int32_t *out, int64_t ostride) {
+    constexpr int KPT = kMaxRowCols / kTopkThreads;
+    __shared__ int32_t s_si[kMaxNSB];
+    const int row = blockIdx.x, tid = threadIdx.x;
+    const RowInfo ri = row_info(rows, k, s, row);
+    const float *lrow = logits + (int64_t)row * ri.ncols;
+    float x[KPT];
+#pragma unroll
+    for (int i = 0; i < KPT; i += 4) {
+        const int c = tid * KPT + i;
+        float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        if (c < ri.valid_cols) v = *(const float4 *)(lrow + c);
+        x[i] = v.x;
+        x[i + 1] = v.y;
+        x[i + 2] = v.z;
+        x[i + 3] = v.w;
+    }
+    for (int i = tid; i < ri.kept; i += kTopkThreads) s_si[i] = ri.si[i];
+    uint32_t key[KPT];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) key[i] = column_key(x[i]);
+    select_topk<kTopkThreads, KPT>(key, topk, out + (int64_t)row * ostride,
+                                   [&](int c) { return sparse_token(s_si, s.lsbk, c); });
+}
+
+// Rows >= CUs: one workgroup per row; waves share the row's valid 64-column groups,
+// logits stay in LDS, then the same workgroup selects.  logits_out (optional) gets a
+// copy of every column.
+template <int QF, int NT, int KPT>
+__global__ __launch_bounds__(NT) void fused_row_kernel(Rows rows, const void *qv, const void *qs,
+                                                       const float *weights, KCache k, Schedule s,
+                                                       float *logits_out, int32_t topk,
+                                                       int32_t *out, int64_t ostride) {
+    __shared__ float s_logit[kMaxRowCols];
+    __shared__ int32_t s_si[kMaxNSB];
+    constexpr int W = NT / kWave;
+    const int row = blockIdx.x, tid = threadIdx.x;
+    const int wave = uniform(tid / kWave);
+    const RowInfo ri = row_info(rows, k, s, row);
+    for (int i = tid; i < ri.kept; i += NT) s_si[i] = ri.si[i];
+    const int vgroups = (ri.valid_cols + 63) / 64;
+    const int per_wave = (vgroups + W - 1) / W;
+    const int g0 = min(wave * per_wave, vgroups), g1 = min(g0 + per_wave, vgroups);
+    float *lout = logits_out ? logits_out + (int64_t)row * ri.ncols : nullptr;
+    {
+        QFrag<QF> f;
+        if (g0 < g1) load_q<QF>(f, qv, qs, weights, row, tid & (kWave - 1));
+        score_groups<QF, 16, QF == 0 ? 4 : 2>(k, f, ri.ks, ri.ke, g0, g1,
+                                     SparseDesc{ri.si, ri.pg, ri.valid_cols, s.sbk},
+                                     [&](int c, float v) {
+                                         if (c < ri.ncols) {
+                                             s_logit[c] = v;
+                                             if (lout) lout[c] = v;
+                                         }
+                                     });
+    }
+    if (lout)
+        for (int c = vgroups * 64 + tid; c < ri.ncols; c += NT) lout[c] = -INFINITY;
+    __syncthreads();
+    uint32_t key[KPT];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const int c = tid * KPT + i;
+        key[i] = c < ri.valid_cols ? column_key(s_logit[c]) : 0u;
+    }
+    select_topk<NT, KPT>(key, topk, out + (int64_t)row * ostride,
+                         [&](int c) { return sparse_token(s_si, s.lsbk, c); });
+}
+
+// Dense scoring (the comparator): column t is token t, every token < max_ctx.
+template <int QF>
+__global__ __launch_bounds__(kScoreThreads) void score_dense_kernel(
+    Rows rows, int32_t max_ctx, const void *qv, const void *qs, const float *weights, KCache k,
+    float *logits, int64_t lstride, int groups_per_wg) {
+    const int row = blockIdx.x;
+    const int wave = uniform(threadIdx.x / kWave);
+    const int ngroups = (max_ctx + 63) / 64;
+    constexpr int PW = 4;  // groups per wave (groups_per_wg = 16)
+    const int g0 = min(blockIdx.y * groups_per_wg + wave * PW, ngroups);
+    const int g1 = min(g0 + PW, ngroups);
+    const int ks = rows.ks ? rows.ks[row] : 0;
+    const int ke = min(rows.ke[row], max_ctx);
+    const int tbl = rows.table ? rows.table[row] : row;
+    const bool tbl_ok = tbl >= 0 && tbl < k.num_tables;
+    const int32_t *bt = k.block_table + (int64_t)(tbl_ok ? tbl : 0) * k.block_table_stride;
+    float *lrow = logits + (int64_t)row * lstride;
+    QFrag<QF> f;
+    if (g0 * 64 < ke && g1 * 64 > ks && tbl_ok)
+        load_q<QF>(f, qv, qs, weights, row, threadIdx.x & (kWave - 1));
+    score_groups<QF, 4, 2>(k, f, ks, ke, g0, g1,
+                                 DenseDesc{bt, ks, tbl_ok ? ke : 0, k.page_size, k.pages_per_table},
+                                 [&](int t, float v) { lrow[t] = v; });  // t < ngroups*64 <= lstride
+}
+
+// Dense selection: the row's candidate tokens (those whose sparse block is in the
+// schedule) are compacted in token order into LDS with their logits, then selected
+// like the sparse path.
+__global__ __launch_bounds__(kDenseTopkThreads) void dense_topk_kernel(Rows rows, KCache k, Schedule s,
+                                                                  const float *logits,
+                                                                  int64_t lstride, int32_t ncols,
+                                                                  int32_t topk, int32_t *out,
+                                                                  int64_t ostride) {
+    constexpr int CPT = kMaxDenseCols / kDenseTopkThreads;   // columns scanned per thread
+    constexpr int KPT = kMaxRowCols / kDenseTopkThreads;     // compacted keys per thread
+    __shared__ uint32_t s_bits[kMaxDenseBlocks / 32];
+    __shared__ float s_val[kMaxRowCols];
+    __shared__ int32_t s_tok[kMaxRowCols];
+    __shared__ int s_scan[kDenseTopkThreads / kWave + 1];
+    const int row = blockIdx.x, tid = threadIdx.x;
+    const RowInfo ri = row_info(rows, k, s, row);
+    const int sbk = s.sbk;
+    const int nblocks = ncols / sbk;
+    for (int i = tid; i < (nblocks + 31) / 32; i += kDenseTopkThreads) s_bits[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < ri.kept; i += kDenseTopkThreads) {
+        const int b = ri.si[i];
+        if (b >= 0 && b < nblocks) atomicOr(&s_bits[b >> 5], 1u << (b & 31));
+    }
+    __syncthreads();
+    auto member = [&](int t) {
+        if (t < ri.ks || t >= ri.ke || t >= ncols) return false;
+        const int b = t / sbk;
+        return ((s_bits[b >> 5] >> (b & 31)) & 1u) != 0u;
+    };
+    int mine = 0;
+    for (int i = 0; i < CPT; ++i) mine += member(tid * CPT + i);
+    int nvalid = 0;
+    int pos = block_excl_scan<kDenseTopkThreads>(mine, &nvalid, s_scan);
+    const float *lrow = logits + (int64_t)row * lstride;
+    for (int i = 0; i < CPT; ++i) {
+        const int t = tid * CPT + i;
+        if (member(t)) {
+            if (pos < kMaxRowCols) {
+                s_val[pos] = lrow[t];
+                s_tok[pos] = t;
+            }
+            ++pos;
+        }
+    }
+    nvalid = min(nvalid, kMaxRowCols);
+    __syncthreads();
+    uint32_t key[KPT];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const int c = tid * KPT + i;
+        key[i] = c < nvalid ? ordered_key(s_val[c]) : 0u;
+    }
+    select_topk<kDenseTopkThreads, KPT>(key, topk, out + (int64_t)row * ostride,
+                                   [&](int c) { return s_tok[c]; });
 }
 
 }  // namespace
@@ -530,33 +880,82 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(Rows rows, Schedule 
 hipError_t launch_expand(const Rows &rows, const KCache &k, const int32_t *cand, int64_t cand_stride,
                          int32_t nb, int32_t cbs, const Schedule &s, hipStream_t stream) {
     if (rows.num_rows == 0) return hipSuccess;
-    hipLaunchKernelGGL(expand_kernel, dim3(rows.num_rows), dim3(kExpandThreads), 0, stream, rows,
-                       k, cand, cand_stride, nb, cbs, s);
+    const dim3 grid((rows.num_rows + kExpandRows - 1) / kExpandRows);
+#define IDX_LAUNCH_EXPAND(E_)                                                                    \
+    hipLaunchKernelGGL(expand_kernel<E_>, grid, dim3(kExpandThreads), 0, stream, rows, k, cand,  \
+                       cand_stride, nb, cbs, s)
+    if (nb <= 64) IDX_LAUNCH_EXPAND(1);
+    else if (nb <= 128) IDX_LAUNCH_EXPAND(2);
+    else if (nb <= 256) IDX_LAUNCH_EXPAND(4);
+    else IDX_LAUNCH_EXPAND(8);
+#undef IDX_LAUNCH_EXPAND
     return hipGetLastError();
 }
 
-static int sparse_groups_per_wg(int32_t num_rows, int ngroups) {
-    // Enough workgroups to cover 256 CUs several times over, each wave at least
-    // one 64-column group.
-    int gpw = 4;
-    while (gpw < 16 && (int64_t)num_rows * ((ngroups + gpw - 1) / gpw) > 4096) gpw *= 2;
-    return gpw;
+static int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
 }
 
-hipError_t launch_score_sparse(int q_format, const Rows &rows, const void *q_values,
-                               const void *q_scales, const float *weights, const KCache &k,
-                               const Schedule &s, float *logits, hipStream_t stream) {
-    if (rows.num_rows == 0) return hipSuccess;
-    const int ngroups = (s.nsb * s.sbk + 63) / 64;
-    const int gpw = sparse_groups_per_wg(rows.num_rows, ngroups);
-    dim3 grid(rows.num_rows, (ngroups + gpw - 1) / gpw);
-    if (q_format == 0)
-        hipLaunchKernelGGL(score_sparse_kernel<0>, grid, dim3(kScoreThreads), 0, stream, rows,
+template <int QF>
+static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const void *q_scales,
+                                  const float *weights, const KCache &k, const Schedule &s,
+                                  float *logits_out, float *workspace, int32_t topk, int32_t *out,
+                                  int64_t out_stride, hipStream_t stream) {
+    const int ncols = s.nsb * s.sbk;
+    const int ngroups = (ncols + 63) / 64;
+    if (rows.num_rows >= device_cus()) {
+        // 8 waves per row, each with up to 8 (fp4) / 4 (fp8) groups of K in flight
+        constexpr int NT = 512;
+#define IDX_LAUNCH_FUSED(KPT_)                                                                   \
+    hipLaunchKernelGGL((fused_row_kernel<QF, NT, KPT_>), dim3(rows.num_rows), dim3(NT), 0, stream, \
+                       rows, q_values, q_scales, weights, k, s, logits_out, topk, out, out_stride)
+        if (ncols <= NT * 4) IDX_LAUNCH_FUSED(4);
+        else if (ncols <= NT * 8) IDX_LAUNCH_FUSED(8);
+        else IDX_LAUNCH_FUSED(16);
+#undef IDX_LAUNCH_FUSED
+        return hipGetLastError();
+    }
+    float *logits = logits_out ? logits_out : workspace;
+    // Enough workgroups to cover the CUs several times over; 4 waves each with at
+    // least one 64-column group.
+    int gpw = 4;
+    while (gpw < 16 && (int64_t)rows.num_rows * ((ngroups + gpw - 1) / gpw) > 4096) gpw *= 2;
+    const dim3 sgrid(rows.num_rows, (ngroups + gpw - 1) / gpw);
+    if (gpw == 4)
+        hipLaunchKernelGGL((score_split_kernel<QF, 1>), sgrid, dim3(kScoreThreads), 0, stream, rows,
+                           q_values, q_scales, weights, k, s, logits, gpw);
+    else if (gpw == 8)
+        hipLaunchKernelGGL((score_split_kernel<QF, 2>), sgrid, dim3(kScoreThreads), 0, stream, rows,
                            q_values, q_scales, weights, k, s, logits, gpw);
     else
-        hipLaunchKernelGGL(score_sparse_kernel<1>, grid, dim3(kScoreThreads), 0, stream, rows,
+        hipLaunchKernelGGL((score_split_kernel<QF, 4>), sgrid, dim3(kScoreThreads), 0, stream, rows,
                            q_values, q_scales, weights, k, s, logits, gpw);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_split_kernel, dim3(rows.num_rows), dim3(kTopkThreads), 0, stream, rows,
+                       k, s, logits, topk, out, out_stride);
     return hipGetLastError();
+}
+
+hipError_t launch_sparse(int q_format, const Rows &rows, const void *q_values, const void *q_scales,
+                         const float *weights, const KCache &k, const Schedule &s, float *logits_out,
+                         float *workspace, int32_t topk, int32_t *out, int64_t out_stride,
+                         hipStream_t stream) {
+    if (rows.num_rows == 0) return hipSuccess;
+    if (q_format == 0)
+        return launch_sparse_q<0>(rows, q_values, q_scales, weights, k, s, logits_out, workspace,
+                                  topk, out, out_stride, stream);
+    return launch_sparse_q<1>(rows, q_values, q_scales, weights, k, s, logits_out, workspace, topk,
+                              out, out_stride, stream);
 }
 
 hipError_t launch_score_dense(int q_format, const Rows &rows, int32_t max_ctx, const void *q_values,
@@ -565,7 +964,7 @@ hipError_t launch_score_dense(int q_format, const Rows &rows, int32_t max_ctx, c
     if (rows.num_rows == 0) return hipSuccess;
     const int ngroups = (max_ctx + 63) / 64;
     const int gpw = 16;
-    dim3 grid(rows.num_rows, (ngroups + gpw - 1) / gpw);
+    const dim3 grid(rows.num_rows, (ngroups + gpw - 1) / gpw);
     if (q_format == 0)
         hipLaunchKernelGGL(score_dense_kernel<0>, grid, dim3(kScoreThreads), 0, stream, rows,
                            max_ctx, q_values, q_scales, weights, k, logits, logits_stride, gpw);
@@ -575,16 +974,12 @@ hipError_t launch_score_dense(int q_format, const Rows &rows, int32_t max_ctx, c
     return hipGetLastError();
 }
 
-hipError_t launch_topk(bool dense, const Rows &rows, const Schedule &s, const float *logits,
-                       int64_t logits_stride, int32_t ncols, int32_t topk, int32_t *out,
-                       int64_t out_stride, hipStream_t stream) {
+hipError_t launch_dense_topk(const Rows &rows, const KCache &k, const Schedule &s,
+                             const float *logits, int64_t logits_stride, int32_t ncols,
+                             int32_t topk, int32_t *out, int64_t out_stride, hipStream_t stream) {
     if (rows.num_rows == 0) return hipSuccess;
-    if (dense)
-        hipLaunchKernelGGL((topk_kernel<64, true>), dim3(rows.num_rows), dim3(kTopkThreads), 0,
-                           stream, rows, s, logits, logits_stride, ncols, topk, out, out_stride);
-    else
-        hipLaunchKernelGGL((topk_kernel<8, false>), dim3(rows.num_rows), dim3(kTopkThreads), 0,
-                           stream, rows, s, logits, logits_stride, ncols, topk, out, out_stride);
+    hipLaunchKernelGGL(dense_topk_kernel, dim3(rows.num_rows), dim3(kDenseTopkThreads), 0, stream, rows, k,
+                       s, logits, logits_stride, ncols, topk, out, out_stride);
     return hipGetLastError();
 }
 
