@@ -43,16 +43,17 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(case, q_format: str, ends: np.ndarray) -> int:
-    """Bytes one launch must move: 68 B of K per valid column (64 B e2m1 + 4 B
-    UE8M0), and per row its query (4352 B MXFP4 / 8196 B fp8 with its row scale),
-    its 64 fp32 weights, ~12 B per candidate block (candidate id, schedule entry,
-    block-table entry) and the 4-byte top-k output slots."""
+def algorithmic_bytes(case, q_format: str, ends: np.ndarray, with_output: bool = True) -> int:
+    """Bytes the scoring of one layer must move: 68 B of K per valid column (64 B
+    e2m1 + 4 B UE8M0), and per row its query (4352 B MXFP4 / 8196 B fp8 with its
+    row scale), its 64 fp32 weights, ~12 B per candidate block (candidate id,
+    schedule entry, block-table entry) and, when the same kernel selects, the
+    4-byte top-k output slots."""
     s = case.spec
     per_col = s.head_dim // 2 + s.head_dim // 32
     q = s.num_heads * (s.head_dim // 2 + s.head_dim // 32) if q_format == "mxfp4" \
         else s.num_heads * s.head_dim + 4
-    per_row = q + 4 * s.num_heads + 12 * s.nb + 4 * s.topk
+    per_row = q + 4 * s.num_heads + 12 * s.nb + (4 * s.topk if with_output else 0)
     return int(ends.astype(np.int64).sum()) * per_col + case.num_rows * per_row
 
 
@@ -90,7 +91,22 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
+                    help="only run a plain device copy of MB megabytes 5 times (the reference "
+                         "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
+
+    if args.calibrate_copy:
+        import torch
+
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -128,6 +144,12 @@ def main():
     torch.cuda.synchronize()
     ends = sched0.end.cpu().numpy()
     step_bytes = algorithmic_bytes(case, args.q_format, ends) * spec.layers
+    # The library scores a whole row per workgroup (and selects in the same kernel)
+    # when there are at least as many rows as CUs; otherwise a split scoring kernel
+    # streams K and a second kernel selects.
+    fused = R >= torch.cuda.get_device_properties(dev).multi_processor_count
+    kernel_name = "fused_row_kernel" if fused else "score_split_kernel"
+    kernel_bytes = algorithmic_bytes(case, args.q_format, ends, with_output=fused)
     pool_bytes = sum(L.pool.numel() for L in base.layers)
     if args.replicas > 0:
         nrep = args.replicas
@@ -161,6 +183,10 @@ def main():
     n_events = args.steps * spec.layers
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(n_events)]
+    for a, b in ev:            # materialise the HIP events before the timed region
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
 
     def step(i, timed):
         p = plans[i % nrep]
@@ -170,12 +196,12 @@ def main():
         for layer, L in enumerate(d.layers):
             qv, qs = L.q(args.q_format)
             if timed:
-                ev[i * spec.layers + layer][0].record(stream)
+                idx.idx_set_timing_events(*ev[i * spec.layers + layer])
             idx.idx_sparse_mqa_logits_topk(cfg, p["rows"], qv, qs, L.weights, p["kc"][layer],
                                            p["sched"].struct, p["out"], p["out"].stride(0), None,
                                            p["ws"], p["ws"].numel(), stream=sh)
             if timed:
-                ev[i * spec.layers + layer][1].record(stream)
+                idx.idx_set_timing_events()
 
     for i in range(args.warmup):
         step(i, False)
@@ -189,17 +215,30 @@ def main():
     kernel_ms = [a.elapsed_time(b) for a, b in ev]
     avg_kernel_s = float(np.mean(kernel_ms)) / 1e3
     cols_per_step = int(ends.astype(np.int64).sum()) * spec.layers
-    launch_bytes = step_bytes / spec.layers
+    launch_bytes = kernel_bytes
     achieved = launch_bytes / avg_kernel_s / 1e9
 
     traffic = None
-    tfile = os.path.join(ROOT, "profiles", f"traffic_sparse_fused_cfg{args.config}_{args.q_format}.json")
+    tfile = os.path.join(ROOT, "profiles", f"traffic_{kernel_name}_cfg{args.config}_{args.q_format}.json")
     if os.path.exists(tfile):
         with open(tfile) as f:
             t = json.load(f)
         if t.get("kernel_source_hash") == kernel_source_hash():
             traffic = t.get("bytes_per_launch")
 
+    # Prefill chunks share each K tile among many rows (K comes from L2), so the MX-FP4
+    # MFMA rate bounds them; decode rows each stream their own K from HBM.
+    flops = 2 * spec.num_heads * spec.head_dim * cols_per_step / spec.layers
+    if spec.mode == "prefill":
+        roof = {"bound": "mfma", "achieved": flops / avg_kernel_s / 1e12,
+                "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s"}
+        roof["frac"] = roof["achieved"] / MXFP4_PEAK_TFLOPS
+    else:
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+    roof.update({"traffic": traffic, "kernel": kernel_name, "avg_launch_us": avg_kernel_s * 1e6,
+                 "algorithmic_bytes_per_launch": launch_bytes, "hbm_gbs": achieved,
+                 "mxfp4_tflops": flops / avg_kernel_s / 1e12})
     out = {
         "metric": METRIC,
         "value": cols_per_step * args.steps / elapsed,
@@ -219,12 +258,7 @@ def main():
                    "heads": spec.num_heads, "head_dim": spec.head_dim, "page_size": spec.page_size,
                    "valid_cols_per_step": cols_per_step, "q_format": args.q_format,
                    "input_copies": nrep, "seed": args.seed},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "sparse_fused_kernel", "avg_launch_us": avg_kernel_s * 1e6,
-                     "algorithmic_bytes_per_launch": launch_bytes,
-                     "mxfp4_tflops": 2 * spec.num_heads * spec.head_dim * cols_per_step
-                                     / spec.layers / avg_kernel_s / 1e12},
+        "roofline": roof,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(case, args.q_format, args.cpu_seconds)

@@ -132,6 +132,14 @@ size_t idx_workspace_bytes(const idx_config *cfg, int32_t max_rows, int32_t max_
 /* Message of the last failing call on this thread ("" if none).  Host. */
 const char *idx_last_error(void);
 
+/* Optional timing hook for benchmarks.  While set, every idx_sparse_mqa_logits_topk
+ * and idx_dense_masked_logits_topk call made on this thread records start_event on
+ * the call's stream immediately before its scoring launch (the kernel that streams
+ * the K cache) and stop_event immediately after it, so hipEventElapsedTime gives that
+ * kernel's duration.  Both are hipEvent_t handles owned by the caller; pass NULL,
+ * NULL to clear.  Host; returns IDX_EINVAL if exactly one of them is NULL. */
+int idx_set_timing_events(void *start_event, void *stop_event);
+
 /* Step a1: candidate expansion.  For each row, drop negative ids, count repeated
  * ids once, sort ascending, split each candidate block into cbs/sbk sparse blocks,
  * keep those holding a token of [ks, ke), pad with -1; end = number of valid

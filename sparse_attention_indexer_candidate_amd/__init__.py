@@ -27,8 +27,8 @@ IDX_MAX_DENSE_COLS = 65536
 IDX_MAX_TOPK = 8192
 
 EXPORTED = ("idx_check_config", "idx_num_sparse_blocks", "idx_schedule_work_bytes",
-            "idx_workspace_bytes", "idx_last_error", "idx_expand_candidates",
-            "idx_sparse_mqa_logits_topk", "idx_dense_masked_logits_topk")
+            "idx_workspace_bytes", "idx_last_error", "idx_set_timing_events",
+            "idx_expand_candidates", "idx_sparse_mqa_logits_topk", "idx_dense_masked_logits_topk")
 
 
 class IdxError(RuntimeError):
@@ -80,6 +80,8 @@ def _load():
     L.idx_workspace_bytes.restype = sz
     L.idx_last_error.argtypes = []
     L.idx_last_error.restype = ctypes.c_char_p
+    L.idx_set_timing_events.argtypes = [vp, vp]
+    L.idx_set_timing_events.restype = ctypes.c_int
     L.idx_expand_candidates.argtypes = [P(idx_config), P(idx_rows), P(idx_kcache), vp, i64,
                                         P(idx_schedule), vp]
     L.idx_expand_candidates.restype = ctypes.c_int
@@ -108,6 +110,20 @@ def _check(rc: int) -> int:
 
 
 # ------------------------------------------------------------- raw C calls --
+
+def idx_set_timing_events(start_event=None, stop_event=None) -> int:
+    """Record the given HIP events (torch.cuda.Event or raw handles) around the scoring
+    launch of subsequent calls on this thread; no arguments clears the hook."""
+    def handle(e):
+        if e is None:
+            return None
+        if hasattr(e, "cuda_event"):
+            if not e.cuda_event:   # torch creates the HIP event lazily on first record
+                e.record()
+            return e.cuda_event
+        return int(e)
+    return _check(lib.idx_set_timing_events(handle(start_event), handle(stop_event)))
+
 
 def idx_check_config(cfg: idx_config) -> idx_config:
     _check(lib.idx_check_config(ctypes.byref(cfg)))

@@ -13,6 +13,7 @@
 namespace {
 
 thread_local char g_err[512] = "";
+thread_local idx::Timing g_timing = {nullptr, nullptr};
 
 int fail(int code, const char *fmt, ...) {
     va_list ap;
@@ -194,6 +195,13 @@ size_t idx_workspace_bytes(const idx_config *cfg, int32_t max_rows, int32_t max_
 
 const char *idx_last_error(void) { return g_err; }
 
+int idx_set_timing_events(void *start_event, void *stop_event) {
+    if ((start_event == nullptr) != (stop_event == nullptr))
+        return fail(IDX_EINVAL, "timing events must be both set or both NULL");
+    g_timing = idx::Timing{(hipEvent_t)start_event, (hipEvent_t)stop_event};
+    return ok();
+}
+
 int idx_expand_candidates(const idx_config *cfg, const idx_rows *rows, const idx_kcache *k,
                           const int32_t *candidate_blocks, int64_t cand_stride,
                           const idx_schedule *sched, void *stream) {
@@ -245,7 +253,7 @@ int idx_sparse_mqa_logits_topk(const idx_config *cfg, const idx_rows *rows, cons
     hipStream_t st = (hipStream_t)stream;
     if ((rc = hip_status(idx::launch_sparse(cfg->q_format, r, q_values, q_scales, weights, kc, s,
                                             logits_out, (float *)workspace, cfg->topk,
-                                            topk_indices, out_stride, st),
+                                            topk_indices, out_stride, g_timing, st),
                          "sparse launch")))
         return rc;
     return ok();
@@ -289,7 +297,7 @@ int idx_dense_masked_logits_topk(const idx_config *cfg, const idx_rows *rows, in
     const idx::Schedule s = to_schedule(cfg, sbk, sched);
     hipStream_t st = (hipStream_t)stream;
     if ((rc = hip_status(idx::launch_score_dense(cfg->q_format, r, max_ctx, q_values, q_scales,
-                                                 weights, kc, logits, lstride, st),
+                                                 weights, kc, logits, lstride, g_timing, st),
                          "dense score launch")))
         return rc;
     if ((rc = hip_status(idx::launch_dense_topk(r, kc, s, logits, lstride, ncols, cfg->topk,

@@ -56,16 +56,22 @@ hipError_t launch_expand(const Rows &rows, const KCache &k, const int32_t *cand,
 // (logits in LDS; copied to logits_out if given); otherwise a split scoring launch
 // writes logits [rows][nsb*sbk] to logits_out or workspace and a second launch
 // selects.
+// Events recorded around the scoring launch (null: none).
+struct Timing {
+    hipEvent_t start, stop;
+};
+
 hipError_t launch_sparse(int q_format, const Rows &rows, const void *q_values, const void *q_scales,
                          const float *weights, const KCache &k, const Schedule &s, float *logits_out,
                          float *workspace, int32_t topk, int32_t *out, int64_t out_stride,
-                         hipStream_t stream);
+                         const Timing &timing, hipStream_t stream);
 
 // Scores every token t < max_ctx of every row into logits [rows][logits_stride]
 // (-inf outside [ks, ke)).
 hipError_t launch_score_dense(int q_format, const Rows &rows, int32_t max_ctx, const void *q_values,
                               const void *q_scales, const float *weights, const KCache &k,
-                              float *logits, int64_t logits_stride, hipStream_t stream);
+                              float *logits, int64_t logits_stride, const Timing &timing,
+                              hipStream_t stream);
 
 // Per-row top-k over the dense logits (tokens masked to the schedule's blocks).
 hipError_t launch_dense_topk(const Rows &rows, const KCache &k, const Schedule &s,

@@ -905,11 +905,17 @@ static int device_cus() {
     return cus[dev];
 }
 
+static hipError_t record(hipEvent_t e, hipStream_t stream) {
+    return e ? hipEventRecord(e, stream) : hipSuccess;
+}
+
 template <int QF>
 static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const void *q_scales,
                                   const float *weights, const KCache &k, const Schedule &s,
                                   float *logits_out, float *workspace, int32_t topk, int32_t *out,
-                                  int64_t out_stride, hipStream_t stream) {
+                                  int64_t out_stride, const Timing &timing, hipStream_t stream) {
+    hipError_t e = record(timing.start, stream);
+    if (e != hipSuccess) return e;
     const int ncols = s.nsb * s.sbk;
     const int ngroups = (ncols + 63) / 64;
     if (rows.num_rows >= device_cus()) {
@@ -922,7 +928,8 @@ static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const 
         else if (ncols <= NT * 8) IDX_LAUNCH_FUSED(8);
         else IDX_LAUNCH_FUSED(16);
 #undef IDX_LAUNCH_FUSED
-        return hipGetLastError();
+        e = hipGetLastError();
+        return e != hipSuccess ? e : record(timing.stop, stream);
     }
     float *logits = logits_out ? logits_out : workspace;
     // Enough workgroups to cover the CUs several times over; 4 waves each with at
@@ -939,7 +946,8 @@ static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const 
     else
         hipLaunchKernelGGL((score_split_kernel<QF, 4>), sgrid, dim3(kScoreThreads), 0, stream, rows,
                            q_values, q_scales, weights, k, s, logits, gpw);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
+    if (e == hipSuccess) e = record(timing.stop, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(topk_split_kernel, dim3(rows.num_rows), dim3(kTopkThreads), 0, stream, rows,
                        k, s, logits, topk, out, out_stride);
@@ -949,29 +957,33 @@ static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const 
 hipError_t launch_sparse(int q_format, const Rows &rows, const void *q_values, const void *q_scales,
                          const float *weights, const KCache &k, const Schedule &s, float *logits_out,
                          float *workspace, int32_t topk, int32_t *out, int64_t out_stride,
-                         hipStream_t stream) {
+                         const Timing &timing, hipStream_t stream) {
     if (rows.num_rows == 0) return hipSuccess;
     if (q_format == 0)
         return launch_sparse_q<0>(rows, q_values, q_scales, weights, k, s, logits_out, workspace,
-                                  topk, out, out_stride, stream);
+                                  topk, out, out_stride, timing, stream);
     return launch_sparse_q<1>(rows, q_values, q_scales, weights, k, s, logits_out, workspace, topk,
-                              out, out_stride, stream);
+                              out, out_stride, timing, stream);
 }
 
 hipError_t launch_score_dense(int q_format, const Rows &rows, int32_t max_ctx, const void *q_values,
                               const void *q_scales, const float *weights, const KCache &k,
-                              float *logits, int64_t logits_stride, hipStream_t stream) {
+                              float *logits, int64_t logits_stride, const Timing &timing,
+                              hipStream_t stream) {
     if (rows.num_rows == 0) return hipSuccess;
     const int ngroups = (max_ctx + 63) / 64;
     const int gpw = 16;
     const dim3 grid(rows.num_rows, (ngroups + gpw - 1) / gpw);
+    hipError_t e = record(timing.start, stream);
+    if (e != hipSuccess) return e;
     if (q_format == 0)
         hipLaunchKernelGGL(score_dense_kernel<0>, grid, dim3(kScoreThreads), 0, stream, rows,
                            max_ctx, q_values, q_scales, weights, k, logits, logits_stride, gpw);
     else
         hipLaunchKernelGGL(score_dense_kernel<1>, grid, dim3(kScoreThreads), 0, stream, rows,
                            max_ctx, q_values, q_scales, weights, k, logits, logits_stride, gpw);
-    return hipGetLastError();
+    e = hipGetLastError();
+    return e != hipSuccess ? e : record(timing.stop, stream);
 }
 
 hipError_t launch_dense_topk(const Rows &rows, const KCache &k, const Schedule &s,
