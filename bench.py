@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "candidate cols scored/s & rows/s incl. top-k; % of HBM / MXFP4-MFMA roofline"
 HBM_PEAK_GBS = 8000.0
 MXFP4_PEAK_TFLOPS = 10066.0
+TIMING_STRIDE = 4          # steps between two timed scoring launches
 KERNEL_SOURCES = ["sparse_attention_indexer_candidate_amd/csrc/idx_kernels.hip",
                   "sparse_attention_indexer_candidate_amd/csrc/idx_api.hip"]
 
@@ -144,11 +145,19 @@ def main():
     torch.cuda.synchronize()
     ends = sched0.end.cpu().numpy()
     step_bytes = algorithmic_bytes(case, args.q_format, ends) * spec.layers
-    # The library scores a whole row per workgroup (and selects in the same kernel)
-    # when there are at least as many rows as CUs; otherwise a split scoring kernel
-    # streams K and a second kernel selects.
-    fused = R >= torch.cuda.get_device_properties(dev).multi_processor_count
-    kernel_name = "fused_row_kernel" if fused else "score_split_kernel"
+    # The library's choice of scoring kernel: with at least 8 rows per CU (MXFP4
+    # queries, 64-token sparse blocks) 4-row groups share K tiles and select in the same
+    # kernel; with at least one row per CU a workgroup scores and selects one row;
+    # otherwise a split scoring kernel streams K and a second kernel selects.
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    ncols = idx.idx_num_sparse_blocks(cfg) * cfg.sparse_block_kv
+    if args.q_format == "mxfp4" and cfg.sparse_block_kv == 64 and ncols <= 8192 and R >= 8 * cus:
+        kernel_name = "row_group_kernel"
+    elif R >= cus:
+        kernel_name = "fused_row_kernel"
+    else:
+        kernel_name = "score_split_kernel"
+    fused = kernel_name != "score_split_kernel"
     kernel_bytes = algorithmic_bytes(case, args.q_format, ends, with_output=fused)
     pool_bytes = sum(L.pool.numel() for L in base.layers)
     if args.replicas > 0:
@@ -180,7 +189,11 @@ def main():
             ws=torch.empty(ws_bytes, dtype=torch.uint8, device=dev)))
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
-    n_events = args.steps * spec.layers
+    # Events ride on the scoring dispatch itself (hipExtLaunchKernel), which costs the
+    # host about 20 us per launch; timing every TIMING_STRIDE-th step keeps the host
+    # ahead of the GPU on short steps.
+    timed_steps = [i for i in range(args.steps) if i % TIMING_STRIDE == 0]
+    n_events = len(timed_steps) * spec.layers
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(n_events)]
     for a, b in ev:            # materialise the HIP events before the timed region
@@ -191,12 +204,13 @@ def main():
     def step(i, timed):
         p = plans[i % nrep]
         d = p["d"]
+        timed = timed and i % TIMING_STRIDE == 0
         idx.idx_expand_candidates(cfg, p["rows"], p["kc"][0], d.candidate_blocks,
                                   d.candidate_blocks.stride(0), p["sched"].struct, stream=sh)
         for layer, L in enumerate(d.layers):
             qv, qs = L.q(args.q_format)
             if timed:
-                idx.idx_set_timing_events(*ev[i * spec.layers + layer])
+                idx.idx_set_timing_events(*ev[(i // TIMING_STRIDE) * spec.layers + layer])
             idx.idx_sparse_mqa_logits_topk(cfg, p["rows"], qv, qs, L.weights, p["kc"][layer],
                                            p["sched"].struct, p["out"], p["out"].stride(0), None,
                                            p["ws"], p["ws"].numel(), stream=sh)

@@ -133,11 +133,12 @@ size_t idx_workspace_bytes(const idx_config *cfg, int32_t max_rows, int32_t max_
 const char *idx_last_error(void);
 
 /* Optional timing hook for benchmarks.  While set, every idx_sparse_mqa_logits_topk
- * and idx_dense_masked_logits_topk call made on this thread records start_event on
- * the call's stream immediately before its scoring launch (the kernel that streams
- * the K cache) and stop_event immediately after it, so hipEventElapsedTime gives that
- * kernel's duration.  Both are hipEvent_t handles owned by the caller; pass NULL,
- * NULL to clear.  Host; returns IDX_EINVAL if exactly one of them is NULL. */
+ * and idx_dense_masked_logits_topk call made on this thread launches its scoring
+ * kernel (the one that streams the K cache) with start_event and stop_event attached
+ * to the dispatch (hipExtLaunchKernel): they take the kernel's own start and end
+ * timestamps, so hipEventElapsedTime gives its duration without queueing gaps.  Both
+ * are hipEvent_t handles owned by the caller; pass NULL, NULL to clear.  Host;
+ * returns IDX_EINVAL if exactly one of them is NULL. */
 int idx_set_timing_events(void *start_event, void *stop_event);
 
 /* Step a1: candidate expansion.  For each row, drop negative ids, count repeated

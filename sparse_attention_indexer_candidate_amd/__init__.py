@@ -63,6 +63,12 @@ class idx_schedule(ctypes.Structure):
 
 
 def _load():
+    # One HIP runtime per process.  torch ships its own libamdhip64 under the same
+    # soname as ROCm's; once torch is loaded, libidx.so binds to that copy.  Loading
+    # libidx.so first would map ROCm's copy too, and the two runtimes do not share
+    # streams or device state (the second one finds no device).
+    import torch  # noqa: F401
+
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python sparse_attention_indexer_candidate_amd/build.py` "

@@ -13,6 +13,9 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # no packed-fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the ReLU-weight epilogue reads every accumulator, so
+    # AGPR results would cost one extra move per element
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-result",
     "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
 ]

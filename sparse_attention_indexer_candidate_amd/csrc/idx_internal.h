@@ -56,7 +56,8 @@ hipError_t launch_expand(const Rows &rows, const KCache &k, const int32_t *cand,
 // (logits in LDS; copied to logits_out if given); otherwise a split scoring launch
 // writes logits [rows][nsb*sbk] to logits_out or workspace and a second launch
 // selects.
-// Events recorded around the scoring launch (null: none).
+// Events attached to the scoring kernel's dispatch, which timestamps its start and end
+// (null: none).
 struct Timing {
     hipEvent_t start, stop;
 };

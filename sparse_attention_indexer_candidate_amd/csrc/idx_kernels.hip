@@ -8,8 +8,12 @@
 //                       reduce; one wave per 64-column group, K loads batched
 //  select_topk          per-row radix select on fp32 logits, ties toward the lower
 //                       column, ascending output, -1 fill (one workgroup per row)
-//  fused_row_kernel     rows >= CUs: one workgroup scores a whole row into LDS and
-//                       selects from LDS (no global round trip, no cross-workgroup sync)
+//  wave_select          the same selection by one wave (row groups)
+//  row_group_kernel     >= 8 rows per CU with MXFP4 queries (prefill chunks): 4 rows
+//                       per workgroup share K tiles; logits in LDS, a wave selects a row
+//  fused_row_kernel     rows >= CUs otherwise: one workgroup scores a whole row into LDS
+//                       and selects from LDS (no global round trip, no cross-workgroup
+//                       sync)
 //  score_split_kernel + topk_split_kernel
 //                       fewer rows than CUs: rows split over workgroups, logits in
 //                       global scratch, selection in a second launch
@@ -49,6 +53,7 @@
 // through kernel boundaries instead.
 #include "idx_internal.h"
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -89,76 +94,62 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 
 // ---------------------------------------------------------------- reductions ---
 
-__device__ __forceinline__ int wave_incl_scan(int x) {
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        int y = __shfl_up(x, o, kWave);
-        if (lane >= o) x += y;
-    }
+// Lane scans use DPP (data-parallel primitives: an operand read from another lane of
+// the same instruction, no LDS traffic).  Four row_shr steps scan each 16-lane row;
+// row_bcast:15 then adds the last lane of rows 0 and 2 into rows 1 and 3, and
+// row_bcast:31 adds lane 31 (the total of rows 0-1) into rows 2 and 3.  A lane whose
+// source does not exist, or whose row the step leaves out, reads the identity.  Call
+// with every lane of the wave active.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_from(uint32_t identity, uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)x, CTRL, ROWS, 0xF, false);
+}
+
+struct OpAdd {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; }
+};
+struct OpMin {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return min(a, b); }
+};
+struct OpMax {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); }
+};
+
+// Inclusive scan over the wave's lanes in lane order.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_scan(uint32_t x, uint32_t identity, Op op) {
+    x = op(x, dpp_from<0x111, 0xF>(identity, x));   // row_shr:1
+    x = op(x, dpp_from<0x112, 0xF>(identity, x));   // row_shr:2
+    x = op(x, dpp_from<0x114, 0xF>(identity, x));   // row_shr:4
+    x = op(x, dpp_from<0x118, 0xF>(identity, x));   // row_shr:8
+    x = op(x, dpp_from<0x142, 0xA>(identity, x));   // row_bcast:15 into rows 1, 3
+    x = op(x, dpp_from<0x143, 0xC>(identity, x));   // row_bcast:31 into rows 2, 3
     return x;
 }
+
+__device__ __forceinline__ int wave_incl_scan(int x) { return (int)wave_scan((uint32_t)x, 0u, OpAdd{}); }
 
 __device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
-    return x;
+    return __builtin_amdgcn_readlane(wave_incl_scan(x), kWave - 1);
 }
 
-// Exclusive prefix sum over the workgroup (NT threads); *total gets the sum.
-// smem holds NT/64 + 1 ints.  Contains barriers: call from every thread.  With
-// REUSE the call ends with a barrier so smem can be reused right away.
-template <int NT, bool REUSE = true>
-__device__ int block_excl_scan(int x, int *total, int *smem) {
-    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-    int incl = wave_incl_scan(x);
-    if (lane == kWave - 1) smem[wid] = incl;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int acc = 0;
-        for (int w = 0; w < NT / kWave; ++w) {
-            int t = smem[w];
-            smem[w] = acc;
-            acc += t;
-        }
-        smem[NT / kWave] = acc;
-    }
-    __syncthreads();
-    int res = smem[wid] + incl - x;
-    *total = smem[NT / kWave];
-    if (REUSE) __syncthreads();
-    return res;
-}
-
-// Workgroup count / min / max of valid keys.  smem holds 3 * NT/64 words and is
-// not reused afterwards (no trailing barrier).
+// Exclusive prefix sum over the workgroup (NT threads); *total gets the sum.  wsum
+// holds NT/64 ints.  One barrier; wsum must not be written again before the next one.
 template <int NT>
-__device__ void block_count_min_max(int n, uint32_t mn, uint32_t mx, int *count, uint32_t *bmin,
-                                    uint32_t *bmax, uint32_t *smem) {
+__device__ int block_excl_scan(int x, int *total, int *wsum) {
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        n += __shfl_xor(n, o, kWave);
-        mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
-    }
-    constexpr int W = NT / kWave;
-    if (lane == 0) {
-        smem[wid] = (uint32_t)n;
-        smem[W + wid] = mn;
-        smem[2 * W + wid] = mx;
-    }
+    const int incl = wave_incl_scan(x);
+    if (lane == kWave - 1) wsum[wid] = incl;
     __syncthreads();
-    int c = 0;
-    uint32_t a = 0xFFFFFFFFu, b = 0u;
-    for (int w = 0; w < W; ++w) {
-        c += (int)smem[w];
-        a = min(a, smem[W + w]);
-        b = max(b, smem[2 * W + w]);
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < NT / kWave; ++w) {
+        const int t = wsum[w];
+        before += w < wid ? t : 0;
+        all += t;
     }
-    *count = c;
-    *bmin = a;
-    *bmax = b;
+    *total = all;
+    return before + incl - x;
 }
 
 // ---------------------------------------------------------------- expansion ----
@@ -552,8 +543,9 @@ __device__ __forceinline__ RowInfo row_info(const Rows &rows, const KCache &k, c
     ri.ks = rows.ks ? rows.ks[row] : 0;
     ri.ke = rows.ke[row];
     const int tbl = rows.table ? rows.table[row] : row;
+    const int kept = uniform(s.kept[row]);   // not behind the table check: both loads fly
     ri.tbl_ok = tbl >= 0 && tbl < k.num_tables;
-    ri.kept = ri.tbl_ok ? max(0, min(uniform(s.kept[row]), s.nsb)) : 0;
+    ri.kept = ri.tbl_ok ? max(0, min(kept, s.nsb)) : 0;
     ri.valid_cols = ri.kept * s.sbk;
     ri.ncols = s.nsb * s.sbk;
     ri.si = s.sparse_indices + (int64_t)row * s.nsb;
@@ -571,113 +563,158 @@ __device__ __forceinline__ uint32_t ordered_key(float x) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Top-k of one row by one workgroup of NT threads.  Thread i holds the keys of
-// columns [i*KPT, (i+1)*KPT) (key 0: invalid column); column order is ascending
-// token order.  count = min(topk, valid).  The count-th largest key is searched
-// MSB-first: the bits above the highest bit where the row's smallest and largest
-// keys differ are common to every key, so the first digit (up to 8 bits) starts
-// right below them; the search stops once the chosen digit's bucket is taken whole.
-// Each digit costs two barriers: histogram (ping-pong buffers, the next one cleared
-// while the current one is scanned), then one wave scans the 256 buckets and
-// publishes the choice.  Selected: keys whose prefix is above the chosen prefix,
-// plus the first k_rem keys equal to it in column order (ties toward the lower
-// token).  Writes orow[0, topk): chosen tokens ascending, then -1.
-template <int NT, int KPT, class TokenOf>
-__device__ void select_topk(const uint32_t (&key)[KPT], int32_t topk, int32_t *orow,
-                            TokenOf token_of) {
-    __shared__ int s_hist[2][256];
-    __shared__ int s_scan[NT / kWave + 1];
-    __shared__ uint32_t s_red[3 * (NT / kWave)];
-    __shared__ int s_sel[2][3];
-    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+// Workgroup LDS of the row selection: one 256-bucket histogram per radix pass (at
+// most four: each pass narrows the key range by 8 bits or more), the per-wave partial
+// statistics and the per-wave totals of the compaction scan.
+template <int NT>
+struct SelectLds {
+    int hist[4][256];
+    uint32_t part[3][NT / kWave];
+    int wsum[NT / kWave];
+};
 
-    for (int i = tid; i < 256; i += NT) s_hist[0][i] = 0;
-    int nv = 0;
+// Zeroes the histograms.  Call before the barrier of block_key_stats.
+template <int NT>
+__device__ __forceinline__ void select_clear(SelectLds<NT> &L) {
+    for (int i = threadIdx.x; i < 4 * 256; i += NT) L.hist[i >> 8][i & 255] = 0;
+}
+
+// Per-thread partial statistics of keys (key 0: invalid column, not counted).
+struct KeyStats {
+    int n = 0;
     uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-        if (key[i] != 0u) {
-            ++nv;
-            mn = min(mn, key[i]);
-            mx = max(mx, key[i]);
+    __device__ __forceinline__ void add(uint32_t k) {
+        if (k != 0u) {
+            ++n;
+            mn = min(mn, k);
+            mx = max(mx, k);
         }
     }
-    int total_valid = 0;
-    uint32_t kmin = 0, kmax = 0;
-    block_count_min_max<NT>(nv, mn, mx, &total_valid, &kmin, &kmax, s_red);
-    const int count = min(topk, total_valid);
-    const bool take_all = count == total_valid;
+};
 
-    int shift = 0, k_rem = count;
-    uint64_t prefix = 0;
-    if (!take_all) {
-        const uint32_t diff = kmin ^ kmax;
-        shift = diff ? 32 - __clz((int)diff) : 0;
-        prefix = (uint64_t)kmin >> shift;
-        for (int pass = 0; shift > 0; ++pass) {
-            const int w = min(8, shift), ns = shift - w;
-            int *h = s_hist[pass & 1];
+// Combines the partials of the workgroup: count of valid keys, smallest and largest
+// valid key.  Contains one barrier (which also publishes whatever the threads wrote to
+// LDS before the call).
+template <int NT>
+__device__ void block_key_stats(KeyStats p, SelectLds<NT> &L, int &count, uint32_t &kmin,
+                                uint32_t &kmax) {
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    const uint32_t n = wave_scan((uint32_t)p.n, 0u, OpAdd{});
+    const uint32_t mn = wave_scan(p.mn, 0xFFFFFFFFu, OpMin{});
+    const uint32_t mx = wave_scan(p.mx, 0u, OpMax{});
+    if (lane == kWave - 1) {
+        L.part[0][wid] = n;
+        L.part[1][wid] = mn;
+        L.part[2][wid] = mx;
+    }
+    __syncthreads();
+    int c = 0;
+    uint32_t a = 0xFFFFFFFFu, b = 0u;
+#pragma unroll
+    for (int w = 0; w < NT / kWave; ++w) {
+        c += (int)L.part[0][w];
+        a = min(a, L.part[1][w]);
+        b = max(b, L.part[2][w]);
+    }
+    count = c;
+    kmin = a;
+    kmax = b;
+}
+
+// Top-k of one row by one workgroup of NT threads.  Thread i holds the keys of columns
+// [i*KPT, (i+1)*KPT) (key 0: invalid column); column order is ascending token order.
+// count_valid, kmin and kmax come from block_key_stats; count = min(topk, count_valid).
+// The count-th largest key is found by radix passes over key - lo, where [lo, hi] is
+// the key range still holding it (first [kmin, kmax]): a pass histograms the top 8
+// bits of the range's width, and every wave scans the 256 buckets from the top, so all
+// waves take the same bucket with no second barrier.  The search stops once the chosen
+// bucket is taken whole or is a single key value.  Selected: keys above hi, plus the
+// first k_rem keys in [lo, hi] in column order (ties toward the lower token).
+// tokens(c0, tok) fills the tokens of columns c0 .. c0+KPT-1.  Writes orow[0, topk):
+// chosen tokens ascending, then -1.
+template <int NT, int KPT, class Tokens>
+__device__ void select_topk(const uint32_t (&key)[KPT], int count_valid, uint32_t kmin,
+                            uint32_t kmax, int32_t topk, int32_t *orow, SelectLds<NT> &L,
+                            Tokens tokens) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int count = min(topk, count_valid);
+    uint32_t lo = 1u, hi = 0u;   // every valid key taken
+    int k_rem = 0;
+    bool whole = true;           // the chosen keys are exactly those >= lo
+    if (count < count_valid) {
+        lo = kmin;
+        hi = kmax;
+        k_rem = count;
+        for (int pass = 0; pass < 4; ++pass) {
+            const uint32_t span = hi - lo;
+            const int s = max(0, 24 - __clz((int)span));   // (span >> s) < 256
+            int *h = L.hist[pass];
 #pragma unroll
             for (int i = 0; i < KPT; ++i) {
-                const uint32_t kk = key[i];
-                if (kk != 0u && ((uint64_t)kk >> shift) == prefix)
-                    atomicAdd(&h[(kk >> ns) & ((1u << w) - 1u)], 1);
+                const uint32_t d = key[i] - lo;
+                if (d <= span) atomicAdd(&h[d >> s], 1);
             }
             __syncthreads();
-            if (tid < kWave) {
-                // lane l owns digits 255-4l .. 252-4l, scanned from the top
-                const int d0 = 255 - 4 * lane;
-                const int c0 = h[d0], c1 = h[d0 - 1], c2 = h[d0 - 2], c3 = h[d0 - 3];
-                const int sum = c0 + c1 + c2 + c3;
-                const int incl = wave_incl_scan(sum);
-                int before = incl - sum;
-                if (before < k_rem && incl >= k_rem) {
-                    int d = d0, c = c0;
-                    if (before + c < k_rem) { before += c; --d; c = c1;
-                        if (before + c < k_rem) { before += c; --d; c = c2;
-                            if (before + c < k_rem) { before += c; --d; c = c3; } } }
-                    s_sel[pass & 1][0] = d;
-                    s_sel[pass & 1][1] = k_rem - before;
-                    s_sel[pass & 1][2] = c;
-                }
-                int *hn = s_hist[(pass + 1) & 1];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) hn[lane + 64 * i] = 0;
-            }
-            __syncthreads();
-            prefix = (prefix << w) | (uint32_t)s_sel[pass & 1][0];
-            k_rem = s_sel[pass & 1][1];
-            shift = ns;
-            if (s_sel[pass & 1][2] == k_rem) break;
+            // lane l owns buckets 255-4l .. 252-4l; exactly one lane's buckets hold
+            // the k_rem-th largest key of the range
+            const int d0 = 255 - 4 * lane;
+            const int c0 = h[d0], c1 = h[d0 - 1], c2 = h[d0 - 2], c3 = h[d0 - 3];
+            const int sum = c0 + c1 + c2 + c3;
+            const int incl = wave_incl_scan(sum);
+            int before = incl - sum, d = d0, c = c0;
+            if (before + c < k_rem) { before += c; --d; c = c1;
+                if (before + c < k_rem) { before += c; --d; c = c2;
+                    if (before + c < k_rem) { before += c; --d; c = c3; } } }
+            const uint64_t m = __ballot(incl - sum < k_rem && incl >= k_rem);
+            const int src = (int)__builtin_ctzll(m);
+            d = __builtin_amdgcn_readlane(d, src);
+            before = __builtin_amdgcn_readlane(before, src);
+            c = __builtin_amdgcn_readlane(c, src);
+            const uint32_t w = s ? (1u << s) - 1u : 0u;
+            lo += (uint32_t)d << s;
+            hi = (hi - lo <= w) ? hi : lo + w;
+            k_rem -= before;
+            whole = c == k_rem;
+            if (whole || s == 0) break;
         }
     }
 
-    // Compaction in column order; gt and eq counts share one scan (each < 2^16).
+    int tok[KPT];
+    if (whole) {
+        int nsel = 0;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) nsel += key[i] >= lo;
+        int tot = 0;
+        int pos = block_excl_scan<NT>(nsel, &tot, L.wsum);
+        tokens(tid * KPT, tok);
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const bool sel = key[i] >= lo;
+            if (sel && pos < count) orow[pos] = tok[i];
+            pos += sel;
+        }
+        for (int i = count + tid; i < topk; i += NT) orow[i] = -1;
+        return;
+    }
+    // Ties at the threshold: compaction in column order; gt and eq counts share one
+    // scan (each < 2^16).
     int ngt = 0, neq = 0;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-        const uint32_t kk = key[i];
-        if (kk == 0u) continue;
-        const uint64_t top = (uint64_t)kk >> shift;
-        ngt += take_all || top > prefix;
-        neq += !take_all && top == prefix;
+        ngt += key[i] > hi;
+        neq += key[i] >= lo && key[i] <= hi;
     }
     int tot = 0;
-    const int excl = block_excl_scan<NT, false>(ngt | (neq << 16), &tot, s_scan);
+    const int excl = block_excl_scan<NT>(ngt | (neq << 16), &tot, L.wsum);
     int gpos = excl & 0xFFFF, epos = excl >> 16;
+    tokens(tid * KPT, tok);
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-        const uint32_t kk = key[i];
-        if (kk == 0u) continue;
-        const uint64_t top = (uint64_t)kk >> shift;
-        if (take_all || top > prefix) {
-            const int pos = gpos + min(epos, k_rem);
-            if (pos < count) orow[pos] = token_of(tid * KPT + i);
-            ++gpos;
-        } else if (top == prefix) {
-            if (epos < k_rem && gpos + epos < count) orow[gpos + epos] = token_of(tid * KPT + i);
-            ++epos;
-        }
+        const bool gt = key[i] > hi, eq = key[i] >= lo && key[i] <= hi;
+        const int pos = gpos + min(epos, k_rem);
+        if ((gt || (eq && epos < k_rem)) && pos < count) orow[pos] = tok[i];
+        gpos += gt;
+        epos += eq;
     }
     for (int i = count + tid; i < topk; i += NT) orow[i] = -1;
 }
@@ -702,15 +739,23 @@ __global__ __launch_bounds__(kScoreThreads) void score_split_kernel(
     const int g1 = min(g0 + PW, ngroups);
     float *lrow = logits + (int64_t)row * ri.ncols;
     QFrag<QF> f;
-    if (g0 * 64 < ri.valid_cols) load_q<QF>(f, qv, qs, weights, row, threadIdx.x & (kWave - 1));
+    load_q<QF>(f, qv, qs, weights, row, threadIdx.x & (kWave - 1));   // not behind kept
     score_groups<QF, PW, PW>(k, f, ri.ks, ri.ke, g0, g1, SparseDesc{ri.si, ri.pg, ri.valid_cols, s.sbk},
                         [&](int c, float v) { if (c < ri.ncols) lrow[c] = v; });
 }
 
-// Token of sparse column c (sbk = 1 << lsbk).
-__device__ __forceinline__ int sparse_token(const int32_t *si_lds, int lsbk, int c) {
-    return (si_lds[c >> lsbk] << lsbk) + (c & ((1 << lsbk) - 1));
-}
+// Tokens of the KPT sparse columns c0 .. c0+KPT-1 (KPT divides sbk = 1 << lsbk, and c0
+// is a multiple of KPT, so they share one sparse block: token = block * sbk + offset).
+template <int KPT>
+struct SparseTokens {
+    const int32_t *si_lds;
+    int lsbk;
+    __device__ __forceinline__ void operator()(int c0, int (&tok)[KPT]) const {
+        const int base = (si_lds[c0 >> lsbk] << lsbk) + (c0 & ((1 << lsbk) - 1));
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) tok[i] = base + i;
+    }
+};
 
 // Key of a scored column: the scoring writes -inf where the column is not a valid
 // token, which becomes the invalid key 0.
@@ -725,6 +770,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(Rows rows, KCa
                                                                   int32_t *out, int64_t ostride) {
     constexpr int KPT = kMaxRowCols / kTopkThreads;
     __shared__ int32_t s_si[kMaxNSB];
+    __shared__ SelectLds<kTopkThreads> s_sel;
     const int row = blockIdx.x, tid = threadIdx.x;
     const RowInfo ri = row_info(rows, k, s, row);
     const float *lrow = logits + (int64_t)row * ri.ncols;
@@ -740,11 +786,19 @@ __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(Rows rows, KCa
         x[i + 3] = v.w;
     }
     for (int i = tid; i < ri.kept; i += kTopkThreads) s_si[i] = ri.si[i];
+    select_clear(s_sel);
     uint32_t key[KPT];
+    KeyStats st;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) key[i] = column_key(x[i]);
-    select_topk<kTopkThreads, KPT>(key, topk, out + (int64_t)row * ostride,
-                                   [&](int c) { return sparse_token(s_si, s.lsbk, c); });
+    for (int i = 0; i < KPT; ++i) {
+        key[i] = column_key(x[i]);
+        st.add(key[i]);
+    }
+    int nvalid;
+    uint32_t kmin, kmax;
+    block_key_stats<kTopkThreads>(st, s_sel, nvalid, kmin, kmax);
+    select_topk<kTopkThreads, KPT>(key, nvalid, kmin, kmax, topk, out + (int64_t)row * ostride,
+                                   s_sel, SparseTokens<KPT>{s_si, s.lsbk});
 }
 
 // Rows >= CUs: one workgroup per row; waves share the row's valid 64-column groups,
@@ -757,11 +811,14 @@ __global__ __launch_bounds__(NT) void fused_row_kernel(Rows rows, const void *qv
                                                        int32_t *out, int64_t ostride) {
     __shared__ float s_logit[kMaxRowCols];
     __shared__ int32_t s_si[kMaxNSB];
+    __shared__ SelectLds<NT> s_sel;
     constexpr int W = NT / kWave;
     const int row = blockIdx.x, tid = threadIdx.x;
     const int wave = uniform(tid / kWave);
     const RowInfo ri = row_info(rows, k, s, row);
     for (int i = tid; i < ri.kept; i += NT) s_si[i] = ri.si[i];
+    select_clear(s_sel);
+    KeyStats st;
     const int vgroups = (ri.valid_cols + 63) / 64;
     const int per_wave = (vgroups + W - 1) / W;
     const int g0 = min(wave * per_wave, vgroups), g1 = min(g0 + per_wave, vgroups);
@@ -775,20 +832,23 @@ __global__ __launch_bounds__(NT) void fused_row_kernel(Rows rows, const void *qv
                                          if (c < ri.ncols) {
                                              s_logit[c] = v;
                                              if (lout) lout[c] = v;
+                                             st.add(column_key(v));
                                          }
                                      });
     }
     if (lout)
         for (int c = vgroups * 64 + tid; c < ri.ncols; c += NT) lout[c] = -INFINITY;
-    __syncthreads();
+    int nvalid;
+    uint32_t kmin, kmax;
+    block_key_stats<NT>(st, s_sel, nvalid, kmin, kmax);   // also publishes s_logit, s_si
     uint32_t key[KPT];
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
         const int c = tid * KPT + i;
         key[i] = c < ri.valid_cols ? column_key(s_logit[c]) : 0u;
     }
-    select_topk<NT, KPT>(key, topk, out + (int64_t)row * ostride,
-                         [&](int c) { return sparse_token(s_si, s.lsbk, c); });
+    select_topk<NT, KPT>(key, nvalid, kmin, kmax, topk, out + (int64_t)row * ostride, s_sel,
+                         SparseTokens<KPT>{s_si, s.lsbk});
 }
 
 // Dense scoring (the comparator): column t is token t, every token < max_ctx.
@@ -829,12 +889,14 @@ __global__ __launch_bounds__(kDenseTopkThreads) void dense_topk_kernel(Rows rows
     __shared__ uint32_t s_bits[kMaxDenseBlocks / 32];
     __shared__ float s_val[kMaxRowCols];
     __shared__ int32_t s_tok[kMaxRowCols];
-    __shared__ int s_scan[kDenseTopkThreads / kWave + 1];
+    __shared__ int s_scan[kDenseTopkThreads / kWave];
+    __shared__ SelectLds<kDenseTopkThreads> s_sel;
     const int row = blockIdx.x, tid = threadIdx.x;
     const RowInfo ri = row_info(rows, k, s, row);
     const int sbk = s.sbk;
     const int nblocks = ncols / sbk;
     for (int i = tid; i < (nblocks + 31) / 32; i += kDenseTopkThreads) s_bits[i] = 0u;
+    select_clear(s_sel);
     __syncthreads();
     for (int i = tid; i < ri.kept; i += kDenseTopkThreads) {
         const int b = ri.si[i];
@@ -864,13 +926,382 @@ __global__ __launch_bounds__(kDenseTopkThreads) void dense_topk_kernel(Rows rows
     nvalid = min(nvalid, kMaxRowCols);
     __syncthreads();
     uint32_t key[KPT];
+    KeyStats st;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
         const int c = tid * KPT + i;
         key[i] = c < nvalid ? ordered_key(s_val[c]) : 0u;
+        st.add(key[i]);
     }
-    select_topk<kDenseTopkThreads, KPT>(key, topk, out + (int64_t)row * ostride,
-                                   [&](int c) { return s_tok[c]; });
+    int count;
+    uint32_t kmin, kmax;
+    block_key_stats<kDenseTopkThreads>(st, s_sel, count, kmin, kmax);
+    select_topk<kDenseTopkThreads, KPT>(key, count, kmin, kmax, topk, out + (int64_t)row * ostride,
+                                        s_sel, [&](int c0, int (&tok)[KPT]) {
+#pragma unroll
+                                            for (int i = 0; i < KPT; ++i) tok[i] = s_tok[c0 + i];
+                                        });
+}
+
+// ---------------------------------------------------------------- row groups ---
+//
+// Many rows on one table (a prefill chunk): a workgroup of kGroupRows waves takes
+// kGroupRows consecutive rows.  When they share a table row, a block id means the same
+// K tokens for all of them, so the workgroup first merges the rows' schedule lists into
+// one list of distinct sparse blocks, each with its page and its slot in every row.
+// Every wave then scores all the rows for the union entries it owns (entries w, w+4,
+// ...): one K tile load feeds kGroupRows x 4 MFMAs instead of 4.  Logits stay in LDS;
+// after one barrier wave r selects row r's top-k on its own (no further barriers).
+// Rows on different table rows are merged one row at a time (no sharing).
+
+constexpr int kGroupRows = 4;
+constexpr int kGroupThreads = kGroupRows * kWave;
+
+template <int NCMAX>
+struct GroupLds {
+    static constexpr int NSB = NCMAX / 64;       // sparse blocks per row (sbk = 64)
+    float logit[kGroupRows][NCMAX];
+    int32_t si[kGroupRows][NSB];
+    int32_t pg[kGroupRows][NSB];
+    int4 uent[kGroupRows * NSB];                 // block, page, slot byte per row, 0
+    uint32_t part[3][kGroupRows][kGroupRows];    // per wave, per row: n, min, max
+    int hist[kGroupRows][256];
+    int wsum[kGroupThreads / kWave];
+};
+
+// Number of entries of the ascending list a[0, n) below x (n <= N, a power of two).
+template <int N>
+__device__ __forceinline__ int lower_bound_lds(const int32_t *a, int n, int32_t x) {
+    int pos = 0;
+#pragma unroll
+    for (int step = N; step > 0; step >>= 1)
+        if (pos + step <= n && a[pos + step - 1] < x) pos += step;
+    return pos;
+}
+
+// a[i] for a runtime i without spilling the register array to scratch memory.
+template <int N>
+__device__ __forceinline__ int pick(const int (&a)[N], int i) {
+    int v = a[0];
+#pragma unroll
+    for (int q = 1; q < N; ++q) v = (i == q) ? a[q] : v;
+    return v;
+}
+
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// One radix pass over the keys that for_each_key(f) hands to f (each key once per
+// lane, from every lane of the wave): histograms the top 8 bits of key - lo over the
+// range [lo, hi] into the wave's 256 buckets and narrows [lo, hi] and k_rem to the
+// bucket holding the k_rem-th largest key.  Returns kSearchOn while the search goes on,
+// kTakeWhole when the bucket is taken whole, kTies when it is one key value of which
+// only the first k_rem (in column order) are taken.  Call with every lane active.
+constexpr int kSearchOn = 0, kTakeWhole = 1, kTies = 2;
+
+template <class ForEach>
+__device__ __forceinline__ int wave_radix_pass(int *hist, uint32_t &lo, uint32_t &hi, int &k_rem,
+                                                ForEach for_each_key) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t span = hi - lo;
+    const int s = max(0, 24 - __clz((int)span));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hist[lane + kWave * i] = 0;
+    const uint32_t base = lo;
+    for_each_key([&](uint32_t kk) {
+        const uint32_t d = kk - base;
+        if (d <= span) atomicAdd(&hist[d >> s], 1);
+    });
+    const int d0 = 255 - 4 * lane;
+    const int c0 = hist[d0], c1 = hist[d0 - 1], c2 = hist[d0 - 2], c3 = hist[d0 - 3];
+    const int sum = c0 + c1 + c2 + c3;
+    const int incl = wave_incl_scan(sum);
+    int before = incl - sum, d = d0, c = c0;
+    if (before + c < k_rem) { before += c; --d; c = c1;
+        if (before + c < k_rem) { before += c; --d; c = c2;
+            if (before + c < k_rem) { before += c; --d; c = c3; } } }
+    const uint64_t m = __ballot(incl - sum < k_rem && incl >= k_rem);
+    const int src = (int)__builtin_ctzll(m);
+    d = __builtin_amdgcn_readlane(d, src);
+    before = __builtin_amdgcn_readlane(before, src);
+    c = __builtin_amdgcn_readlane(c, src);
+    const uint32_t w = s ? (1u << s) - 1u : 0u;
+    lo += (uint32_t)d << s;
+    hi = (hi - lo <= w) ? hi : lo + w;
+    k_rem -= before;
+    return c == k_rem ? kTakeWhole : (s == 0 ? kTies : kSearchOn);
+}
+
+// Top-k of one row by one wave, with the same selection rule as select_topk.  Lane l
+// holds the keys of columns l, l+64, ... in registers (KPL of them, read from the
+// row's LDS logits), so one compaction step covers 64 consecutive columns and its
+// selected tokens go to consecutive output slots.  The first radix pass runs over all
+// keys; the keys left in its bucket are then copied, in column order, over the row's
+// logits (no longer needed) and the remaining passes run on that short list.
+// hist: the wave's own 256 buckets.
+template <int KPL, class TokenOf>
+__device__ __forceinline__ void wave_select(float *lg, int valid_cols, int count_valid, uint32_t kmin,
+                            uint32_t kmax, int32_t topk, int32_t *orow, int *hist,
+                            TokenOf token_of) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int steps = (valid_cols + kWave - 1) / kWave;
+    uint32_t key[KPL];
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+        key[i] = 0u;
+        const int c = i * kWave + lane;
+        if (i < steps && c < valid_cols) key[i] = column_key(lg[c]);
+    }
+    const int count = min(topk, count_valid);
+    uint32_t lo = 1u, hi = 0u;   // every valid key taken
+    int k_rem = 0, state = kTakeWhole;
+    if (count < count_valid) {
+        lo = kmin;
+        hi = kmax;
+        k_rem = count;
+        state = wave_radix_pass(hist, lo, hi, k_rem, [&](auto f) {
+#pragma unroll
+            for (int i = 0; i < KPL; ++i)
+                if (i < steps) f(key[i]);
+        });
+        if (state == kSearchOn) {
+            uint32_t *cand = reinterpret_cast<uint32_t *>(lg);
+            int n = 0;
+#pragma unroll
+            for (int i = 0; i < KPL; ++i) {
+                if (i < steps) {
+                    const bool in = key[i] >= lo && key[i] <= hi;
+                    const uint64_t m = __ballot(in);
+                    if (in) cand[n + lanes_below(m)] = key[i];
+                    n += __popcll(m);
+                }
+            }
+            for (int pass = 1; pass < 4 && state == kSearchOn; ++pass)
+                state = wave_radix_pass(hist, lo, hi, k_rem, [&](auto f) {
+                    for (int j = lane; j < n; j += kWave) f(cand[j]);
+                });
+        }
+    }
+    // Compaction.  Without ties to break the chosen keys are exactly those >= lo.
+    int base = 0, epos = 0;
+    if (state == kTakeWhole) {
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) {
+            if (i < steps) {
+                const bool sel = key[i] >= lo;
+                const uint64_t ms = __ballot(sel);
+                const int pos = base + lanes_below(ms);
+                if (sel && pos < count) orow[pos] = token_of(i, lane);
+                base += __popcll(ms);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) {
+            if (i < steps) {
+                const uint32_t kk = key[i];
+                const bool gt = kk > hi, eq = kk >= lo && kk <= hi;
+                const uint64_t me = __ballot(eq);
+                const bool sel = gt || (eq && epos + lanes_below(me) < k_rem);
+                const uint64_t ms = __ballot(sel);
+                const int pos = base + lanes_below(ms);
+                if (sel && pos < count) orow[pos] = token_of(i, lane);
+                base += __popcll(ms);
+                epos += __popcll(me);
+            }
+        }
+    }
+    for (int i = count + lane; i < topk; i += kWave) orow[i] = -1;
+}
+
+template <int NCMAX>
+__global__ __launch_bounds__(kGroupThreads) void row_group_kernel(
+    Rows rows, const void *qv, const void *qs, const float *weights, KCache k, Schedule s,
+    float *logits_out, int32_t topk, int32_t *out, int64_t ostride) {
+    using L = GroupLds<NCMAX>;
+    constexpr int NSB = L::NSB;
+    __shared__ L lds;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wave = uniform(tid / kWave);
+    // Last group first: in a causal chunk later rows hold more columns, so the longest
+    // workgroups start first and the short ones fill the tail.
+    const int row0 = (gridDim.x - 1 - blockIdx.x) * kGroupRows;
+    const int ncols = s.nsb * 64;
+
+    // Query state first: its loads overlap the schedule merge below.
+    QFrag<0> f[kGroupRows];
+#pragma unroll
+    for (int r = 0; r < kGroupRows; ++r)
+        if (row0 + r < rows.num_rows) load_q<0>(f[r], qv, qs, weights, row0 + r, lane);
+
+    // Row metadata (uniform: every thread reads the same words).
+    int ks[kGroupRows], ke[kGroupRows], kept[kGroupRows], tbl[kGroupRows];
+#pragma unroll
+    for (int r = 0; r < kGroupRows; ++r) {
+        const int row = row0 + r;
+        if (row < rows.num_rows) {
+            const RowInfo ri = row_info(rows, k, s, row);
+            ks[r] = ri.ks;
+            ke[r] = ri.ke;
+            kept[r] = min(ri.kept, NSB);
+            tbl[r] = rows.table ? rows.table[row] : row;
+        } else {
+            ks[r] = ke[r] = kept[r] = 0;
+            tbl[r] = -1 - r;
+        }
+    }
+    bool share = true;
+#pragma unroll
+    for (int r = 1; r < kGroupRows; ++r) share = share && (kept[r] == 0 || tbl[r] == tbl[0]);
+
+    for (int i = tid; i < kGroupRows * NSB; i += kGroupThreads) {
+        const int r = i / NSB, j = i % NSB;
+        int32_t b = INT_MAX, p = -1;
+        if (j < pick(kept, r)) {
+            b = s.sparse_indices[(int64_t)(row0 + r) * s.nsb + j];
+            p = s.pages[(int64_t)(row0 + r) * s.nsb + j];
+        }
+        lds.si[r][j] = b;
+        lds.pg[r][j] = p;
+    }
+    __syncthreads();
+
+    // Union entries: entry (r, j) represents block b unless an earlier row of the
+    // shared group lists it too; slots of b in the other rows come from binary search.
+    constexpr int EPT = (kGroupRows * NSB + kGroupThreads - 1) / kGroupThreads;
+    int4 ent[EPT];
+    bool rep[EPT];
+    int nrep = 0;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        const int i = tid + e * kGroupThreads;
+        const int r = i / NSB, j = i % NSB;
+        rep[e] = false;
+        if (i < kGroupRows * NSB && j < pick(kept, r)) {
+            const int32_t b = lds.si[r][j];
+            uint32_t slots = 0xFFFFFFFFu;
+            bool first = true;
+#pragma unroll
+            for (int q = 0; q < kGroupRows; ++q) {
+                int slot = -1;
+                if (q == r) {
+                    slot = j;
+                } else if (share) {
+                    const int pos = lower_bound_lds<NSB>(lds.si[q], kept[q], b);
+                    if (pos < kept[q] && lds.si[q][pos] == b) slot = pos;
+                }
+                if (slot >= 0) {
+                    slots &= ~(0xFFu << (8 * q));
+                    slots |= (uint32_t)slot << (8 * q);
+                    if (q < r) first = false;
+                }
+            }
+            rep[e] = first;
+            ent[e] = make_int4(b, lds.pg[r][j], (int)slots, 0);
+        }
+        nrep += rep[e];
+    }
+    int ucount = 0;
+    int upos = block_excl_scan<kGroupThreads>(nrep, &ucount, lds.wsum);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+        if (rep[e]) lds.uent[upos++] = ent[e];
+    __syncthreads();
+
+    // Scoring: wave w takes entries w, w + kGroupRows, ...; the next entry's K tiles
+    // load while the current one computes.
+    KeyStats st[kGroupRows];
+    const int n = lane & 15, g = lane >> 4;
+    const uint32_t voff = n * (kHeadDim / 2) + 16 * g;
+    const uint32_t soff = n * (kHeadDim / 32) + g;
+    auto load_entry = [&](int u, KTile (&kt)[4], int4 &e) {
+        e = make_int4(0, -1, -1, 0);
+        if (u < ucount) e = lds.uent[u];
+        e.x = uniform(e.x);
+        e.y = uniform(e.y);
+        e.z = uniform(e.z);
+        const bool ok = e.y >= 0 && e.y < k.num_pages;
+        const int64_t j0 = ok ? ((int64_t)e.x * 64) % k.page_size : 0;
+        const kGlobal uint8_t *vb = (const kGlobal uint8_t *)k.values +
+                                    (ok ? (int64_t)e.y * k.values_page_stride + j0 * 64 : 0);
+        const kGlobal uint8_t *sb = (const kGlobal uint8_t *)k.scales +
+                                    (ok ? (int64_t)e.y * k.scales_page_stride + j0 * 4 : 0);
+        if (!ok) e.z = -1;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const v4u x = *(const kGlobal v4u *)(vb + t * 1024 + voff);
+            kt[t].v = make_uint4(x[0], x[1], x[2], x[3]);
+            kt[t].sc = sb[t * 64 + soff];
+        }
+    };
+    auto score_entry = [&](const KTile (&kt)[4], int4 e) {
+        const uint32_t slots = (uint32_t)e.z;   // 0xFF bytes (or e.z = -1): row absent
+        const int tok = e.x * 64 + lane;
+#pragma unroll
+        for (int r = 0; r < kGroupRows; ++r) {
+            const uint32_t slot = (slots >> (8 * r)) & 0xFFu;
+            if (slot == 0xFFu) continue;
+            const float lg = reduce_transpose4(tile_partial(f[r], kt[0]), tile_partial(f[r], kt[1]),
+                                               tile_partial(f[r], kt[2]), tile_partial(f[r], kt[3]));
+            // Keep two MFMAs ahead of the ReLU-weight epilogue (8 VALU ops per MFMA):
+            // the epilogue of MFMA i runs while MFMA i+1 and i+2 execute.
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+#pragma unroll
+            for (int i = 0; i < 14; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+            const float v = (tok >= ks[r] && tok < ke[r]) ? lg : -INFINITY;
+            const int c = (int)slot * 64 + lane;
+            lds.logit[r][c] = v;
+            if (logits_out) logits_out[(int64_t)(row0 + r) * ncols + c] = v;
+            st[r].add(column_key(v));
+        }
+    };
+    KTile ka[4], kb[4];
+    int4 ea, eb;
+    load_entry(wave, ka, ea);
+    for (int u = wave; u < ucount; u += 2 * kGroupRows) {
+        load_entry(u + kGroupRows, kb, eb);
+        score_entry(ka, ea);
+        load_entry(u + 2 * kGroupRows, ka, ea);
+        score_entry(kb, eb);   // past the last entry eb names no row
+    }
+    if (logits_out)
+        for (int r = 0; r < kGroupRows; ++r)
+            if (row0 + r < rows.num_rows)
+                for (int c = kept[r] * 64 + tid; c < ncols; c += kGroupThreads)
+                    logits_out[(int64_t)(row0 + r) * ncols + c] = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < kGroupRows; ++r) {
+        const uint32_t cn = wave_scan((uint32_t)st[r].n, 0u, OpAdd{});
+        const uint32_t mn = wave_scan(st[r].mn, 0xFFFFFFFFu, OpMin{});
+        const uint32_t mx = wave_scan(st[r].mx, 0u, OpMax{});
+        if (lane == kWave - 1) {
+            lds.part[0][wave][r] = cn;
+            lds.part[1][wave][r] = mn;
+            lds.part[2][wave][r] = mx;
+        }
+    }
+    __syncthreads();
+
+    // Selection: wave r takes row r.
+    const int r = wave, row = row0 + r;
+    if (row >= rows.num_rows) return;
+    int cnt = 0;
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+    for (int w = 0; w < kGroupRows; ++w) {
+        cnt += (int)lds.part[0][w][r];
+        kmin = min(kmin, lds.part[1][w][r]);
+        kmax = max(kmax, lds.part[2][w][r]);
+    }
+    const int32_t *si = lds.si[r];
+    wave_select<NCMAX / kWave>(lds.logit[r], pick(kept, r) * 64, cnt, kmin, kmax, topk,
+                               out + (int64_t)row * ostride, lds.hist[r],
+                               [&](int i, int l) { return si[i] * 64 + l; });
 }
 
 }  // namespace
@@ -905,31 +1336,42 @@ static int device_cus() {
     return cus[dev];
 }
 
-static hipError_t record(hipEvent_t e, hipStream_t stream) {
-    return e ? hipEventRecord(e, stream) : hipSuccess;
-}
 
 template <int QF>
 static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const void *q_scales,
                                   const float *weights, const KCache &k, const Schedule &s,
                                   float *logits_out, float *workspace, int32_t topk, int32_t *out,
                                   int64_t out_stride, const Timing &timing, hipStream_t stream) {
-    hipError_t e = record(timing.start, stream);
-    if (e != hipSuccess) return e;
+    hipError_t e;
     const int ncols = s.nsb * s.sbk;
     const int ngroups = (ncols + 63) / 64;
+    if constexpr (QF == 0) {
+        // Enough rows for two 4-row workgroups per CU: row groups (K tiles shared
+        // across the rows of a table).
+        if (s.sbk == 64 && ncols <= 8192 && rows.num_rows >= 2 * kGroupRows * device_cus()) {
+            const dim3 grid((rows.num_rows + kGroupRows - 1) / kGroupRows);
+#define IDX_LAUNCH_GROUP(NC_)                                                                     \
+    hipExtLaunchKernelGGL(row_group_kernel<NC_>, grid, dim3(kGroupThreads), 0, stream, timing.start, \
+                          timing.stop, 0, rows, q_values, q_scales, weights, k, s, logits_out, topk, \
+                          out, out_stride)
+            if (ncols <= 4096) IDX_LAUNCH_GROUP(4096);
+            else IDX_LAUNCH_GROUP(8192);
+#undef IDX_LAUNCH_GROUP
+            return hipGetLastError();
+        }
+    }
     if (rows.num_rows >= device_cus()) {
         // 8 waves per row, each with up to 8 (fp4) / 4 (fp8) groups of K in flight
         constexpr int NT = 512;
 #define IDX_LAUNCH_FUSED(KPT_)                                                                   \
-    hipLaunchKernelGGL((fused_row_kernel<QF, NT, KPT_>), dim3(rows.num_rows), dim3(NT), 0, stream, \
-                       rows, q_values, q_scales, weights, k, s, logits_out, topk, out, out_stride)
+    hipExtLaunchKernelGGL((fused_row_kernel<QF, NT, KPT_>), dim3(rows.num_rows), dim3(NT), 0,   \
+                          stream, timing.start, timing.stop, 0, rows, q_values, q_scales, weights, \
+                          k, s, logits_out, topk, out, out_stride)
         if (ncols <= NT * 4) IDX_LAUNCH_FUSED(4);
         else if (ncols <= NT * 8) IDX_LAUNCH_FUSED(8);
         else IDX_LAUNCH_FUSED(16);
 #undef IDX_LAUNCH_FUSED
-        e = hipGetLastError();
-        return e != hipSuccess ? e : record(timing.stop, stream);
+        return hipGetLastError();
     }
     float *logits = logits_out ? logits_out : workspace;
     // Enough workgroups to cover the CUs several times over; 4 waves each with at
@@ -938,16 +1380,18 @@ static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const 
     while (gpw < 16 && (int64_t)rows.num_rows * ((ngroups + gpw - 1) / gpw) > 4096) gpw *= 2;
     const dim3 sgrid(rows.num_rows, (ngroups + gpw - 1) / gpw);
     if (gpw == 4)
-        hipLaunchKernelGGL((score_split_kernel<QF, 1>), sgrid, dim3(kScoreThreads), 0, stream, rows,
-                           q_values, q_scales, weights, k, s, logits, gpw);
+        hipExtLaunchKernelGGL((score_split_kernel<QF, 1>), sgrid, dim3(kScoreThreads), 0, stream,
+                              timing.start, timing.stop, 0, rows, q_values, q_scales, weights, k, s,
+                              logits, gpw);
     else if (gpw == 8)
-        hipLaunchKernelGGL((score_split_kernel<QF, 2>), sgrid, dim3(kScoreThreads), 0, stream, rows,
-                           q_values, q_scales, weights, k, s, logits, gpw);
+        hipExtLaunchKernelGGL((score_split_kernel<QF, 2>), sgrid, dim3(kScoreThreads), 0, stream,
+                              timing.start, timing.stop, 0, rows, q_values, q_scales, weights, k, s,
+                              logits, gpw);
     else
-        hipLaunchKernelGGL((score_split_kernel<QF, 4>), sgrid, dim3(kScoreThreads), 0, stream, rows,
-                           q_values, q_scales, weights, k, s, logits, gpw);
+        hipExtLaunchKernelGGL((score_split_kernel<QF, 4>), sgrid, dim3(kScoreThreads), 0, stream,
+                              timing.start, timing.stop, 0, rows, q_values, q_scales, weights, k, s,
+                              logits, gpw);
     e = hipGetLastError();
-    if (e == hipSuccess) e = record(timing.stop, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(topk_split_kernel, dim3(rows.num_rows), dim3(kTopkThreads), 0, stream, rows,
                        k, s, logits, topk, out, out_stride);
@@ -974,16 +1418,15 @@ hipError_t launch_score_dense(int q_format, const Rows &rows, int32_t max_ctx, c
     const int ngroups = (max_ctx + 63) / 64;
     const int gpw = 16;
     const dim3 grid(rows.num_rows, (ngroups + gpw - 1) / gpw);
-    hipError_t e = record(timing.start, stream);
-    if (e != hipSuccess) return e;
     if (q_format == 0)
-        hipLaunchKernelGGL(score_dense_kernel<0>, grid, dim3(kScoreThreads), 0, stream, rows,
-                           max_ctx, q_values, q_scales, weights, k, logits, logits_stride, gpw);
+        hipExtLaunchKernelGGL(score_dense_kernel<0>, grid, dim3(kScoreThreads), 0, stream,
+                              timing.start, timing.stop, 0, rows, max_ctx, q_values, q_scales,
+                              weights, k, logits, logits_stride, gpw);
     else
-        hipLaunchKernelGGL(score_dense_kernel<1>, grid, dim3(kScoreThreads), 0, stream, rows,
-                           max_ctx, q_values, q_scales, weights, k, logits, logits_stride, gpw);
-    e = hipGetLastError();
-    return e != hipSuccess ? e : record(timing.stop, stream);
+        hipExtLaunchKernelGGL(score_dense_kernel<1>, grid, dim3(kScoreThreads), 0, stream,
+                              timing.start, timing.stop, 0, rows, max_ctx, q_values, q_scales,
+                              weights, k, logits, logits_stride, gpw);
+    return hipGetLastError();
 }
 
 hipError_t launch_dense_topk(const Rows &rows, const KCache &k, const Schedule &s,

@@ -176,3 +176,17 @@ def test_dense_call_rejects_bad_arguments():
     assert call() == idx.IDX_EWORKSPACE
     assert call(logits=FAKE, lstride=1000) == idx.IDX_EINVAL
     assert call(ws=FAKE, wsb=16) == idx.IDX_EWORKSPACE
+
+
+def test_one_hip_runtime_per_process():
+    """Importing the binding before torch must not map a second HIP runtime (ROCm's
+    libamdhip64 beside torch's): kernels launched through the second one see no device."""
+    import subprocess
+    import sys
+    code = ("import sparse_attention_indexer_candidate_amd, torch\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "print(len({l.split()[-1] for l in maps if 'libamdhip64' in l}))\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                         timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip().splitlines()[-1] == "1", out.stdout

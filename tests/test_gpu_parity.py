@@ -67,6 +67,16 @@ SMALL = {
     "cbs128_split_sbk32": W.Spec(name="s6", num_rows=11, page_size=128, cbs=128, nb=9, topk=200,
                                  ke_rule="uniform", ke_lo=300, ke_hi=2000, ks_rule="random",
                                  cand_rule="messy", fill="all"),
+    # >= 8 rows per CU: the row-group kernel (4 rows per workgroup); rows on one table
+    # share K tiles, a ragged last group, messy candidates and ks > 0
+    "rowgroup_shared_table_messy": W.Spec(name="s7", num_rows=2051, page_size=128, cbs=64, nb=8,
+                                          topk=100, mode="prefill", ke_rule="uniform", ke_lo=1,
+                                          ke_hi=1500, ks_rule="random", context=1600,
+                                          cand_rule="messy", fill="all"),
+    # ... and rows on their own table rows (no sharing), k above the valid count
+    "rowgroup_own_tables": W.Spec(name="s8", num_rows=2048, page_size=64, cbs=64, nb=6, topk=300,
+                                  ke_rule="uniform", ke_lo=10, ke_hi=3000,
+                                  cand_rule="distinct", fill="all"),
 }
 
 
