@@ -127,6 +127,32 @@ __device__ __forceinline__ uint32_t wave_scan(uint32_t x, uint32_t identity, Op 
     return x;
 }
 
+// x from lane (lane ^ j), j a power of two below 64 (a constant after unrolling), from
+// registers only: quad permutes for 1 and 2, a half-row mirror then a quad reverse for
+// 4, a row rotate by 8 for 8, and the 16- / 32-lane swaps for 16 and 32.
+__device__ __forceinline__ int lane_xor(int x, int j) {
+    const int lane = threadIdx.x & (kWave - 1);
+    switch (j) {
+    case 1: return __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+    case 2: return __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+    case 4: {
+        const int y = __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+        return __builtin_amdgcn_update_dpp(0, y, 0x1B, 0xF, 0xF, false);        // quad_perm 3,2,1,0
+    }
+    case 8: return __builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false);  // row_ror:8
+    case 16: {
+        // rows (0,1,2,3) of the results: first = (x0, x0, x2, x2), second = (x1, x1, x3, x3)
+        const auto r = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+        return (int)((lane & 16) ? r[0] : r[1]);
+    }
+    default: {
+        // halves of the results: first = (lo, lo), second = (hi, hi)
+        const auto r = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+        return (int)((lane & 32) ? r[0] : r[1]);
+    }
+    }
+}
+
 __device__ __forceinline__ int wave_incl_scan(int x) { return (int)wave_scan((uint32_t)x, 0u, OpAdd{}); }
 
 __device__ __forceinline__ int wave_sum(int x) {
@@ -206,7 +232,7 @@ __global__ __launch_bounds__(kExpandThreads) void expand_kernel(Rows rows, KCach
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     const int x = e * kWave + lane;
-                    const int p = __shfl_xor(v[e], j, kWave);
+                    const int p = lane_xor(v[e], j);
                     const bool lower = (x & j) == 0, asc = (x & kk) == 0;
                     v[e] = (lower == asc) ? min(v[e], p) : max(v[e], p);
                 }
@@ -216,7 +242,7 @@ __global__ __launch_bounds__(kExpandThreads) void expand_kernel(Rows rows, KCach
     int nkept = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        int prev = __shfl_up(v[e], 1, kWave);
+        int prev = __builtin_amdgcn_update_dpp(0, v[e], 0x138, 0xF, 0xF, false);   // wave_shr:1
         if (lane == 0) prev = (e == 0) ? -1 : __builtin_amdgcn_readlane(v[e > 0 ? e - 1 : 0], kWave - 1);
         const bool keep = v[e] != INT_MAX && v[e] != prev;
         const uint64_t m = __ballot(keep);
@@ -501,18 +527,95 @@ __device__ __forceinline__ void score_groups(const KCache &k, const QFrag<QF> &f
     }
 }
 
+// Scores units of U 64-column groups that grab() hands out (unit u covers groups
+// [uU, uU+U); grab returns -1 once the row is done), so the waves of a workgroup share
+// a row dynamically and finish together.  Two units are in flight per wave: the next
+// unit's K loads are issued before the current one computes.  Tile descriptors come
+// from desc (read from LDS by the caller); loads are branch-free as in score_groups (a
+// tile with nothing to score, or a unit past the end, reads the pool's first bytes and
+// its result is dropped).  sink(c, logit) receives every column of the units scored.
+template <int QF, int U, class Desc, class Grab, class Sink>
+__device__ __forceinline__ void score_units(const KCache &k, const QFrag<QF> &f, int ks, int ke,
+                                            Desc desc, Grab grab, Sink sink) {
+    static_assert(4 * U <= kWave, "one lane per tile of a unit");
+    const int lane = threadIdx.x & (kWave - 1);
+    const int n = lane & 15, g = lane >> 4;
+    const uint32_t voff = n * (kHeadDim / 2) + 16 * g;
+    const uint32_t soff = n * (kHeadDim / 32) + g;
+    auto issue = [&](int u, KTile (&b)[U][4], int &ttok, uint64_t &okmask) {
+        int page = -1, tt = 0;
+        if (u >= 0 && lane < 4 * U) desc(u * 4 * U + lane, page, tt);
+        const bool ok = page >= 0 && page < k.num_pages && tt >= 0;
+        uint64_t vb = (uint64_t)k.values, sb = (uint64_t)k.scales;
+        if (ok) {
+            const int64_t j0 = tt % k.page_size;
+            vb += (uint64_t)((int64_t)page * k.values_page_stride + j0 * (kHeadDim / 2));
+            sb += (uint64_t)((int64_t)page * k.scales_page_stride + j0 * (kHeadDim / 32));
+        }
+        const uint32_t vlo = (uint32_t)vb, vhi = (uint32_t)(vb >> 32);
+        const uint32_t slo = (uint32_t)sb, shi = (uint32_t)(sb >> 32);
+        okmask = __ballot(ok);
+        ttok = tt;
+#pragma unroll
+        for (int q = 0; q < U; ++q)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int src = q * 4 + t;
+                const kGlobal uint8_t *vp = (const kGlobal uint8_t *)join64(
+                    __builtin_amdgcn_readlane(vhi, src), __builtin_amdgcn_readlane(vlo, src));
+                const kGlobal uint8_t *sp = (const kGlobal uint8_t *)join64(
+                    __builtin_amdgcn_readlane(shi, src), __builtin_amdgcn_readlane(slo, src));
+                const v4u x = *(const kGlobal v4u *)(vp + voff);
+                b[q][t].v = make_uint4(x[0], x[1], x[2], x[3]);
+                b[q][t].sc = sp[soff];
+            }
+    };
+    auto finish = [&](int u, const KTile (&b)[U][4], int ttok, uint64_t okmask) {
+#pragma unroll
+        for (int q = 0; q < U; ++q) {
+            float p[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const float v = tile_partial(f, b[q][t]);
+                p[t] = ((okmask >> (q * 4 + t)) & 1) ? v : 0.0f;
+            }
+            const float lg = reduce_transpose4(p[0], p[1], p[2], p[3]);
+            const int tok = __shfl(ttok, q * 4 + g, kWave) + n;
+            const bool valid = ((okmask >> (q * 4 + g)) & 1) && tok >= ks && tok < ke;
+            sink((u * U + q) * 64 + lane, valid ? lg : -INFINITY);
+        }
+    };
+    KTile ka[U][4], kb[U][4];
+    int ta = 0, tb = 0;
+    uint64_t ma = 0, mb = 0;
+    int ua = grab();
+    issue(ua, ka, ta, ma);
+    int ub = grab();
+    issue(ub, kb, tb, mb);
+    while (true) {
+        if (ua < 0) break;
+        finish(ua, ka, ta, ma);
+        ua = grab();
+        issue(ua, ka, ta, ma);
+        if (ub < 0) break;
+        finish(ub, kb, tb, mb);
+        ub = grab();
+        issue(ub, kb, tb, mb);
+    }
+}
+
 // Tile descriptor of a row's sparse column space: tile t covers columns [16t, 16t+16)
 // of sparse block slot 16t / sbk, tokens sparse_indices[slot] * sbk + 16t % sbk + i,
-// on the page the schedule resolved for that slot.
+// on the page the schedule resolved for that slot.  Slots past the row's kept count
+// hold page -1 (the expansion pads them), so the loads need not wait for that count.
 struct SparseDesc {
     const int32_t *si, *pg;
-    int valid_cols, sbk;
+    int nsb, sbk;
     __device__ __forceinline__ void operator()(int tile, int &page, int &tok) const {
-        const int c = tile * 16;
-        if (c < valid_cols) {
-            const int slot = c / sbk;
+        const int slot = tile * 16 / sbk;
+        if (slot < nsb) {
             page = pg[slot];
-            tok = si[slot] * sbk + c % sbk;
+            tok = si[slot] * sbk + tile * 16 % sbk;
         }
     }
 };
@@ -740,7 +843,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_split_kernel(
     float *lrow = logits + (int64_t)row * ri.ncols;
     QFrag<QF> f;
     load_q<QF>(f, qv, qs, weights, row, threadIdx.x & (kWave - 1));   // not behind kept
-    score_groups<QF, PW, PW>(k, f, ri.ks, ri.ke, g0, g1, SparseDesc{ri.si, ri.pg, ri.valid_cols, s.sbk},
+    score_groups<QF, PW, PW>(k, f, ri.ks, ri.ke, g0, g1, SparseDesc{ri.si, ri.pg, s.nsb, s.sbk},
                         [&](int c, float v) { if (c < ri.ncols) lrow[c] = v; });
 }
 
@@ -779,7 +882,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(Rows rows, KCa
     for (int i = 0; i < KPT; i += 4) {
         const int c = tid * KPT + i;
         float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-        if (c < ri.valid_cols) v = *(const float4 *)(lrow + c);
+        if (c < ri.ncols) v = *(const float4 *)(lrow + c);   // every column is written
         x[i] = v.x;
         x[i + 1] = v.y;
         x[i + 2] = v.z;
@@ -801,9 +904,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(Rows rows, KCa
                                    s_sel, SparseTokens<KPT>{s_si, s.lsbk});
 }
 
-// Rows >= CUs: one workgroup per row; waves share the row's valid 64-column groups,
-// logits stay in LDS, then the same workgroup selects.  logits_out (optional) gets a
-// copy of every column.
+// Rows >= CUs: one workgroup per row; waves take units of the row's valid 64-column
+// groups from a shared counter, logits stay in LDS, then the same workgroup selects.
+// logits_out (optional) gets a copy of every column.
 template <int QF, int NT, int KPT>
 __global__ __launch_bounds__(NT) void fused_row_kernel(Rows rows, const void *qv, const void *qs,
                                                        const float *weights, KCache k, Schedule s,
@@ -811,31 +914,49 @@ __global__ __launch_bounds__(NT) void fused_row_kernel(Rows rows, const void *qv
                                                        int32_t *out, int64_t ostride) {
     __shared__ float s_logit[kMaxRowCols];
     __shared__ int32_t s_si[kMaxNSB];
+    __shared__ int32_t s_pg[kMaxNSB];
+    __shared__ int s_unit;
     __shared__ SelectLds<NT> s_sel;
-    constexpr int W = NT / kWave;
-    const int row = blockIdx.x, tid = threadIdx.x;
-    const int wave = uniform(tid / kWave);
+    const int row = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1);
     const RowInfo ri = row_info(rows, k, s, row);
-    for (int i = tid; i < ri.kept; i += NT) s_si[i] = ri.si[i];
-    select_clear(s_sel);
-    KeyStats st;
-    const int vgroups = (ri.valid_cols + 63) / 64;
-    const int per_wave = (vgroups + W - 1) / W;
-    const int g0 = min(wave * per_wave, vgroups), g1 = min(g0 + per_wave, vgroups);
-    float *lout = logits_out ? logits_out + (int64_t)row * ri.ncols : nullptr;
-    {
-        QFrag<QF> f;
-        if (g0 < g1) load_q<QF>(f, qv, qs, weights, row, tid & (kWave - 1));
-        score_groups<QF, 16, QF == 0 ? 4 : 2>(k, f, ri.ks, ri.ke, g0, g1,
-                                     SparseDesc{ri.si, ri.pg, ri.valid_cols, s.sbk},
-                                     [&](int c, float v) {
-                                         if (c < ri.ncols) {
-                                             s_logit[c] = v;
-                                             if (lout) lout[c] = v;
-                                             st.add(column_key(v));
-                                         }
-                                     });
+    QFrag<QF> f;
+    load_q<QF>(f, qv, qs, weights, row, lane);   // overlaps the schedule copy
+    for (int i = tid; i < ri.kept; i += NT) {
+        s_si[i] = ri.si[i];
+        s_pg[i] = ri.pg[i];
     }
+    if (tid == 0) s_unit = 0;
+    select_clear(s_sel);
+    __syncthreads();
+    KeyStats st;
+    constexpr int U = QF == 0 ? 4 : 2;
+    const int vgroups = (ri.valid_cols + 63) / 64;
+    const int nunits = (vgroups + U - 1) / U;
+    const int valid_cols = ri.valid_cols, sbk = s.sbk;
+    float *lout = logits_out ? logits_out + (int64_t)row * ri.ncols : nullptr;
+    score_units<QF, U>(
+        k, f, ri.ks, ri.ke,
+        [&](int tile, int &page, int &tok) {
+            const int c = tile * 16;
+            if (c < valid_cols) {
+                const int slot = c / sbk;
+                page = s_pg[slot];
+                tok = s_si[slot] * sbk + c % sbk;
+            }
+        },
+        [&]() {
+            int u = 0;
+            if (lane == 0) u = atomicAdd(&s_unit, 1);
+            u = uniform(u);
+            return u < nunits ? u : -1;
+        },
+        [&](int c, float v) {
+            if (c < ri.ncols) {
+                s_logit[c] = v;
+                if (lout) lout[c] = v;
+                st.add(column_key(v));
+            }
+        });
     if (lout)
         for (int c = vgroups * 64 + tid; c < ri.ncols; c += NT) lout[c] = -INFINITY;
     int nvalid;
