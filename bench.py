@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "candidate cols scored/s & rows/s incl. top-k; % of HBM / MXFP4-MFMA roofline"
 HBM_PEAK_GBS = 8000.0
 MXFP4_PEAK_TFLOPS = 10066.0
-TIMING_STRIDE = 4          # steps between two timed scoring launches
+TIMING_STRIDE = 16         # steps between two timed scoring launches
 KERNEL_SOURCES = ["sparse_attention_indexer_candidate_amd/csrc/idx_kernels.hip",
                   "sparse_attention_indexer_candidate_amd/csrc/idx_api.hip"]
 

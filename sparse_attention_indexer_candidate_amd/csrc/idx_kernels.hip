@@ -87,6 +87,12 @@ __device__ __forceinline__ uint64_t join64(int hi, int lo) {
     return ((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo;
 }
 
+// Slot of token t (>= 0) within its page: a mask when the page size is a power of two
+// (the usual case; the test is uniform), a division otherwise.
+__device__ __forceinline__ int page_slot(int t, int page_size) {
+    return (page_size & (page_size - 1)) == 0 ? (t & (page_size - 1)) : t % page_size;
+}
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
     const int lane = threadIdx.x & (kWave - 1);
     return lane == 0 ? 0ull : (~0ull >> (64 - lane));
@@ -388,7 +394,9 @@ __device__ __forceinline__ float relu_weighted(const float (&w)[4], v4f acc, flo
 // Partial weighted ReLU head sum of the lane's 16 heads for its column of one
 // 16-token tile.  The same code serves the sparse and the dense kernels, so a
 // token's logit does not depend on which path scored it.
-__device__ __forceinline__ float tile_partial(const QFrag<0> &f, const KTile &k) {
+// (weights passed apart from the query operands: the row-group kernel keeps them in LDS)
+__device__ __forceinline__ float tile_partial(const QFrag<0> &f, const float (&w)[4][4],
+                                              const KTile &k) {
     const v8i kb = v8i{(int)k.v.x, (int)k.v.y, (int)k.v.z, (int)k.v.w, 0, 0, 0, 0};
     float p = 0.0f;
 #pragma unroll
@@ -396,9 +404,13 @@ __device__ __forceinline__ float tile_partial(const QFrag<0> &f, const KTile &k)
         v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
         acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.a[ht], kb, acc, 4, 4, 0, f.sc[ht],
                                                                0, k.sc);
-        p = relu_weighted(f.w[ht], acc, p);
+        p = relu_weighted(w[ht], acc, p);
     }
     return p;
+}
+
+__device__ __forceinline__ float tile_partial(const QFrag<0> &f, const KTile &k) {
+    return tile_partial(f, f.w, k);
 }
 
 __device__ __forceinline__ float tile_partial(const QFrag<1> &f, const KTile &k) {
@@ -478,7 +490,7 @@ __device__ __forceinline__ void score_groups(const KCache &k, const QFrag<QF> &f
         const bool ok = page >= 0 && page < k.num_pages && ttok >= 0;
         uint64_t vb = (uint64_t)k.values, sb = (uint64_t)k.scales;  // safe, never scored
         if (ok) {
-            const int64_t j0 = ttok % k.page_size;
+            const int64_t j0 = page_slot(ttok, k.page_size);
             vb += (uint64_t)((int64_t)page * k.values_page_stride + j0 * (kHeadDim / 2));
             sb += (uint64_t)((int64_t)page * k.scales_page_stride + j0 * (kHeadDim / 32));
         }
@@ -548,7 +560,7 @@ __device__ __forceinline__ void score_units(const KCache &k, const QFrag<QF> &f,
         const bool ok = page >= 0 && page < k.num_pages && tt >= 0;
         uint64_t vb = (uint64_t)k.values, sb = (uint64_t)k.scales;
         if (ok) {
-            const int64_t j0 = tt % k.page_size;
+            const int64_t j0 = page_slot(tt, k.page_size);
             vb += (uint64_t)((int64_t)page * k.values_page_stride + j0 * (kHeadDim / 2));
             sb += (uint64_t)((int64_t)page * k.scales_page_stride + j0 * (kHeadDim / 32));
         }
@@ -1066,28 +1078,30 @@ __global__ __launch_bounds__(kDenseTopkThreads) void dense_topk_kernel(Rows rows
 
 // ---------------------------------------------------------------- row groups ---
 //
-// Many rows on one table (a prefill chunk): a workgroup of kGroupRows waves takes
-// kGroupRows consecutive rows.  When they share a table row, a block id means the same
-// K tokens for all of them, so the workgroup first merges the rows' schedule lists into
-// one list of distinct sparse blocks, each with its page and its slot in every row.
-// Every wave then scores all the rows for the union entries it owns (entries w, w+4,
-// ...): one K tile load feeds kGroupRows x 4 MFMAs instead of 4.  Logits stay in LDS;
-// after one barrier wave r selects row r's top-k on its own (no further barriers).
-// Rows on different table rows are merged one row at a time (no sharing).
+// Many rows on one table (a prefill chunk): a workgroup of kGroupWaves waves takes GR
+// consecutive rows.  When they share a table row, a block id means the same K tokens
+// for all of them, so the workgroup first merges the rows' schedule lists into one list
+// of distinct sparse blocks, each with its page and its slot in every row.  Every wave
+// then scores all GR rows for the union entries it owns (entries w, w+4, ...): one K
+// tile load feeds GR x 4 MFMAs instead of 4.  Logits stay in LDS; after one barrier
+// wave r selects row r's top-k on its own (no further barriers).  Rows on different
+// table rows are merged one row at a time (no sharing).  GR = 2 keeps the query state
+// at 72 VGPRs and the LDS near 36 KB, so three workgroups share a CU.
 
-constexpr int kGroupRows = 4;
-constexpr int kGroupThreads = kGroupRows * kWave;
+constexpr int kGroupWaves = 4;
+constexpr int kGroupThreads = kGroupWaves * kWave;
 
-template <int NCMAX>
+template <int NCMAX, int GR>
 struct GroupLds {
     static constexpr int NSB = NCMAX / 64;       // sparse blocks per row (sbk = 64)
-    float logit[kGroupRows][NCMAX];
-    int32_t si[kGroupRows][NSB];
-    int32_t pg[kGroupRows][NSB];
-    int4 uent[kGroupRows * NSB];                 // block, page, slot byte per row, 0
-    uint32_t part[3][kGroupRows][kGroupRows];    // per wave, per row: n, min, max
-    int hist[kGroupRows][256];
-    int wsum[kGroupThreads / kWave];
+    float logit[GR][NCMAX];
+    int32_t si[GR][NSB];
+    int32_t pg[GR][NSB];
+    int4 uent[GR * NSB];                         // block, page, slot byte per row, 0
+    uint32_t part[3][kGroupWaves][GR];           // per wave, per row: n, min, max
+    int hist[GR][256 + kWave];                   // buckets + per-lane spare slots
+    float w[GR][kHeads];                         // head weights (not held in registers)
+    int wsum[kGroupWaves];
 };
 
 // Number of entries of the ascending list a[0, n) below x (n <= N, a power of two).
@@ -1117,14 +1131,16 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 // One radix pass over the keys that for_each_key(f) hands to f (each key once per
 // lane, from every lane of the wave): histograms the top 8 bits of key - lo over the
 // range [lo, hi] into the wave's 256 buckets and narrows [lo, hi] and k_rem to the
-// bucket holding the k_rem-th largest key.  Returns kSearchOn while the search goes on,
-// kTakeWhole when the bucket is taken whole, kTies when it is one key value of which
-// only the first k_rem (in column order) are taken.  Call with every lane active.
+// bucket holding the k_rem-th largest key.  Keys outside the range count into the
+// lane's own spare slot hist[256 + lane], so no lane branches.  Returns kSearchOn while
+// the search goes on, kTakeWhole when the bucket is taken whole, kTies when it is one
+// key value of which only the first k_rem (in column order) are taken.  Call with
+// every lane active; hist holds 256 + 64 ints.
 constexpr int kSearchOn = 0, kTakeWhole = 1, kTies = 2;
 
 template <class ForEach>
 __device__ __forceinline__ int wave_radix_pass(int *hist, uint32_t &lo, uint32_t &hi, int &k_rem,
-                                                ForEach for_each_key) {
+                                               ForEach for_each_key) {
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t span = hi - lo;
     const int s = max(0, 24 - __clz((int)span));
@@ -1133,7 +1149,7 @@ __device__ __forceinline__ int wave_radix_pass(int *hist, uint32_t &lo, uint32_t
     const uint32_t base = lo;
     for_each_key([&](uint32_t kk) {
         const uint32_t d = kk - base;
-        if (d <= span) atomicAdd(&hist[d >> s], 1);
+        atomicAdd(&hist[d <= span ? (int)(d >> s) : 256 + lane], 1);
     });
     const int d0 = 255 - 4 * lane;
     const int c0 = hist[d0], c1 = hist[d0 - 1], c2 = hist[d0 - 2], c3 = hist[d0 - 3];
@@ -1157,24 +1173,40 @@ __device__ __forceinline__ int wave_radix_pass(int *hist, uint32_t &lo, uint32_t
 
 // Top-k of one row by one wave, with the same selection rule as select_topk.  Lane l
 // holds the keys of columns l, l+64, ... in registers (KPL of them, read from the
-// row's LDS logits), so one compaction step covers 64 consecutive columns and its
-// selected tokens go to consecutive output slots.  The first radix pass runs over all
-// keys; the keys left in its bucket are then copied, in column order, over the row's
-// logits (no longer needed) and the remaining passes run on that short list.
-// hist: the wave's own 256 buckets.
-template <int KPL, class TokenOf>
-__device__ __forceinline__ void wave_select(float *lg, int valid_cols, int count_valid, uint32_t kmin,
-                            uint32_t kmax, int32_t topk, int32_t *orow, int *hist,
-                            TokenOf token_of) {
+// row's LDS logits), so one step covers 64 consecutive columns; steps run in chunks of
+// 8 behind one uniform check.  The first radix pass runs over all keys; the keys left
+// in its bucket are copied, in column order, over the row's logits (no longer needed)
+// and the remaining passes run on that short list.  The chosen tokens are then staged
+// in column order in the same LDS area and copied out with coalesced stores.  Lane l
+// holds the sparse block ids of slots l, l+64, ... (blk), so a step's token base is a
+// register read.  hist: the wave's 256 buckets + 64 spare slots.
+template <int KPL>
+__device__ __forceinline__ void wave_select(float *lg, const int32_t *si, int kept, int count_valid,
+                                            uint32_t kmin, uint32_t kmax, int32_t topk,
+                                            int32_t *orow, int *hist) {
+    static_assert(KPL % 8 == 0, "steps run in chunks of 8");
+    constexpr int NB = (KPL + kWave - 1) / kWave;
     const int lane = threadIdx.x & (kWave - 1);
-    const int steps = (valid_cols + kWave - 1) / kWave;
+    const int valid_cols = kept * 64;
+    const int chunks = (kept + 7) / 8;            // one step per sparse block (sbk = 64)
+    int blk[NB];
+#pragma unroll
+    for (int q = 0; q < NB; ++q) blk[q] = si[min(q * kWave + lane, KPL - 1)];
     uint32_t key[KPL];
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
-        key[i] = 0u;
         const int c = i * kWave + lane;
-        if (i < steps && c < valid_cols) key[i] = column_key(lg[c]);
+        const float x = lg[c];
+        key[i] = (i < chunks * 8 && c < valid_cols) ? column_key(x) : 0u;
     }
+    auto each_chunk = [&](auto body) {
+#pragma unroll
+        for (int c8 = 0; c8 < KPL / 8; ++c8)
+            if (c8 < chunks) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) body(c8 * 8 + j);
+            }
+    };
     const int count = min(topk, count_valid);
     uint32_t lo = 1u, hi = 0u;   // every valid key taken
     int k_rem = 0, state = kTakeWhole;
@@ -1182,85 +1214,79 @@ __device__ __forceinline__ void wave_select(float *lg, int valid_cols, int count
         lo = kmin;
         hi = kmax;
         k_rem = count;
-        state = wave_radix_pass(hist, lo, hi, k_rem, [&](auto f) {
-#pragma unroll
-            for (int i = 0; i < KPL; ++i)
-                if (i < steps) f(key[i]);
-        });
+        state = wave_radix_pass(hist, lo, hi, k_rem, [&](auto f) { each_chunk([&](int i) { f(key[i]); }); });
         if (state == kSearchOn) {
             uint32_t *cand = reinterpret_cast<uint32_t *>(lg);
             int n = 0;
-#pragma unroll
-            for (int i = 0; i < KPL; ++i) {
-                if (i < steps) {
-                    const bool in = key[i] >= lo && key[i] <= hi;
-                    const uint64_t m = __ballot(in);
-                    if (in) cand[n + lanes_below(m)] = key[i];
-                    n += __popcll(m);
-                }
-            }
+            each_chunk([&](int i) {
+                const bool in = key[i] >= lo && key[i] <= hi;
+                const uint64_t m = __ballot(in);
+                *(in ? &cand[n + lanes_below(m)] : (uint32_t *)&hist[256 + lane]) = key[i];
+                n += __popcll(m);
+            });
             for (int pass = 1; pass < 4 && state == kSearchOn; ++pass)
                 state = wave_radix_pass(hist, lo, hi, k_rem, [&](auto f) {
                     for (int j = lane; j < n; j += kWave) f(cand[j]);
                 });
         }
     }
-    // Compaction.  Without ties to break the chosen keys are exactly those >= lo.
+    // Compaction into LDS (column order), then a coalesced copy.  Without ties to break
+    // the chosen keys are exactly those >= lo.
+    int32_t *stage = reinterpret_cast<int32_t *>(lg);
     int base = 0, epos = 0;
-    if (state == kTakeWhole) {
-#pragma unroll
-        for (int i = 0; i < KPL; ++i) {
-            if (i < steps) {
-                const bool sel = key[i] >= lo;
-                const uint64_t ms = __ballot(sel);
-                const int pos = base + lanes_below(ms);
-                if (sel && pos < count) orow[pos] = token_of(i, lane);
-                base += __popcll(ms);
-            }
+    const bool ties = state != kTakeWhole;
+    each_chunk([&](int i) {
+        const uint32_t kk = key[i];
+        bool sel;
+        if (ties) {
+            const bool eq = kk >= lo && kk <= hi;
+            const uint64_t me = __ballot(eq);
+            sel = kk > hi || (eq && epos + lanes_below(me) < k_rem);
+            epos += __popcll(me);
+        } else {
+            sel = kk >= lo;
         }
-    } else {
-#pragma unroll
-        for (int i = 0; i < KPL; ++i) {
-            if (i < steps) {
-                const uint32_t kk = key[i];
-                const bool gt = kk > hi, eq = kk >= lo && kk <= hi;
-                const uint64_t me = __ballot(eq);
-                const bool sel = gt || (eq && epos + lanes_below(me) < k_rem);
-                const uint64_t ms = __ballot(sel);
-                const int pos = base + lanes_below(ms);
-                if (sel && pos < count) orow[pos] = token_of(i, lane);
-                base += __popcll(ms);
-                epos += __popcll(me);
-            }
-        }
-    }
-    for (int i = count + lane; i < topk; i += kWave) orow[i] = -1;
+        const uint64_t ms = __ballot(sel);
+        const int pos = base + lanes_below(ms);
+        // (slots past kept hold INT_MAX; their tokens only reach the spare slot)
+        const int tok = (int)((uint32_t)__builtin_amdgcn_readlane(blk[i / kWave], i % kWave) * 64u +
+                              (uint32_t)lane);
+        *(sel ? &stage[pos] : &hist[256 + lane]) = tok;
+        base += __popcll(ms);
+    });
+    for (int i = lane; i < topk; i += kWave) orow[i] = i < count ? stage[i] : -1;
 }
 
-template <int NCMAX>
+template <int NCMAX, int GR>
 __global__ __launch_bounds__(kGroupThreads) void row_group_kernel(
     Rows rows, const void *qv, const void *qs, const float *weights, KCache k, Schedule s,
     float *logits_out, int32_t topk, int32_t *out, int64_t ostride) {
-    using L = GroupLds<NCMAX>;
+    static_assert(GR >= 1 && GR <= kGroupWaves, "a wave selects each row");
+    using L = GroupLds<NCMAX, GR>;
     constexpr int NSB = L::NSB;
     __shared__ L lds;
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int wave = uniform(tid / kWave);
     // Last group first: in a causal chunk later rows hold more columns, so the longest
     // workgroups start first and the short ones fill the tail.
-    const int row0 = (gridDim.x - 1 - blockIdx.x) * kGroupRows;
+    const int row0 = (gridDim.x - 1 - blockIdx.x) * GR;
     const int ncols = s.nsb * 64;
 
-    // Query state first: its loads overlap the schedule merge below.
-    QFrag<0> f[kGroupRows];
+    // Query operands first: their loads overlap the schedule merge below.  The head
+    // weights go to LDS (16 VGPRs a row less, so more waves share each SIMD).
+    QFrag<0> f[GR];
 #pragma unroll
-    for (int r = 0; r < kGroupRows; ++r)
-        if (row0 + r < rows.num_rows) load_q<0>(f[r], qv, qs, weights, row0 + r, lane);
+    for (int r = 0; r < GR; ++r)
+        if (row0 + r < rows.num_rows) load_q(f[r], qv, qs, row0 + r, lane);
+    for (int i = tid; i < GR * kHeads; i += kGroupThreads) {
+        const int r = i / kHeads;
+        lds.w[r][i % kHeads] = row0 + r < rows.num_rows ? weights[(int64_t)row0 * kHeads + i] : 0.0f;
+    }
 
     // Row metadata (uniform: every thread reads the same words).
-    int ks[kGroupRows], ke[kGroupRows], kept[kGroupRows], tbl[kGroupRows];
+    int ks[GR], ke[GR], kept[GR], tbl[GR];
 #pragma unroll
-    for (int r = 0; r < kGroupRows; ++r) {
+    for (int r = 0; r < GR; ++r) {
         const int row = row0 + r;
         if (row < rows.num_rows) {
             const RowInfo ri = row_info(rows, k, s, row);
@@ -1275,9 +1301,9 @@ __global__ __launch_bounds__(kGroupThreads) void row_group_kernel(
     }
     bool share = true;
 #pragma unroll
-    for (int r = 1; r < kGroupRows; ++r) share = share && (kept[r] == 0 || tbl[r] == tbl[0]);
+    for (int r = 1; r < GR; ++r) share = share && (kept[r] == 0 || tbl[r] == tbl[0]);
 
-    for (int i = tid; i < kGroupRows * NSB; i += kGroupThreads) {
+    for (int i = tid; i < GR * NSB; i += kGroupThreads) {
         const int r = i / NSB, j = i % NSB;
         int32_t b = INT_MAX, p = -1;
         if (j < pick(kept, r)) {
@@ -1291,7 +1317,7 @@ __global__ __launch_bounds__(kGroupThreads) void row_group_kernel(
 
     // Union entries: entry (r, j) represents block b unless an earlier row of the
     // shared group lists it too; slots of b in the other rows come from binary search.
-    constexpr int EPT = (kGroupRows * NSB + kGroupThreads - 1) / kGroupThreads;
+    constexpr int EPT = (GR * NSB + kGroupThreads - 1) / kGroupThreads;
     int4 ent[EPT];
     bool rep[EPT];
     int nrep = 0;
@@ -1300,12 +1326,12 @@ __global__ __launch_bounds__(kGroupThreads) void row_group_kernel(
         const int i = tid + e * kGroupThreads;
         const int r = i / NSB, j = i % NSB;
         rep[e] = false;
-        if (i < kGroupRows * NSB && j < pick(kept, r)) {
+        if (i < GR * NSB && j < pick(kept, r)) {
             const int32_t b = lds.si[r][j];
             uint32_t slots = 0xFFFFFFFFu;
             bool first = true;
 #pragma unroll
-            for (int q = 0; q < kGroupRows; ++q) {
+            for (int q = 0; q < GR; ++q) {
                 int slot = -1;
                 if (q == r) {
                     slot = j;
@@ -1331,9 +1357,9 @@ __global__ __launch_bounds__(kGroupThreads) void row_group_kernel(
         if (rep[e]) lds.uent[upos++] = ent[e];
     __syncthreads();
 
-    // Scoring: wave w takes entries w, w + kGroupRows, ...; the next entry's K tiles
+    // Scoring: wave w takes entries w, w + kGroupWaves, ...; the next entry's K tiles
     // load while the current one computes.
-    KeyStats st[kGroupRows];
+    KeyStats st[GR];
     const int n = lane & 15, g = lane >> 4;
     const uint32_t voff = n * (kHeadDim / 2) + 16 * g;
     const uint32_t soff = n * (kHeadDim / 32) + g;
@@ -1344,7 +1370,7 @@ __global__ __launch_bounds__(kGroupThreads) void row_group_kernel(
         e.y = uniform(e.y);
         e.z = uniform(e.z);
         const bool ok = e.y >= 0 && e.y < k.num_pages;
-        const int64_t j0 = ok ? ((int64_t)e.x * 64) % k.page_size : 0;
+        const int64_t j0 = ok ? page_slot(e.x * 64, k.page_size) : 0;
         const kGlobal uint8_t *vb = (const kGlobal uint8_t *)k.values +
                                     (ok ? (int64_t)e.y * k.values_page_stride + j0 * 64 : 0);
         const kGlobal uint8_t *sb = (const kGlobal uint8_t *)k.scales +
@@ -1361,11 +1387,20 @@ __global__ __launch_bounds__(kGroupThreads) void row_group_kernel(
         const uint32_t slots = (uint32_t)e.z;   // 0xFF bytes (or e.z = -1): row absent
         const int tok = e.x * 64 + lane;
 #pragma unroll
-        for (int r = 0; r < kGroupRows; ++r) {
+        for (int r = 0; r < GR; ++r) {
             const uint32_t slot = (slots >> (8 * r)) & 0xFFu;
             if (slot == 0xFFu) continue;
-            const float lg = reduce_transpose4(tile_partial(f[r], kt[0]), tile_partial(f[r], kt[1]),
-                                               tile_partial(f[r], kt[2]), tile_partial(f[r], kt[3]));
+            float w[4][4];
+#pragma unroll
+            for (int ht = 0; ht < 4; ++ht) {
+                const float4 x = *(const float4 *)&lds.w[r][16 * ht + 4 * g];
+                w[ht][0] = x.x;
+                w[ht][1] = x.y;
+                w[ht][2] = x.z;
+                w[ht][3] = x.w;
+            }
+            const float lg = reduce_transpose4(tile_partial(f[r], w, kt[0]), tile_partial(f[r], w, kt[1]),
+                                               tile_partial(f[r], w, kt[2]), tile_partial(f[r], w, kt[3]));
             // Keep two MFMAs ahead of the ReLU-weight epilogue (8 VALU ops per MFMA):
             // the epilogue of MFMA i runs while MFMA i+1 and i+2 execute.
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
@@ -1384,19 +1419,19 @@ __global__ __launch_bounds__(kGroupThreads) void row_group_kernel(
     KTile ka[4], kb[4];
     int4 ea, eb;
     load_entry(wave, ka, ea);
-    for (int u = wave; u < ucount; u += 2 * kGroupRows) {
-        load_entry(u + kGroupRows, kb, eb);
+    for (int u = wave; u < ucount; u += 2 * kGroupWaves) {
+        load_entry(u + kGroupWaves, kb, eb);
         score_entry(ka, ea);
-        load_entry(u + 2 * kGroupRows, ka, ea);
+        load_entry(u + 2 * kGroupWaves, ka, ea);
         score_entry(kb, eb);   // past the last entry eb names no row
     }
     if (logits_out)
-        for (int r = 0; r < kGroupRows; ++r)
+        for (int r = 0; r < GR; ++r)
             if (row0 + r < rows.num_rows)
                 for (int c = kept[r] * 64 + tid; c < ncols; c += kGroupThreads)
                     logits_out[(int64_t)(row0 + r) * ncols + c] = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < kGroupRows; ++r) {
+    for (int r = 0; r < GR; ++r) {
         const uint32_t cn = wave_scan((uint32_t)st[r].n, 0u, OpAdd{});
         const uint32_t mn = wave_scan(st[r].mn, 0xFFFFFFFFu, OpMin{});
         const uint32_t mx = wave_scan(st[r].mx, 0u, OpMax{});
@@ -1410,19 +1445,17 @@ __global__ __launch_bounds__(kGroupThreads) void row_group_kernel(
 
     // Selection: wave r takes row r.
     const int r = wave, row = row0 + r;
-    if (row >= rows.num_rows) return;
+    if (r >= GR || row >= rows.num_rows) return;
     int cnt = 0;
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
-    for (int w = 0; w < kGroupRows; ++w) {
+    for (int w = 0; w < kGroupWaves; ++w) {
         cnt += (int)lds.part[0][w][r];
         kmin = min(kmin, lds.part[1][w][r]);
         kmax = max(kmax, lds.part[2][w][r]);
     }
-    const int32_t *si = lds.si[r];
-    wave_select<NCMAX / kWave>(lds.logit[r], pick(kept, r) * 64, cnt, kmin, kmax, topk,
-                               out + (int64_t)row * ostride, lds.hist[r],
-                               [&](int i, int l) { return si[i] * 64 + l; });
+    wave_select<NCMAX / kWave>(lds.logit[r], lds.si[r], pick(kept, r), cnt, kmin, kmax, topk,
+                               out + (int64_t)row * ostride, lds.hist[r]);
 }
 
 }  // namespace
@@ -1467,14 +1500,14 @@ static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const 
     const int ncols = s.nsb * s.sbk;
     const int ngroups = (ncols + 63) / 64;
     if constexpr (QF == 0) {
-        // Enough rows for two 4-row workgroups per CU: row groups (K tiles shared
-        // across the rows of a table).
-        if (s.sbk == 64 && ncols <= 8192 && rows.num_rows >= 2 * kGroupRows * device_cus()) {
-            const dim3 grid((rows.num_rows + kGroupRows - 1) / kGroupRows);
-#define IDX_LAUNCH_GROUP(NC_)                                                                     \
-    hipExtLaunchKernelGGL(row_group_kernel<NC_>, grid, dim3(kGroupThreads), 0, stream, timing.start, \
-                          timing.stop, 0, rows, q_values, q_scales, weights, k, s, logits_out, topk, \
-                          out, out_stride)
+        // At least 8 rows per CU: row groups (K tiles shared across the rows of a table).
+        constexpr int GR = 2;
+        if (s.sbk == 64 && ncols <= 8192 && rows.num_rows >= 8 * device_cus()) {
+            const dim3 grid((rows.num_rows + GR - 1) / GR);
+#define IDX_LAUNCH_GROUP(NC_)                                                                       \
+    hipExtLaunchKernelGGL((row_group_kernel<NC_, GR>), grid, dim3(kGroupThreads), 0, stream,        \
+                          timing.start, timing.stop, 0, rows, q_values, q_scales, weights, k, s,   \
+                          logits_out, topk, out, out_stride)
             if (ncols <= 4096) IDX_LAUNCH_GROUP(4096);
             else IDX_LAUNCH_GROUP(8192);
 #undef IDX_LAUNCH_GROUP
