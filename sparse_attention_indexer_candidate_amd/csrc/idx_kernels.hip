@@ -745,12 +745,15 @@ __device__ void block_key_stats(KeyStats p, SelectLds<NT> &L, int &count, uint32
 // waves take the same bucket with no second barrier.  The search stops once the chosen
 // bucket is taken whole or is a single key value.  Selected: keys above hi, plus the
 // first k_rem keys in [lo, hi] in column order (ties toward the lower token).
-// tokens(c0, tok) fills the tokens of columns c0 .. c0+KPT-1.  Writes orow[0, topk):
+// tokens(c0, tok) fills the tokens of columns c0 .. c0+KPT-1.  The chosen tokens are
+// placed in column order into stage (LDS, >= min(topk, count_valid) ints, free once the
+// keys are in registers) and copied out with coalesced stores: orow[0, topk) gets the
 // chosen tokens ascending, then -1.
 template <int NT, int KPT, class Tokens>
 __device__ void select_topk(const uint32_t (&key)[KPT], int count_valid, uint32_t kmin,
                             uint32_t kmax, int32_t topk, int32_t *orow, SelectLds<NT> &L,
-                            Tokens tokens) {
+                            int32_t *stage, Tokens tokens) {
+    static_assert(NT <= 4 * 256, "the histograms double as spare slots, one per thread");
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int count = min(topk, count_valid);
     uint32_t lo = 1u, hi = 0u;   // every valid key taken
@@ -795,6 +798,9 @@ __device__ void select_topk(const uint32_t (&key)[KPT], int count_valid, uint32_
     }
 
     int tok[KPT];
+    // after the scan's barrier every key is in registers and the histograms are read,
+    // so the stage and the spare slots (unchosen columns write there) are free
+    int *spare = &L.hist[0][0] + tid;
     if (whole) {
         int nsel = 0;
 #pragma unroll
@@ -804,34 +810,35 @@ __device__ void select_topk(const uint32_t (&key)[KPT], int count_valid, uint32_
         tokens(tid * KPT, tok);
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
-            const bool sel = key[i] >= lo;
-            if (sel && pos < count) orow[pos] = tok[i];
+            const bool sel = key[i] >= lo && pos < count;
+            *(sel ? &stage[pos] : spare) = tok[i];
             pos += sel;
         }
-        for (int i = count + tid; i < topk; i += NT) orow[i] = -1;
-        return;
-    }
-    // Ties at the threshold: compaction in column order; gt and eq counts share one
-    // scan (each < 2^16).
-    int ngt = 0, neq = 0;
+    } else {
+        // Ties at the threshold: compaction in column order; gt and eq counts share
+        // one scan (each < 2^16).
+        int ngt = 0, neq = 0;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-        ngt += key[i] > hi;
-        neq += key[i] >= lo && key[i] <= hi;
-    }
-    int tot = 0;
-    const int excl = block_excl_scan<NT>(ngt | (neq << 16), &tot, L.wsum);
-    int gpos = excl & 0xFFFF, epos = excl >> 16;
-    tokens(tid * KPT, tok);
+        for (int i = 0; i < KPT; ++i) {
+            ngt += key[i] > hi;
+            neq += key[i] >= lo && key[i] <= hi;
+        }
+        int tot = 0;
+        const int excl = block_excl_scan<NT>(ngt | (neq << 16), &tot, L.wsum);
+        int gpos = excl & 0xFFFF, epos = excl >> 16;
+        tokens(tid * KPT, tok);
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-        const bool gt = key[i] > hi, eq = key[i] >= lo && key[i] <= hi;
-        const int pos = gpos + min(epos, k_rem);
-        if ((gt || (eq && epos < k_rem)) && pos < count) orow[pos] = tok[i];
-        gpos += gt;
-        epos += eq;
+        for (int i = 0; i < KPT; ++i) {
+            const bool gt = key[i] > hi, eq = key[i] >= lo && key[i] <= hi;
+            const int pos = gpos + min(epos, k_rem);
+            const bool sel = (gt || (eq && epos < k_rem)) && pos < count;
+            *(sel ? &stage[pos] : spare) = tok[i];
+            gpos += gt;
+            epos += eq;
+        }
     }
-    for (int i = count + tid; i < topk; i += NT) orow[i] = -1;
+    __syncthreads();
+    for (int i = tid; i < topk; i += NT) orow[i] = i < count ? stage[i] : -1;
 }
 
 // ---------------------------------------------------------------- kernels ------
@@ -885,6 +892,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(Rows rows, KCa
                                                                   int32_t *out, int64_t ostride) {
     constexpr int KPT = kMaxRowCols / kTopkThreads;
     __shared__ int32_t s_si[kMaxNSB];
+    __shared__ int32_t s_stage[kMaxRowCols];
     __shared__ SelectLds<kTopkThreads> s_sel;
     const int row = blockIdx.x, tid = threadIdx.x;
     const RowInfo ri = row_info(rows, k, s, row);
@@ -913,7 +921,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(Rows rows, KCa
     uint32_t kmin, kmax;
     block_key_stats<kTopkThreads>(st, s_sel, nvalid, kmin, kmax);
     select_topk<kTopkThreads, KPT>(key, nvalid, kmin, kmax, topk, out + (int64_t)row * ostride,
-                                   s_sel, SparseTokens<KPT>{s_si, s.lsbk});
+                                   s_sel, s_stage, SparseTokens<KPT>{s_si, s.lsbk});
 }
 
 // Rows >= CUs: one workgroup per row; waves take units of the row's valid 64-column
@@ -981,7 +989,7 @@ __global__ __launch_bounds__(NT) void fused_row_kernel(Rows rows, const void *qv
         key[i] = c < ri.valid_cols ? column_key(s_logit[c]) : 0u;
     }
     select_topk<NT, KPT>(key, nvalid, kmin, kmax, topk, out + (int64_t)row * ostride, s_sel,
-                         SparseTokens<KPT>{s_si, s.lsbk});
+                         reinterpret_cast<int32_t *>(s_logit), SparseTokens<KPT>{s_si, s.lsbk});
 }
 
 // Dense scoring (the comparator): column t is token t, every token < max_ctx.
@@ -1070,7 +1078,8 @@ __global__ __launch_bounds__(kDenseTopkThreads) void dense_topk_kernel(Rows rows
     uint32_t kmin, kmax;
     block_key_stats<kDenseTopkThreads>(st, s_sel, count, kmin, kmax);
     select_topk<kDenseTopkThreads, KPT>(key, count, kmin, kmax, topk, out + (int64_t)row * ostride,
-                                        s_sel, [&](int c0, int (&tok)[KPT]) {
+                                        s_sel, reinterpret_cast<int32_t *>(s_val),
+                                        [&](int c0, int (&tok)[KPT]) {
 #pragma unroll
                                             for (int i = 0; i < KPT; ++i) tok[i] = s_tok[c0 + i];
                                         });
