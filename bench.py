@@ -58,27 +58,44 @@ def algorithmic_bytes(case, q_format: str, ends: np.ndarray, with_output: bool =
     return int(ends.astype(np.int64).sum()) * per_col + case.num_rows * per_row
 
 
-def cpu_baseline(case, q_format: str, seconds: float):
-    """The oracle (unchanged, single-threaded) over whole passes of the workload's
-    rows, in order, until `seconds` have elapsed or every row has run once."""
+def cpu_baseline(case, q_format: str, seconds: float, threads: int = 1):
+    """The oracle (unchanged) over chunks of 4 of the workload's rows of layer 0, taken in
+    order and wrapping around, until `seconds` of wall time have passed.  With threads > 1
+    the same calls run on that many threads at once (the C oracle releases the GIL and
+    keeps no state between calls), i.e. the rows split across the host cores."""
+    import threading
+
     import oracle
 
     pool = case.layers[0].host_pool(case.spec.page_bytes)
-    rows_done, cols_done, t_total = 0, 0, 0.0
-    order = np.arange(case.num_rows, dtype=np.int32)
-    i = 0
-    while t_total < seconds and i < case.num_rows:
-        chunk = order[i:i + 4]
-        t0 = time.perf_counter()
-        res = oracle.indexer_rows(case, 0, chunk, q_format, pool=pool, with_logits=False)
-        t_total += time.perf_counter() - t0
-        rows_done += chunk.size
-        cols_done += int(res.count.sum())
-        i += chunk.size
-    return dict(value=cols_done / t_total, unit="cols/s", cores=1, kind="oracle",
-                rows_per_s=rows_done / t_total,
-                sample=f"{rows_done} of {case.num_rows} rows of layer 0 ({cols_done} candidate "
-                       f"cols), single-threaded C oracle, {t_total:.1f} s")
+    oracle.indexer_rows(case, 0, np.zeros(1, np.int32), q_format, pool=pool, with_logits=False)
+    lock = threading.Lock()
+    state = {"next": 0, "rows": 0, "cols": 0}
+    t_end = time.perf_counter() + seconds
+
+    def worker():
+        while time.perf_counter() < t_end:
+            with lock:
+                i = state["next"]
+                state["next"] = (i + 4) % case.num_rows
+            chunk = (np.arange(i, i + 4) % case.num_rows).astype(np.int32)
+            res = oracle.indexer_rows(case, 0, chunk, q_format, pool=pool, with_logits=False)
+            with lock:
+                state["rows"] += chunk.size
+                state["cols"] += int(res.count.sum())
+
+    t0 = time.perf_counter()
+    ts = [threading.Thread(target=worker) for _ in range(threads)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    wall = time.perf_counter() - t0
+    return dict(value=state["cols"] / wall, unit="cols/s", cores=threads, kind="oracle",
+                rows_per_s=state["rows"] / wall,
+                sample=f"{state['rows']} row-scorings of layer 0 ({state['cols']} candidate cols, "
+                       f"{case.num_rows} rows wrapping), C oracle on {threads} thread(s), "
+                       f"{wall:.1f} s wall")
 
 
 def main():
@@ -88,6 +105,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2, help="workload 1-5 (default 2)")
     ap.add_argument("--q-format", default="mxfp4", choices=["mxfp4", "fp8"])
+    ap.add_argument("--path", default="sparse", choices=["sparse", "dense"],
+                    help="sparse: idx_sparse_mqa_logits_topk; dense: the comparator "
+                         "idx_dense_masked_logits_topk (scores the whole context)")
     ap.add_argument("--replicas", type=int, default=0, help="input copies (0 = auto)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -146,19 +166,30 @@ def main():
     ends = sched0.end.cpu().numpy()
     step_bytes = algorithmic_bytes(case, args.q_format, ends) * spec.layers
     # The library's choice of scoring kernel: with at least 8 rows per CU (MXFP4
-    # queries, 64-token sparse blocks) 4-row groups share K tiles and select in the same
+    # queries, 64-token sparse blocks) 2-row groups share K tiles and select in the same
     # kernel; with at least one row per CU a workgroup scores and selects one row;
-    # otherwise a split scoring kernel streams K and a second kernel selects.
+    # otherwise a split scoring kernel streams K and a second kernel selects.  The dense
+    # comparator scores every context token in its own kernel.
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     ncols = idx.idx_num_sparse_blocks(cfg) * cfg.sparse_block_kv
-    if args.q_format == "mxfp4" and cfg.sparse_block_kv == 64 and ncols <= 8192 and R >= 8 * cus:
+    ctx = (case.row_ke - (case.row_ks if case.row_ks is not None else 0)).astype(np.int64)
+    max_ctx = int(case.row_ke.max()) if R else 0
+    if args.path == "dense":
+        kernel_name = "score_dense_kernel"
+    elif args.q_format == "mxfp4" and cfg.sparse_block_kv == 64 and ncols <= 8192 and R >= 8 * cus:
         kernel_name = "row_group_kernel"
     elif R >= cus:
         kernel_name = "fused_row_kernel"
     else:
         kernel_name = "score_split_kernel"
-    fused = kernel_name != "score_split_kernel"
-    kernel_bytes = algorithmic_bytes(case, args.q_format, ends, with_output=fused)
+    fused = kernel_name in ("row_group_kernel", "fused_row_kernel")
+    if args.path == "dense":
+        # every context token's K, the row's query state, the logits row written
+        step_bytes = (algorithmic_bytes(case, args.q_format, ctx, with_output=False)
+                      + R * 4 * max_ctx) * spec.layers
+        kernel_bytes = algorithmic_bytes(case, args.q_format, ctx, with_output=False) + R * 4 * max_ctx
+    else:
+        kernel_bytes = algorithmic_bytes(case, args.q_format, ends, with_output=fused)
     pool_bytes = sum(L.pool.numel() for L in base.layers)
     if args.replicas > 0:
         nrep = args.replicas
@@ -178,7 +209,7 @@ def main():
                             q_rowscale=None if L.q_rowscale is None else L.q_rowscale.clone())
                     for L in base.layers]))
 
-    ws_bytes = idx.idx_workspace_bytes(cfg, R, 0)
+    ws_bytes = idx.idx_workspace_bytes(cfg, R, max_ctx if args.path == "dense" else 0)
     plans = []
     for d in reps:
         plans.append(dict(
@@ -211,9 +242,15 @@ def main():
             qv, qs = L.q(args.q_format)
             if timed:
                 idx.idx_set_timing_events(*ev[(i // TIMING_STRIDE) * spec.layers + layer])
-            idx.idx_sparse_mqa_logits_topk(cfg, p["rows"], qv, qs, L.weights, p["kc"][layer],
-                                           p["sched"].struct, p["out"], p["out"].stride(0), None,
-                                           p["ws"], p["ws"].numel(), stream=sh)
+            if args.path == "dense":
+                idx.idx_dense_masked_logits_topk(cfg, p["rows"], max_ctx, qv, qs, L.weights,
+                                                 p["kc"][layer], p["sched"].struct, p["out"],
+                                                 p["out"].stride(0), None, 0, p["ws"],
+                                                 p["ws"].numel(), stream=sh)
+            else:
+                idx.idx_sparse_mqa_logits_topk(cfg, p["rows"], qv, qs, L.weights, p["kc"][layer],
+                                               p["sched"].struct, p["out"], p["out"].stride(0),
+                                               None, p["ws"], p["ws"].numel(), stream=sh)
             if timed:
                 idx.idx_set_timing_events()
 
@@ -229,6 +266,7 @@ def main():
     kernel_ms = [a.elapsed_time(b) for a, b in ev]
     avg_kernel_s = float(np.mean(kernel_ms)) / 1e3
     cols_per_step = int(ends.astype(np.int64).sum()) * spec.layers
+    ctx_cols_per_step = int(ctx.sum()) * spec.layers
     launch_bytes = kernel_bytes
     achieved = launch_bytes / avg_kernel_s / 1e9
 
@@ -242,7 +280,8 @@ def main():
 
     # Prefill chunks share each K tile among many rows (K comes from L2), so the MX-FP4
     # MFMA rate bounds them; decode rows each stream their own K from HBM.
-    flops = 2 * spec.num_heads * spec.head_dim * cols_per_step / spec.layers
+    scored = ctx_cols_per_step if args.path == "dense" else cols_per_step
+    flops = 2 * spec.num_heads * spec.head_dim * scored / spec.layers
     if spec.mode == "prefill":
         roof = {"bound": "mfma", "achieved": flops / avg_kernel_s / 1e12,
                 "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s"}
@@ -251,6 +290,9 @@ def main():
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS}
     roof.update({"traffic": traffic, "kernel": kernel_name, "avg_launch_us": avg_kernel_s * 1e6,
+                 "launch_us_p10": float(np.percentile(kernel_ms, 10)) * 1e3,
+                 "launch_us_p90": float(np.percentile(kernel_ms, 90)) * 1e3,
+                 "timed_launches": len(kernel_ms),
                  "algorithmic_bytes_per_launch": launch_bytes, "hbm_gbs": achieved,
                  "mxfp4_tflops": flops / avg_kernel_s / 1e12})
     out = {
@@ -271,11 +313,16 @@ def main():
                    "candidate_block_size": spec.cbs, "topk": spec.topk, "layers": spec.layers,
                    "heads": spec.num_heads, "head_dim": spec.head_dim, "page_size": spec.page_size,
                    "valid_cols_per_step": cols_per_step, "q_format": args.q_format,
+                   "path": args.path,
                    "input_copies": nrep, "seed": args.seed},
         "roofline": roof,
     }
+    if args.path == "dense":
+        out["context_cols_per_s"] = ctx_cols_per_step * args.steps / elapsed
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(case, args.q_format, args.cpu_seconds)
+        out["cpu_baseline_all_cores"] = cpu_baseline(case, args.q_format, args.cpu_seconds,
+                                                     threads=min(16, os.cpu_count() or 1))
     print(f"# generated inputs in {gen_s:.1f} s; {nrep} input copies", file=sys.stderr)
     print(json.dumps(out), flush=True)
 
