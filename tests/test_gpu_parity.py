@@ -95,6 +95,15 @@ def test_small_case_fp8_query():
     run_and_compare(case, q_format="fp8", tag="fp8")
 
 
+def test_fp8_query_rows_per_cu():
+    """fp8 queries with at least as many rows as CUs: the one-row-per-workgroup kernel."""
+    spec = W.Spec(name="f8r", num_rows=300, page_size=64, cbs=64, nb=8, topk=200,
+                  ke_rule="uniform", ke_lo=10, ke_hi=1500, ks_rule="random", cand_rule="messy",
+                  fill="all", q_formats=("mxfp4", "fp8"))
+    case = W.generate(spec, seed=7)
+    run_and_compare(case, q_format="fp8", tag="fp8_rows")
+
+
 def test_config1_tiny_decode_all_rows():
     run_and_compare(W.generate(W.config(1), 0), tag="cfg1")
 
