@@ -8,9 +8,8 @@
 //                       reduce; one wave per 64-column group, K loads batched
 //  select_topk          per-row radix select on fp32 logits, ties toward the lower
 //                       column, ascending output, -1 fill (one workgroup per row)
-//  wave_select          the same selection by one wave (row groups)
-//  row_group_kernel     >= 8 rows per CU with MXFP4 queries (prefill chunks): 4 rows
-//                       per workgroup share K tiles; logits in LDS, a wave selects a row
+//  row_group_kernel     >= 8 rows per CU with MXFP4 queries (prefill chunks): 2 rows
+//                       per workgroup share K tiles; logits in LDS, selected in turn
 //  fused_row_kernel     rows >= CUs otherwise: one workgroup scores a whole row into LDS
 //                       and selects from LDS (no global round trip, no cross-workgroup
 //                       sync)
@@ -1094,10 +1093,11 @@ __global__ __launch_bounds__(kDenseTopkThreads) void dense_topk_kernel(Rows rows
 // for all of them, so the workgroup first merges the rows' schedule lists into one list
 // of distinct sparse blocks, each with its page and its slot in every row.  Every wave
 // then scores all GR rows for the union entries it owns (entries w, w+4, ...): one K
-// tile load feeds GR x 4 MFMAs instead of 4.  Logits stay in LDS; after one barrier
-// wave r selects row r's top-k on its own (no further barriers).  Rows on different
-// table rows are merged one row at a time (no sharing).  GR = 2 keeps the query state
-// at 72 VGPRs and the LDS near 36 KB, so three workgroups share a CU.
+// tile load feeds GR x 4 MFMAs instead of 4.  Logits stay in LDS; the whole workgroup
+// then selects the rows in turn (select_topk, 16 keys a thread: a quarter of the steps
+// one wave would take).  Rows on different table rows are merged one row at a time (no
+// sharing).  GR = 2 with the weights in LDS keeps a wave at 123 VGPRs and the LDS near
+// 37 KB, so four workgroups share a CU.
 
 constexpr int kGroupWaves = 4;
 constexpr int kGroupThreads = kGroupWaves * kWave;
@@ -1105,12 +1105,21 @@ constexpr int kGroupThreads = kGroupWaves * kWave;
 template <int NCMAX, int GR>
 struct GroupLds {
     static constexpr int NSB = NCMAX / 64;       // sparse blocks per row (sbk = 64)
+    struct alignas(16) Entry {                   // a distinct block of the group
+        int32_t block, page;
+        uint32_t slots;                          // slot byte per row, 0xFF: row lacks it
+        int32_t pad;
+    };
     float logit[GR][NCMAX];
     int32_t si[GR][NSB];
-    int32_t pg[GR][NSB];
-    int4 uent[GR * NSB];                         // block, page, slot byte per row, 0
+    union {                                      // the merge's outputs, then the selection
+        struct {
+            int32_t pg[GR][NSB];
+            Entry uent[GR * NSB];
+        } m;
+        SelectLds<kGroupThreads> sel;
+    } u;
     uint32_t part[3][kGroupWaves][GR];           // per wave, per row: n, min, max
-    int hist[GR][256 + kWave];                   // buckets + per-lane spare slots
     float w[GR][kHeads];                         // head weights (not held in registers)
     int wsum[kGroupWaves];
 };
@@ -1132,140 +1141,6 @@ __device__ __forceinline__ int pick(const int (&a)[N], int i) {
 #pragma unroll
     for (int q = 1; q < N; ++q) v = (i == q) ? a[q] : v;
     return v;
-}
-
-__device__ __forceinline__ int lanes_below(uint64_t m) {
-    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
-// One radix pass over the keys that for_each_key(f) hands to f (each key once per
-// lane, from every lane of the wave): histograms the top 8 bits of key - lo over the
-// range [lo, hi] into the wave's 256 buckets and narrows [lo, hi] and k_rem to the
-// bucket holding the k_rem-th largest key.  Keys outside the range count into the
-// lane's own spare slot hist[256 + lane], so no lane branches.  Returns kSearchOn while
-// the search goes on, kTakeWhole when the bucket is taken whole, kTies when it is one
-// key value of which only the first k_rem (in column order) are taken.  Call with
-// every lane active; hist holds 256 + 64 ints.
-constexpr int kSearchOn = 0, kTakeWhole = 1, kTies = 2;
-
-template <class ForEach>
-__device__ __forceinline__ int wave_radix_pass(int *hist, uint32_t &lo, uint32_t &hi, int &k_rem,
-                                               ForEach for_each_key) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const uint32_t span = hi - lo;
-    const int s = max(0, 24 - __clz((int)span));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) hist[lane + kWave * i] = 0;
-    const uint32_t base = lo;
-    for_each_key([&](uint32_t kk) {
-        const uint32_t d = kk - base;
-        atomicAdd(&hist[d <= span ? (int)(d >> s) : 256 + lane], 1);
-    });
-    const int d0 = 255 - 4 * lane;
-    const int c0 = hist[d0], c1 = hist[d0 - 1], c2 = hist[d0 - 2], c3 = hist[d0 - 3];
-    const int sum = c0 + c1 + c2 + c3;
-    const int incl = wave_incl_scan(sum);
-    int before = incl - sum, d = d0, c = c0;
-    if (before + c < k_rem) { before += c; --d; c = c1;
-        if (before + c < k_rem) { before += c; --d; c = c2;
-            if (before + c < k_rem) { before += c; --d; c = c3; } } }
-    const uint64_t m = __ballot(incl - sum < k_rem && incl >= k_rem);
-    const int src = (int)__builtin_ctzll(m);
-    d = __builtin_amdgcn_readlane(d, src);
-    before = __builtin_amdgcn_readlane(before, src);
-    c = __builtin_amdgcn_readlane(c, src);
-    const uint32_t w = s ? (1u << s) - 1u : 0u;
-    lo += (uint32_t)d << s;
-    hi = (hi - lo <= w) ? hi : lo + w;
-    k_rem -= before;
-    return c == k_rem ? kTakeWhole : (s == 0 ? kTies : kSearchOn);
-}
-
-// Top-k of one row by one wave, with the same selection rule as select_topk.  Lane l
-// holds the keys of columns l, l+64, ... in registers (KPL of them, read from the
-// row's LDS logits), so one step covers 64 consecutive columns; steps run in chunks of
-// 8 behind one uniform check.  The first radix pass runs over all keys; the keys left
-// in its bucket are copied, in column order, over the row's logits (no longer needed)
-// and the remaining passes run on that short list.  The chosen tokens are then staged
-// in column order in the same LDS area and copied out with coalesced stores.  Lane l
-// holds the sparse block ids of slots l, l+64, ... (blk), so a step's token base is a
-// register read.  hist: the wave's 256 buckets + 64 spare slots.
-template <int KPL>
-__device__ __forceinline__ void wave_select(float *lg, const int32_t *si, int kept, int count_valid,
-                                            uint32_t kmin, uint32_t kmax, int32_t topk,
-                                            int32_t *orow, int *hist) {
-    static_assert(KPL % 8 == 0, "steps run in chunks of 8");
-    constexpr int NB = (KPL + kWave - 1) / kWave;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int valid_cols = kept * 64;
-    const int chunks = (kept + 7) / 8;            // one step per sparse block (sbk = 64)
-    int blk[NB];
-#pragma unroll
-    for (int q = 0; q < NB; ++q) blk[q] = si[min(q * kWave + lane, KPL - 1)];
-    uint32_t key[KPL];
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-        const int c = i * kWave + lane;
-        const float x = lg[c];
-        key[i] = (i < chunks * 8 && c < valid_cols) ? column_key(x) : 0u;
-    }
-    auto each_chunk = [&](auto body) {
-#pragma unroll
-        for (int c8 = 0; c8 < KPL / 8; ++c8)
-            if (c8 < chunks) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) body(c8 * 8 + j);
-            }
-    };
-    const int count = min(topk, count_valid);
-    uint32_t lo = 1u, hi = 0u;   // every valid key taken
-    int k_rem = 0, state = kTakeWhole;
-    if (count < count_valid) {
-        lo = kmin;
-        hi = kmax;
-        k_rem = count;
-        state = wave_radix_pass(hist, lo, hi, k_rem, [&](auto f) { each_chunk([&](int i) { f(key[i]); }); });
-        if (state == kSearchOn) {
-            uint32_t *cand = reinterpret_cast<uint32_t *>(lg);
-            int n = 0;
-            each_chunk([&](int i) {
-                const bool in = key[i] >= lo && key[i] <= hi;
-                const uint64_t m = __ballot(in);
-                *(in ? &cand[n + lanes_below(m)] : (uint32_t *)&hist[256 + lane]) = key[i];
-                n += __popcll(m);
-            });
-            for (int pass = 1; pass < 4 && state == kSearchOn; ++pass)
-                state = wave_radix_pass(hist, lo, hi, k_rem, [&](auto f) {
-                    for (int j = lane; j < n; j += kWave) f(cand[j]);
-                });
-        }
-    }
-    // Compaction into LDS (column order), then a coalesced copy.  Without ties to break
-    // the chosen keys are exactly those >= lo.
-    int32_t *stage = reinterpret_cast<int32_t *>(lg);
-    int base = 0, epos = 0;
-    const bool ties = state != kTakeWhole;
-    each_chunk([&](int i) {
-        const uint32_t kk = key[i];
-        bool sel;
-        if (ties) {
-            const bool eq = kk >= lo && kk <= hi;
-            const uint64_t me = __ballot(eq);
-            sel = kk > hi || (eq && epos + lanes_below(me) < k_rem);
-            epos += __popcll(me);
-        } else {
-            sel = kk >= lo;
-        }
-        const uint64_t ms = __ballot(sel);
-        const int pos = base + lanes_below(ms);
-        // (slots past kept hold INT_MAX; their tokens only reach the spare slot)
-        const int tok = (int)((uint32_t)__builtin_amdgcn_readlane(blk[i / kWave], i % kWave) * 64u +
-                              (uint32_t)lane);
-        *(sel ? &stage[pos] : &hist[256 + lane]) = tok;
-        base += __popcll(ms);
-    });
-    for (int i = lane; i < topk; i += kWave) orow[i] = i < count ? stage[i] : -1;
 }
 
 template <int NCMAX, int GR>
@@ -1322,14 +1197,14 @@ __global__ __launch_bounds__(kGroupThreads) void row_group_kernel(
             p = s.pages[(int64_t)(row0 + r) * s.nsb + j];
         }
         lds.si[r][j] = b;
-        lds.pg[r][j] = p;
+        lds.u.m.pg[r][j] = p;
     }
     __syncthreads();
 
     // Union entries: entry (r, j) represents block b unless an earlier row of the
     // shared group lists it too; slots of b in the other rows come from binary search.
     constexpr int EPT = (GR * NSB + kGroupThreads - 1) / kGroupThreads;
-    int4 ent[EPT];
+    typename L::Entry ent[EPT];
     bool rep[EPT];
     int nrep = 0;
 #pragma unroll
@@ -1357,7 +1232,7 @@ __global__ __launch_bounds__(kGroupThreads) void row_group_kernel(
                 }
             }
             rep[e] = first;
-            ent[e] = make_int4(b, lds.pg[r][j], (int)slots, 0);
+            ent[e] = typename L::Entry{b, lds.u.m.pg[r][j], slots, 0};
         }
         nrep += rep[e];
     }
@@ -1365,7 +1240,7 @@ __global__ __launch_bounds__(kGroupThreads) void row_group_kernel(
     int upos = block_excl_scan<kGroupThreads>(nrep, &ucount, lds.wsum);
 #pragma unroll
     for (int e = 0; e < EPT; ++e)
-        if (rep[e]) lds.uent[upos++] = ent[e];
+        if (rep[e]) lds.u.m.uent[upos++] = ent[e];
     __syncthreads();
 
     // Scoring: wave w takes entries w, w + kGroupWaves, ...; the next entry's K tiles
@@ -1376,7 +1251,10 @@ __global__ __launch_bounds__(kGroupThreads) void row_group_kernel(
     const uint32_t soff = n * (kHeadDim / 32) + g;
     auto load_entry = [&](int u, KTile (&kt)[4], int4 &e) {
         e = make_int4(0, -1, -1, 0);
-        if (u < ucount) e = lds.uent[u];
+        if (u < ucount) {
+            const typename L::Entry &x = lds.u.m.uent[u];
+            e = make_int4(x.block, x.page, (int)x.slots, 0);
+        }
         e.x = uniform(e.x);
         e.y = uniform(e.y);
         e.z = uniform(e.z);
@@ -1454,19 +1332,34 @@ __global__ __launch_bounds__(kGroupThreads) void row_group_kernel(
     }
     __syncthreads();
 
-    // Selection: wave r takes row r.
-    const int r = wave, row = row0 + r;
-    if (r >= GR || row >= rows.num_rows) return;
-    int cnt = 0;
-    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+    // Selection: the whole workgroup takes the group's rows in turn (the merge's LDS is
+    // free now and holds the selection's histograms).
+    constexpr int KPT = NCMAX / kGroupThreads;
+#pragma unroll 1
+    for (int r = 0; r < GR; ++r) {
+        const int row = row0 + r;
+        if (row >= rows.num_rows) break;
+        int cnt = 0;
+        uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
-    for (int w = 0; w < kGroupWaves; ++w) {
-        cnt += (int)lds.part[0][w][r];
-        kmin = min(kmin, lds.part[1][w][r]);
-        kmax = max(kmax, lds.part[2][w][r]);
+        for (int w = 0; w < kGroupWaves; ++w) {
+            cnt += (int)lds.part[0][w][r];
+            kmin = min(kmin, lds.part[1][w][r]);
+            kmax = max(kmax, lds.part[2][w][r]);
+        }
+        select_clear(lds.u.sel);
+        __syncthreads();
+        const int valid_cols = pick(kept, r) * 64;
+        uint32_t key[KPT];
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int c = tid * KPT + i;
+            key[i] = c < valid_cols ? column_key(lds.logit[r][c]) : 0u;
+        }
+        select_topk<kGroupThreads, KPT>(key, cnt, kmin, kmax, topk, out + (int64_t)row * ostride,
+                                        lds.u.sel, reinterpret_cast<int32_t *>(lds.logit[r]),
+                                        SparseTokens<KPT>{lds.si[r], 6});
     }
-    wave_select<NCMAX / kWave>(lds.logit[r], lds.si[r], pick(kept, r), cnt, kmin, kmax, topk,
-                               out + (int64_t)row * ostride, lds.hist[r]);
 }
 
 }  // namespace
