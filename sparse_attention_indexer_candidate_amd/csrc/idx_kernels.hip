@@ -1119,7 +1119,6 @@ struct GroupLds {
         } m;
         SelectLds<kGroupThreads> sel;
     } u;
-    uint32_t part[3][kGroupWaves][GR];           // per wave, per row: n, min, max
     float w[GR][kHeads];                         // head weights (not held in registers)
     int wsum[kGroupWaves];
 };
@@ -1245,7 +1244,6 @@ __global__ __launch_bounds__(kGroupThreads) void row_group_kernel(
 
     // Scoring: wave w takes entries w, w + kGroupWaves, ...; the next entry's K tiles
     // load while the current one computes.
-    KeyStats st[GR];
     const int n = lane & 15, g = lane >> 4;
     const uint32_t voff = n * (kHeadDim / 2) + 16 * g;
     const uint32_t soff = n * (kHeadDim / 32) + g;
@@ -1302,7 +1300,6 @@ __global__ __launch_bounds__(kGroupThreads) void row_group_kernel(
             const int c = (int)slot * 64 + lane;
             lds.logit[r][c] = v;
             if (logits_out) logits_out[(int64_t)(row0 + r) * ncols + c] = v;
-            st[r].add(column_key(v));
         }
     };
     KTile ka[4], kb[4];
@@ -1319,17 +1316,6 @@ __global__ __launch_bounds__(kGroupThreads) void row_group_kernel(
             if (row0 + r < rows.num_rows)
                 for (int c = kept[r] * 64 + tid; c < ncols; c += kGroupThreads)
                     logits_out[(int64_t)(row0 + r) * ncols + c] = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < GR; ++r) {
-        const uint32_t cn = wave_scan((uint32_t)st[r].n, 0u, OpAdd{});
-        const uint32_t mn = wave_scan(st[r].mn, 0xFFFFFFFFu, OpMin{});
-        const uint32_t mx = wave_scan(st[r].mx, 0u, OpMax{});
-        if (lane == kWave - 1) {
-            lds.part[0][wave][r] = cn;
-            lds.part[1][wave][r] = mn;
-            lds.part[2][wave][r] = mx;
-        }
-    }
     __syncthreads();
 
     // Selection: the whole workgroup takes the group's rows in turn (the merge's LDS is
@@ -1339,23 +1325,19 @@ __global__ __launch_bounds__(kGroupThreads) void row_group_kernel(
     for (int r = 0; r < GR; ++r) {
         const int row = row0 + r;
         if (row >= rows.num_rows) break;
-        int cnt = 0;
-        uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-#pragma unroll
-        for (int w = 0; w < kGroupWaves; ++w) {
-            cnt += (int)lds.part[0][w][r];
-            kmin = min(kmin, lds.part[1][w][r]);
-            kmax = max(kmax, lds.part[2][w][r]);
-        }
         select_clear(lds.u.sel);
-        __syncthreads();
         const int valid_cols = pick(kept, r) * 64;
         uint32_t key[KPT];
+        KeyStats st;
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int c = tid * KPT + i;
             key[i] = c < valid_cols ? column_key(lds.logit[r][c]) : 0u;
+            st.add(key[i]);
         }
+        int cnt;
+        uint32_t kmin, kmax;
+        block_key_stats<kGroupThreads>(st, lds.u.sel, cnt, kmin, kmax);   // also publishes the clear
         select_topk<kGroupThreads, KPT>(key, cnt, kmin, kmax, topk, out + (int64_t)row * ostride,
                                         lds.u.sel, reinterpret_cast<int32_t *>(lds.logit[r]),
                                         SparseTokens<KPT>{lds.si[r], 6});
