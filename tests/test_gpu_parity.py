@@ -104,6 +104,24 @@ def test_fp8_query_rows_per_cu():
     run_and_compare(case, q_format="fp8", tag="fp8_rows")
 
 
+def test_row_groups_wide_rows_sampled_and_properties():
+    """Row groups over more than 4096 candidate columns (the 8192-column workgroup shape):
+    2048 prefill rows on one table, 100 candidate blocks of 64; the oracle on sampled rows,
+    exact selection for the GPU's own logits on every row."""
+    spec = W.Spec(name="wide", num_rows=2048, page_size=64, cbs=64, nb=100, topk=1500,
+                  mode="prefill", ke_rule="uniform", ke_lo=1, ke_hi=7000, ks_rule="random",
+                  context=7000, cand_rule="messy", fill="all")
+    case = W.generate(spec, seed=3)
+    rows = np.unique(np.r_[0, 1, 2, 3, 1022, 1023, 2046, 2047,
+                           np.random.default_rng(5).integers(0, 2048, 24)]).astype(np.int32)
+    g, res = run_and_compare(case, rows=rows, tag="wide")
+    for i in range(case.num_rows):
+        gt, gl = gpu_row_tokens(res["sparse_indices"][i], int(res["kept"][i]), g.sbk,
+                                int(case.row_ks[i]), int(case.row_ke[i]), res["logits"][i])
+        np.testing.assert_array_equal(res["indices"][i], exact_topk(gt, gl, spec.topk),
+                                      err_msg=f"wide row {i}")
+
+
 def test_config1_tiny_decode_all_rows():
     run_and_compare(W.generate(W.config(1), 0), tag="cfg1")
 
