@@ -677,6 +677,17 @@ __device__ __forceinline__ uint32_t ordered_key(float x) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Column words of the row-group kernel's LDS: a valid column holds its logit's bits,
+// any other kNoColumn (a NaN pattern, taken to mean "no logit").  bits_key is
+// ordered_key on such a word without the -0 step (a scored logit is never -0: each
+// head sum starts from +0 and adds w * ReLU terms, and a round-to-nearest sum is -0
+// only when both operands are); it takes kNoColumn to the invalid key 0 by itself,
+// and -inf, a valid logit, to 0x007FFFFF.
+constexpr uint32_t kNoColumn = 0xFFFFFFFFu;
+__device__ __forceinline__ uint32_t bits_key(uint32_t u) {
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+
 // Workgroup LDS of the row selection: one 256-bucket histogram per radix pass (at
 // most four: each pass narrows the key range by 8 bits or more), the per-wave partial
 // statistics and the per-wave totals of the compaction scan.
@@ -706,16 +717,14 @@ struct KeyStats {
     }
 };
 
-// Combines the partials of the workgroup: count of valid keys, smallest and largest
-// valid key.  Contains one barrier (which also publishes whatever the threads wrote to
-// LDS before the call).
+// Lane kWave-1 of each wave holds its wave's count of valid keys, smallest and largest
+// valid key; combines them over the workgroup.  Contains one barrier (which also
+// publishes whatever the threads wrote to LDS before the call).
 template <int NT>
-__device__ void block_key_stats(KeyStats p, SelectLds<NT> &L, int &count, uint32_t &kmin,
-                                uint32_t &kmax) {
+__device__ __forceinline__ void block_stats_combine(uint32_t n, uint32_t mn, uint32_t mx,
+                                                    SelectLds<NT> &L, int &count,
+                                                    uint32_t &kmin, uint32_t &kmax) {
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-    const uint32_t n = wave_scan((uint32_t)p.n, 0u, OpAdd{});
-    const uint32_t mn = wave_scan(p.mn, 0xFFFFFFFFu, OpMin{});
-    const uint32_t mx = wave_scan(p.mx, 0u, OpMax{});
     if (lane == kWave - 1) {
         L.part[0][wid] = n;
         L.part[1][wid] = mn;
@@ -735,8 +744,50 @@ __device__ void block_key_stats(KeyStats p, SelectLds<NT> &L, int &count, uint32
     kmax = b;
 }
 
+// Combines per-thread partials over the workgroup: count of valid keys, smallest and
+// largest valid key (one barrier, see block_stats_combine).
+template <int NT>
+__device__ void block_key_stats(KeyStats p, SelectLds<NT> &L, int &count, uint32_t &kmin,
+                                uint32_t &kmax) {
+    block_stats_combine<NT>(wave_scan((uint32_t)p.n, 0u, OpAdd{}),
+                            wave_scan(p.mn, 0xFFFFFFFFu, OpMin{}), wave_scan(p.mx, 0u, OpMax{}),
+                            L, count, kmin, kmax);
+}
+
+// True when one of the thread's keys is valid (nonzero).
+template <int KPT>
+__device__ __forceinline__ bool keys_live(const uint32_t (&key)[KPT]) {
+    uint32_t a = 0u;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) a |= key[i];
+    return a != 0u;
+}
+
+// The same statistics straight from the keys in registers (live: keys_live(key), or
+// false only where every key is 0): the count from wave ballots, and the minimum as
+// 1 + min(key - 1), in which the invalid key 0 wraps to the largest value and drops
+// out without a test.  A wave with no live thread skips the keys.
+template <int NT, int KPT>
+__device__ void block_key_stats(const uint32_t (&key)[KPT], bool live, SelectLds<NT> &L,
+                                int &count, uint32_t &kmin, uint32_t &kmax) {
+    uint32_t n = 0, mnm1 = 0xFFFFFFFFu, mx = 0u;
+    if (__ballot(live) != 0ull) {   // uniform: the whole wave takes it or skips it
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            n += (uint32_t)__popcll(__ballot(key[i] != 0u));
+            mnm1 = min(mnm1, key[i] - 1u);
+            mx = max(mx, key[i]);
+        }
+    }
+    block_stats_combine<NT>(n, wave_scan(mnm1, 0xFFFFFFFFu, OpMin{}), wave_scan(mx, 0u, OpMax{}),
+                            L, count, kmin, kmax);
+    kmin += 1u;   // no valid key: 0
+}
+
 // Top-k of one row by one workgroup of NT threads.  Thread i holds the keys of columns
 // [i*KPT, (i+1)*KPT) (key 0: invalid column); column order is ascending token order.
+// live may be false only where all of the thread's keys are 0 (keys_live(key), or a
+// coarser test); such threads skip the per-key work.
 // count_valid, kmin and kmax come from block_key_stats; count = min(topk, count_valid).
 // The count-th largest key is found by radix passes over key - lo, where [lo, hi] is
 // the key range still holding it (first [kmin, kmax]): a pass histograms the top 8
@@ -745,11 +796,11 @@ __device__ void block_key_stats(KeyStats p, SelectLds<NT> &L, int &count, uint32
 // bucket is taken whole or is a single key value.  Selected: keys above hi, plus the
 // first k_rem keys in [lo, hi] in column order (ties toward the lower token).
 // tokens(c0, tok) fills the tokens of columns c0 .. c0+KPT-1.  The chosen tokens are
-// placed in column order into stage (LDS, >= min(topk, count_valid) ints, free once the
-// keys are in registers) and copied out with coalesced stores: orow[0, topk) gets the
-// chosen tokens ascending, then -1.
+// placed in column order into stage (LDS, 16-byte aligned, a multiple of 4 ints and at
+// least count_valid of them, free once the keys are in registers) and copied out with
+// coalesced stores: orow[0, topk) gets the chosen tokens ascending, then -1.
 template <int NT, int KPT, class Tokens>
-__device__ void select_topk(const uint32_t (&key)[KPT], int count_valid, uint32_t kmin,
+__device__ void select_topk(const uint32_t (&key)[KPT], bool live, int count_valid, uint32_t kmin,
                             uint32_t kmax, int32_t topk, int32_t *orow, SelectLds<NT> &L,
                             int32_t *stage, Tokens tokens) {
     static_assert(NT <= 4 * 256, "the histograms double as spare slots, one per thread");
@@ -766,10 +817,25 @@ __device__ void select_topk(const uint32_t (&key)[KPT], int count_valid, uint32_
             const uint32_t span = hi - lo;
             const int s = max(0, 24 - __clz((int)span));   // (span >> s) < 256
             int *h = L.hist[pass];
+            if (pass == 0) {
+                // No range test: every valid key lies in [kmin, kmax], and the
+                // invalid key 0 saturates into bucket 0.  That can only raise bucket
+                // 0's count: the bucket holding the count-th largest valid key is
+                // still the one found below (count < count_valid), and a raised count
+                // there can only turn `whole` false, never true wrongly.  Threads
+                // holding no valid key (columns past the row's end) add nothing, so
+                // few invalid keys meet on bucket 0 (same-address atomics serialize).
+                if (live) {
 #pragma unroll
-            for (int i = 0; i < KPT; ++i) {
-                const uint32_t d = key[i] - lo;
-                if (d <= span) atomicAdd(&h[d >> s], 1);
+                    for (int i = 0; i < KPT; ++i)
+                        atomicAdd(&h[__builtin_elementwise_sub_sat(key[i], lo) >> s], 1);
+                }
+            } else if (live) {
+#pragma unroll
+                for (int i = 0; i < KPT; ++i) {
+                    const uint32_t d = key[i] - lo;
+                    if (d <= span) atomicAdd(&h[d >> s], 1);
+                }
             }
             __syncthreads();
             // lane l owns buckets 255-4l .. 252-4l; exactly one lane's buckets hold
@@ -801,43 +867,67 @@ __device__ void select_topk(const uint32_t (&key)[KPT], int count_valid, uint32_
     // so the stage and the spare slots (unchosen columns write there) are free
     int *spare = &L.hist[0][0] + tid;
     if (whole) {
+        // exactly count keys are >= lo (all valid keys when lo = 1; otherwise the
+        // keys above the final bucket plus that whole bucket)
         int nsel = 0;
+        if (live) {
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) nsel += key[i] >= lo;
+            for (int i = 0; i < KPT; ++i) nsel += key[i] >= lo;
+        }
         int tot = 0;
         int pos = block_excl_scan<NT>(nsel, &tot, L.wsum);
-        tokens(tid * KPT, tok);
+        if (live) {
+            tokens(tid * KPT, tok);
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const bool sel = key[i] >= lo && pos < count;
-            *(sel ? &stage[pos] : spare) = tok[i];
-            pos += sel;
+            for (int i = 0; i < KPT; ++i) {
+                const bool sel = key[i] >= lo;
+                *(sel ? &stage[pos] : spare) = tok[i];
+                pos += sel;
+            }
         }
     } else {
         // Ties at the threshold: compaction in column order; gt and eq counts share
         // one scan (each < 2^16).
         int ngt = 0, neq = 0;
+        if (live) {
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            ngt += key[i] > hi;
-            neq += key[i] >= lo && key[i] <= hi;
+            for (int i = 0; i < KPT; ++i) {
+                ngt += key[i] > hi;
+                neq += key[i] >= lo && key[i] <= hi;
+            }
         }
         int tot = 0;
         const int excl = block_excl_scan<NT>(ngt | (neq << 16), &tot, L.wsum);
         int gpos = excl & 0xFFFF, epos = excl >> 16;
-        tokens(tid * KPT, tok);
+        if (live) {
+            tokens(tid * KPT, tok);
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const bool gt = key[i] > hi, eq = key[i] >= lo && key[i] <= hi;
-            const int pos = gpos + min(epos, k_rem);
-            const bool sel = (gt || (eq && epos < k_rem)) && pos < count;
-            *(sel ? &stage[pos] : spare) = tok[i];
-            gpos += gt;
-            epos += eq;
+            for (int i = 0; i < KPT; ++i) {
+                const bool gt = key[i] > hi, eq = key[i] >= lo && key[i] <= hi;
+                const int pos = gpos + min(epos, k_rem);
+                const bool sel = (gt || (eq && epos < k_rem)) && pos < count;
+                *(sel ? &stage[pos] : spare) = tok[i];
+                gpos += gt;
+                epos += eq;
+            }
         }
     }
     __syncthreads();
-    for (int i = tid; i < topk; i += NT) orow[i] = i < count ? stage[i] : -1;
+    if ((topk & 3) == 0 && (reinterpret_cast<uintptr_t>(orow) & 15) == 0) {
+        // 16-byte stores; stage is read only below count (rounded up to 4, which
+        // stays inside it: its size is a multiple of 4 and at least count_valid)
+        for (int i = 4 * tid; i < topk; i += 4 * NT) {
+            int4 v = make_int4(-1, -1, -1, -1);
+            if (i < count) {
+                const int4 x = *reinterpret_cast<const int4 *>(stage + i);
+                v = make_int4(x.x, i + 1 < count ? x.y : -1, i + 2 < count ? x.z : -1,
+                              i + 3 < count ? x.w : -1);
+            }
+            *reinterpret_cast<int4 *>(orow + i) = v;
+        }
+    } else {
+        for (int i = tid; i < topk; i += NT) orow[i] = i < count ? stage[i] : -1;
+    }
 }
 
 // ---------------------------------------------------------------- kernels ------
@@ -891,7 +981,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(Rows rows, KCa
                                                                   int32_t *out, int64_t ostride) {
     constexpr int KPT = kMaxRowCols / kTopkThreads;
     __shared__ int32_t s_si[kMaxNSB];
-    __shared__ int32_t s_stage[kMaxRowCols];
+    __shared__ alignas(16) int32_t s_stage[kMaxRowCols];
     __shared__ SelectLds<kTopkThreads> s_sel;
     const int row = blockIdx.x, tid = threadIdx.x;
     const RowInfo ri = row_info(rows, k, s, row);
@@ -919,7 +1009,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(Rows rows, KCa
     int nvalid;
     uint32_t kmin, kmax;
     block_key_stats<kTopkThreads>(st, s_sel, nvalid, kmin, kmax);
-    select_topk<kTopkThreads, KPT>(key, nvalid, kmin, kmax, topk, out + (int64_t)row * ostride,
+    select_topk<kTopkThreads, KPT>(key, keys_live(key), nvalid, kmin, kmax, topk, out + (int64_t)row * ostride,
                                    s_sel, s_stage, SparseTokens<KPT>{s_si, s.lsbk});
 }
 
@@ -931,7 +1021,7 @@ __global__ __launch_bounds__(NT) void fused_row_kernel(Rows rows, const void *qv
                                                        const float *weights, KCache k, Schedule s,
                                                        float *logits_out, int32_t topk,
                                                        int32_t *out, int64_t ostride) {
-    __shared__ float s_logit[kMaxRowCols];
+    __shared__ alignas(16) float s_logit[kMaxRowCols];
     __shared__ int32_t s_si[kMaxNSB];
     __shared__ int32_t s_pg[kMaxNSB];
     __shared__ int s_unit;
@@ -985,11 +1075,15 @@ __global__ __launch_bounds__(NT) void fused_row_kernel(Rows rows, const void *qv
     block_key_stats<NT>(st, s_sel, nvalid, kmin, kmax);   // also publishes s_logit, s_si
     uint32_t key[KPT];
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-        const int c = tid * KPT + i;
-        key[i] = c < ri.valid_cols ? column_key(s_logit[c]) : 0u;
+    for (int i = 0; i < KPT; i += 4) {
+        const int c = tid * KPT + i;   // columns past valid_cols: stale LDS, read but not used
+        const float4 x = *reinterpret_cast<const float4 *>(&s_logit[c]);
+        key[i] = c < ri.valid_cols ? column_key(x.x) : 0u;
+        key[i + 1] = c + 1 < ri.valid_cols ? column_key(x.y) : 0u;
+        key[i + 2] = c + 2 < ri.valid_cols ? column_key(x.z) : 0u;
+        key[i + 3] = c + 3 < ri.valid_cols ? column_key(x.w) : 0u;
     }
-    select_topk<NT, KPT>(key, nvalid, kmin, kmax, topk, out + (int64_t)row * ostride, s_sel,
+    select_topk<NT, KPT>(key, keys_live(key), nvalid, kmin, kmax, topk, out + (int64_t)row * ostride, s_sel,
                          reinterpret_cast<int32_t *>(s_logit), SparseTokens<KPT>{s_si, s.lsbk});
 }
 
@@ -1029,7 +1123,7 @@ __global__ __launch_bounds__(kDenseTopkThreads) void dense_topk_kernel(Rows rows
     constexpr int CPT = kMaxDenseCols / kDenseTopkThreads;   // columns scanned per thread
     constexpr int KPT = kMaxRowCols / kDenseTopkThreads;     // compacted keys per thread
     __shared__ uint32_t s_bits[kMaxDenseBlocks / 32];
-    __shared__ float s_val[kMaxRowCols];
+    __shared__ alignas(16) float s_val[kMaxRowCols];
     __shared__ int32_t s_tok[kMaxRowCols];
     __shared__ int s_scan[kDenseTopkThreads / kWave];
     __shared__ SelectLds<kDenseTopkThreads> s_sel;
@@ -1078,7 +1172,7 @@ __global__ __launch_bounds__(kDenseTopkThreads) void dense_topk_kernel(Rows rows
     int count;
     uint32_t kmin, kmax;
     block_key_stats<kDenseTopkThreads>(st, s_sel, count, kmin, kmax);
-    select_topk<kDenseTopkThreads, KPT>(key, count, kmin, kmax, topk, out + (int64_t)row * ostride,
+    select_topk<kDenseTopkThreads, KPT>(key, keys_live(key), count, kmin, kmax, topk, out + (int64_t)row * ostride,
                                         s_sel, reinterpret_cast<int32_t *>(s_val),
                                         [&](int c0, int (&tok)[KPT]) {
 #pragma unroll
@@ -1110,7 +1204,7 @@ struct GroupLds {
         uint32_t slots;                          // slot byte per row, 0xFF: row lacks it
         int32_t pad;
     };
-    float logit[GR][NCMAX];
+    uint32_t logit[GR][NCMAX];                   // column words (bits_key), then the stage
     int32_t si[GR][NSB];
     union {                                      // the merge's outputs, then the selection
         struct {
@@ -1147,6 +1241,7 @@ __global__ __launch_bounds__(kGroupThreads) void row_group_kernel(
     Rows rows, const void *qv, const void *qs, const float *weights, KCache k, Schedule s,
     float *logits_out, int32_t topk, int32_t *out, int64_t ostride) {
     static_assert(GR >= 1 && GR <= kGroupWaves, "a wave selects each row");
+    static_assert(64 % (NCMAX / kGroupThreads) == 0, "a thread's keys lie in one sparse block");
     using L = GroupLds<NCMAX, GR>;
     constexpr int NSB = L::NSB;
     __shared__ L lds;
@@ -1296,10 +1391,10 @@ __global__ __launch_bounds__(kGroupThreads) void row_group_kernel(
                 __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             }
-            const float v = (tok >= ks[r] && tok < ke[r]) ? lg : -INFINITY;
+            const bool valid = tok >= ks[r] && tok < ke[r];
             const int c = (int)slot * 64 + lane;
-            lds.logit[r][c] = v;
-            if (logits_out) logits_out[(int64_t)(row0 + r) * ncols + c] = v;
+            lds.logit[r][c] = valid ? __float_as_uint(lg) : kNoColumn;
+            if (logits_out) logits_out[(int64_t)(row0 + r) * ncols + c] = valid ? lg : -INFINITY;
         }
     };
     KTile ka[4], kb[4];
@@ -1326,19 +1421,26 @@ __global__ __launch_bounds__(kGroupThreads) void row_group_kernel(
         const int row = row0 + r;
         if (row >= rows.num_rows) break;
         select_clear(lds.u.sel);
-        const int valid_cols = pick(kept, r) * 64;
+        // KPT divides 64, so a thread's columns are all below the row's scored columns
+        // (kept blocks of 64) or all above them (stale LDS, read but not used)
+        const bool mine = tid * KPT < pick(kept, r) * 64;
         uint32_t key[KPT];
-        KeyStats st;
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int c = tid * KPT + i;
-            key[i] = c < valid_cols ? column_key(lds.logit[r][c]) : 0u;
-            st.add(key[i]);
+        for (int i = 0; i < KPT; ++i) key[i] = 0u;
+        if (mine) {
+#pragma unroll
+            for (int i = 0; i < KPT; i += 4) {
+                const uint4 x = *reinterpret_cast<const uint4 *>(&lds.logit[r][tid * KPT + i]);
+                key[i] = bits_key(x.x);
+                key[i + 1] = bits_key(x.y);
+                key[i + 2] = bits_key(x.z);
+                key[i + 3] = bits_key(x.w);
+            }
         }
         int cnt;
         uint32_t kmin, kmax;
-        block_key_stats<kGroupThreads>(st, lds.u.sel, cnt, kmin, kmax);   // also publishes the clear
-        select_topk<kGroupThreads, KPT>(key, cnt, kmin, kmax, topk, out + (int64_t)row * ostride,
+        block_key_stats<kGroupThreads>(key, mine, lds.u.sel, cnt, kmin, kmax);   // also publishes the clear
+        select_topk<kGroupThreads, KPT>(key, mine, cnt, kmin, kmax, topk, out + (int64_t)row * ostride,
                                         lds.u.sel, reinterpret_cast<int32_t *>(lds.logit[r]),
                                         SparseTokens<KPT>{lds.si[r], 6});
     }
