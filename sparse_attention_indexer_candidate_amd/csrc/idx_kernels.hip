@@ -689,19 +689,20 @@ __device__ __forceinline__ uint32_t bits_key(uint32_t u) {
 }
 
 // Workgroup LDS of the row selection: one 256-bucket histogram per radix pass (at
-// most four: each pass narrows the key range by 8 bits or more), the per-wave partial
-// statistics and the per-wave totals of the compaction scan.
-template <int NT>
+// most four: each pass narrows the key range by 8 bits or more; NH = 5 when the first
+// digit is a 512-bucket histogram built while scoring, see select_topk), the per-wave
+// partial statistics and the per-wave totals of the compaction scan.
+template <int NT, int NH = 4>
 struct SelectLds {
-    int hist[4][256];
+    alignas(16) int hist[NH][256];
     uint32_t part[3][NT / kWave];
     int wsum[NT / kWave];
 };
 
 // Zeroes the histograms.  Call before the barrier of block_key_stats.
-template <int NT>
-__device__ __forceinline__ void select_clear(SelectLds<NT> &L) {
-    for (int i = threadIdx.x; i < 4 * 256; i += NT) L.hist[i >> 8][i & 255] = 0;
+template <int NT, int NH>
+__device__ __forceinline__ void select_clear(SelectLds<NT, NH> &L) {
+    for (int i = threadIdx.x; i < NH * 256; i += NT) L.hist[i >> 8][i & 255] = 0;
 }
 
 // Per-thread partial statistics of keys (key 0: invalid column, not counted).
@@ -720,9 +721,9 @@ struct KeyStats {
 // Lane kWave-1 of each wave holds its wave's count of valid keys, smallest and largest
 // valid key; combines them over the workgroup.  Contains one barrier (which also
 // publishes whatever the threads wrote to LDS before the call).
-template <int NT>
+template <int NT, int NH>
 __device__ __forceinline__ void block_stats_combine(uint32_t n, uint32_t mn, uint32_t mx,
-                                                    SelectLds<NT> &L, int &count,
+                                                    SelectLds<NT, NH> &L, int &count,
                                                     uint32_t &kmin, uint32_t &kmax) {
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
     if (lane == kWave - 1) {
@@ -746,8 +747,8 @@ __device__ __forceinline__ void block_stats_combine(uint32_t n, uint32_t mn, uin
 
 // Combines per-thread partials over the workgroup: count of valid keys, smallest and
 // largest valid key (one barrier, see block_stats_combine).
-template <int NT>
-__device__ void block_key_stats(KeyStats p, SelectLds<NT> &L, int &count, uint32_t &kmin,
+template <int NT, int NH>
+__device__ void block_key_stats(KeyStats p, SelectLds<NT, NH> &L, int &count, uint32_t &kmin,
                                 uint32_t &kmax) {
     block_stats_combine<NT>(wave_scan((uint32_t)p.n, 0u, OpAdd{}),
                             wave_scan(p.mn, 0xFFFFFFFFu, OpMin{}), wave_scan(p.mx, 0u, OpMax{}),
@@ -767,8 +768,8 @@ __device__ __forceinline__ bool keys_live(const uint32_t (&key)[KPT]) {
 // false only where every key is 0): the count from wave ballots, and the minimum as
 // 1 + min(key - 1), in which the invalid key 0 wraps to the largest value and drops
 // out without a test.  A wave with no live thread skips the keys.
-template <int NT, int KPT>
-__device__ void block_key_stats(const uint32_t (&key)[KPT], bool live, SelectLds<NT> &L,
+template <int NT, int KPT, int NH>
+__device__ void block_key_stats(const uint32_t (&key)[KPT], bool live, SelectLds<NT, NH> &L,
                                 int &count, uint32_t &kmin, uint32_t &kmax) {
     uint32_t n = 0, mnm1 = 0xFFFFFFFFu, mx = 0u;
     if (__ballot(live) != 0ull) {   // uniform: the whole wave takes it or skips it
@@ -784,6 +785,47 @@ __device__ void block_key_stats(const uint32_t (&key)[KPT], bool live, SelectLds
     kmin += 1u;   // no valid key: 0
 }
 
+// Bucket of h[0, 64*B) that holds the k_rem-th largest key counted in it, scanned from
+// the top by one wave (every wave finds the same answer, so no barrier follows): lane
+// l owns buckets 64B-1-Bl down to 64B-B-Bl.  d is the bucket, before the count above
+// it, c its own count.  h is 16-byte aligned.
+template <int B>
+__device__ __forceinline__ void find_bucket(const int *h, int k_rem, int &d, int &before, int &c) {
+    static_assert(B % 4 == 0, "whole 16-byte reads");
+    const int lane = threadIdx.x & (kWave - 1);
+    const int top = 64 * B - 1 - B * lane;
+    int cnt[B];   // cnt[j]: bucket top - j
+#pragma unroll
+    for (int j = 0; j < B; j += 4) {
+        const int4 x = *reinterpret_cast<const int4 *>(h + top - j - 3);
+        cnt[j] = x.w;
+        cnt[j + 1] = x.z;
+        cnt[j + 2] = x.y;
+        cnt[j + 3] = x.x;
+    }
+    int sum = 0;
+#pragma unroll
+    for (int j = 0; j < B; ++j) sum += cnt[j];
+    const int incl = wave_incl_scan(sum);
+    // exactly one lane's buckets hold the k_rem-th largest key (if any lane's do)
+    int bf = incl - sum, dd = top, cc = cnt[0];
+    bool down = true;
+#pragma unroll
+    for (int j = 1; j < B; ++j) {
+        down = down && bf + cc < k_rem;
+        if (down) {
+            bf += cc;
+            --dd;
+            cc = cnt[j];
+        }
+    }
+    const uint64_t m = __ballot(incl - sum < k_rem && incl >= k_rem);
+    const int src = (int)__builtin_ctzll(m);
+    d = __builtin_amdgcn_readlane(dd, src);
+    before = __builtin_amdgcn_readlane(bf, src);
+    c = __builtin_amdgcn_readlane(cc, src);
+}
+
 // Top-k of one row by one workgroup of NT threads.  Thread i holds the keys of columns
 // [i*KPT, (i+1)*KPT) (key 0: invalid column); column order is ascending token order.
 // live may be false only where all of the thread's keys are 0 (keys_live(key), or a
@@ -793,31 +835,49 @@ __device__ void block_key_stats(const uint32_t (&key)[KPT], bool live, SelectLds
 // the key range still holding it (first [kmin, kmax]): a pass histograms the top 8
 // bits of the range's width, and every wave scans the 256 buckets from the top, so all
 // waves take the same bucket with no second barrier.  The search stops once the chosen
-// bucket is taken whole or is a single key value.  Selected: keys above hi, plus the
+// bucket is taken whole or is a single key value.  With PRE the caller has already
+// counted the valid keys per key >> 23 into hist[0..1] (kmin and kmax unused): that
+// first digit needs no pass over the keys, and three 8-, 8- and 7-bit passes remain.
+// Selected: keys above hi, plus the
 // first k_rem keys in [lo, hi] in column order (ties toward the lower token).
 // tokens(c0, tok) fills the tokens of columns c0 .. c0+KPT-1.  The chosen tokens are
 // placed in column order into stage (LDS, 16-byte aligned, a multiple of 4 ints and at
 // least count_valid of them, free once the keys are in registers) and copied out with
 // coalesced stores: orow[0, topk) gets the chosen tokens ascending, then -1.
-template <int NT, int KPT, class Tokens>
+template <int NT, int KPT, bool PRE = false, int NH = 4, class Tokens>
 __device__ void select_topk(const uint32_t (&key)[KPT], bool live, int count_valid, uint32_t kmin,
-                            uint32_t kmax, int32_t topk, int32_t *orow, SelectLds<NT> &L,
+                            uint32_t kmax, int32_t topk, int32_t *orow, SelectLds<NT, NH> &L,
                             int32_t *stage, Tokens tokens) {
-    static_assert(NT <= 4 * 256, "the histograms double as spare slots, one per thread");
-    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    static_assert(NT <= NH * 256, "the histograms double as spare slots, one per thread");
+    static_assert(!PRE || NH == 5, "a prebuilt first digit takes hist[0..1] and 3 more passes");
+    const int tid = threadIdx.x;
     const int count = min(topk, count_valid);
     uint32_t lo = 1u, hi = 0u;   // every valid key taken
     int k_rem = 0;
     bool whole = true;           // the chosen keys are exactly those >= lo
     if (count < count_valid) {
-        lo = kmin;
-        hi = kmax;
         k_rem = count;
-        for (int pass = 0; pass < 4; ++pass) {
+        whole = false;
+        int first = 0;           // histogram of the next pass
+        if constexpr (PRE) {
+            // hist[0..1] holds the count of valid keys per key >> 23 (sign and
+            // exponent: one bucket per binade); the range then has 23 bits left
+            int d, before, c;
+            find_bucket<8>(&L.hist[0][0], k_rem, d, before, c);
+            lo = max((uint32_t)d << 23, 1u);   // the invalid key 0 stays out
+            hi = ((uint32_t)d << 23) | 0x7FFFFFu;
+            k_rem -= before;
+            whole = c == k_rem;
+            first = 2;
+        } else {
+            lo = kmin;
+            hi = kmax;
+        }
+        for (int pass = first; pass < NH && !whole; ++pass) {
             const uint32_t span = hi - lo;
             const int s = max(0, 24 - __clz((int)span));   // (span >> s) < 256
             int *h = L.hist[pass];
-            if (pass == 0) {
+            if (!PRE && pass == 0) {
                 // No range test: every valid key lies in [kmin, kmax], and the
                 // invalid key 0 saturates into bucket 0.  That can only raise bucket
                 // 0's count: the bucket holding the count-th largest valid key is
@@ -838,27 +898,14 @@ __device__ void select_topk(const uint32_t (&key)[KPT], bool live, int count_val
                 }
             }
             __syncthreads();
-            // lane l owns buckets 255-4l .. 252-4l; exactly one lane's buckets hold
-            // the k_rem-th largest key of the range
-            const int d0 = 255 - 4 * lane;
-            const int c0 = h[d0], c1 = h[d0 - 1], c2 = h[d0 - 2], c3 = h[d0 - 3];
-            const int sum = c0 + c1 + c2 + c3;
-            const int incl = wave_incl_scan(sum);
-            int before = incl - sum, d = d0, c = c0;
-            if (before + c < k_rem) { before += c; --d; c = c1;
-                if (before + c < k_rem) { before += c; --d; c = c2;
-                    if (before + c < k_rem) { before += c; --d; c = c3; } } }
-            const uint64_t m = __ballot(incl - sum < k_rem && incl >= k_rem);
-            const int src = (int)__builtin_ctzll(m);
-            d = __builtin_amdgcn_readlane(d, src);
-            before = __builtin_amdgcn_readlane(before, src);
-            c = __builtin_amdgcn_readlane(c, src);
+            int d, before, c;
+            find_bucket<4>(h, k_rem, d, before, c);
             const uint32_t w = s ? (1u << s) - 1u : 0u;
             lo += (uint32_t)d << s;
             hi = (hi - lo <= w) ? hi : lo + w;
             k_rem -= before;
             whole = c == k_rem;
-            if (whole || s == 0) break;
+            if (s == 0) break;
         }
     }
 
@@ -1025,7 +1072,7 @@ __global__ __launch_bounds__(NT) void fused_row_kernel(Rows rows, const void *qv
     __shared__ int32_t s_si[kMaxNSB];
     __shared__ int32_t s_pg[kMaxNSB];
     __shared__ int s_unit;
-    __shared__ SelectLds<NT> s_sel;
+    __shared__ SelectLds<NT, 5> s_sel;
     const int row = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1);
     const RowInfo ri = row_info(rows, k, s, row);
     QFrag<QF> f;
@@ -1037,7 +1084,10 @@ __global__ __launch_bounds__(NT) void fused_row_kernel(Rows rows, const void *qv
     if (tid == 0) s_unit = 0;
     select_clear(s_sel);
     __syncthreads();
-    KeyStats st;
+    // The selection's first digit is counted while scoring (the scoring waits on
+    // memory, so the extra instructions are free): valid keys per key >> 23.
+    int nv = 0;
+    int *hist0 = &s_sel.hist[0][0];
     // 1024 threads (MXFP4 queries) leave 128 VGPRs a wave: units of one group, two in
     // flight, 16 waves a CU; 512 threads (fp8 queries): 2-group units.
     constexpr int U = NT >= 1024 ? 1 : (QF == 0 ? 4 : 2);
@@ -1065,14 +1115,18 @@ __global__ __launch_bounds__(NT) void fused_row_kernel(Rows rows, const void *qv
             if (c < ri.ncols) {
                 s_logit[c] = v;
                 if (lout) lout[c] = v;
-                st.add(column_key(v));
+                if (v != -INFINITY) {
+                    ++nv;
+                    atomicAdd(hist0 + (ordered_key(v) >> 23), 1);
+                }
             }
         });
     if (lout)
         for (int c = vgroups * 64 + tid; c < ri.ncols; c += NT) lout[c] = -INFINITY;
     int nvalid;
-    uint32_t kmin, kmax;
-    block_key_stats<NT>(st, s_sel, nvalid, kmin, kmax);   // also publishes s_logit, s_si
+    uint32_t kmin, kmax;   // not needed with the first digit counted
+    block_stats_combine<NT>(wave_scan((uint32_t)nv, 0u, OpAdd{}), 0u, 0u, s_sel, nvalid, kmin,
+                            kmax);   // also publishes s_logit, s_si and the first digit
     uint32_t key[KPT];
 #pragma unroll
     for (int i = 0; i < KPT; i += 4) {
@@ -1083,7 +1137,7 @@ __global__ __launch_bounds__(NT) void fused_row_kernel(Rows rows, const void *qv
         key[i + 2] = c + 2 < ri.valid_cols ? column_key(x.z) : 0u;
         key[i + 3] = c + 3 < ri.valid_cols ? column_key(x.w) : 0u;
     }
-    select_topk<NT, KPT>(key, keys_live(key), nvalid, kmin, kmax, topk, out + (int64_t)row * ostride, s_sel,
+    select_topk<NT, KPT, true>(key, keys_live(key), nvalid, kmin, kmax, topk, out + (int64_t)row * ostride, s_sel,
                          reinterpret_cast<int32_t *>(s_logit), SparseTokens<KPT>{s_si, s.lsbk});
 }
 
@@ -1285,10 +1339,15 @@ __global__ __launch_bounds__(kGroupThreads) void row_group_kernel(
 
     for (int i = tid; i < GR * NSB; i += kGroupThreads) {
         const int r = i / NSB, j = i % NSB;
+        // loaded without waiting for kept (in bounds: j < nsb), then masked
         int32_t b = INT_MAX, p = -1;
-        if (j < pick(kept, r)) {
+        if (row0 + r < rows.num_rows && j < s.nsb) {
             b = s.sparse_indices[(int64_t)(row0 + r) * s.nsb + j];
             p = s.pages[(int64_t)(row0 + r) * s.nsb + j];
+        }
+        if (j >= pick(kept, r)) {
+            b = INT_MAX;
+            p = -1;
         }
         lds.si[r][j] = b;
         lds.u.m.pg[r][j] = p;
