@@ -1,6 +1,8 @@
 """Helpers that run the HIP path through the C ABI and compare it with the oracle.
 
-Floating point: |gpu - oracle| <= 1e-6 + 1e-5 * |oracle| for every candidate token.
+Floating point: |gpu - oracle| <= 1e-6 + 1e-5 * |oracle| for every candidate token
+(with signed head weights, 1e-5 * sum_h |w_h| ReLU(s_h) in place of |oracle|: the
+same bound when no weight is negative).
 Indices: with theta the oracle's count-th selected logit and tau = 1e-6 + 1e-5*|theta|,
 the GPU picks exactly count distinct valid tokens in ascending order, every token
 with oracle logit > theta + tau, none with oracle logit < theta - tau, -1 in the
@@ -35,16 +37,21 @@ def exact_topk(tokens, logits, topk):
     return out
 
 
-def check_logits(o_tokens, o_logits, g_tokens, g_logits, what=""):
+def check_logits(o_tokens, o_logits, g_tokens, g_logits, what="", o_scale=None):
+    """o_scale (optional): per token sum_h |w_h| * ReLU(s_h), the oracle run with |w|;
+    the relative tolerance applies to it instead of |logit| (the two are equal when no
+    weight is negative; with signed weights the terms cancel, and a sum's rounding
+    error scales with the magnitudes of its terms, not with the result)."""
     np.testing.assert_array_equal(g_tokens, o_tokens, err_msg=f"{what}: candidate tokens differ")
     err = np.abs(g_logits.astype(np.float64) - o_logits.astype(np.float64))
-    lim = ATOL + RTOL * np.abs(o_logits.astype(np.float64))
+    mag = np.abs(o_logits.astype(np.float64)) if o_scale is None else o_scale.astype(np.float64)
+    lim = ATOL + RTOL * mag
     bad = np.nonzero(err > lim)[0]
     assert bad.size == 0, (f"{what}: {bad.size} logits outside tolerance, first token "
                            f"{o_tokens[bad[0]]}: gpu {g_logits[bad[0]]!r} oracle {o_logits[bad[0]]!r}")
 
 
-def check_indices(o_tokens, o_logits, o_idx, g_idx, topk, what=""):
+def check_indices(o_tokens, o_logits, o_idx, g_idx, topk, what="", o_scale=None):
     n = o_tokens.size
     count = min(topk, n)
     assert np.all(g_idx[count:] == -1), f"{what}: slots past count={count} are not -1"
@@ -58,7 +65,9 @@ def check_indices(o_tokens, o_logits, o_idx, g_idx, topk, what=""):
     ol = o_logits.astype(np.float64)
     o_sel = np.isin(o_tokens, o_idx[:count])
     theta = ol[o_sel].min()
-    tau = ATOL + RTOL * abs(theta)
+    # with o_scale (signed weights), the largest magnitude of the row bounds every
+    # logit's error
+    tau = ATOL + RTOL * (abs(theta) if o_scale is None else float(np.max(o_scale)))
     g_sel = np.zeros(n, bool)
     g_sel[pos] = True
     must = ol > theta + tau
@@ -125,8 +134,9 @@ class GpuRun:
                     kept=self.sched.work[:4 * self.case.num_rows].view(torch.int32).cpu().numpy())
 
 
-def compare_rows(case, res, ora, topk, sbk, what=""):
-    """Compare GPU results (dict from GpuRun.fetch) with an oracle RowResult."""
+def compare_rows(case, res, ora, topk, sbk, what="", ora_scale=None):
+    """Compare GPU results (dict from GpuRun.fetch) with an oracle RowResult; ora_scale
+    (optional) is the oracle's RowResult for the same rows with |w| (see check_logits)."""
     for i, r in enumerate(ora.rows):
         r = int(r)
         tag = f"{what} row {r}"
@@ -134,7 +144,8 @@ def compare_rows(case, res, ora, topk, sbk, what=""):
         gt, gl = gpu_row_tokens(res["sparse_indices"][r], int(res["kept"][r]), sbk, ks, ke,
                                 res["logits"][r])
         assert res["end"][r] == ora.count[i], f"{tag}: end {res['end'][r]} != {ora.count[i]}"
-        check_logits(ora.row_tokens(i), ora.row_logits(i), gt, gl, tag)
+        sc = None if ora_scale is None else ora_scale.row_logits(i)
+        check_logits(ora.row_tokens(i), ora.row_logits(i), gt, gl, tag, sc)
         check_indices(ora.row_tokens(i), ora.row_logits(i), ora.indices[i], res["indices"][r],
-                      topk, tag)
+                      topk, tag, sc)
         check_topk_exact_for_own_logits(gt, gl, res["indices"][r], topk, tag)

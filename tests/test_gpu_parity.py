@@ -24,7 +24,7 @@ def _say(msg):
     print(msg, flush=True)
 
 
-def run_and_compare(case, rows=None, layers=(0,), q_format="mxfp4", sbk=0, tag=""):
+def run_and_compare(case, rows=None, layers=(0,), q_format="mxfp4", sbk=0, tag="", scale_case=None):
     dcase = to_device(case, DEV)
     g = GpuRun(case, dcase, sbk=sbk, q_format=q_format)
     _say(f"[{tag}] expand rows={case.num_rows} sbk={g.sbk} fmt={q_format}")
@@ -39,7 +39,10 @@ def run_and_compare(case, rows=None, layers=(0,), q_format="mxfp4", sbk=0, tag="
         np.testing.assert_array_equal(res["end"], end_o, err_msg=f"{tag}: end")
         pool = case.layers[layer].host_pool(case.spec.page_bytes)
         ora = oracle.indexer_rows(case, layer, rows, q_format, pool=pool)
-        compare_rows(case, res, ora, case.spec.topk, g.sbk, f"{tag} layer {layer}")
+        ora_scale = None
+        if scale_case is not None:   # same inputs with |w|: the tolerance's magnitudes
+            ora_scale = oracle.indexer_rows(scale_case, layer, rows, q_format, pool=pool)
+        compare_rows(case, res, ora, case.spec.topk, g.sbk, f"{tag} layer {layer}", ora_scale)
         # the launch configuration of the benchmark (workspace, no logits output)
         g.out.fill_(-7)
         g.score(layer, with_logits=False)
@@ -120,6 +123,83 @@ def test_row_groups_wide_rows_sampled_and_properties():
                                 int(case.row_ks[i]), int(case.row_ke[i]), res["logits"][i])
         np.testing.assert_array_equal(res["indices"][i], exact_topk(gt, gl, spec.topk),
                                       err_msg=f"wide row {i}")
+
+
+def _reweighted(case, kind, seed):
+    """The case with every layer's head weights replaced.  "signed": U(-1, 1) / 8, so
+    logits take both signs (the negative half of the key order and of the first radix
+    digit); "zero": every logit is +0, one tie across the whole row that only the
+    lower-token rule decides."""
+    import dataclasses
+
+    rng = np.random.default_rng(seed)
+    layers = []
+    for L in case.layers:
+        if kind == "signed":
+            w = ((rng.random(L.weights.shape) * 2.0 - 1.0) / 8.0).astype(np.float32)
+        else:
+            w = np.zeros_like(L.weights)
+        layers.append(dataclasses.replace(L, weights=w))
+    return dataclasses.replace(case, layers=layers)
+
+
+def _dense_indices(g, case, ctx):
+    import sparse_attention_indexer_candidate_amd as idx
+
+    R = case.num_rows
+    dout = torch.full((R, case.spec.topk), -7, dtype=torch.int32, device=DEV)
+    dlog = torch.empty((R, ctx), dtype=torch.float32, device=DEV)
+    L = g.dcase.layers[0]
+    qv, qs = L.q("mxfp4")
+    idx.idx_dense_masked_logits_topk(g.cfg, g.rows, ctx, qv, qs, L.weights, g.kcaches[0],
+                                     g.sched.struct, dout, dout.stride(0), dlog, dlog.stride(0))
+    torch.cuda.synchronize()
+    return dout.cpu().numpy()
+
+
+# one case per scoring/selection kernel: fewer rows than CUs (split scoring, separate
+# selection), at least one row per CU (one workgroup a row), 8+ rows per CU on one
+# table (row groups)
+WEIGHT_PATHS = {
+    "split": SMALL["ragged_sbk64_ks"],
+    "fused": W.Spec(name="wf", num_rows=300, page_size=64, cbs=64, nb=8, topk=200,
+                    ke_rule="uniform", ke_lo=10, ke_hi=1500, ks_rule="random",
+                    cand_rule="messy", fill="all"),
+    "rowgroup": SMALL["rowgroup_shared_table_messy"],
+}
+
+
+@pytest.mark.parametrize("kind", ["signed", "zero"])
+@pytest.mark.parametrize("path", sorted(WEIGHT_PATHS))
+def test_signed_and_zero_weights(path, kind):
+    import dataclasses
+
+    case = _reweighted(W.generate(WEIGHT_PATHS[path], seed=13), kind, seed=17)
+    tag = f"w-{kind}-{path}"
+    mag = dataclasses.replace(case, layers=[dataclasses.replace(L, weights=np.abs(L.weights))
+                                            for L in case.layers])
+    g, res = run_and_compare(case, tag=tag, scale_case=mag)
+    k = case.spec.topk
+    for i in range(case.num_rows):
+        gt, gl = gpu_row_tokens(res["sparse_indices"][i], int(res["kept"][i]), g.sbk,
+                                int(case.row_ks[i]), int(case.row_ke[i]), res["logits"][i])
+        if kind == "zero":
+            assert np.all(gl.view(np.uint32) == 0), f"{tag} row {i}: logits not +0"
+            want = np.full(k, -1, np.int32)
+            n = min(k, gt.size)
+            want[:n] = gt[:n]
+            np.testing.assert_array_equal(res["indices"][i], want, err_msg=f"{tag} row {i}")
+        else:
+            np.testing.assert_array_equal(res["indices"][i], exact_topk(gt, gl, k),
+                                          err_msg=f"{tag} row {i}")
+    if kind == "signed":
+        lg = res["logits"][np.isfinite(res["logits"])]
+        assert (lg < 0).any() and (lg > 0).any(), f"{tag}: logits of one sign only"
+    if path == "split":
+        _say(f"[{tag}] dense")
+        ctx = int(case.row_ke.max() + 63) // 64 * 64
+        np.testing.assert_array_equal(_dense_indices(g, case, ctx), res["indices"],
+                                      err_msg=f"{tag}: dense != sparse indices")
 
 
 def test_config1_tiny_decode_all_rows():
