@@ -231,28 +231,40 @@ def main():
         a.record(stream)
         b.record(stream)
     torch.cuda.synchronize()
+    ev_raw = [(idx.event_handle(a), idx.event_handle(b)) for a, b in ev]
+
+    # Every launch of a step is bound once (arguments marshalled ahead), as a serving
+    # loop would: a step then costs the host one foreign call per launch, so short
+    # steps are not bound by Python.
+    for p in plans:
+        d = p["d"]
+        p["expand"] = idx.bind_expand_candidates(cfg, p["rows"], p["kc"][0], d.candidate_blocks,
+                                                 d.candidate_blocks.stride(0), p["sched"].struct,
+                                                 stream=sh)
+        p["layers"] = []
+        for layer, L in enumerate(d.layers):
+            qv, qs = L.q(args.q_format)
+            if args.path == "dense":
+                call = idx.bind_dense_masked_logits_topk(
+                    cfg, p["rows"], max_ctx, qv, qs, L.weights, p["kc"][layer], p["sched"].struct,
+                    p["out"], p["out"].stride(0), None, 0, p["ws"], p["ws"].numel(), stream=sh)
+            else:
+                call = idx.bind_sparse_mqa_logits_topk(
+                    cfg, p["rows"], qv, qs, L.weights, p["kc"][layer], p["sched"].struct,
+                    p["out"], p["out"].stride(0), None, p["ws"], p["ws"].numel(), stream=sh)
+            p["layers"].append(call)
+    set_events = idx.lib.idx_set_timing_events
 
     def step(i, timed):
         p = plans[i % nrep]
-        d = p["d"]
         timed = timed and i % TIMING_STRIDE == 0
-        idx.idx_expand_candidates(cfg, p["rows"], p["kc"][0], d.candidate_blocks,
-                                  d.candidate_blocks.stride(0), p["sched"].struct, stream=sh)
-        for layer, L in enumerate(d.layers):
-            qv, qs = L.q(args.q_format)
+        p["expand"]()
+        for layer, call in enumerate(p["layers"]):
             if timed:
-                idx.idx_set_timing_events(*ev[(i // TIMING_STRIDE) * spec.layers + layer])
-            if args.path == "dense":
-                idx.idx_dense_masked_logits_topk(cfg, p["rows"], max_ctx, qv, qs, L.weights,
-                                                 p["kc"][layer], p["sched"].struct, p["out"],
-                                                 p["out"].stride(0), None, 0, p["ws"],
-                                                 p["ws"].numel(), stream=sh)
-            else:
-                idx.idx_sparse_mqa_logits_topk(cfg, p["rows"], qv, qs, L.weights, p["kc"][layer],
-                                               p["sched"].struct, p["out"], p["out"].stride(0),
-                                               None, p["ws"], p["ws"].numel(), stream=sh)
+                set_events(*ev_raw[(i // TIMING_STRIDE) * spec.layers + layer])
+            call()
             if timed:
-                idx.idx_set_timing_events()
+                set_events(None, None)
 
     for i in range(args.warmup):
         step(i, False)

@@ -172,6 +172,63 @@ def idx_dense_masked_logits_topk(cfg, rows, max_ctx, q_values, q_scales, weights
         logits_stride, _p(workspace), workspace_bytes, _p(stream)))
 
 
+# ------------------------------------------------- calls bound ahead of time --
+
+class BoundCall:
+    """One C entry point with its arguments marshalled once: pointers are read from the
+    tensors when the call is bound, so they must stay alive and in place.  Calling it
+    costs one foreign call (a serving or benchmark loop repeats the same launch)."""
+
+    __slots__ = ("fn", "args", "keep")
+
+    def __init__(self, fn, args, keep):
+        self.fn = fn
+        self.args = tuple(args)
+        self.keep = keep            # the structs the byref arguments point at
+
+    def __call__(self) -> int:
+        rc = self.fn(*self.args)
+        if rc < 0:
+            raise IdxError(rc, idx_last_error())
+        return rc
+
+
+def bind_expand_candidates(cfg, rows, k, candidate_blocks, cand_stride, sched, stream=None):
+    return BoundCall(lib.idx_expand_candidates,
+                     (ctypes.byref(cfg), ctypes.byref(rows), ctypes.byref(k),
+                      ctypes.c_void_p(_p(candidate_blocks)), cand_stride, ctypes.byref(sched),
+                      ctypes.c_void_p(_p(stream))), (cfg, rows, k, sched))
+
+
+def bind_sparse_mqa_logits_topk(cfg, rows, q_values, q_scales, weights, k, sched, topk_indices,
+                                out_stride, logits_out=None, workspace=None, workspace_bytes=0,
+                                stream=None):
+    vp = lambda x: ctypes.c_void_p(_p(x))
+    return BoundCall(lib.idx_sparse_mqa_logits_topk,
+                     (ctypes.byref(cfg), ctypes.byref(rows), vp(q_values), vp(q_scales),
+                      vp(weights), ctypes.byref(k), ctypes.byref(sched), vp(topk_indices),
+                      out_stride, vp(logits_out), vp(workspace), workspace_bytes, vp(stream)),
+                     (cfg, rows, k, sched))
+
+
+def bind_dense_masked_logits_topk(cfg, rows, max_ctx, q_values, q_scales, weights, k, sched,
+                                  topk_indices, out_stride, logits_out=None, logits_stride=0,
+                                  workspace=None, workspace_bytes=0, stream=None):
+    vp = lambda x: ctypes.c_void_p(_p(x))
+    return BoundCall(lib.idx_dense_masked_logits_topk,
+                     (ctypes.byref(cfg), ctypes.byref(rows), max_ctx, vp(q_values), vp(q_scales),
+                      vp(weights), ctypes.byref(k), ctypes.byref(sched), vp(topk_indices),
+                      out_stride, vp(logits_out), logits_stride, vp(workspace), workspace_bytes,
+                      vp(stream)), (cfg, rows, k, sched))
+
+
+def event_handle(e):
+    """Raw HIP event handle of a torch.cuda.Event (created on first use)."""
+    if not e.cuda_event:
+        e.record()
+    return e.cuda_event
+
+
 # ------------------------------------------------------------- torch glue ---
 
 def _p(x):

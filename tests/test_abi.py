@@ -190,3 +190,26 @@ def test_one_hip_runtime_per_process():
                          timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip().splitlines()[-1] == "1", out.stdout
+
+
+def test_bound_calls_check_arguments_like_the_wrappers():
+    """Calls bound ahead of time pass the same arguments to the same C entry points."""
+    c = idx.idx_check_config(cfg())
+    ok = idx.bind_sparse_mqa_logits_topk(c, rows(0), FAKE, FAKE, FAKE, kcache(), sched(), FAKE,
+                                         2048, FAKE)
+    assert ok() == idx.IDX_OK   # zero rows: nothing to launch
+    bad = idx.bind_sparse_mqa_logits_topk(c, rows(2), None, FAKE, FAKE, kcache(), sched(), FAKE,
+                                          2048, FAKE)
+    with pytest.raises(idx.IdxError) as e:
+        bad()
+    assert e.value.code == idx.IDX_EINVAL
+    short = idx.bind_sparse_mqa_logits_topk(c, rows(2), FAKE, FAKE, FAKE, kcache(), sched(), FAKE,
+                                            2048, None, FAKE, 1000)
+    with pytest.raises(idx.IdxError) as e:
+        short()
+    assert e.value.code == idx.IDX_EWORKSPACE
+    assert idx.bind_expand_candidates(c, rows(0), kcache(), FAKE, 64, sched())() == idx.IDX_OK
+    dense = idx.bind_dense_masked_logits_topk(c, rows(2), 0, FAKE, FAKE, FAKE, kcache(), sched(),
+                                              FAKE, 2048, FAKE, 0)
+    with pytest.raises(idx.IdxError):
+        dense()
