@@ -103,7 +103,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, help="workload 1-5 (default 2)")
+    ap.add_argument("--config", type=int, default=2,
+                    help="workload 1-5 (default 2); 6: decode with two rows per request")
     ap.add_argument("--q-format", default="mxfp4", choices=["mxfp4", "fp8"])
     ap.add_argument("--path", default="sparse", choices=["sparse", "dense"],
                     help="sparse: idx_sparse_mqa_logits_topk; dense: the comparator "

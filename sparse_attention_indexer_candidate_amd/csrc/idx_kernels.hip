@@ -1038,7 +1038,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(Rows rows, KCa
     for (int i = 0; i < KPT; i += 4) {
         const int c = tid * KPT + i;
         float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-        if (c < ri.ncols) v = *(const float4 *)(lrow + c);   // every column is written
+        if (c < ri.valid_cols) v = *(const float4 *)(lrow + c);   // the kept blocks' columns
         x[i] = v.x;
         x[i + 1] = v.y;
         x[i + 2] = v.z;

@@ -202,6 +202,31 @@ def test_signed_and_zero_weights(path, kind):
                                       err_msg=f"{tag}: dense != sparse indices")
 
 
+# Decode rows in requests of next_n on one table row (MTP / speculative rows) with
+# overlapping candidate lists: ragged request counts, ks > 0, 4096- and 8192-column
+# shapes, long requests.
+MTP = {
+    "n2": W.Spec(name="m2", num_rows=40, nb=16, topk=300, ke_rule="uniform", ke_lo=200,
+                 ke_hi=3000, cand_rule="mtp_overlap", next_n=2, fill="all"),
+    "n3_ks": W.Spec(name="m3", num_rows=33, nb=12, topk=200, ke_rule="uniform", ke_lo=100,
+                    ke_hi=2500, ks_rule="random", cand_rule="mtp_overlap", next_n=3,
+                    fill="all"),
+    "n4_wide": W.Spec(name="m4", num_rows=24, nb=100, topk=1000, ke_rule="uniform",
+                      ke_lo=3000, ke_hi=9000, cand_rule="mtp_overlap", next_n=4, fill="all"),
+    "n8": W.Spec(name="m8", num_rows=32, nb=20, topk=400, ke_rule="uniform", ke_lo=500,
+                 ke_hi=4000, cand_rule="mtp_overlap", next_n=8, mtp_resample=0.5, fill="all"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MTP))
+def test_mtp_decode_rows_share_k(name):
+    run_and_compare(W.generate(MTP[name], seed=21), tag=name)
+
+
+def test_config6_mtp_decode_all_rows():
+    run_and_compare(W.generate(W.config(6), 0), tag="cfg6")
+
+
 def test_config1_tiny_decode_all_rows():
     run_and_compare(W.generate(W.config(1), 0), tag="cfg1")
 

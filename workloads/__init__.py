@@ -18,6 +18,11 @@ Input model (stated once, used everywhere):
 * fp8 Q variant: x ~ N(0, 1) per element, one fp32 scale per row
   ``s_r = max|x_r| / 448``, codes = e4m3fn round-to-nearest-even of ``x / s_r``.
 * weights: U(0, 1) / 8, fp32, one per (row, head).
+* Decode rows of one request (``next_n`` > 1, MTP / speculative rows): the request's
+  context end is drawn by ``ke_rule`` and row j of it ends j positions later; the
+  request has one table row; with ``cand_rule="mtp_overlap"`` row 0 takes distinct
+  random blocks and each later row keeps row 0's list but redraws each entry with
+  probability ``mtp_resample`` from the blocks not yet listed.
 * Paged K cache: pages of ``page_size`` tokens; a page holds the packed values
   ``[page_size][D/2]`` followed by the scale bytes ``[page_size][D/32]``.  The pool
   has ceil(1.25 x needed) pages; logical pages of every table row map to a random
@@ -124,6 +129,10 @@ class Spec:
     scale_exp: tuple = (-4, 4)
     pool_factor: float = 1.25
     row_offset: int = 0               # prefill: position of row 0 in the request (causal ke = offset+i+1)
+    next_n: int = 1                   # decode: rows per request (MTP / speculative rows) on one
+                                      # table row; row j of a request has ke = the request's + j
+    mtp_resample: float = 0.25        # cand_rule "mtp_overlap": share of row 0's blocks that
+                                      # each later row of the request draws anew
 
     @property
     def page_bytes(self) -> int:
@@ -173,6 +182,14 @@ class Case:
 
 
 def _draw_context(spec: Spec, rng: np.random.Generator):
+    if spec.next_n > 1:
+        # requests of next_n rows: the request's end drawn by the rule, row j one further
+        n = spec.next_n
+        if spec.mode != "decode" or spec.num_rows % n:
+            raise ValueError("next_n > 1 needs decode rows in whole requests")
+        ks_req, ke_req = _draw_context(replace(spec, num_rows=spec.num_rows // n, next_n=1), rng)
+        j = np.arange(spec.num_rows) % n
+        return np.repeat(ks_req, n), np.repeat(ke_req, n) + j
     R = spec.num_rows
     if spec.ke_rule == "fixed":
         ke = np.full(R, spec.ke_lo, dtype=np.int64)
@@ -200,7 +217,11 @@ def _draw_context(spec: Spec, rng: np.random.Generator):
 
 def _draw_block_table(spec: Spec, ke: np.ndarray, rng: np.random.Generator):
     ps = spec.page_size
-    if spec.mode == "decode":
+    if spec.mode == "decode" and spec.next_n > 1:
+        n = spec.next_n                           # one table row per request
+        pages = [(int(ke[r + n - 1]) + ps - 1) // ps for r in range(0, spec.num_rows, n)]
+        row_table = (np.arange(spec.num_rows) // n).astype(np.int32)
+    elif spec.mode == "decode":
         pages = [(int(k) + ps - 1) // ps for k in ke]
         row_table = np.arange(spec.num_rows, dtype=np.int32)
     elif spec.mode == "prefill":
@@ -239,6 +260,21 @@ def _draw_candidates(spec: Spec, ks, ke, rng: np.random.Generator):
                 ids = rng.permutation(nblk)
             else:
                 ids = rng.choice(nblk, size=nb, replace=False)
+        elif spec.cand_rule == "mtp_overlap":
+            # row 0 of a request: distinct random blocks; a later row keeps row 0's list
+            # but draws each entry anew (from blocks not yet listed) with probability
+            # mtp_resample
+            take = min(nb, nblk)
+            if r % spec.next_n == 0 or take == 0:
+                ids = rng.choice(nblk, size=take, replace=False) if take else []
+            else:
+                ids = cand[r - r % spec.next_n][:take].astype(np.int64).copy()
+                ids = ids[ids >= 0]
+                redraw = rng.random(ids.size) < spec.mtp_resample
+                free = np.setdiff1d(np.arange(nblk), ids)
+                m = min(int(redraw.sum()), free.size)
+                ids[np.nonzero(redraw)[0][:m]] = rng.choice(free, size=m, replace=False)
+                ids = rng.permutation(ids)
         elif spec.cand_rule == "messy":
             # duplicates, -1/-2 padding and blocks past ke all appear
             ids = rng.integers(-2, nblk + 3, size=nb)
@@ -370,6 +406,10 @@ CONFIGS = {
     5: Spec(name="sparse_vs_dense_r128_ctx64k_c4096_k2048", num_rows=128, nb=64, topk=2048,
             ke_rule="fixed", ke_lo=65536, ke_hi=65536, cand_rule="distinct", fill="all",
             q_formats=("mxfp4", "fp8")),
+    # Beyond the five: decode with two rows per request (MTP / speculative rows on the
+    # request's table row), the shape of the decode batch with 64 requests.
+    6: Spec(name="mtp_decode_req64_n2_ctx8k-32k_c4096_k2048", num_rows=128, nb=64, topk=2048,
+            ke_rule="uniform", ke_lo=8192, ke_hi=32768, cand_rule="mtp_overlap", next_n=2),
 }
 
 
