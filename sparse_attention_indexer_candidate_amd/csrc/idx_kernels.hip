@@ -544,7 +544,9 @@ __device__ __forceinline__ void score_groups(const KCache &k, const QFrag<QF> &f
 // unit's K loads are issued before the current one computes.  Tile descriptors come
 // from desc (read from LDS by the caller); loads are branch-free as in score_groups (a
 // tile with nothing to score, or a unit past the end, reads the pool's first bytes and
-// its result is dropped).  sink(c, logit) receives every column of the units scored.
+// its result is dropped).  sink(c, logit, valid) receives every column of the units
+// scored; valid says whether the column is a token of [ks, ke) (logit is meaningless
+// otherwise).
 template <int QF, int U, class Desc, class Grab, class Sink>
 __device__ __forceinline__ void score_units(const KCache &k, const QFrag<QF> &f, int ks, int ke,
                                             Desc desc, Grab grab, Sink sink) {
@@ -593,7 +595,7 @@ __device__ __forceinline__ void score_units(const KCache &k, const QFrag<QF> &f,
             const float lg = reduce_transpose4(p[0], p[1], p[2], p[3]);
             const int tok = __shfl(ttok, q * 4 + g, kWave) + n;
             const bool valid = ((okmask >> (q * 4 + g)) & 1) && tok >= ks && tok < ke;
-            sink((u * U + q) * 64 + lane, valid ? lg : -INFINITY);
+            sink((u * U + q) * 64 + lane, lg, valid);
         }
     };
     KTile ka[U][4], kb[U][4];
@@ -677,8 +679,8 @@ __device__ __forceinline__ uint32_t ordered_key(float x) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Column words of the row-group kernel's LDS: a valid column holds its logit's bits,
-// any other kNoColumn (a NaN pattern, taken to mean "no logit").  bits_key is
+// Column words in LDS (the one-row and row-group kernels): a valid column holds its
+// logit's bits, any other kNoColumn (a NaN pattern, taken to mean "no logit").  bits_key is
 // ordered_key on such a word without the -0 step (a scored logit is never -0: each
 // head sum starts from +0 and adds w * ReLU terms, and a round-to-nearest sum is -0
 // only when both operands are); it takes kNoColumn to the invalid key 0 by itself,
@@ -1015,14 +1017,10 @@ struct SparseTokens {
     }
 };
 
-// Key of a scored column: the scoring writes -inf where the column is not a valid
-// token, which becomes the invalid key 0.
-__device__ __forceinline__ uint32_t column_key(float x) {
-    return x == -INFINITY ? 0u : ordered_key(x);
-}
-
 // Selection for rows scored by score_split_kernel: keys from the global logits
-// (loaded before anything else so their latency overlaps the schedule load).
+// (loaded before anything else so their latency overlaps the schedule load).  A
+// column is valid when it lies in a kept block and its token in [ks, ke); the logit's
+// value plays no part (a valid -inf logit is selectable, the lowest of all).
 __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(Rows rows, KCache k, Schedule s,
                                                                   const float *logits, int32_t topk,
                                                                   int32_t *out, int64_t ostride) {
@@ -1033,24 +1031,28 @@ __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(Rows rows, KCa
     const int row = blockIdx.x, tid = threadIdx.x;
     const RowInfo ri = row_info(rows, k, s, row);
     const float *lrow = logits + (int64_t)row * ri.ncols;
+    const int c0 = tid * KPT;   // the thread's KPT columns lie in one sparse block
     float x[KPT];
 #pragma unroll
     for (int i = 0; i < KPT; i += 4) {
-        const int c = tid * KPT + i;
-        float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-        if (c < ri.valid_cols) v = *(const float4 *)(lrow + c);   // the kept blocks' columns
+        float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (c0 + i < ri.valid_cols) v = *(const float4 *)(lrow + c0 + i);   // kept blocks only
         x[i] = v.x;
         x[i + 1] = v.y;
         x[i + 2] = v.z;
         x[i + 3] = v.w;
     }
+    int tok0 = 0;               // token of column c0
+    if (c0 < ri.valid_cols) tok0 = (ri.si[c0 >> s.lsbk] << s.lsbk) + (c0 & (s.sbk - 1));
     for (int i = tid; i < ri.kept; i += kTopkThreads) s_si[i] = ri.si[i];
     select_clear(s_sel);
     uint32_t key[KPT];
     KeyStats st;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-        key[i] = column_key(x[i]);
+        const int t = tok0 + i;
+        const bool valid = c0 + i < ri.valid_cols && t >= ri.ks && t < ri.ke;
+        key[i] = valid ? ordered_key(x[i]) : 0u;
         st.add(key[i]);
     }
     int nvalid;
@@ -1068,7 +1070,7 @@ __global__ __launch_bounds__(NT) void fused_row_kernel(Rows rows, const void *qv
                                                        const float *weights, KCache k, Schedule s,
                                                        float *logits_out, int32_t topk,
                                                        int32_t *out, int64_t ostride) {
-    __shared__ alignas(16) float s_logit[kMaxRowCols];
+    __shared__ alignas(16) uint32_t s_word[kMaxRowCols];   // column words (bits_key), then the stage
     __shared__ int32_t s_si[kMaxNSB];
     __shared__ int32_t s_pg[kMaxNSB];
     __shared__ int s_unit;
@@ -1111,13 +1113,14 @@ __global__ __launch_bounds__(NT) void fused_row_kernel(Rows rows, const void *qv
             u = uniform(u);
             return u < nunits ? u : -1;
         },
-        [&](int c, float v) {
+        [&](int c, float lg, bool valid) {
             if (c < ri.ncols) {
-                s_logit[c] = v;
-                if (lout) lout[c] = v;
-                if (v != -INFINITY) {
+                const uint32_t w = valid ? __float_as_uint(lg) : kNoColumn;
+                s_word[c] = w;
+                if (lout) lout[c] = valid ? lg : -INFINITY;
+                if (valid) {
                     ++nv;
-                    atomicAdd(hist0 + (ordered_key(v) >> 23), 1);
+                    atomicAdd(hist0 + (bits_key(w) >> 23), 1);
                 }
             }
         });
@@ -1126,19 +1129,19 @@ __global__ __launch_bounds__(NT) void fused_row_kernel(Rows rows, const void *qv
     int nvalid;
     uint32_t kmin, kmax;   // not needed with the first digit counted
     block_stats_combine<NT>(wave_scan((uint32_t)nv, 0u, OpAdd{}), 0u, 0u, s_sel, nvalid, kmin,
-                            kmax);   // also publishes s_logit, s_si and the first digit
+                            kmax);   // also publishes s_word, s_si and the first digit
     uint32_t key[KPT];
 #pragma unroll
     for (int i = 0; i < KPT; i += 4) {
         const int c = tid * KPT + i;   // columns past valid_cols: stale LDS, read but not used
-        const float4 x = *reinterpret_cast<const float4 *>(&s_logit[c]);
-        key[i] = c < ri.valid_cols ? column_key(x.x) : 0u;
-        key[i + 1] = c + 1 < ri.valid_cols ? column_key(x.y) : 0u;
-        key[i + 2] = c + 2 < ri.valid_cols ? column_key(x.z) : 0u;
-        key[i + 3] = c + 3 < ri.valid_cols ? column_key(x.w) : 0u;
+        const uint4 x = *reinterpret_cast<const uint4 *>(&s_word[c]);
+        key[i] = c < ri.valid_cols ? bits_key(x.x) : 0u;
+        key[i + 1] = c + 1 < ri.valid_cols ? bits_key(x.y) : 0u;
+        key[i + 2] = c + 2 < ri.valid_cols ? bits_key(x.z) : 0u;
+        key[i + 3] = c + 3 < ri.valid_cols ? bits_key(x.w) : 0u;
     }
     select_topk<NT, KPT, true>(key, keys_live(key), nvalid, kmin, kmax, topk, out + (int64_t)row * ostride, s_sel,
-                         reinterpret_cast<int32_t *>(s_logit), SparseTokens<KPT>{s_si, s.lsbk});
+                         reinterpret_cast<int32_t *>(s_word), SparseTokens<KPT>{s_si, s.lsbk});
 }
 
 // Dense scoring (the comparator): column t is token t, every token < max_ctx.

@@ -43,9 +43,13 @@ def check_logits(o_tokens, o_logits, g_tokens, g_logits, what="", o_scale=None):
     weight is negative; with signed weights the terms cancel, and a sum's rounding
     error scales with the magnitudes of its terms, not with the result)."""
     np.testing.assert_array_equal(g_tokens, o_tokens, err_msg=f"{what}: candidate tokens differ")
-    err = np.abs(g_logits.astype(np.float64) - o_logits.astype(np.float64))
-    mag = np.abs(o_logits.astype(np.float64)) if o_scale is None else o_scale.astype(np.float64)
-    lim = ATOL + RTOL * mag
+    g64, o64 = g_logits.astype(np.float64), o_logits.astype(np.float64)
+    same = g64 == o64                     # also equal infinities (overflowed sums)
+    with np.errstate(invalid="ignore"):
+        err = np.where(same, 0.0, np.abs(g64 - o64))
+    err[np.isnan(err)] = np.inf           # a NaN on either side never matches
+    mag = np.abs(o64) if o_scale is None else o_scale.astype(np.float64)
+    lim = ATOL + RTOL * np.where(np.isfinite(mag), mag, 0.0)
     bad = np.nonzero(err > lim)[0]
     assert bad.size == 0, (f"{what}: {bad.size} logits outside tolerance, first token "
                            f"{o_tokens[bad[0]]}: gpu {g_logits[bad[0]]!r} oracle {o_logits[bad[0]]!r}")
@@ -65,9 +69,15 @@ def check_indices(o_tokens, o_logits, o_idx, g_idx, topk, what="", o_scale=None)
     ol = o_logits.astype(np.float64)
     o_sel = np.isin(o_tokens, o_idx[:count])
     theta = ol[o_sel].min()
+    if not np.isfinite(theta):
+        # the count-th logit is -inf: every finite logit is taken and the -inf ones go
+        # by token order, so the set is exact
+        np.testing.assert_array_equal(chosen, o_idx[:count], err_msg=f"{what}: set differs")
+        return
     # with o_scale (signed weights), the largest magnitude of the row bounds every
     # logit's error
-    tau = ATOL + RTOL * (abs(theta) if o_scale is None else float(np.max(o_scale)))
+    fin = o_scale[np.isfinite(o_scale)] if o_scale is not None else None
+    tau = ATOL + RTOL * (abs(theta) if o_scale is None else float(np.max(fin, initial=0.0)))
     g_sel = np.zeros(n, bool)
     g_sel[pos] = True
     must = ol > theta + tau

@@ -202,6 +202,56 @@ def test_signed_and_zero_weights(path, kind):
                                       err_msg=f"{tag}: dense != sparse indices")
 
 
+def _overflowed(case, frac, seed):
+    """The case with a fraction of its K tokens made to overflow: every query head's
+    first 32-element block is 1.0 at scale 2^13 (the other blocks keep their codes at
+    that scale), the chosen tokens' first block is 6.0 at scale 2^127, and every head
+    weight is negative, so those tokens' logits are -inf in fp32 (GPU accumulation and
+    the oracle's fp64 sum rounded to fp32 alike) while the other logits stay finite."""
+    import dataclasses
+
+    s = case.spec
+    rng = np.random.default_rng(seed)
+    vb = s.values_bytes
+    layers = []
+    for L in case.layers:
+        qv = L.q_values.copy()
+        qv[:, :, :16] = 0x22                      # e2m1 1.0 in both nibbles
+        qs = np.full_like(L.q_scales, 127 + 13)
+        data = L.filled_data.copy()
+        hit = rng.random((data.shape[0], s.page_size)) < frac
+        for p, slot in zip(*np.nonzero(hit)):
+            data[p, slot * (s.head_dim // 2):slot * (s.head_dim // 2) + 16] = 0x77   # 6.0
+            data[p, vb + slot * (s.head_dim // 32)] = 254                          # 2^127
+        w = -(rng.random(L.weights.shape) / 8.0 + 1e-3).astype(np.float32)
+        layers.append(dataclasses.replace(L, q_values=qv, q_scales=qs, filled_data=data,
+                                          weights=w))
+    return dataclasses.replace(case, layers=layers)
+
+
+@pytest.mark.parametrize("path", sorted(WEIGHT_PATHS))
+def test_valid_columns_with_infinite_logits(path):
+    """A valid column whose logit overflowed to -inf is still a candidate (the lowest):
+    it is selected when k reaches it, exactly as the oracle selects it."""
+    case = _overflowed(W.generate(WEIGHT_PATHS[path], seed=13), frac=0.03, seed=19)
+    tag = f"inf-{path}"
+    g, res = run_and_compare(case, tag=tag)
+    ora = oracle.indexer_rows(case, 0, None, "mxfp4",
+                              pool=case.layers[0].host_pool(case.spec.page_bytes))
+    n_inf = n_chosen = 0
+    for i in range(case.num_rows):
+        gt, gl = gpu_row_tokens(res["sparse_indices"][i], int(res["kept"][i]), g.sbk,
+                                int(case.row_ks[i]), int(case.row_ke[i]), res["logits"][i])
+        ol = ora.row_logits(i)
+        np.testing.assert_array_equal(np.isneginf(gl), np.isneginf(ol),
+                                      err_msg=f"{tag} row {i}: -inf columns differ")
+        assert not np.isnan(gl).any(), f"{tag} row {i}: NaN logit"
+        np.testing.assert_array_equal(res["indices"][i], ora.indices[i], err_msg=f"{tag} row {i}")
+        n_inf += int(np.isneginf(ol).sum())
+        n_chosen += int(np.isin(gt[np.isneginf(gl)], res["indices"][i]).sum())
+    assert n_inf > 0 and n_chosen > 0, f"{tag}: no -inf column ({n_inf}) or none chosen ({n_chosen})"
+
+
 # Decode rows in requests of next_n on one table row (MTP / speculative rows) with
 # overlapping candidate lists: ragged request counts, ks > 0, 4096- and 8192-column
 # shapes, long requests.
