@@ -1031,35 +1031,41 @@ __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(Rows rows, KCa
     const int row = blockIdx.x, tid = threadIdx.x;
     const RowInfo ri = row_info(rows, k, s, row);
     const float *lrow = logits + (int64_t)row * ri.ncols;
+    // Loads bounded by the row's column count, not its kept count, so none waits for
+    // the kept load; columns past the kept blocks are masked below.
     const int c0 = tid * KPT;   // the thread's KPT columns lie in one sparse block
     float x[KPT];
 #pragma unroll
     for (int i = 0; i < KPT; i += 4) {
         float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        if (c0 + i < ri.valid_cols) v = *(const float4 *)(lrow + c0 + i);   // kept blocks only
+        if (c0 + i < ri.ncols) v = *(const float4 *)(lrow + c0 + i);   // every column written
         x[i] = v.x;
         x[i + 1] = v.y;
         x[i + 2] = v.z;
         x[i + 3] = v.w;
     }
     int tok0 = 0;               // token of column c0
-    if (c0 < ri.valid_cols) tok0 = (ri.si[c0 >> s.lsbk] << s.lsbk) + (c0 & (s.sbk - 1));
+    if (c0 < ri.ncols) tok0 = (ri.si[c0 >> s.lsbk] << s.lsbk) + (c0 & (s.sbk - 1));
     for (int i = tid; i < ri.kept; i += kTopkThreads) s_si[i] = ri.si[i];
     select_clear(s_sel);
+    // The valid columns of the thread (in a kept block, token in [ks, ke)) are one run
+    // [c0 + lo, c0 + hi): a bit mask, so no key needs a branch.  The scoring never
+    // writes -0 (see bits_key).
+    static_assert(KPT < 32, "one mask bit per key");
+    const int lo = min(KPT, max(0, ri.ks - tok0));
+    const int hi = max(0, min(min(KPT, ri.valid_cols - c0), ri.ke - tok0));
+    const uint32_t vmask = ((1u << hi) - 1u) & ~((1u << lo) - 1u);
     uint32_t key[KPT];
-    KeyStats st;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-        const int t = tok0 + i;
-        const bool valid = c0 + i < ri.valid_cols && t >= ri.ks && t < ri.ke;
-        key[i] = valid ? ordered_key(x[i]) : 0u;
-        st.add(key[i]);
-    }
+    for (int i = 0; i < KPT; ++i)
+        key[i] = bits_key(__float_as_uint(x[i])) & (0u - ((vmask >> i) & 1u));
+    const bool live = vmask != 0u;
     int nvalid;
     uint32_t kmin, kmax;
-    block_key_stats<kTopkThreads>(st, s_sel, nvalid, kmin, kmax);
-    select_topk<kTopkThreads, KPT>(key, keys_live(key), nvalid, kmin, kmax, topk, out + (int64_t)row * ostride,
-                                   s_sel, s_stage, SparseTokens<KPT>{s_si, s.lsbk});
+    block_key_stats<kTopkThreads>(key, live, s_sel, nvalid, kmin, kmax);
+    select_topk<kTopkThreads, KPT>(key, live, nvalid, kmin, kmax, topk,
+                                   out + (int64_t)row * ostride, s_sel, s_stage,
+                                   SparseTokens<KPT>{s_si, s.lsbk});
 }
 
 // Rows >= CUs: one workgroup per row; waves take units of the row's valid 64-column
