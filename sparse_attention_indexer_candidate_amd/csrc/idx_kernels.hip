@@ -7,7 +7,8 @@
 //                       [64 heads x 128] . [128 x 16 tokens], ReLU, fp32 weighted head
 //                       reduce; one wave per 64-column group, K loads batched
 //  select_topk          per-row radix select on fp32 logits, ties toward the lower
-//                       column, ascending output, -1 fill (one workgroup per row)
+//                       column, ascending output, -1 fill (one workgroup per row);
+//                       validity comes from the tokens, never from a logit's value
 //  row_group_kernel     >= 8 rows per CU with MXFP4 queries (prefill chunks): 2 rows
 //                       per workgroup share K tiles; logits in LDS, selected in turn
 //  fused_row_kernel     rows >= CUs otherwise: one workgroup scores a whole row into LDS
@@ -1253,8 +1254,8 @@ __global__ __launch_bounds__(kDenseTopkThreads) void dense_topk_kernel(Rows rows
 // tile load feeds GR x 4 MFMAs instead of 4.  Logits stay in LDS; the whole workgroup
 // then selects the rows in turn (select_topk, 16 keys a thread: a quarter of the steps
 // one wave would take).  Rows on different table rows are merged one row at a time (no
-// sharing).  GR = 2 with the weights in LDS keeps a wave at 123 VGPRs and the LDS near
-// 37 KB, so four workgroups share a CU.
+// sharing).  GR = 2 with the weights in LDS keeps a wave under 128 VGPRs and the LDS
+// near 38 KB, so four workgroups share a CU.
 
 constexpr int kGroupWaves = 4;
 constexpr int kGroupThreads = kGroupWaves * kWave;

@@ -125,6 +125,44 @@ def test_row_groups_wide_rows_sampled_and_properties():
                                       err_msg=f"wide row {i}")
 
 
+def _random_spec(i):
+    """A seeded random shape for the kernel path i % 3 (split, one row per workgroup,
+    row groups): block and page sizes, k, ranges, candidate mess and weight sign vary."""
+    rng = np.random.default_rng(1000 + i)
+    path = i % 3
+    cbs = int(rng.choice([16, 32, 64, 128] if path != 2 else [64, 128]))
+    sbk = 64 if cbs % 64 == 0 else cbs
+    page_size = int(rng.choice([p for p in (16, 32, 64, 128) if p % sbk == 0]))
+    nb = int(rng.integers(1, max(2, min(24, 3000 // cbs))))
+    topk = int(rng.integers(1, nb * cbs + 1))
+    rows = [int(rng.integers(1, 200)), int(rng.integers(256, 360)), 2048 + int(rng.integers(0, 40))][path]
+    ke_hi = int(rng.integers(64, 5000))
+    common = dict(name=f"rand{i}", num_rows=rows, page_size=page_size, cbs=cbs, nb=nb, topk=topk,
+                  ks_rule=str(rng.choice(["zero", "random"])), fill="all",
+                  cand_rule=str(rng.choice(["messy", "distinct"])))
+    if path == 2:   # rows on one table (a prefill chunk's shape)
+        return W.Spec(mode="prefill", ke_rule="uniform", ke_lo=1, ke_hi=ke_hi, context=ke_hi,
+                      **common), bool(rng.random() < 0.5)
+    return W.Spec(ke_rule="uniform", ke_lo=int(rng.integers(0, ke_hi)), ke_hi=ke_hi,
+                  **common), bool(rng.random() < 0.5)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_shapes_all_rows(i):
+    import dataclasses
+
+    spec, signed = _random_spec(i)
+    case = W.generate(spec, seed=i)
+    scale_case = None
+    if signed:
+        case = _reweighted(case, "signed", seed=i)
+        scale_case = dataclasses.replace(
+            case, layers=[dataclasses.replace(L, weights=np.abs(L.weights)) for L in case.layers])
+    _say(f"[rand{i}] rows={spec.num_rows} cbs={spec.cbs} page={spec.page_size} nb={spec.nb} "
+         f"k={spec.topk} ke<={spec.ke_hi} {spec.mode} signed={signed}")
+    run_and_compare(case, tag=f"rand{i}", scale_case=scale_case)
+
+
 def _reweighted(case, kind, seed):
     """The case with every layer's head weights replaced.  "signed": U(-1, 1) / 8, so
     logits take both signs (the negative half of the key order and of the first radix
