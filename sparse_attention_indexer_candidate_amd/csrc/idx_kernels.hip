@@ -1047,7 +1047,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(Rows rows, KCa
     }
     int tok0 = 0;               // token of column c0
     if (c0 < ri.ncols) tok0 = (ri.si[c0 >> s.lsbk] << s.lsbk) + (c0 & (s.sbk - 1));
-    for (int i = tid; i < ri.kept; i += kTopkThreads) s_si[i] = ri.si[i];
+    // every slot [0, nsb) is written by the expansion (-1 past the kept count), so the
+    // copy need not wait for the kept load
+    for (int i = tid; i < s.nsb; i += kTopkThreads) s_si[i] = ri.si[i];
     select_clear(s_sel);
     // The valid columns of the thread (in a kept block, token in [ks, ke)) are one run
     // [c0 + lo, c0 + hi): a bit mask, so no key needs a branch.  The scoring never
@@ -1086,7 +1088,10 @@ __global__ __launch_bounds__(NT) void fused_row_kernel(Rows rows, const void *qv
     const RowInfo ri = row_info(rows, k, s, row);
     QFrag<QF> f;
     load_q<QF>(f, qv, qs, weights, row, lane);   // overlaps the schedule copy
-    for (int i = tid; i < ri.kept; i += NT) {
+    // Every slot [0, nsb) is written by the expansion (-1 past the kept count), so the
+    // copy is not bound by the kept load: the schedule, the kept count and the query
+    // are one memory round trip, not two.
+    for (int i = tid; i < s.nsb; i += NT) {
         s_si[i] = ri.si[i];
         s_pg[i] = ri.pg[i];
     }
