@@ -80,6 +80,21 @@ SMALL = {
     "rowgroup_own_tables": W.Spec(name="s8", num_rows=2048, page_size=64, cbs=64, nb=6, topk=300,
                                   ke_rule="uniform", ke_lo=10, ke_hi=3000,
                                   cand_rule="distinct", fill="all"),
+    # a prefill chunk's K packed into one page holding every position (the contiguous
+    # K-workspace form of the prefill path): one block-table entry, on the split,
+    # one-row-per-workgroup and row-group kernels
+    "one_page_workspace_split": W.Spec(name="s9", num_rows=40, page_size=2048, cbs=64, nb=16,
+                                       topk=128, mode="prefill", ke_rule="uniform", ke_lo=1,
+                                       ke_hi=2048, ks_rule="random", context=2048,
+                                       cand_rule="messy", fill="all"),
+    "one_page_workspace_rows": W.Spec(name="s10", num_rows=300, page_size=2048, cbs=64, nb=16,
+                                      topk=128, mode="prefill", ke_rule="uniform", ke_lo=1,
+                                      ke_hi=2048, ks_rule="random", context=2048,
+                                      cand_rule="messy", fill="all"),
+    "one_page_workspace_rowgroups": W.Spec(name="s11", num_rows=2050, page_size=2048, cbs=64,
+                                           nb=8, topk=100, mode="prefill", ke_rule="uniform",
+                                           ke_lo=1, ke_hi=2048, ks_rule="random", context=2048,
+                                           cand_rule="messy", fill="all"),
 }
 
 

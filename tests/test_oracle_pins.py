@@ -261,6 +261,25 @@ def test_oracle_matches_dense_then_mask_brute_force(chunk):
                 np.testing.assert_array_equal(res.indices[r], idx, err_msg=f"case {i} row {r}")
 
 
+def test_oracle_matches_brute_force_on_one_page_workspace():
+    """A prefill chunk's K packed into one page that holds every position of the
+    request (the contiguous K-workspace form of the prefill path on the backend
+    page): one block-table entry, token t at slot t of page 0."""
+    for seed in range(3):
+        spec = W.Spec(name=f"onepage{seed}", num_rows=20, num_heads=4, head_dim=64, page_size=256,
+                      cbs=16, nb=10, topk=30, mode="prefill", ke_rule="uniform", ke_lo=1, ke_hi=256,
+                      ks_rule="random", context=256, cand_rule="messy", fill="all")
+        case = W.generate(spec, seed=seed)
+        assert case.block_table.shape == (1, 1)
+        pool = case.layers[0].host_pool(spec.page_bytes)
+        res = oracle.indexer_rows(case, pool=pool)
+        for r in range(case.num_rows):
+            idx, toks, lg = brute_row(case, r, pool=pool)
+            np.testing.assert_array_equal(res.row_tokens(r), toks, err_msg=f"seed {seed} row {r}")
+            np.testing.assert_array_equal(res.row_logits(r), lg, err_msg=f"seed {seed} row {r}")
+            np.testing.assert_array_equal(res.indices[r], idx, err_msg=f"seed {seed} row {r}")
+
+
 # ------------------------------------------------------ invariants -----------
 
 def _check_invariants(case, res):
