@@ -326,6 +326,42 @@ def test_mtp_decode_rows_share_k(name):
     run_and_compare(W.generate(MTP[name], seed=21), tag=name)
 
 
+# The kernels' size limits: 8192 candidate columns a row (NB * cbs) and top-k at its
+# 8192 maximum (every valid column taken), or 6000 selected of up to 8192.
+MAX_WIDTH = {
+    "max_width_topk8192_split": W.Spec(name="m1", num_rows=24, page_size=64, cbs=64, nb=128,
+                                       topk=8192, ke_rule="uniform", ke_lo=6000, ke_hi=12000,
+                                       cand_rule="distinct", fill="candidates"),
+    "max_width_select6000_split": W.Spec(name="m2", num_rows=24, page_size=64, cbs=64, nb=128,
+                                         topk=6000, ke_rule="uniform", ke_lo=6000, ke_hi=12000,
+                                         cand_rule="distinct", fill="candidates"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MAX_WIDTH))
+def test_max_width_split_all_rows(name):
+    run_and_compare(W.generate(MAX_WIDTH[name], seed=1), tag=name)
+
+
+@pytest.mark.parametrize("k", [7000, 8192])
+def test_max_width_rows_per_cu_sampled(k):
+    """One workgroup a row at the column and top-k limits: 260 rows of up to 8192
+    columns; the oracle on sampled rows, and on every row the selection is exact for
+    the GPU's own logits."""
+    spec = W.Spec(name=f"m3_{k}", num_rows=260, page_size=64, cbs=64, nb=128, topk=k,
+                  ke_rule="uniform", ke_lo=6000, ke_hi=12000, cand_rule="distinct",
+                  fill="candidates")
+    case = W.generate(spec, seed=2)
+    rows = np.r_[0:4, 128:130, 256:260].astype(np.int32)
+    g, res = run_and_compare(case, rows=rows, tag=f"maxwidth{k}")
+    for i in range(case.num_rows):
+        gt, gl = gpu_row_tokens(res["sparse_indices"][i], int(res["kept"][i]), g.sbk, 0,
+                                int(case.row_ke[i]), res["logits"][i])
+        assert gt.size == res["end"][i], f"maxwidth{k} row {i}"
+        np.testing.assert_array_equal(res["indices"][i], exact_topk(gt, gl, k),
+                                      err_msg=f"maxwidth{k} row {i}")
+
+
 def test_config6_mtp_decode_all_rows():
     run_and_compare(W.generate(W.config(6), 0), tag="cfg6")
 
