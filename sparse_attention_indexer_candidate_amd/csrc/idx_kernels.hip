@@ -17,9 +17,10 @@
 //  score_split_kernel + topk_split_kernel
 //                       fewer rows than CUs: rows split over workgroups, logits in
 //                       global scratch, selection in a second launch
-//  score_dense_kernel + dense_topk_kernel
+//  score_dense_kernel + topk_split_kernel<dense>
 //                       the comparator: every token of [ks, ke) with the same
-//                       per-tile code, masked to the candidates, same selection
+//                       per-tile code, then the candidates' keys gathered from the
+//                       dense row in schedule order and the same selection
 //
 // The operation follows the vLLM DeepSeek-V4.1 pages (sparse_mqa_indexer, the
 // sparse indexer backend source, rocm_paged_mxfp4_indexer): logits over the
@@ -72,8 +73,6 @@ constexpr int kWave = 64;
 constexpr int kMaxNB = 512;          // NB * cbs <= 8192 with cbs >= 16
 constexpr int kMaxNSB = 512;         // NSB * sbk <= 8192 with sbk >= 16
 constexpr int kMaxRowCols = 8192;    // NB * cbs
-constexpr int kMaxDenseCols = 65536;
-constexpr int kMaxDenseBlocks = kMaxDenseCols / 16;
 
 // Pointers rebuilt from integers (per-tile bases read back from lanes) are tagged
 // with the global address space so loads use the global (not flat) path.
@@ -984,7 +983,6 @@ __device__ void select_topk(const uint32_t (&key)[KPT], bool live, int count_val
 
 constexpr int kScoreThreads = 256;
 constexpr int kTopkThreads = 512;
-constexpr int kDenseTopkThreads = 1024;
 
 // Rows split over workgroups: grid = (rows, chunks of groups_per_wg 64-column groups);
 // each wave scores a contiguous quarter of its workgroup's groups into logits.
@@ -1018,35 +1016,50 @@ struct SparseTokens {
     }
 };
 
-// Selection for rows scored by score_split_kernel: keys from the global logits
-// (loaded before anything else so their latency overlaps the schedule load).  A
-// column is valid when it lies in a kept block and its token in [ks, ke); the logit's
-// value plays no part (a valid -inf logit is selectable, the lowest of all).
+// Selection for rows whose logits a separate scoring kernel wrote to global memory.
+// Sparse (DENSE = false): the row's logits in sparse column order (score_split_kernel).
+// Dense (DENSE = true): logits by token, lstride floats apart, lcols tokens a row (a
+// multiple of 16; score_dense_kernel).  The candidate tokens in ascending order are
+// the schedule's sparse blocks in order, so the dense keys are gathered from the row
+// at those tokens and the selection is the sparse one: identical logits give
+// identical indices.  A column is valid when it lies in a kept block and its token in
+// [ks, ke) (dense: and below lcols); the logit's value plays no part (a valid -inf
+// logit is selectable, the lowest of all).
+template <bool DENSE>
 __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(Rows rows, KCache k, Schedule s,
-                                                                  const float *logits, int32_t topk,
-                                                                  int32_t *out, int64_t ostride) {
+                                                                  const float *logits,
+                                                                  int64_t lstride, int32_t lcols,
+                                                                  int32_t topk, int32_t *out,
+                                                                  int64_t ostride) {
     constexpr int KPT = kMaxRowCols / kTopkThreads;
+    static_assert(KPT == 16, "a run of 16 columns: whole float4s, inside one sparse block (sbk >= 16), "
+                             "and a dense run starting at a multiple of 16");
     __shared__ int32_t s_si[kMaxNSB];
     __shared__ alignas(16) int32_t s_stage[kMaxRowCols];
     __shared__ SelectLds<kTopkThreads> s_sel;
     const int row = blockIdx.x, tid = threadIdx.x;
     const RowInfo ri = row_info(rows, k, s, row);
-    const float *lrow = logits + (int64_t)row * ri.ncols;
-    // Loads bounded by the row's column count, not its kept count, so none waits for
-    // the kept load; columns past the kept blocks are masked below.
+    const float *lrow = logits + (int64_t)row * (DENSE ? lstride : (int64_t)ri.ncols);
     const int c0 = tid * KPT;   // the thread's KPT columns lie in one sparse block
+    int tok0 = 0;               // token of column c0
+    if (c0 < ri.ncols) tok0 = (ri.si[c0 >> s.lsbk] << s.lsbk) + (c0 & (s.sbk - 1));
+    // Sparse: columns c0.. (bounded by the row's column count, not its kept count, so
+    // the load does not wait for the kept load; every column was written).  Dense:
+    // tokens tok0.. once the schedule entry is in (tok0 is a multiple of 16, lcols too,
+    // so the run lies wholly inside or outside the row; -1 entries past the kept count
+    // give tok0 < 0 and read nothing).  Columns past the kept blocks are masked below.
+    const int l0 = DENSE ? tok0 : c0;
+    const bool rd = DENSE ? (c0 < ri.ncols && tok0 >= 0 && tok0 < lcols) : (c0 < ri.ncols);
     float x[KPT];
 #pragma unroll
     for (int i = 0; i < KPT; i += 4) {
         float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        if (c0 + i < ri.ncols) v = *(const float4 *)(lrow + c0 + i);   // every column written
+        if (rd) v = *(const float4 *)(lrow + l0 + i);
         x[i] = v.x;
         x[i + 1] = v.y;
         x[i + 2] = v.z;
         x[i + 3] = v.w;
     }
-    int tok0 = 0;               // token of column c0
-    if (c0 < ri.ncols) tok0 = (ri.si[c0 >> s.lsbk] << s.lsbk) + (c0 & (s.sbk - 1));
     // every slot [0, nsb) is written by the expansion (-1 past the kept count), so the
     // copy need not wait for the kept load
     for (int i = tid; i < s.nsb; i += kTopkThreads) s_si[i] = ri.si[i];
@@ -1056,7 +1069,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(Rows rows, KCa
     // writes -0 (see bits_key).
     static_assert(KPT < 32, "one mask bit per key");
     const int lo = min(KPT, max(0, ri.ks - tok0));
-    const int hi = max(0, min(min(KPT, ri.valid_cols - c0), ri.ke - tok0));
+    const int hi = max(0, min(min(KPT, ri.valid_cols - c0),
+                              min(ri.ke, DENSE ? lcols : INT_MAX) - tok0));
     const uint32_t vmask = ((1u << hi) - 1u) & ~((1u << lo) - 1u);
     uint32_t key[KPT];
 #pragma unroll
@@ -1179,74 +1193,6 @@ __global__ __launch_bounds__(kScoreThreads) void score_dense_kernel(
     score_groups<QF, 4, 2>(k, f, ks, ke, g0, g1,
                                  DenseDesc{bt, ks, tbl_ok ? ke : 0, k.page_size, k.pages_per_table},
                                  [&](int t, float v) { lrow[t] = v; });  // t < ngroups*64 <= lstride
-}
-
-// Dense selection: the row's candidate tokens (those whose sparse block is in the
-// schedule) are compacted in token order into LDS with their logits, then selected
-// like the sparse path.
-__global__ __launch_bounds__(kDenseTopkThreads) void dense_topk_kernel(Rows rows, KCache k, Schedule s,
-                                                                  const float *logits,
-                                                                  int64_t lstride, int32_t ncols,
-                                                                  int32_t topk, int32_t *out,
-                                                                  int64_t ostride) {
-    constexpr int CPT = kMaxDenseCols / kDenseTopkThreads;   // columns scanned per thread
-    constexpr int KPT = kMaxRowCols / kDenseTopkThreads;     // compacted keys per thread
-    __shared__ uint32_t s_bits[kMaxDenseBlocks / 32];
-    __shared__ alignas(16) float s_val[kMaxRowCols];
-    __shared__ int32_t s_tok[kMaxRowCols];
-    __shared__ int s_scan[kDenseTopkThreads / kWave];
-    __shared__ SelectLds<kDenseTopkThreads> s_sel;
-    const int row = blockIdx.x, tid = threadIdx.x;
-    const RowInfo ri = row_info(rows, k, s, row);
-    const int sbk = s.sbk;
-    const int nblocks = ncols / sbk;
-    for (int i = tid; i < (nblocks + 31) / 32; i += kDenseTopkThreads) s_bits[i] = 0u;
-    select_clear(s_sel);
-    __syncthreads();
-    for (int i = tid; i < ri.kept; i += kDenseTopkThreads) {
-        const int b = ri.si[i];
-        if (b >= 0 && b < nblocks) atomicOr(&s_bits[b >> 5], 1u << (b & 31));
-    }
-    __syncthreads();
-    auto member = [&](int t) {
-        if (t < ri.ks || t >= ri.ke || t >= ncols) return false;
-        const int b = t / sbk;
-        return ((s_bits[b >> 5] >> (b & 31)) & 1u) != 0u;
-    };
-    int mine = 0;
-    for (int i = 0; i < CPT; ++i) mine += member(tid * CPT + i);
-    int nvalid = 0;
-    int pos = block_excl_scan<kDenseTopkThreads>(mine, &nvalid, s_scan);
-    const float *lrow = logits + (int64_t)row * lstride;
-    for (int i = 0; i < CPT; ++i) {
-        const int t = tid * CPT + i;
-        if (member(t)) {
-            if (pos < kMaxRowCols) {
-                s_val[pos] = lrow[t];
-                s_tok[pos] = t;
-            }
-            ++pos;
-        }
-    }
-    nvalid = min(nvalid, kMaxRowCols);
-    __syncthreads();
-    uint32_t key[KPT];
-    KeyStats st;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-        const int c = tid * KPT + i;
-        key[i] = c < nvalid ? ordered_key(s_val[c]) : 0u;
-        st.add(key[i]);
-    }
-    int count;
-    uint32_t kmin, kmax;
-    block_key_stats<kDenseTopkThreads>(st, s_sel, count, kmin, kmax);
-    select_topk<kDenseTopkThreads, KPT>(key, keys_live(key), count, kmin, kmax, topk, out + (int64_t)row * ostride,
-                                        s_sel, reinterpret_cast<int32_t *>(s_val),
-                                        [&](int c0, int (&tok)[KPT]) {
-#pragma unroll
-                                            for (int i = 0; i < KPT; ++i) tok[i] = s_tok[c0 + i];
-                                        });
 }
 
 // ---------------------------------------------------------------- row groups ---
@@ -1608,8 +1554,8 @@ static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const 
                               logits, gpw);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_split_kernel, dim3(rows.num_rows), dim3(kTopkThreads), 0, stream, rows,
-                       k, s, logits, topk, out, out_stride);
+    hipLaunchKernelGGL(topk_split_kernel<false>, dim3(rows.num_rows), dim3(kTopkThreads), 0, stream,
+                       rows, k, s, logits, (int64_t)0, 0, topk, out, out_stride);
     return hipGetLastError();
 }
 
@@ -1648,8 +1594,8 @@ hipError_t launch_dense_topk(const Rows &rows, const KCache &k, const Schedule &
                              const float *logits, int64_t logits_stride, int32_t ncols,
                              int32_t topk, int32_t *out, int64_t out_stride, hipStream_t stream) {
     if (rows.num_rows == 0) return hipSuccess;
-    hipLaunchKernelGGL(dense_topk_kernel, dim3(rows.num_rows), dim3(kDenseTopkThreads), 0, stream, rows, k,
-                       s, logits, logits_stride, ncols, topk, out, out_stride);
+    hipLaunchKernelGGL(topk_split_kernel<true>, dim3(rows.num_rows), dim3(kTopkThreads), 0, stream,
+                       rows, k, s, logits, logits_stride, ncols, topk, out, out_stride);
     return hipGetLastError();
 }
 

@@ -175,7 +175,12 @@ def test_random_shapes_all_rows(i):
             case, layers=[dataclasses.replace(L, weights=np.abs(L.weights)) for L in case.layers])
     _say(f"[rand{i}] rows={spec.num_rows} cbs={spec.cbs} page={spec.page_size} nb={spec.nb} "
          f"k={spec.topk} ke<={spec.ke_hi} {spec.mode} signed={signed}")
-    run_and_compare(case, tag=f"rand{i}", scale_case=scale_case)
+    g, res = run_and_compare(case, tag=f"rand{i}", scale_case=scale_case)
+    # the dense comparator on the same inputs: the same logits, so the same indices
+    _say(f"[rand{i}] dense")
+    ctx = max(64, int(case.row_ke.max() + 63) // 64 * 64)
+    np.testing.assert_array_equal(_dense_indices(g, case, ctx), res["indices"],
+                                  err_msg=f"rand{i}: dense != sparse indices")
 
 
 def _reweighted(case, kind, seed):
