@@ -98,6 +98,43 @@ def cpu_baseline(case, q_format: str, seconds: float, threads: int = 1):
                        f"{wall:.1f} s wall")
 
 
+def measured_peaks(stream) -> dict:
+    """The chip's measured ceilings for the roofline, from the library's reference
+    kernels timed with events on the bench stream (median of 5 after a warm-up): a read
+    stream over 2 GiB (larger than the caches, so every byte comes from HBM) and an
+    MFMA-only loop on the MX-FP4 instruction the scoring uses."""
+    import torch
+
+    import sparse_attention_indexer_candidate_amd as idx
+
+    nbytes = 2 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=stream.device)
+    sink = torch.empty(idx.IDX_MEASURE_WGS * 4, dtype=torch.float32, device=stream.device)
+    iters = 4096
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b) / 1e3)
+        return float(np.median(ts))
+
+    t_read = timed(lambda: idx.idx_measure_read(buf, nbytes, sink, stream=stream.cuda_stream))
+    t_mfma = timed(lambda: idx.idx_measure_mfma(iters, sink, stream=stream.cuda_stream))
+    del buf
+    return {"read_gbs": nbytes / t_read / 1e9,
+            "mxfp4_tflops": idx.idx_measure_mfma_flops(iters) / t_mfma / 1e12,
+            "how": "idx_measure_read over 2 GiB; idx_measure_mfma (8 independent MX-FP4 "
+                   "16x16x128 MFMA chains a wave, 4096 x 256 threads, operands in registers); "
+                   "median of 5 launches timed with events"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -302,6 +339,9 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS}
+    peaks = measured_peaks(stream)
+    roof["measured_peak"] = peaks["mxfp4_tflops"] if roof["bound"] == "mfma" else peaks["read_gbs"]
+    roof["frac_of_measured"] = roof["achieved"] / roof["measured_peak"]
     roof.update({"traffic": traffic, "kernel": kernel_name, "avg_launch_us": avg_kernel_s * 1e6,
                  "launch_us_p10": float(np.percentile(kernel_ms, 10)) * 1e3,
                  "launch_us_p90": float(np.percentile(kernel_ms, 90)) * 1e3,
@@ -329,6 +369,7 @@ def main():
                    "path": args.path,
                    "input_copies": nrep, "seed": args.seed},
         "roofline": roof,
+        "measured_peaks": peaks,
     }
     if args.path == "dense":
         out["context_cols_per_s"] = ctx_cols_per_step * args.steps / elapsed

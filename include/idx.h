@@ -185,6 +185,27 @@ int idx_dense_masked_logits_topk(const idx_config *cfg, const idx_rows *rows, in
                                  int64_t out_stride, float *logits_out, int64_t logits_stride,
                                  void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---- Measurement (not a step of the indexer) ----
+ * Reference kernels for the two rates that bound the indexer, for a benchmark to time
+ * with events on `stream` next to the indexer's own kernels: the measured read
+ * bandwidth (the K gather streams pages of the cache) and the measured MX-FP4 MFMA
+ * rate (the scoring contraction), beside the published peaks.  Both launch
+ * IDX_MEASURE_WGS workgroups of 256 threads and return IDX_EINVAL (launching nothing)
+ * on a bad argument.
+ *
+ * idx_measure_read: reads every 16-byte word of [src, src + bytes) once (device
+ *   memory; src 16-byte aligned, bytes a nonzero multiple of 16) and writes one
+ *   checksum word per workgroup to sink (device, IDX_MEASURE_WGS uint32).
+ * idx_measure_mfma: every wave runs `iters` (>= 1) rounds of 8 independent
+ *   v_mfma_scale_f32_16x16x128_f8f6f4 on e2m1 operands held in registers and writes
+ *   one float per wave to sink (device, IDX_MEASURE_WGS * 4 floats);
+ *   idx_measure_mfma_flops(iters) is the number of floating-point operations one
+ *   call performs (host). */
+#define IDX_MEASURE_WGS 4096
+int idx_measure_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
+int idx_measure_mfma(int32_t iters, float *sink, void *stream);
+int64_t idx_measure_mfma_flops(int32_t iters);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,9 @@ IDX_MAX_TOPK = 8192
 
 EXPORTED = ("idx_check_config", "idx_num_sparse_blocks", "idx_schedule_work_bytes",
             "idx_workspace_bytes", "idx_last_error", "idx_set_timing_events",
-            "idx_expand_candidates", "idx_sparse_mqa_logits_topk", "idx_dense_masked_logits_topk")
+            "idx_expand_candidates", "idx_sparse_mqa_logits_topk", "idx_dense_masked_logits_topk",
+            "idx_measure_read", "idx_measure_mfma", "idx_measure_mfma_flops")
+IDX_MEASURE_WGS = 4096
 
 
 class IdxError(RuntimeError):
@@ -99,6 +101,12 @@ def _load():
                                                P(idx_kcache), P(idx_schedule), vp, i64, vp, i64,
                                                vp, sz, vp]
     L.idx_dense_masked_logits_topk.restype = ctypes.c_int
+    L.idx_measure_read.argtypes = [vp, sz, vp, vp]
+    L.idx_measure_read.restype = ctypes.c_int
+    L.idx_measure_mfma.argtypes = [i32, vp, vp]
+    L.idx_measure_mfma.restype = ctypes.c_int
+    L.idx_measure_mfma_flops.argtypes = [i32]
+    L.idx_measure_mfma_flops.restype = i64
     return L
 
 
@@ -170,6 +178,20 @@ def idx_dense_masked_logits_topk(cfg, rows, max_ctx, q_values, q_scales, weights
         ctypes.byref(cfg), ctypes.byref(rows), max_ctx, _p(q_values), _p(q_scales), _p(weights),
         ctypes.byref(k), ctypes.byref(sched), _p(topk_indices), out_stride, _p(logits_out),
         logits_stride, _p(workspace), workspace_bytes, _p(stream)))
+
+
+def idx_measure_read(src, nbytes, sink, stream=None):
+    """Reference read stream over nbytes of src (device); sink: IDX_MEASURE_WGS uint32."""
+    return _check(lib.idx_measure_read(_p(src), nbytes, _p(sink), _p(stream)))
+
+
+def idx_measure_mfma(iters, sink, stream=None):
+    """Reference MX-FP4 MFMA loop; sink: IDX_MEASURE_WGS * 4 floats."""
+    return _check(lib.idx_measure_mfma(iters, _p(sink), _p(stream)))
+
+
+def idx_measure_mfma_flops(iters) -> int:
+    return int(lib.idx_measure_mfma_flops(iters))
 
 
 # ------------------------------------------------- calls bound ahead of time --

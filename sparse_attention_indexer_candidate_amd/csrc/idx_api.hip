@@ -307,4 +307,32 @@ int idx_dense_masked_logits_topk(const idx_config *cfg, const idx_rows *rows, in
     return ok();
 }
 
+int idx_measure_read(const void *src, size_t bytes, uint32_t *sink, void *stream) {
+    if (!src || !sink) return fail(IDX_EINVAL, "src and sink must be non-NULL");
+    if (!aligned(src, 16) || bytes % 16 != 0 || bytes == 0)
+        return fail(IDX_EINVAL, "src must be 16-byte aligned and bytes a nonzero multiple of 16");
+    if (!aligned(sink, 4)) return fail(IDX_EINVAL, "sink must be 4-byte aligned");
+    int rc;
+    if ((rc = hip_status(idx::launch_measure_read(src, bytes, sink, (hipStream_t)stream),
+                         "read launch")))
+        return rc;
+    return ok();
+}
+
+int idx_measure_mfma(int32_t iters, float *sink, void *stream) {
+    if (iters < 1) return fail(IDX_EINVAL, "iters %d must be >= 1", iters);
+    if (!sink || !aligned(sink, 4)) return fail(IDX_EINVAL, "sink must be non-NULL and 4-byte aligned");
+    int rc;
+    if ((rc = hip_status(idx::launch_measure_mfma(iters, sink, (hipStream_t)stream), "mfma launch")))
+        return rc;
+    return ok();
+}
+
+static_assert(idx::kMeasureWgs == IDX_MEASURE_WGS, "one workgroup count for the launch and the ABI");
+
+int64_t idx_measure_mfma_flops(int32_t iters) {
+    // waves x rounds x 8 chains x (16 x 16 x 128 multiply-adds x 2)
+    return (int64_t)IDX_MEASURE_WGS * 4 * (iters > 0 ? iters : 0) * 8 * (16 * 16 * 128 * 2);
+}
+
 }  // extern "C"

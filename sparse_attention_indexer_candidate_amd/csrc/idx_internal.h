@@ -79,4 +79,9 @@ hipError_t launch_dense_topk(const Rows &rows, const KCache &k, const Schedule &
                              const float *logits, int64_t logits_stride, int32_t ncols,
                              int32_t topk, int32_t *out, int64_t out_stride, hipStream_t stream);
 
+// Reference kernels for the rates that bound the indexer (measurement only).
+constexpr int kMeasureWgs = 4096;   // workgroups of 256 threads
+hipError_t launch_measure_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream);
+hipError_t launch_measure_mfma(int32_t iters, float *sink, hipStream_t stream);
+
 }  // namespace idx

@@ -471,6 +471,9 @@ __device__ __forceinline__ float reduce_transpose4(float p0, float p1, float p2,
 // reads the pool's first bytes (in bounds, and an L2 hit after the first time) and
 // its result is dropped by a select.  Branch-free loads keep the compiler's
 // memory-counter waits exact (a load under an if makes it wait for everything).
+// K loads carry the non-temporal hint: a decode row reads each K byte once, and the
+// streaming policy measured 4-9 % faster steps than the default one (the row-group
+// kernel, whose rows share K tiles through the caches, keeps the default).
 // sink(c, logit) receives every column of the groups, -inf where the column is not a
 // valid token of [ks, ke).
 template <int QF, int RG, int U, class Desc, class Sink>
@@ -507,9 +510,9 @@ __device__ __forceinline__ void score_groups(const KCache &k, const QFrag<QF> &f
                         __builtin_amdgcn_readlane(vhi, src), __builtin_amdgcn_readlane(vlo, src));
                     const kGlobal uint8_t *sp = (const kGlobal uint8_t *)join64(
                         __builtin_amdgcn_readlane(shi, src), __builtin_amdgcn_readlane(slo, src));
-                    const v4u x = *(const kGlobal v4u *)(vp + voff);
+                    const v4u x = __builtin_nontemporal_load((const kGlobal v4u *)(vp + voff));
                     b[q][t].v = make_uint4(x[0], x[1], x[2], x[3]);
-                    b[q][t].sc = sp[soff];
+                    b[q][t].sc = __builtin_nontemporal_load(sp + soff);
                 }
         };
         auto finish_unit = [&](int u, const KTile(&b)[U][4]) {
@@ -578,9 +581,9 @@ __device__ __forceinline__ void score_units(const KCache &k, const QFrag<QF> &f,
                     __builtin_amdgcn_readlane(vhi, src), __builtin_amdgcn_readlane(vlo, src));
                 const kGlobal uint8_t *sp = (const kGlobal uint8_t *)join64(
                     __builtin_amdgcn_readlane(shi, src), __builtin_amdgcn_readlane(slo, src));
-                const v4u x = *(const kGlobal v4u *)(vp + voff);
+                const v4u x = __builtin_nontemporal_load((const kGlobal v4u *)(vp + voff));
                 b[q][t].v = make_uint4(x[0], x[1], x[2], x[3]);
-                b[q][t].sc = sp[soff];
+                b[q][t].sc = __builtin_nontemporal_load(sp + soff);
             }
     };
     auto finish = [&](int u, const KTile (&b)[U][4], int ttok, uint64_t okmask) {
@@ -1466,6 +1469,72 @@ __global__ __launch_bounds__(kGroupThreads) void row_group_kernel(
     }
 }
 
+
+// ---------------------------------------------------------------- measurement --
+//
+// Reference rates for the roofline, run on the same chip as the indexer: a plain
+// read stream (what the K gather can at best reach) and an MFMA-only loop on the
+// MX-FP4 instruction the scoring uses (what the contraction can at best reach).
+
+constexpr int kMeasureThreads = 256;
+
+// Every 16-byte word of src[0, n16) read once: thread g reads words g + j*T (T = all
+// threads), eight non-temporal loads in flight (the fastest of the shapes measured:
+// 6.3-6.5 TB/s), contiguous across the wave; an XOR of everything read goes to
+// sink[workgroup] so the loads are live.
+__global__ __launch_bounds__(kMeasureThreads) void measure_read_kernel(const uint4 *src, int64_t n16,
+                                                                       uint32_t *sink) {
+    const int64_t nthr = (int64_t)gridDim.x * kMeasureThreads;
+    int64_t i = (int64_t)blockIdx.x * kMeasureThreads + threadIdx.x;
+    uint32_t acc = 0;
+    const v4u *s4 = reinterpret_cast<const v4u *>(src);
+    for (; i + 7 * nthr < n16; i += 8 * nthr) {
+        v4u v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = __builtin_nontemporal_load(s4 + i + j * nthr);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc ^= v[j][0] ^ v[j][1] ^ v[j][2] ^ v[j][3];
+    }
+    for (; i < n16; i += nthr) {
+        const v4u a = __builtin_nontemporal_load(s4 + i);
+        acc ^= a[0] ^ a[1] ^ a[2] ^ a[3];
+    }
+    for (int o = kWave / 2; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o, kWave);
+    __shared__ uint32_t w[kMeasureThreads / kWave];
+    if ((threadIdx.x & (kWave - 1)) == 0) w[threadIdx.x / kWave] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t x = 0;
+        for (int j = 0; j < kMeasureThreads / kWave; ++j) x ^= w[j];
+        sink[blockIdx.x] = x;
+    }
+}
+
+// Each wave: iters rounds of 8 independent v_mfma_scale_f32_16x16x128_f8f6f4 chains on
+// e2m1 operands held in registers (nonzero codes that differ by lane; scale bytes
+// 127), no memory traffic until one float per wave goes to sink.
+__global__ __launch_bounds__(kMeasureThreads) void measure_mfma_kernel(int32_t iters, float *sink) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int x = 0x3A5C1E72 ^ (lane * 0x01030507) ^ iters;
+    const v8i a = v8i{x | 0x11111111, (x >> 3) | 0x22222222, (x << 5) | 0x11111111,
+                      x ^ 0x7F3E1D2C, 0, 0, 0, 0};
+    const v8i b = v8i{(x * 7) | 0x11111111, x ^ 0x5A5A5A5A, (x >> 7) | 0x33333333,
+                      (x * 13) | 0x21212121, 0, 0, 0, 0};
+    v4f acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            acc[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[c], 4, 4, 0, 127, 0,
+                                                                      127);
+    }
+    float t = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) t += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+    if (lane == 0) sink[blockIdx.x * (kMeasureThreads / kWave) + threadIdx.x / kWave] = t;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- launchers ----
@@ -1596,6 +1665,18 @@ hipError_t launch_dense_topk(const Rows &rows, const KCache &k, const Schedule &
     if (rows.num_rows == 0) return hipSuccess;
     hipLaunchKernelGGL(topk_split_kernel<true>, dim3(rows.num_rows), dim3(kTopkThreads), 0, stream,
                        rows, k, s, logits, logits_stride, ncols, topk, out, out_stride);
+    return hipGetLastError();
+}
+
+hipError_t launch_measure_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream) {
+    hipLaunchKernelGGL(measure_read_kernel, dim3(kMeasureWgs), dim3(kMeasureThreads), 0, stream,
+                       (const uint4 *)src, (int64_t)(bytes / 16), sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_measure_mfma(int32_t iters, float *sink, hipStream_t stream) {
+    hipLaunchKernelGGL(measure_mfma_kernel, dim3(kMeasureWgs), dim3(kMeasureThreads), 0, stream, iters,
+                       sink);
     return hipGetLastError();
 }
 

@@ -213,3 +213,20 @@ def test_bound_calls_check_arguments_like_the_wrappers():
                                               FAKE, 2048, FAKE, 0)
     with pytest.raises(idx.IdxError):
         dense()
+
+
+def test_measurement_kernels_reject_bad_arguments_on_the_host():
+    with pytest.raises(idx.IdxError) as e:
+        idx.idx_measure_read(FAKE, 17, FAKE)          # not a multiple of 16 bytes
+    assert e.value.code == idx.IDX_EINVAL
+    with pytest.raises(idx.IdxError):
+        idx.idx_measure_read(FAKE + 4, 64, FAKE)      # src not 16-byte aligned
+    with pytest.raises(idx.IdxError):
+        idx.idx_measure_read(None, 64, FAKE)
+    with pytest.raises(idx.IdxError) as e:
+        idx.idx_measure_mfma(0, FAKE)
+    assert e.value.code == idx.IDX_EINVAL
+    with pytest.raises(idx.IdxError):
+        idx.idx_measure_mfma(16, None)
+    # waves x rounds x 8 chains x 16*16*128 multiply-adds x 2
+    assert idx.idx_measure_mfma_flops(3) == idx.IDX_MEASURE_WGS * 4 * 3 * 8 * 16 * 16 * 128 * 2
