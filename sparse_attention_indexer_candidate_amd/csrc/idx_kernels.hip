@@ -1028,15 +1028,18 @@ struct SparseTokens {
 // identical indices.  A column is valid when it lies in a kept block and its token in
 // [ks, ke) (dense: and below lcols); the logit's value plays no part (a valid -inf
 // logit is selectable, the lowest of all).
-template <bool DENSE>
+// KPT keys a thread (8 for rows of up to 4096 columns, so every thread holds keys; 16
+// up to 8192).
+template <bool DENSE, int KPT>
 __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(Rows rows, KCache k, Schedule s,
                                                                   const float *logits,
                                                                   int64_t lstride, int32_t lcols,
                                                                   int32_t topk, int32_t *out,
                                                                   int64_t ostride) {
-    constexpr int KPT = kMaxRowCols / kTopkThreads;
-    static_assert(KPT == 16, "a run of 16 columns: whole float4s, inside one sparse block (sbk >= 16), "
-                             "and a dense run starting at a multiple of 16");
+    static_assert(KPT == 8 || KPT == 16, "a run of 8 or 16 columns: whole float4s, inside one "
+                  "sparse block (sbk >= 16), and a dense run starting at a multiple of KPT, which "
+                  "divides the row length lcols (a multiple of 64)");
+    static_assert(KPT * kTopkThreads <= kMaxRowCols, "the stage holds every column");
     __shared__ int32_t s_si[kMaxNSB];
     __shared__ alignas(16) int32_t s_stage[kMaxRowCols];
     __shared__ SelectLds<kTopkThreads> s_sel;
@@ -1048,7 +1051,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(Rows rows, KCa
     if (c0 < ri.ncols) tok0 = (ri.si[c0 >> s.lsbk] << s.lsbk) + (c0 & (s.sbk - 1));
     // Sparse: columns c0.. (bounded by the row's column count, not its kept count, so
     // the load does not wait for the kept load; every column was written).  Dense:
-    // tokens tok0.. once the schedule entry is in (tok0 is a multiple of 16, lcols too,
+    // tokens tok0.. once the schedule entry is in (tok0 is a multiple of KPT, lcols of 64,
     // so the run lies wholly inside or outside the row; -1 entries past the kept count
     // give tok0 < 0 and read nothing).  Columns past the kept blocks are masked below.
     const int l0 = DENSE ? tok0 : c0;
@@ -1623,8 +1626,12 @@ static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const 
                               logits, gpw);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_split_kernel<false>, dim3(rows.num_rows), dim3(kTopkThreads), 0, stream,
-                       rows, k, s, logits, (int64_t)0, 0, topk, out, out_stride);
+    if (ncols <= 8 * kTopkThreads)
+        hipLaunchKernelGGL((topk_split_kernel<false, 8>), dim3(rows.num_rows), dim3(kTopkThreads), 0,
+                           stream, rows, k, s, logits, (int64_t)0, 0, topk, out, out_stride);
+    else
+        hipLaunchKernelGGL((topk_split_kernel<false, 16>), dim3(rows.num_rows), dim3(kTopkThreads), 0,
+                           stream, rows, k, s, logits, (int64_t)0, 0, topk, out, out_stride);
     return hipGetLastError();
 }
 
@@ -1663,8 +1670,13 @@ hipError_t launch_dense_topk(const Rows &rows, const KCache &k, const Schedule &
                              const float *logits, int64_t logits_stride, int32_t ncols,
                              int32_t topk, int32_t *out, int64_t out_stride, hipStream_t stream) {
     if (rows.num_rows == 0) return hipSuccess;
-    hipLaunchKernelGGL(topk_split_kernel<true>, dim3(rows.num_rows), dim3(kTopkThreads), 0, stream,
-                       rows, k, s, logits, logits_stride, ncols, topk, out, out_stride);
+    const int nsbcols = s.nsb * s.sbk;   // candidate columns a row
+    if (nsbcols <= 8 * kTopkThreads)
+        hipLaunchKernelGGL((topk_split_kernel<true, 8>), dim3(rows.num_rows), dim3(kTopkThreads), 0,
+                           stream, rows, k, s, logits, logits_stride, ncols, topk, out, out_stride);
+    else
+        hipLaunchKernelGGL((topk_split_kernel<true, 16>), dim3(rows.num_rows), dim3(kTopkThreads), 0,
+                           stream, rows, k, s, logits, logits_stride, ncols, topk, out, out_stride);
     return hipGetLastError();
 }
 
