@@ -16,6 +16,9 @@ FLAGS = [
     # MFMA results in VGPRs: the ReLU-weight epilogue reads every accumulator, so
     # AGPR results would cost one extra move per element
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    # the leading scalar kernel arguments (up to 16 SGPRs) are preloaded at wave launch,
+    # so a kernel's first loads do not wait for a load of their own addresses
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-result",
     "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
 ]
