@@ -1002,22 +1002,30 @@ constexpr int kScoreThreads = 256;
 constexpr int kTopkThreads = 512;
 
 // Rows split over workgroups: grid = (rows, chunks of groups_per_wg 64-column groups);
-// each wave scores a contiguous quarter of its workgroup's groups into logits.
+// each wave scores a contiguous quarter of its workgroup's groups into logits.  The
+// leading scalar arguments are what the first loads need (the row's schedule entries
+// and query): the hardware preloads them into SGPRs at wave launch, so those loads
+// issue at once; ks / ke (only the validity of the scored columns needs them) and the
+// cache geometry arrive while they fly.
 template <int QF, int PW>
 __global__ __launch_bounds__(kScoreThreads) void score_split_kernel(
-    Rows rows, const void *qv, const void *qs, const float *weights, KCache k, Schedule s,
-    float *logits, int groups_per_wg) {
+    const int32_t *si_base, const int32_t *pg_base, const void *qv, const void *qs,
+    const float *weights, int32_t nsb, int32_t sbk, int32_t groups_per_wg, Rows rows, KCache k,
+    float *logits) {
     const int row = blockIdx.x;
     const int wave = uniform(threadIdx.x / kWave);
-    const RowInfo ri = row_info(rows, k, s, row);
-    const int ngroups = (ri.ncols + 63) / 64;
+    const int ncols = nsb * sbk;
+    const int ngroups = (ncols + 63) / 64;
     const int g0 = min(blockIdx.y * groups_per_wg + wave * PW, ngroups);
     const int g1 = min(g0 + PW, ngroups);
-    float *lrow = logits + (int64_t)row * ri.ncols;
     QFrag<QF> f;
-    load_q<QF>(f, qv, qs, weights, row, threadIdx.x & (kWave - 1));   // not behind kept
-    score_groups<QF, PW, PW>(k, f, ri.ks, ri.ke, g0, g1, SparseDesc{ri.si, ri.pg, s.nsb, s.sbk},
-                        [&](int c, float v) { if (c < ri.ncols) lrow[c] = v; });
+    load_q<QF>(f, qv, qs, weights, row, threadIdx.x & (kWave - 1));
+    const int32_t *si = si_base + (int64_t)row * nsb, *pg = pg_base + (int64_t)row * nsb;
+    const int32_t ks_raw = (rows.ks ? rows.ks : rows.ke)[row];   // no load behind a branch
+    const int ks = rows.ks ? ks_raw : 0, ke = rows.ke[row];
+    float *lrow = logits + (int64_t)row * ncols;
+    score_groups<QF, PW, PW>(k, f, ks, ke, g0, g1, SparseDesc{si, pg, nsb, sbk},
+                             [&](int c, float v) { if (c < ncols) lrow[c] = v; });
 }
 
 // Tokens of the KPT sparse columns c0 .. c0+KPT-1 (KPT divides sbk = 1 << lsbk, and c0
@@ -1044,12 +1052,17 @@ struct SparseTokens {
 // logit is selectable, the lowest of all).
 // KPT keys a thread (8 for rows of up to 4096 columns, so every thread holds keys; 16
 // up to 8192).
+//
+// The leading scalar arguments are what the first loads need (the row's logits, its
+// schedule entries, ks / ke / kept): preloaded into SGPRs at wave launch, so those
+// loads are one round trip with no load of their addresses before them.  The table
+// row is not checked here: the expansion lists nothing for a row whose table row is
+// invalid (kept = 0), and the schedule comes from the expansion of the same rows.
 template <bool DENSE, int KPT>
-__global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(Rows rows, KCache k, Schedule s,
-                                                                  const float *logits,
-                                                                  int64_t lstride, int32_t lcols,
-                                                                  int32_t topk, int32_t *out,
-                                                                  int64_t ostride) {
+__global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(
+    const float *logits, const int32_t *si_base, const int32_t *p_ks, const int32_t *p_ke,
+    const int32_t *p_kept, int32_t nsb, int32_t lsbk, int64_t lstride, int32_t lcols,
+    int32_t topk, int32_t *out, int64_t ostride) {
     static_assert(KPT == 8 || KPT == 16, "a run of 8 or 16 columns: whole float4s, inside one "
                   "sparse block (sbk >= 16), and a dense run starting at a multiple of KPT, which "
                   "divides the row length lcols (a multiple of 64)");
@@ -1058,18 +1071,22 @@ __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(Rows rows, KCa
     __shared__ alignas(16) int32_t s_stage[kMaxRowCols];
     __shared__ SelectLds<kTopkThreads> s_sel;
     const int row = blockIdx.x, tid = threadIdx.x;
-    const RowInfo ri = row_info(rows, k, s, row);
-    const float *lrow = logits + (int64_t)row * (DENSE ? lstride : (int64_t)ri.ncols);
+    const int sbk = 1 << lsbk, ncols = nsb << lsbk;
+    const int32_t *si = si_base + (int64_t)row * nsb;
+    const int32_t ks_raw = (p_ks ? p_ks : p_ke)[row];   // no load behind a branch
+    const int ks = p_ks ? ks_raw : 0, ke = p_ke[row];
+    const int valid_cols = max(0, min(uniform(p_kept[row]), nsb)) * sbk;
+    const float *lrow = logits + (int64_t)row * (DENSE ? lstride : (int64_t)ncols);
     const int c0 = tid * KPT;   // the thread's KPT columns lie in one sparse block
     int tok0 = 0;               // token of column c0
-    if (c0 < ri.ncols) tok0 = (ri.si[c0 >> s.lsbk] << s.lsbk) + (c0 & (s.sbk - 1));
+    if (c0 < ncols) tok0 = (si[c0 >> lsbk] << lsbk) + (c0 & (sbk - 1));
     // Sparse: columns c0.. (bounded by the row's column count, not its kept count, so
     // the load does not wait for the kept load; every column was written).  Dense:
     // tokens tok0.. once the schedule entry is in (tok0 is a multiple of KPT, lcols of 64,
     // so the run lies wholly inside or outside the row; -1 entries past the kept count
     // give tok0 < 0 and read nothing).  Columns past the kept blocks are masked below.
     const int l0 = DENSE ? tok0 : c0;
-    const bool rd = DENSE ? (c0 < ri.ncols && tok0 >= 0 && tok0 < lcols) : (c0 < ri.ncols);
+    const bool rd = DENSE ? (c0 < ncols && tok0 >= 0 && tok0 < lcols) : (c0 < ncols);
     float x[KPT];
 #pragma unroll
     for (int i = 0; i < KPT; i += 4) {
@@ -1082,15 +1099,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(Rows rows, KCa
     }
     // every slot [0, nsb) is written by the expansion (-1 past the kept count), so the
     // copy need not wait for the kept load
-    for (int i = tid; i < s.nsb; i += kTopkThreads) s_si[i] = ri.si[i];
+    for (int i = tid; i < nsb; i += kTopkThreads) s_si[i] = si[i];
     select_clear(s_sel);
     // The valid columns of the thread (in a kept block, token in [ks, ke)) are one run
     // [c0 + lo, c0 + hi): a bit mask, so no key needs a branch.  The scoring never
     // writes -0 (see bits_key).
     static_assert(KPT < 32, "one mask bit per key");
-    const int lo = min(KPT, max(0, ri.ks - tok0));
-    const int hi = max(0, min(min(KPT, ri.valid_cols - c0),
-                              min(ri.ke, DENSE ? lcols : INT_MAX) - tok0));
+    const int lo = min(KPT, max(0, ks - tok0));
+    const int hi = max(0, min(min(KPT, valid_cols - c0),
+                              min(ke, DENSE ? lcols : INT_MAX) - tok0));
     const uint32_t vmask = ((1u << hi) - 1u) & ~((1u << lo) - 1u);
     uint32_t key[KPT];
 #pragma unroll
@@ -1102,7 +1119,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(Rows rows, KCa
     block_key_stats<kTopkThreads>(key, live, s_sel, nvalid, kmin, kmax);
     select_topk<kTopkThreads, KPT>(key, live, nvalid, kmin, kmax, topk,
                                    out + (int64_t)row * ostride, s_sel, s_stage,
-                                   SparseTokens<KPT>{s_si, s.lsbk});
+                                   SparseTokens<KPT>{s_si, lsbk});
 }
 
 // Rows >= CUs: one workgroup per row; waves take units of the row's valid 64-column
@@ -1632,20 +1649,22 @@ static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const 
     const dim3 sgrid(rows.num_rows, (ngroups + gpw - 1) / gpw);
     if (gpw == 8)
         hipExtLaunchKernelGGL((score_split_kernel<QF, 2>), sgrid, dim3(kScoreThreads), 0, stream,
-                              timing.start, timing.stop, 0, rows, q_values, q_scales, weights, k, s,
-                              logits, gpw);
+                              timing.start, timing.stop, 0, s.sparse_indices, s.pages, q_values,
+                              q_scales, weights, s.nsb, s.sbk, gpw, rows, k, logits);
     else
         hipExtLaunchKernelGGL((score_split_kernel<QF, 4>), sgrid, dim3(kScoreThreads), 0, stream,
-                              timing.start, timing.stop, 0, rows, q_values, q_scales, weights, k, s,
-                              logits, gpw);
+                              timing.start, timing.stop, 0, s.sparse_indices, s.pages, q_values,
+                              q_scales, weights, s.nsb, s.sbk, gpw, rows, k, logits);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (ncols <= 8 * kTopkThreads)
         hipLaunchKernelGGL((topk_split_kernel<false, 8>), dim3(rows.num_rows), dim3(kTopkThreads), 0,
-                           stream, rows, k, s, logits, (int64_t)0, 0, topk, out, out_stride);
+                           stream, logits, s.sparse_indices, rows.ks, rows.ke, s.kept, s.nsb, s.lsbk,
+                           (int64_t)0, 0, topk, out, out_stride);
     else
         hipLaunchKernelGGL((topk_split_kernel<false, 16>), dim3(rows.num_rows), dim3(kTopkThreads), 0,
-                           stream, rows, k, s, logits, (int64_t)0, 0, topk, out, out_stride);
+                           stream, logits, s.sparse_indices, rows.ks, rows.ke, s.kept, s.nsb, s.lsbk,
+                           (int64_t)0, 0, topk, out, out_stride);
     return hipGetLastError();
 }
 
@@ -1687,10 +1706,12 @@ hipError_t launch_dense_topk(const Rows &rows, const KCache &k, const Schedule &
     const int nsbcols = s.nsb * s.sbk;   // candidate columns a row
     if (nsbcols <= 8 * kTopkThreads)
         hipLaunchKernelGGL((topk_split_kernel<true, 8>), dim3(rows.num_rows), dim3(kTopkThreads), 0,
-                           stream, rows, k, s, logits, logits_stride, ncols, topk, out, out_stride);
+                           stream, logits, s.sparse_indices, rows.ks, rows.ke, s.kept, s.nsb, s.lsbk,
+                           logits_stride, ncols, topk, out, out_stride);
     else
         hipLaunchKernelGGL((topk_split_kernel<true, 16>), dim3(rows.num_rows), dim3(kTopkThreads), 0,
-                           stream, rows, k, s, logits, logits_stride, ncols, topk, out, out_stride);
+                           stream, logits, s.sparse_indices, rows.ks, rows.ke, s.kept, s.nsb, s.lsbk,
+                           logits_stride, ncols, topk, out, out_stride);
     return hipGetLastError();
 }
 
