@@ -1124,25 +1124,39 @@ __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(
 
 // Rows >= CUs: one workgroup per row; waves take units of the row's valid 64-column
 // groups from a shared counter, logits stay in LDS, then the same workgroup selects.
-// logits_out (optional) gets a copy of every column.
+// logits_out (optional) gets a copy of every column.  The leading scalar arguments are
+// what the first loads need (the row's schedule entries and kept count, its query):
+// preloaded into SGPRs at wave launch, so those loads are one round trip.  The table
+// row is not checked here: the expansion lists nothing for a row whose table row is
+// invalid (kept = 0), and the schedule comes from the expansion of the same rows.
 template <int QF, int NT, int KPT>
-__global__ __launch_bounds__(NT) void fused_row_kernel(Rows rows, const void *qv, const void *qs,
-                                                       const float *weights, KCache k, Schedule s,
-                                                       float *logits_out, int32_t topk,
-                                                       int32_t *out, int64_t ostride) {
+__global__ __launch_bounds__(NT) void fused_row_kernel(
+    const int32_t *si_base, const int32_t *pg_base, const void *qv, const void *qs,
+    const float *weights, const int32_t *p_kept, int32_t nsb, int32_t lsbk, Rows rows, KCache k,
+    float *logits_out, int32_t topk, int32_t *out, int64_t ostride) {
     __shared__ alignas(16) uint32_t s_word[kMaxRowCols];   // column words (bits_key), then the stage
     __shared__ int32_t s_si[kMaxNSB];
     __shared__ int32_t s_pg[kMaxNSB];
     __shared__ int s_unit;
     __shared__ SelectLds<NT, 5> s_sel;
     const int row = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1);
-    const RowInfo ri = row_info(rows, k, s, row);
+    const int sbk = 1 << lsbk;
+    RowInfo ri;
+    ri.si = si_base + (int64_t)row * nsb;
+    ri.pg = pg_base + (int64_t)row * nsb;
+    ri.kept = max(0, min(uniform(p_kept[row]), nsb));
+    const int32_t ks_raw = (rows.ks ? rows.ks : rows.ke)[row];   // no load behind a branch
+    ri.ks = rows.ks ? ks_raw : 0;
+    ri.ke = rows.ke[row];
+    ri.valid_cols = ri.kept * sbk;
+    ri.ncols = nsb * sbk;
+    ri.tbl_ok = true;
     QFrag<QF> f;
     load_q<QF>(f, qv, qs, weights, row, lane);   // overlaps the schedule copy
     // Every slot [0, nsb) is written by the expansion (-1 past the kept count), so the
     // copy is not bound by the kept load: the schedule, the kept count and the query
     // are one memory round trip, not two.
-    for (int i = tid; i < s.nsb; i += NT) {
+    for (int i = tid; i < nsb; i += NT) {
         s_si[i] = ri.si[i];
         s_pg[i] = ri.pg[i];
     }
@@ -1158,7 +1172,7 @@ __global__ __launch_bounds__(NT) void fused_row_kernel(Rows rows, const void *qv
     constexpr int U = NT >= 1024 ? 1 : (QF == 0 ? 4 : 2);
     const int vgroups = (ri.valid_cols + 63) / 64;
     const int nunits = (vgroups + U - 1) / U;
-    const int valid_cols = ri.valid_cols, sbk = s.sbk;
+    const int valid_cols = ri.valid_cols;
     float *lout = logits_out ? logits_out + (int64_t)row * ri.ncols : nullptr;
     score_units<QF, U>(
         k, f, ri.ks, ri.ke,
@@ -1204,7 +1218,7 @@ __global__ __launch_bounds__(NT) void fused_row_kernel(Rows rows, const void *qv
         key[i + 3] = c + 3 < ri.valid_cols ? bits_key(x.w) : 0u;
     }
     select_topk<NT, KPT, true>(key, keys_live(key), nvalid, kmin, kmax, topk, out + (int64_t)row * ostride, s_sel,
-                         reinterpret_cast<int32_t *>(s_word), SparseTokens<KPT>{s_si, s.lsbk});
+                         reinterpret_cast<int32_t *>(s_word), SparseTokens<KPT>{s_si, lsbk});
 }
 
 // Dense scoring (the comparator): column t is token t, every token < max_ctx.
@@ -1632,8 +1646,9 @@ static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const 
         constexpr int NT = QF == 0 ? 1024 : 512;
 #define IDX_LAUNCH_FUSED(KPT_)                                                                   \
     hipExtLaunchKernelGGL((fused_row_kernel<QF, NT, KPT_>), dim3(rows.num_rows), dim3(NT), 0,   \
-                          stream, timing.start, timing.stop, 0, rows, q_values, q_scales, weights, \
-                          k, s, logits_out, topk, out, out_stride)
+                          stream, timing.start, timing.stop, 0, s.sparse_indices, s.pages,        \
+                          q_values, q_scales, weights, s.kept, s.nsb, s.lsbk, rows, k, logits_out, \
+                          topk, out, out_stride)
         if (ncols <= NT * 4) IDX_LAUNCH_FUSED(4);
         else if (ncols <= NT * 8) IDX_LAUNCH_FUSED(8);
         else IDX_LAUNCH_FUSED(16);
