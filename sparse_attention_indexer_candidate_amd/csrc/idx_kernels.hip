@@ -1078,28 +1078,32 @@ __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(
     const int valid_cols = max(0, min(uniform(p_kept[row]), nsb)) * sbk;
     const float *lrow = logits + (int64_t)row * (DENSE ? lstride : (int64_t)ncols);
     const int c0 = tid * KPT;   // the thread's KPT columns lie in one sparse block
-    int tok0 = 0;               // token of column c0
-    if (c0 < ncols) tok0 = (si[c0 >> lsbk] << lsbk) + (c0 & (sbk - 1));
-    // Sparse: columns c0.. (bounded by the row's column count, not its kept count, so
-    // the load does not wait for the kept load; every column was written).  Dense:
-    // tokens tok0.. once the schedule entry is in (tok0 is a multiple of KPT, lcols of 64,
-    // so the run lies wholly inside or outside the row; -1 entries past the kept count
-    // give tok0 < 0 and read nothing).  Columns past the kept blocks are masked below.
-    const int l0 = DENSE ? tok0 : c0;
-    const bool rd = DENSE ? (c0 < ncols && tok0 >= 0 && tok0 < lcols) : (c0 < ncols);
+    const bool has = c0 < ncols;
+    // Every load of the prologue is issued before any is used, and none sits behind a
+    // branch (a branch around a load makes the compiler wait for it there): addresses
+    // are clamped into the buffers and the values masked afterwards.  Sparse logits are
+    // columns c0.. (every column was written); dense ones are tokens tok0.., read once
+    // the schedule entry is in (tok0 is a multiple of KPT, lcols of 64, so the run lies
+    // wholly inside or outside the row; -1 entries past the kept count give tok0 < 0).
+    static_assert(kMaxNSB <= kTopkThreads, "one schedule entry a thread for the LDS copy");
+    const int32_t si_c0 = si[min(c0 >> lsbk, nsb - 1)];
+    const int32_t si_cp = si[min(tid, nsb - 1)];
     float x[KPT];
+    auto load_run = [&](int at, bool rd) {
 #pragma unroll
-    for (int i = 0; i < KPT; i += 4) {
-        float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        if (rd) v = *(const float4 *)(lrow + l0 + i);
-        x[i] = v.x;
-        x[i + 1] = v.y;
-        x[i + 2] = v.z;
-        x[i + 3] = v.w;
-    }
-    // every slot [0, nsb) is written by the expansion (-1 past the kept count), so the
-    // copy need not wait for the kept load
-    for (int i = tid; i < nsb; i += kTopkThreads) s_si[i] = si[i];
+        for (int i = 0; i < KPT; i += 4) {
+            float4 v = *(const float4 *)(lrow + (rd ? at : 0) + i);
+            if (!rd) v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            x[i] = v.x;
+            x[i + 1] = v.y;
+            x[i + 2] = v.z;
+            x[i + 3] = v.w;
+        }
+    };
+    if constexpr (!DENSE) load_run(c0, has);
+    const int tok0 = has ? (si_c0 << lsbk) + (c0 & (sbk - 1)) : 0;   // token of column c0
+    if constexpr (DENSE) load_run(tok0, has && tok0 >= 0 && tok0 < lcols);
+    if (tid < nsb) s_si[tid] = si_cp;
     select_clear(s_sel);
     // The valid columns of the thread (in a kept block, token in [ks, ke)) are one run
     // [c0 + lo, c0 + hi): a bit mask, so no key needs a branch.  The scoring never
