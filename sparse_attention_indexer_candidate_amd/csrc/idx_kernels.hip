@@ -80,6 +80,15 @@ constexpr int kMaxRowCols = 8192;    // NB * cbs
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// A zero the compiler cannot see through: added to a uniform index it makes the load a
+// vector load, which issues in program order beside the kernel's other first loads
+// (a scalar load of a uniform address may be scheduled after a later wait).
+__device__ __forceinline__ int opaque_zero() {
+    int z;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+    return z;
+}
+
 // 64-bit value from two 32-bit halves as returned by v_readlane (a signed int): both
 // halves are zero-extended, never sign-extended.
 __device__ __forceinline__ uint64_t join64(int hi, int lo) {
@@ -1073,9 +1082,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(
     const int row = blockIdx.x, tid = threadIdx.x;
     const int sbk = 1 << lsbk, ncols = nsb << lsbk;
     const int32_t *si = si_base + (int64_t)row * nsb;
-    const int32_t ks_raw = (p_ks ? p_ks : p_ke)[row];   // no load behind a branch
-    const int ks = p_ks ? ks_raw : 0, ke = p_ke[row];
-    const int valid_cols = max(0, min(uniform(p_kept[row]), nsb)) * sbk;
+    const int vrow = row + opaque_zero();                  // vector loads, issued first
+    const int32_t ks_raw = (p_ks ? p_ks : p_ke)[vrow];     // no load behind a branch
+    const int ks = p_ks ? ks_raw : 0, ke = p_ke[vrow];
+    const int valid_cols = max(0, min(p_kept[vrow], nsb)) * sbk;
     const float *lrow = logits + (int64_t)row * (DENSE ? lstride : (int64_t)ncols);
     const int c0 = tid * KPT;   // the thread's KPT columns lie in one sparse block
     const bool has = c0 < ncols;
@@ -1149,9 +1159,6 @@ __global__ __launch_bounds__(NT) void fused_row_kernel(
     ri.si = si_base + (int64_t)row * nsb;
     ri.pg = pg_base + (int64_t)row * nsb;
     ri.kept = max(0, min(uniform(p_kept[row]), nsb));
-    const int32_t ks_raw = (rows.ks ? rows.ks : rows.ke)[row];   // no load behind a branch
-    ri.ks = rows.ks ? ks_raw : 0;
-    ri.ke = rows.ke[row];
     ri.valid_cols = ri.kept * sbk;
     ri.ncols = nsb * sbk;
     ri.tbl_ok = true;
@@ -1164,6 +1171,12 @@ __global__ __launch_bounds__(NT) void fused_row_kernel(
         s_si[i] = ri.si[i];
         s_pg[i] = ri.pg[i];
     }
+    // ks / ke (their pointers are not preloaded) are needed only for the validity of the
+    // scored columns; loaded after the first loads so no wait for them comes first
+    const int vrow = row + opaque_zero();
+    const int32_t ks_raw = (rows.ks ? rows.ks : rows.ke)[vrow];   // no load behind a branch
+    ri.ks = rows.ks ? ks_raw : 0;
+    ri.ke = rows.ke[vrow];
     if (tid == 0) s_unit = 0;
     select_clear(s_sel);
     __syncthreads();

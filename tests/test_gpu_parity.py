@@ -496,3 +496,68 @@ def test_invariances_page_permutation_scale_and_weights():
     g3, r3 = run_and_compare(case_c, tag="inv-shuffle")
     np.testing.assert_array_equal(r0["indices"], r3["indices"])
     np.testing.assert_array_equal(r0["logits"].view(np.uint32), r3["logits"].view(np.uint32))
+
+
+@pytest.mark.parametrize("which", ["decode_batch", "rows_per_cu"])
+def test_step_graph_replays_match_eager(which):
+    """A step (expansion, sparse scoring and the dense comparator) captured as one HIP
+    graph on its own stream and replayed several times, with eager steps of other
+    inputs on the same stream between the replays: every replay gives the eager
+    result, bit for bit (the library records no memset and allocates nothing)."""
+    import sparse_attention_indexer_candidate_amd as idx
+
+    spec = W.config(2) if which == "decode_batch" else WEIGHT_PATHS["fused"]
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        sh = stream.cuda_stream
+        runs = []
+        for seed in (0, 1):
+            case = W.generate(spec, seed)
+            d = to_device(case, DEV)
+            s = case.spec
+            cfg = idx.make_config(s.num_heads, s.head_dim, idx.IDX_Q_MXFP4, s.page_size, s.cbs, 0,
+                                  s.nb, s.topk)
+            R = case.num_rows
+            ctx = int(case.row_ke.max() + 63) // 64 * 64
+            rows = idx.make_rows(d.row_ke, d.row_ks, d.row_table)
+            kc = idx.make_kcache(d.layers[0].pool, s.page_size, s.head_dim, d.block_table)
+            sched = idx.Schedule(cfg, R, DEV)
+            out = torch.full((R, s.topk), -7, dtype=torch.int32, device=DEV)
+            dout = torch.full((R, s.topk), -7, dtype=torch.int32, device=DEV)
+            ws = torch.empty(idx.idx_workspace_bytes(cfg, R, ctx), dtype=torch.uint8, device=DEV)
+            qv, qs = d.layers[0].q("mxfp4")
+            calls = [idx.bind_expand_candidates(cfg, rows, kc, d.candidate_blocks,
+                                                d.candidate_blocks.stride(0), sched.struct,
+                                                stream=sh),
+                     idx.bind_sparse_mqa_logits_topk(cfg, rows, qv, qs, d.layers[0].weights, kc,
+                                                     sched.struct, out, out.stride(0), None, ws,
+                                                     ws.numel(), stream=sh),
+                     idx.bind_dense_masked_logits_topk(cfg, rows, ctx, qv, qs,
+                                                       d.layers[0].weights, kc, sched.struct, dout,
+                                                       dout.stride(0), None, 0, ws, ws.numel(),
+                                                       stream=sh)]
+            runs.append(dict(keep=(d, rows, kc, sched, ws), calls=calls, out=out, dout=dout))
+        for r in runs:                                   # eager results
+            for c in r["calls"]:
+                c()
+        torch.cuda.synchronize()
+        for r in runs:
+            r["ref"], r["dref"] = r["out"].clone(), r["dout"].clone()
+        np.testing.assert_array_equal(runs[0]["ref"].cpu().numpy(), runs[0]["dref"].cpu().numpy())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for c in runs[0]["calls"]:
+                c()
+        other = runs[1]
+        for rep in range(3):
+            runs[0]["out"].fill_(-7)
+            runs[0]["dout"].fill_(-7)
+            other["out"].fill_(-7)
+            for c in other["calls"]:                     # eager work between replays
+                c()
+            g.replay()
+            torch.cuda.synchronize()
+            _say(f"[graph {which}] replay {rep}")
+            assert torch.equal(runs[0]["out"], runs[0]["ref"]), f"replay {rep}: sparse indices"
+            assert torch.equal(runs[0]["dout"], runs[0]["dref"]), f"replay {rep}: dense indices"
+            assert torch.equal(other["out"], other["ref"]), f"replay {rep}: eager step"
