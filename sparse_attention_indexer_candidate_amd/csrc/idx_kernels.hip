@@ -21,6 +21,14 @@
 //                       the comparator: every token of [ks, ke) with the same
 //                       per-tile code, then the candidates' keys gathered from the
 //                       dense row in schedule order and the same selection
+//  measure_read_kernel, measure_mfma_kernel
+//                       reference rates for the roofline (read stream, MFMA-only loop)
+//
+// Kernel arguments: the expansion, split and one-row kernels take the pointers their
+// first loads need as leading scalar arguments, which gfx950 preloads into SGPRs at
+// wave launch (the build passes -amdgpu-kernarg-preload-count), and issue those loads
+// before any is used, with no load behind a branch: a kernel's first memory round trip
+// is then its first data, not its own arguments.
 //
 // The operation follows the vLLM DeepSeek-V4.1 pages (sparse_mqa_indexer, the
 // sparse indexer backend source, rocm_paged_mxfp4_indexer): logits over the
