@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "candidate cols scored/s & rows/s incl. top-k; % of HBM / MXFP4-MFMA roofline"
 HBM_PEAK_GBS = 8000.0
 MXFP4_PEAK_TFLOPS = 10066.0
+VALU_PEAK_TLANEOPS = 256 * 4 * 16 * 2.4e9 / 1e12   # 39.3: one op a lane a cycle, every SIMD
 TIMING_STRIDE = 16         # steps between two timed scoring launches
 KERNEL_SOURCES = ["sparse_attention_indexer_candidate_amd/csrc/idx_kernels.hip",
                   "sparse_attention_indexer_candidate_amd/csrc/idx_api.hip"]
@@ -360,6 +361,13 @@ def main():
         roof = {"bound": "mfma", "achieved": flops / avg_kernel_s / 1e12,
                 "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s"}
         roof["frac"] = roof["achieved"] / MXFP4_PEAK_TFLOPS
+        # What actually bounds the contraction here: its ReLU-weight epilogue, one integer
+        # max and one fp32 FMA per (head, column) element on the vector ALUs, whose peak is
+        # 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane-operations per second.
+        lane_ops = 2 * spec.num_heads * scored / spec.layers
+        roof["epilogue_valu"] = {"achieved": lane_ops / avg_kernel_s / 1e12,
+                                 "peak": VALU_PEAK_TLANEOPS, "unit": "T lane-ops/s",
+                                 "frac": lane_ops / avg_kernel_s / 1e12 / VALU_PEAK_TLANEOPS}
     else:
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS}
