@@ -151,6 +151,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--per-layer-calls", action="store_true",
+                    help="one sparse call per layer instead of one multi-layer call")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step as a captured HIP graph (measured slower than direct "
                          "launches on this stack: 21.7 vs 14.8 us a decode-batch step)")
@@ -225,6 +227,13 @@ def main():
     else:
         kernel_name = "score_split_kernel"
     fused = kernel_name in ("row_group_kernel", "fused_row_kernel")
+    # The step's consuming layers go to the library in one call (one launch when the rows
+    # take the one-row kernel); the timing events then ride on that call's scoring launch.
+    layers_call = args.path != "dense" and spec.layers > 1 and not args.per_layer_calls
+    launch_layers = 1
+    if layers_call and kernel_name == "fused_row_kernel":
+        kernel_name, launch_layers = "fused_layers_kernel", spec.layers
+    events_per_step = 1 if layers_call else spec.layers
     if args.path == "dense":
         # every context token's K, the row's query state, the logits row written
         step_bytes = (algorithmic_bytes(case, args.q_format, ctx, with_output=False)
@@ -259,6 +268,8 @@ def main():
             kc=[idx.make_kcache(L.pool, spec.page_size, spec.head_dim, d.block_table) for L in d.layers],
             sched=idx.Schedule(cfg, R, dev),
             out=torch.empty((R, spec.topk), dtype=torch.int32, device=dev),
+            out_l=[torch.empty((R, spec.topk), dtype=torch.int32, device=dev)
+                   for _ in range(spec.layers)],
             ws=torch.empty(ws_bytes, dtype=torch.uint8, device=dev)))
     # A stream of the bench's own (default priority), current for the rest of the run: the
     # step graphs are captured on it and replayed on it, and the directly launched steps
@@ -270,7 +281,7 @@ def main():
     # host about 20 us per launch; timing every TIMING_STRIDE-th step keeps the host
     # ahead of the GPU on short steps.
     timed_steps = [i for i in range(args.steps) if i % TIMING_STRIDE == 0]
-    n_events = len(timed_steps) * spec.layers
+    n_events = len(timed_steps) * events_per_step
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(n_events)]
     for a, b in ev:            # materialise the HIP events before the timed region
@@ -288,7 +299,13 @@ def main():
                                                  d.candidate_blocks.stride(0), p["sched"].struct,
                                                  stream=sh)
         p["layers"] = []
-        for layer, L in enumerate(d.layers):
+        if layers_call:
+            entries = [(*L.q(args.q_format), L.weights, p["kc"][layer], p["out_l"][layer], None)
+                       for layer, L in enumerate(d.layers)]
+            p["layers"].append(idx.bind_sparse_mqa_logits_topk_layers(
+                cfg, p["rows"], p["sched"].struct, entries, spec.topk, p["ws"], p["ws"].numel(),
+                stream=sh))
+        for layer, L in enumerate([] if layers_call else d.layers):
             qv, qs = L.q(args.q_format)
             if args.path == "dense":
                 call = idx.bind_dense_masked_logits_topk(
@@ -305,7 +322,7 @@ def main():
         p["expand"]()
         for layer, call in enumerate(p["layers"]):
             if timed:
-                set_events(*ev_raw[(i // TIMING_STRIDE) * spec.layers + layer])
+                set_events(*ev_raw[(i // TIMING_STRIDE) * events_per_step + layer])
             call()
             if timed:
                 set_events(None, None)
@@ -342,7 +359,7 @@ def main():
     avg_kernel_s = float(np.mean(kernel_ms)) / 1e3
     cols_per_step = int(ends.astype(np.int64).sum()) * spec.layers
     ctx_cols_per_step = int(ctx.sum()) * spec.layers
-    launch_bytes = kernel_bytes
+    launch_bytes = kernel_bytes * launch_layers
     achieved = launch_bytes / avg_kernel_s / 1e9
 
     traffic = None
@@ -356,7 +373,7 @@ def main():
     # Prefill chunks share each K tile among many rows (K comes from L2), so the MX-FP4
     # MFMA rate bounds them; decode rows each stream their own K from HBM.
     scored = ctx_cols_per_step if args.path == "dense" else cols_per_step
-    flops = 2 * spec.num_heads * spec.head_dim * scored / spec.layers
+    flops = 2 * spec.num_heads * spec.head_dim * scored / spec.layers * launch_layers
     if spec.mode == "prefill":
         roof = {"bound": "mfma", "achieved": flops / avg_kernel_s / 1e12,
                 "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s"}
@@ -364,7 +381,7 @@ def main():
         # What actually bounds the contraction here: its ReLU-weight epilogue, one integer
         # max and one fp32 FMA per (head, column) element on the vector ALUs, whose peak is
         # 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane-operations per second.
-        lane_ops = 2 * spec.num_heads * scored / spec.layers
+        lane_ops = 2 * spec.num_heads * scored / spec.layers * launch_layers
         roof["epilogue_valu"] = {"achieved": lane_ops / avg_kernel_s / 1e12,
                                  "peak": VALU_PEAK_TLANEOPS, "unit": "T lane-ops/s",
                                  "frac": lane_ops / avg_kernel_s / 1e12 / VALU_PEAK_TLANEOPS}
@@ -399,6 +416,7 @@ def main():
                    "heads": spec.num_heads, "head_dim": spec.head_dim, "page_size": spec.page_size,
                    "valid_cols_per_step": cols_per_step, "q_format": args.q_format,
                    "path": args.path,
+                   "calls": "one call for all layers" if layers_call else "one call per layer",
                    "launch": (f"HIP graph per step; every {TIMING_STRIDE}th step launched directly "
                               "with timing events") if args.graph else "direct",
                    "input_copies": nrep, "seed": args.seed},

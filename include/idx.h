@@ -169,6 +169,35 @@ int idx_sparse_mqa_logits_topk(const idx_config *cfg, const idx_rows *rows, cons
                                int64_t out_stride, float *logits_out, void *workspace,
                                size_t workspace_bytes, void *stream);
 
+/* Steps a2-a6 for several consuming layers of one step (the pages' multi-layer
+ * decode: the layers after the candidate source reuse one expansion and schedule,
+ * each with its own K cache, query and weights).  Same result, layer by layer, as
+ * calling idx_sparse_mqa_logits_topk once per layer in layer order.  With two or
+ * more layers whose rows take the one-row-per-workgroup kernel (num_rows >= the
+ * device's CUs, and not the prefill row-group case) all layers run in one launch
+ * with two rows on a CU at a time, so one row's selection overlaps another's K
+ * stream.  layers is a HOST array of num_layers
+ * (1..IDX_MAX_LAYERS) entries.  Every layer's k must equal layers[0].k in every field
+ * but values and scales (one page geometry and block table for the step, as the
+ * schedule requires).  workspace: as for idx_sparse_mqa_logits_topk when some
+ * layer's logits_out is NULL; it is reused layer after layer.  The timing events
+ * (idx_set_timing_events), if set, time the one launch, or else the last layer's
+ * scoring kernel. */
+#define IDX_MAX_LAYERS 8
+typedef struct {
+    const void *q_values;          /* as in idx_sparse_mqa_logits_topk */
+    const void *q_scales;
+    const float *weights;
+    idx_kcache k;                  /* this layer's pool */
+    int32_t *topk_indices;         /* int32 rows of out_stride elements */
+    float *logits_out;             /* NULL or float [num_rows][NB*cbs] */
+} idx_layer;
+
+int idx_sparse_mqa_logits_topk_layers(const idx_config *cfg, const idx_rows *rows,
+                                      const idx_schedule *sched, int32_t num_layers,
+                                      const idx_layer *layers, int64_t out_stride,
+                                      void *workspace, size_t workspace_bytes, void *stream);
+
 /* Step a9, the comparator the sparse path replaces (the dense indexer scores the
  * whole context and masks to the candidates: module summary of the
  * sparse_mqa_indexer page): scores every token of [ks, ke) with the same

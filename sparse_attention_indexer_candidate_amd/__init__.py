@@ -28,9 +28,11 @@ IDX_MAX_TOPK = 8192
 
 EXPORTED = ("idx_check_config", "idx_num_sparse_blocks", "idx_schedule_work_bytes",
             "idx_workspace_bytes", "idx_last_error", "idx_set_timing_events",
-            "idx_expand_candidates", "idx_sparse_mqa_logits_topk", "idx_dense_masked_logits_topk",
+            "idx_expand_candidates", "idx_sparse_mqa_logits_topk",
+            "idx_sparse_mqa_logits_topk_layers", "idx_dense_masked_logits_topk",
             "idx_measure_read", "idx_measure_mfma", "idx_measure_mfma_flops")
 IDX_MEASURE_WGS = 4096
+IDX_MAX_LAYERS = 8
 
 
 class IdxError(RuntimeError):
@@ -62,6 +64,12 @@ class idx_rows(ctypes.Structure):
 class idx_schedule(ctypes.Structure):
     _fields_ = [("sparse_indices", ctypes.c_void_p), ("end", ctypes.c_void_p),
                 ("work", ctypes.c_void_p), ("work_bytes", ctypes.c_size_t)]
+
+
+class idx_layer(ctypes.Structure):
+    _fields_ = [("q_values", ctypes.c_void_p), ("q_scales", ctypes.c_void_p),
+                ("weights", ctypes.c_void_p), ("k", idx_kcache),
+                ("topk_indices", ctypes.c_void_p), ("logits_out", ctypes.c_void_p)]
 
 
 def _load():
@@ -97,6 +105,9 @@ def _load():
                                              P(idx_kcache), P(idx_schedule), vp, i64, vp, vp, sz,
                                              vp]
     L.idx_sparse_mqa_logits_topk.restype = ctypes.c_int
+    L.idx_sparse_mqa_logits_topk_layers.argtypes = [P(idx_config), P(idx_rows), P(idx_schedule),
+                                                    i32, P(idx_layer), i64, vp, sz, vp]
+    L.idx_sparse_mqa_logits_topk_layers.restype = ctypes.c_int
     L.idx_dense_masked_logits_topk.argtypes = [P(idx_config), P(idx_rows), i32, vp, vp, vp,
                                                P(idx_kcache), P(idx_schedule), vp, i64, vp, i64,
                                                vp, sz, vp]
@@ -171,6 +182,24 @@ def idx_sparse_mqa_logits_topk(cfg, rows, q_values, q_scales, weights, k, sched,
         _p(workspace), workspace_bytes, _p(stream)))
 
 
+def make_layers(layers):
+    """Host array of idx_layer from (q_values, q_scales, weights, kcache, topk_indices,
+    logits_out or None) tuples."""
+    arr = (idx_layer * len(layers))()
+    for i, (qv, qs, w, k, out, lout) in enumerate(layers):
+        arr[i] = idx_layer(_p(qv), _p(qs), _p(w), k, _p(out), _p(lout))
+    return arr
+
+
+def idx_sparse_mqa_logits_topk_layers(cfg, rows, sched, layers, out_stride, workspace=None,
+                                      workspace_bytes=0, stream=None):
+    """layers: a make_layers() array (or tuples for it); every layer in one call."""
+    arr = layers if isinstance(layers, ctypes.Array) else make_layers(layers)
+    return _check(lib.idx_sparse_mqa_logits_topk_layers(
+        ctypes.byref(cfg), ctypes.byref(rows), ctypes.byref(sched), len(arr), arr, out_stride,
+        _p(workspace), workspace_bytes, _p(stream)))
+
+
 def idx_dense_masked_logits_topk(cfg, rows, max_ctx, q_values, q_scales, weights, k, sched,
                                  topk_indices, out_stride, logits_out=None, logits_stride=0,
                                  workspace=None, workspace_bytes=0, stream=None):
@@ -231,6 +260,16 @@ def bind_sparse_mqa_logits_topk(cfg, rows, q_values, q_scales, weights, k, sched
                       vp(weights), ctypes.byref(k), ctypes.byref(sched), vp(topk_indices),
                       out_stride, vp(logits_out), vp(workspace), workspace_bytes, vp(stream)),
                      (cfg, rows, k, sched))
+
+
+def bind_sparse_mqa_logits_topk_layers(cfg, rows, sched, layers, out_stride, workspace=None,
+                                       workspace_bytes=0, stream=None):
+    arr = layers if isinstance(layers, ctypes.Array) else make_layers(layers)
+    vp = lambda x: ctypes.c_void_p(_p(x))
+    return BoundCall(lib.idx_sparse_mqa_logits_topk_layers,
+                     (ctypes.byref(cfg), ctypes.byref(rows), ctypes.byref(sched), len(arr), arr,
+                      out_stride, vp(workspace), workspace_bytes, vp(stream)),
+                     (cfg, rows, sched, arr))
 
 
 def bind_dense_masked_logits_topk(cfg, rows, max_ctx, q_values, q_scales, weights, k, sched,

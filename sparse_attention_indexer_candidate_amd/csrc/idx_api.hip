@@ -259,6 +259,68 @@ int idx_sparse_mqa_logits_topk(const idx_config *cfg, const idx_rows *rows, cons
     return ok();
 }
 
+int idx_sparse_mqa_logits_topk_layers(const idx_config *cfg, const idx_rows *rows,
+                                      const idx_schedule *sched, int32_t num_layers,
+                                      const idx_layer *layers, int64_t out_stride,
+                                      void *workspace, size_t workspace_bytes, void *stream) {
+    int32_t sbk = 0;
+    int rc;
+    if ((rc = check_filled(cfg, &sbk)) || (rc = check_rows(rows)) ||
+        (rc = check_schedule(cfg, rows, sched)))
+        return rc;
+    if (num_layers < 1 || num_layers > IDX_MAX_LAYERS)
+        return fail(IDX_EINVAL, "num_layers %d must be in [1, %d]", num_layers, IDX_MAX_LAYERS);
+    if (!layers) return fail(IDX_EINVAL, "layers is NULL");
+    if (out_stride < cfg->topk)
+        return fail(IDX_EINVAL, "out_stride %lld < topk %d", (long long)out_stride, cfg->topk);
+    const idx_kcache &k0 = layers[0].k;
+    bool need_ws = false;
+    idx::LayerSet ls = {};
+    for (int l = 0; l < num_layers; ++l) {
+        const idx_layer &L = layers[l];
+        if ((rc = check_kcache(cfg, &L.k)) || (rc = check_q(cfg, L.q_values, L.q_scales, L.weights))) {
+            char why[sizeof g_err];
+            memcpy(why, g_err, sizeof why);
+            return fail(rc, "layer %d: %s", l, why);
+        }
+        const idx_kcache &k = L.k;
+        if (k.values_page_stride != k0.values_page_stride ||
+            k.scales_page_stride != k0.scales_page_stride || k.num_pages != k0.num_pages ||
+            k.block_table != k0.block_table || k.block_table_stride != k0.block_table_stride ||
+            k.num_tables != k0.num_tables || k.pages_per_table != k0.pages_per_table)
+            return fail(IDX_EINVAL, "layer %d: k cache geometry differs from layer 0's (only "
+                        "values and scales may differ)", l);
+        if (!L.topk_indices || !aligned(L.topk_indices, 4))
+            return fail(IDX_EINVAL, "layer %d: topk_indices must be non-NULL and 4-byte aligned", l);
+        if (L.logits_out && !aligned(L.logits_out, 16))
+            return fail(IDX_EINVAL, "layer %d: logits_out must be 16-byte aligned", l);
+        need_ws = need_ws || !L.logits_out;
+        ls.q_values[l] = L.q_values;
+        ls.q_scales[l] = L.q_scales;
+        ls.weights[l] = L.weights;
+        ls.k_values[l] = k.values;
+        ls.k_scales[l] = k.scales;
+        ls.logits_out[l] = L.logits_out;
+        ls.out[l] = L.topk_indices;
+    }
+    const idx::Schedule s = to_schedule(cfg, sbk, sched);
+    if (need_ws) {
+        const size_t need = (size_t)rows->num_rows * s.nsb * s.sbk * sizeof(float);
+        if (!workspace && need) return fail(IDX_EWORKSPACE, "workspace is NULL (needs %zu bytes)", need);
+        if (workspace_bytes < need)
+            return fail(IDX_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+        if (!aligned(workspace, 16)) return fail(IDX_EINVAL, "workspace must be 16-byte aligned");
+    }
+    static_assert(idx::kMaxLayers == IDX_MAX_LAYERS, "one layer limit for the launch and the ABI");
+    if ((rc = hip_status(idx::launch_sparse_layers(cfg->q_format, to_rows(rows), num_layers, ls,
+                                                   to_kcache(cfg, &k0), s, (float *)workspace,
+                                                   cfg->topk, out_stride, g_timing,
+                                                   (hipStream_t)stream),
+                         "sparse layers launch")))
+        return rc;
+    return ok();
+}
+
 int idx_dense_masked_logits_topk(const idx_config *cfg, const idx_rows *rows, int32_t max_ctx,
                                  const void *q_values, const void *q_scales,
                                  const float *weights, const idx_kcache *k,

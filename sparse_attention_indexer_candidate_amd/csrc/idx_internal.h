@@ -67,6 +67,29 @@ hipError_t launch_sparse(int q_format, const Rows &rows, const void *q_values, c
                          float *workspace, int32_t topk, int32_t *out, int64_t out_stride,
                          const Timing &timing, hipStream_t stream);
 
+// Per-layer pointers of a multi-layer sparse call (layers [0, num_layers) used).  The
+// layers share the rows, the schedule and every KCache field but the two pools.
+constexpr int kMaxLayers = 8;
+struct LayerSet {
+    const void *q_values[kMaxLayers];
+    const void *q_scales[kMaxLayers];
+    const float *weights[kMaxLayers];
+    const uint8_t *k_values[kMaxLayers];
+    const uint8_t *k_scales[kMaxLayers];
+    float *logits_out[kMaxLayers];   // entries may be null
+    int32_t *out[kMaxLayers];
+};
+
+// The sparse path for num_layers layers.  With two or more layers whose rows take the
+// one-row kernel, one launch scores and selects every layer, two rows a CU (the timing
+// events ride on it); otherwise each
+// layer is launched as launch_sparse does, in layer order, reusing the workspace (the
+// events ride on every layer's scoring launch, so they time the last).
+hipError_t launch_sparse_layers(int q_format, const Rows &rows, int32_t num_layers,
+                                const LayerSet &layers, const KCache &k, const Schedule &s,
+                                float *workspace, int32_t topk, int64_t out_stride,
+                                const Timing &timing, hipStream_t stream);
+
 // Scores every token t < max_ctx of every row into logits [rows][logits_stride]
 // (-inf outside [ks, ke)).
 hipError_t launch_score_dense(int q_format, const Rows &rows, int32_t max_ctx, const void *q_values,

@@ -14,6 +14,9 @@
 //  fused_row_kernel     rows >= CUs otherwise: one workgroup scores a whole row into LDS
 //                       and selects from LDS (no global round trip, no cross-workgroup
 //                       sync)
+//  fused_layers_kernel  the one-row kernel for several layers sharing a schedule, one
+//                       launch (grid.y = layer); MXFP4: 8-wave rows, two a CU, so one
+//                       row's selection overlaps another's K stream
 //  score_split_kernel + topk_split_kernel
 //                       fewer rows than CUs: rows split over workgroups, logits in
 //                       global scratch, selection in a second launch
@@ -705,20 +708,15 @@ __device__ __forceinline__ RowInfo row_info(const Rows &rows, const KCache &k, c
 
 // ---------------------------------------------------------------- top-k --------
 
-// Order-preserving map of an fp32 logit to uint32 (larger float -> larger key);
-// -0 is first made +0 so the two compare equal.  Finite logits map above 0x007FFFFF,
-// so key 0 is free to mark an invalid column.
-__device__ __forceinline__ uint32_t ordered_key(float x) {
-    const uint32_t u = __float_as_uint(x + 0.0f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
+// Keys: an order-preserving map of an fp32 logit to uint32 (larger float -> larger
+// key): a negative logit's bits are inverted, a non-negative one gets the sign bit
+// set.  Finite logits map above 0x007FFFFF, so key 0 is free to mark an invalid column.
 // Column words in LDS (the one-row and row-group kernels): a valid column holds its
-// logit's bits, any other kNoColumn (a NaN pattern, taken to mean "no logit").  bits_key is
-// ordered_key on such a word without the -0 step (a scored logit is never -0: each
-// head sum starts from +0 and adds w * ReLU terms, and a round-to-nearest sum is -0
-// only when both operands are); it takes kNoColumn to the invalid key 0 by itself,
-// and -inf, a valid logit, to 0x007FFFFF.
+// logit's bits, any other kNoColumn (a NaN pattern, taken to mean "no logit").  The map
+// needs no -0 step (a scored logit is never -0: each head sum starts from +0 and adds
+// w * ReLU terms, and a round-to-nearest sum is -0 only when both operands are); it
+// takes kNoColumn to the invalid key 0 by itself, and -inf, a valid logit, to
+// 0x007FFFFF.
 constexpr uint32_t kNoColumn = 0xFFFFFFFFu;
 __device__ __forceinline__ uint32_t bits_key(uint32_t u) {
     return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
@@ -1146,22 +1144,31 @@ __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(
 
 // Rows >= CUs: one workgroup per row; waves take units of the row's valid 64-column
 // groups from a shared counter, logits stay in LDS, then the same workgroup selects.
-// logits_out (optional) gets a copy of every column.  The leading scalar arguments are
-// what the first loads need (the row's schedule entries and kept count, its query):
-// preloaded into SGPRs at wave launch, so those loads are one round trip.  The table
-// row is not checked here: the expansion lists nothing for a row whose table row is
-// invalid (kept = 0), and the schedule comes from the expansion of the same rows.
-template <int QF, int NT, int KPT>
-__global__ __launch_bounds__(NT) void fused_row_kernel(
-    const int32_t *si_base, const int32_t *pg_base, const void *qv, const void *qs,
-    const float *weights, const int32_t *p_kept, int32_t nsb, int32_t lsbk, Rows rows, KCache k,
-    float *logits_out, int32_t topk, int32_t *out, int64_t ostride) {
-    __shared__ alignas(16) uint32_t s_word[kMaxRowCols];   // column words (bits_key), then the stage
-    __shared__ int32_t s_si[kMaxNSB];
-    __shared__ int32_t s_pg[kMaxNSB];
-    __shared__ int s_unit;
-    __shared__ SelectLds<NT, 5> s_sel;
-    const int row = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1);
+// logits_out (optional) gets a copy of every column.  The table row is not checked
+// here: the expansion lists nothing for a row whose table row is invalid (kept = 0),
+// and the schedule comes from the expansion of the same rows.
+template <int NT>
+struct FusedLds {
+    alignas(16) uint32_t word[kMaxRowCols];   // column words (bits_key), then the stage
+    int32_t si[kMaxNSB];
+    int32_t pg[kMaxNSB];
+    int unit;
+    SelectLds<NT, 5> sel;
+};
+
+// U: 64-column groups a wave takes per unit (two units in flight).
+template <int QF, int NT, int KPT, int U>
+__device__ __forceinline__ void fused_row(
+    FusedLds<NT> &L, int row, const int32_t *si_base, const int32_t *pg_base, const void *qv,
+    const void *qs, const float *weights, const int32_t *p_kept, int32_t nsb, int32_t lsbk,
+    const Rows &rows, const KCache &k, float *logits_out, int32_t topk, int32_t *out,
+    int64_t ostride) {
+    uint32_t *s_word = L.word;
+    int32_t *s_si = L.si;
+    int32_t *s_pg = L.pg;
+    int &s_unit = L.unit;
+    SelectLds<NT, 5> &s_sel = L.sel;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int sbk = 1 << lsbk;
     RowInfo ri;
     ri.si = si_base + (int64_t)row * nsb;
@@ -1192,9 +1199,6 @@ __global__ __launch_bounds__(NT) void fused_row_kernel(
     // memory, so the extra instructions are free): valid keys per key >> 23.
     int nv = 0;
     int *hist0 = &s_sel.hist[0][0];
-    // 1024 threads (MXFP4 queries) leave 128 VGPRs a wave: units of one group, two in
-    // flight, 16 waves a CU; 512 threads (fp8 queries): 2-group units.
-    constexpr int U = NT >= 1024 ? 1 : (QF == 0 ? 4 : 2);
     const int vgroups = (ri.valid_cols + 63) / 64;
     const int nunits = (vgroups + U - 1) / U;
     const int valid_cols = ri.valid_cols;
@@ -1244,6 +1248,42 @@ __global__ __launch_bounds__(NT) void fused_row_kernel(
     }
     select_topk<NT, KPT, true>(key, keys_live(key), nvalid, kmin, kmax, topk, out + (int64_t)row * ostride, s_sel,
                          reinterpret_cast<int32_t *>(s_word), SparseTokens<KPT>{s_si, lsbk});
+}
+
+// One layer.  The leading scalar arguments are what the first loads need (the row's
+// schedule entries and kept count, its query): preloaded into SGPRs at wave launch, so
+// those loads are one round trip.
+template <int QF, int NT, int KPT>
+__global__ __launch_bounds__(NT) void fused_row_kernel(
+    const int32_t *si_base, const int32_t *pg_base, const void *qv, const void *qs,
+    const float *weights, const int32_t *p_kept, int32_t nsb, int32_t lsbk, Rows rows, KCache k,
+    float *logits_out, int32_t topk, int32_t *out, int64_t ostride) {
+    __shared__ FusedLds<NT> lds;
+    // 1024 threads (MXFP4 queries) leave 128 VGPRs a wave: units of one group, 16 waves
+    // a CU; 512 threads (fp8 queries): 2-group units.
+    constexpr int U = NT >= 1024 ? 1 : (QF == 0 ? 4 : 2);
+    fused_row<QF, NT, KPT, U>(lds, blockIdx.x, si_base, pg_base, qv, qs, weights, p_kept, nsb, lsbk,
+                           rows, k, logits_out, topk, out, ostride);
+}
+
+// Several consuming layers of one step in one launch (grid.y = layer): the layers share
+// the rows, the schedule and the cache geometry, and differ in their query, weights, K
+// pool and outputs.  A CU that finishes a row of one layer starts a row of the next at
+// once, so the layers' launch costs and their start and end skews are paid once.  With
+// MXFP4 queries a row takes 8 waves of one-group units held to 128 VGPRs (WPE = 4 waves
+// a SIMD), so two rows share a CU: one selects while the other streams K.
+template <int QF, int NT, int KPT, int U, int WPE>
+__global__ __launch_bounds__(NT, WPE) void fused_layers_kernel(
+    const int32_t *si_base, const int32_t *pg_base, const int32_t *p_kept, int32_t nsb,
+    int32_t lsbk, int32_t topk, Rows rows, KCache k, LayerSet ls, int64_t ostride) {
+    __shared__ FusedLds<NT> lds;
+    const int layer = blockIdx.y;
+    KCache kl = k;
+    kl.values = ls.k_values[layer];
+    kl.scales = ls.k_scales[layer];
+    fused_row<QF, NT, KPT, U>(lds, blockIdx.x, si_base, pg_base, ls.q_values[layer],
+                           ls.q_scales[layer], ls.weights[layer], p_kept, nsb, lsbk, rows, kl,
+                           ls.logits_out[layer], topk, ls.out[layer], ostride);
 }
 
 // Dense scoring (the comparator): column t is token t, every token < max_ctx.
@@ -1718,6 +1758,46 @@ hipError_t launch_sparse(int q_format, const Rows &rows, const void *q_values, c
                                   topk, out, out_stride, timing, stream);
     return launch_sparse_q<1>(rows, q_values, q_scales, weights, k, s, logits_out, workspace, topk,
                               out, out_stride, timing, stream);
+}
+
+hipError_t launch_sparse_layers(int q_format, const Rows &rows, int32_t num_layers,
+                                const LayerSet &layers, const KCache &k, const Schedule &s,
+                                float *workspace, int32_t topk, int64_t out_stride,
+                                const Timing &timing, hipStream_t stream) {
+    if (rows.num_rows == 0 || num_layers == 0) return hipSuccess;
+    const int ncols = s.nsb * s.sbk;
+    const int cus = device_cus();
+    const bool groups = q_format == 0 && s.sbk == 64 && ncols <= 8192 && rows.num_rows >= 8 * cus;
+    if (num_layers >= 2 && rows.num_rows >= cus && !groups) {
+        const dim3 grid(rows.num_rows, num_layers);
+#define IDX_LAUNCH_LAYERS(QF_, NT_, KPT_, U_, WPE_)                                              \
+    hipExtLaunchKernelGGL((fused_layers_kernel<QF_, NT_, KPT_, U_, WPE_>), grid, dim3(NT_), 0,    \
+                          stream,                                                                  \
+                          timing.start, timing.stop, 0, s.sparse_indices, s.pages, s.kept, s.nsb, \
+                          s.lsbk, topk, rows, k, layers, out_stride)
+        if (q_format == 0) {
+            if (ncols <= 512 * 4) IDX_LAUNCH_LAYERS(0, 512, 4, 1, 4);
+            else if (ncols <= 512 * 8) IDX_LAUNCH_LAYERS(0, 512, 8, 1, 4);
+            else IDX_LAUNCH_LAYERS(0, 512, 16, 1, 4);
+        } else {
+            if (ncols <= 512 * 4) IDX_LAUNCH_LAYERS(1, 512, 4, 2, 1);
+            else if (ncols <= 512 * 8) IDX_LAUNCH_LAYERS(1, 512, 8, 2, 1);
+            else IDX_LAUNCH_LAYERS(1, 512, 16, 2, 1);
+        }
+#undef IDX_LAUNCH_LAYERS
+        return hipGetLastError();
+    }
+    for (int l = 0; l < num_layers; ++l) {
+        KCache kl = k;
+        kl.values = layers.k_values[l];
+        kl.scales = layers.k_scales[l];
+        const hipError_t e = launch_sparse(q_format, rows, layers.q_values[l], layers.q_scales[l],
+                                           layers.weights[l], kl, s, layers.logits_out[l],
+                                           workspace, topk, layers.out[l], out_stride, timing,
+                                           stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_score_dense(int q_format, const Rows &rows, int32_t max_ctx, const void *q_values,

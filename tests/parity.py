@@ -134,6 +134,28 @@ class GpuRun:
             None if with_logits else self.workspace,
             0 if with_logits else self.workspace.numel())
 
+    def score_layers(self, layers, with_logits):
+        """One idx_sparse_mqa_logits_topk_layers call over the given layers; returns
+        per-layer (indices, logits or None) device tensors.  with_logits[i] False: that
+        layer writes no logits (the workspace serves it)."""
+        import torch
+
+        R, s = self.case.num_rows, self.spec
+        dev = self.dcase.row_ke.device
+        outs, logs, entries = [], [], []
+        for layer, wl in zip(layers, with_logits):
+            L = self.dcase.layers[layer]
+            qv, qs = L.q(self.q_format)
+            out = torch.full((R, s.topk), -7, dtype=torch.int32, device=dev)
+            lg = torch.empty((R, s.nb * s.cbs), dtype=torch.float32, device=dev) if wl else None
+            outs.append(out)
+            logs.append(lg)
+            entries.append((qv, qs, L.weights, self.kcaches[layer], out, lg))
+        self.idx.idx_sparse_mqa_logits_topk_layers(self.cfg, self.rows, self.sched.struct,
+                                                   entries, s.topk, self.workspace,
+                                                   self.workspace.numel())
+        return outs, logs
+
     def fetch(self):
         import torch
 

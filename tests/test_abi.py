@@ -164,6 +164,44 @@ def test_expand_rejects_bad_arguments():
     assert call(FAKE, 64, sched(sparse_indices=None)) == idx.IDX_EINVAL
 
 
+def layers_call(layers, n=None, r=None, ws=None, wsb=0, ostride=2048):
+    c = idx.idx_check_config(cfg())
+    arr = (idx.idx_layer * max(1, len(layers)))(*layers)
+    return idx.lib.idx_sparse_mqa_logits_topk_layers(
+        ctypes.byref(c), ctypes.byref(r or rows()), ctypes.byref(sched()),
+        len(layers) if n is None else n, arr, ostride, ws, wsb, None)
+
+
+def layer(k=None, qv=FAKE, out=FAKE, logits=FAKE):
+    return idx.idx_layer(qv, FAKE, FAKE, k or kcache(), out, logits)
+
+
+def test_layers_call_rejects_bad_arguments():
+    two = [layer(), layer(kcache(values=FAKE + 0x10000, scales=FAKE + 0x11000))]
+    assert layers_call(two, r=rows(0)) == idx.IDX_OK           # zero rows: nothing launched
+    assert layers_call(two, n=0) == idx.IDX_EINVAL
+    assert layers_call([layer()] * 9) == idx.IDX_EINVAL         # > IDX_MAX_LAYERS
+    assert layers_call(two, ostride=100) == idx.IDX_EINVAL
+    c = idx.idx_check_config(cfg())
+    assert idx.lib.idx_sparse_mqa_logits_topk_layers(
+        ctypes.byref(c), ctypes.byref(rows()), ctypes.byref(sched()), 2, None, 2048, None, 0,
+        None) == idx.IDX_EINVAL
+    # per-layer checks name the layer
+    assert layers_call([layer(), layer(qv=FAKE + 4)]) == idx.IDX_EINVAL
+    assert "layer 1" in idx.idx_last_error()
+    assert layers_call([layer(), layer(out=None)]) == idx.IDX_EINVAL
+    assert layers_call([layer(), layer(k=kcache(values=None))]) == idx.IDX_EINVAL
+    assert "layer 1" in idx.idx_last_error()
+    # one page geometry and block table for every layer
+    for kw in (dict(num_pages=11), dict(block_table=FAKE + 0x100), dict(values_page_stride=4368),
+               dict(pages_per_table=3)):
+        assert layers_call([layer(), layer(k=kcache(**kw))]) == idx.IDX_EINVAL, kw
+        assert "geometry" in idx.idx_last_error()
+    # a layer without logits_out needs the workspace
+    assert layers_call([layer(), layer(logits=None)]) == idx.IDX_EWORKSPACE
+    assert layers_call([layer(), layer(logits=None)], ws=FAKE, wsb=100) == idx.IDX_EWORKSPACE
+
+
 def test_dense_call_rejects_bad_arguments():
     c = idx.idx_check_config(cfg())
     def call(max_ctx=65536, logits=None, lstride=0, ws=None, wsb=0):

@@ -446,6 +446,75 @@ def test_config5_sparse_equals_dense_masked(q_format):
     np.testing.assert_array_equal(dout.cpu().numpy(), res["indices"])
 
 
+LAYERED = {
+    # >= 256 rows of one table row each: every layer in one launch
+    "one_launch": W.Spec(name="ml1", num_rows=300, page_size=64, cbs=64, nb=24, topk=300,
+                         layers=3, ke_rule="uniform", ke_lo=500, ke_hi=3000, ks_rule="random",
+                         cand_rule="messy", fill="all", q_formats=("mxfp4", "fp8")),
+    # fewer rows than CUs: the split kernels, layer after layer
+    "split": W.Spec(name="ml2", num_rows=40, page_size=32, cbs=32, nb=30, topk=500, layers=2,
+                    ke_rule="uniform", ke_lo=100, ke_hi=1500, cand_rule="messy", fill="all",
+                    q_formats=("mxfp4", "fp8")),
+}
+
+
+@pytest.mark.parametrize("q_format", ["mxfp4", "fp8"])
+@pytest.mark.parametrize("name", sorted(LAYERED))
+def test_layers_call_matches_per_layer_calls_and_oracle(name, q_format):
+    case = W.generate(LAYERED[name], seed=5)
+    nl = case.spec.layers
+    g = GpuRun(case, to_device(case, DEV), q_format=q_format)
+    g.expand()
+    with_logits = [i % 2 == 0 for i in range(nl)]     # odd layers use the workspace
+    _say(f"[layers-{name}-{q_format}] one call, {nl} layers")
+    outs, logs = g.score_layers(range(nl), with_logits)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    sample = np.unique(np.r_[0, case.num_rows - 1, rng.integers(0, case.num_rows, 6)]).astype(np.int32)
+    for layer in range(nl):
+        _say(f"[layers-{name}-{q_format}] layer {layer} against its own call")
+        g.out.fill_(-7)
+        g.score(layer, with_logits=True)
+        res = g.fetch()
+        np.testing.assert_array_equal(outs[layer].cpu().numpy(), res["indices"],
+                                      err_msg=f"{name} layer {layer}: indices")
+        if logs[layer] is not None:
+            np.testing.assert_array_equal(logs[layer].cpu().numpy().view(np.uint32),
+                                          res["logits"].view(np.uint32),
+                                          err_msg=f"{name} layer {layer}: logits")
+        pool = case.layers[layer].host_pool(case.spec.page_bytes)
+        ora = oracle.indexer_rows(case, layer, sample, q_format, pool=pool)
+        res["indices"] = outs[layer].cpu().numpy()
+        compare_rows(case, res, ora, case.spec.topk, g.sbk, f"layers-{name} layer {layer}")
+
+
+def test_layers_call_on_long_decode_matches_per_layer_calls():
+    case = W.generate(W.config(4), 0)
+    g = GpuRun(case, to_device(case, DEV))
+    g.expand()
+    _say("[layers-cfg4] one call, 4 layers")
+    outs, logs = g.score_layers(range(4), [True, False, False, True])
+    torch.cuda.synchronize()
+    for layer in range(4):
+        _say(f"[layers-cfg4] layer {layer}")
+        g.out.fill_(-7)
+        g.score(layer, with_logits=True)
+        res = g.fetch()
+        np.testing.assert_array_equal(outs[layer].cpu().numpy(), res["indices"],
+                                      err_msg=f"cfg4 layer {layer}: indices")
+        if logs[layer] is not None:
+            np.testing.assert_array_equal(logs[layer].cpu().numpy().view(np.uint32),
+                                          res["logits"].view(np.uint32))
+    # one layer through the multi-layer entry point takes the one-layer launch
+    one, _ = g.score_layers([3], [False])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(one[0].cpu().numpy(), res["indices"], err_msg="cfg4 one layer")
+    pool = case.layers[3].host_pool(case.spec.page_bytes)
+    ora = oracle.indexer_rows(case, 3, np.array([0, 131, 255], np.int32), "mxfp4", pool=pool)
+    res["indices"] = outs[3].cpu().numpy()
+    compare_rows(case, res, ora, case.spec.topk, g.sbk, "layers-cfg4 layer 3")
+
+
 def test_repeat_calls_are_deterministic_and_reuse_schedule():
     case = W.generate(W.config(2), 1)
     dcase = to_device(case, DEV)
