@@ -70,6 +70,13 @@ SMALL = {
     "cbs128_split_sbk32": W.Spec(name="s6", num_rows=11, page_size=128, cbs=128, nb=9, topk=200,
                                  ke_rule="uniform", ke_lo=300, ke_hi=2000, ks_rule="random",
                                  cand_rule="messy", fill="all"),
+    # >= 2 rows per CU, MXFP4: the one-row kernel with two 8-wave rows a CU
+    "two_rows_a_cu": W.Spec(name="s12", num_rows=600, page_size=64, cbs=64, nb=20, topk=200,
+                            ke_rule="uniform", ke_lo=1, ke_hi=2500, ks_rule="random",
+                            cand_rule="messy", fill="all"),
+    "two_rows_a_cu_sbk16": W.Spec(name="s13", num_rows=520, page_size=32, cbs=16, nb=60, topk=90,
+                                  ke_rule="uniform", ke_lo=50, ke_hi=1200, cand_rule="messy",
+                                  fill="all"),
     # >= 8 rows per CU: the row-group kernel (4 rows per workgroup); rows on one table
     # share K tiles, a ragged last group, messy candidates and ks > 0
     "rowgroup_shared_table_messy": W.Spec(name="s7", num_rows=2051, page_size=128, cbs=64, nb=8,
@@ -348,16 +355,16 @@ def test_max_width_split_all_rows(name):
     run_and_compare(W.generate(MAX_WIDTH[name], seed=1), tag=name)
 
 
-@pytest.mark.parametrize("k", [7000, 8192])
-def test_max_width_rows_per_cu_sampled(k):
-    """One workgroup a row at the column and top-k limits: 260 rows of up to 8192
-    columns; the oracle on sampled rows, and on every row the selection is exact for
-    the GPU's own logits."""
-    spec = W.Spec(name=f"m3_{k}", num_rows=260, page_size=64, cbs=64, nb=128, topk=k,
-                  ke_rule="uniform", ke_lo=6000, ke_hi=12000, cand_rule="distinct",
+@pytest.mark.parametrize("k,nrows", [(7000, 260), (8192, 260), (8192, 520)])
+def test_max_width_rows_per_cu_sampled(k, nrows):
+    """One workgroup a row at the column and top-k limits: 260 rows (one a CU) or 520
+    rows (two a CU) of up to 8192 columns; the oracle on sampled rows, and on every row
+    the selection is exact for the GPU's own logits."""
+    spec = W.Spec(name=f"m3_{k}_{nrows}", num_rows=nrows, page_size=64, cbs=64, nb=128,
+                  topk=k, ke_rule="uniform", ke_lo=6000, ke_hi=12000, cand_rule="distinct",
                   fill="candidates")
     case = W.generate(spec, seed=2)
-    rows = np.r_[0:4, 128:130, 256:260].astype(np.int32)
+    rows = np.r_[0:4, 128:130, nrows - 4:nrows].astype(np.int32)
     g, res = run_and_compare(case, rows=rows, tag=f"maxwidth{k}")
     for i in range(case.num_rows):
         gt, gl = gpu_row_tokens(res["sparse_indices"][i], int(res["kept"][i]), g.sbk, 0,
