@@ -458,6 +458,15 @@ LAYERED = {
     "one_launch": W.Spec(name="ml1", num_rows=300, page_size=64, cbs=64, nb=24, topk=300,
                          layers=3, ke_rule="uniform", ke_lo=500, ke_hi=3000, ks_rule="random",
                          cand_rule="messy", fill="all", q_formats=("mxfp4", "fp8")),
+    # the layer limit (8) in one launch
+    "eight_layers": W.Spec(name="ml3", num_rows=260, page_size=64, cbs=64, nb=8, topk=100,
+                           layers=8, ke_rule="uniform", ke_lo=10, ke_hi=1500, cand_rule="messy",
+                           fill="all", q_formats=("mxfp4", "fp8")),
+    # >= 8 rows per CU on one table (a prefill chunk's shape): row groups, layer by layer
+    "row_groups": W.Spec(name="ml4", num_rows=2050, page_size=128, cbs=64, nb=8, topk=100,
+                         layers=2, mode="prefill", ke_rule="uniform", ke_lo=1, ke_hi=1500,
+                         ks_rule="random", context=1600, cand_rule="messy", fill="all",
+                         q_formats=("mxfp4", "fp8")),
     # fewer rows than CUs: the split kernels, layer after layer
     "split": W.Spec(name="ml2", num_rows=40, page_size=32, cbs=32, nb=30, topk=500, layers=2,
                     ke_rule="uniform", ke_lo=100, ke_hi=1500, cand_rule="messy", fill="all",
