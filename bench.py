@@ -136,6 +136,94 @@ def measured_peaks(stream) -> dict:
                    "median of 5 launches timed with events"}
 
 
+def bench_gather(args, idx, case, cfg, dev, gen_s):
+    """The packed K workspace gather: one request per table row, its positions [0, ke)
+    (the largest ke of the rows on it), layer 0's pool, every step one launch."""
+    import torch
+
+    from workloads.device import to_device
+
+    spec = case.spec
+    tables = np.unique(case.row_table)
+    lens = np.array([int(case.row_ke[case.row_table == t].max()) for t in tables], np.int64)
+    cu = np.r_[0, np.cumsum(lens)].astype(np.int32)
+    total, max_seq = int(cu[-1]), int(lens.max())
+    # bytes per launch: each position's value and scale bytes read and written, its
+    # block-table entry read once per page, cu and the request table
+    pages = int(sum((n + spec.page_size - 1) // spec.page_size for n in lens))
+    launch_bytes = total * (spec.head_dim // 2 + spec.head_dim // 32) * 2 + pages * 4 + 8 * len(lens)
+    base = to_device(case, dev, layers=[0])
+    pool_bytes = base.layers[0].pool.numel()
+    nrep = args.replicas if args.replicas > 0 else max(2, math.ceil(1.5e9 / launch_bytes))
+    nrep = max(1, min(nrep, int(40e9 // max(pool_bytes, 1))))
+    pools = [base.layers[0].pool] + [base.layers[0].pool.clone() for _ in range(nrep - 1)]
+    d_cu = torch.from_numpy(cu).to(dev)
+    d_req = torch.from_numpy(tables.astype(np.int32)).to(dev)
+    vals = torch.empty((total, spec.head_dim // 2), dtype=torch.uint8, device=dev)
+    scs = torch.empty((total, spec.head_dim // 32), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+    calls = [idx.bind_gather_k_workspace(
+        cfg, idx.make_kcache(p, spec.page_size, spec.head_dim, base.block_table), d_cu, vals,
+        scs, max_seq, req_table=d_req, stream=stream.cuda_stream) for p in pools]
+    timed_steps = [i for i in range(args.steps) if i % TIMING_STRIDE == 0]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in timed_steps]
+    for a, b in ev:
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ev_raw = [(idx.event_handle(a), idx.event_handle(b)) for a, b in ev]
+    set_events = idx.lib.idx_set_timing_events
+    for i in range(args.warmup):
+        calls[i % nrep]()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if i % TIMING_STRIDE == 0:
+            set_events(*ev_raw[i // TIMING_STRIDE])
+        calls[i % nrep]()
+        if i % TIMING_STRIDE == 0:
+            set_events(None, None)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kernel_ms = [a.elapsed_time(b) for a, b in ev]
+    avg_s = float(np.mean(kernel_ms)) / 1e3
+    achieved = launch_bytes / avg_s / 1e9
+    peaks = measured_peaks(stream)
+    roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "gather_k_kernel",
+            "measured_peak": peaks["read_gbs"], "frac_of_measured": achieved / peaks["read_gbs"],
+            "avg_launch_us": avg_s * 1e6,
+            "launch_us_p10": float(np.percentile(kernel_ms, 10)) * 1e3,
+            "launch_us_p90": float(np.percentile(kernel_ms, 90)) * 1e3,
+            "timed_launches": len(kernel_ms), "algorithmic_bytes_per_launch": launch_bytes}
+    out = {"metric": "K positions gathered into the packed workspace/s", "value": total * args.steps / elapsed,
+           "unit": "positions/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": elapsed / args.steps * 1e3, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+           "config": {"workload": f"gather_{spec.name}", "requests": len(lens), "positions": total,
+                      "page_size": spec.page_size, "path": "gather", "input_copies": nrep,
+                      "seed": args.seed},
+           "roofline": roof, "measured_peaks": peaks}
+    if not args.no_cpu_baseline:
+        import oracle
+
+        pool = case.layers[0].host_pool(spec.page_bytes)
+        n, t0 = 0, time.perf_counter()
+        for r in range(len(lens)):   # whole requests until the time budget is spent
+            oracle.gather_k_workspace(pool, spec.page_size, spec.head_dim, case.block_table,
+                                      [0, int(lens[r])], req_table=[int(tables[r])])
+            n += int(lens[r])
+            if time.perf_counter() - t0 > args.cpu_seconds:
+                break
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": n / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{n} positions of the first {r + 1} requests, one thread"}
+    print(f"# generated inputs in {gen_s:.1f} s; {nrep} input copies", file=sys.stderr)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,9 +232,10 @@ def main():
     ap.add_argument("--config", type=int, default=2,
                     help="workload 1-5 (default 2); 6: decode with two rows per request")
     ap.add_argument("--q-format", default="mxfp4", choices=["mxfp4", "fp8"])
-    ap.add_argument("--path", default="sparse", choices=["sparse", "dense"],
+    ap.add_argument("--path", default="sparse", choices=["sparse", "dense", "gather"],
                     help="sparse: idx_sparse_mqa_logits_topk; dense: the comparator "
-                         "idx_dense_masked_logits_topk (scores the whole context)")
+                         "idx_dense_masked_logits_topk (scores the whole context); gather: "
+                         "idx_gather_k_workspace of every table row's context [0, ke)")
     ap.add_argument("--replicas", type=int, default=0, help="input copies (0 = auto)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -196,6 +285,8 @@ def main():
     cfg = idx.make_config(spec.num_heads, spec.head_dim,
                           idx.IDX_Q_MXFP4 if args.q_format == "mxfp4" else idx.IDX_Q_FP8_E4M3_ROWSCALE,
                           spec.page_size, spec.cbs, 0, spec.nb, spec.topk)
+    if args.path == "gather":
+        return bench_gather(args, idx, case, cfg, dev, gen_s)
     R = case.num_rows
 
     # Touched bytes per step decide how many copies defeat the Infinity Cache.

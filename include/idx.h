@@ -132,9 +132,11 @@ size_t idx_workspace_bytes(const idx_config *cfg, int32_t max_rows, int32_t max_
 /* Message of the last failing call on this thread ("" if none).  Host. */
 const char *idx_last_error(void);
 
-/* Optional timing hook for benchmarks.  While set, every idx_sparse_mqa_logits_topk
- * and idx_dense_masked_logits_topk call made on this thread launches its scoring
- * kernel (the one that streams the K cache) with start_event and stop_event attached
+/* Optional timing hook for benchmarks.  While set, every idx_sparse_mqa_logits_topk,
+ * idx_sparse_mqa_logits_topk_layers, idx_dense_masked_logits_topk and
+ * idx_gather_k_workspace call made on this thread launches its scoring kernel (the one
+ * that streams the K cache; for the gather, its one kernel) with start_event and
+ * stop_event attached
  * to the dispatch (hipExtLaunchKernel): they take the kernel's own start and end
  * timestamps, so hipEventElapsedTime gives its duration without queueing gaps.  Both
  * are hipEvent_t handles owned by the caller; pass NULL, NULL to clear.  Host;
@@ -213,6 +215,28 @@ int idx_dense_masked_logits_topk(const idx_config *cfg, const idx_rows *rows, in
                                  const idx_schedule *sched, int32_t *topk_indices,
                                  int64_t out_stride, float *logits_out, int64_t logits_stride,
                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* Packed K workspace (the gather of a prefill chunk's paged K into one contiguous
+ * buffer that the pages' backend performs before scoring a chunk, the
+ * cp_gather_indexer_k_quant_cache call on the sparse_mqa_indexer page): request r's
+ * positions p in [0, cu_seq_lens[r+1] - cu_seq_lens[r]) are copied from the paged
+ * cache (table row req_table[r], or r when req_table is NULL) to workspace row
+ * cu_seq_lens[r] + p:
+ *   values_out: u8 [max_tokens][D/2] (16-byte aligned), the row's packed e2m1 values;
+ *   scales_out: u8 [max_tokens][D/32] (4-byte aligned), its UE8M0 scale bytes (one
+ *     int32 a row when D = 128).
+ * cu_seq_lens: int32 [num_reqs + 1] device array, non-decreasing from >= 0.  Rows at
+ * or past max_tokens, and positions at or past max_seq_len (host; bounds every
+ * request's length), are not written; a position whose table row, logical page or
+ * page id is out of range is written as zeros.  k's scales base and page stride must be
+ * 4-byte aligned.  The workspace then serves idx_expand_candidates and the scoring calls
+ * as a one-page cache (page_size >= the chunk's rows, values/scales page strides
+ * max_tokens * D/2 and max_tokens * D/32, a one-entry block table), in workspace
+ * coordinates.  The timing events, if set, ride on the gather launch. */
+int idx_gather_k_workspace(const idx_config *cfg, const idx_kcache *k, int32_t num_reqs,
+                           const int32_t *cu_seq_lens, const int32_t *req_table,
+                           int32_t max_seq_len, int32_t max_tokens, uint8_t *values_out,
+                           uint8_t *scales_out, void *stream);
 
 /* ---- Measurement (not a step of the indexer) ----
  * Reference kernels for the two rates that bound the indexer, for a benchmark to time

@@ -166,3 +166,44 @@ def indexer_rows(case, layer: int = 0, rows=None, q_format: str = "mxfp4", pool=
         _ptr(cand), cand.shape[1], _ptr(rows), n,
         _ptr(idx), s.topk, _ptr(toks), _ptr(lg), cap, _ptr(cnt))
     return RowResult(rows, idx, toks, lg, cnt)
+
+
+def gather_k_workspace(pool, page_size: int, head_dim: int, block_table, cu_seq_lens,
+                       req_table=None, max_seq_len: int | None = None,
+                       max_tokens: int | None = None, fill: int = 0):
+    """The packed K workspace of a prefill chunk: the backend's gather of the chunk's
+    paged K into one contiguous buffer before scoring (sparse_mqa_indexer page,
+    _gather_prefill_chunk_k / cp_gather_indexer_k_quant_cache).  Request r's position p
+    (p < cu[r+1] - cu[r], and p < max_seq_len) is copied to workspace row cu[r] + p
+    (rows >= max_tokens are skipped): its D/2 value bytes and D/32 scale bytes, read
+    through table row req_table[r] (r when None).  The page layout is the workload
+    pool's: values [page_size][D/2] then scales [page_size][D/32].  A position whose
+    table row, logical page or page id is out of range gets zeros; rows never written
+    keep `fill`.  Returns (values [max_tokens, D/2], scales [max_tokens, D/32]) u8."""
+    cu = np.asarray(cu_seq_lens, dtype=np.int64)
+    bt = np.asarray(block_table)
+    vrow, srow = head_dim // 2, head_dim // 32
+    vbytes = page_size * vrow
+    if max_tokens is None:
+        max_tokens = int(cu[-1])
+    if max_seq_len is None:
+        max_seq_len = int(np.max(cu[1:] - cu[:-1], initial=0))
+    values = np.full((max_tokens, vrow), fill, dtype=np.uint8)
+    scales = np.full((max_tokens, srow), fill, dtype=np.uint8)
+    for r in range(len(cu) - 1):
+        tbl = int(req_table[r]) if req_table is not None else r
+        if cu[r] < 0:
+            continue
+        for p in range(int(min(cu[r + 1] - cu[r], max_seq_len))):
+            row = int(cu[r]) + p
+            if row >= max_tokens:
+                break
+            lp, slot = p // page_size, p % page_size
+            page = int(bt[tbl, lp]) if 0 <= tbl < bt.shape[0] and lp < bt.shape[1] else -1
+            if 0 <= page < pool.shape[0]:
+                values[row] = pool[page, slot * vrow:(slot + 1) * vrow]
+                scales[row] = pool[page, vbytes + slot * srow:vbytes + (slot + 1) * srow]
+            else:
+                values[row] = 0
+                scales[row] = 0
+    return values, scales

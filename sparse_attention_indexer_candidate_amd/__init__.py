@@ -30,6 +30,7 @@ EXPORTED = ("idx_check_config", "idx_num_sparse_blocks", "idx_schedule_work_byte
             "idx_workspace_bytes", "idx_last_error", "idx_set_timing_events",
             "idx_expand_candidates", "idx_sparse_mqa_logits_topk",
             "idx_sparse_mqa_logits_topk_layers", "idx_dense_masked_logits_topk",
+            "idx_gather_k_workspace",
             "idx_measure_read", "idx_measure_mfma", "idx_measure_mfma_flops")
 IDX_MEASURE_WGS = 4096
 IDX_MAX_LAYERS = 8
@@ -112,6 +113,9 @@ def _load():
                                                P(idx_kcache), P(idx_schedule), vp, i64, vp, i64,
                                                vp, sz, vp]
     L.idx_dense_masked_logits_topk.restype = ctypes.c_int
+    L.idx_gather_k_workspace.argtypes = [P(idx_config), P(idx_kcache), i32, vp, vp, i32, i32,
+                                         vp, vp, vp]
+    L.idx_gather_k_workspace.restype = ctypes.c_int
     L.idx_measure_read.argtypes = [vp, sz, vp, vp]
     L.idx_measure_read.restype = ctypes.c_int
     L.idx_measure_mfma.argtypes = [i32, vp, vp]
@@ -207,6 +211,33 @@ def idx_dense_masked_logits_topk(cfg, rows, max_ctx, q_values, q_scales, weights
         ctypes.byref(cfg), ctypes.byref(rows), max_ctx, _p(q_values), _p(q_scales), _p(weights),
         ctypes.byref(k), ctypes.byref(sched), _p(topk_indices), out_stride, _p(logits_out),
         logits_stride, _p(workspace), workspace_bytes, _p(stream)))
+
+
+def idx_gather_k_workspace(cfg, k, cu_seq_lens, values_out, scales_out, max_seq_len,
+                           req_table=None, stream=None):
+    """Pack requests' paged K into values_out [N, D/2] / scales_out [N, D/32] (u8 device
+    tensors); cu_seq_lens: int32 device tensor [num_reqs + 1]."""
+    num_reqs = cu_seq_lens.numel() - 1 if cu_seq_lens is not None else 0
+    return _check(lib.idx_gather_k_workspace(
+        ctypes.byref(cfg), ctypes.byref(k), max(0, num_reqs), _p(cu_seq_lens), _p(req_table),
+        max_seq_len, values_out.shape[0], _p(values_out), _p(scales_out), _p(stream)))
+
+
+def bind_gather_k_workspace(cfg, k, cu_seq_lens, values_out, scales_out, max_seq_len,
+                            req_table=None, stream=None):
+    vp = lambda x: ctypes.c_void_p(_p(x))
+    return BoundCall(lib.idx_gather_k_workspace,
+                     (ctypes.byref(cfg), ctypes.byref(k), cu_seq_lens.numel() - 1,
+                      vp(cu_seq_lens), vp(req_table), max_seq_len, values_out.shape[0],
+                      vp(values_out), vp(scales_out), vp(stream)), (cfg, k))
+
+
+def make_workspace_kcache(values, scales, block_table) -> idx_kcache:
+    """The packed workspace as a one-page cache: values u8 [N, D/2], scales u8 [N, D/32],
+    block_table int32 [1, 1] holding 0."""
+    return idx_kcache(values.data_ptr(), values.numel(), scales.data_ptr(), scales.numel(), 1,
+                      block_table.data_ptr(), block_table.stride(0), block_table.shape[0],
+                      block_table.shape[1])
 
 
 def idx_measure_read(src, nbytes, sink, stream=None):

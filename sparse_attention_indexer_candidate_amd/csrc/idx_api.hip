@@ -369,6 +369,30 @@ int idx_dense_masked_logits_topk(const idx_config *cfg, const idx_rows *rows, in
     return ok();
 }
 
+int idx_gather_k_workspace(const idx_config *cfg, const idx_kcache *k, int32_t num_reqs,
+                           const int32_t *cu_seq_lens, const int32_t *req_table,
+                           int32_t max_seq_len, int32_t max_tokens, uint8_t *values_out,
+                           uint8_t *scales_out, void *stream) {
+    int rc;
+    if ((rc = check_filled(cfg, nullptr)) || (rc = check_kcache(cfg, k))) return rc;
+    if (num_reqs < 0 || max_seq_len < 0 || max_tokens < 0)
+        return fail(IDX_EINVAL, "num_reqs, max_seq_len and max_tokens must be >= 0");
+    if (num_reqs > 65535) return fail(IDX_EUNSUPPORTED, "num_reqs %d > 65535", num_reqs);
+    if (num_reqs > 0 && !cu_seq_lens) return fail(IDX_EINVAL, "cu_seq_lens is NULL");
+    if (max_tokens > 0 && (!values_out || !scales_out))
+        return fail(IDX_EINVAL, "values_out and scales_out must be non-NULL");
+    if (!aligned(values_out, 16) || !aligned(scales_out, 4))
+        return fail(IDX_EINVAL, "values_out must be 16-byte and scales_out 4-byte aligned");
+    if (!aligned(k->scales, 4) || k->scales_page_stride % 4 != 0)
+        return fail(IDX_EINVAL, "k scales base and page stride must be 4-byte aligned");
+    if ((rc = hip_status(idx::launch_gather_k(to_kcache(cfg, k), num_reqs, cu_seq_lens, req_table,
+                                              max_seq_len, max_tokens, values_out, scales_out,
+                                              g_timing, (hipStream_t)stream),
+                         "gather launch")))
+        return rc;
+    return ok();
+}
+
 int idx_measure_read(const void *src, size_t bytes, uint32_t *sink, void *stream) {
     if (!src || !sink) return fail(IDX_EINVAL, "src and sink must be non-NULL");
     if (!aligned(src, 16) || bytes % 16 != 0 || bytes == 0)

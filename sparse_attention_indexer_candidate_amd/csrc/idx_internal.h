@@ -102,6 +102,12 @@ hipError_t launch_dense_topk(const Rows &rows, const KCache &k, const Schedule &
                              const float *logits, int64_t logits_stride, int32_t ncols,
                              int32_t topk, int32_t *out, int64_t out_stride, hipStream_t stream);
 
+// Packs requests' paged K into a contiguous workspace (see gather_k_kernel).
+hipError_t launch_gather_k(const KCache &k, int32_t num_reqs, const int32_t *cu_seq_lens,
+                           const int32_t *req_table, int32_t max_seq_len, int32_t max_tokens,
+                           uint8_t *values_out, uint8_t *scales_out, const Timing &timing,
+                           hipStream_t stream);
+
 // Reference kernels for the rates that bound the indexer (measurement only).
 constexpr int kMeasureWgs = 4096;   // workgroups of 256 threads
 hipError_t launch_measure_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream);

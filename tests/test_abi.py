@@ -202,6 +202,25 @@ def test_layers_call_rejects_bad_arguments():
     assert layers_call([layer(), layer(logits=None)], ws=FAKE, wsb=100) == idx.IDX_EWORKSPACE
 
 
+def test_gather_rejects_bad_arguments():
+    c = idx.idx_check_config(cfg())
+    def call(k=None, n=2, cu=FAKE, seq=100, tokens=500, vo=FAKE, so=FAKE):
+        return idx.lib.idx_gather_k_workspace(ctypes.byref(c), ctypes.byref(k or kcache()), n, cu,
+                                              None, seq, tokens, vo, so, None)
+    assert call(n=0) == idx.IDX_OK                   # nothing to gather: no launch
+    assert call(seq=0) == idx.IDX_OK
+    assert call(n=-1) == idx.IDX_EINVAL
+    assert call(n=70000) == idx.IDX_EUNSUPPORTED     # one grid row per request
+    assert call(cu=None) == idx.IDX_EINVAL
+    assert call(vo=None) == idx.IDX_EINVAL
+    assert call(vo=FAKE + 4) == idx.IDX_EINVAL       # values_out not 16-byte aligned
+    assert call(so=FAKE + 2) == idx.IDX_EINVAL       # scales_out not 4-byte aligned
+    assert call(k=kcache(scales=FAKE + 4098)) == idx.IDX_EINVAL
+    assert call(k=kcache(values=None)) == idx.IDX_EINVAL
+    assert idx.lib.idx_gather_k_workspace(ctypes.byref(cfg()), ctypes.byref(kcache()), 1, FAKE,
+                                          None, 1, 1, FAKE, FAKE, None) == idx.IDX_EINVAL
+
+
 def test_dense_call_rejects_bad_arguments():
     c = idx.idx_check_config(cfg())
     def call(max_ctx=65536, logits=None, lstride=0, ws=None, wsb=0):

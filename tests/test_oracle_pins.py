@@ -280,6 +280,64 @@ def test_oracle_matches_brute_force_on_one_page_workspace():
             np.testing.assert_array_equal(res.indices[r], idx, err_msg=f"seed {seed} row {r}")
 
 
+def test_workspace_gather_hand_worked():
+    """Two requests over three pages of two positions (D = 128: 64 value bytes and 4
+    scale bytes a position); request 1's second logical page is out of range."""
+    ps, D = 2, 128
+    pool = np.zeros((3, ps * 68), np.uint8)
+    V = lambda pg, slot: (np.arange(64) + 50 * pg + 7 * slot) % 256
+    S = lambda pg, slot: np.array([200 + 3 * pg + slot, pg, slot, 9])
+    for pg in range(3):
+        for slot in range(ps):
+            pool[pg, slot * 64:(slot + 1) * 64] = V(pg, slot)
+            pool[pg, ps * 64 + slot * 4:ps * 64 + slot * 4 + 4] = S(pg, slot)
+    bt = np.array([[2, 0], [1, 5]], np.int32)       # page 5 does not exist
+    cu = [0, 3, 6]                                   # request 0: 3 positions, request 1: 3
+    vals, scs = oracle.gather_k_workspace(pool, ps, D, bt, cu, max_tokens=7, fill=0xAB)
+    want = [(2, 0), (2, 1), (0, 0), (1, 0), (1, 1)]  # (page, slot) of rows 0..4 by hand
+    for row, (pg, slot) in enumerate(want):
+        np.testing.assert_array_equal(vals[row], V(pg, slot), err_msg=f"row {row}")
+        np.testing.assert_array_equal(scs[row], S(pg, slot), err_msg=f"row {row}")
+    assert np.all(vals[5] == 0) and np.all(scs[5] == 0)        # out-of-range page: zeros
+    assert np.all(vals[6] == 0xAB) and np.all(scs[6] == 0xAB)  # never written
+    # request table, length cap and row cap
+    vals, scs = oracle.gather_k_workspace(pool, ps, D, bt, cu, req_table=[1, 0], max_seq_len=2,
+                                          max_tokens=4, fill=0xAB)
+    for row, (pg, slot) in enumerate([(1, 0), (1, 1), (0xAB, None), (2, 0)]):
+        if slot is None:
+            assert np.all(vals[row] == 0xAB)                   # p = 2 >= max_seq_len
+        else:
+            np.testing.assert_array_equal(vals[row], V(pg, slot), err_msg=f"row {row}")
+
+
+def test_oracle_on_gathered_workspace_equals_paged_cache():
+    """Scoring a chunk from its gathered workspace (one page holding every position) gives
+    the paged cache's logits and indices exactly: the gather moves bytes only."""
+    import dataclasses
+
+    for seed in range(2):
+        spec = W.Spec(name=f"ws{seed}", num_rows=24, num_heads=4, head_dim=64, page_size=32,
+                      cbs=16, nb=10, topk=30, mode="prefill", ke_rule="uniform", ke_lo=1,
+                      ke_hi=320, ks_rule="random", context=320, cand_rule="messy", fill="all")
+        case = W.generate(spec, seed=seed)
+        pool = case.layers[0].host_pool(spec.page_bytes)
+        paged = oracle.indexer_rows(case, pool=pool)
+        n = 320
+        vals, scs = oracle.gather_k_workspace(pool, spec.page_size, spec.head_dim,
+                                              case.block_table, [0, n], req_table=[0])
+        ws_spec = dataclasses.replace(spec, page_size=n)
+        ws_case = dataclasses.replace(case, spec=ws_spec, block_table=np.zeros((1, 1), np.int32))
+        ws_pool = np.concatenate([vals.ravel(), scs.ravel()])[None, :]
+        assert ws_pool.shape[1] == ws_spec.page_bytes
+        packed = oracle.indexer_rows(ws_case, pool=ws_pool)
+        np.testing.assert_array_equal(packed.indices, paged.indices)
+        np.testing.assert_array_equal(packed.count, paged.count)
+        for i in range(case.num_rows):
+            np.testing.assert_array_equal(packed.row_tokens(i), paged.row_tokens(i))
+            np.testing.assert_array_equal(packed.row_logits(i).view(np.uint32),
+                                          paged.row_logits(i).view(np.uint32))
+
+
 # ------------------------------------------------------ invariants -----------
 
 def _check_invariants(case, res):
