@@ -191,8 +191,15 @@ def bench_gather(args, idx, case, cfg, dev, gen_s):
     avg_s = float(np.mean(kernel_ms)) / 1e3
     achieved = launch_bytes / avg_s / 1e9
     peaks = measured_peaks(stream)
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", f"traffic_gather_k_kernel_cfg{args.config}_mxfp4.json")
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            t = json.load(f)
+        if t.get("kernel_source_hash") == kernel_source_hash():
+            traffic = t.get("bytes_per_launch")
     roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "gather_k_kernel",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": "gather_k_kernel",
             "measured_peak": peaks["read_gbs"], "frac_of_measured": achieved / peaks["read_gbs"],
             "avg_launch_us": avg_s * 1e6,
             "launch_us_p10": float(np.percentile(kernel_ms, 10)) * 1e3,
