@@ -218,13 +218,26 @@ def idx_gather_k_workspace(cfg, k, cu_seq_lens, values_out, scales_out, max_seq_
     """Pack requests' paged K into values_out [N, D/2] / scales_out [N, D/32] (u8 device
     tensors); cu_seq_lens: int32 device tensor [num_reqs + 1]."""
     num_reqs = cu_seq_lens.numel() - 1 if cu_seq_lens is not None else 0
+    _check_workspace(cfg, values_out, scales_out)
     return _check(lib.idx_gather_k_workspace(
         ctypes.byref(cfg), ctypes.byref(k), max(0, num_reqs), _p(cu_seq_lens), _p(req_table),
         max_seq_len, values_out.shape[0], _p(values_out), _p(scales_out), _p(stream)))
 
 
+def _check_workspace(cfg, values_out, scales_out):
+    """The library writes max_tokens = values_out.shape[0] rows of D/2 and D/32 bytes:
+    both tensors must hold that many contiguous rows."""
+    for t, row in ((values_out, cfg.head_dim // 2), (scales_out, cfg.head_dim // 32)):
+        if not t.is_contiguous() or t.dim() != 2 or t.shape[1] * t.element_size() != row:
+            raise ValueError(f"workspace tensor must be contiguous [N, {row}] bytes, got "
+                             f"{tuple(t.shape)} x {t.element_size()} B")
+    if scales_out.shape[0] < values_out.shape[0]:
+        raise ValueError("scales_out has fewer rows than values_out")
+
+
 def bind_gather_k_workspace(cfg, k, cu_seq_lens, values_out, scales_out, max_seq_len,
                             req_table=None, stream=None):
+    _check_workspace(cfg, values_out, scales_out)
     vp = lambda x: ctypes.c_void_p(_p(x))
     return BoundCall(lib.idx_gather_k_workspace,
                      (ctypes.byref(cfg), ctypes.byref(k), cu_seq_lens.numel() - 1,

@@ -221,6 +221,18 @@ def test_gather_rejects_bad_arguments():
                                           None, 1, 1, FAKE, FAKE, None) == idx.IDX_EINVAL
 
 
+def test_gather_binding_checks_workspace_shapes():
+    import torch
+
+    c = idx.idx_check_config(cfg())
+    cu = torch.zeros(2, dtype=torch.int32)
+    for vals, scs in ((torch.empty(10, 64, dtype=torch.uint8), torch.empty(9, 4, dtype=torch.uint8)),
+                      (torch.empty(10, 32, dtype=torch.uint8), torch.empty(10, 4, dtype=torch.uint8)),
+                      (torch.empty(64, 10, dtype=torch.uint8).t(), torch.empty(10, 4, dtype=torch.uint8))):
+        with pytest.raises(ValueError):
+            idx.idx_gather_k_workspace(c, kcache(), cu, vals, scs, 1)
+
+
 def test_dense_call_rejects_bad_arguments():
     c = idx.idx_check_config(cfg())
     def call(max_ctx=65536, logits=None, lstride=0, ws=None, wsb=0):
