@@ -178,7 +178,11 @@ int idx_sparse_mqa_logits_topk(const idx_config *cfg, const idx_rows *rows, cons
  * more layers whose rows take the one-row-per-workgroup kernel (num_rows >= the
  * device's CUs, and not the prefill row-group case) all layers run in one launch
  * with two rows on a CU at a time, so one row's selection overlaps another's K
- * stream.  layers is a HOST array of num_layers
+ * stream.  With two or more layers and fewer rows than CUs, every layer runs in one
+ * split scoring launch and one selection launch when each layer's logits have a home:
+ * its logits_out, or its slice of a workspace of idx_workspace_bytes(cfg, num_layers *
+ * num_rows, 0) bytes (layer l at l * num_rows * NB*cbs floats); with a smaller
+ * workspace the layers run one after another.  layers is a HOST array of num_layers
  * (1..IDX_MAX_LAYERS) entries.  Every layer's k must equal layers[0].k in every field
  * but values and scales (one page geometry and block table for the step, as the
  * schedule requires).  workspace: as for idx_sparse_mqa_logits_topk when some

@@ -314,7 +314,8 @@ int idx_sparse_mqa_logits_topk_layers(const idx_config *cfg, const idx_rows *row
     static_assert(idx::kMaxLayers == IDX_MAX_LAYERS, "one layer limit for the launch and the ABI");
     if ((rc = hip_status(idx::launch_sparse_layers(cfg->q_format, to_rows(rows), num_layers, ls,
                                                    to_kcache(cfg, &k0), s, (float *)workspace,
-                                                   cfg->topk, out_stride, g_timing,
+                                                   workspace ? workspace_bytes : 0, cfg->topk,
+                                                   out_stride, g_timing,
                                                    (hipStream_t)stream),
                          "sparse layers launch")))
         return rc;

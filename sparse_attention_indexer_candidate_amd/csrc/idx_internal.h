@@ -80,15 +80,17 @@ struct LayerSet {
     int32_t *out[kMaxLayers];
 };
 
-// The sparse path for num_layers layers.  With two or more layers whose rows take the
-// one-row kernel, one launch scores and selects every layer, two rows a CU (the timing
-// events ride on it); otherwise each
-// layer is launched as launch_sparse does, in layer order, reusing the workspace (the
-// events ride on every layer's scoring launch, so they time the last).
+// The sparse path for num_layers layers.  With two or more layers: rows that take the
+// one-row kernel run every layer in one launch, two rows a CU; fewer rows than CUs run
+// every layer in one split scoring launch and one selection launch (grid z / y = layer)
+// when each layer's logits have a home (its logits_out, or its slice of a workspace of
+// num_layers * rows * NB*cbs floats).  The timing events ride on the (scoring) launch.
+// Otherwise each layer is launched as launch_sparse does, in layer order, reusing the
+// workspace (the events ride on every layer's scoring launch, so they time the last).
 hipError_t launch_sparse_layers(int q_format, const Rows &rows, int32_t num_layers,
                                 const LayerSet &layers, const KCache &k, const Schedule &s,
-                                float *workspace, int32_t topk, int64_t out_stride,
-                                const Timing &timing, hipStream_t stream);
+                                float *workspace, size_t workspace_bytes, int32_t topk,
+                                int64_t out_stride, const Timing &timing, hipStream_t stream);
 
 // Scores every token t < max_ctx of every row into logits [rows][logits_stride]
 // (-inf outside [ks, ke)).

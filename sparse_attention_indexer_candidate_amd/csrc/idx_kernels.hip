@@ -1023,10 +1023,10 @@ constexpr int kTopkThreads = 512;
 // issue at once; ks / ke (only the validity of the scored columns needs them) and the
 // cache geometry arrive while they fly.
 template <int QF, int PW>
-__global__ __launch_bounds__(kScoreThreads) void score_split_kernel(
+__device__ __forceinline__ void score_split_row(
     const int32_t *si_base, const int32_t *pg_base, const void *qv, const void *qs,
-    const float *weights, int32_t nsb, int32_t sbk, int32_t groups_per_wg, Rows rows, KCache k,
-    float *logits) {
+    const float *weights, int32_t nsb, int32_t sbk, int32_t groups_per_wg, const Rows &rows,
+    const KCache &k, float *logits) {
     const int row = blockIdx.x;
     const int wave = uniform(threadIdx.x / kWave);
     const int ncols = nsb * sbk;
@@ -1041,6 +1041,35 @@ __global__ __launch_bounds__(kScoreThreads) void score_split_kernel(
     float *lrow = logits + (int64_t)row * ncols;
     score_groups<QF, PW, PW>(k, f, ks, ke, g0, g1, SparseDesc{si, pg, nsb, sbk},
                              [&](int c, float v) { if (c < ncols) lrow[c] = v; });
+}
+
+template <int QF, int PW>
+__global__ __launch_bounds__(kScoreThreads) void score_split_kernel(
+    const int32_t *si_base, const int32_t *pg_base, const void *qv, const void *qs,
+    const float *weights, int32_t nsb, int32_t sbk, int32_t groups_per_wg, Rows rows, KCache k,
+    float *logits) {
+    score_split_row<QF, PW>(si_base, pg_base, qv, qs, weights, nsb, sbk, groups_per_wg, rows, k,
+                            logits);
+}
+
+// Logits of layer l of a multi-layer split launch: the layer's logits_out, else its slice
+// of the workspace.
+__device__ __forceinline__ float *layer_logits(const LayerSet &ls, int l, float *ws,
+                                               int64_t ws_layer) {
+    return ls.logits_out[l] ? ls.logits_out[l] : ws + (int64_t)l * ws_layer;
+}
+
+// Several layers sharing a schedule, fewer rows than CUs: grid.z = layer.
+template <int QF, int PW>
+__global__ __launch_bounds__(kScoreThreads) void score_split_layers_kernel(
+    const int32_t *si_base, const int32_t *pg_base, int32_t nsb, int32_t sbk,
+    int32_t groups_per_wg, Rows rows, KCache k, LayerSet ls, float *ws, int64_t ws_layer) {
+    const int l = blockIdx.z;
+    KCache kl = k;
+    kl.values = ls.k_values[l];
+    kl.scales = ls.k_scales[l];
+    score_split_row<QF, PW>(si_base, pg_base, ls.q_values[l], ls.q_scales[l], ls.weights[l], nsb,
+                            sbk, groups_per_wg, rows, kl, layer_logits(ls, l, ws, ws_layer));
 }
 
 // Tokens of the KPT sparse columns c0 .. c0+KPT-1 (KPT divides sbk = 1 << lsbk, and c0
@@ -1073,18 +1102,24 @@ struct SparseTokens {
 // loads are one round trip with no load of their addresses before them.  The table
 // row is not checked here: the expansion lists nothing for a row whose table row is
 // invalid (kept = 0), and the schedule comes from the expansion of the same rows.
+struct TopkLds {
+    int32_t si[kMaxNSB];
+    alignas(16) int32_t stage[kMaxRowCols];
+    SelectLds<kTopkThreads> sel;
+};
+
 template <bool DENSE, int KPT>
-__global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(
-    const float *logits, const int32_t *si_base, const int32_t *p_ks, const int32_t *p_ke,
-    const int32_t *p_kept, int32_t nsb, int32_t lsbk, int64_t lstride, int32_t lcols,
-    int32_t topk, int32_t *out, int64_t ostride) {
+__device__ __forceinline__ void topk_split_row(
+    TopkLds &L, const float *logits, const int32_t *si_base, const int32_t *p_ks,
+    const int32_t *p_ke, const int32_t *p_kept, int32_t nsb, int32_t lsbk, int64_t lstride,
+    int32_t lcols, int32_t topk, int32_t *out, int64_t ostride) {
     static_assert(KPT == 8 || KPT == 16, "a run of 8 or 16 columns: whole float4s, inside one "
                   "sparse block (sbk >= 16), and a dense run starting at a multiple of KPT, which "
                   "divides the row length lcols (a multiple of 64)");
     static_assert(KPT * kTopkThreads <= kMaxRowCols, "the stage holds every column");
-    __shared__ int32_t s_si[kMaxNSB];
-    __shared__ alignas(16) int32_t s_stage[kMaxRowCols];
-    __shared__ SelectLds<kTopkThreads> s_sel;
+    int32_t *s_si = L.si;
+    int32_t *s_stage = L.stage;
+    SelectLds<kTopkThreads> &s_sel = L.sel;
     const int row = blockIdx.x, tid = threadIdx.x;
     const int sbk = 1 << lsbk, ncols = nsb << lsbk;
     const int32_t *si = si_base + (int64_t)row * nsb;
@@ -1140,6 +1175,28 @@ __global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(
     select_topk<kTopkThreads, KPT>(key, live, nvalid, kmin, kmax, topk,
                                    out + (int64_t)row * ostride, s_sel, s_stage,
                                    SparseTokens<KPT>{s_si, lsbk});
+}
+
+template <bool DENSE, int KPT>
+__global__ __launch_bounds__(kTopkThreads) void topk_split_kernel(
+    const float *logits, const int32_t *si_base, const int32_t *p_ks, const int32_t *p_ke,
+    const int32_t *p_kept, int32_t nsb, int32_t lsbk, int64_t lstride, int32_t lcols,
+    int32_t topk, int32_t *out, int64_t ostride) {
+    __shared__ TopkLds lds;
+    topk_split_row<DENSE, KPT>(lds, logits, si_base, p_ks, p_ke, p_kept, nsb, lsbk, lstride, lcols,
+                               topk, out, ostride);
+}
+
+// The selection of a multi-layer split launch: grid.y = layer.
+template <int KPT>
+__global__ __launch_bounds__(kTopkThreads) void topk_split_layers_kernel(
+    const int32_t *si_base, const int32_t *p_ks, const int32_t *p_ke, const int32_t *p_kept,
+    int32_t nsb, int32_t lsbk, int32_t topk, LayerSet ls, float *ws, int64_t ws_layer,
+    int64_t ostride) {
+    __shared__ TopkLds lds;
+    const int l = blockIdx.y;
+    topk_split_row<false, KPT>(lds, layer_logits(ls, l, ws, ws_layer), si_base, p_ks, p_ke, p_kept,
+                               nsb, lsbk, (int64_t)0, 0, topk, ls.out[l], ostride);
 }
 
 // Rows >= CUs: one workgroup per row; waves take units of the row's valid 64-column
@@ -1809,13 +1866,59 @@ hipError_t launch_sparse(int q_format, const Rows &rows, const void *q_values, c
                               out, out_stride, timing, stream);
 }
 
+template <int QF>
+static hipError_t launch_split_layers(const Rows &rows, int32_t num_layers, const LayerSet &layers,
+                                      const KCache &k, const Schedule &s, float *workspace,
+                                      int32_t topk, int64_t out_stride, const Timing &timing,
+                                      hipStream_t stream) {
+    const int ncols = s.nsb * s.sbk;
+    const int ngroups = (ncols + 63) / 64;
+    const int64_t ws_layer = (int64_t)rows.num_rows * ncols;
+    int gpw = 8;   // as for one layer (launch_sparse_q)
+    while (gpw < 16 && (int64_t)rows.num_rows * ((ngroups + gpw - 1) / gpw) > 4096) gpw *= 2;
+    const dim3 sgrid(rows.num_rows, (ngroups + gpw - 1) / gpw, num_layers);
+    if (gpw == 8)
+        hipExtLaunchKernelGGL((score_split_layers_kernel<QF, 2>), sgrid, dim3(kScoreThreads), 0,
+                              stream, timing.start, timing.stop, 0, s.sparse_indices, s.pages,
+                              s.nsb, s.sbk, gpw, rows, k, layers, workspace, ws_layer);
+    else
+        hipExtLaunchKernelGGL((score_split_layers_kernel<QF, 4>), sgrid, dim3(kScoreThreads), 0,
+                              stream, timing.start, timing.stop, 0, s.sparse_indices, s.pages,
+                              s.nsb, s.sbk, gpw, rows, k, layers, workspace, ws_layer);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 tgrid(rows.num_rows, num_layers);
+    if (ncols <= 8 * kTopkThreads)
+        hipLaunchKernelGGL((topk_split_layers_kernel<8>), tgrid, dim3(kTopkThreads), 0, stream,
+                           s.sparse_indices, rows.ks, rows.ke, s.kept, s.nsb, s.lsbk, topk, layers,
+                           workspace, ws_layer, out_stride);
+    else
+        hipLaunchKernelGGL((topk_split_layers_kernel<16>), tgrid, dim3(kTopkThreads), 0, stream,
+                           s.sparse_indices, rows.ks, rows.ke, s.kept, s.nsb, s.lsbk, topk, layers,
+                           workspace, ws_layer, out_stride);
+    return hipGetLastError();
+}
+
 hipError_t launch_sparse_layers(int q_format, const Rows &rows, int32_t num_layers,
                                 const LayerSet &layers, const KCache &k, const Schedule &s,
-                                float *workspace, int32_t topk, int64_t out_stride,
-                                const Timing &timing, hipStream_t stream) {
+                                float *workspace, size_t workspace_bytes, int32_t topk,
+                                int64_t out_stride, const Timing &timing, hipStream_t stream) {
     if (rows.num_rows == 0 || num_layers == 0) return hipSuccess;
     const int ncols = s.nsb * s.sbk;
     const int cus = device_cus();
+    if (num_layers >= 2 && rows.num_rows < cus) {
+        // every layer's logits must have a home: its logits_out or its workspace slice
+        bool all_out = true;
+        for (int l = 0; l < num_layers; ++l) all_out = all_out && layers.logits_out[l];
+        const size_t need = (size_t)num_layers * rows.num_rows * ncols * sizeof(float);
+        if (all_out || (workspace && workspace_bytes >= need)) {
+            if (q_format == 0)
+                return launch_split_layers<0>(rows, num_layers, layers, k, s, workspace, topk,
+                                              out_stride, timing, stream);
+            return launch_split_layers<1>(rows, num_layers, layers, k, s, workspace, topk,
+                                          out_stride, timing, stream);
+        }
+    }
     const bool groups = q_format == 0 && s.sbk == 64 && ncols <= 8192 && rows.num_rows >= 8 * cus;
     if (num_layers >= 2 && rows.num_rows >= cus && !groups) {
         const dim3 grid(rows.num_rows, num_layers);

@@ -134,10 +134,12 @@ class GpuRun:
             None if with_logits else self.workspace,
             0 if with_logits else self.workspace.numel())
 
-    def score_layers(self, layers, with_logits):
+    def score_layers(self, layers, with_logits, workspace_layers=1):
         """One idx_sparse_mqa_logits_topk_layers call over the given layers; returns
         per-layer (indices, logits or None) device tensors.  with_logits[i] False: that
-        layer writes no logits (the workspace serves it)."""
+        layer writes no logits (the workspace serves it).  workspace_layers: the
+        workspace holds that many layers' logits (all of them lets fewer rows than CUs
+        run every layer in one split launch)."""
         import torch
 
         R, s = self.case.num_rows, self.spec
@@ -151,9 +153,12 @@ class GpuRun:
             outs.append(out)
             logs.append(lg)
             entries.append((qv, qs, L.weights, self.kcaches[layer], out, lg))
+        ws = self.workspace
+        if workspace_layers > 1:
+            ws = torch.empty(self.idx.idx_workspace_bytes(self.cfg, R * workspace_layers, 0),
+                             dtype=torch.uint8, device=dev)
         self.idx.idx_sparse_mqa_logits_topk_layers(self.cfg, self.rows, self.sched.struct,
-                                                   entries, s.topk, self.workspace,
-                                                   self.workspace.numel())
+                                                   entries, s.topk, ws, ws.numel())
         return outs, logs
 
     def fetch(self):

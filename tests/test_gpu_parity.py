@@ -485,6 +485,21 @@ def test_layers_call_matches_per_layer_calls_and_oracle(name, q_format):
     _say(f"[layers-{name}-{q_format}] one call, {nl} layers")
     outs, logs = g.score_layers(range(nl), with_logits)
     torch.cuda.synchronize()
+    # a workspace for every layer's logits, and every layer with its own logits: fewer rows
+    # than CUs then take the batched split launches
+    _say(f"[layers-{name}-{q_format}] workspace for all layers")
+    outs_w, logs_w = g.score_layers(range(nl), with_logits, workspace_layers=nl)
+    _say(f"[layers-{name}-{q_format}] every layer with logits")
+    outs_a, logs_a = g.score_layers(range(nl), [True] * nl)
+    torch.cuda.synchronize()
+    for layer in range(nl):
+        np.testing.assert_array_equal(outs_w[layer].cpu().numpy(), outs[layer].cpu().numpy(),
+                                      err_msg=f"{name} layer {layer}: full workspace")
+        np.testing.assert_array_equal(outs_a[layer].cpu().numpy(), outs[layer].cpu().numpy(),
+                                      err_msg=f"{name} layer {layer}: all logits")
+        np.testing.assert_array_equal(logs_a[layer].cpu().numpy().view(np.uint32),
+                                      (logs[layer] if logs[layer] is not None else logs_a[layer])
+                                      .cpu().numpy().view(np.uint32))
     rng = np.random.default_rng(11)
     sample = np.unique(np.r_[0, case.num_rows - 1, rng.integers(0, case.num_rows, 6)]).astype(np.int32)
     for layer in range(nl):
