@@ -247,6 +247,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--layers", type=int, default=0,
+                    help="consuming layers a step (0: the workload's own); each layer gets its "
+                         "own K pool, query and weights, all sharing one schedule")
     ap.add_argument("--per-layer-calls", action="store_true",
                     help="one sparse call per layer instead of one multi-layer call")
     ap.add_argument("--graph", action="store_true",
@@ -285,6 +288,10 @@ def main():
     spec = W.config(args.config)
     if args.q_format == "fp8" and "fp8" not in spec.q_formats:
         spec = W.config(args.config, q_formats=("mxfp4", "fp8"))
+    if args.layers > 0 and args.layers != spec.layers:
+        import dataclasses
+
+        spec = dataclasses.replace(spec, layers=args.layers, name=f"{spec.name}_l{args.layers}")
     t0 = time.time()
     case = W.generate(spec, args.seed)
     gen_s = time.time() - t0
@@ -331,6 +338,8 @@ def main():
     launch_layers = 1
     if layers_call and kernel_name == "fused_row_kernel":
         kernel_name, launch_layers = "fused_layers_kernel", spec.layers
+    elif layers_call and kernel_name == "score_split_kernel":
+        kernel_name, launch_layers = "score_split_layers_kernel", spec.layers
     events_per_step = 1 if layers_call else spec.layers
     if args.path == "dense":
         # every context token's K, the row's query state, the logits row written
@@ -358,7 +367,10 @@ def main():
                             q_rowscale=None if L.q_rowscale is None else L.q_rowscale.clone())
                     for L in base.layers]))
 
-    ws_bytes = idx.idx_workspace_bytes(cfg, R, max_ctx if args.path == "dense" else 0)
+    # a multi-layer call on fewer rows than CUs keeps every layer's logits (one launch
+    # scores them all)
+    ws_rows = R * (spec.layers if kernel_name == "score_split_layers_kernel" else 1)
+    ws_bytes = idx.idx_workspace_bytes(cfg, ws_rows, max_ctx if args.path == "dense" else 0)
     plans = []
     for d in reps:
         plans.append(dict(
