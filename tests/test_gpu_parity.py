@@ -734,3 +734,60 @@ def test_gather_then_score_equals_paged_cache():
     torch.cuda.synchronize()
     np.testing.assert_array_equal(out.cpu().numpy(), ref["indices"])
     np.testing.assert_array_equal(lg.cpu().numpy().view(np.uint32), ref["logits"].view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["split", "one_launch"])
+def test_layers_call_graph_replays_match_eager(name):
+    """The expansion and one multi-layer call (every layer's logits in the workspace, so
+    fewer rows than CUs take the batched split launches) captured as one HIP graph and
+    replayed with eager steps of other inputs between the replays: every replay gives
+    the eager indices of every layer."""
+    import sparse_attention_indexer_candidate_amd as idx
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        sh = stream.cuda_stream
+        runs = []
+        for seed in (0, 1):
+            case = W.generate(LAYERED[name], seed)
+            d = to_device(case, DEV)
+            s = case.spec
+            R, nl = case.num_rows, s.layers
+            cfg = idx.make_config(s.num_heads, s.head_dim, idx.IDX_Q_MXFP4, s.page_size, s.cbs, 0,
+                                  s.nb, s.topk)
+            rows = idx.make_rows(d.row_ke, d.row_ks, d.row_table)
+            kcs = [idx.make_kcache(L.pool, s.page_size, s.head_dim, d.block_table) for L in d.layers]
+            sched = idx.Schedule(cfg, R, DEV)
+            outs = [torch.full((R, s.topk), -7, dtype=torch.int32, device=DEV) for _ in range(nl)]
+            ws = torch.empty(idx.idx_workspace_bytes(cfg, R * nl, 0), dtype=torch.uint8, device=DEV)
+            entries = [(*L.q("mxfp4"), L.weights, kcs[i], outs[i], None)
+                       for i, L in enumerate(d.layers)]
+            calls = [idx.bind_expand_candidates(cfg, rows, kcs[0], d.candidate_blocks,
+                                                d.candidate_blocks.stride(0), sched.struct,
+                                                stream=sh),
+                     idx.bind_sparse_mqa_logits_topk_layers(cfg, rows, sched.struct, entries, s.topk,
+                                                            ws, ws.numel(), stream=sh)]
+            runs.append(dict(keep=(d, rows, kcs, sched, ws), calls=calls, outs=outs))
+        for r in runs:                                   # eager results
+            for c in r["calls"]:
+                c()
+        torch.cuda.synchronize()
+        for r in runs:
+            r["refs"] = [o.clone() for o in r["outs"]]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for c in runs[0]["calls"]:
+                c()
+        other = runs[1]
+        for rep in range(3):
+            for o in runs[0]["outs"] + other["outs"]:
+                o.fill_(-7)
+            for c in other["calls"]:                     # eager work between replays
+                c()
+            g.replay()
+            torch.cuda.synchronize()
+            _say(f"[graph layers {name}] replay {rep}")
+            for layer, (o, ref) in enumerate(zip(runs[0]["outs"], runs[0]["refs"])):
+                assert torch.equal(o, ref), f"replay {rep} layer {layer}"
+            for layer, (o, ref) in enumerate(zip(other["outs"], other["refs"])):
+                assert torch.equal(o, ref), f"eager between replays, layer {layer}"
