@@ -136,6 +136,19 @@ def measured_peaks(stream) -> dict:
                    "median of 5 launches timed with events"}
 
 
+def gather_workload(case):
+    """(table rows, request lengths, algorithmic bytes a launch) of the gather benchmark:
+    one request per table row, of its rows' largest ke.  A launch reads and writes each
+    position's D/2 value and D/32 scale bytes, reads one block-table entry a page, and
+    reads cu and the request table (8 B a request)."""
+    spec = case.spec
+    tables = np.unique(case.row_table)
+    lens = np.array([int(case.row_ke[case.row_table == t].max()) for t in tables], np.int64)
+    pages = int(sum((n + spec.page_size - 1) // spec.page_size for n in lens))
+    per_pos = spec.head_dim // 2 + spec.head_dim // 32
+    return tables, lens, int(lens.sum()) * per_pos * 2 + pages * 4 + 8 * len(lens)
+
+
 def bench_gather(args, idx, case, cfg, dev, gen_s):
     """The packed K workspace gather: one request per table row, its positions [0, ke)
     (the largest ke of the rows on it), layer 0's pool, every step one launch."""
@@ -144,14 +157,9 @@ def bench_gather(args, idx, case, cfg, dev, gen_s):
     from workloads.device import to_device
 
     spec = case.spec
-    tables = np.unique(case.row_table)
-    lens = np.array([int(case.row_ke[case.row_table == t].max()) for t in tables], np.int64)
+    tables, lens, launch_bytes = gather_workload(case)
     cu = np.r_[0, np.cumsum(lens)].astype(np.int32)
     total, max_seq = int(cu[-1]), int(lens.max())
-    # bytes per launch: each position's value and scale bytes read and written, its
-    # block-table entry read once per page, cu and the request table
-    pages = int(sum((n + spec.page_size - 1) // spec.page_size for n in lens))
-    launch_bytes = total * (spec.head_dim // 2 + spec.head_dim // 32) * 2 + pages * 4 + 8 * len(lens)
     base = to_device(case, dev, layers=[0])
     pool_bytes = base.layers[0].pool.numel()
     nrep = args.replicas if args.replicas > 0 else max(2, math.ceil(1.5e9 / launch_bytes))

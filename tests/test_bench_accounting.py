@@ -29,6 +29,15 @@ def test_algorithmic_bytes_by_hand():
     assert bench.algorithmic_bytes(case, "fp8", ends) == k_bytes + 4 * row8
 
 
+def test_gather_bytes_by_hand():
+    case = W.generate(W.config(1), 0)          # 4 decode rows, one table row each, page 64
+    case.row_ke[:] = [4096, 65, 1, 0]
+    tables, lens, nbytes = bench.gather_workload(case)
+    assert list(lens) == [4096, 65, 1, 0]
+    # 68 bytes a position read and 68 written; block-table entries: 64 + 2 + 1 + 0 pages
+    assert nbytes == (4096 + 65 + 1) * 136 + (64 + 2 + 1) * 4 + 8 * 4
+
+
 def test_more_than_one_gpu_is_refused_with_a_message():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
