@@ -467,6 +467,15 @@ LAYERED = {
                          layers=2, mode="prefill", ke_rule="uniform", ke_lo=1, ke_hi=1500,
                          ks_rule="random", context=1600, cand_rule="messy", fill="all",
                          q_formats=("mxfp4", "fp8")),
+    # 4096-column rows in one launch (8 keys a thread at 512 threads)
+    "one_launch_4096": W.Spec(name="ml5", num_rows=260, page_size=64, cbs=64, nb=64, topk=2048,
+                              layers=2, ke_rule="uniform", ke_lo=3000, ke_hi=9000,
+                              cand_rule="distinct", fill="candidates"),
+    # fewer rows than CUs at the column and top-k limits: the batched split selection
+    # with 16 keys a thread
+    "split_wide": W.Spec(name="ml6", num_rows=24, page_size=64, cbs=64, nb=128, topk=7000,
+                         layers=2, ke_rule="uniform", ke_lo=6000, ke_hi=12000,
+                         cand_rule="distinct", fill="candidates"),
     # fewer rows than CUs: the split kernels, layer after layer
     "split": W.Spec(name="ml2", num_rows=40, page_size=32, cbs=32, nb=30, topk=500, layers=2,
                     ke_rule="uniform", ke_lo=100, ke_hi=1500, cand_rule="messy", fill="all",
@@ -477,7 +486,12 @@ LAYERED = {
 @pytest.mark.parametrize("q_format", ["mxfp4", "fp8"])
 @pytest.mark.parametrize("name", sorted(LAYERED))
 def test_layers_call_matches_per_layer_calls_and_oracle(name, q_format):
-    case = W.generate(LAYERED[name], seed=5)
+    import dataclasses
+
+    spec = LAYERED[name]
+    if q_format not in spec.q_formats:
+        spec = dataclasses.replace(spec, q_formats=("mxfp4", "fp8"))
+    case = W.generate(spec, seed=5)
     nl = case.spec.layers
     g = GpuRun(case, to_device(case, DEV), q_format=q_format)
     g.expand()
