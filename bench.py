@@ -348,6 +348,8 @@ def main():
         kernel_name, launch_layers = "fused_layers_kernel", spec.layers
     elif layers_call and kernel_name == "score_split_kernel":
         kernel_name, launch_layers = "score_split_layers_kernel", spec.layers
+    elif layers_call and kernel_name == "row_group_kernel":
+        kernel_name, launch_layers = "row_group_layers_kernel", spec.layers
     events_per_step = 1 if layers_call else spec.layers
     if args.path == "dense":
         # every context token's K, the row's query state, the logits row written

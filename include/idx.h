@@ -182,7 +182,8 @@ int idx_sparse_mqa_logits_topk(const idx_config *cfg, const idx_rows *rows, cons
  * split scoring launch and one selection launch when each layer's logits have a home:
  * its logits_out, or its slice of a workspace of idx_workspace_bytes(cfg, num_layers *
  * num_rows, 0) bytes (layer l at l * num_rows * NB*cbs floats); with a smaller
- * workspace the layers run one after another.  layers is a HOST array of num_layers
+ * workspace the layers run one after another.  A prefill chunk's rows (the row-group
+ * case) run every layer in one launch as well.  layers is a HOST array of num_layers
  * (1..IDX_MAX_LAYERS) entries.  Every layer's k must equal layers[0].k in every field
  * but values and scales (one page geometry and block table for the step, as the
  * schedule requires).  workspace: as for idx_sparse_mqa_logits_topk when some

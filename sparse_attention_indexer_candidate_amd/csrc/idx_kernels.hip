@@ -1425,14 +1425,14 @@ __device__ __forceinline__ int pick(const int (&a)[N], int i) {
 }
 
 template <int NCMAX, int GR>
-__global__ __launch_bounds__(kGroupThreads) void row_group_kernel(
-    Rows rows, const void *qv, const void *qs, const float *weights, KCache k, Schedule s,
-    float *logits_out, int32_t topk, int32_t *out, int64_t ostride) {
+__device__ __forceinline__ void row_group_rows(
+    GroupLds<NCMAX, GR> &lds, const Rows &rows, const void *qv, const void *qs,
+    const float *weights, const KCache &k, const Schedule &s, float *logits_out, int32_t topk,
+    int32_t *out, int64_t ostride) {
     static_assert(GR >= 1 && GR <= kGroupWaves, "a wave selects each row");
     static_assert(64 % (NCMAX / kGroupThreads) == 0, "a thread's keys lie in one sparse block");
     using L = GroupLds<NCMAX, GR>;
     constexpr int NSB = L::NSB;
-    __shared__ L lds;
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int wave = uniform(tid / kWave);
     // Last group first: in a causal chunk later rows hold more columns, so the longest
@@ -1637,6 +1637,29 @@ __global__ __launch_bounds__(kGroupThreads) void row_group_kernel(
                                         lds.u.sel, reinterpret_cast<int32_t *>(lds.logit[r]),
                                         SparseTokens<KPT>{lds.si[r], 6});
     }
+}
+
+template <int NCMAX, int GR>
+__global__ __launch_bounds__(kGroupThreads) void row_group_kernel(
+    Rows rows, const void *qv, const void *qs, const float *weights, KCache k, Schedule s,
+    float *logits_out, int32_t topk, int32_t *out, int64_t ostride) {
+    __shared__ GroupLds<NCMAX, GR> lds;
+    row_group_rows<NCMAX, GR>(lds, rows, qv, qs, weights, k, s, logits_out, topk, out, ostride);
+}
+
+// Several layers of a prefill chunk sharing one schedule, one launch (grid.y = layer):
+// each layer's groups go heaviest first, and the next layer's heavy groups fill the CUs
+// that the previous layer's light ones leave.
+template <int NCMAX, int GR>
+__global__ __launch_bounds__(kGroupThreads) void row_group_layers_kernel(
+    Rows rows, KCache k, Schedule s, LayerSet ls, int32_t topk, int64_t ostride) {
+    __shared__ GroupLds<NCMAX, GR> lds;
+    const int l = blockIdx.y;
+    KCache kl = k;
+    kl.values = ls.k_values[l];
+    kl.scales = ls.k_scales[l];
+    row_group_rows<NCMAX, GR>(lds, rows, ls.q_values[l], ls.q_scales[l], ls.weights[l], kl, s,
+                              ls.logits_out[l], topk, ls.out[l], ostride);
 }
 
 
@@ -1906,6 +1929,20 @@ hipError_t launch_sparse_layers(int q_format, const Rows &rows, int32_t num_laye
     if (rows.num_rows == 0 || num_layers == 0) return hipSuccess;
     const int ncols = s.nsb * s.sbk;
     const int cus = device_cus();
+    const bool groups = q_format == 0 && s.sbk == 64 && ncols <= 8192 && rows.num_rows >= 8 * cus;
+    if (num_layers >= 2 && groups) {
+        constexpr int GR = 2;
+        const dim3 grid((rows.num_rows + GR - 1) / GR, num_layers);
+        if (ncols <= 4096)
+            hipExtLaunchKernelGGL((row_group_layers_kernel<4096, GR>), grid, dim3(kGroupThreads), 0,
+                                  stream, timing.start, timing.stop, 0, rows, k, s, layers, topk,
+                                  out_stride);
+        else
+            hipExtLaunchKernelGGL((row_group_layers_kernel<8192, GR>), grid, dim3(kGroupThreads), 0,
+                                  stream, timing.start, timing.stop, 0, rows, k, s, layers, topk,
+                                  out_stride);
+        return hipGetLastError();
+    }
     if (num_layers >= 2 && rows.num_rows < cus) {
         // every layer's logits must have a home: its logits_out or its workspace slice
         bool all_out = true;
@@ -1919,7 +1956,6 @@ hipError_t launch_sparse_layers(int q_format, const Rows &rows, int32_t num_laye
                                           out_stride, timing, stream);
         }
     }
-    const bool groups = q_format == 0 && s.sbk == 64 && ncols <= 8192 && rows.num_rows >= 8 * cus;
     if (num_layers >= 2 && rows.num_rows >= cus && !groups) {
         const dim3 grid(rows.num_rows, num_layers);
 #define IDX_LAUNCH_LAYERS(QF_, NT_, KPT_, U_, WPE_)                                              \
