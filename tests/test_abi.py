@@ -30,6 +30,32 @@ def test_library_exports_every_declared_function():
         assert hasattr(lib, n), n
 
 
+def test_header_is_c99_and_struct_layouts_match_the_binding(tmp_path):
+    """include/idx.h compiles as plain C99 and each struct's size and field offsets in C
+    equal the ctypes mirror's."""
+    import subprocess
+
+    structs = ["idx_config", "idx_kcache", "idx_rows", "idx_schedule", "idx_layer"]
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "idx.h"', "int main(void) {"]
+    for name in structs:
+        lines.append(f'    printf("{name} %zu\\n", sizeof({name}));')
+        for f, _ in getattr(idx, name)._fields_:
+            lines.append(f'    printf("{name}.{f} %zu\\n", offsetof({name}, {f}));')
+    lines += ["    return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-o", str(exe)], check=True)
+    got = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                  check=True).stdout.splitlines())
+    for name in structs:
+        st = getattr(idx, name)
+        assert int(got[name]) == ctypes.sizeof(st), name
+        for f, _ in st._fields_:
+            assert int(got[f"{name}.{f}"]) == getattr(st, f).offset, f"{name}.{f}"
+
+
 def cfg(**kw):
     base = dict(num_heads=64, head_dim=128, q_format=0, page_size=64, candidate_block_size=64,
                 sparse_block_kv=0, num_candidate_blocks=64, topk=2048)
