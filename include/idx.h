@@ -171,9 +171,10 @@ int idx_sparse_mqa_logits_topk(const idx_config *cfg, const idx_rows *rows, cons
                                int64_t out_stride, float *logits_out, void *workspace,
                                size_t workspace_bytes, void *stream);
 
-/* Steps a2-a6 for several consuming layers of one step (the pages' multi-layer
- * decode: the layers after the candidate source reuse one expansion and schedule,
- * each with its own K cache, query and weights).  Same result, layer by layer, as
+/* Steps a2-a6 for several consuming layers of one step (the DeepSeek-V4.1 sparse
+ * indexer backend source: the per-row schedule scratch that the first consuming
+ * layer fills is reused by the later ones, each with its own K cache, query and
+ * weights).  Same result, layer by layer, as
  * calling idx_sparse_mqa_logits_topk once per layer in layer order.  With two or
  * more layers whose rows take the one-row-per-workgroup kernel (num_rows >= the
  * device's CUs, and not the prefill row-group case) all layers run in one launch
