@@ -708,6 +708,16 @@ def test_gather_k_workspace_matches_oracle():
     torch.cuda.synchronize()
     np.testing.assert_array_equal(vals.cpu().numpy(), want_v)
     np.testing.assert_array_equal(scs.cpu().numpy(), want_s)
+    # no request table: request r reads table row r
+    want_v, want_s = oracle.gather_k_workspace(pool, spec.page_size, spec.head_dim, bt, cu,
+                                               max_seq_len=max_seq, max_tokens=max_tokens,
+                                               fill=0x5C)
+    vals.fill_(0x5C)
+    scs.fill_(0x5C)
+    idx.idx_gather_k_workspace(cfg, kc, torch.from_numpy(cu).to(DEV), vals, scs, max_seq)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(vals.cpu().numpy(), want_v)
+    np.testing.assert_array_equal(scs.cpu().numpy(), want_s)
 
 
 def test_gather_then_score_equals_paged_cache():
