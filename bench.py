@@ -1,17 +1,20 @@
 """Throughput of the candidate-consuming sparse MQA-logits indexer on one MI355X.
 
 One step = the whole hot path over one batch: idx_expand_candidates (the shared
-sparse-column schedule) followed by idx_sparse_mqa_logits_topk for every consumer
-layer (paged gather, MX-scaled MFMA, ReLU + fp32 head reduce, per-row top-k).  The
-default workload is the decode batch (64 rows, contexts 8k-32k, 64 candidate blocks
-of 64 tokens, top-2048).  Inputs are seeded and synthetic and already resident in
-HBM when the timed region starts; the step rotates through enough copies of them
-(distinct device buffers) that no step finds its K pages in the 256 MB Infinity
-Cache.
+sparse-column schedule) followed by the consuming layers (paged gather, MX-scaled
+MFMA, ReLU + fp32 head reduce, per-row top-k): one idx_sparse_mqa_logits_topk_layers
+call for a step's layers.  The default workload is the largest one that fits one GPU,
+the long-context decode batch (256 rows, contexts 32k-128k, 128 candidate blocks of
+64 tokens, top-2048, 4 consuming layers sharing one schedule).  Inputs are seeded and
+synthetic and already resident in HBM when the timed region starts; the step rotates
+through enough copies of them (distinct device buffers) that no step finds its K
+pages in the 256 MB Infinity Cache.
 
 Prints one JSON line: candidate columns scored per second (and rows/s), the
 dominant kernel's roofline (algorithmic bytes per launch / average launch time,
-timed with HIP events on its stream), and the CPU oracle timed on a bounded sample.
+timed with HIP events attached to at least 50 of its launches on the bench stream,
+in a pass after the timed steps), the step-level bandwidth, the prefill chunk's
+MX-FP4 roofline from the same run, and the CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -32,7 +35,7 @@ METRIC = "candidate cols scored/s & rows/s incl. top-k; % of HBM / MXFP4-MFMA ro
 HBM_PEAK_GBS = 8000.0
 MXFP4_PEAK_TFLOPS = 10066.0
 VALU_PEAK_TLANEOPS = 256 * 4 * 16 * 2.4e9 / 1e12   # 39.3: one op a lane a cycle, every SIMD
-TIMING_STRIDE = 16         # steps between two timed scoring launches
+EVENT_STEPS = 64           # steps of the event-timed pass (each times its scoring launches)
 KERNEL_SOURCES = ["sparse_attention_indexer_candidate_amd/csrc/idx_kernels.hip",
                   "sparse_attention_indexer_candidate_amd/csrc/idx_api.hip"]
 
@@ -59,11 +62,30 @@ def algorithmic_bytes(case, q_format: str, ends: np.ndarray, with_output: bool =
     return int(ends.astype(np.int64).sum()) * per_col + case.num_rows * per_row
 
 
+def host_cpu() -> dict:
+    """The host CPU the oracle runs on: model name, logical CPUs, CPUs this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        allowed = os.cpu_count() or 1
+    return {"cpu_model": model, "nproc": os.cpu_count() or 1, "cpus_allowed": allowed}
+
+
 def cpu_baseline(case, q_format: str, seconds: float, threads: int = 1):
     """The oracle (unchanged) over chunks of 4 of the workload's rows of layer 0, taken in
-    order and wrapping around, until `seconds` of wall time have passed.  With threads > 1
-    the same calls run on that many threads at once (the C oracle releases the GIL and
-    keeps no state between calls), i.e. the rows split across the host cores."""
+    order and wrapping around, until `seconds` of wall time have passed.  threads == 1:
+    on the calling thread pinned to one CPU (restored afterwards).  threads > 1: the same
+    calls on that many threads at once (the C oracle releases the GIL and keeps no state
+    between calls), i.e. the rows split across the host cores."""
     import threading
 
     import oracle
@@ -85,18 +107,33 @@ def cpu_baseline(case, q_format: str, seconds: float, threads: int = 1):
                 state["rows"] += chunk.size
                 state["cols"] += int(res.count.sum())
 
+    pinned = None
     t0 = time.perf_counter()
-    ts = [threading.Thread(target=worker) for _ in range(threads)]
-    for t in ts:
-        t.start()
-    for t in ts:
-        t.join()
+    if threads == 1:
+        try:
+            old = os.sched_getaffinity(0)
+            pinned = min(old)
+            os.sched_setaffinity(0, {pinned})
+        except (AttributeError, OSError):
+            old = None
+        try:
+            worker()
+        finally:
+            if old is not None:
+                os.sched_setaffinity(0, old)
+    else:
+        ts = [threading.Thread(target=worker) for _ in range(threads)]
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
     wall = time.perf_counter() - t0
+    where = f"pinned to CPU {pinned}" if pinned is not None else f"{threads} thread(s)"
     return dict(value=state["cols"] / wall, unit="cols/s", cores=threads, kind="oracle",
-                rows_per_s=state["rows"] / wall,
+                rows_per_s=state["rows"] / wall, **host_cpu(),
                 sample=f"{state['rows']} row-scorings of layer 0 ({state['cols']} candidate cols, "
                        f"{case.num_rows} rows wrapping), C oracle on {threads} thread(s), "
-                       f"{wall:.1f} s wall")
+                       f"{where}, {wall:.1f} s wall")
 
 
 def measured_peaks(stream) -> dict:
@@ -174,9 +211,8 @@ def bench_gather(args, idx, case, cfg, dev, gen_s):
     calls = [idx.bind_gather_k_workspace(
         cfg, idx.make_kcache(p, spec.page_size, spec.head_dim, base.block_table), d_cu, vals,
         scs, max_seq, req_table=d_req, stream=stream.cuda_stream) for p in pools]
-    timed_steps = [i for i in range(args.steps) if i % TIMING_STRIDE == 0]
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in timed_steps]
+          for _ in range(max(EVENT_STEPS, 1))]
     for a, b in ev:
         a.record(stream)
         b.record(stream)
@@ -188,13 +224,15 @@ def bench_gather(args, idx, case, cfg, dev, gen_s):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        if i % TIMING_STRIDE == 0:
-            set_events(*ev_raw[i // TIMING_STRIDE])
         calls[i % nrep]()
-        if i % TIMING_STRIDE == 0:
-            set_events(None, None)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    # event-timed pass (not part of the timed steps): every launch carries its events
+    for i, pair in enumerate(ev_raw):
+        set_events(*pair)
+        calls[i % nrep]()
+        set_events(None, None)
+    torch.cuda.synchronize()
     kernel_ms = [a.elapsed_time(b) for a, b in ev]
     avg_s = float(np.mean(kernel_ms)) / 1e3
     achieved = launch_bytes / avg_s / 1e9
@@ -239,21 +277,251 @@ def bench_gather(args, idx, case, cfg, dev, gen_s):
     print(json.dumps(out), flush=True)
 
 
+def traffic_for(kernel_name: str, config: int, q_format: str):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE counters of this
+    kernel on this workload, or None when none were taken for the current kernel sources."""
+    tfile = os.path.join(ROOT, "profiles", f"traffic_{kernel_name}_cfg{config}_{q_format}.json")
+    if not os.path.exists(tfile):
+        return None
+    with open(tfile) as f:
+        t = json.load(f)
+    return t.get("bytes_per_launch") if t.get("kernel_source_hash") == kernel_source_hash() else None
+
+
+def run_workload(idx, W, config: int, args, dev, stream, steps: int, warmup: int,
+                 layers: int = 0, per_layer_calls: bool = False, graph: bool = False):
+    """Generates one workload, times `steps` steps (after `warmup`) with nothing attached,
+    then an event pass of EVENT_STEPS steps whose scoring launches carry dispatch events.
+    Returns the measurements and the accounting the report needs."""
+    import torch
+
+    from workloads.device import to_device
+
+    spec = W.config(config)
+    if args.q_format == "fp8" and "fp8" not in spec.q_formats:
+        spec = W.config(config, q_formats=("mxfp4", "fp8"))
+    if layers > 0 and layers != spec.layers:
+        import dataclasses
+
+        spec = dataclasses.replace(spec, layers=layers, name=f"{spec.name}_l{layers}")
+    t0 = time.time()
+    case = W.generate(spec, args.seed)
+    gen_s = time.time() - t0
+    cfg = idx.make_config(spec.num_heads, spec.head_dim,
+                          idx.IDX_Q_MXFP4 if args.q_format == "mxfp4" else idx.IDX_Q_FP8_E4M3_ROWSCALE,
+                          spec.page_size, spec.cbs, 0, spec.nb, spec.topk)
+    R = case.num_rows
+
+    # Touched bytes per step decide how many copies defeat the Infinity Cache.
+    sched0 = idx.Schedule(cfg, R, dev)
+    base = to_device(case, dev)
+    kc0 = idx.make_kcache(base.layers[0].pool, spec.page_size, spec.head_dim, base.block_table)
+    rows0 = idx.make_rows(base.row_ke, base.row_ks, base.row_table)
+    idx.idx_expand_candidates(cfg, rows0, kc0, base.candidate_blocks,
+                              base.candidate_blocks.stride(0), sched0.struct)
+    torch.cuda.synchronize()
+    ends = sched0.end.cpu().numpy()
+    ctx = (case.row_ke - (case.row_ks if case.row_ks is not None else 0)).astype(np.int64)
+    max_ctx = int(case.row_ke.max()) if R else 0
+
+    # The step's consuming layers go to the library in one call; the library reports
+    # which kernels that call launches (one rule for the launch and this accounting).
+    dense = args.path == "dense"
+    layers_call = not dense and spec.layers > 1 and not per_layer_calls
+    ncols = idx.idx_num_sparse_blocks(cfg) * cfg.sparse_block_kv
+    ws_rows_all = R * spec.layers
+    plan = idx.idx_sparse_plan(cfg, R, spec.layers if layers_call else 1, logits_home=True)
+    if dense:
+        kernel_name, fused, launch_layers = "score_dense_kernel", False, 1
+    else:
+        kernel_name = plan["scoring_kernel"]
+        fused = plan["selects_in_scoring_kernel"]
+        launch_layers = plan["layers_per_scoring_launch"]
+    calls_per_step = 1 if layers_call else spec.layers
+    if dense:
+        # every context token's K, the row's query state, the logits row written
+        kernel_bytes = algorithmic_bytes(case, args.q_format, ctx, with_output=False) + R * 4 * max_ctx
+        step_bytes = (kernel_bytes + R * 4 * spec.topk) * spec.layers
+    else:
+        kernel_bytes = algorithmic_bytes(case, args.q_format, ends, with_output=fused)
+        step_bytes = algorithmic_bytes(case, args.q_format, ends) * spec.layers
+    pool_bytes = sum(L.pool.numel() for L in base.layers)
+    if args.replicas > 0:
+        nrep = args.replicas
+    else:
+        nrep = max(2, math.ceil(1.5e9 / step_bytes))
+        nrep = max(1, min(nrep, int(40e9 // max(pool_bytes, 1))))
+
+    reps = [base]
+    for _ in range(nrep - 1):
+        reps.append(type(base)(
+            row_ks=base.row_ks.clone(), row_ke=base.row_ke.clone(), row_table=base.row_table.clone(),
+            block_table=base.block_table.clone(), candidate_blocks=base.candidate_blocks.clone(),
+            layers=[type(L)(pool=L.pool.clone(), weights=L.weights.clone(),
+                            q_values=None if L.q_values is None else L.q_values.clone(),
+                            q_scales=None if L.q_scales is None else L.q_scales.clone(),
+                            q_fp8=None if L.q_fp8 is None else L.q_fp8.clone(),
+                            q_rowscale=None if L.q_rowscale is None else L.q_rowscale.clone())
+                    for L in base.layers]))
+
+    # a multi-layer call on fewer rows than CUs keeps every layer's logits (one launch
+    # scores them all)
+    ws_rows = ws_rows_all if layers_call else R
+    ws_bytes = idx.idx_workspace_bytes(cfg, ws_rows, max_ctx if dense else 0)
+    plans = []
+    for d in reps:
+        plans.append(dict(
+            d=d, rows=idx.make_rows(d.row_ke, d.row_ks, d.row_table),
+            kc=[idx.make_kcache(L.pool, spec.page_size, spec.head_dim, d.block_table) for L in d.layers],
+            sched=idx.Schedule(cfg, R, dev),
+            out=torch.empty((R, spec.topk), dtype=torch.int32, device=dev),
+            out_l=[torch.empty((R, spec.topk), dtype=torch.int32, device=dev)
+                   for _ in range(spec.layers)],
+            ws=torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)))
+    sh = stream.cuda_stream
+    n_events = EVENT_STEPS * calls_per_step
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_events)]
+    for a, b in ev:            # materialise the HIP events before the timed region
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ev_raw = [(idx.event_handle(a), idx.event_handle(b)) for a, b in ev]
+
+    # Every launch of a step is bound once (arguments marshalled ahead), as a serving
+    # loop would: a step then costs the host one foreign call per launch, so short
+    # steps are not bound by Python.
+    for p in plans:
+        d = p["d"]
+        p["expand"] = idx.bind_expand_candidates(cfg, p["rows"], p["kc"][0], d.candidate_blocks,
+                                                 d.candidate_blocks.stride(0), p["sched"].struct,
+                                                 stream=sh)
+        p["layers"] = []
+        if layers_call:
+            entries = [(*L.q(args.q_format), L.weights, p["kc"][layer], p["out_l"][layer], None)
+                       for layer, L in enumerate(d.layers)]
+            p["layers"].append(idx.bind_sparse_mqa_logits_topk_layers(
+                cfg, p["rows"], p["sched"].struct, entries, spec.topk, p["ws"], p["ws"].numel(),
+                stream=sh))
+        for layer, L in enumerate([] if layers_call else d.layers):
+            qv, qs = L.q(args.q_format)
+            if dense:
+                call = idx.bind_dense_masked_logits_topk(
+                    cfg, p["rows"], max_ctx, qv, qs, L.weights, p["kc"][layer], p["sched"].struct,
+                    p["out"], p["out"].stride(0), None, 0, p["ws"], p["ws"].numel(), stream=sh)
+            else:
+                call = idx.bind_sparse_mqa_logits_topk(
+                    cfg, p["rows"], qv, qs, L.weights, p["kc"][layer], p["sched"].struct,
+                    p["out"], p["out"].stride(0), None, p["ws"], p["ws"].numel(), stream=sh)
+            p["layers"].append(call)
+    set_events = idx.lib.idx_set_timing_events
+
+    def launch(p, events=None):
+        p["expand"]()
+        for c, call in enumerate(p["layers"]):
+            if events is not None:
+                set_events(*events[c])
+            call()
+            if events is not None:
+                set_events(None, None)
+
+    for i in range(warmup):
+        launch(plans[i % nrep])
+    torch.cuda.synchronize()
+    if graph:
+        for p in plans:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                launch(p)
+            p["graph"] = g
+        for i in range(warmup):
+            plans[i % nrep]["graph"].replay()
+        torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        p = plans[i % nrep]
+        if graph:
+            p["graph"].replay()
+        else:
+            launch(p)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    # Event pass, after the timed steps and not counted in them: the events ride on the
+    # scoring dispatch itself (hipExtLaunchKernel), which costs the host ~20 us a launch.
+    for i in range(EVENT_STEPS):
+        launch(plans[i % nrep], ev_raw[i * calls_per_step:(i + 1) * calls_per_step])
+    torch.cuda.synchronize()
+    kernel_ms = [a.elapsed_time(b) for a, b in ev]
+    return dict(spec=spec, case=case, cfg=cfg, ends=ends, ctx=ctx, max_ctx=max_ctx, R=R,
+                gen_s=gen_s, kernel_name=kernel_name, fused=fused, launch_layers=launch_layers,
+                layers_call=layers_call, plan=plan, kernel_bytes=kernel_bytes,
+                step_bytes=step_bytes, nrep=nrep, elapsed=elapsed, steps=steps,
+                kernel_ms=kernel_ms)
+
+
+def roofline(m, config: int, q_format: str, peaks: dict, dense: bool) -> dict:
+    """The scoring kernel's roofline object from run_workload's measurements."""
+    spec, kernel_ms = m["spec"], m["kernel_ms"]
+    avg_s = float(np.mean(kernel_ms)) / 1e3
+    cols_per_layer = int(m["ends"].astype(np.int64).sum())
+    scored = int(m["ctx"].sum()) if dense else cols_per_layer
+    launch_bytes = m["kernel_bytes"] * m["launch_layers"]
+    achieved_gbs = launch_bytes / avg_s / 1e9
+    flops = 2 * spec.num_heads * spec.head_dim * scored * m["launch_layers"]
+    step_s = m["elapsed"] / m["steps"]
+    if spec.mode == "prefill":
+        # Prefill chunks share each K tile among many rows (K comes from L2), so the MX-FP4
+        # MFMA rate bounds them; decode rows each stream their own K from HBM.
+        roof = {"bound": "mfma", "achieved": flops / avg_s / 1e12, "peak": MXFP4_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+        # What actually bounds the contraction here: its ReLU-weight epilogue, one integer
+        # max and one fp32 FMA per (head, column) element on the vector ALUs, whose peak is
+        # 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane-operations per second.
+        lane_ops = 2 * spec.num_heads * scored * m["launch_layers"]
+        roof["epilogue_valu"] = {"achieved": lane_ops / avg_s / 1e12, "peak": VALU_PEAK_TLANEOPS,
+                                 "unit": "T lane-ops/s",
+                                 "frac": lane_ops / avg_s / 1e12 / VALU_PEAK_TLANEOPS}
+        roof["step_tflops"] = flops / m["launch_layers"] * spec.layers / step_s / 1e12
+        roof["step_frac"] = roof["step_tflops"] / MXFP4_PEAK_TFLOPS
+    else:
+        roof = {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+        # the whole step (expansion + every layer's launches) against the same peak
+        roof["step_gbs"] = m["step_bytes"] / step_s / 1e9
+        roof["step_frac"] = roof["step_gbs"] / HBM_PEAK_GBS
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["measured_peak"] = peaks["mxfp4_tflops"] if roof["bound"] == "mfma" else peaks["read_gbs"]
+    roof["frac_of_measured"] = roof["achieved"] / roof["measured_peak"]
+    roof.update({"traffic": traffic_for(m["kernel_name"], config, q_format),
+                 "kernel": m["kernel_name"], "avg_launch_us": avg_s * 1e6,
+                 "launch_us_p10": float(np.percentile(kernel_ms, 10)) * 1e3,
+                 "launch_us_p90": float(np.percentile(kernel_ms, 90)) * 1e3,
+                 "timed_launches": len(kernel_ms),
+                 "timing": "dispatch events on the scoring launch, in an event pass after the "
+                           "timed steps",
+                 "algorithmic_bytes_per_launch": launch_bytes, "hbm_gbs": achieved_gbs,
+                 "mxfp4_tflops": flops / avg_s / 1e12})
+    return roof
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2,
-                    help="workload 1-5 (default 2); 6: decode with two rows per request")
+    ap.add_argument("--config", type=int, default=4,
+                    help="workload 1-5 (default 4, the long-context decode batch); 6: decode "
+                         "with two rows per request")
     ap.add_argument("--q-format", default="mxfp4", choices=["mxfp4", "fp8"])
     ap.add_argument("--path", default="sparse", choices=["sparse", "dense", "gather"],
-                    help="sparse: idx_sparse_mqa_logits_topk; dense: the comparator "
+                    help="sparse: the indexer; dense: the comparator "
                          "idx_dense_masked_logits_topk (scores the whole context); gather: "
                          "idx_gather_k_workspace of every table row's context [0, ke)")
     ap.add_argument("--replicas", type=int, default=0, help="input copies (0 = auto)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill chunk's MX-FP4 roofline (reported beside the "
+                         "headline workload's)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--layers", type=int, default=0,
                     help="consuming layers a step (0: the workload's own); each layer gets its "
@@ -261,8 +529,8 @@ def main():
     ap.add_argument("--per-layer-calls", action="store_true",
                     help="one sparse call per layer instead of one multi-layer call")
     ap.add_argument("--graph", action="store_true",
-                    help="replay each step as a captured HIP graph (measured slower than direct "
-                         "launches on this stack: 21.7 vs 14.8 us a decode-batch step)")
+                    help="replay each timed step as a captured HIP graph (measured slower than "
+                         "direct launches on this stack: 21.7 vs 14.8 us a decode-batch step)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB megabytes 5 times (the reference "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -289,234 +557,28 @@ def main():
 
     import sparse_attention_indexer_candidate_amd as idx
     import workloads as W
-    from workloads.device import to_device
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    spec = W.config(args.config)
-    if args.q_format == "fp8" and "fp8" not in spec.q_formats:
-        spec = W.config(args.config, q_formats=("mxfp4", "fp8"))
-    if args.layers > 0 and args.layers != spec.layers:
-        import dataclasses
-
-        spec = dataclasses.replace(spec, layers=args.layers, name=f"{spec.name}_l{args.layers}")
-    t0 = time.time()
-    case = W.generate(spec, args.seed)
-    gen_s = time.time() - t0
-
-    cfg = idx.make_config(spec.num_heads, spec.head_dim,
-                          idx.IDX_Q_MXFP4 if args.q_format == "mxfp4" else idx.IDX_Q_FP8_E4M3_ROWSCALE,
-                          spec.page_size, spec.cbs, 0, spec.nb, spec.topk)
     if args.path == "gather":
-        return bench_gather(args, idx, case, cfg, dev, gen_s)
-    R = case.num_rows
-
-    # Touched bytes per step decide how many copies defeat the Infinity Cache.
-    sched0 = idx.Schedule(cfg, R, dev)
-    base = to_device(case, dev)
-    kc0 = [idx.make_kcache(L.pool, spec.page_size, spec.head_dim, base.block_table)
-           for L in base.layers]
-    rows0 = idx.make_rows(base.row_ke, base.row_ks, base.row_table)
-    idx.idx_expand_candidates(cfg, rows0, kc0[0], base.candidate_blocks,
-                              base.candidate_blocks.stride(0), sched0.struct)
-    torch.cuda.synchronize()
-    ends = sched0.end.cpu().numpy()
-    step_bytes = algorithmic_bytes(case, args.q_format, ends) * spec.layers
-    # The library's choice of scoring kernel: with at least 8 rows per CU (MXFP4
-    # queries, 64-token sparse blocks) 2-row groups share K tiles and select in the same
-    # kernel; with at least one row per CU a workgroup scores and selects one row;
-    # otherwise a split scoring kernel streams K and a second kernel selects.  The dense
-    # comparator scores every context token in its own kernel.
-    cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    ncols = idx.idx_num_sparse_blocks(cfg) * cfg.sparse_block_kv
-    ctx = (case.row_ke - (case.row_ks if case.row_ks is not None else 0)).astype(np.int64)
-    max_ctx = int(case.row_ke.max()) if R else 0
-    if args.path == "dense":
-        kernel_name = "score_dense_kernel"
-    elif args.q_format == "mxfp4" and cfg.sparse_block_kv == 64 and ncols <= 8192 and R >= 8 * cus:
-        kernel_name = "row_group_kernel"
-    elif R >= cus:
-        kernel_name = "fused_row_kernel"
-    else:
-        kernel_name = "score_split_kernel"
-    fused = kernel_name in ("row_group_kernel", "fused_row_kernel")
-    # The step's consuming layers go to the library in one call (one launch when the rows
-    # take the one-row kernel); the timing events then ride on that call's scoring launch.
-    layers_call = args.path != "dense" and spec.layers > 1 and not args.per_layer_calls
-    launch_layers = 1
-    if layers_call and kernel_name == "fused_row_kernel":
-        kernel_name, launch_layers = "fused_layers_kernel", spec.layers
-    elif layers_call and kernel_name == "score_split_kernel":
-        kernel_name, launch_layers = "score_split_layers_kernel", spec.layers
-    elif layers_call and kernel_name == "row_group_kernel":
-        kernel_name, launch_layers = "row_group_layers_kernel", spec.layers
-    events_per_step = 1 if layers_call else spec.layers
-    if args.path == "dense":
-        # every context token's K, the row's query state, the logits row written
-        step_bytes = (algorithmic_bytes(case, args.q_format, ctx, with_output=False)
-                      + R * 4 * max_ctx) * spec.layers
-        kernel_bytes = algorithmic_bytes(case, args.q_format, ctx, with_output=False) + R * 4 * max_ctx
-    else:
-        kernel_bytes = algorithmic_bytes(case, args.q_format, ends, with_output=fused)
-    pool_bytes = sum(L.pool.numel() for L in base.layers)
-    if args.replicas > 0:
-        nrep = args.replicas
-    else:
-        nrep = max(2, math.ceil(1.5e9 / step_bytes))
-        nrep = max(1, min(nrep, int(40e9 // max(pool_bytes, 1))))
-
-    reps = [base]
-    for _ in range(nrep - 1):
-        reps.append(type(base)(
-            row_ks=base.row_ks.clone(), row_ke=base.row_ke.clone(), row_table=base.row_table.clone(),
-            block_table=base.block_table.clone(), candidate_blocks=base.candidate_blocks.clone(),
-            layers=[type(L)(pool=L.pool.clone(), weights=L.weights.clone(),
-                            q_values=None if L.q_values is None else L.q_values.clone(),
-                            q_scales=None if L.q_scales is None else L.q_scales.clone(),
-                            q_fp8=None if L.q_fp8 is None else L.q_fp8.clone(),
-                            q_rowscale=None if L.q_rowscale is None else L.q_rowscale.clone())
-                    for L in base.layers]))
-
-    # a multi-layer call on fewer rows than CUs keeps every layer's logits (one launch
-    # scores them all)
-    ws_rows = R * (spec.layers if kernel_name == "score_split_layers_kernel" else 1)
-    ws_bytes = idx.idx_workspace_bytes(cfg, ws_rows, max_ctx if args.path == "dense" else 0)
-    plans = []
-    for d in reps:
-        plans.append(dict(
-            d=d, rows=idx.make_rows(d.row_ke, d.row_ks, d.row_table),
-            kc=[idx.make_kcache(L.pool, spec.page_size, spec.head_dim, d.block_table) for L in d.layers],
-            sched=idx.Schedule(cfg, R, dev),
-            out=torch.empty((R, spec.topk), dtype=torch.int32, device=dev),
-            out_l=[torch.empty((R, spec.topk), dtype=torch.int32, device=dev)
-                   for _ in range(spec.layers)],
-            ws=torch.empty(ws_bytes, dtype=torch.uint8, device=dev)))
-    # A stream of the bench's own (default priority), current for the rest of the run: the
-    # step graphs are captured on it and replayed on it, and the directly launched steps
-    # that carry the timing events go to it too, so every step stays in order.
+        spec = W.config(args.config)
+        t0 = time.time()
+        case = W.generate(spec, args.seed)
+        cfg = idx.make_config(spec.num_heads, spec.head_dim, idx.IDX_Q_MXFP4, spec.page_size,
+                              spec.cbs, 0, spec.nb, spec.topk)
+        return bench_gather(args, idx, case, cfg, dev, time.time() - t0)
+    # A stream of the bench's own (default priority), current for the rest of the run.
     stream = torch.cuda.Stream()
     torch.cuda.set_stream(stream)
-    sh = stream.cuda_stream
-    # Events ride on the scoring dispatch itself (hipExtLaunchKernel), which costs the
-    # host about 20 us per launch; timing every TIMING_STRIDE-th step keeps the host
-    # ahead of the GPU on short steps.
-    timed_steps = [i for i in range(args.steps) if i % TIMING_STRIDE == 0]
-    n_events = len(timed_steps) * events_per_step
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(n_events)]
-    for a, b in ev:            # materialise the HIP events before the timed region
-        a.record(stream)
-        b.record(stream)
-    torch.cuda.synchronize()
-    ev_raw = [(idx.event_handle(a), idx.event_handle(b)) for a, b in ev]
-
-    # Every launch of a step is bound once (arguments marshalled ahead), as a serving
-    # loop would: a step then costs the host one foreign call per launch, so short
-    # steps are not bound by Python.
-    for p in plans:
-        d = p["d"]
-        p["expand"] = idx.bind_expand_candidates(cfg, p["rows"], p["kc"][0], d.candidate_blocks,
-                                                 d.candidate_blocks.stride(0), p["sched"].struct,
-                                                 stream=sh)
-        p["layers"] = []
-        if layers_call:
-            entries = [(*L.q(args.q_format), L.weights, p["kc"][layer], p["out_l"][layer], None)
-                       for layer, L in enumerate(d.layers)]
-            p["layers"].append(idx.bind_sparse_mqa_logits_topk_layers(
-                cfg, p["rows"], p["sched"].struct, entries, spec.topk, p["ws"], p["ws"].numel(),
-                stream=sh))
-        for layer, L in enumerate([] if layers_call else d.layers):
-            qv, qs = L.q(args.q_format)
-            if args.path == "dense":
-                call = idx.bind_dense_masked_logits_topk(
-                    cfg, p["rows"], max_ctx, qv, qs, L.weights, p["kc"][layer], p["sched"].struct,
-                    p["out"], p["out"].stride(0), None, 0, p["ws"], p["ws"].numel(), stream=sh)
-            else:
-                call = idx.bind_sparse_mqa_logits_topk(
-                    cfg, p["rows"], qv, qs, L.weights, p["kc"][layer], p["sched"].struct,
-                    p["out"], p["out"].stride(0), None, p["ws"], p["ws"].numel(), stream=sh)
-            p["layers"].append(call)
-    set_events = idx.lib.idx_set_timing_events
-
-    def launch(p, i=0, timed=False):
-        p["expand"]()
-        for layer, call in enumerate(p["layers"]):
-            if timed:
-                set_events(*ev_raw[(i // TIMING_STRIDE) * events_per_step + layer])
-            call()
-            if timed:
-                set_events(None, None)
-
-    def step(i, timed):
-        # With --graph the step is one HIP graph replay (one host call for all its
-        # launches); the steps that carry the timing events are launched directly.
-        p = plans[i % nrep]
-        timed = timed and i % TIMING_STRIDE == 0
-        if "graph" in p and not timed:
-            p["graph"].replay()
-        else:
-            launch(p, i, timed)
-
-    for i in range(args.warmup):
-        step(i, False)
-    torch.cuda.synchronize()
-    if args.graph:
-        for p in plans:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                launch(p)
-            p["graph"] = g
-        for i in range(args.warmup):
-            step(i, False)
-        torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, True)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-
-    kernel_ms = [a.elapsed_time(b) for a, b in ev]
-    avg_kernel_s = float(np.mean(kernel_ms)) / 1e3
-    cols_per_step = int(ends.astype(np.int64).sum()) * spec.layers
-    ctx_cols_per_step = int(ctx.sum()) * spec.layers
-    launch_bytes = kernel_bytes * launch_layers
-    achieved = launch_bytes / avg_kernel_s / 1e9
-
-    traffic = None
-    tfile = os.path.join(ROOT, "profiles", f"traffic_{kernel_name}_cfg{args.config}_{args.q_format}.json")
-    if os.path.exists(tfile):
-        with open(tfile) as f:
-            t = json.load(f)
-        if t.get("kernel_source_hash") == kernel_source_hash():
-            traffic = t.get("bytes_per_launch")
-
-    # Prefill chunks share each K tile among many rows (K comes from L2), so the MX-FP4
-    # MFMA rate bounds them; decode rows each stream their own K from HBM.
-    scored = ctx_cols_per_step if args.path == "dense" else cols_per_step
-    flops = 2 * spec.num_heads * spec.head_dim * scored / spec.layers * launch_layers
-    if spec.mode == "prefill":
-        roof = {"bound": "mfma", "achieved": flops / avg_kernel_s / 1e12,
-                "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s"}
-        roof["frac"] = roof["achieved"] / MXFP4_PEAK_TFLOPS
-        # What actually bounds the contraction here: its ReLU-weight epilogue, one integer
-        # max and one fp32 FMA per (head, column) element on the vector ALUs, whose peak is
-        # 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane-operations per second.
-        lane_ops = 2 * spec.num_heads * scored / spec.layers * launch_layers
-        roof["epilogue_valu"] = {"achieved": lane_ops / avg_kernel_s / 1e12,
-                                 "peak": VALU_PEAK_TLANEOPS, "unit": "T lane-ops/s",
-                                 "frac": lane_ops / avg_kernel_s / 1e12 / VALU_PEAK_TLANEOPS}
-    else:
-        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS}
+    dense = args.path == "dense"
+    m = run_workload(idx, W, args.config, args, dev, stream, args.steps, args.warmup,
+                     layers=args.layers, per_layer_calls=args.per_layer_calls, graph=args.graph)
+    spec, R = m["spec"], m["R"]
     peaks = measured_peaks(stream)
-    roof["measured_peak"] = peaks["mxfp4_tflops"] if roof["bound"] == "mfma" else peaks["read_gbs"]
-    roof["frac_of_measured"] = roof["achieved"] / roof["measured_peak"]
-    roof.update({"traffic": traffic, "kernel": kernel_name, "avg_launch_us": avg_kernel_s * 1e6,
-                 "launch_us_p10": float(np.percentile(kernel_ms, 10)) * 1e3,
-                 "launch_us_p90": float(np.percentile(kernel_ms, 90)) * 1e3,
-                 "timed_launches": len(kernel_ms),
-                 "algorithmic_bytes_per_launch": launch_bytes, "hbm_gbs": achieved,
-                 "mxfp4_tflops": flops / avg_kernel_s / 1e12})
+    roof = roofline(m, args.config, args.q_format, peaks, dense)
+    cols_per_step = int(m["ends"].astype(np.int64).sum()) * spec.layers
+    ctx_cols_per_step = int(m["ctx"].sum()) * spec.layers
+    elapsed = m["elapsed"]
     out = {
         "metric": METRIC,
         "value": cols_per_step * args.steps / elapsed,
@@ -536,20 +598,32 @@ def main():
                    "heads": spec.num_heads, "head_dim": spec.head_dim, "page_size": spec.page_size,
                    "valid_cols_per_step": cols_per_step, "q_format": args.q_format,
                    "path": args.path,
-                   "calls": "one call for all layers" if layers_call else "one call per layer",
-                   "launch": (f"HIP graph per step; every {TIMING_STRIDE}th step launched directly "
-                              "with timing events") if args.graph else "direct",
-                   "input_copies": nrep, "seed": args.seed},
+                   "calls": "one call for all layers" if m["layers_call"] else "one call per layer",
+                   "launch": "HIP graph per step" if args.graph else "direct",
+                   "input_copies": m["nrep"], "seed": args.seed},
         "roofline": roof,
         "measured_peaks": peaks,
     }
-    if args.path == "dense":
+    if dense:
         out["context_cols_per_s"] = ctx_cols_per_step * args.steps / elapsed
+    if not args.no_prefill and not dense and args.config != 3 and args.q_format == "mxfp4":
+        # the prefill chunk (4096 rows of one request), whose bound is the MX-FP4 MFMA rate
+        pm = run_workload(idx, W, 3, args, dev, stream, max(args.steps, 20), args.warmup)
+        pr = roofline(pm, 3, args.q_format, peaks, False)
+        pcols = int(pm["ends"].astype(np.int64).sum())
+        out["prefill"] = {"workload": pm["spec"].name, "rows": pm["R"],
+                          "ms_per_step": pm["elapsed"] / pm["steps"] * 1e3,
+                          "cols_per_s": pcols * pm["steps"] / pm["elapsed"],
+                          "rows_per_s": pm["R"] * pm["steps"] / pm["elapsed"],
+                          "steps": pm["steps"], "input_copies": pm["nrep"], "roofline": pr}
+        del pm
     if not args.no_cpu_baseline:
+        case = m["case"]
         out["cpu_baseline"] = cpu_baseline(case, args.q_format, args.cpu_seconds)
+        allowed = host_cpu()["cpus_allowed"]
         out["cpu_baseline_all_cores"] = cpu_baseline(case, args.q_format, args.cpu_seconds,
-                                                     threads=min(16, os.cpu_count() or 1))
-    print(f"# generated inputs in {gen_s:.1f} s; {nrep} input copies", file=sys.stderr)
+                                                     threads=max(1, min(16, allowed)))
+    print(f"# generated inputs in {m['gen_s']:.1f} s; {m['nrep']} input copies", file=sys.stderr)
     print(json.dumps(out), flush=True)
 
 

@@ -113,26 +113,81 @@ typedef struct {
     size_t work_bytes;
 } idx_schedule;
 
-/* Validate a configuration and fill in sparse_block_kv when it is 0: 64 if
- * cbs % 64 == 0, else cbs when cbs is 16 or 32 (the backend's
- * pick_sparse_block_kv, whose body the pages do not show).  Host only. */
+/* Validate a configuration once, before any step, and fill in sparse_block_kv when it
+ * is 0: 64 if cbs % 64 == 0, else cbs when cbs is 16 or 32.  Restates the engine-start
+ * checks of DeepseekV41SparseIndexerMetadataBuilder.__init__ (DeepSeek-V4.1 sparse
+ * indexer backend source page): a two-level model needs candidate_block_size > 0 and
+ * candidate_topk_blocks > 0, the page size must be a multiple of the sparse block size
+ * that pick_sparse_block_kv chooses (its body is not shown; the rule above is this
+ * library's reading), and the top-k must fit the sparse columns
+ * (check_deep_select_layout, body not shown either: 1 <= topk <= NB*cbs here, with the
+ * kernels' limits IDX_MAX_ROW_COLS and IDX_MAX_TOPK).  Like the builder, which raises at
+ * engine start instead of falling back per step, an unsupported configuration is an
+ * error (IDX_EUNSUPPORTED / IDX_EINVAL), never a slower path.  cfg: host struct, read,
+ * and sparse_block_kv written on success.  Host only. */
 int idx_check_config(idx_config *cfg);
 
-/* NSB = NB * (cbs / sbk) sparse blocks per row, or a negative idx_status. Host. */
+/* NSB = NB * (cbs / sbk) sparse blocks a row: the builder's num_sparse_blocks
+ * (candidate_topk_blocks * (candidate_block_size // sparse_block_kv), backend source
+ * page), which sizes the per-row sparse_indices.  Returns NSB, or a negative
+ * idx_status for a bad config.  Host. */
 int32_t idx_num_sparse_blocks(const idx_config *cfg);
 
-/* Bytes of idx_schedule.work for up to max_rows rows.  Host; 0 on a bad config. */
+/* Bytes of idx_schedule.work for up to max_rows rows.  The builder owns the per-row
+ * scratch of the sparse schedule (sparse_indices, end and the column buffers, sized by
+ * its maximum row count at construction, backend source page) so that the layer op
+ * allocates nothing per step; here the caller allocates it once from this size.  Host;
+ * 0 on a bad config or max_rows < 0. */
 size_t idx_schedule_work_bytes(const idx_config *cfg, int32_t max_rows);
 
 /* Bytes of scratch for up to max_rows rows: the sparse path needs
  * max_rows * NB * cbs fp32 logits; the dense comparator max_rows * max_ctx
- * (pass max_ctx = 0 when it is not used).  Host; 0 on a bad config. */
+ * (pass max_ctx = 0 when it is not used).  The pages size the logits scratch the same
+ * way, rows x candidate columns for the sparse kernels (the builder's prefill budget) and
+ * rows x context for the dense indexer (its profiling-run reservation on the
+ * sparse_mqa_indexer page); the caller allocates it once.  Host; 0 on a bad config. */
 size_t idx_workspace_bytes(const idx_config *cfg, int32_t max_rows, int32_t max_ctx);
 
-/* Message of the last failing call on this thread ("" if none).  Host. */
+/* Message of the last failing call on this thread ("" if none): the text the pages'
+ * builder puts in its ValueError / NotImplementedError (engine start) and the layer
+ * its per-step asserts, as a C status (the return value) plus this message.  The
+ * string is thread-local and owned by the library; it stays valid until the thread's
+ * next call.  Host. */
 const char *idx_last_error(void);
 
-/* Optional timing hook for benchmarks.  While set, every idx_sparse_mqa_logits_topk,
+/* Launch plan of a sparse call: which kernels idx_sparse_mqa_logits_topk (num_layers = 1)
+ * or idx_sparse_mqa_logits_topk_layers launches for these sizes on the calling thread's
+ * current device (the choice depends on its CU count).  Not a step of the method (the
+ * pages fix what is computed, not how it is launched); it lets a caller that accounts
+ * for a call's kernels, such as a benchmark, read the choice the launch makes. */
+enum {
+    IDX_PLAN_NONE = 0,             /* no rows or no layers: nothing launched */
+    IDX_PLAN_SPLIT = 1,            /* per layer: split scoring kernel, then a selection kernel */
+    IDX_PLAN_ONE_ROW = 2,          /* per layer: one workgroup scores and selects a row */
+    IDX_PLAN_ROW_GROUP = 3,        /* per layer: 2-row groups share K tiles, score and select */
+    IDX_PLAN_SPLIT_LAYERS = 4,     /* all layers: one split scoring and one selection launch */
+    IDX_PLAN_ONE_ROW_LAYERS = 5,   /* all layers in one launch of one-row workgroups */
+    IDX_PLAN_ROW_GROUP_LAYERS = 6  /* all layers in one launch of row groups */
+};
+typedef struct {
+    int32_t plan;                       /* IDX_PLAN_* */
+    int32_t layers_per_scoring_launch;  /* layers one launch of the scoring kernel covers */
+    int32_t selects_in_scoring_kernel;  /* 1: no logits leave the scoring kernel */
+    const char *scoring_kernel;         /* the kernel that streams K (static string) */
+    const char *selection_kernel;       /* the separate selection kernel, or "" */
+} idx_plan_info;
+
+/* Fills *out for a call on num_rows rows and num_layers layers (1..IDX_MAX_LAYERS).
+ * logits_home: nonzero when every layer's logits have a home for the batched split
+ * launches (each layer's logits_out is set, or the workspace holds num_layers * num_rows *
+ * NB*cbs floats); it matters only with fewer rows than CUs.  Returns IDX_OK or a
+ * negative idx_status (bad config, negative rows, layers out of range, out NULL).  Host;
+ * queries the current device's CU count once. */
+int idx_sparse_plan(const idx_config *cfg, int32_t num_rows, int32_t num_layers,
+                    int32_t logits_home, idx_plan_info *out);
+
+/* Optional timing hook for benchmarks (not a step of the method: the pages publish no
+ * timings).  While set, every idx_sparse_mqa_logits_topk,
  * idx_sparse_mqa_logits_topk_layers, idx_dense_masked_logits_topk and
  * idx_gather_k_workspace call made on this thread launches its scoring kernel (the one
  * that streams the K cache; for the gather, its one kernel) with start_event and
@@ -148,13 +203,28 @@ int idx_set_timing_events(void *start_event, void *stop_event);
  * keep those holding a token of [ks, ke), pad with -1; end = number of valid
  * tokens.  candidate_blocks is int32 [num_rows][cand_stride] (first NB used).
  * Runs once per step; the schedule then serves every consuming layer whose K
- * cache uses the same block table and pool size. */
+ * cache uses the same block table and pool size.  The pages: the first consuming layer
+ * of a step builds the candidate expansion and schedule that all later ones reuse
+ * (backend source page, module docstring and SparseMQARowsMetadata: sparse_indices
+ * [rows, num_sparse_blocks] and end [rows]); each candidate block of cbs tokens splits
+ * into cbs / sparse_block_kv sparse blocks (the builder's num_sparse_blocks).  k: its
+ * block table resolves each listed sparse block's page once per step (stored in the
+ * schedule's work buffer).  Errors: IDX_EINVAL / IDX_EWORKSPACE on the host before any
+ * launch (null pointers, a cand_stride below NB, a work buffer too small). */
 int idx_expand_candidates(const idx_config *cfg, const idx_rows *rows, const idx_kcache *k,
                           const int32_t *candidate_blocks, int64_t cand_stride,
                           const idx_schedule *sched, void *stream);
 
 /* Steps a2-a6 (and a8 with the fp8 format): paged gather, MX-scaled MFMA,
- * ReLU + fp32 weighted head reduce, masking, per-row top-k.
+ * ReLU + fp32 weighted head reduce, masking, per-row top-k.  The consuming layer's call
+ * of SparseMQAIndexer.forward (sparse_mqa_indexer page), which fills the index buffer
+ * with -1 and calls sparse_mqa_logits_paged_decode for the decode rows (one query per
+ * row, row_ks = 0, row_ke = the compressed context length, a block-table row each) and
+ * sparse_mqa_logits_prefill_chunk per prefill chunk (row_ks / row_ke = the chunk's
+ * cu_seqlen_ks / cu_seqlen_ke); and of RocmSparseMQAIndexer.forward
+ * (rocm_paged_mxfp4_indexer page), which scores the same candidate pool straight from the
+ * paged MXFP4 cache with fp32 weights and fp32 logits.  One entry point serves both row
+ * kinds (the backend page's SparseMQARowsMetadata covers both).
  *   q_values: MXFP4 u8 [num_rows][H][D/2]; FP8 u8 [num_rows][H][D]
  *   q_scales: MXFP4 u8 [num_rows][H][D/32]; FP8 float [num_rows] (s_r > 0)
  *   weights:  float [num_rows][H]

@@ -30,7 +30,7 @@ EXPORTED = ("idx_check_config", "idx_num_sparse_blocks", "idx_schedule_work_byte
             "idx_workspace_bytes", "idx_last_error", "idx_set_timing_events",
             "idx_expand_candidates", "idx_sparse_mqa_logits_topk",
             "idx_sparse_mqa_logits_topk_layers", "idx_dense_masked_logits_topk",
-            "idx_gather_k_workspace",
+            "idx_gather_k_workspace", "idx_sparse_plan",
             "idx_measure_read", "idx_measure_mfma", "idx_measure_mfma_flops")
 IDX_MEASURE_WGS = 4096
 IDX_MAX_LAYERS = 8
@@ -71,6 +71,21 @@ class idx_layer(ctypes.Structure):
     _fields_ = [("q_values", ctypes.c_void_p), ("q_scales", ctypes.c_void_p),
                 ("weights", ctypes.c_void_p), ("k", idx_kcache),
                 ("topk_indices", ctypes.c_void_p), ("logits_out", ctypes.c_void_p)]
+
+
+IDX_PLAN_NONE = 0
+IDX_PLAN_SPLIT = 1
+IDX_PLAN_ONE_ROW = 2
+IDX_PLAN_ROW_GROUP = 3
+IDX_PLAN_SPLIT_LAYERS = 4
+IDX_PLAN_ONE_ROW_LAYERS = 5
+IDX_PLAN_ROW_GROUP_LAYERS = 6
+
+
+class idx_plan_info(ctypes.Structure):
+    _fields_ = [("plan", ctypes.c_int32), ("layers_per_scoring_launch", ctypes.c_int32),
+                ("selects_in_scoring_kernel", ctypes.c_int32),
+                ("scoring_kernel", ctypes.c_char_p), ("selection_kernel", ctypes.c_char_p)]
 
 
 def _load():
@@ -116,6 +131,8 @@ def _load():
     L.idx_gather_k_workspace.argtypes = [P(idx_config), P(idx_kcache), i32, vp, vp, i32, i32,
                                          vp, vp, vp]
     L.idx_gather_k_workspace.restype = ctypes.c_int
+    L.idx_sparse_plan.argtypes = [P(idx_config), i32, i32, i32, P(idx_plan_info)]
+    L.idx_sparse_plan.restype = ctypes.c_int
     L.idx_measure_read.argtypes = [vp, sz, vp, vp]
     L.idx_measure_read.restype = ctypes.c_int
     L.idx_measure_mfma.argtypes = [i32, vp, vp]
@@ -169,6 +186,19 @@ def idx_schedule_work_bytes(cfg: idx_config, max_rows: int) -> int:
 
 def idx_workspace_bytes(cfg: idx_config, max_rows: int, max_ctx: int = 0) -> int:
     return lib.idx_workspace_bytes(ctypes.byref(cfg), max_rows, max_ctx)
+
+
+def idx_sparse_plan(cfg: idx_config, num_rows: int, num_layers: int = 1,
+                    logits_home: bool = False) -> dict:
+    """The launch plan the library takes for a sparse call of these sizes on the current
+    device: plan id, scoring / selection kernel names, layers per scoring launch."""
+    info = idx_plan_info()
+    _check(lib.idx_sparse_plan(ctypes.byref(cfg), num_rows, num_layers, int(bool(logits_home)),
+                               ctypes.byref(info)))
+    return dict(plan=info.plan, layers_per_scoring_launch=info.layers_per_scoring_launch,
+                selects_in_scoring_kernel=bool(info.selects_in_scoring_kernel),
+                scoring_kernel=info.scoring_kernel.decode(),
+                selection_kernel=info.selection_kernel.decode())
 
 
 def idx_expand_candidates(cfg, rows, k, candidate_blocks, cand_stride, sched, stream=None):

@@ -9,8 +9,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 namespace {
+
 
 thread_local char g_err[512] = "";
 thread_local idx::Timing g_timing = {nullptr, nullptr};
@@ -194,6 +196,56 @@ size_t idx_workspace_bytes(const idx_config *cfg, int32_t max_rows, int32_t max_
 }
 
 const char *idx_last_error(void) { return g_err; }
+
+int idx_sparse_plan(const idx_config *cfg, int32_t num_rows, int32_t num_layers,
+                    int32_t logits_home, idx_plan_info *out) {
+    int32_t sbk = 0;
+    int rc;
+    if ((rc = check(cfg, &sbk))) return rc;
+    if (!out) return fail(IDX_EINVAL, "out is NULL");
+    if (num_rows < 0) return fail(IDX_EINVAL, "num_rows %d < 0", num_rows);
+    if (num_layers < 1 || num_layers > IDX_MAX_LAYERS)
+        return fail(IDX_EINVAL, "num_layers %d must be in [1, %d]", num_layers, IDX_MAX_LAYERS);
+    const int32_t ncols = cfg->num_candidate_blocks * cfg->candidate_block_size;
+    const idx::Plan p = idx::plan_sparse(cfg->q_format, sbk, ncols, num_rows, num_layers,
+                                         idx::device_cus(), logits_home != 0);
+    static_assert(IDX_PLAN_ROW_GROUP_LAYERS == idx::kPlanRowGroupLayers &&
+                  IDX_PLAN_SPLIT == idx::kPlanSplit, "one numbering of the plans");
+    idx_plan_info info = {p, 1, 0, "", ""};
+    switch (p) {
+    case idx::kPlanNone: break;
+    case idx::kPlanSplit:
+        info.scoring_kernel = "score_split_kernel";
+        info.selection_kernel = "topk_split_kernel";
+        break;
+    case idx::kPlanOneRow:
+        info.scoring_kernel = "fused_row_kernel";
+        info.selects_in_scoring_kernel = 1;
+        break;
+    case idx::kPlanRowGroup:
+        info.scoring_kernel = "row_group_kernel";
+        info.selects_in_scoring_kernel = 1;
+        break;
+    case idx::kPlanSplitLayers:
+        info.scoring_kernel = "score_split_layers_kernel";
+        info.selection_kernel = "topk_split_layers_kernel";
+        info.layers_per_scoring_launch = num_layers;
+        break;
+    case idx::kPlanOneRowLayers:
+        info.scoring_kernel = "fused_layers_kernel";
+        info.selects_in_scoring_kernel = 1;
+        info.layers_per_scoring_launch = num_layers;
+        break;
+    case idx::kPlanRowGroupLayers:
+        info.scoring_kernel = "row_group_layers_kernel";
+        info.selects_in_scoring_kernel = 1;
+        info.layers_per_scoring_launch = num_layers;
+        break;
+    }
+    if (p == idx::kPlanNone) info.layers_per_scoring_launch = 0;
+    *out = info;
+    return ok();
+}
 
 int idx_set_timing_events(void *start_event, void *stop_event) {
     if ((start_event == nullptr) != (stop_event == nullptr))

@@ -62,6 +62,29 @@ struct Timing {
     hipEvent_t start, stop;
 };
 
+// Launch plans of the sparse path (the C ABI's IDX_PLAN_* values).  One rule picks the
+// plan for the launchers below and for idx_sparse_plan, so callers that account for a
+// call's kernels (a benchmark) read the same choice the launch makes.
+enum Plan : int {
+    kPlanNone = 0,            // no rows or no layers: nothing is launched
+    kPlanSplit = 1,           // per layer: score_split_kernel, then topk_split_kernel
+    kPlanOneRow = 2,          // per layer: fused_row_kernel (one workgroup scores and selects a row)
+    kPlanRowGroup = 3,        // per layer: row_group_kernel (2-row groups share K tiles)
+    kPlanSplitLayers = 4,     // all layers: score_split_layers_kernel, then topk_split_layers_kernel
+    kPlanOneRowLayers = 5,    // all layers in one fused_layers_kernel launch
+    kPlanRowGroupLayers = 6,  // all layers in one row_group_layers_kernel launch
+};
+
+// CUs of the calling thread's current device (256 if the query fails).
+int device_cus();
+
+// The plan of a sparse call: q_format, sparse block size, candidate columns a row
+// (NB*cbs), rows, layers, the device's CUs, and whether every layer's logits have a
+// home for a batched split launch (each layer's logits_out, or a workspace of
+// num_layers * num_rows * ncols floats).
+Plan plan_sparse(int q_format, int32_t sbk, int32_t ncols, int32_t num_rows, int32_t num_layers,
+                 int cus, bool logits_home);
+
 hipError_t launch_sparse(int q_format, const Rows &rows, const void *q_values, const void *q_scales,
                          const float *weights, const KCache &k, const Schedule &s, float *logits_out,
                          float *workspace, int32_t topk, int32_t *out, int64_t out_stride,

@@ -1786,7 +1786,7 @@ hipError_t launch_expand(const Rows &rows, const KCache &k, const int32_t *cand,
     return hipGetLastError();
 }
 
-static int device_cus() {
+int device_cus() {
     static int cus[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -1800,6 +1800,19 @@ static int device_cus() {
 }
 
 
+Plan plan_sparse(int q_format, int32_t sbk, int32_t ncols, int32_t num_rows, int32_t num_layers,
+                 int cus, bool logits_home) {
+    if (num_rows <= 0 || num_layers <= 0) return kPlanNone;
+    // At least 8 rows per CU with MXFP4 queries and 64-token sparse blocks: row groups
+    // (K tiles shared across the rows of a table).
+    const bool groups = q_format == 0 && sbk == 64 && ncols <= 8192 && num_rows >= 8 * cus;
+    if (groups) return num_layers >= 2 ? kPlanRowGroupLayers : kPlanRowGroup;
+    if (num_rows >= cus) return num_layers >= 2 ? kPlanOneRowLayers : kPlanOneRow;
+    // fewer rows than CUs: every layer in one split launch pair when each layer's logits
+    // have a home, else layer by layer
+    return num_layers >= 2 && logits_home ? kPlanSplitLayers : kPlanSplit;
+}
+
 template <int QF>
 static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const void *q_scales,
                                   const float *weights, const KCache &k, const Schedule &s,
@@ -1808,10 +1821,10 @@ static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const 
     hipError_t e;
     const int ncols = s.nsb * s.sbk;
     const int ngroups = (ncols + 63) / 64;
+    const Plan plan = plan_sparse(QF, s.sbk, ncols, rows.num_rows, 1, device_cus(), true);
     if constexpr (QF == 0) {
-        // At least 8 rows per CU: row groups (K tiles shared across the rows of a table).
         constexpr int GR = 2;
-        if (s.sbk == 64 && ncols <= 8192 && rows.num_rows >= 8 * device_cus()) {
+        if (plan == kPlanRowGroup) {
             const dim3 grid((rows.num_rows + GR - 1) / GR);
 #define IDX_LAUNCH_GROUP(NC_)                                                                       \
     hipExtLaunchKernelGGL((row_group_kernel<NC_, GR>), grid, dim3(kGroupThreads), 0, stream,        \
@@ -1823,7 +1836,7 @@ static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const 
             return hipGetLastError();
         }
     }
-    if (rows.num_rows >= device_cus()) {
+    if (plan == kPlanOneRow) {
         // MXFP4, one row a CU: 16 waves with 1-group units (measured 10 % faster 4-layer
         // steps than 8 waves with 4-group units: the row's last unit, and so the wait
         // before the selection, is shorter).  MXFP4 with two or more rows a CU: 8 waves
@@ -1928,9 +1941,15 @@ hipError_t launch_sparse_layers(int q_format, const Rows &rows, int32_t num_laye
                                 int64_t out_stride, const Timing &timing, hipStream_t stream) {
     if (rows.num_rows == 0 || num_layers == 0) return hipSuccess;
     const int ncols = s.nsb * s.sbk;
-    const int cus = device_cus();
-    const bool groups = q_format == 0 && s.sbk == 64 && ncols <= 8192 && rows.num_rows >= 8 * cus;
-    if (num_layers >= 2 && groups) {
+    // every layer's logits must have a home for the batched split launches: its
+    // logits_out or its slice of the workspace
+    bool all_out = true;
+    for (int l = 0; l < num_layers; ++l) all_out = all_out && layers.logits_out[l];
+    const size_t need = (size_t)num_layers * rows.num_rows * ncols * sizeof(float);
+    const bool home = all_out || (workspace && workspace_bytes >= need);
+    const Plan plan = plan_sparse(q_format, s.sbk, ncols, rows.num_rows, num_layers, device_cus(),
+                                  home);
+    if (plan == kPlanRowGroupLayers) {
         constexpr int GR = 2;
         const dim3 grid((rows.num_rows + GR - 1) / GR, num_layers);
         if (ncols <= 4096)
@@ -1943,20 +1962,14 @@ hipError_t launch_sparse_layers(int q_format, const Rows &rows, int32_t num_laye
                                   out_stride);
         return hipGetLastError();
     }
-    if (num_layers >= 2 && rows.num_rows < cus) {
-        // every layer's logits must have a home: its logits_out or its workspace slice
-        bool all_out = true;
-        for (int l = 0; l < num_layers; ++l) all_out = all_out && layers.logits_out[l];
-        const size_t need = (size_t)num_layers * rows.num_rows * ncols * sizeof(float);
-        if (all_out || (workspace && workspace_bytes >= need)) {
-            if (q_format == 0)
-                return launch_split_layers<0>(rows, num_layers, layers, k, s, workspace, topk,
-                                              out_stride, timing, stream);
-            return launch_split_layers<1>(rows, num_layers, layers, k, s, workspace, topk,
+    if (plan == kPlanSplitLayers) {
+        if (q_format == 0)
+            return launch_split_layers<0>(rows, num_layers, layers, k, s, workspace, topk,
                                           out_stride, timing, stream);
-        }
+        return launch_split_layers<1>(rows, num_layers, layers, k, s, workspace, topk, out_stride,
+                                      timing, stream);
     }
-    if (num_layers >= 2 && rows.num_rows >= cus && !groups) {
+    if (plan == kPlanOneRowLayers) {
         const dim3 grid(rows.num_rows, num_layers);
 #define IDX_LAUNCH_LAYERS(QF_, NT_, KPT_, U_, WPE_)                                              \
     hipExtLaunchKernelGGL((fused_layers_kernel<QF_, NT_, KPT_, U_, WPE_>), grid, dim3(NT_), 0,    \

@@ -35,7 +35,8 @@ def test_header_is_c99_and_struct_layouts_match_the_binding(tmp_path):
     equal the ctypes mirror's."""
     import subprocess
 
-    structs = ["idx_config", "idx_kcache", "idx_rows", "idx_schedule", "idx_layer"]
+    structs = ["idx_config", "idx_kcache", "idx_rows", "idx_schedule", "idx_layer",
+               "idx_plan_info"]
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "idx.h"', "int main(void) {"]
     for name in structs:
         lines.append(f'    printf("{name} %zu\\n", sizeof({name}));')
@@ -325,3 +326,45 @@ def test_measurement_kernels_reject_bad_arguments_on_the_host():
         idx.idx_measure_mfma(16, None)
     # waves x rounds x 8 chains x 16*16*128 multiply-adds x 2
     assert idx.idx_measure_mfma_flops(3) == idx.IDX_MEASURE_WGS * 4 * 3 * 8 * 16 * 16 * 128 * 2
+
+
+def test_sparse_plan_rule_on_the_host():
+    """The launch plan for each row / layer count (host only: without a GPU the CU count
+    query falls back to 256, the MI355X's).  The rule: MXFP4 queries, 64-token sparse
+    blocks and >= 8 rows per CU take row groups; >= 1 row per CU one workgroup a row;
+    fewer rows split rows over workgroups, all layers in one launch pair only when every
+    layer's logits have a home."""
+    c = idx.make_config()
+    cus = 256
+    want = [
+        (0, 1, False, idx.IDX_PLAN_NONE, ""),
+        (64, 1, False, idx.IDX_PLAN_SPLIT, "score_split_kernel"),
+        (cus - 1, 4, True, idx.IDX_PLAN_SPLIT_LAYERS, "score_split_layers_kernel"),
+        (64, 4, False, idx.IDX_PLAN_SPLIT, "score_split_kernel"),
+        (cus, 1, False, idx.IDX_PLAN_ONE_ROW, "fused_row_kernel"),
+        (cus, 4, False, idx.IDX_PLAN_ONE_ROW_LAYERS, "fused_layers_kernel"),
+        (8 * cus - 1, 1, False, idx.IDX_PLAN_ONE_ROW, "fused_row_kernel"),
+        (8 * cus, 1, False, idx.IDX_PLAN_ROW_GROUP, "row_group_kernel"),
+        (4096, 2, False, idx.IDX_PLAN_ROW_GROUP_LAYERS, "row_group_layers_kernel"),
+    ]
+    for rows, layers, home, plan, kernel in want:
+        p = idx.idx_sparse_plan(c, rows, layers, home)
+        assert (p["plan"], p["scoring_kernel"]) == (plan, kernel), (rows, layers, home, p)
+        fused = plan in (idx.IDX_PLAN_ONE_ROW, idx.IDX_PLAN_ROW_GROUP, idx.IDX_PLAN_ONE_ROW_LAYERS,
+                         idx.IDX_PLAN_ROW_GROUP_LAYERS)
+        assert p["selects_in_scoring_kernel"] == fused
+        assert p["selection_kernel"] == ("" if fused or plan == idx.IDX_PLAN_NONE else
+                                         p["scoring_kernel"].replace("score_", "topk_"))
+        multi = plan in (idx.IDX_PLAN_SPLIT_LAYERS, idx.IDX_PLAN_ONE_ROW_LAYERS,
+                         idx.IDX_PLAN_ROW_GROUP_LAYERS)
+        assert p["layers_per_scoring_launch"] == (0 if plan == idx.IDX_PLAN_NONE else
+                                                  layers if multi else 1)
+    # fp8 queries and 32-token sparse blocks never take row groups
+    c8 = idx.make_config(q_format=idx.IDX_Q_FP8_E4M3_ROWSCALE)
+    assert idx.idx_sparse_plan(c8, 4096)["plan"] == idx.IDX_PLAN_ONE_ROW
+    c32 = idx.make_config(candidate_block_size=32, num_candidate_blocks=64)
+    assert idx.idx_sparse_plan(c32, 4096)["plan"] == idx.IDX_PLAN_ONE_ROW
+    for bad in [(c, -1, 1), (c, 4, 0), (c, 4, idx.IDX_MAX_LAYERS + 1)]:
+        with pytest.raises(idx.IdxError):
+            idx.idx_sparse_plan(*bad)
+
