@@ -241,6 +241,27 @@ int idx_sparse_mqa_logits_topk(const idx_config *cfg, const idx_rows *rows, cons
                                int64_t out_stride, float *logits_out, void *workspace,
                                size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): idx_sparse_mqa_logits_topk without
+ * the workspace argument.  When the call needs a logits scratch (logits_out NULL and
+ * fewer rows than the device's CUs, so rows are split over workgroups and a second
+ * kernel selects: idx_sparse_plan's IDX_PLAN_SPLIT), the logits go to a static scratch
+ * array of IDX_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends; num_rows * NB * cbs * 4 bytes must fit in it (always true for the split
+ * plan on a 256-CU MI355X: at most 255 rows of 8192 columns), else IDX_EWORKSPACE and
+ * nothing is launched.  Every other argument, the results and the errors are those of
+ * idx_sparse_mqa_logits_topk.  The call allocates nothing (no hipMalloc, no allocating
+ * library routine); its first call on a device looks up that device's scratch address.
+ * The scratch keeps the last call's contents, and every logit a call reads it has
+ * written first.  Calls that overlap on one GPU (on different streams, or from several
+ * threads at once) share that GPU's scratch and race: order them on one stream. */
+#define IDX_NOALLOC_SCRATCH_BYTES (8u << 20)
+int idx_sparse_mqa_logits_topk_noalloc(const idx_config *cfg, const idx_rows *rows,
+                                       const void *q_values, const void *q_scales,
+                                       const float *weights, const idx_kcache *k,
+                                       const idx_schedule *sched, int32_t *topk_indices,
+                                       int64_t out_stride, float *logits_out, void *stream);
+
 /* Steps a2-a6 for several consuming layers of one step (the DeepSeek-V4.1 sparse
  * indexer backend source: the per-row schedule scratch that the first consuming
  * layer fills is reused by the later ones, each with its own K cache, query and

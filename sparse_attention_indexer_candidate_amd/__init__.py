@@ -30,10 +30,11 @@ EXPORTED = ("idx_check_config", "idx_num_sparse_blocks", "idx_schedule_work_byte
             "idx_workspace_bytes", "idx_last_error", "idx_set_timing_events",
             "idx_expand_candidates", "idx_sparse_mqa_logits_topk",
             "idx_sparse_mqa_logits_topk_layers", "idx_dense_masked_logits_topk",
-            "idx_gather_k_workspace", "idx_sparse_plan",
+            "idx_gather_k_workspace", "idx_sparse_plan", "idx_sparse_mqa_logits_topk_noalloc",
             "idx_measure_read", "idx_measure_mfma", "idx_measure_mfma_flops")
 IDX_MEASURE_WGS = 4096
 IDX_MAX_LAYERS = 8
+IDX_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 class IdxError(RuntimeError):
@@ -121,6 +122,10 @@ def _load():
                                              P(idx_kcache), P(idx_schedule), vp, i64, vp, vp, sz,
                                              vp]
     L.idx_sparse_mqa_logits_topk.restype = ctypes.c_int
+    L.idx_sparse_mqa_logits_topk_noalloc.argtypes = [P(idx_config), P(idx_rows), vp, vp, vp,
+                                                     P(idx_kcache), P(idx_schedule), vp, i64, vp,
+                                                     vp]
+    L.idx_sparse_mqa_logits_topk_noalloc.restype = ctypes.c_int
     L.idx_sparse_mqa_logits_topk_layers.argtypes = [P(idx_config), P(idx_rows), P(idx_schedule),
                                                     i32, P(idx_layer), i64, vp, sz, vp]
     L.idx_sparse_mqa_logits_topk_layers.restype = ctypes.c_int
@@ -214,6 +219,16 @@ def idx_sparse_mqa_logits_topk(cfg, rows, q_values, q_scales, weights, k, sched,
         ctypes.byref(cfg), ctypes.byref(rows), _p(q_values), _p(q_scales), _p(weights),
         ctypes.byref(k), ctypes.byref(sched), _p(topk_indices), out_stride, _p(logits_out),
         _p(workspace), workspace_bytes, _p(stream)))
+
+
+def idx_sparse_mqa_logits_topk_noalloc(cfg, rows, q_values, q_scales, weights, k, sched,
+                                       topk_indices, out_stride, logits_out=None, stream=None):
+    """idx_sparse_mqa_logits_topk without a workspace: the library's static per-GPU scratch
+    holds the logits when the call needs them kept (allocates nothing)."""
+    return _check(lib.idx_sparse_mqa_logits_topk_noalloc(
+        ctypes.byref(cfg), ctypes.byref(rows), _p(q_values), _p(q_scales), _p(weights),
+        ctypes.byref(k), ctypes.byref(sched), _p(topk_indices), out_stride, _p(logits_out),
+        _p(stream)))
 
 
 def make_layers(layers):

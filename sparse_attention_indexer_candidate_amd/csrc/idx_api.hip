@@ -13,6 +13,18 @@
 
 namespace {
 
+// Scratch of idx_sparse_mqa_logits_topk_noalloc (the split path's logits, fewer rows
+// than CUs), so that entry point needs no workspace and allocates nothing.  Each GPU the
+// library runs on holds its own copy for the life of the process.  Host code never uses
+// this name as an address (on the host it is a stand-in symbol): scratch_device_ptr()
+// looks up each device's copy once with hipGetSymbolAddress and that pointer is what
+// the kernels receive.
+static_assert(IDX_NOALLOC_SCRATCH_BYTES % 256 == 0, "whole 256-byte granules");
+static __device__ __align__(256) uint8_t scratch[IDX_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
 
 thread_local char g_err[512] = "";
 thread_local idx::Timing g_timing = {nullptr, nullptr};
@@ -152,6 +164,28 @@ idx::Schedule to_schedule(const idx_config *cfg, int32_t sbk, const idx_schedule
 
 int hip_status(hipError_t e, const char *what) {
     if (e != hipSuccess) return fail(IDX_EHIP, "%s: %s", what, hipGetErrorString(e));
+    return IDX_OK;
+}
+
+// The current device's copy of `scratch`, looked up on the first call on that device
+// (with that device current) and kept.  Returns IDX_OK and sets *out, or an error.
+int scratch_device_ptr(void **out) {
+    int dev = 0;
+    int rc;
+    if ((rc = hip_status(hipGetDevice(&dev), "hipGetDevice"))) return rc;
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(IDX_EUNSUPPORTED, "device %d: the scratch table holds %d devices", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if ((rc = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)),
+                             "hipGetSymbolAddress(scratch)")))
+            return rc;
+        if (!p) return fail(IDX_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
     return IDX_OK;
 }
 
@@ -306,6 +340,48 @@ int idx_sparse_mqa_logits_topk(const idx_config *cfg, const idx_rows *rows, cons
     if ((rc = hip_status(idx::launch_sparse(cfg->q_format, r, q_values, q_scales, weights, kc, s,
                                             logits_out, (float *)workspace, cfg->topk,
                                             topk_indices, out_stride, g_timing, st),
+                         "sparse launch")))
+        return rc;
+    return ok();
+}
+
+int idx_sparse_mqa_logits_topk_noalloc(const idx_config *cfg, const idx_rows *rows,
+                                       const void *q_values, const void *q_scales,
+                                       const float *weights, const idx_kcache *k,
+                                       const idx_schedule *sched, int32_t *topk_indices,
+                                       int64_t out_stride, float *logits_out, void *stream) {
+    int32_t sbk = 0;
+    int rc;
+    if ((rc = check_filled(cfg, &sbk)) || (rc = check_rows(rows)) || (rc = check_kcache(cfg, k)) ||
+        (rc = check_schedule(cfg, rows, sched)) || (rc = check_q(cfg, q_values, q_scales, weights)))
+        return rc;
+    if (!topk_indices || !aligned(topk_indices, 4))
+        return fail(IDX_EINVAL, "topk_indices must be non-NULL and 4-byte aligned");
+    if (out_stride < cfg->topk)
+        return fail(IDX_EINVAL, "out_stride %lld < topk %d", (long long)out_stride, cfg->topk);
+    if (logits_out && !aligned(logits_out, 16))
+        return fail(IDX_EINVAL, "logits_out must be 16-byte aligned");
+    if (rows->num_rows == 0) return ok();   // nothing to launch, nothing to look up
+    const idx::Schedule s = to_schedule(cfg, sbk, sched);
+    const int32_t ncols = s.nsb * s.sbk;
+    // Only the split plan (fewer rows than CUs) keeps logits outside the scoring kernel;
+    // without logits_out they go to this device's static scratch.
+    float *scratch_logits = nullptr;
+    if (!logits_out && idx::plan_sparse(cfg->q_format, sbk, ncols, rows->num_rows, 1,
+                                        idx::device_cus(), true) == idx::kPlanSplit) {
+        const size_t need = (size_t)rows->num_rows * ncols * sizeof(float);
+        if (need > IDX_NOALLOC_SCRATCH_BYTES)
+            return fail(IDX_EWORKSPACE, "the call needs %zu bytes of logits scratch, more than "
+                        "the %u bytes of static scratch (use idx_sparse_mqa_logits_topk with a "
+                        "workspace)", need, (unsigned)IDX_NOALLOC_SCRATCH_BYTES);
+        void *p = nullptr;
+        if ((rc = scratch_device_ptr(&p))) return rc;
+        scratch_logits = (float *)p;
+    }
+    if ((rc = hip_status(idx::launch_sparse(cfg->q_format, to_rows(rows), q_values, q_scales,
+                                            weights, to_kcache(cfg, k), s, logits_out,
+                                            scratch_logits, cfg->topk, topk_indices, out_stride,
+                                            g_timing, (hipStream_t)stream),
                          "sparse launch")))
         return rc;
     return ok();

@@ -368,3 +368,26 @@ def test_sparse_plan_rule_on_the_host():
         with pytest.raises(idx.IdxError):
             idx.idx_sparse_plan(*bad)
 
+
+def test_noalloc_call_checks_arguments_and_zero_rows_launch_nothing():
+    """idx_sparse_mqa_logits_topk_noalloc applies the same host checks as the workspace
+    form (no workspace argument), and zero rows succeed without touching a device."""
+    c = idx.make_config()
+    rows0 = idx.idx_rows(0, None, FAKE, None)
+    k = idx.idx_kcache(FAKE, 64 * 64, FAKE, 64 * 4, 10, FAKE, 4, 1, 4)
+    nsb = idx.idx_num_sparse_blocks(c)
+    sched = idx.idx_schedule(FAKE, FAKE, FAKE, idx.idx_schedule_work_bytes(c, 4))
+    call = lambda **kw: idx.idx_sparse_mqa_logits_topk_noalloc(
+        c, kw.get("rows", rows0), FAKE, FAKE, FAKE, k, kw.get("sched", sched),
+        kw.get("out", FAKE), kw.get("stride", 2048), kw.get("lout"))
+    assert call() == idx.IDX_OK
+    for kw, code in [(dict(out=None), idx.IDX_EINVAL), (dict(stride=100), idx.IDX_EINVAL),
+                     (dict(lout=FAKE + 4), idx.IDX_EINVAL),
+                     (dict(rows=idx.idx_rows(4, None, None, None)), idx.IDX_EINVAL),
+                     (dict(rows=idx.idx_rows(4, None, FAKE, None),
+                           sched=idx.idx_schedule(FAKE, FAKE, FAKE, 4)), idx.IDX_EWORKSPACE)]:
+        with pytest.raises(idx.IdxError) as e:
+            call(**kw)
+        assert e.value.code == code, kw
+    assert nsb == 64
+    assert idx.IDX_NOALLOC_SCRATCH_BYTES >= 255 * 8192 * 4   # the split plan always fits
