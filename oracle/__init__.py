@@ -23,11 +23,13 @@ _lib = None
 
 Q_MXFP4 = 0
 Q_FP8 = 1
+SCORE_FP32 = 0
+SCORE_BF16 = 1
 
 
 def build() -> str:
     """Compile oracle.c (plain C, -O2, no FP contraction) into liboracle.so."""
-    tmp = _LIB + ".tmp"
+    tmp = f"{_LIB}.tmp{os.getpid()}"   # concurrent builders never share a temporary
     subprocess.check_call(["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fPIC", "-shared",
                            "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
     os.replace(tmp, _LIB)
@@ -44,9 +46,11 @@ def lib():
                 build()
             L = ctypes.CDLL(_LIB)
         d, i, i32p = ctypes.c_double, ctypes.c_int, ctypes.c_void_p
-        for name in ("orc_e2m1", "orc_ue8m0", "orc_e4m3fn"):
+        for name in ("orc_e2m1", "orc_ue8m0", "orc_e4m3fn", "orc_bf16"):
             getattr(L, name).restype = d
             getattr(L, name).argtypes = [i]
+        L.orc_round_bf16.restype = d
+        L.orc_round_bf16.argtypes = [d]
         L.orc_candidate_tokens.restype = ctypes.c_int32
         L.orc_candidate_tokens.argtypes = [i32p, i, i, ctypes.c_int32, ctypes.c_int32, i32p]
         L.orc_expand_row.restype = ctypes.c_int32
@@ -56,8 +60,9 @@ def lib():
         L.orc_select_topk.argtypes = [i32p, i32p, ctypes.c_int32, ctypes.c_int32, i32p]
         p, i64 = ctypes.c_void_p, ctypes.c_int64
         L.orc_indexer_rows.restype = i
-        L.orc_indexer_rows.argtypes = [i, i, i, i, i, i, i, p, p, p, p, p, p, i64, p, i64, p, i64,
-                                       p, p, p, p, i64, p, ctypes.c_int32, p, i64, p, p, i64, p]
+        L.orc_indexer_rows.argtypes = [i, i, i, i, i, i, i, i, p, p, p, p, p, p, i64, p, i64, p,
+                                       i64, p, p, p, p, i64, p, ctypes.c_int32, p, i64, p, p, i64,
+                                       p]
         _lib = L
     return _lib
 
@@ -76,6 +81,15 @@ def ue8m0(b: int) -> float:
 
 def e4m3fn(b: int) -> float:
     return lib().orc_e4m3fn(int(b))
+
+
+def bf16(code: int) -> float:
+    return lib().orc_bf16(int(code))
+
+
+def round_bf16(x: float) -> float:
+    """x rounded to the nearest bf16 value (ties to even), as a float."""
+    return lib().orc_round_bf16(float(x))
 
 
 def candidate_tokens(cand_row, cbs: int, ks: int, ke: int) -> np.ndarray:
@@ -138,9 +152,12 @@ def default_threads() -> int:
 
 
 def indexer_rows(case, layer: int = 0, rows=None, q_format: str = "mxfp4", pool=None,
-                 with_logits: bool = True, threads: int = 1) -> RowResult:
+                 with_logits: bool = True, threads: int = 1,
+                 score_format: str = "fp32") -> RowResult:
     """Run the oracle over the given rows (default: all) of one layer of a case.
 
+    score_format "bf16": the layer's bf16 weights (LayerData.weights_bf16) and logits
+    rounded to bf16 before the selection; "fp32": fp32 weights and logits.
     threads > 1 runs the same single-threaded C call on disjoint chunks of the rows
     at once (the C oracle keeps no state between calls and ctypes releases the GIL);
     each row's arithmetic is unchanged, only rows run side by side."""
@@ -160,7 +177,7 @@ def indexer_rows(case, layer: int = 0, rows=None, q_format: str = "mxfp4", pool=
         chunks = [c for c in np.array_split(rows, nchunk) if c.size]
         with ThreadPoolExecutor(max_workers=threads) as ex:
             parts = list(ex.map(lambda c: indexer_rows(case, layer, c, q_format, pool,
-                                                       with_logits, 1), chunks))
+                                                       with_logits, 1, score_format), chunks))
 
         def cat(f):
             return np.concatenate([getattr(p, f) for p in parts])
@@ -175,15 +192,19 @@ def indexer_rows(case, layer: int = 0, rows=None, q_format: str = "mxfp4", pool=
     lg = np.empty((n, cap), dtype=np.float32) if with_logits else None
     cnt = np.empty(n, dtype=np.int32)
     fmt = Q_MXFP4 if q_format == "mxfp4" else Q_FP8
+    if score_format == "bf16":
+        sfmt, w = SCORE_BF16, np.ascontiguousarray(L.weights_bf16, dtype=np.uint16)
+    else:
+        sfmt, w = SCORE_FP32, np.ascontiguousarray(L.weights, dtype=np.float32)
     cand = np.ascontiguousarray(case.candidate_blocks, dtype=np.int32)
     bt = np.ascontiguousarray(case.block_table, dtype=np.int32)
     lib().orc_indexer_rows(
-        s.num_heads, s.head_dim, s.page_size, s.cbs, s.nb, s.topk, fmt,
+        s.num_heads, s.head_dim, s.page_size, s.cbs, s.nb, s.topk, fmt, sfmt,
         _ptr(L.q_values) if fmt == Q_MXFP4 else None,
         _ptr(L.q_scales) if fmt == Q_MXFP4 else None,
         _ptr(L.q_fp8) if fmt == Q_FP8 else None,
         _ptr(L.q_rowscale) if fmt == Q_FP8 else None,
-        _ptr(np.ascontiguousarray(L.weights, dtype=np.float32)),
+        _ptr(w),
         _ptr(pool), s.page_bytes, pool.ctypes.data + vb, s.page_bytes,
         _ptr(bt), bt.shape[1],
         _ptr(case.row_ks), _ptr(case.row_ke), _ptr(case.row_table),

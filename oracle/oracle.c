@@ -32,6 +32,15 @@
  *    are written in ascending token order and the slots after them hold -1
  *    (SparseMQAIndexer.forward fills the index buffer with -1 before scoring).
  *
+ *  - The bf16 scoring variant, the SM100 layer's semantics: the per-head
+ *    weights are bfloat16 (sparse_mqa_indexer page, SparseMQAIndexer
+ *    weights_dtype) and the top-k runs on the kernels' bf16 logits with no fp32
+ *    fallback (backend source page, DeepseekV41SparseIndexerMetadataBuilder
+ *    __init__, the DeepSelect comment).  Reading: the weights are widened
+ *    exactly, the logit is the same sum, and its exact value is rounded once to
+ *    the nearest bf16 (ties to the even significand) before the selection,
+ *    whose tie rule is unchanged.
+ *
  *  - The sparse-column schedule: each candidate block of cbs tokens becomes
  *    cbs/sbk sparse blocks of sbk tokens; sparse_indices lists the sparse
  *    blocks that hold a token of [ks, ke), ascending, padded with -1; end is
@@ -45,8 +54,9 @@
  * scale bytes [page][D/32] at two independently strided base pointers.
  *
  * Parity pins: every function here is pinned by a CPU test against hand-worked
- * decodes, library decodes (torch float8_e4m3fn / float8_e8m0fnu), closed
- * forms, an independent dense-then-mask brute force and invariants.
+ * decodes and roundings, library decodes and conversions (torch float8_e4m3fn /
+ * float8_e8m0fnu / bfloat16), closed forms, an independent dense-then-mask
+ * brute force and invariants.
  */
 #include <math.h>
 #include <stdint.h>
@@ -55,6 +65,8 @@
 
 #define ORC_Q_MXFP4 0
 #define ORC_Q_FP8 1
+#define ORC_SCORE_FP32 0
+#define ORC_SCORE_BF16 1
 
 /* ---- element and scale decoding (OCP MX v1.0) ------------------------------ */
 
@@ -92,6 +104,50 @@ double orc_e4m3fn(int b)
     else
         mag = ldexp(1.0 + m / 8.0, e - 7);
     return s ? -mag : mag;
+}
+
+/* bf16 (bfloat16): 1 sign bit, 8 exponent bits (bias 127), 7 mantissa bits;
+ * exponent field 0 encodes subnormals m/128 * 2^-126, field 255 infinity (m = 0)
+ * or NaN. */
+double orc_bf16(int code)
+{
+    int s = (code >> 15) & 1;
+    int e = (code >> 7) & 255;
+    int m = code & 127;
+    double mag;
+    if (e == 255)
+        mag = m ? NAN : INFINITY;
+    else if (e == 0)
+        mag = ldexp(m / 128.0, -126);
+    else
+        mag = ldexp(1.0 + m / 128.0, e - 127);
+    return s ? -mag : mag;
+}
+
+/* x rounded to the nearest bf16 value, ties to the even significand.  A bf16
+ * value has 8 significant bits, so in the binade [2^(e-1), 2^e) its spacing is
+ * 2^(e-8); below 2^-126 (subnormals) the spacing stays 2^-133.  A magnitude
+ * that rounds to 2^128 or above is past the largest finite bf16 and becomes
+ * infinity.  Zeros, infinities and NaN pass through. */
+double orc_round_bf16(double x)
+{
+    if (x == 0.0 || isnan(x) || isinf(x))
+        return x;
+    double a = fabs(x);
+    int e;
+    frexp(a, &e);                       /* a in [2^(e-1), 2^e) */
+    int lsb = (e - 1) - 7;              /* exponent of the spacing */
+    if (lsb < -133)
+        lsb = -133;
+    double q = ldexp(a, -lsb);          /* a in units of the spacing (exact) */
+    double fl = floor(q), frac = q - fl;
+    double r = fl;
+    if (frac > 0.5 || (frac == 0.5 && fmod(fl, 2.0) != 0.0))
+        r = fl + 1.0;
+    double v = ldexp(r, lsb);
+    if (v >= ldexp(1.0, 128))
+        v = INFINITY;
+    return x < 0 ? -v : v;
 }
 
 /* Element d of a packed e2m1 vector: element 2i is the low nibble of byte i,
@@ -222,9 +278,9 @@ static void dequant_q(int q_format, int H, int D, const uint8_t *qv, const uint8
         }
 }
 
-/* logit = fp32( sum_h w[h] * relu(dot_h) ), dot_h = s_r * (q_h . k) for FP8 Q. */
-static float row_logit(int H, int D, const double *q, const double *k, const float *w,
-                       int q_format, double rowscale)
+/* sum_h w[h] * relu(dot_h) in fp64, dot_h = s_r * (q_h . k) for FP8 Q. */
+static double row_logit(int H, int D, const double *q, const double *k, const double *w,
+                        int q_format, double rowscale)
 {
     double acc = 0.0;
     for (int h = 0; h < H; h++) {
@@ -234,8 +290,17 @@ static float row_logit(int H, int D, const double *q, const double *k, const flo
         if (q_format == ORC_Q_FP8)
             dot *= rowscale;
         double relu = dot > 0.0 ? dot : 0.0;
-        acc += (double)w[h] * relu;
+        acc += w[h] * relu;
     }
+    return acc;
+}
+
+/* The logit the selection sees: the fp64 sum rounded once, to fp32 (round to
+ * nearest even) or, in the bf16 variant, to the nearest bf16. */
+static float final_logit(double acc, int score_format)
+{
+    if (score_format == ORC_SCORE_BF16)
+        return (float)orc_round_bf16(acc);
     return (float)acc;
 }
 
@@ -289,12 +354,14 @@ int32_t orc_select_topk(const int32_t *tokens, const float *logits, int32_t n, i
  *   out_tokens / out_logits[i*tok_stride ..] T and its logits (optional, may be NULL)
  *   out_count[i] = |T|                        (optional)
  * q_values/q_scales are [R][H][D/2] / [R][H][D/32]; q_fp8 is [R][H][D];
- * q_rowscale [R]; weights [R][H]; candidate_blocks [R][cand_stride].
+ * q_rowscale [R]; weights [R][H], fp32 (score_format ORC_SCORE_FP32) or bf16
+ * codes (ORC_SCORE_BF16); candidate_blocks [R][cand_stride].
  * Returns 0.
  */
 int orc_indexer_rows(int num_heads, int head_dim, int page_size, int cbs, int nb, int topk,
-                     int q_format, const uint8_t *q_values, const uint8_t *q_scales,
-                     const uint8_t *q_fp8, const float *q_rowscale, const float *weights,
+                     int q_format, int score_format, const uint8_t *q_values,
+                     const uint8_t *q_scales, const uint8_t *q_fp8, const float *q_rowscale,
+                     const void *weights,
                      const uint8_t *k_values, int64_t k_values_page_stride,
                      const uint8_t *k_scales, int64_t k_scales_page_stride,
                      const int32_t *block_table, int64_t block_table_stride,
@@ -307,6 +374,7 @@ int orc_indexer_rows(int num_heads, int head_dim, int page_size, int cbs, int nb
     int H = num_heads, D = head_dim;
     double *q = (double *)malloc(sizeof(double) * H * D);
     double *k = (double *)malloc(sizeof(double) * D);
+    double *w = (double *)malloc(sizeof(double) * H);
     int64_t cap = (int64_t)nb * cbs;
     int32_t *tokens = (int32_t *)malloc(sizeof(int32_t) * (cap > 0 ? cap : 1));
     float *logits = (float *)malloc(sizeof(float) * (cap > 0 ? cap : 1));
@@ -321,12 +389,16 @@ int orc_indexer_rows(int num_heads, int head_dim, int page_size, int cbs, int nb
                   q_scales ? q_scales + (int64_t)r * H * (D / 32) : NULL,
                   q_fp8 ? q_fp8 + (int64_t)r * H * D : NULL, q);
         double rs = (q_format == ORC_Q_FP8) ? (double)q_rowscale[r] : 1.0;
+        for (int h = 0; h < H; h++)
+            w[h] = score_format == ORC_SCORE_BF16
+                       ? orc_bf16(((const uint16_t *)weights)[(int64_t)r * H + h])
+                       : (double)((const float *)weights)[(int64_t)r * H + h];
         orc_kview kv = {H, D, page_size, k_values, k_values_page_stride,
                         k_scales, k_scales_page_stride,
                         block_table + (int64_t)tbl * block_table_stride};
         for (int32_t j = 0; j < n; j++) {
             dequant_k(&kv, tokens[j], k);
-            logits[j] = row_logit(H, D, q, k, weights + (int64_t)r * H, q_format, rs);
+            logits[j] = final_logit(row_logit(H, D, q, k, w, q_format, rs), score_format);
         }
         orc_select_topk(tokens, logits, n, topk, out_indices + (int64_t)i * out_stride);
         if (out_tokens)
@@ -338,6 +410,7 @@ int orc_indexer_rows(int num_heads, int head_dim, int page_size, int cbs, int nb
     }
     free(q);
     free(k);
+    free(w);
     free(tokens);
     free(logits);
     return 0;

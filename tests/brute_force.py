@@ -11,6 +11,9 @@ Element decodes come from outside the oracle: e2m1 from the hand-derived table i
 tests/golden/e2m1_codes.txt, UE8M0 and e4m3fn from PyTorch's float8_e8m0fnu and
 float8_e4m3fn conversions.  Tiny inputs only.
 """
+import math
+from fractions import Fraction
+
 import numpy as np
 import torch
 
@@ -52,8 +55,42 @@ def q_matrix(case, layer, r, q_format):
     return _E4M3[L.q_fp8[r]], float(L.q_rowscale[r])
 
 
-def row(case, r, layer=0, q_format="mxfp4", pool=None):
-    """(indices[topk], candidate tokens, their fp32 logits) for row r."""
+def round_bf16_exact(x: float) -> float:
+    """x rounded to the nearest bf16 value in exact rational arithmetic: the two bf16
+    neighbours of |x| at the binade's spacing, the nearer one, a tie to the one with an
+    even significand; at or past 2^128 infinity."""
+    if x == 0.0 or not math.isfinite(x):
+        return x
+    a = Fraction(abs(x))
+    e = 0
+    while Fraction(2) ** e <= a:
+        e += 1
+    while Fraction(2) ** (e - 1) > a:
+        e -= 1
+    spacing = Fraction(2) ** max(e - 8, -133)
+    lo = (a // spacing) * spacing
+    hi = lo + spacing
+    if a - lo < hi - a:
+        v = lo
+    elif hi - a < a - lo:
+        v = hi
+    else:
+        v = lo if (lo / spacing) % 2 == 0 else hi
+    v = math.inf if v >= Fraction(2) ** 128 else float(v)
+    return -v if x < 0 else v
+
+
+def weights(L, r, score_format):
+    """Row r's head weights as fp64: fp32, or the bf16 codes decoded by PyTorch."""
+    if score_format == "bf16":
+        codes = torch.from_numpy(L.weights_bf16[r].view(np.int16).copy())
+        return codes.view(torch.bfloat16).to(torch.float64).numpy()
+    return L.weights[r].astype(np.float64)
+
+
+def row(case, r, layer=0, q_format="mxfp4", pool=None, score_format="fp32"):
+    """(indices[topk], candidate tokens, their logits) for row r (fp32 logits, or
+    bf16-rounded ones held in fp32 with score_format "bf16")."""
     s = case.spec
     L = case.layers[layer]
     if pool is None:
@@ -66,11 +103,14 @@ def row(case, r, layer=0, q_format="mxfp4", pool=None):
     if q_format == "fp8":
         S = S * rs
     relu = np.where(S > 0, S, 0.0)
-    w = L.weights[r].astype(np.float64)
+    w = weights(L, r, score_format)
     acc = np.zeros(ke)
     for h in range(s.num_heads):                 # head sum in index order
         acc = acc + w[h] * relu[h]
-    logits = acc.astype(np.float32)
+    if score_format == "bf16":
+        logits = np.array([round_bf16_exact(float(v)) for v in acc], dtype=np.float32)
+    else:
+        logits = acc.astype(np.float32)
     blocks = set(int(b) for b in case.candidate_blocks[r] if b >= 0)
     t = np.arange(ke)
     keep = (t >= ks) & np.isin(t // s.cbs, np.array(sorted(blocks), dtype=np.int64))

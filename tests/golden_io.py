@@ -27,3 +27,12 @@ def packed_examples():
 
 def scale_fp8_examples():
     return [(c[0], int(c[1], 0), float(c[2])) for c in _rows("ue8m0_e4m3_examples.txt")]
+
+
+def bf16_examples():
+    """(kind, x or code, expected) rows of bf16_round.txt; kind "round" or "decode"."""
+    out = []
+    for c in _rows("bf16_round.txt"):
+        x = int(c[1], 16) if c[0] == "decode" else float(c[1])
+        out.append((c[0], x, float(c[2])))
+    return out

@@ -23,7 +23,7 @@ MUTANTS = {
     "e4m3_bias": ("mag = ldexp(1.0 + m / 8.0, e - 7);", "mag = ldexp(1.0 + m / 8.0, e - 8);"),
     "tie_toward_higher": ("return (x->t > y->t) - (x->t < y->t);", "return (x->t < y->t) - (x->t > y->t);"),
     "scale_block_shift": ("orc_ue8m0(s[d / 32]);", "orc_ue8m0(s[(d / 32 + 1) % (D / 32)]);"),
-    "one_weight_for_all_heads": ("acc += (double)w[h] * relu;", "acc += (double)w[0] * relu;"),
+    "one_weight_for_all_heads": ("acc += w[h] * relu;", "acc += w[0] * relu;"),
     "duplicates_kept": ("if (m == 0 || ids_out[i] != ids_out[m - 1])", "if (1)"),
     "ks_ignored": ("        if (lo < ks)\n            lo = ks;\n        if (hi > ke)\n            hi = ke;\n        for",
                    "        if (hi > ke)\n            hi = ke;\n        for"),
@@ -35,6 +35,16 @@ MUTANTS = {
     "output_unsorted": ("    qsort(out, count, sizeof(int32_t), cmp_i32);\n", ""),
     "last_head_dropped": ("    for (int h = 0; h < H; h++) {\n        double dot", "    for (int h = 0; h < H - (H > 1); h++) {\n        double dot"),
     "expand_end_counts_blocks": ("                valid += (int32_t)(hi - lo);", "                valid += (int32_t)sbk;"),
+    # the bf16 scoring variant
+    "bf16_truncates": ("if (frac > 0.5 || (frac == 0.5 && fmod(fl, 2.0) != 0.0))", "if (0)"),
+    "bf16_ties_away": ("if (frac > 0.5 || (frac == 0.5 && fmod(fl, 2.0) != 0.0))", "if (frac >= 0.5)"),
+    "bf16_rounds_through_fp32": ("return (float)orc_round_bf16(acc);", "return (float)orc_round_bf16((float)acc);"),
+    "bf16_logits_not_rounded": ("return (float)orc_round_bf16(acc);", "return (float)acc;"),
+    "bf16_exponent_bias": ("mag = ldexp(1.0 + m / 128.0, e - 127);", "mag = ldexp(1.0 + m / 128.0, e - 128);"),
+    "bf16_weight_mantissa_dropped": ("orc_bf16(((const uint16_t *)weights)[(int64_t)r * H + h])",
+                                     "orc_bf16(((const uint16_t *)weights)[(int64_t)r * H + h] & 0xFF80)"),
+    "bf16_subnormal_spacing": ("    if (lsb < -133)\n        lsb = -133;", "    if (lsb < -126)\n        lsb = -126;"),
+    "bf16_no_overflow": ("    if (v >= ldexp(1.0, 128))\n        v = INFINITY;\n", ""),
 }
 
 

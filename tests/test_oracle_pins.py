@@ -16,7 +16,7 @@ import torch
 import oracle
 import workloads as W
 from brute_force import row as brute_row
-from golden_io import e2m1_table, packed_examples, scale_fp8_examples
+from golden_io import bf16_examples, e2m1_table, packed_examples, scale_fp8_examples
 
 pytestmark = []
 
@@ -51,6 +51,95 @@ def test_hand_worked_scale_and_fp8_examples():
     for kind, b, v in scale_fp8_examples():
         got = oracle.ue8m0(b) if kind == "ue8m0" else oracle.e4m3fn(b)
         assert got == v and np.signbit(got) == np.signbit(v), (kind, b, got, v)
+
+
+def test_bf16_decode_matches_torch_bfloat16():
+    codes = torch.arange(65536, dtype=torch.int32).to(torch.int16)
+    ref = codes.view(torch.bfloat16).to(torch.float64).numpy()
+    for c in range(65536):
+        got, want = oracle.bf16(c), ref[c]
+        if np.isnan(want):
+            assert np.isnan(got), hex(c)
+        else:
+            assert got == want and np.signbit(got) == np.signbit(want), (hex(c), got, want)
+
+
+def test_bf16_hand_worked_roundings_and_decodes():
+    for kind, x, want in bf16_examples():
+        got = oracle.round_bf16(x) if kind == "round" else oracle.bf16(x)
+        assert got == want and np.signbit(got) == np.signbit(want), (kind, x, got, want)
+
+
+def test_bf16_rounding_matches_torch_on_fp32_values():
+    """For binary32 inputs one rounding to bf16 is PyTorch's float -> bfloat16 conversion
+    (round to nearest even); the bit patterns cover every binade, subnormals and both
+    signs, plus the halfway cases of each (low 16 bits 0x8000)."""
+    rng = np.random.default_rng(7)
+    bits = rng.integers(0, 1 << 32, size=20000, dtype=np.uint64).astype(np.uint32)
+    halfway = (bits & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    bits = np.concatenate([bits, halfway])
+    x = bits.view(np.float32)
+    x = x[np.isfinite(x)]
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).to(torch.float64).numpy()
+    for xi, want in zip(x, ref):
+        got = oracle.round_bf16(float(xi))
+        assert got == want and np.signbit(got) == np.signbit(want), (float(xi), got, want)
+
+
+def test_bf16_scoring_closed_form_ties_after_rounding():
+    # One head, weight 1 (bf16 0x3F80), Q scales 2^0.  Q: element 0 = 4.0 (code 6), block
+    # 1 all 1.0 (code 2).  K of token t: element 0 = 4.0 with block scale 2^6 (4 * 4 * 64
+    # = 1024), the first t elements of block 1 = 1.0 with block scale 2^2 (+ 4t):
+    # dot_t = 1024 + 4t.  fp32 logits are all distinct: top-4 = {12, 13, 14, 15}.  In bf16
+    # the spacing is 8 on [1024, 2048), so 1024 + 4t rounds to (by hand, ties to even):
+    want_bf16 = [1024, 1032, 1032, 1040, 1040, 1040, 1048, 1056,
+                 1056, 1056, 1064, 1072, 1072, 1072, 1080, 1088]
+    # except token 1, which also gets 2^-14 from block 2 (Q 1.0 against K 0.5 * 2^-13):
+    # its exact logit 1028 + 2^-14 lies just above the bf16 tie 1028 and rounds to 1032,
+    # while its fp32 logit is 1028 (2^-14 is half of fp32's spacing there, a tie to the
+    # even 1028), which a second rounding would send to 1024.
+    # top-4 in bf16: 1088 (t=15), 1080 (14), then the three-way tie at 1072 (11, 12, 13)
+    # gives the two lower tokens 11 and 12.
+    case = _one_row_case(H=1, D=128, topk=4)
+    L = case.layers[0]
+    L.weights[:] = 1.0
+    qv = np.zeros(64, np.uint8)
+    qv[0] = 0x06
+    qv[16:32] = 0x22
+    qv[32] = 0x02                                        # element 64 (block 2): 1.0
+    L.q_values[0, 0] = qv
+    for t in range(16):
+        kv = np.zeros(64, np.uint8)
+        kv[0] = 0x06
+        for d in range(32, 32 + t):
+            kv[d // 2] |= 0x2 << (4 * (d & 1))
+        if t == 1:
+            kv[32] = 0x01                                # element 64: 0.5, block scale 2^-13
+        _set_k(case, t, kv, np.array([127 + 6, 127 + 2, 127 - 13, 127], np.uint8))
+    res = oracle.indexer_rows(case)
+    np.testing.assert_array_equal(res.row_logits(0), 1024.0 + 4.0 * np.arange(16))
+    np.testing.assert_array_equal(res.indices[0], [12, 13, 14, 15])
+    resb = oracle.indexer_rows(case, score_format="bf16")
+    np.testing.assert_array_equal(resb.row_logits(0), np.array(want_bf16, np.float32))
+    np.testing.assert_array_equal(resb.indices[0], [11, 12, 14, 15])
+
+
+@pytest.mark.parametrize("chunk", range(4))
+def test_bf16_scoring_matches_brute_force(chunk):
+    """bf16 weights and bf16-rounded logits: the oracle against the dense-then-mask brute
+    force, whose rounding is exact rational arithmetic and whose weight decode is
+    PyTorch's."""
+    for i in range(chunk * 25, chunk * 25 + 25):
+        rng = np.random.default_rng(5000 + i)
+        spec = _tiny_spec(rng, i)
+        case = W.generate(spec, seed=100 + i)
+        pool = case.layers[0].host_pool(spec.page_bytes)
+        res = oracle.indexer_rows(case, pool=pool, score_format="bf16")
+        for r in range(case.num_rows):
+            idx, toks, lg = brute_row(case, r, pool=pool, score_format="bf16")
+            np.testing.assert_array_equal(res.row_tokens(r), toks, err_msg=f"case {i} row {r}")
+            np.testing.assert_array_equal(res.row_logits(r), lg, err_msg=f"case {i} row {r}")
+            np.testing.assert_array_equal(res.indices[r], idx, err_msg=f"case {i} row {r}")
 
 
 # ------------------------------------------------------ hand-built cases ----

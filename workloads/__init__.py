@@ -154,6 +154,15 @@ class LayerData:
     q_fp8: np.ndarray | None = None           # uint8 [R, H, D]    (e4m3fn codes)
     q_rowscale: np.ndarray | None = None      # float32 [R]
 
+    @property
+    def weights_bf16(self) -> np.ndarray:
+        """The weights as bf16 codes (uint16 [R, H]): each fp32 weight rounded to the
+        nearest bf16, ties to even (the producer's encoding of the bf16-weights variant;
+        the weights are finite)."""
+        u = np.ascontiguousarray(self.weights, dtype=np.float32).view(np.uint32)
+        return ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+                >> np.uint32(16)).astype(np.uint16)
+
     def host_pool(self, page_bytes: int) -> np.ndarray:
         """The whole page pool as one [num_pages, page_bytes] uint8 array.
 
