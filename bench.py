@@ -48,17 +48,19 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(case, q_format: str, ends: np.ndarray, with_output: bool = True) -> int:
+def algorithmic_bytes(case, q_format: str, ends: np.ndarray, with_output: bool = True,
+                      score_format: str = "fp32") -> int:
     """Bytes the scoring of one layer must move: 68 B of K per valid column (64 B
     e2m1 + 4 B UE8M0), and per row its query (4352 B MXFP4 / 8196 B fp8 with its
-    row scale), its 64 fp32 weights, ~12 B per candidate block (candidate id,
-    schedule entry, block-table entry) and, when the same kernel selects, the
-    4-byte top-k output slots."""
+    row scale), its 64 weights (fp32, or bf16 in the bf16 scoring format), ~12 B per
+    candidate block (candidate id, schedule entry, block-table entry) and, when the same
+    kernel selects, the 4-byte top-k output slots."""
     s = case.spec
     per_col = s.head_dim // 2 + s.head_dim // 32
     q = s.num_heads * (s.head_dim // 2 + s.head_dim // 32) if q_format == "mxfp4" \
         else s.num_heads * s.head_dim + 4
-    per_row = q + 4 * s.num_heads + 12 * s.nb + (4 * s.topk if with_output else 0)
+    wbytes = 2 if score_format == "bf16" else 4
+    per_row = q + wbytes * s.num_heads + 12 * s.nb + (4 * s.topk if with_output else 0)
     return int(ends.astype(np.int64).sum()) * per_col + case.num_rows * per_row
 
 
@@ -309,8 +311,10 @@ def run_workload(idx, W, config: int, args, dev, stream, steps: int, warmup: int
     gen_s = time.time() - t0
     cfg = idx.make_config(spec.num_heads, spec.head_dim,
                           idx.IDX_Q_MXFP4 if args.q_format == "mxfp4" else idx.IDX_Q_FP8_E4M3_ROWSCALE,
-                          spec.page_size, spec.cbs, 0, spec.nb, spec.topk)
+                          spec.page_size, spec.cbs, 0, spec.nb, spec.topk,
+                          idx.IDX_SCORE_BF16 if args.score_format == "bf16" else idx.IDX_SCORE_FP32)
     R = case.num_rows
+    sfmt = args.score_format
 
     # Touched bytes per step decide how many copies defeat the Infinity Cache.
     sched0 = idx.Schedule(cfg, R, dev)
@@ -340,11 +344,13 @@ def run_workload(idx, W, config: int, args, dev, stream, steps: int, warmup: int
     calls_per_step = 1 if layers_call else spec.layers
     if dense:
         # every context token's K, the row's query state, the logits row written
-        kernel_bytes = algorithmic_bytes(case, args.q_format, ctx, with_output=False) + R * 4 * max_ctx
+        kernel_bytes = algorithmic_bytes(case, args.q_format, ctx, with_output=False,
+                                         score_format=sfmt) + R * 4 * max_ctx
         step_bytes = (kernel_bytes + R * 4 * spec.topk) * spec.layers
     else:
-        kernel_bytes = algorithmic_bytes(case, args.q_format, ends, with_output=fused)
-        step_bytes = algorithmic_bytes(case, args.q_format, ends) * spec.layers
+        kernel_bytes = algorithmic_bytes(case, args.q_format, ends, with_output=fused,
+                                         score_format=sfmt)
+        step_bytes = algorithmic_bytes(case, args.q_format, ends, score_format=sfmt) * spec.layers
     pool_bytes = sum(L.pool.numel() for L in base.layers)
     if args.replicas > 0:
         nrep = args.replicas
@@ -358,6 +364,7 @@ def run_workload(idx, W, config: int, args, dev, stream, steps: int, warmup: int
             row_ks=base.row_ks.clone(), row_ke=base.row_ke.clone(), row_table=base.row_table.clone(),
             block_table=base.block_table.clone(), candidate_blocks=base.candidate_blocks.clone(),
             layers=[type(L)(pool=L.pool.clone(), weights=L.weights.clone(),
+                            weights_bf16=L.weights_bf16.clone(),
                             q_values=None if L.q_values is None else L.q_values.clone(),
                             q_scales=None if L.q_scales is None else L.q_scales.clone(),
                             q_fp8=None if L.q_fp8 is None else L.q_fp8.clone(),
@@ -398,7 +405,7 @@ def run_workload(idx, W, config: int, args, dev, stream, steps: int, warmup: int
                                                  stream=sh)
         p["layers"] = []
         if layers_call:
-            entries = [(*L.q(args.q_format), L.weights, p["kc"][layer], p["out_l"][layer], None)
+            entries = [(*L.q(args.q_format), L.w(sfmt), p["kc"][layer], p["out_l"][layer], None)
                        for layer, L in enumerate(d.layers)]
             p["layers"].append(idx.bind_sparse_mqa_logits_topk_layers(
                 cfg, p["rows"], p["sched"].struct, entries, spec.topk, p["ws"], p["ws"].numel(),
@@ -407,11 +414,11 @@ def run_workload(idx, W, config: int, args, dev, stream, steps: int, warmup: int
             qv, qs = L.q(args.q_format)
             if dense:
                 call = idx.bind_dense_masked_logits_topk(
-                    cfg, p["rows"], max_ctx, qv, qs, L.weights, p["kc"][layer], p["sched"].struct,
+                    cfg, p["rows"], max_ctx, qv, qs, L.w(sfmt), p["kc"][layer], p["sched"].struct,
                     p["out"], p["out"].stride(0), None, 0, p["ws"], p["ws"].numel(), stream=sh)
             else:
                 call = idx.bind_sparse_mqa_logits_topk(
-                    cfg, p["rows"], qv, qs, L.weights, p["kc"][layer], p["sched"].struct,
+                    cfg, p["rows"], qv, qs, L.w(sfmt), p["kc"][layer], p["sched"].struct,
                     p["out"], p["out"].stride(0), None, p["ws"], p["ws"].numel(), stream=sh)
             p["layers"].append(call)
     set_events = idx.lib.idx_set_timing_events
@@ -512,6 +519,9 @@ def main():
                     help="workload 1-5 (default 4, the long-context decode batch); 6: decode "
                          "with two rows per request")
     ap.add_argument("--q-format", default="mxfp4", choices=["mxfp4", "fp8"])
+    ap.add_argument("--score-format", default="fp32", choices=["fp32", "bf16"],
+                    help="fp32 weights and logits (default), or bf16 weights with bf16-rounded "
+                         "logits")
     ap.add_argument("--path", default="sparse", choices=["sparse", "dense", "gather"],
                     help="sparse: the indexer; dense: the comparator "
                          "idx_dense_masked_logits_topk (scores the whole context); gather: "
@@ -597,6 +607,7 @@ def main():
                    "candidate_block_size": spec.cbs, "topk": spec.topk, "layers": spec.layers,
                    "heads": spec.num_heads, "head_dim": spec.head_dim, "page_size": spec.page_size,
                    "valid_cols_per_step": cols_per_step, "q_format": args.q_format,
+                   "score_format": args.score_format,
                    "path": args.path,
                    "calls": "one call for all layers" if m["layers_call"] else "one call per layer",
                    "launch": "HIP graph per step" if args.graph else "direct",

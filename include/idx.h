@@ -55,6 +55,17 @@ typedef enum {
  * name the fp8 x fp4 kernel variant on the backend source page). */
 enum { IDX_Q_MXFP4 = 0, IDX_Q_FP8_E4M3_ROWSCALE = 1 };
 
+/* Scoring formats.  FP32: fp32 head weights and fp32 logits, the gfx950 layer's
+ * (rocm_paged_mxfp4_indexer page, RocmSparseMQAIndexer.weights_dtype: the head reduce
+ * costs the same in either dtype there, so weights and logits stay fp32).  BF16: the
+ * SM100 layer's semantics (sparse_mqa_indexer page, SparseMQAIndexer.weights_dtype =
+ * bfloat16; backend source page, DeepseekV41SparseIndexerMetadataBuilder.__init__: the
+ * top-k runs on the kernels' bf16 logits with no fp32 fallback): bf16 head weights
+ * (codes, widened exactly) and every logit rounded to the nearest bf16 (ties to even)
+ * before the selection, whose rule is unchanged (ties toward the lower token).  Use it
+ * where indices must match that path; with 8 significant bits ties are common. */
+enum { IDX_SCORE_FP32 = 0, IDX_SCORE_BF16 = 1 };
+
 /* Per-model configuration, checked once (the backend builder's engine-start
  * checks on the sparse indexer backend page).  Host struct. */
 typedef struct {
@@ -66,6 +77,7 @@ typedef struct {
     int32_t sparse_block_kv;       /* sbk: tokens per sparse block; 0 = choose (filled in) */
     int32_t num_candidate_blocks;  /* NB: candidate ids per row, > 0 */
     int32_t topk;                  /* 1 <= topk <= NB * cbs, and <= IDX_MAX_TOPK */
+    int32_t score_format;          /* IDX_SCORE_* */
 } idx_config;
 
 /* Kernel limits (sizes of the on-chip top-k working set). */
@@ -227,7 +239,8 @@ int idx_expand_candidates(const idx_config *cfg, const idx_rows *rows, const idx
  * kinds (the backend page's SparseMQARowsMetadata covers both).
  *   q_values: MXFP4 u8 [num_rows][H][D/2]; FP8 u8 [num_rows][H][D]
  *   q_scales: MXFP4 u8 [num_rows][H][D/32]; FP8 float [num_rows] (s_r > 0)
- *   weights:  float [num_rows][H]
+ *   weights:  IDX_SCORE_FP32: float [num_rows][H], 4-byte aligned;
+ *             IDX_SCORE_BF16: bf16 codes uint16 [num_rows][H], 8-byte aligned
  *   topk_indices: int32 rows of out_stride elements; slots [0, topk) written
  *   logits_out: NULL, or float [num_rows][NB*cbs]: the logit of sparse column c
  *     (token sparse_indices[c / sbk] * sbk + c % sbk), -inf where invalid
@@ -236,7 +249,7 @@ int idx_expand_candidates(const idx_config *cfg, const idx_rows *rows, const idx
  * Serves decode rows and a prefill chunk alike; the schedule must come from
  * idx_expand_candidates on the same rows. */
 int idx_sparse_mqa_logits_topk(const idx_config *cfg, const idx_rows *rows, const void *q_values,
-                               const void *q_scales, const float *weights, const idx_kcache *k,
+                               const void *q_scales, const void *weights, const idx_kcache *k,
                                const idx_schedule *sched, int32_t *topk_indices,
                                int64_t out_stride, float *logits_out, void *workspace,
                                size_t workspace_bytes, void *stream);
@@ -258,7 +271,7 @@ int idx_sparse_mqa_logits_topk(const idx_config *cfg, const idx_rows *rows, cons
 #define IDX_NOALLOC_SCRATCH_BYTES (8u << 20)
 int idx_sparse_mqa_logits_topk_noalloc(const idx_config *cfg, const idx_rows *rows,
                                        const void *q_values, const void *q_scales,
-                                       const float *weights, const idx_kcache *k,
+                                       const void *weights, const idx_kcache *k,
                                        const idx_schedule *sched, int32_t *topk_indices,
                                        int64_t out_stride, float *logits_out, void *stream);
 
@@ -286,7 +299,7 @@ int idx_sparse_mqa_logits_topk_noalloc(const idx_config *cfg, const idx_rows *ro
 typedef struct {
     const void *q_values;          /* as in idx_sparse_mqa_logits_topk */
     const void *q_scales;
-    const float *weights;
+    const void *weights;
     idx_kcache k;                  /* this layer's pool */
     int32_t *topk_indices;         /* int32 rows of out_stride elements */
     float *logits_out;             /* NULL or float [num_rows][NB*cbs] */
@@ -308,7 +321,7 @@ int idx_sparse_mqa_logits_topk_layers(const idx_config *cfg, const idx_rows *row
  *     bytes when logits_out is NULL.  max_ctx bounds every ke. */
 int idx_dense_masked_logits_topk(const idx_config *cfg, const idx_rows *rows, int32_t max_ctx,
                                  const void *q_values, const void *q_scales,
-                                 const float *weights, const idx_kcache *k,
+                                 const void *weights, const idx_kcache *k,
                                  const idx_schedule *sched, int32_t *topk_indices,
                                  int64_t out_stride, float *logits_out, int64_t logits_stride,
                                  void *workspace, size_t workspace_bytes, void *stream);

@@ -61,8 +61,8 @@ def lib():
         p, i64 = ctypes.c_void_p, ctypes.c_int64
         L.orc_indexer_rows.restype = i
         L.orc_indexer_rows.argtypes = [i, i, i, i, i, i, i, i, p, p, p, p, p, p, i64, p, i64, p,
-                                       i64, p, p, p, p, i64, p, ctypes.c_int32, p, i64, p, p, i64,
-                                       p]
+                                       i64, p, p, p, p, i64, p, ctypes.c_int32, p, i64, p, p, p,
+                                       i64, p]
         _lib = L
     return _lib
 
@@ -132,18 +132,22 @@ def select_topk(tokens, logits, topk: int) -> np.ndarray:
 class RowResult:
     """Oracle output for a list of rows."""
 
-    def __init__(self, rows, indices, tokens, logits, count):
+    def __init__(self, rows, indices, tokens, logits, count, exact=None):
         self.rows = rows          # int32 [n]
         self.indices = indices    # int32 [n, topk]
         self.tokens = tokens      # int32 [n, cap] (first count[i] valid)
         self.logits = logits      # float32 [n, cap]
         self.count = count        # int32 [n]
+        self.exact = exact        # float64 [n, cap]: the sums before the final rounding
 
     def row_tokens(self, i):
         return self.tokens[i, :self.count[i]]
 
     def row_logits(self, i):
         return self.logits[i, :self.count[i]]
+
+    def row_exact(self, i):
+        return self.exact[i, :self.count[i]]
 
 
 def default_threads() -> int:
@@ -183,13 +187,15 @@ def indexer_rows(case, layer: int = 0, rows=None, q_format: str = "mxfp4", pool=
             return np.concatenate([getattr(p, f) for p in parts])
 
         return RowResult(rows, cat("indices"), cat("tokens") if with_logits else None,
-                         cat("logits") if with_logits else None, cat("count"))
+                         cat("logits") if with_logits else None, cat("count"),
+                         cat("exact") if with_logits else None)
     vb = s.values_bytes
     n = rows.size
     cap = max(1, s.nb * s.cbs)
     idx = np.empty((n, s.topk), dtype=np.int32)
     toks = np.empty((n, cap), dtype=np.int32) if with_logits else None
     lg = np.empty((n, cap), dtype=np.float32) if with_logits else None
+    ex = np.empty((n, cap), dtype=np.float64) if with_logits else None
     cnt = np.empty(n, dtype=np.int32)
     fmt = Q_MXFP4 if q_format == "mxfp4" else Q_FP8
     if score_format == "bf16":
@@ -209,8 +215,8 @@ def indexer_rows(case, layer: int = 0, rows=None, q_format: str = "mxfp4", pool=
         _ptr(bt), bt.shape[1],
         _ptr(case.row_ks), _ptr(case.row_ke), _ptr(case.row_table),
         _ptr(cand), cand.shape[1], _ptr(rows), n,
-        _ptr(idx), s.topk, _ptr(toks), _ptr(lg), cap, _ptr(cnt))
-    return RowResult(rows, idx, toks, lg, cnt)
+        _ptr(idx), s.topk, _ptr(toks), _ptr(lg), _ptr(ex), cap, _ptr(cnt))
+    return RowResult(rows, idx, toks, lg, cnt, ex)
 
 
 def gather_k_workspace(pool, page_size: int, head_dim: int, block_table, cu_seq_lens,

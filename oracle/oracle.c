@@ -352,6 +352,8 @@ int32_t orc_select_topk(const int32_t *tokens, const float *logits, int32_t n, i
  * Outputs for selected row i:
  *   out_indices[i*out_stride + 0 .. topk)    chosen tokens then -1
  *   out_tokens / out_logits[i*tok_stride ..] T and its logits (optional, may be NULL)
+ *   out_exact[i*tok_stride ..]               the fp64 sums before the final rounding
+ *                                            (optional, may be NULL)
  *   out_count[i] = |T|                        (optional)
  * q_values/q_scales are [R][H][D/2] / [R][H][D/32]; q_fp8 is [R][H][D];
  * q_rowscale [R]; weights [R][H], fp32 (score_format ORC_SCORE_FP32) or bf16
@@ -368,8 +370,8 @@ int orc_indexer_rows(int num_heads, int head_dim, int page_size, int cbs, int nb
                      const int32_t *row_ks, const int32_t *row_ke, const int32_t *row_table,
                      const int32_t *candidate_blocks, int64_t cand_stride, const int32_t *rows,
                      int32_t n_sel, int32_t *out_indices, int64_t out_stride,
-                     int32_t *out_tokens, float *out_logits, int64_t tok_stride,
-                     int32_t *out_count)
+                     int32_t *out_tokens, float *out_logits, double *out_exact,
+                     int64_t tok_stride, int32_t *out_count)
 {
     int H = num_heads, D = head_dim;
     double *q = (double *)malloc(sizeof(double) * H * D);
@@ -378,6 +380,7 @@ int orc_indexer_rows(int num_heads, int head_dim, int page_size, int cbs, int nb
     int64_t cap = (int64_t)nb * cbs;
     int32_t *tokens = (int32_t *)malloc(sizeof(int32_t) * (cap > 0 ? cap : 1));
     float *logits = (float *)malloc(sizeof(float) * (cap > 0 ? cap : 1));
+    double *exact = (double *)malloc(sizeof(double) * (cap > 0 ? cap : 1));
     for (int32_t i = 0; i < n_sel; i++) {
         int32_t r = rows[i];
         int32_t ks = row_ks ? row_ks[r] : 0, ke = row_ke[r];
@@ -398,13 +401,16 @@ int orc_indexer_rows(int num_heads, int head_dim, int page_size, int cbs, int nb
                         block_table + (int64_t)tbl * block_table_stride};
         for (int32_t j = 0; j < n; j++) {
             dequant_k(&kv, tokens[j], k);
-            logits[j] = final_logit(row_logit(H, D, q, k, w, q_format, rs), score_format);
+            exact[j] = row_logit(H, D, q, k, w, q_format, rs);
+            logits[j] = final_logit(exact[j], score_format);
         }
         orc_select_topk(tokens, logits, n, topk, out_indices + (int64_t)i * out_stride);
         if (out_tokens)
             memcpy(out_tokens + (int64_t)i * tok_stride, tokens, sizeof(int32_t) * n);
         if (out_logits)
             memcpy(out_logits + (int64_t)i * tok_stride, logits, sizeof(float) * n);
+        if (out_exact)
+            memcpy(out_exact + (int64_t)i * tok_stride, exact, sizeof(double) * n);
         if (out_count)
             out_count[i] = n;
     }
@@ -413,5 +419,6 @@ int orc_indexer_rows(int num_heads, int head_dim, int page_size, int cbs, int nb
     free(w);
     free(tokens);
     free(logits);
+    free(exact);
     return 0;
 }

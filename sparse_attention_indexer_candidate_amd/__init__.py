@@ -22,6 +22,8 @@ IDX_EWORKSPACE = -3
 IDX_EHIP = -4
 IDX_Q_MXFP4 = 0
 IDX_Q_FP8_E4M3_ROWSCALE = 1
+IDX_SCORE_FP32 = 0
+IDX_SCORE_BF16 = 1
 IDX_MAX_ROW_COLS = 8192
 IDX_MAX_DENSE_COLS = 65536
 IDX_MAX_TOPK = 8192
@@ -47,7 +49,8 @@ class idx_config(ctypes.Structure):
     _fields_ = [("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("q_format", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("candidate_block_size", ctypes.c_int32), ("sparse_block_kv", ctypes.c_int32),
-                ("num_candidate_blocks", ctypes.c_int32), ("topk", ctypes.c_int32)]
+                ("num_candidate_blocks", ctypes.c_int32), ("topk", ctypes.c_int32),
+                ("score_format", ctypes.c_int32)]
 
 
 class idx_kcache(ctypes.Structure):
@@ -396,10 +399,10 @@ def _p(x):
 
 def make_config(num_heads=64, head_dim=128, q_format=IDX_Q_MXFP4, page_size=64,
                 candidate_block_size=64, sparse_block_kv=0, num_candidate_blocks=64,
-                topk=2048) -> idx_config:
+                topk=2048, score_format=IDX_SCORE_FP32) -> idx_config:
     return idx_check_config(idx_config(num_heads, head_dim, q_format, page_size,
                                        candidate_block_size, sparse_block_kv,
-                                       num_candidate_blocks, topk))
+                                       num_candidate_blocks, topk, score_format))
 
 
 def make_kcache(pool, page_size, head_dim, block_table) -> idx_kcache:

@@ -53,6 +53,8 @@ int check(const idx_config *cfg, int32_t *sbk_out) {
                     idx::kHeads, idx::kHeadDim, cfg->num_heads, cfg->head_dim);
     if (cfg->q_format != IDX_Q_MXFP4 && cfg->q_format != IDX_Q_FP8_E4M3_ROWSCALE)
         return fail(IDX_EINVAL, "unknown q_format %d", cfg->q_format);
+    if (cfg->score_format != IDX_SCORE_FP32 && cfg->score_format != IDX_SCORE_BF16)
+        return fail(IDX_EINVAL, "unknown score_format %d", cfg->score_format);
     if (cfg->candidate_block_size <= 0 || cfg->num_candidate_blocks <= 0)
         return fail(IDX_EINVAL, "candidate_block_size (%d) and num_candidate_blocks (%d) must be > 0",
                     cfg->candidate_block_size, cfg->num_candidate_blocks);
@@ -133,10 +135,12 @@ int check_schedule(const idx_config *cfg, const idx_rows *rows, const idx_schedu
     return IDX_OK;
 }
 
-int check_q(const idx_config *cfg, const void *qv, const void *qs, const float *w) {
+int check_q(const idx_config *cfg, const void *qv, const void *qs, const void *w) {
     if (!qv || !qs || !w) return fail(IDX_EINVAL, "q_values, q_scales and weights must be non-NULL");
     if (!aligned(qv, 16)) return fail(IDX_EINVAL, "q_values must be 16-byte aligned");
-    if (!aligned(w, 4)) return fail(IDX_EINVAL, "weights must be 4-byte aligned");
+    if (cfg->score_format == IDX_SCORE_BF16 ? !aligned(w, 8) : !aligned(w, 4))
+        return fail(IDX_EINVAL, "weights must be %d-byte aligned",
+                    cfg->score_format == IDX_SCORE_BF16 ? 8 : 4);
     if (cfg->q_format == IDX_Q_FP8_E4M3_ROWSCALE && !aligned(qs, 4))
         return fail(IDX_EINVAL, "fp8 row scales must be 4-byte aligned");
     return IDX_OK;
@@ -310,7 +314,7 @@ int idx_expand_candidates(const idx_config *cfg, const idx_rows *rows, const idx
 }
 
 int idx_sparse_mqa_logits_topk(const idx_config *cfg, const idx_rows *rows, const void *q_values,
-                               const void *q_scales, const float *weights, const idx_kcache *k,
+                               const void *q_scales, const void *weights, const idx_kcache *k,
                                const idx_schedule *sched, int32_t *topk_indices,
                                int64_t out_stride, float *logits_out, void *workspace,
                                size_t workspace_bytes, void *stream) {
@@ -337,9 +341,10 @@ int idx_sparse_mqa_logits_topk(const idx_config *cfg, const idx_rows *rows, cons
     const idx::Rows r = to_rows(rows);
     const idx::KCache kc = to_kcache(cfg, k);
     hipStream_t st = (hipStream_t)stream;
-    if ((rc = hip_status(idx::launch_sparse(cfg->q_format, r, q_values, q_scales, weights, kc, s,
-                                            logits_out, (float *)workspace, cfg->topk,
-                                            topk_indices, out_stride, g_timing, st),
+    if ((rc = hip_status(idx::launch_sparse(cfg->q_format, cfg->score_format, r, q_values,
+                                            q_scales, weights, kc, s, logits_out,
+                                            (float *)workspace, cfg->topk, topk_indices,
+                                            out_stride, g_timing, st),
                          "sparse launch")))
         return rc;
     return ok();
@@ -347,7 +352,7 @@ int idx_sparse_mqa_logits_topk(const idx_config *cfg, const idx_rows *rows, cons
 
 int idx_sparse_mqa_logits_topk_noalloc(const idx_config *cfg, const idx_rows *rows,
                                        const void *q_values, const void *q_scales,
-                                       const float *weights, const idx_kcache *k,
+                                       const void *weights, const idx_kcache *k,
                                        const idx_schedule *sched, int32_t *topk_indices,
                                        int64_t out_stride, float *logits_out, void *stream) {
     int32_t sbk = 0;
@@ -378,8 +383,9 @@ int idx_sparse_mqa_logits_topk_noalloc(const idx_config *cfg, const idx_rows *ro
         if ((rc = scratch_device_ptr(&p))) return rc;
         scratch_logits = (float *)p;
     }
-    if ((rc = hip_status(idx::launch_sparse(cfg->q_format, to_rows(rows), q_values, q_scales,
-                                            weights, to_kcache(cfg, k), s, logits_out,
+    if ((rc = hip_status(idx::launch_sparse(cfg->q_format, cfg->score_format, to_rows(rows),
+                                            q_values, q_scales, weights, to_kcache(cfg, k), s,
+                                            logits_out,
                                             scratch_logits, cfg->topk, topk_indices, out_stride,
                                             g_timing, (hipStream_t)stream),
                          "sparse launch")))
@@ -440,7 +446,8 @@ int idx_sparse_mqa_logits_topk_layers(const idx_config *cfg, const idx_rows *row
         if (!aligned(workspace, 16)) return fail(IDX_EINVAL, "workspace must be 16-byte aligned");
     }
     static_assert(idx::kMaxLayers == IDX_MAX_LAYERS, "one layer limit for the launch and the ABI");
-    if ((rc = hip_status(idx::launch_sparse_layers(cfg->q_format, to_rows(rows), num_layers, ls,
+    if ((rc = hip_status(idx::launch_sparse_layers(cfg->q_format, cfg->score_format,
+                                                   to_rows(rows), num_layers, ls,
                                                    to_kcache(cfg, &k0), s, (float *)workspace,
                                                    workspace ? workspace_bytes : 0, cfg->topk,
                                                    out_stride, g_timing,
@@ -452,7 +459,7 @@ int idx_sparse_mqa_logits_topk_layers(const idx_config *cfg, const idx_rows *row
 
 int idx_dense_masked_logits_topk(const idx_config *cfg, const idx_rows *rows, int32_t max_ctx,
                                  const void *q_values, const void *q_scales,
-                                 const float *weights, const idx_kcache *k,
+                                 const void *weights, const idx_kcache *k,
                                  const idx_schedule *sched, int32_t *topk_indices,
                                  int64_t out_stride, float *logits_out, int64_t logits_stride,
                                  void *workspace, size_t workspace_bytes, void *stream) {
@@ -487,8 +494,9 @@ int idx_dense_masked_logits_topk(const idx_config *cfg, const idx_rows *rows, in
     const idx::KCache kc = to_kcache(cfg, k);
     const idx::Schedule s = to_schedule(cfg, sbk, sched);
     hipStream_t st = (hipStream_t)stream;
-    if ((rc = hip_status(idx::launch_score_dense(cfg->q_format, r, max_ctx, q_values, q_scales,
-                                                 weights, kc, logits, lstride, g_timing, st),
+    if ((rc = hip_status(idx::launch_score_dense(cfg->q_format, cfg->score_format, r, max_ctx,
+                                                 q_values, q_scales, weights, kc, logits,
+                                                 lstride, g_timing, st),
                          "dense score launch")))
         return rc;
     if ((rc = hip_status(idx::launch_dense_topk(r, kc, s, logits, lstride, ncols, cfg->topk,

@@ -85,10 +85,13 @@ int device_cus();
 Plan plan_sparse(int q_format, int32_t sbk, int32_t ncols, int32_t num_rows, int32_t num_layers,
                  int cus, bool logits_home);
 
-hipError_t launch_sparse(int q_format, const Rows &rows, const void *q_values, const void *q_scales,
-                         const float *weights, const KCache &k, const Schedule &s, float *logits_out,
-                         float *workspace, int32_t topk, int32_t *out, int64_t out_stride,
-                         const Timing &timing, hipStream_t stream);
+// score_format: 0 = fp32 weights [rows][64] and fp32 logits; 1 = bf16 weights (codes,
+// 8-byte aligned rows) and every logit rounded to bf16 before the selection.
+hipError_t launch_sparse(int q_format, int score_format, const Rows &rows, const void *q_values,
+                         const void *q_scales, const void *weights, const KCache &k,
+                         const Schedule &s, float *logits_out, float *workspace, int32_t topk,
+                         int32_t *out, int64_t out_stride, const Timing &timing,
+                         hipStream_t stream);
 
 // Per-layer pointers of a multi-layer sparse call (layers [0, num_layers) used).  The
 // layers share the rows, the schedule and every KCache field but the two pools.
@@ -96,7 +99,7 @@ constexpr int kMaxLayers = 8;
 struct LayerSet {
     const void *q_values[kMaxLayers];
     const void *q_scales[kMaxLayers];
-    const float *weights[kMaxLayers];
+    const void *weights[kMaxLayers];
     const uint8_t *k_values[kMaxLayers];
     const uint8_t *k_scales[kMaxLayers];
     float *logits_out[kMaxLayers];   // entries may be null
@@ -110,17 +113,18 @@ struct LayerSet {
 // num_layers * rows * NB*cbs floats).  The timing events ride on the (scoring) launch.
 // Otherwise each layer is launched as launch_sparse does, in layer order, reusing the
 // workspace (the events ride on every layer's scoring launch, so they time the last).
-hipError_t launch_sparse_layers(int q_format, const Rows &rows, int32_t num_layers,
-                                const LayerSet &layers, const KCache &k, const Schedule &s,
-                                float *workspace, size_t workspace_bytes, int32_t topk,
-                                int64_t out_stride, const Timing &timing, hipStream_t stream);
+hipError_t launch_sparse_layers(int q_format, int score_format, const Rows &rows,
+                                int32_t num_layers, const LayerSet &layers, const KCache &k,
+                                const Schedule &s, float *workspace, size_t workspace_bytes,
+                                int32_t topk, int64_t out_stride, const Timing &timing,
+                                hipStream_t stream);
 
 // Scores every token t < max_ctx of every row into logits [rows][logits_stride]
 // (-inf outside [ks, ke)).
-hipError_t launch_score_dense(int q_format, const Rows &rows, int32_t max_ctx, const void *q_values,
-                              const void *q_scales, const float *weights, const KCache &k,
-                              float *logits, int64_t logits_stride, const Timing &timing,
-                              hipStream_t stream);
+hipError_t launch_score_dense(int q_format, int score_format, const Rows &rows, int32_t max_ctx,
+                              const void *q_values, const void *q_scales, const void *weights,
+                              const KCache &k, float *logits, int64_t logits_stride,
+                              const Timing &timing, hipStream_t stream);
 
 // Per-row top-k over the dense logits (tokens masked to the schedule's blocks).
 hipError_t launch_dense_topk(const Rows &rows, const KCache &k, const Schedule &s,

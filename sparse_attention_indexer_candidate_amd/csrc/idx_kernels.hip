@@ -391,23 +391,46 @@ __device__ __forceinline__ void load_q(QFrag<1> &f, const void *qv, const void *
     }
 }
 
+// bf16 code(s) in a 32-bit word -> fp32: the low half, the high half (exact widening).
+__device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xFFFF0000u); }
+
+// fp32 -> the nearest bf16 value (ties to the even significand), kept as the fp32 it
+// widens to: the bf16 scoring format rounds every logit so before the selection.
+__device__ __forceinline__ float round_bf16(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return __uint_as_float((u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u);
+}
+
+// The logit the selection sees: fp32 (sf = 0) or rounded to bf16 (sf = 1).
+__device__ __forceinline__ float score_out(int sf, float x) { return sf ? round_bf16(x) : x; }
+
+// Weights of the lane's 16 heads: fp32 (sf = 0) or bf16 codes (sf = 1), each lane's 4
+// consecutive heads read as two 8-byte loads issued whatever the format (no load behind
+// a branch: fp32 takes bytes [0, 16) of its run, bf16 bytes [0, 8) twice; both stay inside
+// the row's weights, which are 8-byte aligned).
 template <int QF>
-__device__ __forceinline__ void load_q_weights(QFrag<QF> &f, const void *qs, const float *weights,
-                                               int row, int lane) {
+__device__ __forceinline__ void load_q_weights(QFrag<QF> &f, const void *qs, const void *weights,
+                                               int sf, int row, int lane) {
     const int g = lane >> 4;
     const float rs = (QF == 1) ? ((const float *)qs)[row] : 1.0f;
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-            f.w[ht][v] = weights[(int64_t)row * kHeads + 16 * ht + 4 * g + v] * rs;
+    for (int ht = 0; ht < 4; ++ht) {
+        const int64_t i = (int64_t)row * kHeads + 16 * ht + 4 * g;
+        const uint8_t *p = (const uint8_t *)weights + (i << (2 - sf));
+        const uint2 a = *(const uint2 *)p, b = *(const uint2 *)(p + (sf ? 0 : 8));
+        f.w[ht][0] = (sf ? bf16_lo(a.x) : __uint_as_float(a.x)) * rs;
+        f.w[ht][1] = (sf ? bf16_hi(a.x) : __uint_as_float(a.y)) * rs;
+        f.w[ht][2] = (sf ? bf16_lo(a.y) : __uint_as_float(b.x)) * rs;
+        f.w[ht][3] = (sf ? bf16_hi(a.y) : __uint_as_float(b.y)) * rs;
+    }
 }
 
 template <int QF>
 __device__ __forceinline__ void load_q(QFrag<QF> &f, const void *qv, const void *qs,
-                                       const float *weights, int row, int lane) {
+                                       const void *weights, int sf, int row, int lane) {
     load_q(f, qv, qs, row, lane);
-    load_q_weights(f, qs, weights, row, lane);
+    load_q_weights(f, qs, weights, sf, row, lane);
 }
 
 // ReLU as one integer max on the float's bits: negative values (and -0) have the
@@ -512,7 +535,7 @@ __device__ __forceinline__ float reduce_transpose4(float p0, float p1, float p2,
 // valid token of [ks, ke).
 template <int QF, int RG, int U, class Desc, class Sink>
 __device__ __forceinline__ void score_groups(const KCache &k, const QFrag<QF> &f, int ks, int ke,
-                                             int g0, int g1, Desc desc, Sink sink) {
+                                             int g0, int g1, int sf, Desc desc, Sink sink) {
     static_assert(RG <= 16 && RG % U == 0, "units must tile a round of at most 16 groups");
     constexpr int NU = RG / U;
     const int lane = threadIdx.x & (kWave - 1);
@@ -560,7 +583,7 @@ __device__ __forceinline__ void score_groups(const KCache &k, const QFrag<QF> &f
                     const float v = tile_partial(f, b[q][t]);
                     p[t] = ((okmask >> (grp * 4 + t)) & 1) ? v : 0.0f;
                 }
-                const float lg = reduce_transpose4(p[0], p[1], p[2], p[3]);
+                const float lg = score_out(sf, reduce_transpose4(p[0], p[1], p[2], p[3]));
                 const int tok = __shfl(ttok, grp * 4 + g, kWave) + n;
                 const bool valid = ((okmask >> (grp * 4 + g)) & 1) && tok >= ks && tok < ke;
                 sink((r0 + grp) * 64 + lane, valid ? lg : -INFINITY);
@@ -586,7 +609,7 @@ __device__ __forceinline__ void score_groups(const KCache &k, const QFrag<QF> &f
 // otherwise).
 template <int QF, int U, class Desc, class Grab, class Sink>
 __device__ __forceinline__ void score_units(const KCache &k, const QFrag<QF> &f, int ks, int ke,
-                                            Desc desc, Grab grab, Sink sink) {
+                                            int sf, Desc desc, Grab grab, Sink sink) {
     static_assert(4 * U <= kWave, "one lane per tile of a unit");
     const int lane = threadIdx.x & (kWave - 1);
     const int n = lane & 15, g = lane >> 4;
@@ -629,7 +652,7 @@ __device__ __forceinline__ void score_units(const KCache &k, const QFrag<QF> &f,
                 const float v = tile_partial(f, b[q][t]);
                 p[t] = ((okmask >> (q * 4 + t)) & 1) ? v : 0.0f;
             }
-            const float lg = reduce_transpose4(p[0], p[1], p[2], p[3]);
+            const float lg = score_out(sf, reduce_transpose4(p[0], p[1], p[2], p[3]));
             const int tok = __shfl(ttok, q * 4 + g, kWave) + n;
             const bool valid = ((okmask >> (q * 4 + g)) & 1) && tok >= ks && tok < ke;
             sink((u * U + q) * 64 + lane, lg, valid);
@@ -1025,8 +1048,8 @@ constexpr int kTopkThreads = 512;
 template <int QF, int PW>
 __device__ __forceinline__ void score_split_row(
     const int32_t *si_base, const int32_t *pg_base, const void *qv, const void *qs,
-    const float *weights, int32_t nsb, int32_t sbk, int32_t groups_per_wg, const Rows &rows,
-    const KCache &k, float *logits) {
+    const void *weights, int32_t nsb, int32_t sbk, int32_t groups_per_wg, const Rows &rows,
+    const KCache &k, float *logits, int sf) {
     const int row = blockIdx.x;
     const int wave = uniform(threadIdx.x / kWave);
     const int ncols = nsb * sbk;
@@ -1034,22 +1057,22 @@ __device__ __forceinline__ void score_split_row(
     const int g0 = min(blockIdx.y * groups_per_wg + wave * PW, ngroups);
     const int g1 = min(g0 + PW, ngroups);
     QFrag<QF> f;
-    load_q<QF>(f, qv, qs, weights, row, threadIdx.x & (kWave - 1));
+    load_q<QF>(f, qv, qs, weights, sf, row, threadIdx.x & (kWave - 1));
     const int32_t *si = si_base + (int64_t)row * nsb, *pg = pg_base + (int64_t)row * nsb;
     const int32_t ks_raw = (rows.ks ? rows.ks : rows.ke)[row];   // no load behind a branch
     const int ks = rows.ks ? ks_raw : 0, ke = rows.ke[row];
     float *lrow = logits + (int64_t)row * ncols;
-    score_groups<QF, PW, PW>(k, f, ks, ke, g0, g1, SparseDesc{si, pg, nsb, sbk},
+    score_groups<QF, PW, PW>(k, f, ks, ke, g0, g1, sf, SparseDesc{si, pg, nsb, sbk},
                              [&](int c, float v) { if (c < ncols) lrow[c] = v; });
 }
 
 template <int QF, int PW>
 __global__ __launch_bounds__(kScoreThreads) void score_split_kernel(
     const int32_t *si_base, const int32_t *pg_base, const void *qv, const void *qs,
-    const float *weights, int32_t nsb, int32_t sbk, int32_t groups_per_wg, Rows rows, KCache k,
-    float *logits) {
+    const void *weights, int32_t nsb, int32_t sbk, int32_t groups_per_wg, Rows rows, KCache k,
+    float *logits, int32_t sf) {
     score_split_row<QF, PW>(si_base, pg_base, qv, qs, weights, nsb, sbk, groups_per_wg, rows, k,
-                            logits);
+                            logits, sf);
 }
 
 // Logits of layer l of a multi-layer split launch: the layer's logits_out, else its slice
@@ -1063,13 +1086,14 @@ __device__ __forceinline__ float *layer_logits(const LayerSet &ls, int l, float 
 template <int QF, int PW>
 __global__ __launch_bounds__(kScoreThreads) void score_split_layers_kernel(
     const int32_t *si_base, const int32_t *pg_base, int32_t nsb, int32_t sbk,
-    int32_t groups_per_wg, Rows rows, KCache k, LayerSet ls, float *ws, int64_t ws_layer) {
+    int32_t groups_per_wg, Rows rows, KCache k, LayerSet ls, float *ws, int64_t ws_layer,
+    int32_t sf) {
     const int l = blockIdx.z;
     KCache kl = k;
     kl.values = ls.k_values[l];
     kl.scales = ls.k_scales[l];
     score_split_row<QF, PW>(si_base, pg_base, ls.q_values[l], ls.q_scales[l], ls.weights[l], nsb,
-                            sbk, groups_per_wg, rows, kl, layer_logits(ls, l, ws, ws_layer));
+                            sbk, groups_per_wg, rows, kl, layer_logits(ls, l, ws, ws_layer), sf);
 }
 
 // Tokens of the KPT sparse columns c0 .. c0+KPT-1 (KPT divides sbk = 1 << lsbk, and c0
@@ -1217,9 +1241,9 @@ struct FusedLds {
 template <int QF, int NT, int KPT, int U>
 __device__ __forceinline__ void fused_row(
     FusedLds<NT> &L, int row, const int32_t *si_base, const int32_t *pg_base, const void *qv,
-    const void *qs, const float *weights, const int32_t *p_kept, int32_t nsb, int32_t lsbk,
+    const void *qs, const void *weights, const int32_t *p_kept, int32_t nsb, int32_t lsbk,
     const Rows &rows, const KCache &k, float *logits_out, int32_t topk, int32_t *out,
-    int64_t ostride) {
+    int64_t ostride, int sf) {
     uint32_t *s_word = L.word;
     int32_t *s_si = L.si;
     int32_t *s_pg = L.pg;
@@ -1235,7 +1259,7 @@ __device__ __forceinline__ void fused_row(
     ri.ncols = nsb * sbk;
     ri.tbl_ok = true;
     QFrag<QF> f;
-    load_q<QF>(f, qv, qs, weights, row, lane);   // overlaps the schedule copy
+    load_q<QF>(f, qv, qs, weights, sf, row, lane);   // overlaps the schedule copy
     // Every slot [0, nsb) is written by the expansion (-1 past the kept count), so the
     // copy is not bound by the kept load: the schedule, the kept count and the query
     // are one memory round trip, not two.
@@ -1261,7 +1285,7 @@ __device__ __forceinline__ void fused_row(
     const int valid_cols = ri.valid_cols;
     float *lout = logits_out ? logits_out + (int64_t)row * ri.ncols : nullptr;
     score_units<QF, U>(
-        k, f, ri.ks, ri.ke,
+        k, f, ri.ks, ri.ke, sf,
         [&](int tile, int &page, int &tok) {
             const int c = tile * 16;
             if (c < valid_cols) {
@@ -1316,11 +1340,11 @@ __device__ __forceinline__ void fused_row(
 template <int QF, int NT, int KPT, int U, int WPE>
 __global__ __launch_bounds__(NT, WPE) void fused_row_kernel(
     const int32_t *si_base, const int32_t *pg_base, const void *qv, const void *qs,
-    const float *weights, const int32_t *p_kept, int32_t nsb, int32_t lsbk, Rows rows, KCache k,
-    float *logits_out, int32_t topk, int32_t *out, int64_t ostride) {
+    const void *weights, const int32_t *p_kept, int32_t nsb, int32_t lsbk, Rows rows, KCache k,
+    float *logits_out, int32_t topk, int32_t *out, int64_t ostride, int32_t sf) {
     __shared__ FusedLds<NT> lds;
     fused_row<QF, NT, KPT, U>(lds, blockIdx.x, si_base, pg_base, qv, qs, weights, p_kept, nsb, lsbk,
-                           rows, k, logits_out, topk, out, ostride);
+                           rows, k, logits_out, topk, out, ostride, sf);
 }
 
 // Several consuming layers of one step in one launch (grid.y = layer): the layers share
@@ -1332,7 +1356,7 @@ __global__ __launch_bounds__(NT, WPE) void fused_row_kernel(
 template <int QF, int NT, int KPT, int U, int WPE>
 __global__ __launch_bounds__(NT, WPE) void fused_layers_kernel(
     const int32_t *si_base, const int32_t *pg_base, const int32_t *p_kept, int32_t nsb,
-    int32_t lsbk, int32_t topk, Rows rows, KCache k, LayerSet ls, int64_t ostride) {
+    int32_t lsbk, int32_t topk, Rows rows, KCache k, LayerSet ls, int64_t ostride, int32_t sf) {
     __shared__ FusedLds<NT> lds;
     const int layer = blockIdx.y;
     KCache kl = k;
@@ -1340,14 +1364,14 @@ __global__ __launch_bounds__(NT, WPE) void fused_layers_kernel(
     kl.scales = ls.k_scales[layer];
     fused_row<QF, NT, KPT, U>(lds, blockIdx.x, si_base, pg_base, ls.q_values[layer],
                            ls.q_scales[layer], ls.weights[layer], p_kept, nsb, lsbk, rows, kl,
-                           ls.logits_out[layer], topk, ls.out[layer], ostride);
+                           ls.logits_out[layer], topk, ls.out[layer], ostride, sf);
 }
 
 // Dense scoring (the comparator): column t is token t, every token < max_ctx.
 template <int QF>
 __global__ __launch_bounds__(kScoreThreads) void score_dense_kernel(
-    Rows rows, int32_t max_ctx, const void *qv, const void *qs, const float *weights, KCache k,
-    float *logits, int64_t lstride, int groups_per_wg) {
+    Rows rows, int32_t max_ctx, const void *qv, const void *qs, const void *weights, KCache k,
+    float *logits, int64_t lstride, int groups_per_wg, int32_t sf) {
     const int row = blockIdx.x;
     const int wave = uniform(threadIdx.x / kWave);
     const int ngroups = (max_ctx + 63) / 64;
@@ -1362,8 +1386,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_dense_kernel(
     float *lrow = logits + (int64_t)row * lstride;
     QFrag<QF> f;
     if (g0 * 64 < ke && g1 * 64 > ks && tbl_ok)
-        load_q<QF>(f, qv, qs, weights, row, threadIdx.x & (kWave - 1));
-    score_groups<QF, 4, 2>(k, f, ks, ke, g0, g1,
+        load_q<QF>(f, qv, qs, weights, sf, row, threadIdx.x & (kWave - 1));
+    score_groups<QF, 4, 2>(k, f, ks, ke, g0, g1, sf,
                                  DenseDesc{bt, ks, tbl_ok ? ke : 0, k.page_size, k.pages_per_table},
                                  [&](int t, float v) { lrow[t] = v; });  // t < ngroups*64 <= lstride
 }
@@ -1427,8 +1451,8 @@ __device__ __forceinline__ int pick(const int (&a)[N], int i) {
 template <int NCMAX, int GR>
 __device__ __forceinline__ void row_group_rows(
     GroupLds<NCMAX, GR> &lds, const Rows &rows, const void *qv, const void *qs,
-    const float *weights, const KCache &k, const Schedule &s, float *logits_out, int32_t topk,
-    int32_t *out, int64_t ostride) {
+    const void *weights, const KCache &k, const Schedule &s, float *logits_out, int32_t topk,
+    int32_t *out, int64_t ostride, int sf) {
     static_assert(GR >= 1 && GR <= kGroupWaves, "a wave selects each row");
     static_assert(64 % (NCMAX / kGroupThreads) == 0, "a thread's keys lie in one sparse block");
     using L = GroupLds<NCMAX, GR>;
@@ -1447,8 +1471,14 @@ __device__ __forceinline__ void row_group_rows(
     for (int r = 0; r < GR; ++r)
         if (row0 + r < rows.num_rows) load_q(f[r], qv, qs, row0 + r, lane);
     for (int i = tid; i < GR * kHeads; i += kGroupThreads) {
+        // fp32, or a bf16 code read as the aligned 32-bit word holding it (the weights
+        // are 8-byte aligned, so that word lies inside them); no load behind a branch
         const int r = i / kHeads;
-        lds.w[r][i % kHeads] = row0 + r < rows.num_rows ? weights[(int64_t)row0 * kHeads + i] : 0.0f;
+        const int64_t e = (int64_t)row0 * kHeads + min(i, (rows.num_rows - row0) * kHeads - 1);
+        const uint32_t x = *(const uint32_t *)((const uint8_t *)weights +
+                                               (sf ? (e * 2) & ~(int64_t)3 : e * 4));
+        const float wv = sf ? ((e & 1) ? bf16_hi(x) : bf16_lo(x)) : __uint_as_float(x);
+        lds.w[r][i % kHeads] = row0 + r < rows.num_rows ? wv : 0.0f;
     }
 
     // Row metadata (uniform: every thread reads the same words).
@@ -1574,8 +1604,9 @@ __device__ __forceinline__ void row_group_rows(
                 w[ht][2] = x.z;
                 w[ht][3] = x.w;
             }
-            const float lg = reduce_transpose4(tile_partial(f[r], w, kt[0]), tile_partial(f[r], w, kt[1]),
-                                               tile_partial(f[r], w, kt[2]), tile_partial(f[r], w, kt[3]));
+            const float lg = score_out(sf, reduce_transpose4(
+                tile_partial(f[r], w, kt[0]), tile_partial(f[r], w, kt[1]),
+                tile_partial(f[r], w, kt[2]), tile_partial(f[r], w, kt[3])));
             // Keep two MFMAs ahead of the ReLU-weight epilogue (8 VALU ops per MFMA):
             // the epilogue of MFMA i runs while MFMA i+1 and i+2 execute.
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
@@ -1641,10 +1672,11 @@ __device__ __forceinline__ void row_group_rows(
 
 template <int NCMAX, int GR>
 __global__ __launch_bounds__(kGroupThreads) void row_group_kernel(
-    Rows rows, const void *qv, const void *qs, const float *weights, KCache k, Schedule s,
-    float *logits_out, int32_t topk, int32_t *out, int64_t ostride) {
+    Rows rows, const void *qv, const void *qs, const void *weights, KCache k, Schedule s,
+    float *logits_out, int32_t topk, int32_t *out, int64_t ostride, int32_t sf) {
     __shared__ GroupLds<NCMAX, GR> lds;
-    row_group_rows<NCMAX, GR>(lds, rows, qv, qs, weights, k, s, logits_out, topk, out, ostride);
+    row_group_rows<NCMAX, GR>(lds, rows, qv, qs, weights, k, s, logits_out, topk, out, ostride,
+                              sf);
 }
 
 // Several layers of a prefill chunk sharing one schedule, one launch (grid.y = layer):
@@ -1652,14 +1684,14 @@ __global__ __launch_bounds__(kGroupThreads) void row_group_kernel(
 // that the previous layer's light ones leave.
 template <int NCMAX, int GR>
 __global__ __launch_bounds__(kGroupThreads) void row_group_layers_kernel(
-    Rows rows, KCache k, Schedule s, LayerSet ls, int32_t topk, int64_t ostride) {
+    Rows rows, KCache k, Schedule s, LayerSet ls, int32_t topk, int64_t ostride, int32_t sf) {
     __shared__ GroupLds<NCMAX, GR> lds;
     const int l = blockIdx.y;
     KCache kl = k;
     kl.values = ls.k_values[l];
     kl.scales = ls.k_scales[l];
     row_group_rows<NCMAX, GR>(lds, rows, ls.q_values[l], ls.q_scales[l], ls.weights[l], kl, s,
-                              ls.logits_out[l], topk, ls.out[l], ostride);
+                              ls.logits_out[l], topk, ls.out[l], ostride, sf);
 }
 
 
@@ -1815,7 +1847,7 @@ Plan plan_sparse(int q_format, int32_t sbk, int32_t ncols, int32_t num_rows, int
 
 template <int QF>
 static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const void *q_scales,
-                                  const float *weights, const KCache &k, const Schedule &s,
+                                  const void *weights, int sf, const KCache &k, const Schedule &s,
                                   float *logits_out, float *workspace, int32_t topk, int32_t *out,
                                   int64_t out_stride, const Timing &timing, hipStream_t stream) {
     hipError_t e;
@@ -1829,7 +1861,7 @@ static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const 
 #define IDX_LAUNCH_GROUP(NC_)                                                                       \
     hipExtLaunchKernelGGL((row_group_kernel<NC_, GR>), grid, dim3(kGroupThreads), 0, stream,        \
                           timing.start, timing.stop, 0, rows, q_values, q_scales, weights, k, s,   \
-                          logits_out, topk, out, out_stride)
+                          logits_out, topk, out, out_stride, sf)
             if (ncols <= 4096) IDX_LAUNCH_GROUP(4096);
             else IDX_LAUNCH_GROUP(8192);
 #undef IDX_LAUNCH_GROUP
@@ -1846,7 +1878,7 @@ static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const 
     hipExtLaunchKernelGGL((fused_row_kernel<QF, NT_, KPT_, U_, WPE_>), dim3(rows.num_rows),       \
                           dim3(NT_), 0, stream, timing.start, timing.stop, 0, s.sparse_indices,   \
                           s.pages, q_values, q_scales, weights, s.kept, s.nsb, s.lsbk, rows, k,   \
-                          logits_out, topk, out, out_stride)
+                          logits_out, topk, out, out_stride, sf)
         if constexpr (QF == 0) {
             if (rows.num_rows < 2 * device_cus()) {
                 if (ncols <= 1024 * 4) IDX_LAUNCH_FUSED(1024, 4, 1, 1);
@@ -1872,11 +1904,11 @@ static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const 
     if (gpw == 8)
         hipExtLaunchKernelGGL((score_split_kernel<QF, 2>), sgrid, dim3(kScoreThreads), 0, stream,
                               timing.start, timing.stop, 0, s.sparse_indices, s.pages, q_values,
-                              q_scales, weights, s.nsb, s.sbk, gpw, rows, k, logits);
+                              q_scales, weights, s.nsb, s.sbk, gpw, rows, k, logits, sf);
     else
         hipExtLaunchKernelGGL((score_split_kernel<QF, 4>), sgrid, dim3(kScoreThreads), 0, stream,
                               timing.start, timing.stop, 0, s.sparse_indices, s.pages, q_values,
-                              q_scales, weights, s.nsb, s.sbk, gpw, rows, k, logits);
+                              q_scales, weights, s.nsb, s.sbk, gpw, rows, k, logits, sf);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (ncols <= 8 * kTopkThreads)
@@ -1890,21 +1922,22 @@ static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const 
     return hipGetLastError();
 }
 
-hipError_t launch_sparse(int q_format, const Rows &rows, const void *q_values, const void *q_scales,
-                         const float *weights, const KCache &k, const Schedule &s, float *logits_out,
-                         float *workspace, int32_t topk, int32_t *out, int64_t out_stride,
-                         const Timing &timing, hipStream_t stream) {
+hipError_t launch_sparse(int q_format, int score_format, const Rows &rows, const void *q_values,
+                         const void *q_scales, const void *weights, const KCache &k,
+                         const Schedule &s, float *logits_out, float *workspace, int32_t topk,
+                         int32_t *out, int64_t out_stride, const Timing &timing,
+                         hipStream_t stream) {
     if (rows.num_rows == 0) return hipSuccess;
     if (q_format == 0)
-        return launch_sparse_q<0>(rows, q_values, q_scales, weights, k, s, logits_out, workspace,
-                                  topk, out, out_stride, timing, stream);
-    return launch_sparse_q<1>(rows, q_values, q_scales, weights, k, s, logits_out, workspace, topk,
-                              out, out_stride, timing, stream);
+        return launch_sparse_q<0>(rows, q_values, q_scales, weights, score_format, k, s,
+                                  logits_out, workspace, topk, out, out_stride, timing, stream);
+    return launch_sparse_q<1>(rows, q_values, q_scales, weights, score_format, k, s, logits_out,
+                              workspace, topk, out, out_stride, timing, stream);
 }
 
 template <int QF>
 static hipError_t launch_split_layers(const Rows &rows, int32_t num_layers, const LayerSet &layers,
-                                      const KCache &k, const Schedule &s, float *workspace,
+                                      int sf, const KCache &k, const Schedule &s, float *workspace,
                                       int32_t topk, int64_t out_stride, const Timing &timing,
                                       hipStream_t stream) {
     const int ncols = s.nsb * s.sbk;
@@ -1916,11 +1949,11 @@ static hipError_t launch_split_layers(const Rows &rows, int32_t num_layers, cons
     if (gpw == 8)
         hipExtLaunchKernelGGL((score_split_layers_kernel<QF, 2>), sgrid, dim3(kScoreThreads), 0,
                               stream, timing.start, timing.stop, 0, s.sparse_indices, s.pages,
-                              s.nsb, s.sbk, gpw, rows, k, layers, workspace, ws_layer);
+                              s.nsb, s.sbk, gpw, rows, k, layers, workspace, ws_layer, sf);
     else
         hipExtLaunchKernelGGL((score_split_layers_kernel<QF, 4>), sgrid, dim3(kScoreThreads), 0,
                               stream, timing.start, timing.stop, 0, s.sparse_indices, s.pages,
-                              s.nsb, s.sbk, gpw, rows, k, layers, workspace, ws_layer);
+                              s.nsb, s.sbk, gpw, rows, k, layers, workspace, ws_layer, sf);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 tgrid(rows.num_rows, num_layers);
@@ -1935,10 +1968,12 @@ static hipError_t launch_split_layers(const Rows &rows, int32_t num_layers, cons
     return hipGetLastError();
 }
 
-hipError_t launch_sparse_layers(int q_format, const Rows &rows, int32_t num_layers,
-                                const LayerSet &layers, const KCache &k, const Schedule &s,
-                                float *workspace, size_t workspace_bytes, int32_t topk,
-                                int64_t out_stride, const Timing &timing, hipStream_t stream) {
+hipError_t launch_sparse_layers(int q_format, int score_format, const Rows &rows,
+                                int32_t num_layers, const LayerSet &layers, const KCache &k,
+                                const Schedule &s, float *workspace, size_t workspace_bytes,
+                                int32_t topk, int64_t out_stride, const Timing &timing,
+                                hipStream_t stream) {
+    const int sf = score_format;
     if (rows.num_rows == 0 || num_layers == 0) return hipSuccess;
     const int ncols = s.nsb * s.sbk;
     // every layer's logits must have a home for the batched split launches: its
@@ -1955,19 +1990,19 @@ hipError_t launch_sparse_layers(int q_format, const Rows &rows, int32_t num_laye
         if (ncols <= 4096)
             hipExtLaunchKernelGGL((row_group_layers_kernel<4096, GR>), grid, dim3(kGroupThreads), 0,
                                   stream, timing.start, timing.stop, 0, rows, k, s, layers, topk,
-                                  out_stride);
+                                  out_stride, sf);
         else
             hipExtLaunchKernelGGL((row_group_layers_kernel<8192, GR>), grid, dim3(kGroupThreads), 0,
                                   stream, timing.start, timing.stop, 0, rows, k, s, layers, topk,
-                                  out_stride);
+                                  out_stride, sf);
         return hipGetLastError();
     }
     if (plan == kPlanSplitLayers) {
         if (q_format == 0)
-            return launch_split_layers<0>(rows, num_layers, layers, k, s, workspace, topk,
+            return launch_split_layers<0>(rows, num_layers, layers, sf, k, s, workspace, topk,
                                           out_stride, timing, stream);
-        return launch_split_layers<1>(rows, num_layers, layers, k, s, workspace, topk, out_stride,
-                                      timing, stream);
+        return launch_split_layers<1>(rows, num_layers, layers, sf, k, s, workspace, topk,
+                                      out_stride, timing, stream);
     }
     if (plan == kPlanOneRowLayers) {
         const dim3 grid(rows.num_rows, num_layers);
@@ -1975,7 +2010,7 @@ hipError_t launch_sparse_layers(int q_format, const Rows &rows, int32_t num_laye
     hipExtLaunchKernelGGL((fused_layers_kernel<QF_, NT_, KPT_, U_, WPE_>), grid, dim3(NT_), 0,    \
                           stream,                                                                  \
                           timing.start, timing.stop, 0, s.sparse_indices, s.pages, s.kept, s.nsb, \
-                          s.lsbk, topk, rows, k, layers, out_stride)
+                          s.lsbk, topk, rows, k, layers, out_stride, sf)
         if (q_format == 0) {
             if (ncols <= 512 * 4) IDX_LAUNCH_LAYERS(0, 512, 4, 1, 4);
             else if (ncols <= 512 * 8) IDX_LAUNCH_LAYERS(0, 512, 8, 1, 4);
@@ -1992,19 +2027,19 @@ hipError_t launch_sparse_layers(int q_format, const Rows &rows, int32_t num_laye
         KCache kl = k;
         kl.values = layers.k_values[l];
         kl.scales = layers.k_scales[l];
-        const hipError_t e = launch_sparse(q_format, rows, layers.q_values[l], layers.q_scales[l],
-                                           layers.weights[l], kl, s, layers.logits_out[l],
-                                           workspace, topk, layers.out[l], out_stride, timing,
-                                           stream);
+        const hipError_t e = launch_sparse(q_format, sf, rows, layers.q_values[l],
+                                           layers.q_scales[l], layers.weights[l], kl, s,
+                                           layers.logits_out[l], workspace, topk, layers.out[l],
+                                           out_stride, timing, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
 }
 
-hipError_t launch_score_dense(int q_format, const Rows &rows, int32_t max_ctx, const void *q_values,
-                              const void *q_scales, const float *weights, const KCache &k,
-                              float *logits, int64_t logits_stride, const Timing &timing,
-                              hipStream_t stream) {
+hipError_t launch_score_dense(int q_format, int score_format, const Rows &rows, int32_t max_ctx,
+                              const void *q_values, const void *q_scales, const void *weights,
+                              const KCache &k, float *logits, int64_t logits_stride,
+                              const Timing &timing, hipStream_t stream) {
     if (rows.num_rows == 0) return hipSuccess;
     const int ngroups = (max_ctx + 63) / 64;
     const int gpw = 16;
@@ -2012,11 +2047,11 @@ hipError_t launch_score_dense(int q_format, const Rows &rows, int32_t max_ctx, c
     if (q_format == 0)
         hipExtLaunchKernelGGL(score_dense_kernel<0>, grid, dim3(kScoreThreads), 0, stream,
                               timing.start, timing.stop, 0, rows, max_ctx, q_values, q_scales,
-                              weights, k, logits, logits_stride, gpw);
+                              weights, k, logits, logits_stride, gpw, score_format);
     else
         hipExtLaunchKernelGGL(score_dense_kernel<1>, grid, dim3(kScoreThreads), 0, stream,
                               timing.start, timing.stop, 0, rows, max_ctx, q_values, q_scales,
-                              weights, k, logits, logits_stride, gpw);
+                              weights, k, logits, logits_stride, gpw, score_format);
     return hipGetLastError();
 }
 

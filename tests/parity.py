@@ -93,10 +93,49 @@ def check_topk_exact_for_own_logits(g_tokens, g_logits, g_idx, topk, what=""):
                                   err_msg=f"{what}: GPU top-k is not exact for its own logits")
 
 
+def round_bf16_np(x):
+    """float64 array -> the nearest bf16 values (ties to even) as float64: spacing
+    2^(e-8) on [2^(e-1), 2^e), 2^-133 below 2^-126, infinity from 2^128 on (numpy's rint
+    rounds halves to even)."""
+    x = np.asarray(x, np.float64)
+    a = np.abs(x)
+    _, e = np.frexp(a)
+    lsb = np.maximum(e - 8, -133)
+    v = np.ldexp(np.rint(np.ldexp(a, -lsb)), lsb)
+    v = np.where(v >= 2.0 ** 128, np.inf, v)
+    v = np.where(np.isfinite(a), v, a)
+    return np.copysign(v, x)
+
+
+def check_logits_bf16(o_tokens, o_exact, o_logits, g_tokens, g_logits, what=""):
+    """bf16 scoring: each GPU logit is a bf16 value (low 16 bits zero) that rounds some
+    value within the fp32 tolerance of the oracle's exact sum: between the roundings of
+    exact - tol and exact + tol (rounding is monotone), so it equals the oracle's bf16
+    logit except where the exact sum lies within tol of a rounding midpoint."""
+    np.testing.assert_array_equal(g_tokens, o_tokens, err_msg=f"{what}: candidate tokens differ")
+    assert np.all((g_logits.view(np.uint32) & 0xFFFF) == 0), f"{what}: a logit is not a bf16 value"
+    tol = ATOL + RTOL * np.abs(o_exact)
+    lo, hi = round_bf16_np(o_exact - tol), round_bf16_np(o_exact + tol)
+    g = g_logits.astype(np.float64)
+    bad = np.nonzero(~((g >= lo) & (g <= hi)))[0]
+    assert bad.size == 0, (f"{what}: {bad.size} bf16 logits outside the allowed roundings, first "
+                           f"token {o_tokens[bad[0]]}: gpu {g[bad[0]]!r} exact {o_exact[bad[0]]!r} "
+                           f"oracle {o_logits[bad[0]]!r}")
+
+
+def check_indices_bf16(o_tokens, o_logits, o_idx, g_logits, g_idx, topk, what=""):
+    """bf16 scoring: the GPU's selection is exact for its own bf16 logits (checked by the
+    caller); where those equal the oracle's bf16 logits on the whole row, the indices are
+    the oracle's exactly (ties included)."""
+    if np.array_equal(g_logits.astype(np.float32).view(np.uint32),
+                      o_logits.astype(np.float32).view(np.uint32)):
+        np.testing.assert_array_equal(g_idx, o_idx, err_msg=f"{what}: indices differ")
+
+
 class GpuRun:
     """One configured indexer over a device case: schedule + per-layer calls."""
 
-    def __init__(self, case, dcase, sbk=0, q_format="mxfp4"):
+    def __init__(self, case, dcase, sbk=0, q_format="mxfp4", score_format="fp32"):
         import torch
 
         import sparse_attention_indexer_candidate_amd as idx
@@ -105,9 +144,11 @@ class GpuRun:
         s = case.spec
         self.case, self.dcase, self.spec = case, dcase, s
         self.q_format = q_format
+        self.score_format = score_format
         self.cfg = idx.make_config(s.num_heads, s.head_dim,
                                    idx.IDX_Q_MXFP4 if q_format == "mxfp4" else idx.IDX_Q_FP8_E4M3_ROWSCALE,
-                                   s.page_size, s.cbs, sbk, s.nb, s.topk)
+                                   s.page_size, s.cbs, sbk, s.nb, s.topk,
+                                   idx.IDX_SCORE_BF16 if score_format == "bf16" else idx.IDX_SCORE_FP32)
         self.sbk = self.cfg.sparse_block_kv
         R = case.num_rows
         dev = dcase.row_ke.device
@@ -129,7 +170,7 @@ class GpuRun:
         L = self.dcase.layers[layer]
         qv, qs = L.q(self.q_format)
         self.idx.idx_sparse_mqa_logits_topk(
-            self.cfg, self.rows, qv, qs, L.weights, self.kcaches[layer], self.sched.struct,
+            self.cfg, self.rows, qv, qs, L.w(self.score_format), self.kcaches[layer], self.sched.struct,
             self.out, self.out.stride(0), self.logits if with_logits else None,
             None if with_logits else self.workspace,
             0 if with_logits else self.workspace.numel())
@@ -152,7 +193,7 @@ class GpuRun:
             lg = torch.empty((R, s.nb * s.cbs), dtype=torch.float32, device=dev) if wl else None
             outs.append(out)
             logs.append(lg)
-            entries.append((qv, qs, L.weights, self.kcaches[layer], out, lg))
+            entries.append((qv, qs, L.w(self.score_format), self.kcaches[layer], out, lg))
         ws = self.workspace
         if workspace_layers > 1:
             ws = torch.empty(self.idx.idx_workspace_bytes(self.cfg, R * workspace_layers, 0),
@@ -171,9 +212,10 @@ class GpuRun:
                     kept=self.sched.work[:4 * self.case.num_rows].view(torch.int32).cpu().numpy())
 
 
-def compare_rows(case, res, ora, topk, sbk, what="", ora_scale=None):
+def compare_rows(case, res, ora, topk, sbk, what="", ora_scale=None, score_format="fp32"):
     """Compare GPU results (dict from GpuRun.fetch) with an oracle RowResult; ora_scale
-    (optional) is the oracle's RowResult for the same rows with |w| (see check_logits)."""
+    (optional) is the oracle's RowResult for the same rows with |w| (see check_logits).
+    score_format "bf16": the bf16 rules above (ora from the oracle's bf16 scoring)."""
     for i, r in enumerate(ora.rows):
         r = int(r)
         tag = f"{what} row {r}"
@@ -181,6 +223,12 @@ def compare_rows(case, res, ora, topk, sbk, what="", ora_scale=None):
         gt, gl = gpu_row_tokens(res["sparse_indices"][r], int(res["kept"][r]), sbk, ks, ke,
                                 res["logits"][r])
         assert res["end"][r] == ora.count[i], f"{tag}: end {res['end'][r]} != {ora.count[i]}"
+        if score_format == "bf16":
+            check_logits_bf16(ora.row_tokens(i), ora.row_exact(i), ora.row_logits(i), gt, gl, tag)
+            check_topk_exact_for_own_logits(gt, gl, res["indices"][r], topk, tag)
+            check_indices_bf16(ora.row_tokens(i), ora.row_logits(i), ora.indices[i], gl,
+                               res["indices"][r], topk, tag)
+            continue
         sc = None if ora_scale is None else ora_scale.row_logits(i)
         check_logits(ora.row_tokens(i), ora.row_logits(i), gt, gl, tag, sc)
         check_indices(ora.row_tokens(i), ora.row_logits(i), ora.indices[i], res["indices"][r],

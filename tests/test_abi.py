@@ -59,7 +59,7 @@ def test_header_is_c99_and_struct_layouts_match_the_binding(tmp_path):
 
 def cfg(**kw):
     base = dict(num_heads=64, head_dim=128, q_format=0, page_size=64, candidate_block_size=64,
-                sparse_block_kv=0, num_candidate_blocks=64, topk=2048)
+                sparse_block_kv=0, num_candidate_blocks=64, topk=2048, score_format=0)
     base.update(kw)
     return idx.idx_config(*[base[f] for f, _ in idx.idx_config._fields_])
 
@@ -76,6 +76,8 @@ def test_sparse_block_pick(cbs, want):
     (dict(num_heads=32), idx.IDX_EUNSUPPORTED),
     (dict(head_dim=64), idx.IDX_EUNSUPPORTED),
     (dict(q_format=7), idx.IDX_EINVAL),
+    (dict(score_format=2), idx.IDX_EINVAL),
+    (dict(score_format=-1), idx.IDX_EINVAL),
     (dict(candidate_block_size=0), idx.IDX_EINVAL),
     (dict(num_candidate_blocks=0), idx.IDX_EINVAL),
     (dict(candidate_block_size=48), idx.IDX_EUNSUPPORTED),
@@ -391,3 +393,21 @@ def test_noalloc_call_checks_arguments_and_zero_rows_launch_nothing():
         assert e.value.code == code, kw
     assert nsb == 64
     assert idx.IDX_NOALLOC_SCRATCH_BYTES >= 255 * 8192 * 4   # the split plan always fits
+
+
+def test_bf16_weights_alignment_is_checked():
+    """bf16 weights must be 8-byte aligned (fp32: 4); checked before any launch."""
+    c = cfg(score_format=idx.IDX_SCORE_BF16)
+    idx.idx_check_config(c)
+    k = idx.idx_kcache(FAKE, 64 * 64, FAKE, 64 * 4, 10, FAKE, 4, 1, 4)
+    sched = idx.idx_schedule(FAKE, FAKE, FAKE, idx.idx_schedule_work_bytes(c, 4))
+    rows = idx.idx_rows(0, None, FAKE, None)
+    for w, ok in [(FAKE, True), (FAKE + 8, True), (FAKE + 4, False), (FAKE + 2, False)]:
+        call = lambda: idx.idx_sparse_mqa_logits_topk(c, rows, FAKE, FAKE, w, k, sched, FAKE,
+                                                      2048, FAKE)
+        if ok:
+            assert call() == idx.IDX_OK
+        else:
+            with pytest.raises(idx.IdxError) as e:
+                call()
+            assert e.value.code == idx.IDX_EINVAL and "8-byte" in str(e.value)

@@ -25,9 +25,10 @@ def _say(msg):
     print(msg, flush=True)
 
 
-def run_and_compare(case, rows=None, layers=(0,), q_format="mxfp4", sbk=0, tag="", scale_case=None):
+def run_and_compare(case, rows=None, layers=(0,), q_format="mxfp4", sbk=0, tag="", scale_case=None,
+                    score_format="fp32"):
     dcase = to_device(case, DEV)
-    g = GpuRun(case, dcase, sbk=sbk, q_format=q_format)
+    g = GpuRun(case, dcase, sbk=sbk, q_format=q_format, score_format=score_format)
     _say(f"[{tag}] expand rows={case.num_rows} sbk={g.sbk} fmt={q_format}")
     g.expand()
     si_o, end_o = oracle.expand(case, g.sbk)
@@ -39,12 +40,14 @@ def run_and_compare(case, rows=None, layers=(0,), q_format="mxfp4", sbk=0, tag="
         np.testing.assert_array_equal(res["sparse_indices"], si_o, err_msg=f"{tag}: schedule")
         np.testing.assert_array_equal(res["end"], end_o, err_msg=f"{tag}: end")
         pool = case.layers[layer].host_pool(case.spec.page_bytes)
-        ora = oracle.indexer_rows(case, layer, rows, q_format, pool=pool, threads=THREADS)
+        ora = oracle.indexer_rows(case, layer, rows, q_format, pool=pool, threads=THREADS,
+                                  score_format=score_format)
         ora_scale = None
         if scale_case is not None:   # same inputs with |w|: the tolerance's magnitudes
             ora_scale = oracle.indexer_rows(scale_case, layer, rows, q_format, pool=pool,
                                             threads=THREADS)
-        compare_rows(case, res, ora, case.spec.topk, g.sbk, f"{tag} layer {layer}", ora_scale)
+        compare_rows(case, res, ora, case.spec.topk, g.sbk, f"{tag} layer {layer}", ora_scale,
+                     score_format=score_format)
         # the launch configuration of the benchmark (workspace, no logits output)
         g.out.fill_(-7)
         g.score(layer, with_logits=False)
@@ -793,3 +796,79 @@ def test_layers_call_graph_replays_match_eager(name):
                 assert torch.equal(o, ref), f"replay {rep} layer {layer}"
             for layer, (o, ref) in enumerate(zip(other["outs"], other["refs"])):
                 assert torch.equal(o, ref), f"eager between replays, layer {layer}"
+
+
+# ---------------------------------------------------------------- bf16 scoring ----
+# bf16 head weights and bf16-rounded logits (the SM100 layer's semantics): every kernel
+# path against the oracle's bf16 scoring, every row.
+
+BF16_PATHS = {
+    "split": SMALL["ragged_sbk64_ks"],
+    "split_sbk16": SMALL["sbk16"],
+    "one_row": WEIGHT_PATHS["fused"],
+    "two_rows_a_cu": SMALL["two_rows_a_cu"],
+    "row_groups": SMALL["rowgroup_shared_table_messy"],
+}
+
+
+@pytest.mark.parametrize("path", sorted(BF16_PATHS))
+def test_bf16_scoring_kernel_paths_all_rows(path):
+    run_and_compare(W.generate(BF16_PATHS[path], seed=31), tag=f"bf16-{path}",
+                    score_format="bf16")
+
+
+def test_bf16_scoring_fp8_query():
+    spec = W.Spec(name="bf8", num_rows=40, page_size=64, cbs=64, nb=12, topk=150,
+                  ke_rule="uniform", ke_lo=10, ke_hi=2500, ks_rule="random", cand_rule="messy",
+                  fill="all", q_formats=("mxfp4", "fp8"))
+    run_and_compare(W.generate(spec, seed=6), q_format="fp8", tag="bf16-fp8", score_format="bf16")
+
+
+def test_bf16_scoring_decode_batch_all_rows():
+    run_and_compare(W.generate(W.config(2), 0), tag="bf16-cfg2", score_format="bf16")
+
+
+def test_bf16_scoring_long_decode_layers_call_all_rows():
+    """The long-context decode batch in bf16 scoring: one multi-layer call (one launch)
+    for the four layers, each layer's indices equal to its own call's, every row of every
+    layer against the oracle's bf16 scoring."""
+    case = W.generate(W.config(4), 0)
+    g = GpuRun(case, to_device(case, DEV), score_format="bf16")
+    g.expand()
+    _say("[bf16-cfg4] one call, 4 layers")
+    outs, _ = g.score_layers(range(4), [False] * 4)
+    torch.cuda.synchronize()
+    for layer in range(4):
+        _say(f"[bf16-cfg4] layer {layer}")
+        g.out.fill_(-7)
+        g.score(layer, with_logits=True)
+        res = g.fetch()
+        np.testing.assert_array_equal(outs[layer].cpu().numpy(), res["indices"],
+                                      err_msg=f"bf16 cfg4 layer {layer}: one call != per layer")
+        pool = case.layers[layer].host_pool(case.spec.page_bytes)
+        ora = oracle.indexer_rows(case, layer, None, "mxfp4", pool=pool, threads=THREADS,
+                                  score_format="bf16")
+        compare_rows(case, res, ora, case.spec.topk, g.sbk, f"bf16-cfg4 layer {layer}",
+                     score_format="bf16")
+
+
+def test_bf16_scoring_prefill_chunk_all_rows():
+    run_and_compare(W.generate(W.config(3), 0), tag="bf16-cfg3", score_format="bf16")
+
+
+def test_bf16_scoring_dense_equals_sparse():
+    """The dense comparator in bf16 scoring returns the sparse path's indices (the same
+    per-column arithmetic and the same rounding)."""
+    import sparse_attention_indexer_candidate_amd as idx
+
+    case = W.generate(W.config(5), 0)
+    g, res = run_and_compare(case, tag="bf16-cfg5", score_format="bf16")
+    R, ctx = case.num_rows, 65536
+    dout = torch.full((R, case.spec.topk), -7, dtype=torch.int32, device=DEV)
+    dlog = torch.empty((R, ctx), dtype=torch.float32, device=DEV)
+    L = g.dcase.layers[0]
+    qv, qs = L.q("mxfp4")
+    idx.idx_dense_masked_logits_topk(g.cfg, g.rows, ctx, qv, qs, L.w("bf16"), g.kcaches[0],
+                                     g.sched.struct, dout, dout.stride(0), dlog, dlog.stride(0))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(dout.cpu().numpy(), res["indices"], err_msg="dense != sparse")

@@ -19,6 +19,11 @@ class DeviceLayer:
     q_scales: object = None      # uint8 [R, H, D/32]
     q_fp8: object = None         # uint8 [R, H, D]
     q_rowscale: object = None    # float32 [R]
+    weights_bf16: object = None  # int16 [R, H]: the weights' bf16 codes
+
+    def w(self, score_format: str = "fp32"):
+        """The weights argument for the given scoring format."""
+        return self.weights_bf16 if score_format == "bf16" else self.weights
 
     def q(self, q_format: str):
         """(q_values, q_scales) arguments for the given query format."""
@@ -55,7 +60,8 @@ def layer_to_device(spec, L, device):
         q_values=None if L.q_values is None else _t(L.q_values, device),
         q_scales=None if L.q_scales is None else _t(L.q_scales, device),
         q_fp8=None if L.q_fp8 is None else _t(L.q_fp8, device),
-        q_rowscale=None if L.q_rowscale is None else _t(L.q_rowscale.astype(np.float32), device))
+        q_rowscale=None if L.q_rowscale is None else _t(L.q_rowscale.astype(np.float32), device),
+        weights_bf16=_t(L.weights_bf16.view(np.int16), device))
 
 
 def to_device(case, device, layers=None) -> DeviceCase:
