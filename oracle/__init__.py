@@ -63,6 +63,9 @@ def lib():
         L.orc_indexer_rows.argtypes = [i, i, i, i, i, i, i, i, p, p, p, p, p, p, i64, p, i64, p,
                                        i64, p, p, p, p, i64, p, ctypes.c_int32, p, i64, p, p, p,
                                        i64, p]
+        L.orc_source_candidates.restype = i
+        L.orc_source_candidates.argtypes = [i, i, i, i, i, i, i, p, p, p, p, p, p, i64, p, i64, p,
+                                            i64, p, p, p, p, ctypes.c_int32, p, i64, p, i64]
         _lib = L
     return _lib
 
@@ -258,3 +261,52 @@ def gather_k_workspace(pool, page_size: int, head_dim: int, block_table, cu_seq_
                 values[row] = 0
                 scales[row] = 0
     return values, scales
+
+
+def source_candidates(case, layer: int = 0, rows=None, nb: int | None = None,
+                      q_format: str = "mxfp4", score_format: str = "fp32", pool=None,
+                      threads: int = 1, score_width: int = 0):
+    """The candidate-source layer's published pool for the given rows (default: all):
+    (candidate_blocks int32 [n, nb], block scores float32 [n, score_width] or None).
+    Block b of cbs = case.spec.cbs tokens scores the largest logit among its tokens in
+    the row's [ks, ke) (NaN where it holds none); the row publishes the nb best blocks,
+    ties toward the lower block id, ascending, then -1.  nb defaults to case.spec.nb."""
+    s = case.spec
+    L = case.layers[layer]
+    nb = s.nb if nb is None else nb
+    if rows is None:
+        rows = np.arange(case.num_rows, dtype=np.int32)
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    if pool is None:
+        pool = L.host_pool(s.page_bytes)
+    pool = np.ascontiguousarray(pool)
+    if threads > 1 and rows.size > 1:
+        from concurrent.futures import ThreadPoolExecutor
+
+        lib()
+        chunks = [c for c in np.array_split(rows, min(rows.size, 4 * threads)) if c.size]
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            parts = list(ex.map(lambda c: source_candidates(case, layer, c, nb, q_format,
+                                                            score_format, pool, 1, score_width),
+                                chunks))
+        return (np.concatenate([p[0] for p in parts]),
+                np.concatenate([p[1] for p in parts]) if score_width else None)
+    n = rows.size
+    cand = np.empty((n, max(nb, 1)), dtype=np.int32)
+    score = np.empty((n, score_width), dtype=np.float32) if score_width else None
+    fmt = Q_MXFP4 if q_format == "mxfp4" else Q_FP8
+    if score_format == "bf16":
+        sfmt, w = SCORE_BF16, np.ascontiguousarray(L.weights_bf16, dtype=np.uint16)
+    else:
+        sfmt, w = SCORE_FP32, np.ascontiguousarray(L.weights, dtype=np.float32)
+    bt = np.ascontiguousarray(case.block_table, dtype=np.int32)
+    lib().orc_source_candidates(
+        s.num_heads, s.head_dim, s.page_size, s.cbs, nb, fmt, sfmt,
+        _ptr(L.q_values) if fmt == Q_MXFP4 else None,
+        _ptr(L.q_scales) if fmt == Q_MXFP4 else None,
+        _ptr(L.q_fp8) if fmt == Q_FP8 else None,
+        _ptr(L.q_rowscale) if fmt == Q_FP8 else None,
+        _ptr(w), _ptr(pool), s.page_bytes, pool.ctypes.data + s.values_bytes, s.page_bytes,
+        _ptr(bt), bt.shape[1], _ptr(case.row_ks), _ptr(case.row_ke), _ptr(case.row_table),
+        _ptr(rows), n, _ptr(cand), cand.shape[1], _ptr(score), score_width)
+    return cand[:, :nb], score

@@ -41,6 +41,16 @@
  *    the nearest bf16 (ties to the even significand) before the selection,
  *    whose tie rule is unchanged.
  *
+ *  - The candidate-source layer's publication of the candidate pool (the
+ *    rocm_paged_mxfp4_indexer page: RocmSparseAttnIndexer, whose forward_hip
+ *    hands candidate_blocks and candidate_write to the dense indexer; the
+ *    sparse_mqa_indexer page's summary: the source layer publishes the top
+ *    candidate blocks).  The pages give no pooling rule; the reading taken:
+ *    the source scores every token of the row's [ks, ke) with the same
+ *    per-token logit, a block of cbs tokens scores the largest logit among
+ *    its tokens in [ks, ke), and the row publishes the NB blocks with the
+ *    largest scores (ties toward the lower block id), ascending, then -1.
+ *
  *  - The sparse-column schedule: each candidate block of cbs tokens becomes
  *    cbs/sbk sparse blocks of sbk tokens; sparse_indices lists the sparse
  *    blocks that hold a token of [ks, ke), ascending, padded with -1; end is
@@ -304,6 +314,23 @@ static float final_logit(double acc, int score_format)
     return (float)acc;
 }
 
+/* Row r's query q[h][d], its weights w[h] (fp32, or bf16 codes widened exactly) and
+ * its fp8 row scale (1 for MXFP4); layouts as described at orc_indexer_rows. */
+static double row_query(int H, int D, int q_format, int score_format, const uint8_t *q_values,
+                        const uint8_t *q_scales, const uint8_t *q_fp8, const float *q_rowscale,
+                        const void *weights, int32_t r, double *q, double *w)
+{
+    dequant_q(q_format, H, D,
+              q_values ? q_values + (int64_t)r * H * (D / 2) : NULL,
+              q_scales ? q_scales + (int64_t)r * H * (D / 32) : NULL,
+              q_fp8 ? q_fp8 + (int64_t)r * H * D : NULL, q);
+    for (int h = 0; h < H; h++)
+        w[h] = score_format == ORC_SCORE_BF16
+                   ? orc_bf16(((const uint16_t *)weights)[(int64_t)r * H + h])
+                   : (double)((const float *)weights)[(int64_t)r * H + h];
+    return (q_format == ORC_Q_FP8) ? (double)q_rowscale[r] : 1.0;
+}
+
 /* ---- top-k selection -------------------------------------------------------- */
 
 typedef struct {
@@ -322,6 +349,15 @@ static int cmp_pair(const void *a, const void *b)
     return (x->t > y->t) - (x->t < y->t);
 }
 
+/* out[0, count) holds the chosen ids: sort them ascending and fill out[count, width)
+ * with -1. */
+static void emit_ascending(int32_t *out, int32_t count, int32_t width)
+{
+    qsort(out, count, sizeof(int32_t), cmp_i32);
+    for (int32_t i = count; i < width; i++)
+        out[i] = -1;
+}
+
 /* out[0, count) = the chosen tokens ascending, out[count, topk) = -1. */
 int32_t orc_select_topk(const int32_t *tokens, const float *logits, int32_t n, int32_t topk,
                         int32_t *out)
@@ -335,11 +371,109 @@ int32_t orc_select_topk(const int32_t *tokens, const float *logits, int32_t n, i
     int32_t count = n < topk ? n : topk;
     for (int32_t i = 0; i < count; i++)
         out[i] = p[i].t;
-    qsort(out, count, sizeof(int32_t), cmp_i32);
-    for (int32_t i = count; i < topk; i++)
-        out[i] = -1;
+    emit_ascending(out, count, topk);
     free(p);
     return count;
+}
+
+/* ---- the candidate-source layer ---------------------------------------------- */
+
+typedef struct {
+    float score;
+    int32_t b;
+} orc_block;
+
+/* Larger block score first; equal fp32 scores by lower block id. */
+static int cmp_block(const void *a, const void *b)
+{
+    const orc_block *x = (const orc_block *)a, *y = (const orc_block *)b;
+    if (x->score > y->score)
+        return -1;
+    if (x->score < y->score)
+        return 1;
+    return (x->b > y->b) - (x->b < y->b);
+}
+
+/*
+ * For each row r = rows[i] (i < n_sel), with ks, ke and the table row as in
+ * orc_indexer_rows below:
+ *   logit[t] for every t in [ks, ke)  (the same per-token definition)
+ *   score[b] = max of logit[t] over the tokens t of block b (b*cbs <= t <
+ *              (b+1)*cbs) that lie in [ks, ke); block b is eligible when it
+ *              holds at least one such token
+ *   out_cand[i*cand_stride + 0 .. nb): the min(nb, #eligible) eligible blocks
+ *              with the largest scores (ties toward the lower block id), in
+ *              ascending block order, then -1
+ *   out_score[i*score_stride + b] (optional): score[b] for b < score_stride,
+ *              NaN where block b is not eligible
+ * Returns 0.
+ */
+int orc_source_candidates(int num_heads, int head_dim, int page_size, int cbs, int nb,
+                          int q_format, int score_format, const uint8_t *q_values,
+                          const uint8_t *q_scales, const uint8_t *q_fp8,
+                          const float *q_rowscale, const void *weights,
+                          const uint8_t *k_values, int64_t k_values_page_stride,
+                          const uint8_t *k_scales, int64_t k_scales_page_stride,
+                          const int32_t *block_table, int64_t block_table_stride,
+                          const int32_t *row_ks, const int32_t *row_ke,
+                          const int32_t *row_table, const int32_t *rows, int32_t n_sel,
+                          int32_t *out_cand, int64_t cand_stride, float *out_score,
+                          int64_t score_stride)
+{
+    int H = num_heads, D = head_dim;
+    double *q = (double *)malloc(sizeof(double) * H * D);
+    double *k = (double *)malloc(sizeof(double) * D);
+    double *w = (double *)malloc(sizeof(double) * H);
+    for (int32_t i = 0; i < n_sel; i++) {
+        int32_t r = rows[i];
+        int32_t ks = row_ks ? row_ks[r] : 0, ke = row_ke[r];
+        int32_t tbl = row_table ? row_table[r] : r;
+        int32_t nblk = ke > 0 ? (ke + cbs - 1) / cbs : 0;
+        double rs = row_query(H, D, q_format, score_format, q_values, q_scales, q_fp8,
+                              q_rowscale, weights, r, q, w);
+        orc_kview kv = {H, D, page_size, k_values, k_values_page_stride,
+                        k_scales, k_scales_page_stride,
+                        block_table + (int64_t)tbl * block_table_stride};
+        orc_block *blk = (orc_block *)malloc(sizeof(orc_block) * (nblk > 0 ? nblk : 1));
+        int32_t n_el = 0;
+        for (int32_t b = 0; b < nblk; b++) {
+            int64_t lo = (int64_t)b * cbs, hi = lo + cbs;
+            if (lo < ks)
+                lo = ks;
+            if (hi > ke)
+                hi = ke;
+            float best = 0.0f;
+            int any = 0;
+            for (int64_t t = lo; t < hi; t++) {
+                dequant_k(&kv, (int32_t)t, k);
+                float lg = final_logit(row_logit(H, D, q, k, w, q_format, rs), score_format);
+                if (!any || lg > best)
+                    best = lg;
+                any = 1;
+            }
+            if (out_score && b < score_stride)
+                out_score[(int64_t)i * score_stride + b] = any ? best : NAN;
+            if (any) {
+                blk[n_el].score = best;
+                blk[n_el].b = b;
+                n_el++;
+            }
+        }
+        if (out_score)
+            for (int64_t b = nblk; b < score_stride; b++)
+                out_score[(int64_t)i * score_stride + b] = NAN;
+        qsort(blk, n_el, sizeof(orc_block), cmp_block);
+        int32_t count = n_el < nb ? n_el : nb;
+        int32_t *out = out_cand + (int64_t)i * cand_stride;
+        for (int32_t j = 0; j < count; j++)
+            out[j] = blk[j].b;
+        emit_ascending(out, count, nb);
+        free(blk);
+    }
+    free(q);
+    free(k);
+    free(w);
+    return 0;
 }
 
 /* ---- one call over a list of rows ------------------------------------------- */
@@ -387,15 +521,8 @@ int orc_indexer_rows(int num_heads, int head_dim, int page_size, int cbs, int nb
         int32_t tbl = row_table ? row_table[r] : r;
         int32_t n = orc_candidate_tokens(candidate_blocks + (int64_t)r * cand_stride, nb, cbs,
                                          ks, ke, tokens);
-        dequant_q(q_format, H, D,
-                  q_values ? q_values + (int64_t)r * H * (D / 2) : NULL,
-                  q_scales ? q_scales + (int64_t)r * H * (D / 32) : NULL,
-                  q_fp8 ? q_fp8 + (int64_t)r * H * D : NULL, q);
-        double rs = (q_format == ORC_Q_FP8) ? (double)q_rowscale[r] : 1.0;
-        for (int h = 0; h < H; h++)
-            w[h] = score_format == ORC_SCORE_BF16
-                       ? orc_bf16(((const uint16_t *)weights)[(int64_t)r * H + h])
-                       : (double)((const float *)weights)[(int64_t)r * H + h];
+        double rs = row_query(H, D, q_format, score_format, q_values, q_scales, q_fp8,
+                              q_rowscale, weights, r, q, w);
         orc_kview kv = {H, D, page_size, k_values, k_values_page_stride,
                         k_scales, k_scales_page_stride,
                         block_table + (int64_t)tbl * block_table_stride};

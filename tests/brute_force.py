@@ -88,14 +88,13 @@ def weights(L, r, score_format):
     return L.weights[r].astype(np.float64)
 
 
-def row(case, r, layer=0, q_format="mxfp4", pool=None, score_format="fp32"):
-    """(indices[topk], candidate tokens, their logits) for row r (fp32 logits, or
-    bf16-rounded ones held in fp32 with score_format "bf16")."""
+def dense_logits(case, r, layer=0, q_format="mxfp4", pool=None, score_format="fp32"):
+    """The logits of every position t < ke of row r (fp32, or bf16-rounded held in fp32)."""
     s = case.spec
     L = case.layers[layer]
     if pool is None:
         pool = L.host_pool(s.page_bytes)
-    ks, ke = int(case.row_ks[r]), int(case.row_ke[r])
+    ke = int(case.row_ke[r])
     table_row = case.block_table[case.row_table[r]]
     K = dense_k(case, layer, table_row, ke, pool)
     Q, rs = q_matrix(case, layer, r, q_format)
@@ -108,9 +107,16 @@ def row(case, r, layer=0, q_format="mxfp4", pool=None, score_format="fp32"):
     for h in range(s.num_heads):                 # head sum in index order
         acc = acc + w[h] * relu[h]
     if score_format == "bf16":
-        logits = np.array([round_bf16_exact(float(v)) for v in acc], dtype=np.float32)
-    else:
-        logits = acc.astype(np.float32)
+        return np.array([round_bf16_exact(float(v)) for v in acc], dtype=np.float32)
+    return acc.astype(np.float32)
+
+
+def row(case, r, layer=0, q_format="mxfp4", pool=None, score_format="fp32"):
+    """(indices[topk], candidate tokens, their logits) for row r (fp32 logits, or
+    bf16-rounded ones held in fp32 with score_format "bf16")."""
+    s = case.spec
+    ks, ke = int(case.row_ks[r]), int(case.row_ke[r])
+    logits = dense_logits(case, r, layer, q_format, pool, score_format)
     blocks = set(int(b) for b in case.candidate_blocks[r] if b >= 0)
     t = np.arange(ke)
     keep = (t >= ks) & np.isin(t // s.cbs, np.array(sorted(blocks), dtype=np.int64))
@@ -120,3 +126,27 @@ def row(case, r, layer=0, q_format="mxfp4", pool=None, score_format="fp32"):
     out = np.full(s.topk, -1, dtype=np.int32)
     out[:count] = np.sort(tk[order[:count]])
     return out, tk.astype(np.int32), lk
+
+
+def source_row(case, r, nb, layer=0, q_format="mxfp4", pool=None, score_format="fp32"):
+    """The candidate-source publication of row r: every position's logit, block maxima
+    over [ks, ke) with numpy's maximum.reduceat, the nb best blocks by a full lexsort
+    (score descending, block ascending), ascending, -1 padded.  Returns (blocks[nb],
+    {block: score})."""
+    s = case.spec
+    ks, ke = int(case.row_ks[r]), int(case.row_ke[r])
+    logits = dense_logits(case, r, layer, q_format, pool, score_format)
+    first, last = ks // s.cbs, (ke - 1) // s.cbs if ke > ks else -1
+    ids = np.arange(first, last + 1)
+    scores = {}
+    if ids.size:
+        starts = np.maximum(ids * s.cbs, ks) - ks
+        m = np.maximum.reduceat(logits[ks:ke], starts)
+        scores = {int(b): float(v) for b, v in zip(ids, m)}
+    b = np.array(sorted(scores), dtype=np.int64)
+    v = np.array([scores[int(x)] for x in b], dtype=np.float64)
+    order = np.lexsort((b, -v)) if b.size else np.zeros(0, np.int64)
+    count = min(nb, b.size)
+    out = np.full(nb, -1, np.int32)
+    out[:count] = np.sort(b[order[:count]])
+    return out, scores

@@ -44,6 +44,17 @@ MUTANTS = {
     "bf16_weight_mantissa_dropped": ("orc_bf16(((const uint16_t *)weights)[(int64_t)r * H + h])",
                                      "orc_bf16(((const uint16_t *)weights)[(int64_t)r * H + h] & 0xFF80)"),
     "bf16_subnormal_spacing": ("    if (lsb < -133)\n        lsb = -133;", "    if (lsb < -126)\n        lsb = -126;"),
+    # the candidate-source layer
+    "source_sum_pooling": ("                if (!any || lg > best)\n                    best = lg;",
+                           "                best = any ? best + lg : lg;"),
+    "source_ties_toward_higher_block": ("    return (x->b > y->b) - (x->b < y->b);",
+                                        "    return (x->b < y->b) - (x->b > y->b);"),
+    "source_ks_ignored": ("            if (lo < ks)\n                lo = ks;\n            if (hi > ke)\n                hi = ke;\n            float best",
+                          "            if (hi > ke)\n                hi = ke;\n            float best"),
+    "source_partial_block_past_ke": ("            if (lo < ks)\n                lo = ks;\n            if (hi > ke)\n                hi = ke;\n            float best",
+                                     "            if (lo < ks)\n                lo = ks;\n            float best"),
+    "source_publishes_by_score_order": ("            out[j] = blk[j].b;\n        emit_ascending(out, count, nb);",
+                                        "            out[j] = blk[j].b;\n        for (int32_t j = count; j < nb; j++)\n            out[j] = -1;"),
     "bf16_no_overflow": ("    if (v >= ldexp(1.0, 128))\n        v = INFINITY;\n", ""),
 }
 

@@ -16,6 +16,7 @@ import torch
 import oracle
 import workloads as W
 from brute_force import row as brute_row
+from brute_force import source_row as brute_source_row
 from golden_io import bf16_examples, e2m1_table, packed_examples, scale_fp8_examples
 
 pytestmark = []
@@ -519,3 +520,83 @@ def test_expand_matches_token_set_definition():
         np.testing.assert_array_equal(si[:n], want)
         assert np.all(si[n:] == -1)
         np.testing.assert_array_equal(oracle.candidate_tokens(cand, cbs, ks, ke), sorted(toks))
+
+
+# ------------------------------------------------------ candidate source ---------
+
+@pytest.mark.parametrize("chunk", range(4))
+def test_source_candidates_match_brute_force(chunk):
+    """The source layer's publication against the brute force (dense logits with numpy,
+    block maxima by reduceat, a full lexsort), exactly, in both scoring formats."""
+    for i in range(chunk * 25, chunk * 25 + 25):
+        rng = np.random.default_rng(7000 + i)
+        spec = _tiny_spec(rng, i)
+        case = W.generate(spec, seed=200 + i)
+        pool = case.layers[0].host_pool(spec.page_bytes)
+        nb = int(rng.integers(1, 12))
+        sfmt = "bf16" if i % 3 == 0 else "fp32"
+        width = 400
+        for fmt in spec.q_formats:
+            cand, score = oracle.source_candidates(case, nb=nb, q_format=fmt, pool=pool,
+                                                   score_format=sfmt, score_width=width)
+            for r in range(case.num_rows):
+                want, wscores = brute_source_row(case, r, nb, q_format=fmt, pool=pool,
+                                                 score_format=sfmt)
+                np.testing.assert_array_equal(cand[r], want, err_msg=f"case {i} row {r}")
+                got = {b: float(score[r, b]) for b in range(width) if not np.isnan(score[r, b])}
+                assert got == wscores, f"case {i} row {r}"
+
+
+def test_source_candidates_closed_form():
+    # One head, weight 1; K zero except one token in each of blocks 2, 5, 6 with dots
+    # 3 * 2^s (s = 1, 3, 2): block scores 6, 24, 12, every other block of the 8 scores 0.
+    # nb = 2 -> blocks 5 and 6; nb = 4 -> 2, 5, 6 and the lowest zero block, 0.
+    # With ks = 20 and ke = 90 the eligible blocks are 1..5 (block 1 = tokens 16..31 and
+    # block 5 = tokens 80..95 only partly in range; block 0 lies below ks, block 6 at or
+    # past ke); the block-5 token at t = 91 is past ke, so block 5 scores 0, and nb = 3
+    # gives block 2 (6) and the two lowest of the zero-score blocks 1, 3, 4, 5: 1 and 3.
+    case = _one_row_case(H=1, D=128, ps=16, n_tokens=128, cbs=16, nb=8, topk=4)
+    L = case.layers[0]
+    L.weights[:] = 1.0
+    qv = np.zeros(64, np.uint8)
+    qv[0] = 0x05                                         # element 0: 3.0
+    L.q_values[0, 0] = qv
+    for t, sc in ((33, 1), (91, 3), (100, 2)):           # blocks 2, 5, 6
+        kv = np.zeros(64, np.uint8)
+        kv[0] = 0x02                                     # element 0: 1.0
+        _set_k(case, t, kv, np.array([127 + sc, 127, 127, 127], np.uint8))
+    cand, score = oracle.source_candidates(case, nb=2, score_width=8)
+    np.testing.assert_array_equal(cand[0], [5, 6])
+    np.testing.assert_array_equal(score[0], [0, 0, 6, 0, 0, 24, 12, 0])
+    cand, _ = oracle.source_candidates(case, nb=4)
+    np.testing.assert_array_equal(cand[0], [0, 2, 5, 6])
+    case.row_ks[0], case.row_ke[0] = 20, 90
+    cand, score = oracle.source_candidates(case, nb=3, score_width=8)
+    np.testing.assert_array_equal(cand[0], [1, 2, 3])
+    assert np.isnan(score[0, 0]) and np.isnan(score[0, 6]) and np.isnan(score[0, 7])
+    np.testing.assert_array_equal(score[0, 1:6], [0, 6, 0, 0, 0])
+
+
+def test_source_candidates_invariants():
+    for i in range(30):
+        spec = W.Spec(name="si", num_rows=3, num_heads=2, head_dim=32, page_size=8, cbs=8, nb=6,
+                      topk=4, ke_rule="uniform", ke_lo=0, ke_hi=120, ks_rule="random",
+                      cand_rule="distinct", fill="all")
+        case = W.generate(spec, i)
+        nb = 1 + i % 9
+        cand, score = oracle.source_candidates(case, nb=nb, score_width=16)
+        for r in range(case.num_rows):
+            ks, ke = int(case.row_ks[r]), int(case.row_ke[r])
+            eligible = [b for b in range(16) if max(b * 8, ks) < min(b * 8 + 8, ke)]
+            count = min(nb, len(eligible))
+            assert np.all(cand[r, count:] == -1)
+            chosen = cand[r, :count]
+            assert np.all(np.diff(chosen) > 0) and set(chosen) <= set(eligible)
+            rest = [b for b in eligible if b not in set(chosen)]
+            if count and rest:
+                lo = min(score[r, b] for b in chosen)
+                hi = max(score[r, b] for b in rest)
+                assert lo >= hi
+                if lo == hi:
+                    assert max(b for b in chosen if score[r, b] == lo) < \
+                        min(b for b in rest if score[r, b] == hi)
