@@ -279,6 +279,140 @@ def bench_gather(args, idx, case, cfg, dev, gen_s):
     print(json.dumps(out), flush=True)
 
 
+def source_bytes(case, q_format: str, max_ctx: int, score_format: str = "fp32") -> int:
+    """Bytes the candidate-source layer must move a launch pair: 68 B of K for every
+    context token of each row's [ks, ke), the row's query and weights (as for the sparse
+    path), one 4-byte part key per min(cbs, 64) positions of max_ctx written by the scoring
+    kernel and read by the selection, and NB published block ids."""
+    s = case.spec
+    ctx = (case.row_ke - case.row_ks).astype(np.int64)
+    per_col = s.head_dim // 2 + s.head_dim // 32
+    q = s.num_heads * (s.head_dim // 2 + s.head_dim // 32) if q_format == "mxfp4" \
+        else s.num_heads * s.head_dim + 4
+    wbytes = 2 if score_format == "bf16" else 4
+    parts = (max_ctx + 63) // 64 * (64 // min(64, s.cbs))
+    per_row = q + wbytes * s.num_heads + 2 * 4 * parts + 4 * s.nb
+    return int(ctx.sum()) * per_col + case.num_rows * per_row
+
+
+def bench_source(args, idx, W, dev, stream):
+    """The candidate-source layer (idx_publish_candidates): every context token of every
+    row scored, blocks pooled by their largest logit, NB blocks published a row."""
+    import torch
+
+    from workloads.device import to_device
+
+    spec = W.config(args.config)
+    t0 = time.time()
+    case = W.generate(spec, args.seed)
+    gen_s = time.time() - t0
+    sfmt = args.score_format
+    cfg = idx.make_config(spec.num_heads, spec.head_dim,
+                          idx.IDX_Q_MXFP4 if args.q_format == "mxfp4" else idx.IDX_Q_FP8_E4M3_ROWSCALE,
+                          spec.page_size, spec.cbs, 0, spec.nb, spec.topk,
+                          idx.IDX_SCORE_BF16 if sfmt == "bf16" else idx.IDX_SCORE_FP32)
+    R = case.num_rows
+    max_ctx = int(case.row_ke.max())
+    launch_bytes = source_bytes(case, args.q_format, max_ctx, sfmt)
+    base = to_device(case, dev, layers=[0])
+    pool_bytes = base.layers[0].pool.numel()
+    nrep = args.replicas if args.replicas > 0 else max(2, math.ceil(1.5e9 / launch_bytes))
+    nrep = max(1, min(nrep, int(40e9 // max(pool_bytes, 1))))
+    reps = [base.layers[0]] + [type(base.layers[0])(
+        pool=base.layers[0].pool.clone(), weights=base.layers[0].weights.clone(),
+        weights_bf16=base.layers[0].weights_bf16.clone(),
+        q_values=None if base.layers[0].q_values is None else base.layers[0].q_values.clone(),
+        q_scales=None if base.layers[0].q_scales is None else base.layers[0].q_scales.clone(),
+        q_fp8=None if base.layers[0].q_fp8 is None else base.layers[0].q_fp8.clone(),
+        q_rowscale=None if base.layers[0].q_rowscale is None else base.layers[0].q_rowscale.clone())
+        for _ in range(nrep - 1)]
+    rows = idx.make_rows(base.row_ke, base.row_ks, base.row_table)
+    cand = torch.empty((R, spec.nb), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(4, idx.idx_publish_workspace_bytes(cfg, R, max_ctx)), dtype=torch.uint8,
+                     device=dev)
+    sh = stream.cuda_stream
+    calls = []
+    for L in reps:
+        qv, qs = L.q(args.q_format)
+        kc = idx.make_kcache(L.pool, spec.page_size, spec.head_dim, base.block_table)
+        calls.append(idx.bind_publish_candidates(cfg, rows, max_ctx, qv, qs, L.w(sfmt), kc, cand,
+                                                 cand.stride(0), None, 0, ws, ws.numel(),
+                                                 stream=sh))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(EVENT_STEPS)]
+    for a, b in ev:
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ev_raw = [(idx.event_handle(a), idx.event_handle(b)) for a, b in ev]
+    set_events = idx.lib.idx_set_timing_events
+    for i in range(args.warmup):
+        calls[i % nrep]()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        calls[i % nrep]()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    for i, pair in enumerate(ev_raw):
+        set_events(*pair)
+        calls[i % nrep]()
+        set_events(None, None)
+    torch.cuda.synchronize()
+    kernel_ms = [a.elapsed_time(b) for a, b in ev]
+    avg_s = float(np.mean(kernel_ms)) / 1e3
+    step_s = elapsed / args.steps
+    peaks = measured_peaks(stream)
+    ctx_cols = int((case.row_ke - case.row_ks).astype(np.int64).sum())
+    # the scoring kernel's share: everything but the selection's read of the part keys
+    # and the published ids
+    parts = (max_ctx + 63) // 64 * (64 // min(64, spec.cbs))
+    score_bytes = launch_bytes - R * (4 * parts + 4 * spec.nb)
+    achieved = score_bytes / avg_s / 1e9
+    roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "step_gbs": launch_bytes / step_s / 1e9,
+            "step_frac": launch_bytes / step_s / 1e9 / HBM_PEAK_GBS,
+            "traffic": traffic_for("score_pool_kernel", args.config, args.q_format),
+            "kernel": "score_pool_kernel", "measured_peak": peaks["read_gbs"],
+            "frac_of_measured": achieved / peaks["read_gbs"], "avg_launch_us": avg_s * 1e6,
+            "launch_us_p10": float(np.percentile(kernel_ms, 10)) * 1e3,
+            "launch_us_p90": float(np.percentile(kernel_ms, 90)) * 1e3,
+            "timed_launches": len(kernel_ms),
+            "timing": "dispatch events on the scoring launch, in an event pass after the timed "
+                      "steps",
+            "algorithmic_bytes_per_launch": score_bytes}
+    out = {"metric": "context cols scored/s by the candidate-source layer (candidate blocks "
+                     "published)",
+           "value": ctx_cols / step_s, "unit": "cols/s", "rows_per_s": R / step_s,
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": step_s * 1e3, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None,
+           "dtype": "mxfp4" if args.q_format == "mxfp4" else "fp8e4m3xmxfp4", "data": "synthetic",
+           "config": {"workload": f"source_{spec.name}", "rows": R, "max_ctx": max_ctx,
+                      "candidate_blocks": spec.nb, "candidate_block_size": spec.cbs,
+                      "q_format": args.q_format, "score_format": sfmt, "path": "source",
+                      "input_copies": nrep, "seed": args.seed},
+           "roofline": roof, "measured_peaks": peaks}
+    if not args.no_cpu_baseline:
+        import oracle
+
+        pool = case.layers[0].host_pool(spec.page_bytes)
+        n, cols, t0 = 0, 0, time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_seconds:   # whole rows, one thread
+            r = n % R
+            oracle.source_candidates(case, 0, np.array([r], np.int32), spec.nb, args.q_format,
+                                     sfmt, pool=pool)
+            cols += int(case.row_ke[r] - case.row_ks[r])
+            n += 1
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = dict(value=cols / dt, unit="cols/s", cores=1, kind="oracle",
+                                   rows_per_s=n / dt, **host_cpu(),
+                                   sample=f"{n} rows ({cols} context cols), one thread, "
+                                          f"{dt:.1f} s wall")
+    print(f"# generated inputs in {gen_s:.1f} s; {nrep} input copies", file=sys.stderr)
+    print(json.dumps(out), flush=True)
+
+
 def traffic_for(kernel_name: str, config: int, q_format: str):
     """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE counters of this
     kernel on this workload, or None when none were taken for the current kernel sources."""
@@ -522,10 +656,11 @@ def main():
     ap.add_argument("--score-format", default="fp32", choices=["fp32", "bf16"],
                     help="fp32 weights and logits (default), or bf16 weights with bf16-rounded "
                          "logits")
-    ap.add_argument("--path", default="sparse", choices=["sparse", "dense", "gather"],
+    ap.add_argument("--path", default="sparse", choices=["sparse", "dense", "gather", "source"],
                     help="sparse: the indexer; dense: the comparator "
                          "idx_dense_masked_logits_topk (scores the whole context); gather: "
-                         "idx_gather_k_workspace of every table row's context [0, ke)")
+                         "idx_gather_k_workspace of every table row's context [0, ke); source: "
+                         "the candidate-source layer idx_publish_candidates")
     ap.add_argument("--replicas", type=int, default=0, help="input copies (0 = auto)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -580,6 +715,8 @@ def main():
     # A stream of the bench's own (default priority), current for the rest of the run.
     stream = torch.cuda.Stream()
     torch.cuda.set_stream(stream)
+    if args.path == "source":
+        return bench_source(args, idx, W, dev, stream)
     dense = args.path == "dense"
     m = run_workload(idx, W, args.config, args, dev, stream, args.steps, args.warmup,
                      layers=args.layers, per_layer_calls=args.per_layer_calls, graph=args.graph)

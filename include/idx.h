@@ -326,6 +326,35 @@ int idx_dense_masked_logits_topk(const idx_config *cfg, const idx_rows *rows, in
                                  int64_t out_stride, float *logits_out, int64_t logits_stride,
                                  void *workspace, size_t workspace_bytes, void *stream);
 
+/* The candidate-source layer: publishes the candidate pool that the consuming layers read
+ * (rocm_paged_mxfp4_indexer page: RocmSparseAttnIndexer, a two-level indexer's source
+ * layer, hands candidate_blocks and candidate_write to the dense indexer's HIP path;
+ * sparse_mqa_indexer page, module summary: the candidate-source indexer publishes the top
+ * candidate blocks and later indexers pick their top-k tokens inside them).  The pages
+ * give no pooling rule; this library's reading: every token t of a row's [ks, ke) is
+ * scored with the same per-token logit as the consuming path (and the dense comparator),
+ * a block b of cbs = candidate_block_size tokens scores the largest logit among its tokens
+ * in [ks, ke) (blocks holding none are not eligible), and the row publishes the NB =
+ * num_candidate_blocks eligible blocks with the largest scores, ties toward the lower
+ * block id, in ascending block order, then -1 (fewer eligible blocks than NB).  The result
+ * is the consuming layers' candidate_blocks input (idx_expand_candidates).
+ *   candidate_blocks: int32 [num_rows][cand_stride], the first NB slots written
+ *   max_ctx: bounds every ke (like the dense comparator); ceil(max_ctx / cbs) <= 4096
+ *   logits_out: NULL, or float [num_rows][logits_stride] (logits_stride >=
+ *     round_up(max_ctx, 64)): token t at column t, -inf outside [ks, ke)
+ *   workspace: idx_publish_workspace_bytes(cfg, num_rows, max_ctx) bytes (per-part
+ *     maxima of the scoring pass), 4-byte aligned
+ * Needs the block table to map every page of [0, ke).  Two launches (scoring with the
+ * block maxima reduced in the same pass, then the block selection); the timing events, if
+ * set, ride on the scoring launch.  Errors as for the other calls, on the host before any
+ * launch. */
+size_t idx_publish_workspace_bytes(const idx_config *cfg, int32_t max_rows, int32_t max_ctx);
+int idx_publish_candidates(const idx_config *cfg, const idx_rows *rows, int32_t max_ctx,
+                           const void *q_values, const void *q_scales, const void *weights,
+                           const idx_kcache *k, int32_t *candidate_blocks, int64_t cand_stride,
+                           float *logits_out, int64_t logits_stride, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
 /* Packed K workspace (the gather of a prefill chunk's paged K into one contiguous
  * buffer that the pages' backend performs before scoring a chunk, the
  * cp_gather_indexer_k_quant_cache call on the sparse_mqa_indexer page): request r's

@@ -33,6 +33,7 @@ EXPORTED = ("idx_check_config", "idx_num_sparse_blocks", "idx_schedule_work_byte
             "idx_expand_candidates", "idx_sparse_mqa_logits_topk",
             "idx_sparse_mqa_logits_topk_layers", "idx_dense_masked_logits_topk",
             "idx_gather_k_workspace", "idx_sparse_plan", "idx_sparse_mqa_logits_topk_noalloc",
+            "idx_publish_workspace_bytes", "idx_publish_candidates",
             "idx_measure_read", "idx_measure_mfma", "idx_measure_mfma_flops")
 IDX_MEASURE_WGS = 4096
 IDX_MAX_LAYERS = 8
@@ -139,6 +140,11 @@ def _load():
     L.idx_gather_k_workspace.argtypes = [P(idx_config), P(idx_kcache), i32, vp, vp, i32, i32,
                                          vp, vp, vp]
     L.idx_gather_k_workspace.restype = ctypes.c_int
+    L.idx_publish_workspace_bytes.argtypes = [P(idx_config), i32, i32]
+    L.idx_publish_workspace_bytes.restype = sz
+    L.idx_publish_candidates.argtypes = [P(idx_config), P(idx_rows), i32, vp, vp, vp,
+                                         P(idx_kcache), vp, i64, vp, i64, vp, sz, vp]
+    L.idx_publish_candidates.restype = ctypes.c_int
     L.idx_sparse_plan.argtypes = [P(idx_config), i32, i32, i32, P(idx_plan_info)]
     L.idx_sparse_plan.restype = ctypes.c_int
     L.idx_measure_read.argtypes = [vp, sz, vp, vp]
@@ -259,6 +265,31 @@ def idx_dense_masked_logits_topk(cfg, rows, max_ctx, q_values, q_scales, weights
         ctypes.byref(cfg), ctypes.byref(rows), max_ctx, _p(q_values), _p(q_scales), _p(weights),
         ctypes.byref(k), ctypes.byref(sched), _p(topk_indices), out_stride, _p(logits_out),
         logits_stride, _p(workspace), workspace_bytes, _p(stream)))
+
+
+def idx_publish_workspace_bytes(cfg: idx_config, max_rows: int, max_ctx: int) -> int:
+    return lib.idx_publish_workspace_bytes(ctypes.byref(cfg), max_rows, max_ctx)
+
+
+def idx_publish_candidates(cfg, rows, max_ctx, q_values, q_scales, weights, k, candidate_blocks,
+                           cand_stride, logits_out=None, logits_stride=0, workspace=None,
+                           workspace_bytes=0, stream=None):
+    """The candidate-source layer: writes candidate_blocks [rows, >= NB] (int32 device)."""
+    return _check(lib.idx_publish_candidates(
+        ctypes.byref(cfg), ctypes.byref(rows), max_ctx, _p(q_values), _p(q_scales), _p(weights),
+        ctypes.byref(k), _p(candidate_blocks), cand_stride, _p(logits_out), logits_stride,
+        _p(workspace), workspace_bytes, _p(stream)))
+
+
+def bind_publish_candidates(cfg, rows, max_ctx, q_values, q_scales, weights, k,
+                            candidate_blocks, cand_stride, logits_out=None, logits_stride=0,
+                            workspace=None, workspace_bytes=0, stream=None):
+    vp = lambda x: ctypes.c_void_p(_p(x))
+    return BoundCall(lib.idx_publish_candidates,
+                     (ctypes.byref(cfg), ctypes.byref(rows), max_ctx, vp(q_values), vp(q_scales),
+                      vp(weights), ctypes.byref(k), vp(candidate_blocks), cand_stride,
+                      vp(logits_out), logits_stride, vp(workspace), workspace_bytes, vp(stream)),
+                     (cfg, rows, k))
 
 
 def idx_gather_k_workspace(cfg, k, cu_seq_lens, values_out, scales_out, max_seq_len,

@@ -506,6 +506,56 @@ int idx_dense_masked_logits_topk(const idx_config *cfg, const idx_rows *rows, in
     return ok();
 }
 
+size_t idx_publish_workspace_bytes(const idx_config *cfg, int32_t max_rows, int32_t max_ctx) {
+    if (check(cfg, nullptr)) return 0;
+    if (max_rows < 0 || max_ctx < 0) {
+        fail(IDX_EINVAL, "max_rows and max_ctx must be >= 0");
+        return 0;
+    }
+    ok();
+    return (size_t)max_rows * idx::publish_parts_per_row(max_ctx, cfg->candidate_block_size) *
+           sizeof(uint32_t);
+}
+
+int idx_publish_candidates(const idx_config *cfg, const idx_rows *rows, int32_t max_ctx,
+                           const void *q_values, const void *q_scales, const void *weights,
+                           const idx_kcache *k, int32_t *candidate_blocks, int64_t cand_stride,
+                           float *logits_out, int64_t logits_stride, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+    int rc;
+    if ((rc = check_filled(cfg, nullptr)) || (rc = check_rows(rows)) ||
+        (rc = check_kcache(cfg, k)) || (rc = check_q(cfg, q_values, q_scales, weights)))
+        return rc;
+    const int32_t cbs = cfg->candidate_block_size, nb = cfg->num_candidate_blocks;
+    if (max_ctx <= 0 || ((int64_t)max_ctx + cbs - 1) / cbs > idx::kMaxPublishBlocks)
+        return fail(IDX_EUNSUPPORTED, "max_ctx %d must be in [1, %lld] (%d blocks of %d tokens)",
+                    max_ctx, (long long)idx::kMaxPublishBlocks * cbs, idx::kMaxPublishBlocks, cbs);
+    if (!candidate_blocks || !aligned(candidate_blocks, 4))
+        return fail(IDX_EINVAL, "candidate_blocks must be non-NULL and 4-byte aligned");
+    if (cand_stride < nb)
+        return fail(IDX_EINVAL, "cand_stride %lld < num_candidate_blocks %d",
+                    (long long)cand_stride, nb);
+    const int64_t ncols = ((int64_t)max_ctx + 63) / 64 * 64;
+    if (logits_out && (logits_stride < ncols || !aligned(logits_out, 4)))
+        return fail(IDX_EINVAL, "logits_stride %lld must be >= %lld and logits_out 4-byte aligned",
+                    (long long)logits_stride, (long long)ncols);
+    const size_t need = (size_t)rows->num_rows *
+                        idx::publish_parts_per_row(max_ctx, cbs) * sizeof(uint32_t);
+    if (need && !workspace) return fail(IDX_EWORKSPACE, "workspace is NULL (needs %zu bytes)", need);
+    if (workspace_bytes < need)
+        return fail(IDX_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    if (!aligned(workspace, 4)) return fail(IDX_EINVAL, "workspace must be 4-byte aligned");
+    if ((rc = hip_status(idx::launch_publish(cfg->q_format, cfg->score_format, to_rows(rows),
+                                             max_ctx, q_values, q_scales, weights,
+                                             to_kcache(cfg, k), cbs, nb, candidate_blocks,
+                                             cand_stride, logits_out, logits_stride,
+                                             (uint32_t *)workspace, g_timing,
+                                             (hipStream_t)stream),
+                         "publish launch")))
+        return rc;
+    return ok();
+}
+
 int idx_gather_k_workspace(const idx_config *cfg, const idx_kcache *k, int32_t num_reqs,
                            const int32_t *cu_seq_lens, const int32_t *req_table,
                            int32_t max_seq_len, int32_t max_tokens, uint8_t *values_out,

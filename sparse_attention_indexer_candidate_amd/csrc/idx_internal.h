@@ -126,6 +126,22 @@ hipError_t launch_score_dense(int q_format, int score_format, const Rows &rows, 
                               const KCache &k, float *logits, int64_t logits_stride,
                               const Timing &timing, hipStream_t stream);
 
+// The candidate-source layer's publication: every token of [ks, ke) of each row scored
+// (logits optional: null, or [rows][logits_stride] with -inf outside [ks, ke)), blocks of
+// cbs tokens scored by their largest logit, the nb best blocks written to cand [rows]
+// [cand_stride] ascending, then -1.  parts: scratch of rows * publish_parts_per_row
+// uint32.  Requires ceil(max_ctx / cbs) <= kMaxPublishBlocks and nb <= 512.
+constexpr int kMaxPublishBlocks = 4096;
+inline int64_t publish_parts_per_row(int32_t max_ctx, int32_t cbs) {
+    const int64_t p = cbs >= 64 ? 64 : cbs;
+    return ((int64_t)max_ctx + 63) / 64 * (64 / p);
+}
+hipError_t launch_publish(int q_format, int score_format, const Rows &rows, int32_t max_ctx,
+                          const void *q_values, const void *q_scales, const void *weights,
+                          const KCache &k, int32_t cbs, int32_t nb, int32_t *cand,
+                          int64_t cand_stride, float *logits, int64_t logits_stride,
+                          uint32_t *parts, const Timing &timing, hipStream_t stream);
+
 // Per-row top-k over the dense logits (tokens masked to the schedule's blocks).
 hipError_t launch_dense_topk(const Rows &rows, const KCache &k, const Schedule &s,
                              const float *logits, int64_t logits_stride, int32_t ncols,

@@ -411,3 +411,33 @@ def test_bf16_weights_alignment_is_checked():
             with pytest.raises(idx.IdxError) as e:
                 call()
             assert e.value.code == idx.IDX_EINVAL and "8-byte" in str(e.value)
+
+
+def test_publish_call_checks_arguments_and_sizes():
+    """idx_publish_candidates: every bad argument is rejected on the host; zero rows launch
+    nothing; the workspace holds one uint32 per part of min(cbs, 64) tokens a row."""
+    c = cfg(num_candidate_blocks=64, topk=64)
+    idx.idx_check_config(c)
+    assert idx.idx_publish_workspace_bytes(c, 128, 65536) == 128 * 1024 * 4
+    c16 = cfg(candidate_block_size=16, num_candidate_blocks=64, topk=64)
+    idx.idx_check_config(c16)
+    assert idx.idx_publish_workspace_bytes(c16, 2, 100) == 2 * 2 * 4 * 4
+    k = idx.idx_kcache(FAKE, 64 * 64, FAKE, 64 * 4, 10, FAKE, 4, 1, 4)
+    rows0 = idx.idx_rows(0, None, FAKE, None)
+    rows4 = idx.idx_rows(4, None, FAKE, None)
+
+    def call(rows=rows0, max_ctx=4096, cand=FAKE, stride=64, lout=None, lstride=0,
+             ws=FAKE, wsb=1 << 20, w=FAKE):
+        return idx.idx_publish_candidates(c, rows, max_ctx, FAKE, FAKE, w, k, cand, stride,
+                                          lout, lstride, ws, wsb)
+    assert call() == idx.IDX_OK
+    for kw, code in [(dict(max_ctx=0), idx.IDX_EUNSUPPORTED),
+                     (dict(max_ctx=4096 * 64 + 1), idx.IDX_EUNSUPPORTED),
+                     (dict(cand=None), idx.IDX_EINVAL), (dict(stride=63), idx.IDX_EINVAL),
+                     (dict(lout=FAKE, lstride=100), idx.IDX_EINVAL),
+                     (dict(rows=rows4, ws=None), idx.IDX_EWORKSPACE),
+                     (dict(rows=rows4, wsb=4 * 64 * 4 - 4), idx.IDX_EWORKSPACE),
+                     (dict(w=None), idx.IDX_EINVAL)]:
+        with pytest.raises(idx.IdxError) as e:
+            call(**kw)
+        assert e.value.code == code, kw

@@ -43,3 +43,15 @@ def test_more_than_one_gpu_is_refused_with_a_message():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_source_bytes_by_hand():
+    case = W.generate(W.config(1), 0)          # 4 rows, cbs 64, 16 blocks published a row
+    case.row_ks[:] = [0, 10, 0, 0]
+    case.row_ke[:] = [4096, 4096, 100, 0]
+    ctx = 4096 + 4086 + 100 + 0
+    parts = 4096 // 64                          # one part key a 64-token part of max_ctx
+    row = 64 * 68 + 64 * 4 + 2 * 4 * parts + 4 * 16
+    assert bench.source_bytes(case, "mxfp4", 4096) == ctx * 68 + 4 * row
+    # bf16 weights: 2 bytes a head
+    assert bench.source_bytes(case, "mxfp4", 4096, "bf16") == ctx * 68 + 4 * (row - 64 * 2)
