@@ -1546,11 +1546,14 @@ __device__ __forceinline__ int pick(const int (&a)[N], int i) {
     return v;
 }
 
-template <int NCMAX, int GR>
+// SF: the scoring format (0 fp32, 1 bf16), a template parameter here because this kernel
+// is bound by its vector ALU work (the fp32 form carries no rounding instructions).
+template <int NCMAX, int GR, int SF>
 __device__ __forceinline__ void row_group_rows(
     GroupLds<NCMAX, GR> &lds, const Rows &rows, const void *qv, const void *qs,
     const void *weights, const KCache &k, const Schedule &s, float *logits_out, int32_t topk,
-    int32_t *out, int64_t ostride, int sf) {
+    int32_t *out, int64_t ostride) {
+    constexpr int sf = SF;
     static_assert(GR >= 1 && GR <= kGroupWaves, "a wave selects each row");
     static_assert(64 % (NCMAX / kGroupThreads) == 0, "a thread's keys lie in one sparse block");
     using L = GroupLds<NCMAX, GR>;
@@ -1713,7 +1716,10 @@ __device__ __forceinline__ void row_group_rows(
                 __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             }
-            const bool valid = tok >= ks[r] && tok < ke[r];
+            // the block's 64 tokens all lie in [ks, ke) except in a row's first and last
+            // kept blocks (uniform test), so the per-column test is mostly skipped
+            const bool full = e.x * 64 >= ks[r] && e.x * 64 + 64 <= ke[r];
+            const bool valid = full || (tok >= ks[r] && tok < ke[r]);
             const int c = (int)slot * 64 + lane;
             lds.logit[r][c] = valid ? __float_as_uint(lg) : kNoColumn;
             if (logits_out) logits_out[(int64_t)(row0 + r) * ncols + c] = valid ? lg : -INFINITY;
@@ -1742,6 +1748,21 @@ __device__ __forceinline__ void row_group_rows(
     for (int r = 0; r < GR; ++r) {
         const int row = row0 + r;
         if (row >= rows.num_rows) break;
+        // The row's valid tokens are its kept blocks' tokens in column order (ascending),
+        // less those of the first block below ks and of the last block at or past ke (the
+        // kept blocks are ascending and each meets [ks, ke)).  When they number at most
+        // topk every one is chosen whatever its logit: write them straight out.
+        const int kr = pick(kept, r), ksr = pick(ks, r), ker = pick(ke, r);
+        const int lead = kr ? max(0, ksr - 64 * lds.si[r][0]) : 0;
+        const int trail = kr ? max(0, 64 * lds.si[r][kr - 1] + 64 - ker) : 0;
+        const int nvalid = kr * 64 - lead - trail;
+        if (nvalid <= topk) {
+            int32_t *orow = out + (int64_t)row * ostride;
+            for (int c = lead + tid; c < kr * 64 - trail; c += kGroupThreads)
+                orow[c - lead] = lds.si[r][c >> 6] * 64 + (c & 63);
+            for (int i = max(nvalid, 0) + tid; i < topk; i += kGroupThreads) orow[i] = -1;
+            continue;
+        }
         select_clear(lds.u.sel);
         // KPT divides 64, so a thread's columns are all below the row's scored columns
         // (kept blocks of 64) or all above them (stale LDS, read but not used)
@@ -1768,28 +1789,28 @@ __device__ __forceinline__ void row_group_rows(
     }
 }
 
-template <int NCMAX, int GR>
+template <int NCMAX, int GR, int SF>
 __global__ __launch_bounds__(kGroupThreads) void row_group_kernel(
     Rows rows, const void *qv, const void *qs, const void *weights, KCache k, Schedule s,
-    float *logits_out, int32_t topk, int32_t *out, int64_t ostride, int32_t sf) {
+    float *logits_out, int32_t topk, int32_t *out, int64_t ostride) {
     __shared__ GroupLds<NCMAX, GR> lds;
-    row_group_rows<NCMAX, GR>(lds, rows, qv, qs, weights, k, s, logits_out, topk, out, ostride,
-                              sf);
+    row_group_rows<NCMAX, GR, SF>(lds, rows, qv, qs, weights, k, s, logits_out, topk, out,
+                                  ostride);
 }
 
 // Several layers of a prefill chunk sharing one schedule, one launch (grid.y = layer):
 // each layer's groups go heaviest first, and the next layer's heavy groups fill the CUs
 // that the previous layer's light ones leave.
-template <int NCMAX, int GR>
+template <int NCMAX, int GR, int SF>
 __global__ __launch_bounds__(kGroupThreads) void row_group_layers_kernel(
-    Rows rows, KCache k, Schedule s, LayerSet ls, int32_t topk, int64_t ostride, int32_t sf) {
+    Rows rows, KCache k, Schedule s, LayerSet ls, int32_t topk, int64_t ostride) {
     __shared__ GroupLds<NCMAX, GR> lds;
     const int l = blockIdx.y;
     KCache kl = k;
     kl.values = ls.k_values[l];
     kl.scales = ls.k_scales[l];
-    row_group_rows<NCMAX, GR>(lds, rows, ls.q_values[l], ls.q_scales[l], ls.weights[l], kl, s,
-                              ls.logits_out[l], topk, ls.out[l], ostride, sf);
+    row_group_rows<NCMAX, GR, SF>(lds, rows, ls.q_values[l], ls.q_scales[l], ls.weights[l], kl,
+                                  s, ls.logits_out[l], topk, ls.out[l], ostride);
 }
 
 
@@ -1956,12 +1977,17 @@ static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const 
         constexpr int GR = 2;
         if (plan == kPlanRowGroup) {
             const dim3 grid((rows.num_rows + GR - 1) / GR);
-#define IDX_LAUNCH_GROUP(NC_)                                                                       \
-    hipExtLaunchKernelGGL((row_group_kernel<NC_, GR>), grid, dim3(kGroupThreads), 0, stream,        \
+#define IDX_LAUNCH_GROUP(NC_, SF_)                                                                  \
+    hipExtLaunchKernelGGL((row_group_kernel<NC_, GR, SF_>), grid, dim3(kGroupThreads), 0, stream,   \
                           timing.start, timing.stop, 0, rows, q_values, q_scales, weights, k, s,   \
-                          logits_out, topk, out, out_stride, sf)
-            if (ncols <= 4096) IDX_LAUNCH_GROUP(4096);
-            else IDX_LAUNCH_GROUP(8192);
+                          logits_out, topk, out, out_stride)
+            if (ncols <= 4096) {
+                if (sf) IDX_LAUNCH_GROUP(4096, 1);
+                else IDX_LAUNCH_GROUP(4096, 0);
+            } else {
+                if (sf) IDX_LAUNCH_GROUP(8192, 1);
+                else IDX_LAUNCH_GROUP(8192, 0);
+            }
 #undef IDX_LAUNCH_GROUP
             return hipGetLastError();
         }
@@ -2085,14 +2111,17 @@ hipError_t launch_sparse_layers(int q_format, int score_format, const Rows &rows
     if (plan == kPlanRowGroupLayers) {
         constexpr int GR = 2;
         const dim3 grid((rows.num_rows + GR - 1) / GR, num_layers);
-        if (ncols <= 4096)
-            hipExtLaunchKernelGGL((row_group_layers_kernel<4096, GR>), grid, dim3(kGroupThreads), 0,
-                                  stream, timing.start, timing.stop, 0, rows, k, s, layers, topk,
-                                  out_stride, sf);
-        else
-            hipExtLaunchKernelGGL((row_group_layers_kernel<8192, GR>), grid, dim3(kGroupThreads), 0,
-                                  stream, timing.start, timing.stop, 0, rows, k, s, layers, topk,
-                                  out_stride, sf);
+#define IDX_LAUNCH_GROUP_LAYERS(NC_, SF_)                                                          \
+    hipExtLaunchKernelGGL((row_group_layers_kernel<NC_, GR, SF_>), grid, dim3(kGroupThreads), 0,     \
+                          stream, timing.start, timing.stop, 0, rows, k, s, layers, topk, out_stride)
+        if (ncols <= 4096) {
+            if (sf) IDX_LAUNCH_GROUP_LAYERS(4096, 1);
+            else IDX_LAUNCH_GROUP_LAYERS(4096, 0);
+        } else {
+            if (sf) IDX_LAUNCH_GROUP_LAYERS(8192, 1);
+            else IDX_LAUNCH_GROUP_LAYERS(8192, 0);
+        }
+#undef IDX_LAUNCH_GROUP_LAYERS
         return hipGetLastError();
     }
     if (plan == kPlanSplitLayers) {
