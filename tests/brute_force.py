@@ -101,11 +101,12 @@ def dense_logits(case, r, layer=0, q_format="mxfp4", pool=None, score_format="fp
     S = Q @ K.T                                  # [H, ke], exact in fp64 for these inputs
     if q_format == "fp8":
         S = S * rs
-    relu = np.where(S > 0, S, 0.0)
+    relu = np.where((S > 0) | np.isnan(S), S, 0.0)   # ReLU passes NaN
     w = weights(L, r, score_format)
     acc = np.zeros(ke)
     for h in range(s.num_heads):                 # head sum in index order
         acc = acc + w[h] * relu[h]
+    acc = np.where(np.isnan(acc), -np.inf, acc)     # a NaN logit ranks as -inf
     if score_format == "bf16":
         return np.array([round_bf16_exact(float(v)) for v in acc], dtype=np.float32)
     return acc.astype(np.float32)

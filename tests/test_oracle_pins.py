@@ -201,6 +201,31 @@ def test_closed_form_constant_inputs_give_1024():
         L.q_values[:] = 0x22
 
 
+def test_nan_scale_bytes_give_minus_inf_logits():
+    # UE8M0 0xFF is NaN: a token whose K scale block is NaN has a NaN dot on every head;
+    # ReLU passes it, the sum is NaN and the logit is -inf, the lowest rank (ties with
+    # other -inf logits toward the lower token).  Constant inputs otherwise: 1024 each.
+    case = _one_row_case(H=64, D=128, topk=16)
+    L = case.layers[0]
+    L.q_values[:] = 0x22
+    L.weights[:] = 1.0 / 8.0
+    for t in range(16):
+        _set_k(case, t, 0x11, np.array([128, 255 if t in (3, 9) else 128, 128, 128], np.uint8))
+    res = oracle.indexer_rows(case)
+    want = np.full(16, 1024.0, np.float32)
+    want[[3, 9]] = -np.inf
+    np.testing.assert_array_equal(res.row_logits(0), want)
+    case.spec = W.Spec(**{**case.spec.__dict__, "topk": 15})
+    res = oracle.indexer_rows(case)
+    np.testing.assert_array_equal(res.indices[0], [t for t in range(16) if t != 9])
+    # a NaN Q scale byte on one head: every dot of that head is NaN, every logit -inf, so
+    # the lowest tokens win
+    L.q_scales[0, 5, 2] = 255
+    res = oracle.indexer_rows(case)
+    assert np.all(res.row_logits(0) == -np.inf)
+    np.testing.assert_array_equal(res.indices[0], list(range(15)))
+
+
 def test_closed_form_weights_are_per_head():
     # Only head 3 is positive: logit = w[3] * 128 whatever the other weights are.
     case = _one_row_case(H=8, D=128, topk=16)
