@@ -57,8 +57,10 @@
  *    the number of valid tokens (backend page: num_sparse_blocks computed in
  *    the builder __init__; SparseMQARowsMetadata.sparse_indices / .end).
  *
- * NaN inputs (the pages say nothing of them): ReLU passes a NaN dot product
- * through, as PyTorch's relu does, and a NaN logit ranks as -inf.
+ * NaN inputs (the pages say nothing of them): ReLU maps a NaN dot product (from
+ * a UE8M0 scale byte 0xFF or an e4m3 NaN code) to 0, as C's fmax and IEEE 754
+ * maxNum do, so it contributes nothing; a NaN logit (a NaN or infinite weight)
+ * ranks as -inf.
  *
  * Points the pages leave open are read as follows, each restated where used:
  * negative candidate ids are padding, repeated ids count once, element 2i of a
@@ -302,16 +304,16 @@ static double row_logit(int H, int D, const double *q, const double *k, const do
             dot += q[h * D + d] * k[d];
         if (q_format == ORC_Q_FP8)
             dot *= rowscale;
-        double relu = (dot > 0.0 || isnan(dot)) ? dot : 0.0;   /* ReLU passes NaN */
+        double relu = dot > 0.0 ? dot : 0.0;   /* ReLU(NaN) = 0 */
         acc += w[h] * relu;
     }
     return acc;
 }
 
 /* The logit the selection sees: the fp64 sum rounded once, to fp32 (round to
- * nearest even) or, in the bf16 variant, to the nearest bf16.  A NaN sum (a NaN
- * scale byte, 0xFF in UE8M0, or a NaN e4m3 code in its inputs) becomes -inf: it
- * ranks below every number and ties with -inf toward the lower token. */
+ * nearest even) or, in the bf16 variant, to the nearest bf16.  A NaN sum (a NaN or
+ * infinite weight) becomes -inf: it ranks below every number and ties with -inf
+ * toward the lower token. */
 static float final_logit(double acc, int score_format)
 {
     if (isnan(acc))

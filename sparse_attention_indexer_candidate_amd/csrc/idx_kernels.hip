@@ -402,8 +402,14 @@ __device__ __forceinline__ float round_bf16(float x) {
     return __uint_as_float((u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u);
 }
 
-// The logit the selection sees: fp32 (sf = 0) or rounded to bf16 (sf = 1).
-__device__ __forceinline__ float score_out(int sf, float x) { return sf ? round_bf16(x) : x; }
+// The logit the selection sees: fp32 (sf = 0) or rounded to bf16 (sf = 1); a NaN (a NaN
+// or infinite weight) becomes -inf, the lowest rank.  So every logit that reaches a
+// selection is a number, and the column word kNoColumn (a NaN pattern) can only mean
+// "no column".
+__device__ __forceinline__ float score_out(int sf, float x) {
+    x = __builtin_isnan(x) ? -INFINITY : x;
+    return sf ? round_bf16(x) : x;
+}
 
 // Weights of the lane's 16 heads: fp32 (sf = 0) or bf16 codes (sf = 1), each lane's 4
 // consecutive heads read as two 8-byte loads issued whatever the format (no load behind
@@ -435,7 +441,10 @@ __device__ __forceinline__ void load_q(QFrag<QF> &f, const void *qv, const void 
 
 // ReLU as one integer max on the float's bits: negative values (and -0) have the
 // sign bit set, so they become +0; non-negative values pass unchanged.  (fmaxf would
-// cost a second instruction to quiet NaN inputs.)
+// cost a second instruction to quiet NaN inputs.)  A NaN dot product (a NaN scale byte
+// or e4m3 code among its inputs) comes out of the matrix cores with the sign bit set
+// (measured on both the MX-FP4 and the bf16 MFMA), so it becomes 0, the ReLU(NaN) = 0
+// rule of the oracle.
 __device__ __forceinline__ float relu(float x) {
     return __int_as_float(max(__float_as_int(x), 0));
 }
@@ -470,8 +479,10 @@ __device__ __forceinline__ float tile_partial(const QFrag<0> &f, const KTile &k)
 }
 
 __device__ __forceinline__ float tile_partial(const QFrag<1> &f, const KTile &k) {
-    // 2^(sc - 127) as fp32 (sc = 0 is the subnormal 2^-127)
-    const float scale = __uint_as_float(k.sc == 0 ? 0x00400000u : (uint32_t)k.sc << 23);
+    // 2^(sc - 127) as fp32 (sc = 0 is the subnormal 2^-127; 0xFF is NaN in UE8M0, as the
+    // MX-scaled MFMA of the MXFP4 path reads it)
+    const float scale = __uint_as_float(k.sc == 0 ? 0x00400000u
+                                        : k.sc == 0xFF ? 0x7FC00000u : (uint32_t)k.sc << 23);
     const uint32_t d[4] = {k.v.x, k.v.y, k.v.z, k.v.w};
     v8bf b[4];
 #pragma unroll

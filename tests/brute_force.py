@@ -101,7 +101,7 @@ def dense_logits(case, r, layer=0, q_format="mxfp4", pool=None, score_format="fp
     S = Q @ K.T                                  # [H, ke], exact in fp64 for these inputs
     if q_format == "fp8":
         S = S * rs
-    relu = np.where((S > 0) | np.isnan(S), S, 0.0)   # ReLU passes NaN
+    relu = np.where(S > 0, S, 0.0)                  # ReLU(NaN) = 0
     w = weights(L, r, score_format)
     acc = np.zeros(ke)
     for h in range(s.num_heads):                 # head sum in index order

@@ -872,3 +872,56 @@ def test_bf16_scoring_dense_equals_sparse():
                                      g.sched.struct, dout, dout.stride(0), dlog, dlog.stride(0))
     torch.cuda.synchronize()
     np.testing.assert_array_equal(dout.cpu().numpy(), res["indices"], err_msg="dense != sparse")
+
+
+# ---------------------------------------------------------------- NaN inputs ------
+# One rule on both sides: a NaN scale byte (UE8M0 0xFF) or e4m3 code makes a NaN dot
+# product, which ReLU maps to 0 (the matrix cores return NaN with the sign bit set, and
+# the kernels' ReLU is an integer max); a NaN logit (a NaN weight) ranks as -inf (lowest,
+# ties toward the lower token), so the selection's counts and keys always agree.
+
+def _with_nan_inputs(case, q_format, seed):
+    """A copy of the case with K scale byte 0xFF on ~1 % of every row's candidate tokens,
+    a NaN query element on one head of row 0 and a NaN weight on row 1."""
+    import dataclasses
+
+    rng = np.random.default_rng(seed)
+    s = case.spec
+    L = case.layers[0]
+    data = L.filled_data.copy()
+    for r in range(case.num_rows):
+        toks = oracle.candidate_tokens(case.candidate_blocks[r], s.cbs, int(case.row_ks[r]),
+                                       int(case.row_ke[r]))
+        for t in rng.choice(toks, size=max(1, toks.size // 100), replace=False) if toks.size else []:
+            page = case.block_table[case.row_table[r], t // s.page_size]
+            i = int(np.searchsorted(L.filled_pages, page))
+            data[i, s.values_bytes + (t % s.page_size) * (s.head_dim // 32) + int(rng.integers(4))] = 0xFF
+    w = L.weights.copy()
+    w[1, 33] = np.nan
+    kw = dict(filled_data=data, weights=w)
+    if q_format == "mxfp4":
+        qs = L.q_scales.copy()
+        qs[0, 7, 1] = 0xFF
+        kw["q_scales"] = qs
+    else:
+        q8 = L.q_fp8.copy()
+        q8[0, 7, 40] = 0x7F          # e4m3fn S.1111.111: NaN
+        kw["q_fp8"] = q8
+    return dataclasses.replace(case, layers=[dataclasses.replace(L, **kw)] + case.layers[1:])
+
+
+@pytest.mark.parametrize("q_format", ["mxfp4", "fp8"])
+@pytest.mark.parametrize("path", sorted(WEIGHT_PATHS))
+def test_nan_scale_bytes_follow_the_nan_rule(path, q_format):
+    import dataclasses
+
+    spec = WEIGHT_PATHS[path]
+    if q_format == "fp8":
+        if path == "rowgroup":
+            pytest.skip("row groups serve MXFP4 queries only")
+        spec = dataclasses.replace(spec, q_formats=("mxfp4", "fp8"))
+    case = _with_nan_inputs(W.generate(spec, seed=19), q_format, seed=23)
+    g, res = run_and_compare(case, q_format=q_format, tag=f"nan-{path}-{q_format}")
+    # row 1: every logit -inf (its NaN weight), so its lowest tokens win
+    ora = oracle.indexer_rows(case, 0, np.array([1], np.int32), q_format)
+    assert np.all(ora.row_logits(0) == -np.inf)

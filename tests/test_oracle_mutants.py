@@ -16,9 +16,9 @@ SRC = os.path.join(ROOT, "oracle", "oracle.c")
 
 MUTANTS = {
     "nibble_order": ("return (d & 1) ? (b >> 4) : (b & 15);", "return (d & 1) ? (b & 15) : (b >> 4);"),
-    "no_relu": ("double relu = (dot > 0.0 || isnan(dot)) ? dot : 0.0;", "double relu = dot;"),
-    "relu_drops_nan": ("double relu = (dot > 0.0 || isnan(dot)) ? dot : 0.0;",
-                       "double relu = dot > 0.0 ? dot : 0.0;"),
+    "no_relu": ("double relu = dot > 0.0 ? dot : 0.0;", "double relu = dot;"),
+    "relu_keeps_nan": ("double relu = dot > 0.0 ? dot : 0.0;",
+                       "double relu = (dot > 0.0 || isnan(dot)) ? dot : 0.0;"),
     "nan_logit_kept": ("    if (isnan(acc))\n        return -INFINITY;\n", ""),
     "e2m1_subnormal": ("(e == 0) ? 0.5 * m", "(e == 0) ? 1.0 * m"),
     "e2m1_bias": ("ldexp(1.0 + 0.5 * m, e - 1)", "ldexp(1.0 + 0.5 * m, e)"),

@@ -201,10 +201,11 @@ def test_closed_form_constant_inputs_give_1024():
         L.q_values[:] = 0x22
 
 
-def test_nan_scale_bytes_give_minus_inf_logits():
-    # UE8M0 0xFF is NaN: a token whose K scale block is NaN has a NaN dot on every head;
-    # ReLU passes it, the sum is NaN and the logit is -inf, the lowest rank (ties with
-    # other -inf logits toward the lower token).  Constant inputs otherwise: 1024 each.
+def test_nan_rules():
+    # UE8M0 0xFF is NaN: a token whose K scale block is NaN has a NaN dot on every head,
+    # ReLU maps each to 0, so its logit is 0; a NaN Q scale block on head 5 removes that
+    # head from every token (1024 - 16 = 1008 with the constant inputs below).  A NaN
+    # weight makes every logit NaN, which ranks as -inf: the lowest tokens win.
     case = _one_row_case(H=64, D=128, topk=16)
     L = case.layers[0]
     L.q_values[:] = 0x22
@@ -213,17 +214,19 @@ def test_nan_scale_bytes_give_minus_inf_logits():
         _set_k(case, t, 0x11, np.array([128, 255 if t in (3, 9) else 128, 128, 128], np.uint8))
     res = oracle.indexer_rows(case)
     want = np.full(16, 1024.0, np.float32)
-    want[[3, 9]] = -np.inf
+    want[[3, 9]] = 0.0
     np.testing.assert_array_equal(res.row_logits(0), want)
-    case.spec = W.Spec(**{**case.spec.__dict__, "topk": 15})
+    case.spec = W.Spec(**{**case.spec.__dict__, "topk": 14})
     res = oracle.indexer_rows(case)
-    np.testing.assert_array_equal(res.indices[0], [t for t in range(16) if t != 9])
-    # a NaN Q scale byte on one head: every dot of that head is NaN, every logit -inf, so
-    # the lowest tokens win
+    np.testing.assert_array_equal(res.indices[0], [t for t in range(16) if t not in (3, 9)])
     L.q_scales[0, 5, 2] = 255
     res = oracle.indexer_rows(case)
+    want[[t for t in range(16) if t not in (3, 9)]] = 1008.0
+    np.testing.assert_array_equal(res.row_logits(0), want)
+    L.weights[0, 11] = np.nan
+    res = oracle.indexer_rows(case)
     assert np.all(res.row_logits(0) == -np.inf)
-    np.testing.assert_array_equal(res.indices[0], list(range(15)))
+    np.testing.assert_array_equal(res.indices[0], list(range(14)))
 
 
 def test_closed_form_weights_are_per_head():
