@@ -395,6 +395,15 @@ int idx_gather_k_workspace(const idx_config *cfg, const idx_kcache *k, int32_t n
  *   call performs (host). */
 #define IDX_MEASURE_WGS 4096
 int idx_measure_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
+/* idx_measure_fp8_dot: the two ways to form the fp8-query dot products, for the record
+ *   of why the fp8 path converts to bf16 (an accuracy check, not a rate): 16 query rows
+ *   of e4m3 codes (q_e4m3 u8 [16][128], device) against 16 tokens of e2m1 codes with UE8M0
+ *   block scales (k_e2m1 u8 [16][64] packed, k_scales u8 [16][4], device) -> out fp32
+ *   [16 rows][16 tokens] (device).  mode 0: the MX-scaled fp8 x fp4 MFMA on the codes;
+ *   mode 1: both operands converted exactly to bf16 and the bf16 MFMA, as the fp8-query
+ *   scoring kernels do.  One wave; IDX_EINVAL on a bad argument. */
+int idx_measure_fp8_dot(const uint8_t *q_e4m3, const uint8_t *k_e2m1, const uint8_t *k_scales,
+                        int32_t mode, float *out, void *stream);
 int idx_measure_mfma(int32_t iters, float *sink, void *stream);
 int64_t idx_measure_mfma_flops(int32_t iters);
 

@@ -34,7 +34,8 @@ EXPORTED = ("idx_check_config", "idx_num_sparse_blocks", "idx_schedule_work_byte
             "idx_sparse_mqa_logits_topk_layers", "idx_dense_masked_logits_topk",
             "idx_gather_k_workspace", "idx_sparse_plan", "idx_sparse_mqa_logits_topk_noalloc",
             "idx_publish_workspace_bytes", "idx_publish_candidates",
-            "idx_measure_read", "idx_measure_mfma", "idx_measure_mfma_flops")
+            "idx_measure_read", "idx_measure_mfma", "idx_measure_mfma_flops",
+            "idx_measure_fp8_dot")
 IDX_MEASURE_WGS = 4096
 IDX_MAX_LAYERS = 8
 IDX_NOALLOC_SCRATCH_BYTES = 8 << 20
@@ -151,6 +152,8 @@ def _load():
     L.idx_measure_read.restype = ctypes.c_int
     L.idx_measure_mfma.argtypes = [i32, vp, vp]
     L.idx_measure_mfma.restype = ctypes.c_int
+    L.idx_measure_fp8_dot.argtypes = [vp, vp, vp, i32, vp, vp]
+    L.idx_measure_fp8_dot.restype = ctypes.c_int
     L.idx_measure_mfma_flops.argtypes = [i32]
     L.idx_measure_mfma_flops.restype = i64
     return L
@@ -340,6 +343,13 @@ def idx_measure_read(src, nbytes, sink, stream=None):
 def idx_measure_mfma(iters, sink, stream=None):
     """Reference MX-FP4 MFMA loop; sink: IDX_MEASURE_WGS * 4 floats."""
     return _check(lib.idx_measure_mfma(iters, _p(sink), _p(stream)))
+
+
+def idx_measure_fp8_dot(q_e4m3, k_e2m1, k_scales, mode, out, stream=None):
+    """16 x 16 e4m3 . (e2m1 x UE8M0) dot products into out (fp32 [16, 16], device):
+    mode 0 the MX-scaled fp8 x fp4 MFMA, mode 1 the exact bf16 route of the kernels."""
+    return _check(lib.idx_measure_fp8_dot(_p(q_e4m3), _p(k_e2m1), _p(k_scales), mode, _p(out),
+                                          _p(stream)))
 
 
 def idx_measure_mfma_flops(iters) -> int:

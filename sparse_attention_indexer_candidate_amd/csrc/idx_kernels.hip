@@ -1904,6 +1904,60 @@ __global__ __launch_bounds__(kGatherThreads) void gather_k_kernel(
     if (part == 0) *reinterpret_cast<uint32_t *>(scales_out + dst * (kHeadDim / 32)) = sc;
 }
 
+// The two ways of forming e4m3 x (e2m1 with UE8M0 block scales) dot products over 128
+// dimensions, for 16 query rows against 16 tokens, one wave: (mode 0) the MX-scaled
+// v_mfma_scale_f32_16x16x128_f8f6f4 on the raw codes (query scale bytes 127), and (mode 1)
+// the fp8-query kernels' route: both operands converted exactly to bf16 (the token's
+// scale applied in the conversion) and v_mfma_f32_16x16x32_bf16.  q: e4m3 [16][128];
+// kv: packed e2m1 [16][64]; ks: UE8M0 [16][4]; out: fp32 [16 rows][16 tokens].
+__global__ __launch_bounds__(kWave) void measure_fp8_dot_kernel(const uint8_t *q,
+                                                                const uint8_t *kv,
+                                                                const uint8_t *ks, int32_t mode,
+                                                                float *out) {
+    const int lane = threadIdx.x, n = lane & 15, g = lane >> 4;
+    // B: token n, dimensions [32g, 32g + 32) as 16 bytes, and their scale byte
+    const uint4 kb = *(const uint4 *)(kv + n * 64 + 16 * g);
+    const int ksc = ks[n * 4 + g];
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (mode == 0) {
+        // A: row n, bytes j < 16 -> dimension 16g + j, bytes j >= 16 -> 64 + 16g + j - 16
+        const uint4 a0 = *(const uint4 *)(q + n * 128 + 16 * g);
+        const uint4 a1 = *(const uint4 *)(q + n * 128 + 64 + 16 * g);
+        const v8i a = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                          (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+        const v8i b = v8i{(int)kb.x, (int)kb.y, (int)kb.z, (int)kb.w, 0, 0, 0, 0};
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 4, 0, 127, 0, ksc);
+    } else {
+        // A: row n, dimensions [32g, 32g + 32) as bf16 (the bf16 MFMA's k slot of step s,
+        // lane group g, element j carries dimension 32g + 8s + j, as in load_q)
+        const uint8_t *pq = q + n * 128 + 32 * g;
+        const uint4 x = *(const uint4 *)pq, y = *(const uint4 *)(pq + 16);
+        const uint32_t dq[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+        v8bf qa[4];
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+            qa[st] = cat4(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(dq[2 * st], 1.0f, false),
+                          __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(dq[2 * st], 1.0f, true),
+                          __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(dq[2 * st + 1], 1.0f, false),
+                          __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(dq[2 * st + 1], 1.0f, true));
+        KTile kt{kb, ksc};
+        const float scale = __uint_as_float(ksc == 0 ? 0x00400000u
+                                            : ksc == 0xFF ? 0x7FC00000u : (uint32_t)ksc << 23);
+        const uint32_t d[4] = {kt.v.x, kt.v.y, kt.v.z, kt.v.w};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const v8bf b = cat4(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[st], scale, 0),
+                                __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[st], scale, 1),
+                                __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[st], scale, 2),
+                                __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[st], scale, 3));
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[st], b, acc, 0, 0, 0);
+        }
+    }
+    // C: lane holds token n, rows 4g + v
+#pragma unroll
+    for (int v = 0; v < 4; ++v) out[(4 * g + v) * 16 + n] = acc[v];
+}
+
 // Each wave: iters rounds of 8 independent v_mfma_scale_f32_16x16x128_f8f6f4 chains on
 // e2m1 operands held in registers (nonzero codes that differ by lane; scale bytes
 // 127), no memory traffic until one float per wave goes to sink.
@@ -2253,6 +2307,13 @@ hipError_t launch_gather_k(const KCache &k, int32_t num_reqs, const int32_t *cu_
 hipError_t launch_measure_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream) {
     hipLaunchKernelGGL(measure_read_kernel, dim3(kMeasureWgs), dim3(kMeasureThreads), 0, stream,
                        (const uint4 *)src, (int64_t)(bytes / 16), sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_measure_fp8_dot(const uint8_t *q, const uint8_t *kv, const uint8_t *ks,
+                                  int32_t mode, float *out, hipStream_t stream) {
+    hipLaunchKernelGGL(measure_fp8_dot_kernel, dim3(1), dim3(kWave), 0, stream, q, kv, ks, mode,
+                       out);
     return hipGetLastError();
 }
 

@@ -19,7 +19,7 @@ FAKE = 0x100000          # 16-byte aligned, never dereferenced
 def declared_functions():
     src = open(os.path.join(ROOT, "include", "idx.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(idx_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(idx_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_function():
@@ -311,6 +311,14 @@ def test_bound_calls_check_arguments_like_the_wrappers():
                                               FAKE, 2048, FAKE, 0)
     with pytest.raises(idx.IdxError):
         dense()
+
+
+def test_fp8_dot_measurement_rejects_bad_arguments():
+    for args in [(None, FAKE, FAKE, 0, FAKE), (FAKE, FAKE, FAKE, 2, FAKE),
+                 (FAKE + 4, FAKE, FAKE, 0, FAKE), (FAKE, FAKE, FAKE, 1, None)]:
+        with pytest.raises(idx.IdxError) as e:
+            idx.idx_measure_fp8_dot(*args)
+        assert e.value.code == idx.IDX_EINVAL
 
 
 def test_measurement_kernels_reject_bad_arguments_on_the_host():

@@ -925,3 +925,65 @@ def test_nan_scale_bytes_follow_the_nan_rule(path, q_format):
     # row 1: every logit -inf (its NaN weight), so its lowest tokens win
     ora = oracle.indexer_rows(case, 0, np.array([1], np.int32), q_format)
     assert np.all(ora.row_logits(0) == -np.inf)
+
+
+def test_fp8_query_products_need_the_bf16_route():
+    """Why fp8 queries go through bf16: the MX-scaled fp8 x fp4 MFMA adds its products in a
+    narrow adder.  Worked case: 448 + 2^-9 (e4m3 0x7E and 0x01 against e2m1 1.0) comes out
+    448 from it and exact from the bf16 route.  On random e4m3 / e2m1 data (the workloads'
+    encodings) the logits it gives miss the 1e-5 tolerance, the bf16 route's do not."""
+    import sparse_attention_indexer_candidate_amd as idx
+
+    def run(q, kv, ks):
+        outs = []
+        for mode in (0, 1):
+            out = torch.zeros((16, 16), dtype=torch.float32, device=DEV)
+            idx.idx_measure_fp8_dot(torch.from_numpy(q).to(DEV), torch.from_numpy(kv).to(DEV),
+                                    torch.from_numpy(ks).to(DEV), mode, out)
+            outs.append(out)
+        torch.cuda.synchronize()
+        return [o.cpu().numpy().astype(np.float64) for o in outs]
+
+    def exact(q, kv, ks):
+        e4 = np.array([oracle.e4m3fn(b) for b in range(256)])
+        e2 = np.array([oracle.e2m1(c) for c in range(16)])
+        qd = e4[q]                                                   # [16, 128]
+        kd = np.empty((16, 128))
+        kd[:, 0::2], kd[:, 1::2] = e2[kv & 15], e2[kv >> 4]
+        kd *= np.repeat(np.array([[oracle.ue8m0(int(b)) for b in r] for r in ks]), 32, axis=1)
+        terms = qd[:, None, :] * kd[None, :, :]                      # [row, token, d]
+        return terms.sum(-1), np.abs(terms).sum(-1)
+
+    q = np.zeros((16, 128), np.uint8)
+    kv = np.zeros((16, 64), np.uint8)
+    ks = np.full((16, 4), 127, np.uint8)
+    q[0, 0], q[0, 1] = 0x7E, 0x01                                    # 448, 2^-9
+    kv[0, 0] = 0x22                                                  # elements 0, 1: 1.0
+    mx, bf = run(q, kv, ks)
+    assert mx[0, 0] == 448.0, mx[0, 0]
+    assert bf[0, 0] == 448.0 + 2.0 ** -9, bf[0, 0]
+
+    # workload-shaped data: the fp8 query recipe (N(0,1), row scale max/448, e4m3 codes)
+    # for 16 heads, e2m1 K of N(0,1) with scales 2^[-4, 4]; 16 heads with U(0,1)/8 weights
+    # give each token's logit sum_h w_h ReLU(dot), checked against 1e-6 + 1e-5 |logit|
+    rng = np.random.default_rng(7)
+    spec = W.Spec(name="acc", num_rows=1, num_heads=16, head_dim=128, q_formats=("fp8",))
+    bad = {0: 0, 1: 0}
+    worst = {0: 0.0, 1: 0.0}
+    for trial in range(200):
+        q8, rs = W._draw_q_fp8(spec, rng)
+        q = np.ascontiguousarray(q8[0])
+        kv = W._e2m1_packed(rng, 16 * 128).reshape(16, 64)
+        ks = W._ue8m0_scales(rng, (16, 4), (-4, 4))
+        want, _ = exact(q, kv, ks)
+        w = rng.random(16) / 8.0
+        lw = (w[:, None] * np.maximum(want * rs[0], 0.0)).sum(0)
+        for mode, got in enumerate(run(q, kv, ks)):
+            lg = (w[:, None] * np.maximum(got * rs[0], 0.0)).sum(0)
+            err = np.abs(lg - lw)
+            bad[mode] += int((err > 1e-6 + 1e-5 * np.abs(lw)).sum())
+            worst[mode] = max(worst[mode], float(np.max(err / np.abs(lw))))
+    _say(f"[fp8 products] 3200 logits outside the tolerance: MX fp8 x fp4 {bad[0]} (worst "
+         f"relative error {worst[0]:.1e}), bf16 route {bad[1]} (worst {worst[1]:.1e})")
+    assert bad[1] == 0
+    assert bad[0] > 0
