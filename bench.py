@@ -167,12 +167,16 @@ def measured_peaks(stream) -> dict:
 
     t_read = timed(lambda: idx.idx_measure_read(buf, nbytes, sink, stream=stream.cuda_stream))
     t_mfma = timed(lambda: idx.idx_measure_mfma(iters, sink, stream=stream.cuda_stream))
+    t_relu = timed(lambda: idx.idx_measure_mfma_relu(iters // 4, sink,
+                                                      stream=stream.cuda_stream))
     del buf
     return {"read_gbs": nbytes / t_read / 1e9,
             "mxfp4_tflops": idx.idx_measure_mfma_flops(iters) / t_mfma / 1e12,
+            "mxfp4_relu_epilogue_tflops": idx.idx_measure_mfma_flops(iters // 4) / t_relu / 1e12,
             "how": "idx_measure_read over 2 GiB; idx_measure_mfma (8 independent MX-FP4 "
                    "16x16x128 MFMA chains a wave, 4096 x 256 threads, operands in registers); "
-                   "median of 5 launches timed with events"}
+                   "idx_measure_mfma_relu (the same MFMAs, each product through the ReLU-weight "
+                   "epilogue, 9 VALU operations per MFMA); median of 5 launches timed with events"}
 
 
 def gather_workload(case):
@@ -624,6 +628,16 @@ def roofline(m, config: int, q_format: str, peaks: dict, dense: bool) -> dict:
                                  "frac": lane_ops / avg_s / 1e12 / VALU_PEAK_TLANEOPS}
         roof["step_tflops"] = flops / m["launch_layers"] * spec.layers / step_s / 1e12
         roof["step_frac"] = roof["step_tflops"] / MXFP4_PEAK_TFLOPS
+        # The per-row byte count reads a request's K once per row; what must cross HBM is
+        # that K once per request (the longest row of each block table) plus the per-row
+        # query, weights, schedule and output.
+        case = m["case"]
+        per_col = spec.head_dim // 2 + spec.head_dim // 32
+        uniq_cols = sum(int(case.row_ke[case.row_table == t].max())
+                        for t in np.unique(case.row_table))
+        uniq_bytes = (m["kernel_bytes"] - int(m["ends"].astype(np.int64).sum()) * per_col
+                      + uniq_cols * per_col) * m["launch_layers"]
+        roof["unique_bytes_per_launch"] = uniq_bytes
     else:
         roof = {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
         # the whole step (expansion + every layer's launches) against the same peak
@@ -632,6 +646,10 @@ def roofline(m, config: int, q_format: str, peaks: dict, dense: bool) -> dict:
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["measured_peak"] = peaks["mxfp4_tflops"] if roof["bound"] == "mfma" else peaks["read_gbs"]
     roof["frac_of_measured"] = roof["achieved"] / roof["measured_peak"]
+    if roof["bound"] == "mfma":
+        # the MFMA rate left once the same SIMDs issue the ReLU-weight epilogue
+        roof["epilogue_ceiling"] = peaks["mxfp4_relu_epilogue_tflops"]
+        roof["frac_of_epilogue_ceiling"] = roof["achieved"] / roof["epilogue_ceiling"]
     roof.update({"traffic": traffic_for(m["kernel_name"], config, q_format),
                  "kernel": m["kernel_name"], "avg_launch_us": avg_s * 1e6,
                  "launch_us_p10": float(np.percentile(kernel_ms, 10)) * 1e3,
@@ -641,6 +659,9 @@ def roofline(m, config: int, q_format: str, peaks: dict, dense: bool) -> dict:
                            "timed steps",
                  "algorithmic_bytes_per_launch": launch_bytes, "hbm_gbs": achieved_gbs,
                  "mxfp4_tflops": flops / avg_s / 1e12})
+    if "unique_bytes_per_launch" in roof:
+        roof["operand_gbs"] = achieved_gbs
+        roof["hbm_gbs"] = roof["unique_bytes_per_launch"] / avg_s / 1e9
     return roof
 
 

@@ -392,7 +392,13 @@ int idx_gather_k_workspace(const idx_config *cfg, const idx_kcache *k, int32_t n
  *   v_mfma_scale_f32_16x16x128_f8f6f4 on e2m1 operands held in registers and writes
  *   one float per wave to sink (device, IDX_MEASURE_WGS * 4 floats);
  *   idx_measure_mfma_flops(iters) is the number of floating-point operations one
- *   call performs (host). */
+ *   call performs (host).
+ * idx_measure_mfma_relu: the same MFMA count as idx_measure_mfma, each product fresh
+ *   and folded through the ReLU-weight epilogue of the indexer score (an integer max
+ *   and an fp32 FMA per accumulator, 9 VALU operations per MFMA); it measures the MFMA
+ *   rate left once the vector ALUs issue that epilogue on the same SIMDs, the ceiling
+ *   of a scoring loop whose K tiles come from cache.  Same sink and flop count as
+ *   idx_measure_mfma. */
 #define IDX_MEASURE_WGS 4096
 int idx_measure_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
 /* idx_measure_fp8_dot: the two ways to form the fp8-query dot products, for the record
@@ -405,6 +411,7 @@ int idx_measure_read(const void *src, size_t bytes, uint32_t *sink, void *stream
 int idx_measure_fp8_dot(const uint8_t *q_e4m3, const uint8_t *k_e2m1, const uint8_t *k_scales,
                         int32_t mode, float *out, void *stream);
 int idx_measure_mfma(int32_t iters, float *sink, void *stream);
+int idx_measure_mfma_relu(int32_t iters, float *sink, void *stream);
 int64_t idx_measure_mfma_flops(int32_t iters);
 
 #ifdef __cplusplus

@@ -34,8 +34,8 @@ EXPORTED = ("idx_check_config", "idx_num_sparse_blocks", "idx_schedule_work_byte
             "idx_sparse_mqa_logits_topk_layers", "idx_dense_masked_logits_topk",
             "idx_gather_k_workspace", "idx_sparse_plan", "idx_sparse_mqa_logits_topk_noalloc",
             "idx_publish_workspace_bytes", "idx_publish_candidates",
-            "idx_measure_read", "idx_measure_mfma", "idx_measure_mfma_flops",
-            "idx_measure_fp8_dot")
+            "idx_measure_read", "idx_measure_mfma", "idx_measure_mfma_relu",
+            "idx_measure_mfma_flops", "idx_measure_fp8_dot")
 IDX_MEASURE_WGS = 4096
 IDX_MAX_LAYERS = 8
 IDX_NOALLOC_SCRATCH_BYTES = 8 << 20
@@ -152,6 +152,8 @@ def _load():
     L.idx_measure_read.restype = ctypes.c_int
     L.idx_measure_mfma.argtypes = [i32, vp, vp]
     L.idx_measure_mfma.restype = ctypes.c_int
+    L.idx_measure_mfma_relu.argtypes = [i32, vp, vp]
+    L.idx_measure_mfma_relu.restype = ctypes.c_int
     L.idx_measure_fp8_dot.argtypes = [vp, vp, vp, i32, vp, vp]
     L.idx_measure_fp8_dot.restype = ctypes.c_int
     L.idx_measure_mfma_flops.argtypes = [i32]
@@ -343,6 +345,12 @@ def idx_measure_read(src, nbytes, sink, stream=None):
 def idx_measure_mfma(iters, sink, stream=None):
     """Reference MX-FP4 MFMA loop; sink: IDX_MEASURE_WGS * 4 floats."""
     return _check(lib.idx_measure_mfma(iters, _p(sink), _p(stream)))
+
+
+def idx_measure_mfma_relu(iters, sink, stream=None):
+    """The MX-FP4 MFMA loop with the ReLU-weight epilogue on every product; sink as
+    idx_measure_mfma, same flop count."""
+    return _check(lib.idx_measure_mfma_relu(iters, _p(sink), _p(stream)))
 
 
 def idx_measure_fp8_dot(q_e4m3, k_e2m1, k_scales, mode, out, stream=None):

@@ -601,6 +601,16 @@ int idx_measure_mfma(int32_t iters, float *sink, void *stream) {
     return ok();
 }
 
+int idx_measure_mfma_relu(int32_t iters, float *sink, void *stream) {
+    if (iters < 1) return fail(IDX_EINVAL, "iters %d must be >= 1", iters);
+    if (!sink || !aligned(sink, 4)) return fail(IDX_EINVAL, "sink must be non-NULL and 4-byte aligned");
+    int rc;
+    if ((rc = hip_status(idx::launch_measure_mfma_relu(iters, sink, (hipStream_t)stream),
+                         "mfma relu launch")))
+        return rc;
+    return ok();
+}
+
 int idx_measure_fp8_dot(const uint8_t *q_e4m3, const uint8_t *k_e2m1, const uint8_t *k_scales,
                         int32_t mode, float *out, void *stream) {
     if (!q_e4m3 || !k_e2m1 || !k_scales || !out)

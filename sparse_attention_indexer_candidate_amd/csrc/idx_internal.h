@@ -157,6 +157,7 @@ hipError_t launch_gather_k(const KCache &k, int32_t num_reqs, const int32_t *cu_
 constexpr int kMeasureWgs = 4096;   // workgroups of 256 threads
 hipError_t launch_measure_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream);
 hipError_t launch_measure_mfma(int32_t iters, float *sink, hipStream_t stream);
+hipError_t launch_measure_mfma_relu(int32_t iters, float *sink, hipStream_t stream);
 hipError_t launch_measure_fp8_dot(const uint8_t *q, const uint8_t *kv, const uint8_t *ks,
                                   int32_t mode, float *out, hipStream_t stream);
 

@@ -24,8 +24,9 @@
 //                       the comparator: every token of [ks, ke) with the same
 //                       per-tile code, then the candidates' keys gathered from the
 //                       dense row in schedule order and the same selection
-//  measure_read_kernel, measure_mfma_kernel
-//                       reference rates for the roofline (read stream, MFMA-only loop)
+//  measure_read_kernel, measure_mfma_kernel, measure_mfma_relu_kernel
+//                       reference rates for the roofline (read stream, MFMA-only loop,
+//                       MFMA loop with the ReLU-weight epilogue)
 //
 // Kernel arguments: the expansion, split and one-row kernels take the pointers their
 // first loads need as leading scalar arguments, which gfx950 preloads into SGPRs at
@@ -1983,6 +1984,35 @@ __global__ __launch_bounds__(kMeasureThreads) void measure_mfma_kernel(int32_t i
     if (lane == 0) sink[blockIdx.x * (kMeasureThreads / kWave) + threadIdx.x / kWave] = t;
 }
 
+// The MFMA rate that the scoring epilogue leaves: the same 8 MX-FP4 MFMAs a round as
+// measure_mfma_kernel, each a fresh product (C = 0, the B operand bumped by one VALU add),
+// and every product's 4 accumulators folded through the ReLU-weight epilogue (an integer
+// max and an fp32 FMA each), 9 VALU operations per MFMA, as the prefill scoring loop
+// issues them.  Registers only; one float per wave goes to sink.
+__global__ __launch_bounds__(kMeasureThreads) void measure_mfma_relu_kernel(int32_t iters,
+                                                                           float *sink) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int x = 0x3A5C1E72 ^ (lane * 0x01030507) ^ iters;
+    const v8i a = v8i{x | 0x11111111, (x >> 3) | 0x22222222, (x << 5) | 0x11111111,
+                      x ^ 0x7F3E1D2C, 0, 0, 0, 0};
+    v8i b = v8i{(x * 7) | 0x11111111, x ^ 0x5A5A5A5A, (x >> 7) | 0x33333333,
+                (x * 13) | 0x21212121, 0, 0, 0, 0};
+    const float w[4] = {0.125f + lane * 1e-3f, 0.25f, -0.5f, 0.375f};
+    float p = 0.0f;
+    for (int it = 0; it < iters; ++it) {
+        v4f r[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            b[0] += 0x10;
+            r[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                a, b, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 4, 4, 0, 127, 0, 127);
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) p = relu_weighted(w, r[c], p);
+    }
+    if (lane == 0) sink[blockIdx.x * (kMeasureThreads / kWave) + threadIdx.x / kWave] = p;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- launchers ----
@@ -2320,6 +2350,12 @@ hipError_t launch_measure_fp8_dot(const uint8_t *q, const uint8_t *kv, const uin
 hipError_t launch_measure_mfma(int32_t iters, float *sink, hipStream_t stream) {
     hipLaunchKernelGGL(measure_mfma_kernel, dim3(kMeasureWgs), dim3(kMeasureThreads), 0, stream, iters,
                        sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_measure_mfma_relu(int32_t iters, float *sink, hipStream_t stream) {
+    hipLaunchKernelGGL(measure_mfma_relu_kernel, dim3(kMeasureWgs), dim3(kMeasureThreads), 0, stream,
+                       iters, sink);
     return hipGetLastError();
 }
 

@@ -334,6 +334,11 @@ def test_measurement_kernels_reject_bad_arguments_on_the_host():
     assert e.value.code == idx.IDX_EINVAL
     with pytest.raises(idx.IdxError):
         idx.idx_measure_mfma(16, None)
+    with pytest.raises(idx.IdxError) as e:
+        idx.idx_measure_mfma_relu(0, FAKE)
+    assert e.value.code == idx.IDX_EINVAL
+    with pytest.raises(idx.IdxError):
+        idx.idx_measure_mfma_relu(16, FAKE + 2)
     # waves x rounds x 8 chains x 16*16*128 multiply-adds x 2
     assert idx.idx_measure_mfma_flops(3) == idx.IDX_MEASURE_WGS * 4 * 3 * 8 * 16 * 16 * 128 * 2
 

@@ -987,3 +987,29 @@ def test_fp8_query_products_need_the_bf16_route():
          f"relative error {worst[0]:.1e}), bf16 route {bad[1]} (worst {worst[1]:.1e})")
     assert bad[1] == 0
     assert bad[0] > 0
+
+
+def test_measurement_kernels_run_and_read_every_word():
+    """The roofline's reference kernels: the read stream folds every 32-bit word of its
+    buffer into the per-workgroup XORs (checked against numpy), and both MFMA loops give
+    finite, repeatable sinks."""
+    import sparse_attention_indexer_candidate_amd as idx
+
+    rng = np.random.default_rng(5)
+    for nbytes in (1 << 20, (3 << 16) + 48):
+        host = rng.integers(0, 1 << 32, nbytes // 4, dtype=np.uint64).astype(np.uint32)
+        src = torch.from_numpy(host.view(np.uint8).copy()).to(DEV)
+        sink = torch.zeros(idx.IDX_MEASURE_WGS, dtype=torch.int32, device=DEV)
+        idx.idx_measure_read(src, nbytes, sink)
+        torch.cuda.synchronize()
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        assert got == np.bitwise_xor.reduce(host), nbytes
+    for fn in (idx.idx_measure_mfma, idx.idx_measure_mfma_relu):
+        outs = []
+        for _ in range(2):
+            sink = torch.full((idx.IDX_MEASURE_WGS * 4,), np.nan, dtype=torch.float32, device=DEV)
+            fn(3, sink)
+            torch.cuda.synchronize()
+            outs.append(sink.cpu().numpy())
+        assert np.all(np.isfinite(outs[0])), fn.__name__
+        np.testing.assert_array_equal(outs[0], outs[1], err_msg=fn.__name__)
