@@ -687,7 +687,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the prefill chunk's MX-FP4 roofline (reported beside the "
-                         "headline workload's)")
+                         "long-context decode workload's, the default)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--layers", type=int, default=0,
                     help="consuming layers a step (0: the workload's own); each layer gets its "
@@ -775,7 +775,7 @@ def main():
     }
     if dense:
         out["context_cols_per_s"] = ctx_cols_per_step * args.steps / elapsed
-    if not args.no_prefill and not dense and args.config != 3 and args.q_format == "mxfp4":
+    if not args.no_prefill and not dense and args.config == 4 and args.q_format == "mxfp4":
         # the prefill chunk (4096 rows of one request), whose bound is the MX-FP4 MFMA rate
         pm = run_workload(idx, W, 3, args, dev, stream, max(args.steps, 20), args.warmup)
         pr = roofline(pm, 3, args.q_format, peaks, False)

@@ -280,11 +280,12 @@ int idx_sparse_mqa_logits_topk_noalloc(const idx_config *cfg, const idx_rows *ro
  * layer fills is reused by the later ones, each with its own K cache, query and
  * weights).  Same result, layer by layer, as
  * calling idx_sparse_mqa_logits_topk once per layer in layer order.  With two or
- * more layers whose rows take the one-row-per-workgroup kernel (num_rows >= the
- * device's CUs, and not the prefill row-group case) all layers run in one launch
- * with two rows on a CU at a time, so one row's selection overlaps another's K
- * stream.  With two or more layers and fewer rows than CUs, every layer runs in one
- * split scoring launch and one selection launch when each layer's logits have a home:
+ * more layers whose row-layers take the one-row-per-workgroup kernel (num_rows *
+ * num_layers >= the device's CUs, and not the prefill row-group case) all layers run in
+ * one launch with two row-layers on a CU at a time, so one's selection overlaps
+ * another's K stream.  With two or more layers and fewer row-layers than CUs, every
+ * layer runs in one split scoring launch and one selection launch when each layer's
+ * logits have a home:
  * its logits_out, or its slice of a workspace of idx_workspace_bytes(cfg, num_layers *
  * num_rows, 0) bytes (layer l at l * num_rows * NB*cbs floats); with a smaller
  * workspace the layers run one after another.  A prefill chunk's rows (the row-group

@@ -2054,8 +2054,13 @@ Plan plan_sparse(int q_format, int32_t sbk, int32_t ncols, int32_t num_rows, int
     const bool groups = q_format == 0 && sbk == 64 && ncols <= 8192 && num_rows >= 8 * cus;
     if (groups) return num_layers >= 2 ? kPlanRowGroupLayers : kPlanRowGroup;
     if (num_rows >= cus) return num_layers >= 2 ? kPlanOneRowLayers : kPlanOneRow;
-    // fewer rows than CUs: every layer in one split launch pair when each layer's logits
-    // have a home, else layer by layer
+    // Fewer rows than CUs but at least as many row-layers: one workgroup a row-layer, all
+    // layers in one launch (measured 14-25 % faster steps than the split launch pair on
+    // 64- and 128-row decode batches with 2 to 8 layers, both query formats: the
+    // selection runs in the scoring launch and no logits leave it).
+    if (num_layers >= 2 && (int64_t)num_rows * num_layers >= cus) return kPlanOneRowLayers;
+    // otherwise every layer in one split launch pair when each layer's logits have a
+    // home, else layer by layer
     return num_layers >= 2 && logits_home ? kPlanSplitLayers : kPlanSplit;
 }
 

@@ -347,15 +347,19 @@ def test_sparse_plan_rule_on_the_host():
     """The launch plan for each row / layer count (host only: without a GPU the CU count
     query falls back to 256, the MI355X's).  The rule: MXFP4 queries, 64-token sparse
     blocks and >= 8 rows per CU take row groups; >= 1 row per CU one workgroup a row;
-    fewer rows split rows over workgroups, all layers in one launch pair only when every
-    layer's logits have a home."""
+    fewer rows but at least one row-layer per CU one workgroup a row-layer; fewer still
+    split rows over workgroups, all layers in one launch pair only when every layer's
+    logits have a home."""
     c = idx.make_config()
     cus = 256
     want = [
         (0, 1, False, idx.IDX_PLAN_NONE, ""),
         (64, 1, False, idx.IDX_PLAN_SPLIT, "score_split_kernel"),
-        (cus - 1, 4, True, idx.IDX_PLAN_SPLIT_LAYERS, "score_split_layers_kernel"),
-        (64, 4, False, idx.IDX_PLAN_SPLIT, "score_split_kernel"),
+        (cus - 1, 4, True, idx.IDX_PLAN_ONE_ROW_LAYERS, "fused_layers_kernel"),
+        (64, 4, False, idx.IDX_PLAN_ONE_ROW_LAYERS, "fused_layers_kernel"),
+        (32, 8, True, idx.IDX_PLAN_ONE_ROW_LAYERS, "fused_layers_kernel"),
+        (63, 4, True, idx.IDX_PLAN_SPLIT_LAYERS, "score_split_layers_kernel"),
+        (63, 4, False, idx.IDX_PLAN_SPLIT, "score_split_kernel"),
         (cus, 1, False, idx.IDX_PLAN_ONE_ROW, "fused_row_kernel"),
         (cus, 4, False, idx.IDX_PLAN_ONE_ROW_LAYERS, "fused_layers_kernel"),
         (8 * cus - 1, 1, False, idx.IDX_PLAN_ONE_ROW, "fused_row_kernel"),

@@ -455,6 +455,10 @@ LAYERED = {
     "split_wide": W.Spec(name="ml6", num_rows=24, page_size=64, cbs=64, nb=128, topk=7000,
                          layers=2, ke_rule="uniform", ke_lo=6000, ke_hi=12000,
                          cand_rule="distinct", fill="candidates"),
+    # fewer rows than CUs but more row-layers: one workgroup a row-layer in one launch
+    "row_layers": W.Spec(name="ml7", num_rows=40, page_size=64, cbs=64, nb=16, topk=300,
+                         layers=8, ke_rule="uniform", ke_lo=10, ke_hi=1200, cand_rule="messy",
+                         fill="all", q_formats=("mxfp4", "fp8")),
     # fewer rows than CUs: the split kernels, layer after layer
     "split": W.Spec(name="ml2", num_rows=40, page_size=32, cbs=32, nb=30, topk=500, layers=2,
                     ke_rule="uniform", ke_lo=100, ke_hi=1500, cand_rule="messy", fill="all",
@@ -1013,3 +1017,4 @@ def test_measurement_kernels_run_and_read_every_word():
             outs.append(sink.cpu().numpy())
         assert np.all(np.isfinite(outs[0])), fn.__name__
         np.testing.assert_array_equal(outs[0], outs[1], err_msg=fn.__name__)
+
