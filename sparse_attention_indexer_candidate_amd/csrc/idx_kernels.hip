@@ -1052,18 +1052,33 @@ __device__ void select_topk(const uint32_t (&key)[KPT], bool live, int count_val
 constexpr int kScoreThreads = 256;
 constexpr int kTopkThreads = 512;
 
+// Rows of one request (speculative / MTP rows: consecutive rows on one table row) read
+// mostly the same K blocks.  Workgroups go to the 8 XCDs round-robin by linear id, and
+// each XCD has its own L2, so blockIdx.x is mapped to rows such that the 8 consecutive
+// rows of every aligned group of 8 run on one XCD (their blockIdx.x values lie 8 apart,
+// so they are also dispatched close together) and a block that several of them read
+// crosses the fabric once.  Rows past the last whole 64-row block keep their index.
+// Measured on 64 requests of two decode rows: 18.2-18.5 vs 19.2-19.9 us a step, with the
+// scoring kernel's fetches down from 35.6 MB to the 22.5 MB of distinct blocks; no
+// change on rows that share nothing.  (A one-dimensional grid with the same placement
+// computed from the linear id was ~3 us slower on every workload.)
+__device__ __forceinline__ int xcd_grouped_row(int x, int num_rows) {
+    const int full = num_rows & ~63;
+    return x < full ? (x & ~63) + 8 * (x & 7) + ((x >> 3) & 7) : x;
+}
+
 // Rows split over workgroups: grid = (rows, chunks of groups_per_wg 64-column groups);
 // each wave scores a contiguous quarter of its workgroup's groups into logits.  The
 // leading scalar arguments are what the first loads need (the row's schedule entries
-// and query): the hardware preloads them into SGPRs at wave launch, so those loads
-// issue at once; ks / ke (only the validity of the scored columns needs them) and the
-// cache geometry arrive while they fly.
+// and query, and the row count that places the row): the hardware preloads them into
+// SGPRs at wave launch, so those loads issue at once; ks / ke (only the validity of the
+// scored columns needs them) and the cache geometry arrive while they fly.
 template <int QF, int PW>
 __device__ __forceinline__ void score_split_row(
     const int32_t *si_base, const int32_t *pg_base, const void *qv, const void *qs,
-    const void *weights, int32_t nsb, int32_t sbk, int32_t groups_per_wg, const Rows &rows,
-    const KCache &k, float *logits, int sf) {
-    const int row = blockIdx.x;
+    const void *weights, int32_t nsb, int32_t sbk, int32_t groups_per_wg, int32_t num_rows,
+    const Rows &rows, const KCache &k, float *logits, int sf) {
+    const int row = xcd_grouped_row(blockIdx.x, num_rows);
     const int wave = uniform(threadIdx.x / kWave);
     const int ncols = nsb * sbk;
     const int ngroups = (ncols + 63) / 64;
@@ -1084,10 +1099,10 @@ __device__ __forceinline__ void score_split_row(
 template <int QF, int PW>
 __global__ __launch_bounds__(kScoreThreads) void score_split_kernel(
     const int32_t *si_base, const int32_t *pg_base, const void *qv, const void *qs,
-    const void *weights, int32_t nsb, int32_t sbk, int32_t groups_per_wg, Rows rows, KCache k,
-    float *logits, int32_t sf) {
-    score_split_row<QF, PW>(si_base, pg_base, qv, qs, weights, nsb, sbk, groups_per_wg, rows, k,
-                            logits, sf);
+    const void *weights, int32_t nsb, int32_t sbk, int32_t groups_per_wg, int32_t num_rows,
+    Rows rows, KCache k, float *logits, int32_t sf) {
+    score_split_row<QF, PW>(si_base, pg_base, qv, qs, weights, nsb, sbk, groups_per_wg, num_rows,
+                            rows, k, logits, sf);
 }
 
 // Logits of layer l of a multi-layer split launch: the layer's logits_out, else its slice
@@ -1101,14 +1116,15 @@ __device__ __forceinline__ float *layer_logits(const LayerSet &ls, int l, float 
 template <int QF, int PW>
 __global__ __launch_bounds__(kScoreThreads) void score_split_layers_kernel(
     const int32_t *si_base, const int32_t *pg_base, int32_t nsb, int32_t sbk,
-    int32_t groups_per_wg, Rows rows, KCache k, LayerSet ls, float *ws, int64_t ws_layer,
-    int32_t sf) {
+    int32_t groups_per_wg, int32_t num_rows, Rows rows, KCache k, LayerSet ls, float *ws,
+    int64_t ws_layer, int32_t sf) {
     const int l = blockIdx.z;
     KCache kl = k;
     kl.values = ls.k_values[l];
     kl.scales = ls.k_scales[l];
     score_split_row<QF, PW>(si_base, pg_base, ls.q_values[l], ls.q_scales[l], ls.weights[l], nsb,
-                            sbk, groups_per_wg, rows, kl, layer_logits(ls, l, ws, ws_layer), sf);
+                            sbk, groups_per_wg, num_rows, rows, kl,
+                            layer_logits(ls, l, ws, ws_layer), sf);
 }
 
 // Tokens of the KPT sparse columns c0 .. c0+KPT-1 (KPT divides sbk = 1 << lsbk, and c0
@@ -2128,11 +2144,13 @@ static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const 
     if (gpw == 8)
         hipExtLaunchKernelGGL((score_split_kernel<QF, 2>), sgrid, dim3(kScoreThreads), 0, stream,
                               timing.start, timing.stop, 0, s.sparse_indices, s.pages, q_values,
-                              q_scales, weights, s.nsb, s.sbk, gpw, rows, k, logits, sf);
+                              q_scales, weights, s.nsb, s.sbk, gpw, rows.num_rows, rows, k,
+                              logits, sf);
     else
         hipExtLaunchKernelGGL((score_split_kernel<QF, 4>), sgrid, dim3(kScoreThreads), 0, stream,
                               timing.start, timing.stop, 0, s.sparse_indices, s.pages, q_values,
-                              q_scales, weights, s.nsb, s.sbk, gpw, rows, k, logits, sf);
+                              q_scales, weights, s.nsb, s.sbk, gpw, rows.num_rows, rows, k,
+                              logits, sf);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (ncols <= 8 * kTopkThreads)
@@ -2173,11 +2191,13 @@ static hipError_t launch_split_layers(const Rows &rows, int32_t num_layers, cons
     if (gpw == 8)
         hipExtLaunchKernelGGL((score_split_layers_kernel<QF, 2>), sgrid, dim3(kScoreThreads), 0,
                               stream, timing.start, timing.stop, 0, s.sparse_indices, s.pages,
-                              s.nsb, s.sbk, gpw, rows, k, layers, workspace, ws_layer, sf);
+                              s.nsb, s.sbk, gpw, rows.num_rows, rows, k, layers, workspace,
+                              ws_layer, sf);
     else
         hipExtLaunchKernelGGL((score_split_layers_kernel<QF, 4>), sgrid, dim3(kScoreThreads), 0,
                               stream, timing.start, timing.stop, 0, s.sparse_indices, s.pages,
-                              s.nsb, s.sbk, gpw, rows, k, layers, workspace, ws_layer, sf);
+                              s.nsb, s.sbk, gpw, rows.num_rows, rows, k, layers, workspace,
+                              ws_layer, sf);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 tgrid(rows.num_rows, num_layers);
