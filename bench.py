@@ -330,7 +330,7 @@ def bench_source(args, idx, W, dev, stream):
         q_fp8=None if base.layers[0].q_fp8 is None else base.layers[0].q_fp8.clone(),
         q_rowscale=None if base.layers[0].q_rowscale is None else base.layers[0].q_rowscale.clone())
         for _ in range(nrep - 1)]
-    rows = idx.make_rows(base.row_ke, base.row_ks, base.row_table)
+    rows = idx.make_rows(base.row_ke, base.row_ks, base.row_table, spec.next_n)
     cand = torch.empty((R, spec.nb), dtype=torch.int32, device=dev)
     ws = torch.empty(max(4, idx.idx_publish_workspace_bytes(cfg, R, max_ctx)), dtype=torch.uint8,
                      device=dev)
@@ -458,7 +458,7 @@ def run_workload(idx, W, config: int, args, dev, stream, steps: int, warmup: int
     sched0 = idx.Schedule(cfg, R, dev)
     base = to_device(case, dev)
     kc0 = idx.make_kcache(base.layers[0].pool, spec.page_size, spec.head_dim, base.block_table)
-    rows0 = idx.make_rows(base.row_ke, base.row_ks, base.row_table)
+    rows0 = idx.make_rows(base.row_ke, base.row_ks, base.row_table, spec.next_n)
     idx.idx_expand_candidates(cfg, rows0, kc0, base.candidate_blocks,
                               base.candidate_blocks.stride(0), sched0.struct)
     torch.cuda.synchronize()
@@ -516,7 +516,7 @@ def run_workload(idx, W, config: int, args, dev, stream, steps: int, warmup: int
     plans = []
     for d in reps:
         plans.append(dict(
-            d=d, rows=idx.make_rows(d.row_ke, d.row_ks, d.row_table),
+            d=d, rows=idx.make_rows(d.row_ke, d.row_ks, d.row_table, spec.next_n),
             kc=[idx.make_kcache(L.pool, spec.page_size, spec.head_dim, d.block_table) for L in d.layers],
             sched=idx.Schedule(cfg, R, dev),
             out=torch.empty((R, spec.topk), dtype=torch.int32, device=dev),

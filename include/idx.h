@@ -106,12 +106,20 @@ typedef struct {
 
 /* The rows of one call (SparseMQARowsMetadata on the backend page): decode rows
  * (ks = 0, ke = the compressed context length, one table row each) or one prefill
- * chunk (per-row [ks, ke), all rows on the request's table row). */
+ * chunk (per-row [ks, ke), all rows on the request's table row).
+ * rows_per_request: how many consecutive rows belong to one request and share its
+ * table row, as the next_n query rows of a request do in SparseMQAIndexer.forward
+ * (sparse_mqa_indexer page: q of shape [batch, next_n, H, D]; MTP / speculative
+ * rows); 0 or 1: independent rows.  A placement hint, nothing more: with a value
+ * above 1 the decode scoring kernels run each aligned group of 8 consecutive rows on
+ * one XCD, so the K blocks those rows share cross the fabric once (through that XCD's
+ * L2).  Results never depend on it; negative values are IDX_EINVAL. */
 typedef struct {
     int32_t num_rows;              /* >= 0; 0 launches nothing */
     const int32_t *row_ks;         /* [num_rows] K-range start, or NULL for all 0 */
     const int32_t *row_ke;         /* [num_rows] exclusive K-range end */
     const int32_t *row_table;      /* [num_rows] row -> table row, or NULL for row r -> r */
+    int32_t rows_per_request;      /* >= 0; placement hint (above) */
 } idx_rows;
 
 /* The shared sparse-column schedule of one step (built by idx_expand_candidates,

@@ -65,7 +65,8 @@ class idx_kcache(ctypes.Structure):
 
 class idx_rows(ctypes.Structure):
     _fields_ = [("num_rows", ctypes.c_int32), ("row_ks", ctypes.c_void_p),
-                ("row_ke", ctypes.c_void_p), ("row_table", ctypes.c_void_p)]
+                ("row_ke", ctypes.c_void_p), ("row_table", ctypes.c_void_p),
+                ("rows_per_request", ctypes.c_int32)]
 
 
 class idx_schedule(ctypes.Structure):
@@ -464,8 +465,9 @@ def make_kcache(pool, page_size, head_dim, block_table) -> idx_kcache:
                       block_table.shape[0], block_table.shape[1])
 
 
-def make_rows(row_ke, row_ks=None, row_table=None) -> idx_rows:
-    return idx_rows(row_ke.shape[0], _p(row_ks), _p(row_ke), _p(row_table))
+def make_rows(row_ke, row_ks=None, row_table=None, rows_per_request=1) -> idx_rows:
+    """rows_per_request: consecutive rows of one request (next_n), a placement hint."""
+    return idx_rows(row_ke.shape[0], _p(row_ks), _p(row_ke), _p(row_table), rows_per_request)
 
 
 class Schedule:

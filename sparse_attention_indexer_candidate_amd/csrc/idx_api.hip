@@ -95,6 +95,8 @@ int check_rows(const idx_rows *rows) {
     if (!rows) return fail(IDX_EINVAL, "rows is NULL");
     if (rows->num_rows < 0) return fail(IDX_EINVAL, "num_rows %d < 0", rows->num_rows);
     if (rows->num_rows > 0 && !rows->row_ke) return fail(IDX_EINVAL, "row_ke is NULL");
+    if (rows->rows_per_request < 0)
+        return fail(IDX_EINVAL, "rows_per_request %d < 0", rows->rows_per_request);
     return IDX_OK;
 }
 
@@ -153,7 +155,7 @@ idx::KCache to_kcache(const idx_config *cfg, const idx_kcache *k) {
 }
 
 idx::Rows to_rows(const idx_rows *r) {
-    return idx::Rows{r->num_rows, r->row_ks, r->row_ke, r->row_table};
+    return idx::Rows{r->num_rows, r->row_ks, r->row_ke, r->row_table, r->rows_per_request};
 }
 
 idx::Schedule to_schedule(const idx_config *cfg, int32_t sbk, const idx_schedule *s) {

@@ -36,6 +36,7 @@ struct Rows {
     const int32_t *ks;     // may be null (all 0)
     const int32_t *ke;
     const int32_t *table;  // may be null (row r -> r)
+    int32_t rows_per_request;   // > 1: consecutive rows share K (placement hint)
 };
 
 struct Schedule {

@@ -1054,16 +1054,19 @@ constexpr int kTopkThreads = 512;
 
 // Rows of one request (speculative / MTP rows: consecutive rows on one table row) read
 // mostly the same K blocks.  Workgroups go to the 8 XCDs round-robin by linear id, and
-// each XCD has its own L2, so blockIdx.x is mapped to rows such that the 8 consecutive
-// rows of every aligned group of 8 run on one XCD (their blockIdx.x values lie 8 apart,
-// so they are also dispatched close together) and a block that several of them read
-// crosses the fabric once.  Rows past the last whole 64-row block keep their index.
-// Measured on 64 requests of two decode rows: 18.2-18.5 vs 19.2-19.9 us a step, with the
-// scoring kernel's fetches down from 35.6 MB to the 22.5 MB of distinct blocks; no
-// change on rows that share nothing.  (A one-dimensional grid with the same placement
-// computed from the linear id was ~3 us slower on every workload.)
-__device__ __forceinline__ int xcd_grouped_row(int x, int num_rows) {
-    const int full = num_rows & ~63;
+// each XCD has its own L2, so when the caller declares such rows (rows_per_request > 1)
+// blockIdx.x is mapped to rows such that the 8 consecutive rows of every aligned group
+// of 8 run on one XCD (their blockIdx.x values lie 8 apart, so they are also dispatched
+// close together) and a block that several of them read crosses the fabric once.
+// group_rows: the row count with that placement, 0 for none (identity); rows past the
+// last whole 64-row block keep their index.  Measured on 64 requests of two decode rows
+// (split kernels): 18.2-18.5 vs 19.2-19.9 us a step, the scoring kernel's fetches down
+// from 35.6 MB to the 22.5 MB of distinct blocks; on 256 requests of two rows and 128 of
+// four (one-row kernel): 33.6-35.4 vs 37.3-38.3 and 32.3-33.0 vs 38.7-39.4 us.  Rows that
+// share nothing lose ~2 % with it in the one-row kernel, hence the hint.  (A
+// one-dimensional grid with the same placement was ~3 us slower on every workload.)
+__device__ __forceinline__ int xcd_grouped_row(int x, int group_rows) {
+    const int full = group_rows & ~63;
     return x < full ? (x & ~63) + 8 * (x & 7) + ((x >> 3) & 7) : x;
 }
 
@@ -1076,9 +1079,9 @@ __device__ __forceinline__ int xcd_grouped_row(int x, int num_rows) {
 template <int QF, int PW>
 __device__ __forceinline__ void score_split_row(
     const int32_t *si_base, const int32_t *pg_base, const void *qv, const void *qs,
-    const void *weights, int32_t nsb, int32_t sbk, int32_t groups_per_wg, int32_t num_rows,
+    const void *weights, int32_t nsb, int32_t sbk, int32_t groups_per_wg, int32_t group_rows,
     const Rows &rows, const KCache &k, float *logits, int sf) {
-    const int row = xcd_grouped_row(blockIdx.x, num_rows);
+    const int row = xcd_grouped_row(blockIdx.x, group_rows);
     const int wave = uniform(threadIdx.x / kWave);
     const int ncols = nsb * sbk;
     const int ngroups = (ncols + 63) / 64;
@@ -1099,10 +1102,10 @@ __device__ __forceinline__ void score_split_row(
 template <int QF, int PW>
 __global__ __launch_bounds__(kScoreThreads) void score_split_kernel(
     const int32_t *si_base, const int32_t *pg_base, const void *qv, const void *qs,
-    const void *weights, int32_t nsb, int32_t sbk, int32_t groups_per_wg, int32_t num_rows,
+    const void *weights, int32_t nsb, int32_t sbk, int32_t groups_per_wg, int32_t group_rows,
     Rows rows, KCache k, float *logits, int32_t sf) {
-    score_split_row<QF, PW>(si_base, pg_base, qv, qs, weights, nsb, sbk, groups_per_wg, num_rows,
-                            rows, k, logits, sf);
+    score_split_row<QF, PW>(si_base, pg_base, qv, qs, weights, nsb, sbk, groups_per_wg,
+                            group_rows, rows, k, logits, sf);
 }
 
 // Logits of layer l of a multi-layer split launch: the layer's logits_out, else its slice
@@ -1116,14 +1119,14 @@ __device__ __forceinline__ float *layer_logits(const LayerSet &ls, int l, float 
 template <int QF, int PW>
 __global__ __launch_bounds__(kScoreThreads) void score_split_layers_kernel(
     const int32_t *si_base, const int32_t *pg_base, int32_t nsb, int32_t sbk,
-    int32_t groups_per_wg, int32_t num_rows, Rows rows, KCache k, LayerSet ls, float *ws,
+    int32_t groups_per_wg, int32_t group_rows, Rows rows, KCache k, LayerSet ls, float *ws,
     int64_t ws_layer, int32_t sf) {
     const int l = blockIdx.z;
     KCache kl = k;
     kl.values = ls.k_values[l];
     kl.scales = ls.k_scales[l];
     score_split_row<QF, PW>(si_base, pg_base, ls.q_values[l], ls.q_scales[l], ls.weights[l], nsb,
-                            sbk, groups_per_wg, num_rows, rows, kl,
+                            sbk, groups_per_wg, group_rows, rows, kl,
                             layer_logits(ls, l, ws, ws_layer), sf);
 }
 
@@ -1371,10 +1374,11 @@ __device__ __forceinline__ void fused_row(
 template <int QF, int NT, int KPT, int U, int WPE>
 __global__ __launch_bounds__(NT, WPE) void fused_row_kernel(
     const int32_t *si_base, const int32_t *pg_base, const void *qv, const void *qs,
-    const void *weights, const int32_t *p_kept, int32_t nsb, int32_t lsbk, Rows rows, KCache k,
-    float *logits_out, int32_t topk, int32_t *out, int64_t ostride, int32_t sf) {
+    const void *weights, const int32_t *p_kept, int32_t nsb, int32_t lsbk, int32_t group_rows,
+    Rows rows, KCache k, float *logits_out, int32_t topk, int32_t *out, int64_t ostride,
+    int32_t sf) {
     __shared__ FusedLds<NT> lds;
-    fused_row<QF, NT, KPT, U>(lds, blockIdx.x, si_base, pg_base, qv, qs, weights, p_kept, nsb, lsbk,
+    fused_row<QF, NT, KPT, U>(lds, xcd_grouped_row(blockIdx.x, group_rows), si_base, pg_base, qv, qs, weights, p_kept, nsb, lsbk,
                            rows, k, logits_out, topk, out, ostride, sf);
 }
 
@@ -1387,13 +1391,14 @@ __global__ __launch_bounds__(NT, WPE) void fused_row_kernel(
 template <int QF, int NT, int KPT, int U, int WPE>
 __global__ __launch_bounds__(NT, WPE) void fused_layers_kernel(
     const int32_t *si_base, const int32_t *pg_base, const int32_t *p_kept, int32_t nsb,
-    int32_t lsbk, int32_t topk, Rows rows, KCache k, LayerSet ls, int64_t ostride, int32_t sf) {
+    int32_t lsbk, int32_t topk, int32_t group_rows, Rows rows, KCache k, LayerSet ls,
+    int64_t ostride, int32_t sf) {
     __shared__ FusedLds<NT> lds;
     const int layer = blockIdx.y;
     KCache kl = k;
     kl.values = ls.k_values[layer];
     kl.scales = ls.k_scales[layer];
-    fused_row<QF, NT, KPT, U>(lds, blockIdx.x, si_base, pg_base, ls.q_values[layer],
+    fused_row<QF, NT, KPT, U>(lds, xcd_grouped_row(blockIdx.x, group_rows), si_base, pg_base, ls.q_values[layer],
                            ls.q_scales[layer], ls.weights[layer], p_kept, nsb, lsbk, rows, kl,
                            ls.logits_out[layer], topk, ls.out[layer], ostride, sf);
 }
@@ -2048,6 +2053,11 @@ hipError_t launch_expand(const Rows &rows, const KCache &k, const int32_t *cand,
     return hipGetLastError();
 }
 
+// group_rows argument of the decode scoring kernels (see xcd_grouped_row).
+static int32_t grouped_rows(const Rows &rows) {
+    return rows.rows_per_request > 1 ? rows.num_rows : 0;
+}
+
 int device_cus() {
     static int cus[64] = {0};
     int dev = 0;
@@ -2117,7 +2127,8 @@ static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const 
 #define IDX_LAUNCH_FUSED(NT_, KPT_, U_, WPE_)                                                    \
     hipExtLaunchKernelGGL((fused_row_kernel<QF, NT_, KPT_, U_, WPE_>), dim3(rows.num_rows),       \
                           dim3(NT_), 0, stream, timing.start, timing.stop, 0, s.sparse_indices,   \
-                          s.pages, q_values, q_scales, weights, s.kept, s.nsb, s.lsbk, rows, k,   \
+                          s.pages, q_values, q_scales, weights, s.kept, s.nsb, s.lsbk,            \
+                          grouped_rows(rows), rows, k,                                             \
                           logits_out, topk, out, out_stride, sf)
         if constexpr (QF == 0) {
             if (rows.num_rows < 2 * device_cus()) {
@@ -2144,12 +2155,12 @@ static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const 
     if (gpw == 8)
         hipExtLaunchKernelGGL((score_split_kernel<QF, 2>), sgrid, dim3(kScoreThreads), 0, stream,
                               timing.start, timing.stop, 0, s.sparse_indices, s.pages, q_values,
-                              q_scales, weights, s.nsb, s.sbk, gpw, rows.num_rows, rows, k,
+                              q_scales, weights, s.nsb, s.sbk, gpw, grouped_rows(rows), rows, k,
                               logits, sf);
     else
         hipExtLaunchKernelGGL((score_split_kernel<QF, 4>), sgrid, dim3(kScoreThreads), 0, stream,
                               timing.start, timing.stop, 0, s.sparse_indices, s.pages, q_values,
-                              q_scales, weights, s.nsb, s.sbk, gpw, rows.num_rows, rows, k,
+                              q_scales, weights, s.nsb, s.sbk, gpw, grouped_rows(rows), rows, k,
                               logits, sf);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -2191,12 +2202,12 @@ static hipError_t launch_split_layers(const Rows &rows, int32_t num_layers, cons
     if (gpw == 8)
         hipExtLaunchKernelGGL((score_split_layers_kernel<QF, 2>), sgrid, dim3(kScoreThreads), 0,
                               stream, timing.start, timing.stop, 0, s.sparse_indices, s.pages,
-                              s.nsb, s.sbk, gpw, rows.num_rows, rows, k, layers, workspace,
+                              s.nsb, s.sbk, gpw, grouped_rows(rows), rows, k, layers, workspace,
                               ws_layer, sf);
     else
         hipExtLaunchKernelGGL((score_split_layers_kernel<QF, 4>), sgrid, dim3(kScoreThreads), 0,
                               stream, timing.start, timing.stop, 0, s.sparse_indices, s.pages,
-                              s.nsb, s.sbk, gpw, rows.num_rows, rows, k, layers, workspace,
+                              s.nsb, s.sbk, gpw, grouped_rows(rows), rows, k, layers, workspace,
                               ws_layer, sf);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -2257,7 +2268,7 @@ hipError_t launch_sparse_layers(int q_format, int score_format, const Rows &rows
     hipExtLaunchKernelGGL((fused_layers_kernel<QF_, NT_, KPT_, U_, WPE_>), grid, dim3(NT_), 0,    \
                           stream,                                                                  \
                           timing.start, timing.stop, 0, s.sparse_indices, s.pages, s.kept, s.nsb, \
-                          s.lsbk, topk, rows, k, layers, out_stride, sf)
+                          s.lsbk, topk, grouped_rows(rows), rows, k, layers, out_stride, sf)
         if (q_format == 0) {
             if (ncols <= 512 * 4) IDX_LAUNCH_LAYERS(0, 512, 4, 1, 4);
             else if (ncols <= 512 * 8) IDX_LAUNCH_LAYERS(0, 512, 8, 1, 4);

@@ -152,7 +152,7 @@ class GpuRun:
         self.sbk = self.cfg.sparse_block_kv
         R = case.num_rows
         dev = dcase.row_ke.device
-        self.rows = idx.make_rows(dcase.row_ke, dcase.row_ks, dcase.row_table)
+        self.rows = idx.make_rows(dcase.row_ke, dcase.row_ks, dcase.row_table, s.next_n)
         self.sched = idx.Schedule(self.cfg, R, dev)
         self.kcaches = [idx.make_kcache(L.pool, s.page_size, s.head_dim, dcase.block_table)
                         for L in dcase.layers]

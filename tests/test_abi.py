@@ -125,7 +125,7 @@ def kcache(**kw):
 
 
 def rows(n=2, **kw):
-    base = dict(num_rows=n, row_ks=None, row_ke=FAKE, row_table=None)
+    base = dict(num_rows=n, row_ks=None, row_ke=FAKE, row_table=None, rows_per_request=1)
     base.update(kw)
     return idx.idx_rows(*[base[f] for f, _ in idx.idx_rows._fields_])
 
@@ -156,6 +156,7 @@ def sparse_call(c=None, r=None, k=None, s=None, qv=FAKE, qs=FAKE, w=FAKE, out=FA
     (dict(s=sched(end=None)), idx.IDX_EINVAL),
     (dict(r=rows(-1)), idx.IDX_EINVAL),
     (dict(r=rows(2, row_ke=None)), idx.IDX_EINVAL),
+    (dict(r=rows(2, rows_per_request=-1)), idx.IDX_EINVAL),
     (dict(k=kcache(values=None)), idx.IDX_EINVAL),
     (dict(k=kcache(num_pages=0)), idx.IDX_EINVAL),
     (dict(k=kcache(block_table_stride=2)), idx.IDX_EINVAL),

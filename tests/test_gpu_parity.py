@@ -335,6 +335,60 @@ def test_mtp_decode_rows_share_k(name):
     run_and_compare(W.generate(MTP[name], seed=21), tag=name)
 
 
+# Enough rows that the placement hint (rows_per_request > 1) permutes whole 64-row blocks:
+# the split kernels (130 rows: two blocks and a 2-row tail), one workgroup a row (520 rows)
+# and one launch of one-row workgroups for two layers (130 rows x 2).
+MTP_PLACED = {
+    "n2_split": W.Spec(name="mp2", num_rows=130, nb=16, topk=300, ke_rule="uniform",
+                       ke_lo=200, ke_hi=3000, cand_rule="mtp_overlap", next_n=2, fill="all"),
+    "n4_one_row": W.Spec(name="mp4", num_rows=520, nb=16, topk=300, ke_rule="uniform",
+                         ke_lo=200, ke_hi=3000, cand_rule="mtp_overlap", next_n=4, fill="all"),
+    "n2_two_layers": W.Spec(name="mp2l", num_rows=130, nb=16, topk=300, layers=2,
+                            ke_rule="uniform", ke_lo=200, ke_hi=3000, cand_rule="mtp_overlap",
+                            next_n=2, fill="all"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MTP_PLACED))
+def test_mtp_rows_placed_by_request_match_unplaced_and_oracle(name):
+    """The placement hint changes which workgroup scores which row, never a result: every
+    row against the oracle, and indices and logits bit for bit against the same calls
+    made without the hint."""
+    import sparse_attention_indexer_candidate_amd as idx
+
+    case = W.generate(MTP_PLACED[name], seed=23)
+    nl = case.spec.layers
+    g, _ = run_and_compare(case, layers=tuple(range(nl)), tag=name)
+    dcase = g.dcase
+    plain = GpuRun(case, dcase)
+    plain.rows = idx.make_rows(dcase.row_ke, dcase.row_ks, dcase.row_table, 1)
+    plain.expand()
+    g.expand()
+    for layer in range(nl):
+        _say(f"[{name}] layer {layer}: with and without the hint")
+        g.score(layer, with_logits=True)
+        a = g.fetch()
+        plain.score(layer, with_logits=True)
+        b = plain.fetch()
+        np.testing.assert_array_equal(a["indices"], b["indices"], err_msg=f"{name} {layer}")
+        np.testing.assert_array_equal(a["logits"].view(np.uint32), b["logits"].view(np.uint32))
+    if nl > 1:
+        assert g.idx.idx_sparse_plan(g.cfg, case.num_rows, nl)["plan"] == \
+            g.idx.IDX_PLAN_ONE_ROW_LAYERS
+        outs, logs = g.score_layers(range(nl), [True] * nl)
+        outs_p, logs_p = plain.score_layers(range(nl), [True] * nl)
+        torch.cuda.synchronize()
+        for layer in range(nl):
+            np.testing.assert_array_equal(outs[layer].cpu().numpy(), outs_p[layer].cpu().numpy())
+            np.testing.assert_array_equal(logs[layer].cpu().numpy().view(np.uint32),
+                                          logs_p[layer].cpu().numpy().view(np.uint32))
+            pool = case.layers[layer].host_pool(case.spec.page_bytes)
+            ora = oracle.indexer_rows(case, layer, None, "mxfp4", pool=pool, threads=THREADS)
+            res = g.fetch()
+            res["indices"], res["logits"] = outs[layer].cpu().numpy(), logs[layer].cpu().numpy()
+            compare_rows(case, res, ora, case.spec.topk, g.sbk, f"{name} one launch {layer}")
+
+
 # The kernels' size limits: 8192 candidate columns a row (NB * cbs) and top-k at its
 # 8192 maximum (every valid column taken), or 6000 selected of up to 8192.
 MAX_WIDTH = {
