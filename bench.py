@@ -243,13 +243,7 @@ def bench_gather(args, idx, case, cfg, dev, gen_s):
     avg_s = float(np.mean(kernel_ms)) / 1e3
     achieved = launch_bytes / avg_s / 1e9
     peaks = measured_peaks(stream)
-    traffic = None
-    tfile = os.path.join(ROOT, "profiles", f"traffic_gather_k_kernel_cfg{args.config}_mxfp4.json")
-    if os.path.exists(tfile):
-        with open(tfile) as f:
-            t = json.load(f)
-        if t.get("kernel_source_hash") == kernel_source_hash():
-            traffic = t.get("bytes_per_launch")
+    traffic = traffic_for("gather_k_kernel", f"gather_{spec.name}", "mxfp4")
     roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": "gather_k_kernel",
             "measured_peak": peaks["read_gbs"], "frac_of_measured": achieved / peaks["read_gbs"],
@@ -376,7 +370,8 @@ def bench_source(args, idx, W, dev, stream):
     roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "step_gbs": launch_bytes / step_s / 1e9,
             "step_frac": launch_bytes / step_s / 1e9 / HBM_PEAK_GBS,
-            "traffic": traffic_for("score_pool_kernel", args.config, args.q_format),
+            "traffic": traffic_for("score_pool_kernel", f"source_{spec.name}", args.q_format,
+                                   args.score_format),
             "kernel": "score_pool_kernel", "measured_peak": peaks["read_gbs"],
             "frac_of_measured": achieved / peaks["read_gbs"], "avg_launch_us": avg_s * 1e6,
             "launch_us_p10": float(np.percentile(kernel_ms, 10)) * 1e3,
@@ -417,10 +412,17 @@ def bench_source(args, idx, W, dev, stream):
     print(json.dumps(out), flush=True)
 
 
-def traffic_for(kernel_name: str, config: int, q_format: str):
+def traffic_file(kernel_name: str, workload: str, q_format: str, score_format: str = "fp32"):
+    """profiles/ file of the FETCH_SIZE / WRITE_SIZE counters of one kernel on one workload
+    (its full name: rows, sizes and layer count) in one query and scoring format."""
+    sfx = "_bf16" if score_format == "bf16" else ""
+    return os.path.join(ROOT, "profiles", f"traffic_{kernel_name}_{workload}_{q_format}{sfx}.json")
+
+
+def traffic_for(kernel_name: str, workload: str, q_format: str, score_format: str = "fp32"):
     """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE counters of this
     kernel on this workload, or None when none were taken for the current kernel sources."""
-    tfile = os.path.join(ROOT, "profiles", f"traffic_{kernel_name}_cfg{config}_{q_format}.json")
+    tfile = traffic_file(kernel_name, workload, q_format, score_format)
     if not os.path.exists(tfile):
         return None
     with open(tfile) as f:
@@ -604,7 +606,8 @@ def run_workload(idx, W, config: int, args, dev, stream, steps: int, warmup: int
                 kernel_ms=kernel_ms)
 
 
-def roofline(m, config: int, q_format: str, peaks: dict, dense: bool) -> dict:
+def roofline(m, config: int, q_format: str, peaks: dict, dense: bool,
+             score_format: str = "fp32") -> dict:
     """The scoring kernel's roofline object from run_workload's measurements."""
     spec, kernel_ms = m["spec"], m["kernel_ms"]
     avg_s = float(np.mean(kernel_ms)) / 1e3
@@ -650,7 +653,7 @@ def roofline(m, config: int, q_format: str, peaks: dict, dense: bool) -> dict:
         # the MFMA rate left once the same SIMDs issue the ReLU-weight epilogue
         roof["epilogue_ceiling"] = peaks["mxfp4_relu_epilogue_tflops"]
         roof["frac_of_epilogue_ceiling"] = roof["achieved"] / roof["epilogue_ceiling"]
-    roof.update({"traffic": traffic_for(m["kernel_name"], config, q_format),
+    roof.update({"traffic": traffic_for(m["kernel_name"], spec.name, q_format, score_format),
                  "kernel": m["kernel_name"], "avg_launch_us": avg_s * 1e6,
                  "launch_us_p10": float(np.percentile(kernel_ms, 10)) * 1e3,
                  "launch_us_p90": float(np.percentile(kernel_ms, 90)) * 1e3,
@@ -743,7 +746,7 @@ def main():
                      layers=args.layers, per_layer_calls=args.per_layer_calls, graph=args.graph)
     spec, R = m["spec"], m["R"]
     peaks = measured_peaks(stream)
-    roof = roofline(m, args.config, args.q_format, peaks, dense)
+    roof = roofline(m, args.config, args.q_format, peaks, dense, args.score_format)
     cols_per_step = int(m["ends"].astype(np.int64).sum()) * spec.layers
     ctx_cols_per_step = int(m["ctx"].sum()) * spec.layers
     elapsed = m["elapsed"]
@@ -778,7 +781,7 @@ def main():
     if not args.no_prefill and not dense and args.config == 4 and args.q_format == "mxfp4":
         # the prefill chunk (4096 rows of one request), whose bound is the MX-FP4 MFMA rate
         pm = run_workload(idx, W, 3, args, dev, stream, max(args.steps, 20), args.warmup)
-        pr = roofline(pm, 3, args.q_format, peaks, False)
+        pr = roofline(pm, 3, args.q_format, peaks, False, args.score_format)
         pcols = int(pm["ends"].astype(np.int64).sum())
         out["prefill"] = {"workload": pm["spec"].name, "rows": pm["R"],
                           "ms_per_step": pm["elapsed"] / pm["steps"] * 1e3,
