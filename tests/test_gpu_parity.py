@@ -144,6 +144,21 @@ def test_row_groups_wide_rows_all_rows():
     run_and_compare(W.generate(spec, seed=3), tag="wide")
 
 
+def test_row_groups_many_short_rows_all_rows():
+    """A prefill chunk of 20001 rows (an odd count: the last row group holds one row) of
+    short causal rows on one table: 10001 row-group workgroups dispatched heaviest first,
+    every row against the oracle."""
+    spec = W.Spec(name="many", num_rows=20001, page_size=64, cbs=64, nb=4, topk=100,
+                  mode="prefill", ke_rule="uniform", ke_lo=1, ke_hi=256, ks_rule="random",
+                  context=256, cand_rule="messy", fill="all")
+    import sparse_attention_indexer_candidate_amd as idx
+
+    case = W.generate(spec, seed=11)
+    cfg = idx.make_config(page_size=64, candidate_block_size=64, num_candidate_blocks=4, topk=100)
+    assert idx.idx_sparse_plan(cfg, case.num_rows, 1)["plan"] == idx.IDX_PLAN_ROW_GROUP
+    run_and_compare(case, tag="many")
+
+
 def _random_spec(i):
     """A seeded random shape for the kernel path i % 3 (split, one row per workgroup,
     row groups): block and page sizes, k, ranges, candidate mess and weight sign vary."""
