@@ -546,7 +546,13 @@ __device__ __forceinline__ float reduce_transpose4(float p0, float p1, float p2,
 // sink(c, logit, valid) receives every column of the groups; valid says whether the
 // column is a token of [ks, ke) (the logit is meaningless otherwise).  Every lane of the
 // wave calls it together.
-template <int QF, int RG, int U, class Desc, class Sink>
+//
+// G64 (every 64-column group is one 64-token run of one page: 64-token sparse blocks, or
+// the dense comparator on pages of a multiple of 64 tokens): lane q resolves group q of
+// the round (desc.group), the four tiles of a group load from one base with immediate
+// offsets, and a group is scored or dropped whole (4 lane reads a group instead of 16,
+// no per-tile selects).
+template <int QF, int RG, int U, bool G64, class Desc, class Sink>
 __device__ __forceinline__ void score_groups(const KCache &k, const QFrag<QF> &f, int ks, int ke,
                                              int g0, int g1, int sf, Desc desc, Sink sink) {
     static_assert(RG <= 16 && RG % U == 0, "units must tile a round of at most 16 groups");
@@ -555,6 +561,62 @@ __device__ __forceinline__ void score_groups(const KCache &k, const QFrag<QF> &f
     const int n = lane & 15, g = lane >> 4;
     const uint32_t voff = n * (kHeadDim / 2) + 16 * g;
     const uint32_t soff = n * (kHeadDim / 32) + g;
+    if constexpr (G64) {
+        for (int r0 = g0; r0 < g1; r0 += RG) {
+            const int ng = min(RG, g1 - r0);
+            int page = -1, ttok = 0;
+            if (lane < ng) desc.group(r0 + lane, page, ttok);
+            const bool ok = page >= 0 && page < k.num_pages && ttok >= 0;
+            uint64_t vb = (uint64_t)k.values, sb = (uint64_t)k.scales;  // safe, never scored
+            if (ok) {
+                const int64_t j0 = page_slot(ttok, k.page_size);
+                vb += (uint64_t)((int64_t)page * k.values_page_stride + j0 * (kHeadDim / 2));
+                sb += (uint64_t)((int64_t)page * k.scales_page_stride + j0 * (kHeadDim / 32));
+            }
+            const uint32_t vlo = (uint32_t)vb, vhi = (uint32_t)(vb >> 32);
+            const uint32_t slo = (uint32_t)sb, shi = (uint32_t)(sb >> 32);
+            const uint64_t okmask = __ballot(ok);  // bit q: group q has something to score
+            KTile kt[2][U][4];
+            auto load_unit = [&](int u, KTile(&b)[U][4]) {
+#pragma unroll
+                for (int q = 0; q < U; ++q) {
+                    const int src = u * U + q;
+                    const kGlobal uint8_t *vp = (const kGlobal uint8_t *)join64(
+                        __builtin_amdgcn_readlane(vhi, src), __builtin_amdgcn_readlane(vlo, src));
+                    const kGlobal uint8_t *sp = (const kGlobal uint8_t *)join64(
+                        __builtin_amdgcn_readlane(shi, src), __builtin_amdgcn_readlane(slo, src));
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const v4u x = __builtin_nontemporal_load(
+                            (const kGlobal v4u *)(vp + t * 16 * (kHeadDim / 2) + voff));
+                        b[q][t].v = make_uint4(x[0], x[1], x[2], x[3]);
+                        b[q][t].sc =
+                            __builtin_nontemporal_load(sp + t * 16 * (kHeadDim / 32) + soff);
+                    }
+                }
+            };
+            auto finish_unit = [&](int u, const KTile(&b)[U][4]) {
+#pragma unroll
+                for (int q = 0; q < U; ++q) {
+                    const int grp = u * U + q;
+                    if (grp >= ng) break;
+                    const float lg = score_out(
+                        sf, reduce_transpose4(tile_partial(f, b[q][0]), tile_partial(f, b[q][1]),
+                                              tile_partial(f, b[q][2]), tile_partial(f, b[q][3])));
+                    const int tok = __builtin_amdgcn_readlane(ttok, grp) + lane;
+                    const bool valid = ((okmask >> grp) & 1) && tok >= ks && tok < ke;
+                    sink((r0 + grp) * 64 + lane, lg, valid);
+                }
+            };
+            load_unit(0, kt[0]);
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                if (u + 1 < NU) load_unit(u + 1, kt[(u + 1) & 1]);
+                if (u * U < ng) finish_unit(u, kt[u & 1]);
+            }
+        }
+        return;
+    }
     for (int r0 = g0; r0 < g1; r0 += RG) {
         const int ng = min(RG, g1 - r0);
         int page = -1, ttok = 0;
@@ -620,7 +682,14 @@ __device__ __forceinline__ void score_groups(const KCache &k, const QFrag<QF> &f
 // its result is dropped).  sink(c, logit, valid) receives every column of the units
 // scored; valid says whether the column is a token of [ks, ke) (logit is meaningless
 // otherwise).
-template <int QF, int U, class Desc, class Grab, class Sink>
+//
+// G64 (64-token sparse blocks, so every page holds whole 64-token runs): a group is one
+// run of one page, its four tiles are consecutive 1 KB value runs and 64-byte scale runs.
+// One uniform descriptor then serves the whole group; the loads use a scalar base with
+// immediate offsets, and a group is scored or dropped whole.  Per group that saves the
+// per-tile descriptor lanes, 16 lane reads, the 64-bit address arithmetic per tile, the
+// per-tile drop selects and the token shuffle (vector ALU time the epilogue shares).
+template <int QF, int U, bool G64, class Desc, class Grab, class Sink>
 __device__ __forceinline__ void score_units(const KCache &k, const QFrag<QF> &f, int ks, int ke,
                                             int sf, Desc desc, Grab grab, Sink sink) {
     static_assert(4 * U <= kWave, "one lane per tile of a unit");
@@ -628,6 +697,66 @@ __device__ __forceinline__ void score_units(const KCache &k, const QFrag<QF> &f,
     const int n = lane & 15, g = lane >> 4;
     const uint32_t voff = n * (kHeadDim / 2) + 16 * g;
     const uint32_t soff = n * (kHeadDim / 32) + g;
+    if constexpr (G64) {
+        auto issue = [&](int u, KTile (&b)[U][4], int (&t0)[U], uint32_t &okm) {
+            okm = 0u;
+#pragma unroll
+            for (int q = 0; q < U; ++q) {
+                int page = -1, tt = 0;
+                if (u >= 0) desc((u * U + q) * 4, page, tt);   // every lane: one LDS word
+                page = uniform(page);
+                tt = uniform(tt);
+                const bool ok = page >= 0 && page < k.num_pages && tt >= 0;
+                int64_t ov = 0, os = 0;   // a dropped group reads the pool's first bytes
+                if (ok) {
+                    const int64_t j0 = page_slot(tt, k.page_size);
+                    ov = (int64_t)page * k.values_page_stride + j0 * (kHeadDim / 2);
+                    os = (int64_t)page * k.scales_page_stride + j0 * (kHeadDim / 32);
+                }
+                const kGlobal uint8_t *vp = (const kGlobal uint8_t *)k.values + ov;
+                const kGlobal uint8_t *sp = (const kGlobal uint8_t *)k.scales + os;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const v4u x = __builtin_nontemporal_load(
+                        (const kGlobal v4u *)(vp + t * 16 * (kHeadDim / 2) + voff));
+                    b[q][t].v = make_uint4(x[0], x[1], x[2], x[3]);
+                    b[q][t].sc = __builtin_nontemporal_load(sp + t * 16 * (kHeadDim / 32) + soff);
+                }
+                t0[q] = tt;
+                okm |= (uint32_t)ok << q;
+            }
+        };
+        auto finish = [&](int u, const KTile (&b)[U][4], const int (&t0)[U], uint32_t okm) {
+#pragma unroll
+            for (int q = 0; q < U; ++q) {
+                const float lg = score_out(
+                    sf, reduce_transpose4(tile_partial(f, b[q][0]), tile_partial(f, b[q][1]),
+                                          tile_partial(f, b[q][2]), tile_partial(f, b[q][3])));
+                const int tok = t0[q] + lane;
+                const bool full = t0[q] >= ks && t0[q] + 64 <= ke;   // uniform
+                const bool valid = ((okm >> q) & 1u) && (full || (tok >= ks && tok < ke));
+                sink((u * U + q) * 64 + lane, lg, valid);
+            }
+        };
+        KTile ka[U][4], kb[U][4];
+        int ta[U], tb[U];
+        uint32_t ma = 0u, mb = 0u;
+        int ua = grab();
+        issue(ua, ka, ta, ma);
+        int ub = grab();
+        issue(ub, kb, tb, mb);
+        while (true) {
+            if (ua < 0) break;
+            finish(ua, ka, ta, ma);
+            ua = grab();
+            issue(ua, ka, ta, ma);
+            if (ub < 0) break;
+            finish(ub, kb, tb, mb);
+            ub = grab();
+            issue(ub, kb, tb, mb);
+        }
+        return;
+    }
     auto issue = [&](int u, KTile (&b)[U][4], int &ttok, uint64_t &okmask) {
         int page = -1, tt = 0;
         if (u >= 0 && lane < 4 * U) desc(u * 4 * U + lane, page, tt);
@@ -704,6 +833,10 @@ struct SparseDesc {
             tok = si[slot] * sbk + tile * 16 % sbk;
         }
     }
+    // 64-column group grp when sbk = 64: its one sparse block
+    __device__ __forceinline__ void group(int grp, int &page, int &tok) const {
+        (*this)(grp * 4, page, tok);
+    }
 };
 
 // Tile descriptor of the dense comparator: tile t is tokens [16t, 16t+16).
@@ -713,6 +846,15 @@ struct DenseDesc {
     __device__ __forceinline__ void operator()(int tile, int &page, int &tok) const {
         const int t0 = tile * 16;
         if (t0 < ke && t0 + 16 > ks) {
+            const int lp = t0 / page_size;
+            if (lp < pages_per_table) page = bt[lp];
+            tok = t0;
+        }
+    }
+    // tokens [64 grp, 64 grp + 64) when page_size is a multiple of 64: one page
+    __device__ __forceinline__ void group(int grp, int &page, int &tok) const {
+        const int t0 = grp * 64;
+        if (t0 < ke && t0 + 64 > ks) {
             const int lp = t0 / page_size;
             if (lp < pages_per_table) page = bt[lp];
             tok = t0;
@@ -1076,7 +1218,7 @@ __device__ __forceinline__ int xcd_grouped_row(int x, int group_rows) {
 // and query, and the row count that places the row): the hardware preloads them into
 // SGPRs at wave launch, so those loads issue at once; ks / ke (only the validity of the
 // scored columns needs them) and the cache geometry arrive while they fly.
-template <int QF, int PW>
+template <int QF, int PW, bool G64>
 __device__ __forceinline__ void score_split_row(
     const int32_t *si_base, const int32_t *pg_base, const void *qv, const void *qs,
     const void *weights, int32_t nsb, int32_t sbk, int32_t groups_per_wg, int32_t group_rows,
@@ -1093,19 +1235,19 @@ __device__ __forceinline__ void score_split_row(
     const int32_t ks_raw = (rows.ks ? rows.ks : rows.ke)[row];   // no load behind a branch
     const int ks = rows.ks ? ks_raw : 0, ke = rows.ke[row];
     float *lrow = logits + (int64_t)row * ncols;
-    score_groups<QF, PW, PW>(k, f, ks, ke, g0, g1, sf, SparseDesc{si, pg, nsb, sbk},
+    score_groups<QF, PW, PW, G64>(k, f, ks, ke, g0, g1, sf, SparseDesc{si, pg, nsb, sbk},
                              [&](int c, float v, bool ok) {
                                  if (c < ncols) lrow[c] = ok ? v : -INFINITY;
                              });
 }
 
-template <int QF, int PW>
+template <int QF, int PW, bool G64>
 __global__ __launch_bounds__(kScoreThreads) void score_split_kernel(
     const int32_t *si_base, const int32_t *pg_base, const void *qv, const void *qs,
     const void *weights, int32_t nsb, int32_t sbk, int32_t groups_per_wg, int32_t group_rows,
     Rows rows, KCache k, float *logits, int32_t sf) {
-    score_split_row<QF, PW>(si_base, pg_base, qv, qs, weights, nsb, sbk, groups_per_wg,
-                            group_rows, rows, k, logits, sf);
+    score_split_row<QF, PW, G64>(si_base, pg_base, qv, qs, weights, nsb, sbk, groups_per_wg,
+                                 group_rows, rows, k, logits, sf);
 }
 
 // Logits of layer l of a multi-layer split launch: the layer's logits_out, else its slice
@@ -1116,7 +1258,7 @@ __device__ __forceinline__ float *layer_logits(const LayerSet &ls, int l, float 
 }
 
 // Several layers sharing a schedule, fewer rows than CUs: grid.z = layer.
-template <int QF, int PW>
+template <int QF, int PW, bool G64>
 __global__ __launch_bounds__(kScoreThreads) void score_split_layers_kernel(
     const int32_t *si_base, const int32_t *pg_base, int32_t nsb, int32_t sbk,
     int32_t groups_per_wg, int32_t group_rows, Rows rows, KCache k, LayerSet ls, float *ws,
@@ -1125,9 +1267,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_split_layers_kernel(
     KCache kl = k;
     kl.values = ls.k_values[l];
     kl.scales = ls.k_scales[l];
-    score_split_row<QF, PW>(si_base, pg_base, ls.q_values[l], ls.q_scales[l], ls.weights[l], nsb,
-                            sbk, groups_per_wg, group_rows, rows, kl,
-                            layer_logits(ls, l, ws, ws_layer), sf);
+    score_split_row<QF, PW, G64>(si_base, pg_base, ls.q_values[l], ls.q_scales[l],
+                                 ls.weights[l], nsb, sbk, groups_per_wg, group_rows, rows, kl,
+                                 layer_logits(ls, l, ws, ws_layer), sf);
 }
 
 // Tokens of the KPT sparse columns c0 .. c0+KPT-1 (KPT divides sbk = 1 << lsbk, and c0
@@ -1272,7 +1414,7 @@ struct FusedLds {
 };
 
 // U: 64-column groups a wave takes per unit (two units in flight).
-template <int QF, int NT, int KPT, int U>
+template <int QF, int NT, int KPT, int U, bool G64>
 __device__ __forceinline__ void fused_row(
     FusedLds<NT> &L, int row, const int32_t *si_base, const int32_t *pg_base, const void *qv,
     const void *qs, const void *weights, const int32_t *p_kept, int32_t nsb, int32_t lsbk,
@@ -1318,7 +1460,7 @@ __device__ __forceinline__ void fused_row(
     const int nunits = (vgroups + U - 1) / U;
     const int valid_cols = ri.valid_cols;
     float *lout = logits_out ? logits_out + (int64_t)row * ri.ncols : nullptr;
-    score_units<QF, U>(
+    score_units<QF, U, G64>(
         k, f, ri.ks, ri.ke, sf,
         [&](int tile, int &page, int &tok) {
             const int c = tile * 16;
@@ -1371,15 +1513,16 @@ __device__ __forceinline__ void fused_row(
 // row a CU), or, with at least two rows per CU, 8 waves held to 128 VGPRs (WPE = 4
 // waves a SIMD) so that two rows share a CU and one selects while the other streams
 // K; fp8 queries: 8 waves of 2-group units.
-template <int QF, int NT, int KPT, int U, int WPE>
+template <int QF, int NT, int KPT, int U, int WPE, bool G64>
 __global__ __launch_bounds__(NT, WPE) void fused_row_kernel(
     const int32_t *si_base, const int32_t *pg_base, const void *qv, const void *qs,
     const void *weights, const int32_t *p_kept, int32_t nsb, int32_t lsbk, int32_t group_rows,
     Rows rows, KCache k, float *logits_out, int32_t topk, int32_t *out, int64_t ostride,
     int32_t sf) {
     __shared__ FusedLds<NT> lds;
-    fused_row<QF, NT, KPT, U>(lds, xcd_grouped_row(blockIdx.x, group_rows), si_base, pg_base, qv, qs, weights, p_kept, nsb, lsbk,
-                           rows, k, logits_out, topk, out, ostride, sf);
+    fused_row<QF, NT, KPT, U, G64>(lds, xcd_grouped_row(blockIdx.x, group_rows), si_base,
+                                   pg_base, qv, qs, weights, p_kept, nsb, lsbk, rows, k,
+                                   logits_out, topk, out, ostride, sf);
 }
 
 // Several consuming layers of one step in one launch (grid.y = layer): the layers share
@@ -1388,7 +1531,7 @@ __global__ __launch_bounds__(NT, WPE) void fused_row_kernel(
 // once, so the layers' launch costs and their start and end skews are paid once.  With
 // MXFP4 queries a row takes 8 waves of one-group units held to 128 VGPRs (WPE = 4 waves
 // a SIMD), so two rows share a CU: one selects while the other streams K.
-template <int QF, int NT, int KPT, int U, int WPE>
+template <int QF, int NT, int KPT, int U, int WPE, bool G64>
 __global__ __launch_bounds__(NT, WPE) void fused_layers_kernel(
     const int32_t *si_base, const int32_t *pg_base, const int32_t *p_kept, int32_t nsb,
     int32_t lsbk, int32_t topk, int32_t group_rows, Rows rows, KCache k, LayerSet ls,
@@ -1398,13 +1541,15 @@ __global__ __launch_bounds__(NT, WPE) void fused_layers_kernel(
     KCache kl = k;
     kl.values = ls.k_values[layer];
     kl.scales = ls.k_scales[layer];
-    fused_row<QF, NT, KPT, U>(lds, xcd_grouped_row(blockIdx.x, group_rows), si_base, pg_base, ls.q_values[layer],
-                           ls.q_scales[layer], ls.weights[layer], p_kept, nsb, lsbk, rows, kl,
-                           ls.logits_out[layer], topk, ls.out[layer], ostride, sf);
+    fused_row<QF, NT, KPT, U, G64>(lds, xcd_grouped_row(blockIdx.x, group_rows), si_base,
+                                   pg_base, ls.q_values[layer], ls.q_scales[layer],
+                                   ls.weights[layer], p_kept, nsb, lsbk, rows, kl,
+                                   ls.logits_out[layer], topk, ls.out[layer], ostride, sf);
 }
 
-// Dense scoring (the comparator): column t is token t, every token < max_ctx.
-template <int QF>
+// Dense scoring (the comparator): column t is token t, every token < max_ctx.  G64: pages
+// hold a multiple of 64 tokens.
+template <int QF, bool G64>
 __global__ __launch_bounds__(kScoreThreads) void score_dense_kernel(
     Rows rows, int32_t max_ctx, const void *qv, const void *qs, const void *weights, KCache k,
     float *logits, int64_t lstride, int groups_per_wg, int32_t sf) {
@@ -1423,11 +1568,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_dense_kernel(
     QFrag<QF> f;
     if (g0 * 64 < ke && g1 * 64 > ks && tbl_ok)
         load_q<QF>(f, qv, qs, weights, sf, row, threadIdx.x & (kWave - 1));
-    score_groups<QF, 4, 2>(k, f, ks, ke, g0, g1, sf,
-                                 DenseDesc{bt, ks, tbl_ok ? ke : 0, k.page_size, k.pages_per_table},
-                                 [&](int t, float v, bool ok) {    // t < ngroups*64 <= lstride
-                                     lrow[t] = ok ? v : -INFINITY;
-                                 });
+    score_groups<QF, 4, 2, G64>(k, f, ks, ke, g0, g1, sf,
+                                DenseDesc{bt, ks, tbl_ok ? ke : 0, k.page_size, k.pages_per_table},
+                                [&](int t, float v, bool ok) {    // t < ngroups*64 <= lstride
+                                    lrow[t] = ok ? v : -INFINITY;
+                                });
 }
 
 // ------------------------------------------------------- candidate source -------
@@ -1444,7 +1589,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_dense_kernel(
 // Scoring with part keys: as score_dense_kernel (same per-column arithmetic), the logits
 // optional (logits may be null), parts [rows][pstride] (pstride = ngroups * 64 / p) with
 // p = 1 << lp (16, 32 or 64).
-template <int QF>
+template <int QF, bool G64>
 __global__ __launch_bounds__(kScoreThreads) void score_pool_kernel(
     Rows rows, int32_t max_ctx, const void *qv, const void *qs, const void *weights, KCache k,
     float *logits, int64_t lstride, uint32_t *parts, int64_t pstride, int32_t lp,
@@ -1467,7 +1612,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_pool_kernel(
     QFrag<QF> f;
     if (g0 * 64 < ke && g1 * 64 > ks && tbl_ok)
         load_q<QF>(f, qv, qs, weights, sf, row, lane);
-    score_groups<QF, 4, 2>(k, f, ks, ke, g0, g1, sf,
+    score_groups<QF, 4, 2, G64>(k, f, ks, ke, g0, g1, sf,
                            DenseDesc{bt, ks, tbl_ok ? ke : 0, k.page_size, k.pages_per_table},
                            [&](int t, float v, bool ok) {   // t < ngroups*64 <= lstride
                                if (lrow) lrow[t] = ok ? v : -INFINITY;
@@ -2124,12 +2269,16 @@ static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const 
         // before the selection, is shorter).  MXFP4 with two or more rows a CU: 8 waves
         // with 1-group units, two rows a CU (measured 23 % faster on 512-2000 rows of 4096
         // columns).  fp8 queries need more registers: 8 waves, 2-group units.
-#define IDX_LAUNCH_FUSED(NT_, KPT_, U_, WPE_)                                                    \
-    hipExtLaunchKernelGGL((fused_row_kernel<QF, NT_, KPT_, U_, WPE_>), dim3(rows.num_rows),       \
+#define IDX_LAUNCH_FUSED_G(NT_, KPT_, U_, WPE_, G64_)                                           \
+    hipExtLaunchKernelGGL((fused_row_kernel<QF, NT_, KPT_, U_, WPE_, G64_>), dim3(rows.num_rows), \
                           dim3(NT_), 0, stream, timing.start, timing.stop, 0, s.sparse_indices,   \
                           s.pages, q_values, q_scales, weights, s.kept, s.nsb, s.lsbk,            \
-                          grouped_rows(rows), rows, k,                                             \
-                          logits_out, topk, out, out_stride, sf)
+                          grouped_rows(rows), rows, k, logits_out, topk, out, out_stride, sf)
+#define IDX_LAUNCH_FUSED(NT_, KPT_, U_, WPE_)                                                    \
+    do {                                                                                           \
+        if (s.sbk == 64) IDX_LAUNCH_FUSED_G(NT_, KPT_, U_, WPE_, true);                            \
+        else IDX_LAUNCH_FUSED_G(NT_, KPT_, U_, WPE_, false);                                       \
+    } while (0)
         if constexpr (QF == 0) {
             if (rows.num_rows < 2 * device_cus()) {
                 if (ncols <= 1024 * 4) IDX_LAUNCH_FUSED(1024, 4, 1, 1);
@@ -2143,6 +2292,7 @@ static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const 
         else if (ncols <= 512 * 8) IDX_LAUNCH_FUSED(512, 8, U, WPE);
         else IDX_LAUNCH_FUSED(512, 16, U, WPE);
 #undef IDX_LAUNCH_FUSED
+#undef IDX_LAUNCH_FUSED_G
         return hipGetLastError();
     }
     float *logits = logits_out ? logits_out : workspace;
@@ -2152,16 +2302,22 @@ static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const 
     int gpw = 8;
     while (gpw < 16 && (int64_t)rows.num_rows * ((ngroups + gpw - 1) / gpw) > 4096) gpw *= 2;
     const dim3 sgrid(rows.num_rows, (ngroups + gpw - 1) / gpw);
+#define IDX_LAUNCH_SPLIT_G(PW_, G64_)                                                              \
+    hipExtLaunchKernelGGL((score_split_kernel<QF, PW_, G64_>), sgrid, dim3(kScoreThreads), 0,      \
+                          stream, timing.start, timing.stop, 0, s.sparse_indices, s.pages,         \
+                          q_values, q_scales, weights, s.nsb, s.sbk, gpw, grouped_rows(rows),      \
+                          rows, k, logits, sf)
+#define IDX_LAUNCH_SPLIT(PW_)                                                                      \
+    do {                                                                                           \
+        if (s.sbk == 64) IDX_LAUNCH_SPLIT_G(PW_, true);                                            \
+        else IDX_LAUNCH_SPLIT_G(PW_, false);                                                       \
+    } while (0)
     if (gpw == 8)
-        hipExtLaunchKernelGGL((score_split_kernel<QF, 2>), sgrid, dim3(kScoreThreads), 0, stream,
-                              timing.start, timing.stop, 0, s.sparse_indices, s.pages, q_values,
-                              q_scales, weights, s.nsb, s.sbk, gpw, grouped_rows(rows), rows, k,
-                              logits, sf);
+        IDX_LAUNCH_SPLIT(2);
     else
-        hipExtLaunchKernelGGL((score_split_kernel<QF, 4>), sgrid, dim3(kScoreThreads), 0, stream,
-                              timing.start, timing.stop, 0, s.sparse_indices, s.pages, q_values,
-                              q_scales, weights, s.nsb, s.sbk, gpw, grouped_rows(rows), rows, k,
-                              logits, sf);
+        IDX_LAUNCH_SPLIT(4);
+#undef IDX_LAUNCH_SPLIT
+#undef IDX_LAUNCH_SPLIT_G
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (ncols <= 8 * kTopkThreads)
@@ -2199,16 +2355,22 @@ static hipError_t launch_split_layers(const Rows &rows, int32_t num_layers, cons
     int gpw = 8;   // as for one layer (launch_sparse_q)
     while (gpw < 16 && (int64_t)rows.num_rows * ((ngroups + gpw - 1) / gpw) > 4096) gpw *= 2;
     const dim3 sgrid(rows.num_rows, (ngroups + gpw - 1) / gpw, num_layers);
+#define IDX_LAUNCH_SPLIT_LAYERS_G(PW_, G64_)                                                       \
+    hipExtLaunchKernelGGL((score_split_layers_kernel<QF, PW_, G64_>), sgrid, dim3(kScoreThreads),  \
+                          0, stream, timing.start, timing.stop, 0, s.sparse_indices, s.pages,      \
+                          s.nsb, s.sbk, gpw, grouped_rows(rows), rows, k, layers, workspace,       \
+                          ws_layer, sf)
+#define IDX_LAUNCH_SPLIT_LAYERS(PW_)                                                               \
+    do {                                                                                           \
+        if (s.sbk == 64) IDX_LAUNCH_SPLIT_LAYERS_G(PW_, true);                                     \
+        else IDX_LAUNCH_SPLIT_LAYERS_G(PW_, false);                                                \
+    } while (0)
     if (gpw == 8)
-        hipExtLaunchKernelGGL((score_split_layers_kernel<QF, 2>), sgrid, dim3(kScoreThreads), 0,
-                              stream, timing.start, timing.stop, 0, s.sparse_indices, s.pages,
-                              s.nsb, s.sbk, gpw, grouped_rows(rows), rows, k, layers, workspace,
-                              ws_layer, sf);
+        IDX_LAUNCH_SPLIT_LAYERS(2);
     else
-        hipExtLaunchKernelGGL((score_split_layers_kernel<QF, 4>), sgrid, dim3(kScoreThreads), 0,
-                              stream, timing.start, timing.stop, 0, s.sparse_indices, s.pages,
-                              s.nsb, s.sbk, gpw, grouped_rows(rows), rows, k, layers, workspace,
-                              ws_layer, sf);
+        IDX_LAUNCH_SPLIT_LAYERS(4);
+#undef IDX_LAUNCH_SPLIT_LAYERS
+#undef IDX_LAUNCH_SPLIT_LAYERS_G
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 tgrid(rows.num_rows, num_layers);
@@ -2264,11 +2426,16 @@ hipError_t launch_sparse_layers(int q_format, int score_format, const Rows &rows
     }
     if (plan == kPlanOneRowLayers) {
         const dim3 grid(rows.num_rows, num_layers);
+#define IDX_LAUNCH_LAYERS_G(QF_, NT_, KPT_, U_, WPE_, G64_)                                      \
+    hipExtLaunchKernelGGL((fused_layers_kernel<QF_, NT_, KPT_, U_, WPE_, G64_>), grid, dim3(NT_),  \
+                          0, stream, timing.start, timing.stop, 0, s.sparse_indices, s.pages,      \
+                          s.kept, s.nsb, s.lsbk, topk, grouped_rows(rows), rows, k, layers,        \
+                          out_stride, sf)
 #define IDX_LAUNCH_LAYERS(QF_, NT_, KPT_, U_, WPE_)                                              \
-    hipExtLaunchKernelGGL((fused_layers_kernel<QF_, NT_, KPT_, U_, WPE_>), grid, dim3(NT_), 0,    \
-                          stream,                                                                  \
-                          timing.start, timing.stop, 0, s.sparse_indices, s.pages, s.kept, s.nsb, \
-                          s.lsbk, topk, grouped_rows(rows), rows, k, layers, out_stride, sf)
+    do {                                                                                           \
+        if (s.sbk == 64) IDX_LAUNCH_LAYERS_G(QF_, NT_, KPT_, U_, WPE_, true);                      \
+        else IDX_LAUNCH_LAYERS_G(QF_, NT_, KPT_, U_, WPE_, false);                                 \
+    } while (0)
         if (q_format == 0) {
             if (ncols <= 512 * 4) IDX_LAUNCH_LAYERS(0, 512, 4, 1, 4);
             else if (ncols <= 512 * 8) IDX_LAUNCH_LAYERS(0, 512, 8, 1, 4);
@@ -2279,6 +2446,7 @@ hipError_t launch_sparse_layers(int q_format, int score_format, const Rows &rows
             else IDX_LAUNCH_LAYERS(1, 512, 16, 2, 1);
         }
 #undef IDX_LAUNCH_LAYERS
+#undef IDX_LAUNCH_LAYERS_G
         return hipGetLastError();
     }
     for (int l = 0; l < num_layers; ++l) {
@@ -2302,14 +2470,19 @@ hipError_t launch_score_dense(int q_format, int score_format, const Rows &rows, 
     const int ngroups = (max_ctx + 63) / 64;
     const int gpw = 16;
     const dim3 grid(rows.num_rows, (ngroups + gpw - 1) / gpw);
-    if (q_format == 0)
-        hipExtLaunchKernelGGL(score_dense_kernel<0>, grid, dim3(kScoreThreads), 0, stream,
-                              timing.start, timing.stop, 0, rows, max_ctx, q_values, q_scales,
-                              weights, k, logits, logits_stride, gpw, score_format);
-    else
-        hipExtLaunchKernelGGL(score_dense_kernel<1>, grid, dim3(kScoreThreads), 0, stream,
-                              timing.start, timing.stop, 0, rows, max_ctx, q_values, q_scales,
-                              weights, k, logits, logits_stride, gpw, score_format);
+#define IDX_LAUNCH_DENSE(QF_, G64_)                                                                \
+    hipExtLaunchKernelGGL((score_dense_kernel<QF_, G64_>), grid, dim3(kScoreThreads), 0, stream,   \
+                          timing.start, timing.stop, 0, rows, max_ctx, q_values, q_scales,         \
+                          weights, k, logits, logits_stride, gpw, score_format)
+    const bool g64 = k.page_size % 64 == 0;
+    if (q_format == 0) {
+        if (g64) IDX_LAUNCH_DENSE(0, true);
+        else IDX_LAUNCH_DENSE(0, false);
+    } else {
+        if (g64) IDX_LAUNCH_DENSE(1, true);
+        else IDX_LAUNCH_DENSE(1, false);
+    }
+#undef IDX_LAUNCH_DENSE
     return hipGetLastError();
 }
 
@@ -2324,16 +2497,19 @@ hipError_t launch_publish(int q_format, int score_format, const Rows &rows, int3
     const int64_t pstride = publish_parts_per_row(max_ctx, cbs);
     const int gpw = 16;
     const dim3 grid(rows.num_rows, (ngroups + gpw - 1) / gpw);
-    if (q_format == 0)
-        hipExtLaunchKernelGGL(score_pool_kernel<0>, grid, dim3(kScoreThreads), 0, stream,
-                              timing.start, timing.stop, 0, rows, max_ctx, q_values, q_scales,
-                              weights, k, logits, logits_stride, parts, pstride, lp, gpw,
-                              score_format);
-    else
-        hipExtLaunchKernelGGL(score_pool_kernel<1>, grid, dim3(kScoreThreads), 0, stream,
-                              timing.start, timing.stop, 0, rows, max_ctx, q_values, q_scales,
-                              weights, k, logits, logits_stride, parts, pstride, lp, gpw,
-                              score_format);
+#define IDX_LAUNCH_POOL(QF_, G64_)                                                                 \
+    hipExtLaunchKernelGGL((score_pool_kernel<QF_, G64_>), grid, dim3(kScoreThreads), 0, stream,    \
+                          timing.start, timing.stop, 0, rows, max_ctx, q_values, q_scales,         \
+                          weights, k, logits, logits_stride, parts, pstride, lp, gpw, score_format)
+    const bool g64 = k.page_size % 64 == 0;
+    if (q_format == 0) {
+        if (g64) IDX_LAUNCH_POOL(0, true);
+        else IDX_LAUNCH_POOL(0, false);
+    } else {
+        if (g64) IDX_LAUNCH_POOL(1, true);
+        else IDX_LAUNCH_POOL(1, false);
+    }
+#undef IDX_LAUNCH_POOL
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     static_assert(8 * kTopkThreads == kMaxPublishBlocks, "one thread's 8 blocks in registers");
