@@ -501,6 +501,38 @@ def test_config5_sparse_equals_dense_masked(q_format):
     np.testing.assert_array_equal(dout.cpu().numpy(), res["indices"])
 
 
+@pytest.mark.parametrize("page_size", [16, 32])
+def test_dense_comparator_on_small_pages(page_size):
+    """The dense comparator on pages shorter than a 64-token group (each group spans
+    several pages, so tiles are resolved one by one): the same indices as the sparse path
+    (checked against the oracle on every row) and logits bitwise equal at the candidate
+    tokens."""
+    import sparse_attention_indexer_candidate_amd as idx
+
+    spec = W.Spec(name=f"dp{page_size}", num_rows=24, page_size=page_size, cbs=page_size,
+                  nb=40, topk=100, ke_rule="uniform", ke_lo=100, ke_hi=2000, ks_rule="random",
+                  cand_rule="messy", fill="all")
+    case = W.generate(spec, seed=13)
+    g, res = run_and_compare(case, tag=f"dense-p{page_size}")
+    R = case.num_rows
+    ctx = int(case.row_ke.max())
+    lstride = (ctx + 63) // 64 * 64
+    dlog = torch.empty((R, lstride), dtype=torch.float32, device=DEV)
+    dout = torch.full((R, spec.topk), -7, dtype=torch.int32, device=DEV)
+    L = g.dcase.layers[0]
+    qv, qs = L.q("mxfp4")
+    idx.idx_dense_masked_logits_topk(g.cfg, g.rows, ctx, qv, qs, L.weights, g.kcaches[0],
+                                     g.sched.struct, dout, dout.stride(0), dlog, dlog.stride(0))
+    torch.cuda.synchronize()
+    dout_np, dl = dout.cpu().numpy(), dlog.cpu().numpy()
+    np.testing.assert_array_equal(dout_np, res["indices"], err_msg="dense != sparse indices")
+    for i in range(R):
+        gt, gl = gpu_row_tokens(res["sparse_indices"][i], int(res["kept"][i]), g.sbk,
+                                int(case.row_ks[i]), int(case.row_ke[i]), res["logits"][i])
+        np.testing.assert_array_equal(dl[i, gt].view(np.uint32), gl.view(np.uint32),
+                                      err_msg=f"dense logits differ bitwise row {i}")
+
+
 LAYERED = {
     # >= 256 rows of one table row each: every layer in one launch
     "one_launch": W.Spec(name="ml1", num_rows=300, page_size=64, cbs=64, nb=24, topk=300,
