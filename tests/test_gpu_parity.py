@@ -107,6 +107,21 @@ SMALL = {
                                            nb=8, topk=100, mode="prefill", ke_rule="uniform",
                                            ke_lo=1, ke_hi=2048, ks_rule="random", context=2048,
                                            cand_rule="messy", fill="all"),
+    # top-1 (a single survivor of the radix search) on the split, one-row and row-group kernels
+    "topk1_split": W.Spec(name="s14", num_rows=30, page_size=64, cbs=64, nb=10, topk=1,
+                          ke_rule="uniform", ke_lo=1, ke_hi=2000, ks_rule="random",
+                          cand_rule="messy", fill="all"),
+    "topk1_rows": W.Spec(name="s15", num_rows=300, page_size=64, cbs=64, nb=10, topk=1,
+                         ke_rule="uniform", ke_lo=1, ke_hi=2000, ks_rule="random",
+                         cand_rule="messy", fill="all"),
+    "topk1_rowgroups": W.Spec(name="s16", num_rows=2050, page_size=64, cbs=64, nb=8, topk=1,
+                              mode="prefill", ke_rule="uniform", ke_lo=1, ke_hi=1500,
+                              ks_rule="random", context=1600, cand_rule="messy", fill="all"),
+    # candidate blocks of four pages each (cbs 256 on 64-token pages: four sparse blocks a
+    # candidate, each on its own page)
+    "cbs256_pages64": W.Spec(name="s17", num_rows=25, page_size=64, cbs=256, nb=6, topk=200,
+                             ke_rule="uniform", ke_lo=100, ke_hi=3000, ks_rule="random",
+                             cand_rule="messy", fill="all"),
 }
 
 
