@@ -416,7 +416,8 @@ int idx_measure_read(const void *src, size_t bytes, uint32_t *sink, void *stream
  *   block scales (k_e2m1 u8 [16][64] packed, k_scales u8 [16][4], device) -> out fp32
  *   [16 rows][16 tokens] (device).  mode 0: the MX-scaled fp8 x fp4 MFMA on the codes;
  *   mode 1: both operands converted exactly to bf16 and the bf16 MFMA, as the fp8-query
- *   scoring kernels do.  One wave; IDX_EINVAL on a bad argument. */
+ *   scoring kernels do; mode 2: the MX-scaled fp8 x fp8 MFMA with K's e2m1 values
+ *   converted exactly to e4m3.  One wave; IDX_EINVAL on a bad argument. */
 int idx_measure_fp8_dot(const uint8_t *q_e4m3, const uint8_t *k_e2m1, const uint8_t *k_scales,
                         int32_t mode, float *out, void *stream);
 int idx_measure_mfma(int32_t iters, float *sink, void *stream);

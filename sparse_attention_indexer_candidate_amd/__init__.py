@@ -356,7 +356,8 @@ def idx_measure_mfma_relu(iters, sink, stream=None):
 
 def idx_measure_fp8_dot(q_e4m3, k_e2m1, k_scales, mode, out, stream=None):
     """16 x 16 e4m3 . (e2m1 x UE8M0) dot products into out (fp32 [16, 16], device):
-    mode 0 the MX-scaled fp8 x fp4 MFMA, mode 1 the exact bf16 route of the kernels."""
+    mode 0 the MX-scaled fp8 x fp4 MFMA, mode 1 the exact bf16 route of the kernels,
+    mode 2 the MX-scaled fp8 x fp8 MFMA on K converted exactly to e4m3."""
     return _check(lib.idx_measure_fp8_dot(_p(q_e4m3), _p(k_e2m1), _p(k_scales), mode, _p(out),
                                           _p(stream)))
 

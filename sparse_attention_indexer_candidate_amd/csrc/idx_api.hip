@@ -619,7 +619,7 @@ int idx_measure_fp8_dot(const uint8_t *q_e4m3, const uint8_t *k_e2m1, const uint
         return fail(IDX_EINVAL, "q_e4m3, k_e2m1, k_scales and out must be non-NULL");
     if (!aligned(q_e4m3, 16) || !aligned(k_e2m1, 16) || !aligned(out, 4))
         return fail(IDX_EINVAL, "q_e4m3 and k_e2m1 must be 16-byte aligned, out 4-byte aligned");
-    if (mode != 0 && mode != 1) return fail(IDX_EINVAL, "mode %d must be 0 or 1", mode);
+    if (mode < 0 || mode > 2) return fail(IDX_EINVAL, "mode %d must be 0, 1 or 2", mode);
     int rc;
     if ((rc = hip_status(idx::launch_measure_fp8_dot(q_e4m3, k_e2m1, k_scales, mode, out,
                                                      (hipStream_t)stream),

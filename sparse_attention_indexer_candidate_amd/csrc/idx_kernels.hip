@@ -2086,14 +2086,42 @@ __global__ __launch_bounds__(kWave) void measure_fp8_dot_kernel(const uint8_t *q
     const uint4 kb = *(const uint4 *)(kv + n * 64 + 16 * g);
     const int ksc = ks[n * 4 + g];
     v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (mode == 0) {
+    if (mode == 0 || mode == 2) {
         // A: row n, bytes j < 16 -> dimension 16g + j, bytes j >= 16 -> 64 + 16g + j - 16
         const uint4 a0 = *(const uint4 *)(q + n * 128 + 16 * g);
         const uint4 a1 = *(const uint4 *)(q + n * 128 + 64 + 16 * g);
         const v8i a = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
                           (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-        const v8i b = v8i{(int)kb.x, (int)kb.y, (int)kb.z, (int)kb.w, 0, 0, 0, 0};
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 4, 0, 127, 0, ksc);
+        if (mode == 0) {
+            const v8i b = v8i{(int)kb.x, (int)kb.y, (int)kb.z, (int)kb.w, 0, 0, 0, 0};
+            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 4, 0, 127, 0,
+                                                                   ksc);
+        } else {
+            // B as e4m3 in A's layout: token n's e2m1 values of dimensions [16g, 16g+16)
+            // (packed bytes [8g, 8g+8)) and [64+16g, 64+16g+16) (bytes [32+8g, 32+8g+8)),
+            // each converted exactly (every e2m1 value is an e4m3 value)
+            const uint2 k0 = *(const uint2 *)(kv + n * 64 + 8 * g);
+            const uint2 k1 = *(const uint2 *)(kv + n * 64 + 32 + 8 * g);
+            const uint32_t src[4] = {k0.x, k0.y, k1.x, k1.y};
+            int b8[8];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                uint32_t lo = 0u, hi = 0u;   // nibbles 0-3 and 4-7 of src[w], low first
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t c = (src[w] >> (4 * j)) & 15u, m = c & 7u;
+                    const uint32_t e = (m == 0u ? 0u : m == 1u ? 0x30u : 0x38u + 4u * (m - 2u)) |
+                                       ((c & 8u) << 4);
+                    if (j < 4) lo |= e << (8 * j);
+                    else hi |= e << (8 * (j - 4));
+                }
+                b8[2 * w] = (int)lo;
+                b8[2 * w + 1] = (int)hi;
+            }
+            const v8i b = v8i{b8[0], b8[1], b8[2], b8[3], b8[4], b8[5], b8[6], b8[7]};
+            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, 127, 0,
+                                                                   ksc);
+        }
     } else {
         // A: row n, dimensions [32g, 32g + 32) as bf16 (the bf16 MFMA's k slot of step s,
         // lane group g, element j carries dimension 32g + 8s + j, as in load_q)

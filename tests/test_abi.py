@@ -315,7 +315,7 @@ def test_bound_calls_check_arguments_like_the_wrappers():
 
 
 def test_fp8_dot_measurement_rejects_bad_arguments():
-    for args in [(None, FAKE, FAKE, 0, FAKE), (FAKE, FAKE, FAKE, 2, FAKE),
+    for args in [(None, FAKE, FAKE, 0, FAKE), (FAKE, FAKE, FAKE, 3, FAKE), (FAKE, FAKE, FAKE, -1, FAKE),
                  (FAKE + 4, FAKE, FAKE, 0, FAKE), (FAKE, FAKE, FAKE, 1, None)]:
         with pytest.raises(idx.IdxError) as e:
             idx.idx_measure_fp8_dot(*args)

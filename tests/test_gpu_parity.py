@@ -1050,13 +1050,14 @@ def test_nan_scale_bytes_follow_the_nan_rule(path, q_format):
 def test_fp8_query_products_need_the_bf16_route():
     """Why fp8 queries go through bf16: the MX-scaled fp8 x fp4 MFMA adds its products in a
     narrow adder.  Worked case: 448 + 2^-9 (e4m3 0x7E and 0x01 against e2m1 1.0) comes out
-    448 from it and exact from the bf16 route.  On random e4m3 / e2m1 data (the workloads'
-    encodings) the logits it gives miss the 1e-5 tolerance, the bf16 route's do not."""
+    448 from it, and from the fp8 x fp8 form on K converted exactly to e4m3, and exact from
+    the bf16 route.  On random e4m3 / e2m1 data (the workloads' encodings) the logits the
+    fp8 x fp4 form gives miss the 1e-5 tolerance, the bf16 route's do not."""
     import sparse_attention_indexer_candidate_amd as idx
 
     def run(q, kv, ks):
         outs = []
-        for mode in (0, 1):
+        for mode in (0, 1, 2):
             out = torch.zeros((16, 16), dtype=torch.float32, device=DEV)
             idx.idx_measure_fp8_dot(torch.from_numpy(q).to(DEV), torch.from_numpy(kv).to(DEV),
                                     torch.from_numpy(ks).to(DEV), mode, out)
@@ -1079,17 +1080,18 @@ def test_fp8_query_products_need_the_bf16_route():
     ks = np.full((16, 4), 127, np.uint8)
     q[0, 0], q[0, 1] = 0x7E, 0x01                                    # 448, 2^-9
     kv[0, 0] = 0x22                                                  # elements 0, 1: 1.0
-    mx, bf = run(q, kv, ks)
+    mx, bf, mx8 = run(q, kv, ks)
     assert mx[0, 0] == 448.0, mx[0, 0]
     assert bf[0, 0] == 448.0 + 2.0 ** -9, bf[0, 0]
+    assert mx8[0, 0] != 448.0 + 2.0 ** -9, mx8[0, 0]
 
     # workload-shaped data: the fp8 query recipe (N(0,1), row scale max/448, e4m3 codes)
     # for 16 heads, e2m1 K of N(0,1) with scales 2^[-4, 4]; 16 heads with U(0,1)/8 weights
     # give each token's logit sum_h w_h ReLU(dot), checked against 1e-6 + 1e-5 |logit|
     rng = np.random.default_rng(7)
     spec = W.Spec(name="acc", num_rows=1, num_heads=16, head_dim=128, q_formats=("fp8",))
-    bad = {0: 0, 1: 0}
-    worst = {0: 0.0, 1: 0.0}
+    bad = {0: 0, 1: 0, 2: 0}
+    worst = {0: 0.0, 1: 0.0, 2: 0.0}
     for trial in range(200):
         q8, rs = W._draw_q_fp8(spec, rng)
         q = np.ascontiguousarray(q8[0])
@@ -1104,7 +1106,8 @@ def test_fp8_query_products_need_the_bf16_route():
             bad[mode] += int((err > 1e-6 + 1e-5 * np.abs(lw)).sum())
             worst[mode] = max(worst[mode], float(np.max(err / np.abs(lw))))
     _say(f"[fp8 products] 3200 logits outside the tolerance: MX fp8 x fp4 {bad[0]} (worst "
-         f"relative error {worst[0]:.1e}), bf16 route {bad[1]} (worst {worst[1]:.1e})")
+         f"relative error {worst[0]:.1e}), MX fp8 x fp8 {bad[2]} (worst {worst[2]:.1e}), "
+         f"bf16 route {bad[1]} (worst {worst[1]:.1e})")
     assert bad[1] == 0
     assert bad[0] > 0
 
