@@ -36,15 +36,18 @@ HBM_PEAK_GBS = 8000.0
 MXFP4_PEAK_TFLOPS = 10066.0
 VALU_PEAK_TLANEOPS = 256 * 4 * 16 * 2.4e9 / 1e12   # 39.3: one op a lane a cycle, every SIMD
 EVENT_STEPS = 64           # steps of the event-timed pass (each times its scoring launches)
-KERNEL_SOURCES = ["sparse_attention_indexer_candidate_amd/csrc/idx_kernels.hip",
-                  "sparse_attention_indexer_candidate_amd/csrc/idx_api.hip"]
+KERNEL_SOURCE_DIR = "sparse_attention_indexer_candidate_amd/csrc"
 
 
 def kernel_source_hash() -> str:
+    """Hash of every library source (csrc/*.hip, csrc/*.h), which a stored traffic count
+    must match to be reported."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+    d = os.path.join(ROOT, KERNEL_SOURCE_DIR)
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 

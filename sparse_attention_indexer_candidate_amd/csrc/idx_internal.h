@@ -1,5 +1,7 @@
 // Internal interface between the C-ABI entry points (idx_api.hip) and the kernel
-// launchers (idx_kernels.hip).  Not installed; not part of the ABI.
+// launchers (idx_expand.hip, idx_sparse.hip, idx_row_groups.hip, idx_dense.hip,
+// idx_gather.hip, idx_measure.hip; their shared device code is idx_device.h).  Not
+// installed; not part of the ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -119,6 +121,18 @@ hipError_t launch_sparse_layers(int q_format, int score_format, const Rows &rows
                                 const Schedule &s, float *workspace, size_t workspace_bytes,
                                 int32_t topk, int64_t out_stride, const Timing &timing,
                                 hipStream_t stream);
+
+// Row groups (plan kPlanRowGroup / kPlanRowGroupLayers; MXFP4 queries, sbk = 64, NB*cbs <=
+// 8192): two rows a workgroup share K tiles, logits in LDS, selected in turn.  Called by
+// launch_sparse / launch_sparse_layers when their plan says so; the events ride on the
+// launch.
+hipError_t launch_row_groups(const Rows &rows, const void *q_values, const void *q_scales,
+                             const void *weights, int sf, const KCache &k, const Schedule &s,
+                             float *logits_out, int32_t topk, int32_t *out, int64_t out_stride,
+                             const Timing &timing, hipStream_t stream);
+hipError_t launch_row_groups_layers(const Rows &rows, int32_t num_layers, const LayerSet &layers,
+                                    int sf, const KCache &k, const Schedule &s, int32_t topk,
+                                    int64_t out_stride, const Timing &timing, hipStream_t stream);
 
 // Scores every token t < max_ctx of every row into logits [rows][logits_stride]
 // (-inf outside [ks, ke)).

@@ -1,0 +1,498 @@
+// Sparse scoring and selection over the step's schedule, and the choice among the
+// launch shapes (plan_sparse):
+//
+//  fused_row_kernel     rows >= CUs: one workgroup scores a whole row into LDS
+//                       and selects from LDS (no global round trip, no cross-workgroup
+//                       sync); MXFP4 with >= 2 rows a CU: 8-wave rows, two a CU
+//  fused_layers_kernel  the one-row kernel for several layers sharing a schedule, one
+//                       launch (grid.y = layer); MXFP4: 8-wave rows, two a CU, so one
+//                       row's selection overlaps another's K stream
+//  score_split_kernel + topk_split_kernel
+//                       fewer rows than CUs: rows split over workgroups, logits in
+//                       global scratch, selection in a second launch (and the
+//                       multi-layer pair, grid.z / grid.y = layer)
+//  row groups           >= 8 rows a CU with MXFP4 queries: idx_row_groups.hip
+
+#include "idx_device.h"
+
+namespace idx {
+namespace {
+
+// Rows of one request (speculative / MTP rows: consecutive rows on one table row) read
+// mostly the same K blocks.  Workgroups go to the 8 XCDs round-robin by linear id, and
+// each XCD has its own L2, so when the caller declares such rows (rows_per_request > 1)
+// blockIdx.x is mapped to rows such that the 8 consecutive rows of every aligned group
+// of 8 run on one XCD (their blockIdx.x values lie 8 apart, so they are also dispatched
+// close together) and a block that several of them read crosses the fabric once.
+// group_rows: the row count with that placement, 0 for none (identity); rows past the
+// last whole 64-row block keep their index.  Measured on 64 requests of two decode rows
+// (split kernels): 18.2-18.5 vs 19.2-19.9 us a step, the scoring kernel's fetches down
+// from 35.6 MB to the 22.5 MB of distinct blocks; on 256 requests of two rows and 128 of
+// four (one-row kernel): 33.6-35.4 vs 37.3-38.3 and 32.3-33.0 vs 38.7-39.4 us.  Rows that
+// share nothing lose ~2 % with it in the one-row kernel, hence the hint.  (A
+// one-dimensional grid with the same placement was ~3 us slower on every workload.)
+__device__ __forceinline__ int xcd_grouped_row(int x, int group_rows) {
+    const int full = group_rows & ~63;
+    return x < full ? (x & ~63) + 8 * (x & 7) + ((x >> 3) & 7) : x;
+}
+
+// Rows split over workgroups: grid = (rows, chunks of groups_per_wg 64-column groups);
+// each wave scores a contiguous quarter of its workgroup's groups into logits.  The
+// leading scalar arguments are what the first loads need (the row's schedule entries
+// and query, and the row count that places the row): the hardware preloads them into
+// SGPRs at wave launch, so those loads issue at once; ks / ke (only the validity of the
+// scored columns needs them) and the cache geometry arrive while they fly.
+template <int QF, int PW, bool G64>
+__device__ __forceinline__ void score_split_row(
+    const int32_t *si_base, const int32_t *pg_base, const void *qv, const void *qs,
+    const void *weights, int32_t nsb, int32_t sbk, int32_t groups_per_wg, int32_t group_rows,
+    const Rows &rows, const KCache &k, float *logits, int sf) {
+    const int row = xcd_grouped_row(blockIdx.x, group_rows);
+    const int wave = uniform(threadIdx.x / kWave);
+    const int ncols = nsb * sbk;
+    const int ngroups = (ncols + 63) / 64;
+    const int g0 = min(blockIdx.y * groups_per_wg + wave * PW, ngroups);
+    const int g1 = min(g0 + PW, ngroups);
+    QFrag<QF> f;
+    load_q<QF>(f, qv, qs, weights, sf, row, threadIdx.x & (kWave - 1));
+    const int32_t *si = si_base + (int64_t)row * nsb, *pg = pg_base + (int64_t)row * nsb;
+    const int32_t ks_raw = (rows.ks ? rows.ks : rows.ke)[row];   // no load behind a branch
+    const int ks = rows.ks ? ks_raw : 0, ke = rows.ke[row];
+    float *lrow = logits + (int64_t)row * ncols;
+    score_groups<QF, PW, PW, G64>(k, f, ks, ke, g0, g1, sf, SparseDesc{si, pg, nsb, sbk},
+                             [&](int c, float v, bool ok) {
+                                 if (c < ncols) lrow[c] = ok ? v : -INFINITY;
+                             });
+}
+
+template <int QF, int PW, bool G64>
+__global__ __launch_bounds__(kScoreThreads) void score_split_kernel(
+    const int32_t *si_base, const int32_t *pg_base, const void *qv, const void *qs,
+    const void *weights, int32_t nsb, int32_t sbk, int32_t groups_per_wg, int32_t group_rows,
+    Rows rows, KCache k, float *logits, int32_t sf) {
+    score_split_row<QF, PW, G64>(si_base, pg_base, qv, qs, weights, nsb, sbk, groups_per_wg,
+                                 group_rows, rows, k, logits, sf);
+}
+
+// Logits of layer l of a multi-layer split launch: the layer's logits_out, else its slice
+// of the workspace.
+__device__ __forceinline__ float *layer_logits(const LayerSet &ls, int l, float *ws,
+                                               int64_t ws_layer) {
+    return ls.logits_out[l] ? ls.logits_out[l] : ws + (int64_t)l * ws_layer;
+}
+
+// Several layers sharing a schedule, fewer rows than CUs: grid.z = layer.
+template <int QF, int PW, bool G64>
+__global__ __launch_bounds__(kScoreThreads) void score_split_layers_kernel(
+    const int32_t *si_base, const int32_t *pg_base, int32_t nsb, int32_t sbk,
+    int32_t groups_per_wg, int32_t group_rows, Rows rows, KCache k, LayerSet ls, float *ws,
+    int64_t ws_layer, int32_t sf) {
+    const int l = blockIdx.z;
+    KCache kl = k;
+    kl.values = ls.k_values[l];
+    kl.scales = ls.k_scales[l];
+    score_split_row<QF, PW, G64>(si_base, pg_base, ls.q_values[l], ls.q_scales[l],
+                                 ls.weights[l], nsb, sbk, groups_per_wg, group_rows, rows, kl,
+                                 layer_logits(ls, l, ws, ws_layer), sf);
+}
+
+// The selection of a multi-layer split launch: grid.y = layer.
+template <int KPT>
+__global__ __launch_bounds__(kTopkThreads) void topk_split_layers_kernel(
+    const int32_t *si_base, const int32_t *p_ks, const int32_t *p_ke, const int32_t *p_kept,
+    int32_t nsb, int32_t lsbk, int32_t topk, LayerSet ls, float *ws, int64_t ws_layer,
+    int64_t ostride) {
+    __shared__ TopkLds lds;
+    const int l = blockIdx.y;
+    topk_split_row<false, KPT>(lds, layer_logits(ls, l, ws, ws_layer), si_base, p_ks, p_ke, p_kept,
+                               nsb, lsbk, (int64_t)0, 0, topk, ls.out[l], ostride);
+}
+
+// Rows >= CUs: one workgroup per row; waves take units of the row's valid 64-column
+// groups from a shared counter, logits stay in LDS, then the same workgroup selects.
+// logits_out (optional) gets a copy of every column.  The table row is not checked
+// here: the expansion lists nothing for a row whose table row is invalid (kept = 0),
+// and the schedule comes from the expansion of the same rows.
+template <int NT>
+struct FusedLds {
+    alignas(16) uint32_t word[kMaxRowCols];   // column words (bits_key), then the stage
+    int32_t si[kMaxNSB];
+    int32_t pg[kMaxNSB];
+    int unit;
+    SelectLds<NT, 5> sel;
+};
+
+// U: 64-column groups a wave takes per unit (two units in flight).
+template <int QF, int NT, int KPT, int U, bool G64>
+__device__ __forceinline__ void fused_row(
+    FusedLds<NT> &L, int row, const int32_t *si_base, const int32_t *pg_base, const void *qv,
+    const void *qs, const void *weights, const int32_t *p_kept, int32_t nsb, int32_t lsbk,
+    const Rows &rows, const KCache &k, float *logits_out, int32_t topk, int32_t *out,
+    int64_t ostride, int sf) {
+    uint32_t *s_word = L.word;
+    int32_t *s_si = L.si;
+    int32_t *s_pg = L.pg;
+    int &s_unit = L.unit;
+    SelectLds<NT, 5> &s_sel = L.sel;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int sbk = 1 << lsbk;
+    RowInfo ri;
+    ri.si = si_base + (int64_t)row * nsb;
+    ri.pg = pg_base + (int64_t)row * nsb;
+    ri.kept = max(0, min(uniform(p_kept[row]), nsb));
+    ri.valid_cols = ri.kept * sbk;
+    ri.ncols = nsb * sbk;
+    ri.tbl_ok = true;
+    QFrag<QF> f;
+    load_q<QF>(f, qv, qs, weights, sf, row, lane);   // overlaps the schedule copy
+    // Every slot [0, nsb) is written by the expansion (-1 past the kept count), so the
+    // copy is not bound by the kept load: the schedule, the kept count and the query
+    // are one memory round trip, not two.
+    for (int i = tid; i < nsb; i += NT) {
+        s_si[i] = ri.si[i];
+        s_pg[i] = ri.pg[i];
+    }
+    // ks / ke (their pointers are not preloaded) are needed only for the validity of the
+    // scored columns; loaded after the first loads so no wait for them comes first
+    const int vrow = row + opaque_zero();
+    const int32_t ks_raw = (rows.ks ? rows.ks : rows.ke)[vrow];   // no load behind a branch
+    ri.ks = rows.ks ? ks_raw : 0;
+    ri.ke = rows.ke[vrow];
+    if (tid == 0) s_unit = 0;
+    select_clear(s_sel);
+    __syncthreads();
+    // The selection's first digit is counted while scoring (the scoring waits on
+    // memory, so the extra instructions are free): valid keys per key >> 23.
+    int nv = 0;
+    int *hist0 = &s_sel.hist[0][0];
+    const int vgroups = (ri.valid_cols + 63) / 64;
+    const int nunits = (vgroups + U - 1) / U;
+    const int valid_cols = ri.valid_cols;
+    float *lout = logits_out ? logits_out + (int64_t)row * ri.ncols : nullptr;
+    score_units<QF, U, G64>(
+        k, f, ri.ks, ri.ke, sf,
+        [&](int tile, int &page, int &tok) {
+            const int c = tile * 16;
+            if (c < valid_cols) {
+                const int slot = c / sbk;
+                page = s_pg[slot];
+                tok = s_si[slot] * sbk + c % sbk;
+            }
+        },
+        [&]() {
+            int u = 0;
+            if (lane == 0) u = atomicAdd(&s_unit, 1);
+            u = uniform(u);
+            return u < nunits ? u : -1;
+        },
+        [&](int c, float lg, bool valid) {
+            if (c < ri.ncols) {
+                const uint32_t w = valid ? __float_as_uint(lg) : kNoColumn;
+                s_word[c] = w;
+                if (lout) lout[c] = valid ? lg : -INFINITY;
+                if (valid) {
+                    ++nv;
+                    atomicAdd(hist0 + (bits_key(w) >> 23), 1);
+                }
+            }
+        });
+    if (lout)
+        for (int c = vgroups * 64 + tid; c < ri.ncols; c += NT) lout[c] = -INFINITY;
+    int nvalid;
+    uint32_t kmin, kmax;   // not needed with the first digit counted
+    block_stats_combine<NT>(wave_scan((uint32_t)nv, 0u, OpAdd{}), 0u, 0u, s_sel, nvalid, kmin,
+                            kmax);   // also publishes s_word, s_si and the first digit
+    uint32_t key[KPT];
+#pragma unroll
+    for (int i = 0; i < KPT; i += 4) {
+        const int c = tid * KPT + i;   // columns past valid_cols: stale LDS, read but not used
+        const uint4 x = *reinterpret_cast<const uint4 *>(&s_word[c]);
+        key[i] = c < ri.valid_cols ? bits_key(x.x) : 0u;
+        key[i + 1] = c + 1 < ri.valid_cols ? bits_key(x.y) : 0u;
+        key[i + 2] = c + 2 < ri.valid_cols ? bits_key(x.z) : 0u;
+        key[i + 3] = c + 3 < ri.valid_cols ? bits_key(x.w) : 0u;
+    }
+    select_topk<NT, KPT, true>(key, keys_live(key), nvalid, kmin, kmax, topk, out + (int64_t)row * ostride, s_sel,
+                         reinterpret_cast<int32_t *>(s_word), SparseTokens<KPT>{s_si, lsbk});
+}
+
+// One layer.  The leading scalar arguments are what the first loads need (the row's
+// schedule entries and kept count, its query): preloaded into SGPRs at wave launch, so
+// those loads are one round trip.  MXFP4 queries: 16 waves of one-group units a row (one
+// row a CU), or, with at least two rows per CU, 8 waves held to 128 VGPRs (WPE = 4
+// waves a SIMD) so that two rows share a CU and one selects while the other streams
+// K; fp8 queries: 8 waves of 2-group units.
+template <int QF, int NT, int KPT, int U, int WPE, bool G64>
+__global__ __launch_bounds__(NT, WPE) void fused_row_kernel(
+    const int32_t *si_base, const int32_t *pg_base, const void *qv, const void *qs,
+    const void *weights, const int32_t *p_kept, int32_t nsb, int32_t lsbk, int32_t group_rows,
+    Rows rows, KCache k, float *logits_out, int32_t topk, int32_t *out, int64_t ostride,
+    int32_t sf) {
+    __shared__ FusedLds<NT> lds;
+    fused_row<QF, NT, KPT, U, G64>(lds, xcd_grouped_row(blockIdx.x, group_rows), si_base,
+                                   pg_base, qv, qs, weights, p_kept, nsb, lsbk, rows, k,
+                                   logits_out, topk, out, ostride, sf);
+}
+
+// Several consuming layers of one step in one launch (grid.y = layer): the layers share
+// the rows, the schedule and the cache geometry, and differ in their query, weights, K
+// pool and outputs.  A CU that finishes a row of one layer starts a row of the next at
+// once, so the layers' launch costs and their start and end skews are paid once.  With
+// MXFP4 queries a row takes 8 waves of one-group units held to 128 VGPRs (WPE = 4 waves
+// a SIMD), so two rows share a CU: one selects while the other streams K.
+template <int QF, int NT, int KPT, int U, int WPE, bool G64>
+__global__ __launch_bounds__(NT, WPE) void fused_layers_kernel(
+    const int32_t *si_base, const int32_t *pg_base, const int32_t *p_kept, int32_t nsb,
+    int32_t lsbk, int32_t topk, int32_t group_rows, Rows rows, KCache k, LayerSet ls,
+    int64_t ostride, int32_t sf) {
+    __shared__ FusedLds<NT> lds;
+    const int layer = blockIdx.y;
+    KCache kl = k;
+    kl.values = ls.k_values[layer];
+    kl.scales = ls.k_scales[layer];
+    fused_row<QF, NT, KPT, U, G64>(lds, xcd_grouped_row(blockIdx.x, group_rows), si_base,
+                                   pg_base, ls.q_values[layer], ls.q_scales[layer],
+                                   ls.weights[layer], p_kept, nsb, lsbk, rows, kl,
+                                   ls.logits_out[layer], topk, ls.out[layer], ostride, sf);
+}
+
+}  // namespace
+
+// group_rows argument of the decode scoring kernels (see xcd_grouped_row).
+static int32_t grouped_rows(const Rows &rows) {
+    return rows.rows_per_request > 1 ? rows.num_rows : 0;
+}
+
+int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+
+Plan plan_sparse(int q_format, int32_t sbk, int32_t ncols, int32_t num_rows, int32_t num_layers,
+                 int cus, bool logits_home) {
+    if (num_rows <= 0 || num_layers <= 0) return kPlanNone;
+    // At least 8 rows per CU with MXFP4 queries and 64-token sparse blocks: row groups
+    // (K tiles shared across the rows of a table).
+    const bool groups = q_format == 0 && sbk == 64 && ncols <= 8192 && num_rows >= 8 * cus;
+    if (groups) return num_layers >= 2 ? kPlanRowGroupLayers : kPlanRowGroup;
+    if (num_rows >= cus) return num_layers >= 2 ? kPlanOneRowLayers : kPlanOneRow;
+    // Fewer rows than CUs but at least as many row-layers: one workgroup a row-layer, all
+    // layers in one launch (measured 14-25 % faster steps than the split launch pair on
+    // 64- and 128-row decode batches with 2 to 8 layers, both query formats: the
+    // selection runs in the scoring launch and no logits leave it).
+    if (num_layers >= 2 && (int64_t)num_rows * num_layers >= cus) return kPlanOneRowLayers;
+    // otherwise every layer in one split launch pair when each layer's logits have a
+    // home, else layer by layer
+    return num_layers >= 2 && logits_home ? kPlanSplitLayers : kPlanSplit;
+}
+
+template <int QF>
+static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const void *q_scales,
+                                  const void *weights, int sf, const KCache &k, const Schedule &s,
+                                  float *logits_out, float *workspace, int32_t topk, int32_t *out,
+                                  int64_t out_stride, const Timing &timing, hipStream_t stream) {
+    hipError_t e;
+    const int ncols = s.nsb * s.sbk;
+    const int ngroups = (ncols + 63) / 64;
+    const Plan plan = plan_sparse(QF, s.sbk, ncols, rows.num_rows, 1, device_cus(), true);
+    if constexpr (QF == 0) {
+        if (plan == kPlanRowGroup)
+            return launch_row_groups(rows, q_values, q_scales, weights, sf, k, s, logits_out,
+                                     topk, out, out_stride, timing, stream);
+    }
+    if (plan == kPlanOneRow) {
+        // MXFP4, one row a CU: 16 waves with 1-group units (measured 10 % faster 4-layer
+        // steps than 8 waves with 4-group units: the row's last unit, and so the wait
+        // before the selection, is shorter).  MXFP4 with two or more rows a CU: 8 waves
+        // with 1-group units, two rows a CU (measured 23 % faster on 512-2000 rows of 4096
+        // columns).  fp8 queries need more registers: 8 waves, 2-group units.
+#define IDX_LAUNCH_FUSED_G(NT_, KPT_, U_, WPE_, G64_)                                           \
+    hipExtLaunchKernelGGL((fused_row_kernel<QF, NT_, KPT_, U_, WPE_, G64_>), dim3(rows.num_rows), \
+                          dim3(NT_), 0, stream, timing.start, timing.stop, 0, s.sparse_indices,   \
+                          s.pages, q_values, q_scales, weights, s.kept, s.nsb, s.lsbk,            \
+                          grouped_rows(rows), rows, k, logits_out, topk, out, out_stride, sf)
+#define IDX_LAUNCH_FUSED(NT_, KPT_, U_, WPE_)                                                    \
+    do {                                                                                           \
+        if (s.sbk == 64) IDX_LAUNCH_FUSED_G(NT_, KPT_, U_, WPE_, true);                            \
+        else IDX_LAUNCH_FUSED_G(NT_, KPT_, U_, WPE_, false);                                       \
+    } while (0)
+        if constexpr (QF == 0) {
+            if (rows.num_rows < 2 * device_cus()) {
+                if (ncols <= 1024 * 4) IDX_LAUNCH_FUSED(1024, 4, 1, 1);
+                else IDX_LAUNCH_FUSED(1024, 8, 1, 1);
+                return hipGetLastError();
+            }
+        }
+        constexpr int U = QF == 0 ? 1 : 2;
+        constexpr int WPE = QF == 0 ? 4 : 1;
+        if (ncols <= 512 * 4) IDX_LAUNCH_FUSED(512, 4, U, WPE);
+        else if (ncols <= 512 * 8) IDX_LAUNCH_FUSED(512, 8, U, WPE);
+        else IDX_LAUNCH_FUSED(512, 16, U, WPE);
+#undef IDX_LAUNCH_FUSED
+#undef IDX_LAUNCH_FUSED_G
+        return hipGetLastError();
+    }
+    float *logits = logits_out ? logits_out : workspace;
+    // Enough workgroups to cover the CUs several times over; 4 waves each with two or
+    // more 64-column groups (two groups a wave hide the schedule-to-K load chain better
+    // than one: measured 3-7 % faster steps on 64- and 128-row decode batches).
+    int gpw = 8;
+    while (gpw < 16 && (int64_t)rows.num_rows * ((ngroups + gpw - 1) / gpw) > 4096) gpw *= 2;
+    const dim3 sgrid(rows.num_rows, (ngroups + gpw - 1) / gpw);
+#define IDX_LAUNCH_SPLIT_G(PW_, G64_)                                                              \
+    hipExtLaunchKernelGGL((score_split_kernel<QF, PW_, G64_>), sgrid, dim3(kScoreThreads), 0,      \
+                          stream, timing.start, timing.stop, 0, s.sparse_indices, s.pages,         \
+                          q_values, q_scales, weights, s.nsb, s.sbk, gpw, grouped_rows(rows),      \
+                          rows, k, logits, sf)
+#define IDX_LAUNCH_SPLIT(PW_)                                                                      \
+    do {                                                                                           \
+        if (s.sbk == 64) IDX_LAUNCH_SPLIT_G(PW_, true);                                            \
+        else IDX_LAUNCH_SPLIT_G(PW_, false);                                                       \
+    } while (0)
+    if (gpw == 8)
+        IDX_LAUNCH_SPLIT(2);
+    else
+        IDX_LAUNCH_SPLIT(4);
+#undef IDX_LAUNCH_SPLIT
+#undef IDX_LAUNCH_SPLIT_G
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (ncols <= 8 * kTopkThreads)
+        hipLaunchKernelGGL((topk_split_kernel<false, 8>), dim3(rows.num_rows), dim3(kTopkThreads), 0,
+                           stream, logits, s.sparse_indices, rows.ks, rows.ke, s.kept, s.nsb, s.lsbk,
+                           (int64_t)0, 0, topk, out, out_stride);
+    else
+        hipLaunchKernelGGL((topk_split_kernel<false, 16>), dim3(rows.num_rows), dim3(kTopkThreads), 0,
+                           stream, logits, s.sparse_indices, rows.ks, rows.ke, s.kept, s.nsb, s.lsbk,
+                           (int64_t)0, 0, topk, out, out_stride);
+    return hipGetLastError();
+}
+
+hipError_t launch_sparse(int q_format, int score_format, const Rows &rows, const void *q_values,
+                         const void *q_scales, const void *weights, const KCache &k,
+                         const Schedule &s, float *logits_out, float *workspace, int32_t topk,
+                         int32_t *out, int64_t out_stride, const Timing &timing,
+                         hipStream_t stream) {
+    if (rows.num_rows == 0) return hipSuccess;
+    if (q_format == 0)
+        return launch_sparse_q<0>(rows, q_values, q_scales, weights, score_format, k, s,
+                                  logits_out, workspace, topk, out, out_stride, timing, stream);
+    return launch_sparse_q<1>(rows, q_values, q_scales, weights, score_format, k, s, logits_out,
+                              workspace, topk, out, out_stride, timing, stream);
+}
+
+template <int QF>
+static hipError_t launch_split_layers(const Rows &rows, int32_t num_layers, const LayerSet &layers,
+                                      int sf, const KCache &k, const Schedule &s, float *workspace,
+                                      int32_t topk, int64_t out_stride, const Timing &timing,
+                                      hipStream_t stream) {
+    const int ncols = s.nsb * s.sbk;
+    const int ngroups = (ncols + 63) / 64;
+    const int64_t ws_layer = (int64_t)rows.num_rows * ncols;
+    int gpw = 8;   // as for one layer (launch_sparse_q)
+    while (gpw < 16 && (int64_t)rows.num_rows * ((ngroups + gpw - 1) / gpw) > 4096) gpw *= 2;
+    const dim3 sgrid(rows.num_rows, (ngroups + gpw - 1) / gpw, num_layers);
+#define IDX_LAUNCH_SPLIT_LAYERS_G(PW_, G64_)                                                       \
+    hipExtLaunchKernelGGL((score_split_layers_kernel<QF, PW_, G64_>), sgrid, dim3(kScoreThreads),  \
+                          0, stream, timing.start, timing.stop, 0, s.sparse_indices, s.pages,      \
+                          s.nsb, s.sbk, gpw, grouped_rows(rows), rows, k, layers, workspace,       \
+                          ws_layer, sf)
+#define IDX_LAUNCH_SPLIT_LAYERS(PW_)                                                               \
+    do {                                                                                           \
+        if (s.sbk == 64) IDX_LAUNCH_SPLIT_LAYERS_G(PW_, true);                                     \
+        else IDX_LAUNCH_SPLIT_LAYERS_G(PW_, false);                                                \
+    } while (0)
+    if (gpw == 8)
+        IDX_LAUNCH_SPLIT_LAYERS(2);
+    else
+        IDX_LAUNCH_SPLIT_LAYERS(4);
+#undef IDX_LAUNCH_SPLIT_LAYERS
+#undef IDX_LAUNCH_SPLIT_LAYERS_G
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 tgrid(rows.num_rows, num_layers);
+    if (ncols <= 8 * kTopkThreads)
+        hipLaunchKernelGGL((topk_split_layers_kernel<8>), tgrid, dim3(kTopkThreads), 0, stream,
+                           s.sparse_indices, rows.ks, rows.ke, s.kept, s.nsb, s.lsbk, topk, layers,
+                           workspace, ws_layer, out_stride);
+    else
+        hipLaunchKernelGGL((topk_split_layers_kernel<16>), tgrid, dim3(kTopkThreads), 0, stream,
+                           s.sparse_indices, rows.ks, rows.ke, s.kept, s.nsb, s.lsbk, topk, layers,
+                           workspace, ws_layer, out_stride);
+    return hipGetLastError();
+}
+
+hipError_t launch_sparse_layers(int q_format, int score_format, const Rows &rows,
+                                int32_t num_layers, const LayerSet &layers, const KCache &k,
+                                const Schedule &s, float *workspace, size_t workspace_bytes,
+                                int32_t topk, int64_t out_stride, const Timing &timing,
+                                hipStream_t stream) {
+    const int sf = score_format;
+    if (rows.num_rows == 0 || num_layers == 0) return hipSuccess;
+    const int ncols = s.nsb * s.sbk;
+    // every layer's logits must have a home for the batched split launches: its
+    // logits_out or its slice of the workspace
+    bool all_out = true;
+    for (int l = 0; l < num_layers; ++l) all_out = all_out && layers.logits_out[l];
+    const size_t need = (size_t)num_layers * rows.num_rows * ncols * sizeof(float);
+    const bool home = all_out || (workspace && workspace_bytes >= need);
+    const Plan plan = plan_sparse(q_format, s.sbk, ncols, rows.num_rows, num_layers, device_cus(),
+                                  home);
+    if (plan == kPlanRowGroupLayers)
+        return launch_row_groups_layers(rows, num_layers, layers, sf, k, s, topk, out_stride,
+                                        timing, stream);
+    if (plan == kPlanSplitLayers) {
+        if (q_format == 0)
+            return launch_split_layers<0>(rows, num_layers, layers, sf, k, s, workspace, topk,
+                                          out_stride, timing, stream);
+        return launch_split_layers<1>(rows, num_layers, layers, sf, k, s, workspace, topk,
+                                      out_stride, timing, stream);
+    }
+    if (plan == kPlanOneRowLayers) {
+        const dim3 grid(rows.num_rows, num_layers);
+#define IDX_LAUNCH_LAYERS_G(QF_, NT_, KPT_, U_, WPE_, G64_)                                      \
+    hipExtLaunchKernelGGL((fused_layers_kernel<QF_, NT_, KPT_, U_, WPE_, G64_>), grid, dim3(NT_),  \
+                          0, stream, timing.start, timing.stop, 0, s.sparse_indices, s.pages,      \
+                          s.kept, s.nsb, s.lsbk, topk, grouped_rows(rows), rows, k, layers,        \
+                          out_stride, sf)
+#define IDX_LAUNCH_LAYERS(QF_, NT_, KPT_, U_, WPE_)                                              \
+    do {                                                                                           \
+        if (s.sbk == 64) IDX_LAUNCH_LAYERS_G(QF_, NT_, KPT_, U_, WPE_, true);                      \
+        else IDX_LAUNCH_LAYERS_G(QF_, NT_, KPT_, U_, WPE_, false);                                 \
+    } while (0)
+        if (q_format == 0) {
+            if (ncols <= 512 * 4) IDX_LAUNCH_LAYERS(0, 512, 4, 1, 4);
+            else if (ncols <= 512 * 8) IDX_LAUNCH_LAYERS(0, 512, 8, 1, 4);
+            else IDX_LAUNCH_LAYERS(0, 512, 16, 1, 4);
+        } else {
+            if (ncols <= 512 * 4) IDX_LAUNCH_LAYERS(1, 512, 4, 2, 1);
+            else if (ncols <= 512 * 8) IDX_LAUNCH_LAYERS(1, 512, 8, 2, 1);
+            else IDX_LAUNCH_LAYERS(1, 512, 16, 2, 1);
+        }
+#undef IDX_LAUNCH_LAYERS
+#undef IDX_LAUNCH_LAYERS_G
+        return hipGetLastError();
+    }
+    for (int l = 0; l < num_layers; ++l) {
+        KCache kl = k;
+        kl.values = layers.k_values[l];
+        kl.scales = layers.k_scales[l];
+        const hipError_t e = launch_sparse(q_format, sf, rows, layers.q_values[l],
+                                           layers.q_scales[l], layers.weights[l], kl, s,
+                                           layers.logits_out[l], workspace, topk, layers.out[l],
+                                           out_stride, timing, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace idx

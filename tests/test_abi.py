@@ -30,6 +30,17 @@ def test_library_exports_every_declared_function():
         assert hasattr(lib, n), n
 
 
+def test_build_compiles_every_kernel_source():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_idx_build_check", os.path.join(ROOT, "sparse_attention_indexer_candidate_amd", "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    csrc = os.path.join(ROOT, "sparse_attention_indexer_candidate_amd", "csrc")
+    on_disk = sorted("csrc/" + n for n in os.listdir(csrc) if n.endswith(".hip"))
+    assert sorted(b.SOURCES) == on_disk
+
+
 def test_header_is_c99_and_struct_layouts_match_the_binding(tmp_path):
     """include/idx.h compiles as plain C99 and each struct's size and field offsets in C
     equal the ctypes mirror's."""
