@@ -721,8 +721,8 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(rows shard across GPUs with no exchange; see the design notes)", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(rows would shard across GPUs with no exchange)", file=sys.stderr)
         sys.exit(2)
 
     import torch

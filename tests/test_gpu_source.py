@@ -178,8 +178,8 @@ def test_publication_full_size_comparison_workload():
 
 def test_two_level_pipeline_source_then_consumer():
     """Layer 0 publishes each row's pool; the consuming layer 1 expands and scores it.  The
-    GPU pool equals the oracle's; the consumer's result on it matches the oracle's
-    indexer on the oracle's pool."""
+    candidate pool published on the GPU equals the oracle's; the consumer's result on it
+    matches the oracle's indexer on the oracle's pool."""
     spec = W.Spec(name="two", num_rows=48, page_size=64, cbs=64, nb=16, topk=300, layers=2,
                   ke_rule="uniform", ke_lo=2000, ke_hi=9000, ks_rule="zero",
                   cand_rule="distinct", fill="all")
