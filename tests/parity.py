@@ -234,3 +234,54 @@ def compare_rows(case, res, ora, topk, sbk, what="", ora_scale=None, score_forma
         check_indices(ora.row_tokens(i), ora.row_logits(i), ora.indices[i], res["indices"][r],
                       topk, tag, sc)
         check_topk_exact_for_own_logits(gt, gl, res["indices"][r], topk, tag)
+
+
+def corrupt_tables(case, seed):
+    """Inputs that break the K cache's preconditions, and the inputs the oracle scores in
+    their place.
+
+    Returns (bad, clean, bad_rows, bad_pages).  bad: about an eighth of the block-table
+    entries that in-range candidates reach point outside the pool (-1, num_pages + 3 and
+    INT32_MAX in turn), and two rows' table rows lie outside [0, num_tables) (-1 and
+    num_tables).  The library drops the sparse blocks of such pages and rows from the
+    schedule without reading them, so its result on bad is the oracle's on clean: the
+    original tables, with every candidate block on a corrupted page removed (-1) and no
+    candidates for the two rows.  Requires cbs <= page_size (a candidate block lies in one
+    page).  bad_pages: bool [num_tables, pages_per_table], True where an entry was
+    corrupted."""
+    import workloads as W
+
+    s = case.spec
+    assert s.cbs <= s.page_size and s.page_size % s.cbs == 0, "a candidate block in one page"
+    rng = np.random.default_rng(seed)
+    T, P = case.block_table.shape
+    cand = case.candidate_blocks
+    reach = np.zeros((T, P), bool)
+    for r in range(case.num_rows):
+        c = cand[r]
+        c = c[(c >= 0) & (c.astype(np.int64) * s.cbs < case.row_ke[r])]
+        lp = c.astype(np.int64) * s.cbs // s.page_size
+        reach[case.row_table[r], lp[lp < P]] = True
+    ti, pi = np.nonzero(reach & (case.block_table >= 0))
+    pick = rng.choice(len(ti), size=max(3, len(ti) // 8), replace=False)
+    bad_bt = case.block_table.copy()
+    num_pages = case.layers[0].num_pages
+    outside = np.array([-1, num_pages + 3, np.iinfo(np.int32).max], np.int64)
+    bad_bt[ti[pick], pi[pick]] = outside[np.arange(len(pick)) % 3]
+    bad_pages = np.zeros((T, P), bool)
+    bad_pages[ti[pick], pi[pick]] = True
+    bad_rows = rng.choice(case.num_rows, size=2, replace=False)
+    bad_rt = case.row_table.copy()
+    bad_rt[bad_rows[0]] = -1
+    bad_rt[bad_rows[1]] = T
+    clean = cand.copy()
+    for r in range(case.num_rows):
+        lp = np.maximum(clean[r].astype(np.int64), 0) * s.cbs // s.page_size
+        hit = (clean[r] >= 0) & (lp < P) & bad_pages[case.row_table[r], np.minimum(lp, P - 1)]
+        clean[r, hit] = -1
+    clean[bad_rows] = -1
+    bad = W.Case(s, case.seed, case.row_ks, case.row_ke, bad_rt.astype(np.int32),
+                 bad_bt.astype(np.int32), cand, case.layers)
+    good = W.Case(s, case.seed, case.row_ks, case.row_ke, case.row_table, case.block_table,
+                  clean.astype(np.int32), case.layers)
+    return bad, good, bad_rows, bad_pages

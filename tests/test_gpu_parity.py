@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import workloads as W
-from parity import GpuRun, compare_rows, exact_topk, gpu_row_tokens
+from parity import GpuRun, compare_rows, corrupt_tables, exact_topk, gpu_row_tokens
 from workloads.device import to_device
 
 pytestmark = pytest.mark.gpu
@@ -82,7 +82,7 @@ SMALL = {
     "two_rows_a_cu_sbk16": W.Spec(name="s13", num_rows=520, page_size=32, cbs=16, nb=60, topk=90,
                                   ke_rule="uniform", ke_lo=50, ke_hi=1200, cand_rule="messy",
                                   fill="all"),
-    # >= 8 rows per CU: the row-group kernel (4 rows per workgroup); rows on one table
+    # >= 8 rows per CU: the row-group kernel (2 rows per workgroup); rows on one table
     # share K tiles, a ragged last group, messy candidates and ks > 0
     "rowgroup_shared_table_messy": W.Spec(name="s7", num_rows=2051, page_size=128, cbs=64, nb=8,
                                           topk=100, mode="prefill", ke_rule="uniform", ke_lo=1,
@@ -546,6 +546,73 @@ def test_dense_comparator_on_small_pages(page_size):
                                 int(case.row_ks[i]), int(case.row_ke[i]), res["logits"][i])
         np.testing.assert_array_equal(dl[i, gt].view(np.uint32), gl.view(np.uint32),
                                       err_msg=f"dense logits differ bitwise row {i}")
+
+
+# Block-table entries outside the pool and table rows outside [0, num_tables), on each
+# launch shape: split rows, one row per workgroup (128-token pages, two candidate blocks
+# a page), row groups (a prefill chunk on one table)
+DROPPED = {
+    "split": W.Spec(name="dr1", num_rows=40, page_size=64, cbs=64, nb=16, topk=200,
+                    ke_rule="uniform", ke_lo=300, ke_hi=3000, ks_rule="random",
+                    cand_rule="messy", fill="all"),
+    "one_row": W.Spec(name="dr2", num_rows=300, page_size=128, cbs=64, nb=20, topk=150,
+                      ke_rule="uniform", ke_lo=300, ke_hi=3000, ks_rule="random",
+                      cand_rule="messy", fill="all"),
+    "row_groups": W.Spec(name="dr3", num_rows=2050, page_size=64, cbs=64, nb=8, topk=100,
+                         mode="prefill", ke_rule="uniform", ke_lo=1, ke_hi=1500,
+                         ks_rule="random", context=1600, cand_rule="messy", fill="all"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DROPPED))
+def test_pages_outside_the_pool_and_invalid_table_rows_are_dropped(name):
+    """Sparse blocks on pages outside the pool, and every block of a row whose table row is
+    out of range, leave the schedule unread: the schedule, logits and indices equal the
+    oracle's on the original tables with those candidate blocks removed.  The dense
+    comparator on the same inputs gives the sparse indices, with -inf at every token of a
+    dropped page and on the rows without a table."""
+    import sparse_attention_indexer_candidate_amd as idx
+
+    case = W.generate(DROPPED[name], seed=21)
+    bad, clean, bad_rows, bad_pages = corrupt_tables(case, seed=5)
+    s = case.spec
+    tag = f"drop-{name}"
+    _say(f"[{tag}] rows={bad.num_rows} corrupted entries={int(bad_pages.sum())} "
+         f"bad rows={bad_rows.tolist()}")
+    g = GpuRun(bad, to_device(bad, DEV))
+    g.expand()
+    g.score(0)
+    res = g.fetch()
+    si_o, end_o = oracle.expand(clean, g.sbk)
+    np.testing.assert_array_equal(res["sparse_indices"], si_o, err_msg=f"{tag}: schedule")
+    np.testing.assert_array_equal(res["end"], end_o, err_msg=f"{tag}: end")
+    assert np.all(res["indices"][bad_rows] == -1) and np.all(res["end"][bad_rows] == 0)
+    ora = oracle.indexer_rows(clean, 0, None, "mxfp4", threads=THREADS)
+    compare_rows(clean, res, ora, s.topk, g.sbk, tag)
+    if name != "split":
+        return
+    R = bad.num_rows
+    ctx = int(bad.row_ke.max())
+    lstride = (ctx + 63) // 64 * 64
+    dlog = torch.empty((R, lstride), dtype=torch.float32, device=DEV)
+    dout = torch.full((R, s.topk), -7, dtype=torch.int32, device=DEV)
+    L = g.dcase.layers[0]
+    qv, qs = L.q("mxfp4")
+    _say(f"[{tag}] dense")
+    idx.idx_dense_masked_logits_topk(g.cfg, g.rows, ctx, qv, qs, L.weights, g.kcaches[0],
+                                     g.sched.struct, dout, dout.stride(0), dlog, dlog.stride(0))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(dout.cpu().numpy(), res["indices"], err_msg="dense != sparse")
+    dl = dlog.cpu().numpy()
+    assert np.all(dl[bad_rows, :ctx] == -np.inf)
+    for r in range(R):
+        if r in bad_rows:
+            continue
+        ks, ke = int(bad.row_ks[r]), int(bad.row_ke[r])
+        toks = np.arange(ks, ke)
+        dropped = bad_pages[bad.row_table[r], toks // s.page_size]
+        assert np.all(dl[r, toks[dropped]] == -np.inf), f"{tag}: row {r} dropped page scored"
+        assert np.all(np.isfinite(dl[r, toks[~dropped]])), f"{tag}: row {r} mapped token"
 
 
 LAYERED = {

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import workloads as W
-from parity import GpuRun, check_indices, check_logits, compare_rows, exact_topk
+from parity import GpuRun, check_indices, check_logits, compare_rows, corrupt_tables, exact_topk
 from workloads.device import to_device
 
 pytestmark = pytest.mark.gpu
@@ -174,6 +174,40 @@ def test_publication_full_size_comparison_workload():
     _say("[source-cfg5] publish")
     cand, logits = publish(case, to_device(case, DEV), nb=64)
     compare_publication(case, cand, logits, 64, "source-cfg5")
+
+
+def test_publication_drops_pages_outside_the_pool_and_invalid_table_rows():
+    """The source layer on block-table entries outside the pool and table rows out of range:
+    those tokens are not read (-inf logits), a block without a scored token is not eligible,
+    a row without a table publishes nothing, every scored token's logit equals bit for bit
+    the one the original tables give (that publication checked against the oracle), and the
+    publication is exact for the GPU's own block scores."""
+    spec = W.Spec(name="pd", num_rows=40, page_size=64, cbs=64, nb=16, topk=200,
+                  ke_rule="uniform", ke_lo=300, ke_hi=3000, ks_rule="random",
+                  cand_rule="messy", fill="all")
+    case = W.generate(spec, seed=21)
+    bad, _, bad_rows, bad_pages = corrupt_tables(case, seed=5)
+    _say(f"[publish-drop] corrupted entries={int(bad_pages.sum())} bad rows={bad_rows.tolist()}")
+    c0, l0 = publish(case, to_device(case, DEV))
+    compare_publication(case, c0, l0, spec.nb, "publish-drop original")
+    c1, l1 = publish(bad, to_device(bad, DEV))
+    ctx = int(case.row_ke.max())
+    for r in range(case.num_rows):
+        what = f"publish-drop row {r}"
+        if r in bad_rows:
+            assert np.all(c1[r] == -1) and np.all(l1[r, :ctx] == -np.inf), what
+            continue
+        ks, ke = int(case.row_ks[r]), int(case.row_ke[r])
+        toks = np.arange(ks, ke)
+        dropped = bad_pages[case.row_table[r], toks // spec.page_size]
+        assert np.all(l1[r, toks[dropped]] == -np.inf), f"{what}: a dropped token was scored"
+        np.testing.assert_array_equal(l1[r, toks[~dropped]].view(np.uint32),
+                                      l0[r, toks[~dropped]].view(np.uint32), err_msg=what)
+        kept = toks[~dropped]
+        blocks = np.unique(kept // spec.cbs).astype(np.int32)
+        scores = np.array([l1[r, kept[kept // spec.cbs == b]].max() for b in blocks],
+                          dtype=np.float32)
+        np.testing.assert_array_equal(c1[r], exact_topk(blocks, scores, spec.nb), err_msg=what)
 
 
 def test_two_level_pipeline_source_then_consumer():

@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 import workloads as W
-from parity import check_indices_bf16, check_logits_bf16, round_bf16_np
+from parity import check_indices_bf16, check_logits_bf16, corrupt_tables, round_bf16_np
 
 
 def test_round_bf16_np_matches_oracle_rounding():
@@ -60,3 +60,41 @@ def test_bf16_checker_catches_planted_mistakes(mistake):
         except AssertionError:
             caught = True
     assert caught, mistake
+
+
+@pytest.mark.parametrize("page_size,mode", [(64, "decode"), (128, "decode"), (64, "prefill")])
+def test_corrupted_tables_and_their_clean_candidates(page_size, mode):
+    """The inputs of the dropped-page GPU tests: every corrupted block-table entry lies
+    outside the pool and was reached by an in-range candidate; the clean candidates are
+    the originals minus exactly the blocks on corrupted pages, and nothing for the two rows
+    whose table row is out of range."""
+    spec = W.Spec(name="ct", num_rows=60, page_size=page_size, cbs=64, nb=12, topk=50, mode=mode,
+                  ke_rule="uniform", ke_lo=100, ke_hi=1500, ks_rule="random",
+                  context=1600 if mode == "prefill" else 0, cand_rule="messy", fill="all")
+    case = W.generate(spec, seed=3)
+    bad, clean, bad_rows, bad_pages = corrupt_tables(case, seed=5)
+    T, P = case.block_table.shape
+    npages = case.layers[0].num_pages
+    assert bad_pages.sum() >= 3
+    v = bad.block_table[bad_pages].astype(np.int64)
+    assert np.all((v < 0) | (v >= npages))
+    np.testing.assert_array_equal(bad.block_table[~bad_pages], case.block_table[~bad_pages])
+    assert bad.row_table[bad_rows[0]] == -1 and bad.row_table[bad_rows[1]] == T
+    np.testing.assert_array_equal(np.delete(bad.row_table, bad_rows),
+                                  np.delete(case.row_table, bad_rows))
+    np.testing.assert_array_equal(bad.candidate_blocks, case.candidate_blocks)
+    reached = np.zeros_like(bad_pages)
+    for r in range(case.num_rows):
+        c = case.candidate_blocks[r].astype(np.int64)
+        c = c[(c >= 0) & (c * spec.cbs < case.row_ke[r])] * spec.cbs // spec.page_size
+        reached[case.row_table[r], c[c < P]] = True
+    assert np.all(reached[bad_pages])
+    for r in range(case.num_rows):
+        c, cc = case.candidate_blocks[r], clean.candidate_blocks[r]
+        if r in bad_rows:
+            assert np.all(cc == -1)
+            continue
+        for b, bc in zip(c, cc):
+            lp = int(b) * spec.cbs // spec.page_size
+            on_bad = b >= 0 and lp < P and bad_pages[case.row_table[r], lp]
+            assert bc == (-1 if on_bad else b)
