@@ -65,8 +65,16 @@ __device__ __forceinline__ void score_split_row(
                              });
 }
 
+// fp8 queries with two groups a wave: at most 168 VGPRs, so three workgroups share a CU
+// (the compiler's own choice, 170, fits two: measured 5 % slower steps on 128-row decode
+// batches and on rows in requests of two).  With four groups a wave that bound would spill.
+template <int QF, int PW>
+constexpr int split_waves_per_simd() {
+    return QF == 1 && PW == 2 ? 3 : 1;
+}
+
 template <int QF, int PW, bool G64>
-__global__ __launch_bounds__(kScoreThreads) void score_split_kernel(
+__global__ __launch_bounds__(kScoreThreads, (split_waves_per_simd<QF, PW>())) void score_split_kernel(
     const int32_t *si_base, const int32_t *pg_base, const void *qv, const void *qs,
     const void *weights, int32_t nsb, int32_t sbk, int32_t groups_per_wg, int32_t group_rows,
     Rows rows, KCache k, float *logits, int32_t sf) {
@@ -83,7 +91,7 @@ __device__ __forceinline__ float *layer_logits(const LayerSet &ls, int l, float 
 
 // Several layers sharing a schedule, fewer rows than CUs: grid.z = layer.
 template <int QF, int PW, bool G64>
-__global__ __launch_bounds__(kScoreThreads) void score_split_layers_kernel(
+__global__ __launch_bounds__(kScoreThreads, (split_waves_per_simd<QF, PW>())) void score_split_layers_kernel(
     const int32_t *si_base, const int32_t *pg_base, int32_t nsb, int32_t sbk,
     int32_t groups_per_wg, int32_t group_rows, Rows rows, KCache k, LayerSet ls, float *ws,
     int64_t ws_layer, int32_t sf) {
