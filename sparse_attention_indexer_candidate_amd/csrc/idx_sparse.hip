@@ -247,7 +247,12 @@ __global__ __launch_bounds__(NT, WPE) void fused_row_kernel(
 // pool and outputs.  A CU that finishes a row of one layer starts a row of the next at
 // once, so the layers' launch costs and their start and end skews are paid once.  With
 // MXFP4 queries a row takes 8 waves of one-group units held to 128 VGPRs (WPE = 4 waves
-// a SIMD), so two rows share a CU: one selects while the other streams K.
+// a SIMD), so two rows share a CU: one selects while the other streams K.  fp8 queries
+// (208-238 VGPRs, two waves a SIMD) with at least two row-layers a CU: 4 waves a row, two
+// rows a CU, so the CUs take the row-layers in half as many rounds, each ending in a
+// selection (measured 4 % faster launches on the four-layer long decode than one 8-wave
+// row a CU); the keys a thread then lie in one sparse block (KPT <= sbk), which with 32
+// keys needs sbk >= 32, else the 8-wave form.
 template <int QF, int NT, int KPT, int U, int WPE, bool G64>
 __global__ __launch_bounds__(NT, WPE) void fused_layers_kernel(
     const int32_t *si_base, const int32_t *pg_base, const int32_t *p_kept, int32_t nsb,
@@ -481,6 +486,12 @@ hipError_t launch_sparse_layers(int q_format, int score_format, const Rows &rows
             if (ncols <= 512 * 4) IDX_LAUNCH_LAYERS(0, 512, 4, 1, 4);
             else if (ncols <= 512 * 8) IDX_LAUNCH_LAYERS(0, 512, 8, 1, 4);
             else IDX_LAUNCH_LAYERS(0, 512, 16, 1, 4);
+        } else if ((int64_t)rows.num_rows * num_layers >= 2 * device_cus() &&
+                   (ncols <= 256 * 16 || s.sbk >= 32)) {
+            if (ncols <= 256 * 4) IDX_LAUNCH_LAYERS(1, 256, 4, 2, 2);
+            else if (ncols <= 256 * 8) IDX_LAUNCH_LAYERS(1, 256, 8, 2, 2);
+            else if (ncols <= 256 * 16) IDX_LAUNCH_LAYERS(1, 256, 16, 2, 2);
+            else IDX_LAUNCH_LAYERS(1, 256, 32, 2, 2);
         } else {
             if (ncols <= 512 * 4) IDX_LAUNCH_LAYERS(1, 512, 4, 2, 1);
             else if (ncols <= 512 * 8) IDX_LAUNCH_LAYERS(1, 512, 8, 2, 1);

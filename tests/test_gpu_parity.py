@@ -642,6 +642,15 @@ LAYERED = {
     "row_layers": W.Spec(name="ml7", num_rows=40, page_size=64, cbs=64, nb=16, topk=300,
                          layers=8, ke_rule="uniform", ke_lo=10, ke_hi=1200, cand_rule="messy",
                          fill="all", q_formats=("mxfp4", "fp8")),
+    # two row-layers a CU at the column limit: fp8 queries take 4-wave rows with 32 keys a
+    # thread (sbk 64)
+    "wide_two_rows_a_cu": W.Spec(name="ml8", num_rows=260, page_size=64, cbs=64, nb=128,
+                                 topk=2048, layers=2, ke_rule="uniform", ke_lo=6000,
+                                 ke_hi=12000, cand_rule="distinct", fill="candidates"),
+    # ... and with 16-token sparse blocks, too short for 32 keys a thread: 8-wave rows
+    "wide_sbk16": W.Spec(name="ml9", num_rows=260, page_size=32, cbs=16, nb=320, topk=1000,
+                         layers=2, ke_rule="uniform", ke_lo=3000, ke_hi=9000,
+                         cand_rule="messy", fill="candidates"),
     # fewer rows than CUs: the split kernels, layer after layer
     "split": W.Spec(name="ml2", num_rows=40, page_size=32, cbs=32, nb=30, topk=500, layers=2,
                     ke_rule="uniform", ke_lo=100, ke_hi=1500, cand_rule="messy", fill="all",
