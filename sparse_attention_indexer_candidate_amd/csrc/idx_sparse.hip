@@ -229,7 +229,8 @@ __device__ __forceinline__ void fused_row(
 // those loads are one round trip.  MXFP4 queries: 16 waves of one-group units a row (one
 // row a CU), or, with at least two rows per CU, 8 waves held to 128 VGPRs (WPE = 4
 // waves a SIMD) so that two rows share a CU and one selects while the other streams
-// K; fp8 queries: 8 waves of 2-group units.
+// K; fp8 queries: 8 waves of 2-group units, or with at least two rows per CU 4 waves,
+// two rows a CU (the keys a thread in one sparse block: 32 keys need sbk >= 32).
 template <int QF, int NT, int KPT, int U, int WPE, bool G64>
 __global__ __launch_bounds__(NT, WPE) void fused_row_kernel(
     const int32_t *si_base, const int32_t *pg_base, const void *qv, const void *qs,
@@ -342,6 +343,17 @@ static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const 
             if (rows.num_rows < 2 * device_cus()) {
                 if (ncols <= 1024 * 4) IDX_LAUNCH_FUSED(1024, 4, 1, 1);
                 else IDX_LAUNCH_FUSED(1024, 8, 1, 1);
+                return hipGetLastError();
+            }
+        }
+        if constexpr (QF == 1) {
+            // fp8 with two or more rows a CU: 4-wave rows, two a CU (as fused_layers_kernel;
+            // measured 7-8 % faster steps on 512 and 1024 rows of 4096 columns)
+            if (rows.num_rows >= 2 * device_cus() && (ncols <= 256 * 16 || s.sbk >= 32)) {
+                if (ncols <= 256 * 4) IDX_LAUNCH_FUSED(256, 4, 2, 2);
+                else if (ncols <= 256 * 8) IDX_LAUNCH_FUSED(256, 8, 2, 2);
+                else if (ncols <= 256 * 16) IDX_LAUNCH_FUSED(256, 16, 2, 2);
+                else IDX_LAUNCH_FUSED(256, 32, 2, 2);
                 return hipGetLastError();
             }
         }

@@ -149,6 +149,26 @@ def test_fp8_query_rows_per_cu():
     run_and_compare(case, q_format="fp8", tag="fp8_rows")
 
 
+@pytest.mark.parametrize("shape", ["narrow", "wide", "wide_sbk16"])
+def test_fp8_query_two_rows_a_cu(shape):
+    """fp8 queries with at least two rows per CU: 4-wave rows, two a CU (32 keys a thread
+    at 8192 columns), or 8-wave rows where 16-token sparse blocks are too short for that."""
+    specs = {
+        "narrow": W.Spec(name="f8n", num_rows=600, page_size=64, cbs=64, nb=12, topk=200,
+                         ke_rule="uniform", ke_lo=10, ke_hi=2500, ks_rule="random",
+                         cand_rule="messy", fill="all"),
+        "wide": W.Spec(name="f8w", num_rows=520, page_size=64, cbs=64, nb=128, topk=2048,
+                       ke_rule="uniform", ke_lo=6000, ke_hi=12000, cand_rule="distinct",
+                       fill="candidates"),
+        "wide_sbk16": W.Spec(name="f8s", num_rows=520, page_size=32, cbs=16, nb=320, topk=1000,
+                             ke_rule="uniform", ke_lo=3000, ke_hi=9000, cand_rule="messy",
+                             fill="candidates"),
+    }
+    import dataclasses
+    spec = dataclasses.replace(specs[shape], q_formats=("mxfp4", "fp8"))
+    run_and_compare(W.generate(spec, seed=11), q_format="fp8", tag=f"fp8_two_rows_{shape}")
+
+
 def test_row_groups_wide_rows_all_rows():
     """Row groups over more than 4096 candidate columns (the 8192-column workgroup shape):
     2048 prefill rows on one table, 100 candidate blocks of 64, every row against the
