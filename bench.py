@@ -434,10 +434,14 @@ def traffic_for(kernel_name: str, workload: str, q_format: str, score_format: st
 
 
 def run_workload(idx, W, config: int, args, dev, stream, steps: int, warmup: int,
-                 layers: int = 0, per_layer_calls: bool = False, graph: bool = False):
+                 layers: int = 0, per_layer_calls: bool = False, graph: bool = False,
+                 rows: int = 0):
     """Generates one workload, times `steps` steps (after `warmup`) with nothing attached,
     then an event pass of EVENT_STEPS steps whose scoring launches carry dispatch events.
-    Returns the measurements and the accounting the report needs."""
+    Returns the measurements and the accounting the report needs.  layers / rows (> 0)
+    replace the workload's layer and row counts (its other parameters unchanged)."""
+    import dataclasses
+
     import torch
 
     from workloads.device import to_device
@@ -446,9 +450,9 @@ def run_workload(idx, W, config: int, args, dev, stream, steps: int, warmup: int
     if args.q_format == "fp8" and "fp8" not in spec.q_formats:
         spec = W.config(config, q_formats=("mxfp4", "fp8"))
     if layers > 0 and layers != spec.layers:
-        import dataclasses
-
         spec = dataclasses.replace(spec, layers=layers, name=f"{spec.name}_l{layers}")
+    if rows > 0 and rows != spec.num_rows:
+        spec = dataclasses.replace(spec, num_rows=rows, name=f"{spec.name}_rows{rows}")
     t0 = time.time()
     case = W.generate(spec, args.seed)
     gen_s = time.time() - t0
@@ -698,6 +702,9 @@ def main():
     ap.add_argument("--layers", type=int, default=0,
                     help="consuming layers a step (0: the workload's own); each layer gets its "
                          "own K pool, query and weights, all sharing one schedule")
+    ap.add_argument("--rows", type=int, default=0,
+                    help="query rows a step (0: the workload's own; sparse and dense paths), "
+                         "e.g. --config 6 --rows 512 for 256 requests of two decode rows")
     ap.add_argument("--per-layer-calls", action="store_true",
                     help="one sparse call per layer instead of one multi-layer call")
     ap.add_argument("--graph", action="store_true",
@@ -725,6 +732,10 @@ def main():
               "(rows would shard across GPUs with no exchange)", file=sys.stderr)
         sys.exit(2)
 
+    if args.rows and args.path in ("gather", "source"):
+        print("--rows applies to the sparse and dense paths", file=sys.stderr)
+        sys.exit(2)
+
     import torch
 
     import sparse_attention_indexer_candidate_amd as idx
@@ -746,7 +757,8 @@ def main():
         return bench_source(args, idx, W, dev, stream)
     dense = args.path == "dense"
     m = run_workload(idx, W, args.config, args, dev, stream, args.steps, args.warmup,
-                     layers=args.layers, per_layer_calls=args.per_layer_calls, graph=args.graph)
+                     layers=args.layers, per_layer_calls=args.per_layer_calls, graph=args.graph,
+                     rows=args.rows)
     spec, R = m["spec"], m["R"]
     peaks = measured_peaks(stream)
     roof = roofline(m, args.config, args.q_format, peaks, dense, args.score_format)
