@@ -1,7 +1,8 @@
 """The entry point that allocates nothing (idx_sparse_mqa_logits_topk_noalloc), through the
 C ABI: its indices equal idx_sparse_mqa_logits_topk's (workspace form) bit for bit, on two
 calls in a row, the second on a smaller input, on the split plan (its logits live in the
-library's static scratch) and on the one-row plan (no scratch needed)."""
+library's static scratch; MXFP4 and fp8 queries) and on the one-row plan (no scratch
+needed)."""
 import numpy as np
 import pytest
 import torch
@@ -14,10 +15,10 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def _noalloc_matches_workspace_call(case, tag):
+def _noalloc_matches_workspace_call(case, tag, q_format="mxfp4"):
     import sparse_attention_indexer_candidate_amd as idx
 
-    g = GpuRun(case, to_device(case, DEV))
+    g = GpuRun(case, to_device(case, DEV), q_format=q_format)
     g.expand()
     print(f"[{tag}] rows={case.num_rows} plan={idx.idx_sparse_plan(g.cfg, case.num_rows)}",
           flush=True)
@@ -25,7 +26,7 @@ def _noalloc_matches_workspace_call(case, tag):
     torch.cuda.synchronize()
     want = g.out.cpu().numpy().copy()
     L = g.dcase.layers[0]
-    qv, qs = L.q("mxfp4")
+    qv, qs = L.q(q_format)
     out = torch.full_like(g.out, -7)
     idx.idx_sparse_mqa_logits_topk_noalloc(g.cfg, g.rows, qv, qs, L.weights, g.kcaches[0],
                                            g.sched.struct, out, out.stride(0))
@@ -52,6 +53,15 @@ def test_noalloc_split_plan_two_calls_second_smaller():
                               cand_rule="messy", fill="all"), seed=3)
     _noalloc_matches_workspace_call(big, "noalloc-split-1")
     _noalloc_matches_workspace_call(small, "noalloc-split-2")
+
+
+def test_noalloc_split_plan_fp8_queries_two_calls_second_smaller():
+    big = W.generate(W.config(5, q_formats=("mxfp4", "fp8")), 0)   # 128 rows: split plan
+    small = W.generate(W.Spec(name="nf", num_rows=30, page_size=32, cbs=32, nb=40, topk=200,
+                              ke_rule="uniform", ke_lo=100, ke_hi=2000, ks_rule="random",
+                              cand_rule="messy", fill="all", q_formats=("mxfp4", "fp8")), seed=6)
+    _noalloc_matches_workspace_call(big, "noalloc-fp8-1", "fp8")
+    _noalloc_matches_workspace_call(small, "noalloc-fp8-2", "fp8")
 
 
 def test_noalloc_one_row_plan_two_calls_second_smaller():
