@@ -3,10 +3,11 @@
 //
 //  fused_row_kernel     rows >= CUs: one workgroup scores a whole row into LDS
 //                       and selects from LDS (no global round trip, no cross-workgroup
-//                       sync); MXFP4 with >= 2 rows a CU: 8-wave rows, two a CU
+//                       sync); with >= 2 rows a CU two rows share a CU (MXFP4: 8-wave
+//                       rows, fp8: 4-wave rows)
 //  fused_layers_kernel  the one-row kernel for several layers sharing a schedule, one
-//                       launch (grid.y = layer); MXFP4: 8-wave rows, two a CU, so one
-//                       row's selection overlaps another's K stream
+//                       launch (grid.y = layer); two row-layers a CU, so one row's
+//                       selection overlaps another's K stream
 //  score_split_kernel + topk_split_kernel
 //                       fewer rows than CUs: rows split over workgroups, logits in
 //                       global scratch, selection in a second launch (and the
@@ -328,7 +329,8 @@ static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const 
         // steps than 8 waves with 4-group units: the row's last unit, and so the wait
         // before the selection, is shorter).  MXFP4 with two or more rows a CU: 8 waves
         // with 1-group units, two rows a CU (measured 23 % faster on 512-2000 rows of 4096
-        // columns).  fp8 queries need more registers: 8 waves, 2-group units.
+        // columns).  fp8 queries need more registers: 2-group units, 8 waves a row, or 4
+        // waves and two rows a CU when there are two or more rows a CU.
 #define IDX_LAUNCH_FUSED_G(NT_, KPT_, U_, WPE_, G64_)                                           \
     hipExtLaunchKernelGGL((fused_row_kernel<QF, NT_, KPT_, U_, WPE_, G64_>), dim3(rows.num_rows), \
                           dim3(NT_), 0, stream, timing.start, timing.stop, 0, s.sparse_indices,   \
