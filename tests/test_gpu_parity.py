@@ -237,6 +237,29 @@ def test_random_shapes_all_rows(i):
                                   err_msg=f"rand{i}: dense != sparse indices")
 
 
+@pytest.mark.parametrize("i", range(12))
+def test_random_shapes_fp8_queries_and_bf16_scoring(i):
+    """Seeded random shapes (as test_random_shapes_all_rows) with fp8 queries, bf16 scoring
+    or both: the split, one-row and many-row launch forms of each (fp8 rows at two or more
+    a CU take 4-wave rows; MXFP4 many-row cases take row groups)."""
+    import dataclasses
+
+    spec, signed = _random_spec(100 + i)
+    q_format = "fp8" if i % 2 == 0 else "mxfp4"
+    score_format = "bf16" if i % 4 in (1, 2) else "fp32"
+    spec = dataclasses.replace(spec, name=f"rq{i}", q_formats=("mxfp4", "fp8"))
+    case = W.generate(spec, seed=50 + i)
+    scale_case = None
+    if signed and score_format == "fp32":
+        case = _reweighted(case, "signed", seed=i)
+        scale_case = dataclasses.replace(
+            case, layers=[dataclasses.replace(L, weights=np.abs(L.weights)) for L in case.layers])
+    _say(f"[rq{i}] rows={spec.num_rows} cbs={spec.cbs} page={spec.page_size} nb={spec.nb} "
+         f"k={spec.topk} {spec.mode} {q_format} {score_format} signed={scale_case is not None}")
+    run_and_compare(case, tag=f"rq{i}", q_format=q_format, score_format=score_format,
+                    scale_case=scale_case)
+
+
 def _reweighted(case, kind, seed):
     """The case with every layer's head weights replaced.  "signed": U(-1, 1) / 8, so
     logits take both signs (the negative half of the key order and of the first radix
