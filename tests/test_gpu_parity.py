@@ -709,7 +709,36 @@ def test_layers_call_matches_per_layer_calls_and_oracle(name, q_format):
     spec = LAYERED[name]
     if q_format not in spec.q_formats:
         spec = dataclasses.replace(spec, q_formats=("mxfp4", "fp8"))
-    case = W.generate(spec, seed=5)
+    _check_layers_call(W.generate(spec, seed=5), name, q_format)
+
+
+@pytest.mark.parametrize("i", range(10))
+def test_random_layers_calls(i):
+    """Seeded random multi-layer calls: 2-8 layers, row counts that take each multi-layer
+    form (batched split launches, one launch of row-layers, two fp8 row-layers a CU, row
+    groups), random block and page sizes and k; the same checks as the fixed cases."""
+    import dataclasses
+
+    rng = np.random.default_rng(7000 + i)
+    spec, _ = _random_spec(200 + i)
+    layers = int(rng.integers(2, 9))
+    form = i % 4
+    rows = [int(rng.integers(8, 256 // layers)), int(rng.integers(256 // layers + 1, 255)),
+            int(rng.integers(256, 400)), spec.num_rows][form]
+    if form == 3 and spec.mode != "prefill":
+        spec = dataclasses.replace(spec, mode="prefill", ke_lo=1, context=spec.ke_hi)
+        rows = 2048 + int(rng.integers(0, 40))
+    spec = dataclasses.replace(spec, name=f"rl{i}", num_rows=rows, layers=layers,
+                               q_formats=("mxfp4", "fp8"))
+    q_format = ("mxfp4", "fp8")[(i + i // 4) % 2]   # each form with both formats
+    _say(f"[rl{i}] rows={rows} layers={layers} cbs={spec.cbs} page={spec.page_size} "
+         f"nb={spec.nb} k={spec.topk} {spec.mode} {q_format}")
+    _check_layers_call(W.generate(spec, seed=70 + i), f"rl{i}", q_format)
+
+
+def _check_layers_call(case, name, q_format):
+    """One multi-layer call (and its full-workspace and all-logits forms) against one call
+    per layer, bit for bit, and every layer against the oracle on every row."""
     nl = case.spec.layers
     g = GpuRun(case, to_device(case, DEV), q_format=q_format)
     g.expand()
