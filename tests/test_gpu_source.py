@@ -125,6 +125,31 @@ def test_publication_matches_oracle_all_rows(name):
     compare_publication(case, cand, logits, nb, f"source-{name}")
 
 
+@pytest.mark.parametrize("i", range(8))
+def test_random_publications(i):
+    """Seeded random publications: block sizes 16-256 on pages of a multiple of the sparse
+    block, NB from 1 to min(64, 8192 / cbs), ragged [ks, ke), both query formats and both
+    score formats."""
+    rng = np.random.default_rng(9000 + i)
+    cbs = int(rng.choice([16, 32, 64, 128, 256]))
+    sbk = 64 if cbs % 64 == 0 else cbs
+    page_size = int(rng.choice([p for p in (16, 32, 64, 128, 256) if p % sbk == 0]))
+    ke_hi = int(rng.integers(cbs, min(4096 * cbs, 20000)))
+    nb = int(rng.integers(1, min(64, 8192 // cbs) + 1))   # NB * cbs <= 8192
+    spec = W.Spec(name=f"rp{i}", num_rows=int(rng.integers(1, 90)), page_size=page_size, cbs=cbs,
+                  nb=nb, topk=min(100, nb * cbs), ke_rule="uniform",
+                  ke_lo=int(rng.integers(0, ke_hi)), ke_hi=ke_hi,
+                  ks_rule=str(rng.choice(["zero", "random"])), cand_rule="distinct", fill="all",
+                  q_formats=("mxfp4", "fp8"))
+    q_format = ("mxfp4", "fp8")[i % 2]
+    score_format = ("fp32", "bf16")[(i // 2) % 2]
+    case = W.generate(spec, seed=90 + i)
+    _say(f"[rp{i}] rows={spec.num_rows} cbs={cbs} page={page_size} nb={nb} ke<={ke_hi} "
+         f"{q_format} {score_format}")
+    cand, logits = publish(case, to_device(case, DEV), q_format=q_format, score_format=score_format)
+    compare_publication(case, cand, logits, nb, f"rp{i}", q_format, score_format)
+
+
 @pytest.mark.parametrize("variant", ["fp8", "bf16", "zero_weights", "signed_weights"])
 def test_publication_variants(variant):
     spec = W.Spec(name="pv", num_rows=30, page_size=64, cbs=64, nb=12, topk=100,
