@@ -461,14 +461,18 @@ def make_kcache(pool, page_size, head_dim, block_table) -> idx_kcache:
     packed values [page_size][D/2] followed by the scales [page_size][D/32], and an
     int32 block table [num_tables, pages_per_table]."""
     page_bytes = pool.shape[1]
-    return idx_kcache(pool.data_ptr(), page_bytes, pool.data_ptr() + page_size * head_dim // 2,
-                      page_bytes, pool.shape[0], block_table.data_ptr(), block_table.stride(0),
-                      block_table.shape[0], block_table.shape[1])
+    k = idx_kcache(pool.data_ptr(), page_bytes, pool.data_ptr() + page_size * head_dim // 2,
+                   page_bytes, pool.shape[0], block_table.data_ptr(), block_table.stride(0),
+                   block_table.shape[0], block_table.shape[1])
+    k._tensors = (pool, block_table)   # the struct holds their addresses: keep them alive
+    return k
 
 
 def make_rows(row_ke, row_ks=None, row_table=None, rows_per_request=1) -> idx_rows:
     """rows_per_request: consecutive rows of one request (next_n), a placement hint."""
-    return idx_rows(row_ke.shape[0], _p(row_ks), _p(row_ke), _p(row_table), rows_per_request)
+    r = idx_rows(row_ke.shape[0], _p(row_ks), _p(row_ke), _p(row_table), rows_per_request)
+    r._tensors = (row_ke, row_ks, row_table)   # the struct holds their addresses
+    return r
 
 
 class Schedule:

@@ -9,17 +9,19 @@ namespace {
 // [0, cu[r+1] - cu[r]) go to workspace rows cu[r] + p, D/2 value bytes and D/32 scale
 // bytes a row.  grid = (tiles of kGatherTokens positions, requests); four threads copy a
 // position's 64 value bytes, 16 each, and the first of them its 4 scale bytes.  A
-// position whose table row, logical page or page id is out of range gets zeros; rows at
-// or past max_tokens are not written.  A plain stream: HBM-bound, read once.
+// position whose table row, logical page or page id is out of range gets zeros; positions
+// at or past max_seq_len and rows at or past max_tokens are not written.  A plain stream:
+// HBM-bound, read once.
 constexpr int kGatherTokens = 64;
 constexpr int kGatherThreads = kGatherTokens * 4;
 
 __global__ __launch_bounds__(kGatherThreads) void gather_k_kernel(
-    const int32_t *cu, const int32_t *req_table, int32_t max_tokens, KCache k,
-    uint8_t *values_out, uint8_t *scales_out) {
+    const int32_t *cu, const int32_t *req_table, int32_t max_seq_len, int32_t max_tokens,
+    KCache k, uint8_t *values_out, uint8_t *scales_out) {
     const int r = blockIdx.y, tid = threadIdx.x, part = tid & 3;
     const int p = blockIdx.x * kGatherTokens + (tid >> 2);
-    const int c0 = cu[r], len = cu[r + 1] - c0;
+    // the grid covers max_seq_len rounded up to whole tiles: the tail is cut here
+    const int c0 = cu[r], len = min(cu[r + 1] - c0, max_seq_len);
     const int tbl = req_table ? req_table[r] : r;
     if (c0 < 0 || p >= len || (int64_t)c0 + p >= max_tokens) return;
     const int64_t dst = (int64_t)c0 + p;
@@ -51,8 +53,8 @@ hipError_t launch_gather_k(const KCache &k, int32_t num_reqs, const int32_t *cu_
     if (num_reqs == 0 || max_seq_len == 0 || max_tokens == 0) return hipSuccess;
     const dim3 grid((max_seq_len + kGatherTokens - 1) / kGatherTokens, num_reqs);
     hipExtLaunchKernelGGL(gather_k_kernel, grid, dim3(kGatherThreads), 0, stream, timing.start,
-                          timing.stop, 0, cu_seq_lens, req_table, max_tokens, k, values_out,
-                          scales_out);
+                          timing.stop, 0, cu_seq_lens, req_table, max_seq_len, max_tokens, k,
+                          values_out, scales_out);
     return hipGetLastError();
 }
 

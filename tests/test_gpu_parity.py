@@ -969,6 +969,58 @@ def test_gather_k_workspace_matches_oracle():
     np.testing.assert_array_equal(scs.cpu().numpy(), want_s)
 
 
+@pytest.mark.parametrize("i", range(10))
+def test_random_gathers(i):
+    """Seeded random gathers, byte for byte against the oracle: page sizes 16-256, 1-40
+    requests (some empty), request tables with rows out of range, page ids outside the
+    pool, and caps on the sequence length and on the workspace rows."""
+    import sparse_attention_indexer_candidate_amd as idx
+
+    rng = np.random.default_rng(8000 + i)
+    page_size = (16, 32, 64, 128, 256)[i % 5]
+    cbs = min(64, page_size)
+    nreq = int(rng.integers(1, 41))
+    spec = W.Spec(name=f"rg{i}", num_rows=nreq, page_size=page_size, cbs=cbs, nb=4, topk=16,
+                  ke_rule="uniform", ke_lo=0, ke_hi=int(rng.integers(1, 6000)),
+                  cand_rule="distinct", fill="all")
+    case = W.generate(spec, seed=80 + i)
+    lens = case.row_ke.astype(np.int64)
+    lens[rng.random(nreq) < 0.15] = 0
+    cu = np.r_[0, np.cumsum(lens)].astype(np.int32)
+    T = case.block_table.shape[0]
+    req = rng.permutation(T)[:nreq].astype(np.int32) if T >= nreq else \
+        rng.integers(0, T, nreq).astype(np.int32)
+    bad = rng.random(nreq) < 0.1
+    req[bad] = np.where(rng.random(int(bad.sum())) < 0.5, -1, T).astype(np.int32)
+    bt = case.block_table.copy()
+    live = np.argwhere(bt >= 0)
+    if len(live):
+        pick = live[rng.choice(len(live), size=max(1, len(live) // 10), replace=False)]
+        bt[pick[:, 0], pick[:, 1]] = np.where(rng.random(len(pick)) < 0.5, -1,
+                                              case.layers[0].num_pages + 7)
+    total = int(cu[-1])
+    max_seq = max(1, int(lens.max()) - int(rng.integers(0, 2) * rng.integers(0, 300)))
+    max_tokens = max(1, total - int(rng.integers(0, 2) * rng.integers(0, 500)))
+    pool = case.layers[0].host_pool(spec.page_bytes)
+    want_v, want_s = oracle.gather_k_workspace(pool, page_size, spec.head_dim, bt, cu,
+                                               req_table=req, max_seq_len=max_seq,
+                                               max_tokens=max_tokens, fill=0xAB)
+    d = to_device(case, DEV)
+    # every device array the launch reads stays referenced until it has finished (the
+    # K-cache struct holds only the table's address)
+    dbt, dcu, dreq = (torch.from_numpy(a).to(DEV) for a in (bt, cu, req))
+    cfg = idx.make_config(64, 128, idx.IDX_Q_MXFP4, page_size, cbs, 0, spec.nb, spec.topk)
+    kc = idx.make_kcache(d.layers[0].pool, page_size, spec.head_dim, dbt)
+    vals = torch.full((max_tokens, 64), 0xAB, dtype=torch.uint8, device=DEV)
+    scs = torch.full((max_tokens, 4), 0xAB, dtype=torch.uint8, device=DEV)
+    _say(f"[rg{i}] page={page_size} requests={nreq} positions={total} max_seq={max_seq} "
+         f"rows={max_tokens} bad tables={int(bad.sum())}")
+    idx.idx_gather_k_workspace(cfg, kc, dcu, vals, scs, max_seq, req_table=dreq)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(vals.cpu().numpy(), want_v)
+    np.testing.assert_array_equal(scs.cpu().numpy(), want_s)
+
+
 def test_gather_then_score_equals_paged_cache():
     """A prefill chunk scored from its gathered workspace (one page of 2048 positions)
     gives the paged cache's indices and logits bit for bit."""
