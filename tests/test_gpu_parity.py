@@ -591,6 +591,47 @@ def test_dense_comparator_on_small_pages(page_size):
                                       err_msg=f"dense logits differ bitwise row {i}")
 
 
+@pytest.mark.parametrize("name", ["split", "one_row", "row_groups"])
+def test_range_edges_and_strides(name):
+    """Rows with ks < 0, ks past ke, ke = 0 and ke < 0 (the empty and full readings of
+    [ks, ke)), candidate arrays with a wider stride whose padding holds valid-looking ids
+    (never read), and output rows wider than k (slots past k untouched): the schedule,
+    logits and indices against the oracle on every row."""
+    import dataclasses
+
+    spec = DROPPED[name]
+    case = W.generate(spec, seed=31)
+    rng = np.random.default_rng(4)
+    ks, ke = case.row_ks.copy(), case.row_ke.copy()
+    r = rng.permutation(case.num_rows)
+    ks[r[0:4]] = -5                                  # every token from 0
+    ks[r[4:8]] = ke[r[4:8]] + 10                     # ks past ke: empty
+    ks[r[8:10]] = np.maximum(ke[r[8:10]] - 1, 0)     # one token
+    ke[r[10:12]] = 0
+    ke[r[12:14]] = -3
+    case = dataclasses.replace(case, row_ks=ks.astype(np.int32), row_ke=ke.astype(np.int32))
+    d = to_device(case, DEV)
+    R, nb, k = case.num_rows, spec.nb, spec.topk
+    padded = torch.from_numpy(np.concatenate(
+        [case.candidate_blocks, np.tile(np.arange(5, dtype=np.int32), (R, 1))], axis=1)).to(DEV)
+    d.candidate_blocks = padded[:, :nb]              # stride nb + 5
+    g = GpuRun(case, d)
+    wide = torch.full((R, k + 7), -7, dtype=torch.int32, device=DEV)
+    g.out = wide[:, :k]                              # out_stride k + 7
+    _say(f"[edges-{name}] rows={R} cand_stride={d.candidate_blocks.stride(0)} "
+         f"out_stride={g.out.stride(0)}")
+    g.expand()
+    g.score(0)
+    res = g.fetch()
+    si_o, end_o = oracle.expand(case, g.sbk)
+    np.testing.assert_array_equal(res["sparse_indices"], si_o, err_msg="schedule")
+    np.testing.assert_array_equal(res["end"], end_o, err_msg="end")
+    ora = oracle.indexer_rows(case, 0, None, "mxfp4", threads=THREADS)
+    compare_rows(case, res, ora, k, g.sbk, f"edges-{name}")
+    assert np.all(wide[:, k:].cpu().numpy() == -7), "wrote past k"
+    assert np.all(res["indices"][r[4:8]] == -1) and np.all(res["indices"][r[10:14]] == -1)
+
+
 # Block-table entries outside the pool and table rows outside [0, num_tables), on each
 # launch shape: split rows, one row per workgroup (128-token pages, two candidate blocks
 # a page), row groups (a prefill chunk on one table)
