@@ -175,12 +175,14 @@ class GpuRun:
             None if with_logits else self.workspace,
             0 if with_logits else self.workspace.numel())
 
-    def score_layers(self, layers, with_logits, workspace_layers=1):
+    def score_layers(self, layers, with_logits, workspace_layers=1, out_pad=0):
         """One idx_sparse_mqa_logits_topk_layers call over the given layers; returns
         per-layer (indices, logits or None) device tensors.  with_logits[i] False: that
         layer writes no logits (the workspace serves it).  workspace_layers: the
         workspace holds that many layers' logits (all of them lets fewer rows than CUs
-        run every layer in one split launch)."""
+        run every layer in one split launch).  out_pad: each layer's indices are a view
+        of a [rows][topk + out_pad] buffer filled with -7 (out_stride topk + out_pad),
+        whose extra columns padded_tail reads."""
         import torch
 
         R, s = self.case.num_rows, self.spec
@@ -189,7 +191,8 @@ class GpuRun:
         for layer, wl in zip(layers, with_logits):
             L = self.dcase.layers[layer]
             qv, qs = L.q(self.q_format)
-            out = torch.full((R, s.topk), -7, dtype=torch.int32, device=dev)
+            out = torch.full((R, s.topk + out_pad), -7, dtype=torch.int32, device=dev)
+            out = out[:, :s.topk]
             lg = torch.empty((R, s.nb * s.cbs), dtype=torch.float32, device=dev) if wl else None
             outs.append(out)
             logs.append(lg)
@@ -199,8 +202,9 @@ class GpuRun:
             ws = torch.empty(self.idx.idx_workspace_bytes(self.cfg, R * workspace_layers, 0),
                              dtype=torch.uint8, device=dev)
         self.idx.idx_sparse_mqa_logits_topk_layers(self.cfg, self.rows, self.sched.struct,
-                                                   entries, s.topk, ws, ws.numel())
+                                                   entries, s.topk + out_pad, ws, ws.numel())
         return outs, logs
+
 
     def fetch(self):
         import torch
@@ -211,6 +215,14 @@ class GpuRun:
                     end=self.sched.end.cpu().numpy(),
                     kept=self.sched.work[:4 * self.case.num_rows].view(torch.int32).cpu().numpy())
 
+
+def padded_tail(out_view, pad):
+    """The pad columns [topk, topk + pad) of a score_layers output view, on the host."""
+    import torch
+
+    R, k = out_view.shape
+    full = torch.as_strided(out_view, (R, k + pad), (out_view.stride(0), 1))
+    return full[:, k:].cpu().numpy()
 
 def compare_rows(case, res, ora, topk, sbk, what="", ora_scale=None, score_format="fp32"):
     """Compare GPU results (dict from GpuRun.fetch) with an oracle RowResult; ora_scale

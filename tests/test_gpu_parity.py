@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import workloads as W
-from parity import GpuRun, compare_rows, corrupt_tables, exact_topk, gpu_row_tokens
+from parity import GpuRun, compare_rows, corrupt_tables, exact_topk, gpu_row_tokens, padded_tail
 from workloads.device import to_device
 
 pytestmark = pytest.mark.gpu
@@ -793,7 +793,13 @@ def _check_layers_call(case, name, q_format):
     outs_w, logs_w = g.score_layers(range(nl), with_logits, workspace_layers=nl)
     _say(f"[layers-{name}-{q_format}] every layer with logits")
     outs_a, logs_a = g.score_layers(range(nl), [True] * nl)
+    _say(f"[layers-{name}-{q_format}] output rows wider than k")
+    outs_p, _ = g.score_layers(range(nl), with_logits, out_pad=5)
     torch.cuda.synchronize()
+    for layer in range(nl):
+        np.testing.assert_array_equal(outs_p[layer].cpu().numpy(), outs[layer].cpu().numpy(),
+                                      err_msg=f"{name} layer {layer}: out_stride k + 5")
+        assert np.all(padded_tail(outs_p[layer], 5) == -7), f"{name} layer {layer}: wrote past k"
     for layer in range(nl):
         np.testing.assert_array_equal(outs_w[layer].cpu().numpy(), outs[layer].cpu().numpy(),
                                       err_msg=f"{name} layer {layer}: full workspace")
