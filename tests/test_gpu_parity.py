@@ -699,6 +699,93 @@ def test_pages_outside_the_pool_and_invalid_table_rows_are_dropped(name):
         assert np.all(np.isfinite(dl[r, toks[~dropped]])), f"{tag}: row {r} mapped token"
 
 
+@pytest.mark.parametrize("name", sorted(DROPPED))
+def test_separate_value_and_scale_pools(name):
+    """The two-pointer K cache: the values and the scales copied into two separate pools,
+    each with its own page stride (values padded by 256 bytes a page; scales by 3 bytes
+    from an odd base, as byte loads allow), give the interleaved pool's schedule, logits
+    and indices bit for bit; on the split shape also the dense comparator, the source
+    publication and (with 4-byte aligned scale pages, as it requires) the K gather."""
+    import sparse_attention_indexer_candidate_amd as idx
+
+    spec = DROPPED[name]
+    case = W.generate(spec, seed=17)
+    d = to_device(case, DEV)
+    g = GpuRun(case, d)
+    g.expand()
+    g.score(0)
+    ref = g.fetch()
+    ps, pool, bt = spec.page_size, d.layers[0].pool, d.block_table
+    P = pool.shape[0]
+    vals = torch.zeros((P, ps * 64 + 256), dtype=torch.uint8, device=DEV)
+    vals[:, :ps * 64] = pool[:, :ps * 64]
+    sstride = ps * 4 + 3
+    sbuf = torch.zeros(P * sstride + 64, dtype=torch.uint8, device=DEV)
+    torch.as_strided(sbuf, (P, ps * 4), (sstride, 1), 1).copy_(pool[:, ps * 64:])
+    k_split = idx.idx_kcache(vals.data_ptr(), vals.stride(0), sbuf.data_ptr() + 1, sstride, P,
+                             bt.data_ptr(), bt.stride(0), bt.shape[0], bt.shape[1])
+    k_ref = g.kcaches[0]
+    g.kcaches[0] = k_split
+    _say(f"[pools-{name}] rows={case.num_rows} values stride {vals.stride(0)} scales stride "
+         f"{sstride}")
+    g.out.fill_(-7)
+    g.expand()
+    g.score(0)
+    res = g.fetch()
+    for key in ("sparse_indices", "end", "indices"):
+        np.testing.assert_array_equal(res[key], ref[key], err_msg=f"pools-{name}: {key}")
+    np.testing.assert_array_equal(res["logits"].view(np.uint32), ref["logits"].view(np.uint32))
+    if name != "split":
+        return
+    R, k = case.num_rows, spec.topk
+    L = d.layers[0]
+    qv, qs = L.q("mxfp4")
+    ctx = int(case.row_ke.max())
+    lstride = (ctx + 63) // 64 * 64
+    dense = []
+    for kc in (k_ref, k_split):
+        dlog = torch.empty((R, lstride), dtype=torch.float32, device=DEV)
+        dout = torch.full((R, k), -7, dtype=torch.int32, device=DEV)
+        idx.idx_dense_masked_logits_topk(g.cfg, g.rows, ctx, qv, qs, L.weights, kc,
+                                         g.sched.struct, dout, dout.stride(0), dlog,
+                                         dlog.stride(0))
+        dense.append((dout, dlog))
+    pub = []
+    ws = torch.empty(max(4, idx.idx_publish_workspace_bytes(g.cfg, R, ctx)), dtype=torch.uint8,
+                     device=DEV)
+    for kc in (k_ref, k_split):
+        cand = torch.full((R, spec.nb), -7, dtype=torch.int32, device=DEV)
+        plog = torch.empty((R, lstride), dtype=torch.float32, device=DEV)
+        idx.idx_publish_candidates(g.cfg, g.rows, ctx, qv, qs, L.weights, kc, cand,
+                                   cand.stride(0), plog, plog.stride(0), ws, ws.numel())
+        torch.cuda.synchronize()
+        pub.append((cand.cpu().numpy(), plog.cpu().numpy()))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(dense[1][0].cpu().numpy(), dense[0][0].cpu().numpy())
+    np.testing.assert_array_equal(dense[1][1].cpu().numpy().view(np.uint32),
+                                  dense[0][1].cpu().numpy().view(np.uint32))
+    np.testing.assert_array_equal(pub[1][0], pub[0][0])
+    np.testing.assert_array_equal(pub[1][1].view(np.uint32), pub[0][1].view(np.uint32))
+    # the gather reads a position's scale bytes as one word: 4-byte aligned scale pages
+    sstride4 = ps * 4 + 4
+    sbuf4 = torch.zeros((P, sstride4), dtype=torch.uint8, device=DEV)
+    sbuf4[:, :ps * 4] = pool[:, ps * 64:]
+    k_split4 = idx.idx_kcache(vals.data_ptr(), vals.stride(0), sbuf4.data_ptr(), sstride4, P,
+                              bt.data_ptr(), bt.stride(0), bt.shape[0], bt.shape[1])
+    lens = case.row_ke.astype(np.int64)
+    cu = torch.from_numpy(np.r_[0, np.cumsum(lens)].astype(np.int32)).to(DEV)
+    n = int(lens.sum())
+    got = []
+    for kc in (k_ref, k_split4):
+        gv = torch.full((n, 64), 0xAB, dtype=torch.uint8, device=DEV)
+        gs = torch.full((n, 4), 0xAB, dtype=torch.uint8, device=DEV)
+        idx.idx_gather_k_workspace(g.cfg, kc, cu, gv, gs, int(lens.max()))
+        torch.cuda.synchronize()
+        got.append((gv.cpu().numpy(), gs.cpu().numpy()))
+    np.testing.assert_array_equal(got[1][0], got[0][0])
+    np.testing.assert_array_equal(got[1][1], got[0][1])
+
+
 LAYERED = {
     # >= 256 rows of one table row each: every layer in one launch
     "one_launch": W.Spec(name="ml1", num_rows=300, page_size=64, cbs=64, nb=24, topk=300,
