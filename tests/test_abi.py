@@ -125,6 +125,50 @@ def test_sizes():
     assert idx.idx_workspace_bytes(cfg(num_heads=1), 4, 0) == 0
 
 
+def test_size_queries_return_zero_on_bad_input():
+    c = idx.idx_check_config(cfg())
+    assert idx.idx_schedule_work_bytes(c, -1) == 0
+    assert idx.idx_schedule_work_bytes(cfg(num_heads=1), 4) == 0
+    assert idx.idx_publish_workspace_bytes(cfg(num_heads=1), 4, 1024) == 0
+
+
+def test_last_error_is_per_thread():
+    """Each thread reads the message of its own last failing call; a thread with no
+    failure reads "", and other threads' failures leave it unchanged."""
+    import threading
+
+    def fail_with(**kw):
+        return idx.lib.idx_check_config(ctypes.byref(cfg(**kw)))
+
+    assert fail_with(topk=0) != idx.IDX_OK
+    main_msg = idx.idx_last_error()
+    assert main_msg
+    seen = {}
+
+    def worker(name, kw):
+        if kw is not None:
+            assert fail_with(**kw) != idx.IDX_OK
+        seen[name] = idx.idx_last_error()
+
+    threads = [threading.Thread(target=worker, args=("heads", dict(num_heads=1))),
+               threading.Thread(target=worker, args=("dim", dict(head_dim=64))),
+               threading.Thread(target=worker, args=("none", None))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert seen["none"] == ""
+    assert seen["heads"] and seen["dim"] and seen["heads"] != seen["dim"]
+    assert main_msg not in (seen["heads"], seen["dim"])
+    assert idx.idx_last_error() == main_msg
+
+
+def test_timing_events_need_both_or_neither():
+    assert idx.lib.idx_set_timing_events(FAKE, None) == idx.IDX_EINVAL
+    assert idx.lib.idx_set_timing_events(None, FAKE) == idx.IDX_EINVAL
+    assert idx.lib.idx_set_timing_events(None, None) == idx.IDX_OK
+
+
 # ----------------------------------------------------------- call argument checks --
 
 def kcache(**kw):
