@@ -117,6 +117,21 @@ SMALL = {
     "topk1_rowgroups": W.Spec(name="s16", num_rows=2050, page_size=64, cbs=64, nb=8, topk=1,
                               mode="prefill", ke_rule="uniform", ke_lo=1, ke_hi=1500,
                               ks_rule="random", context=1600, cand_rule="messy", fill="all"),
+    # the expansion's register sort at each width: 2 ids a lane just past 128 candidates is
+    # the smallest 4-id case, 256 the largest; 512 (16-token blocks, 8192 columns) the
+    # 8-id maximum; and 4 ids a lane on the one-row kernel
+    "nb129_e4": W.Spec(name="s18", num_rows=24, page_size=32, cbs=32, nb=129, topk=1000,
+                       ke_rule="uniform", ke_lo=1000, ke_hi=9000, ks_rule="random",
+                       cand_rule="messy", fill="all"),
+    "nb256_e4": W.Spec(name="s19", num_rows=20, page_size=16, cbs=16, nb=256, topk=2000,
+                       ke_rule="uniform", ke_lo=500, ke_hi=9000, ks_rule="random",
+                       cand_rule="messy", fill="all"),
+    "nb512_e8": W.Spec(name="s20", num_rows=16, page_size=16, cbs=16, nb=512, topk=4000,
+                       ke_rule="uniform", ke_lo=2000, ke_hi=12000, ks_rule="random",
+                       cand_rule="messy", fill="all"),
+    "nb200_e4_rows": W.Spec(name="s21", num_rows=300, page_size=32, cbs=32, nb=200, topk=1500,
+                            ke_rule="uniform", ke_lo=1000, ke_hi=9000, cand_rule="messy",
+                            fill="all"),
     # candidate blocks of four pages each (cbs 256 on 64-token pages: four sparse blocks a
     # candidate, each on its own page)
     "cbs256_pages64": W.Spec(name="s17", num_rows=25, page_size=64, cbs=256, nb=6, topk=200,
