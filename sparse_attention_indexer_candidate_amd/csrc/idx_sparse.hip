@@ -66,16 +66,24 @@ __device__ __forceinline__ void score_split_row(
                              });
 }
 
-// fp8 queries with two groups a wave: at most 168 VGPRs, so three workgroups share a CU
-// (the compiler's own choice, 170, fits two: measured 5 % slower steps on 128-row decode
-// batches and on rows in requests of two).  With four groups a wave that bound would spill.
-template <int QF, int PW>
+// Split grid: 8 groups a workgroup, two a wave (two groups a wave hide the schedule-to-K
+// load chain better than one: measured 3-7 % faster steps on 64- and 128-row decode
+// batches).  The split plan takes fewer rows than CUs, so the grid (rows x up to 16
+// chunks of a row's 128 groups) stays within a few thousand workgroups and covers the CUs
+// several times over.
+constexpr int kSplitGroupsPerWave = 2;
+constexpr int kSplitGroupsPerWg = (kScoreThreads / kWave) * kSplitGroupsPerWave;
+
+// fp8 queries: at most 168 VGPRs, so three workgroups share a CU (the compiler's own
+// choice, 170, fits two: measured 5 % slower steps on 128-row decode batches and on rows
+// in requests of two).
+template <int QF>
 constexpr int split_waves_per_simd() {
-    return QF == 1 && PW == 2 ? 3 : 1;
+    return QF == 1 ? 3 : 1;
 }
 
 template <int QF, int PW, bool G64>
-__global__ __launch_bounds__(kScoreThreads, (split_waves_per_simd<QF, PW>())) void score_split_kernel(
+__global__ __launch_bounds__(kScoreThreads, (split_waves_per_simd<QF>())) void score_split_kernel(
     const int32_t *si_base, const int32_t *pg_base, const void *qv, const void *qs,
     const void *weights, int32_t nsb, int32_t sbk, int32_t groups_per_wg, int32_t group_rows,
     Rows rows, KCache k, float *logits, int32_t sf) {
@@ -92,7 +100,7 @@ __device__ __forceinline__ float *layer_logits(const LayerSet &ls, int l, float 
 
 // Several layers sharing a schedule, fewer rows than CUs: grid.z = layer.
 template <int QF, int PW, bool G64>
-__global__ __launch_bounds__(kScoreThreads, (split_waves_per_simd<QF, PW>())) void score_split_layers_kernel(
+__global__ __launch_bounds__(kScoreThreads, (split_waves_per_simd<QF>())) void score_split_layers_kernel(
     const int32_t *si_base, const int32_t *pg_base, int32_t nsb, int32_t sbk,
     int32_t groups_per_wg, int32_t group_rows, Rows rows, KCache k, LayerSet ls, float *ws,
     int64_t ws_layer, int32_t sf) {
@@ -369,27 +377,17 @@ static hipError_t launch_sparse_q(const Rows &rows, const void *q_values, const 
         return hipGetLastError();
     }
     float *logits = logits_out ? logits_out : workspace;
-    // Enough workgroups to cover the CUs several times over; 4 waves each with two or
-    // more 64-column groups (two groups a wave hide the schedule-to-K load chain better
-    // than one: measured 3-7 % faster steps on 64- and 128-row decode batches).
-    int gpw = 8;
-    while (gpw < 16 && (int64_t)rows.num_rows * ((ngroups + gpw - 1) / gpw) > 4096) gpw *= 2;
+    const int gpw = kSplitGroupsPerWg;
     const dim3 sgrid(rows.num_rows, (ngroups + gpw - 1) / gpw);
-#define IDX_LAUNCH_SPLIT_G(PW_, G64_)                                                              \
-    hipExtLaunchKernelGGL((score_split_kernel<QF, PW_, G64_>), sgrid, dim3(kScoreThreads), 0,      \
-                          stream, timing.start, timing.stop, 0, s.sparse_indices, s.pages,         \
-                          q_values, q_scales, weights, s.nsb, s.sbk, gpw, grouped_rows(rows),      \
-                          rows, k, logits, sf)
-#define IDX_LAUNCH_SPLIT(PW_)                                                                      \
-    do {                                                                                           \
-        if (s.sbk == 64) IDX_LAUNCH_SPLIT_G(PW_, true);                                            \
-        else IDX_LAUNCH_SPLIT_G(PW_, false);                                                       \
-    } while (0)
-    if (gpw == 8)
-        IDX_LAUNCH_SPLIT(2);
+#define IDX_LAUNCH_SPLIT_G(G64_)                                                                   \
+    hipExtLaunchKernelGGL((score_split_kernel<QF, kSplitGroupsPerWave, G64_>), sgrid,              \
+                          dim3(kScoreThreads), 0, stream, timing.start, timing.stop, 0,            \
+                          s.sparse_indices, s.pages, q_values, q_scales, weights, s.nsb, s.sbk,    \
+                          gpw, grouped_rows(rows), rows, k, logits, sf)
+    if (s.sbk == 64)
+        IDX_LAUNCH_SPLIT_G(true);
     else
-        IDX_LAUNCH_SPLIT(4);
-#undef IDX_LAUNCH_SPLIT
+        IDX_LAUNCH_SPLIT_G(false);
 #undef IDX_LAUNCH_SPLIT_G
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -425,24 +423,17 @@ static hipError_t launch_split_layers(const Rows &rows, int32_t num_layers, cons
     const int ncols = s.nsb * s.sbk;
     const int ngroups = (ncols + 63) / 64;
     const int64_t ws_layer = (int64_t)rows.num_rows * ncols;
-    int gpw = 8;   // as for one layer (launch_sparse_q)
-    while (gpw < 16 && (int64_t)rows.num_rows * ((ngroups + gpw - 1) / gpw) > 4096) gpw *= 2;
+    const int gpw = kSplitGroupsPerWg;   // as for one layer (launch_sparse_q)
     const dim3 sgrid(rows.num_rows, (ngroups + gpw - 1) / gpw, num_layers);
-#define IDX_LAUNCH_SPLIT_LAYERS_G(PW_, G64_)                                                       \
-    hipExtLaunchKernelGGL((score_split_layers_kernel<QF, PW_, G64_>), sgrid, dim3(kScoreThreads),  \
-                          0, stream, timing.start, timing.stop, 0, s.sparse_indices, s.pages,      \
-                          s.nsb, s.sbk, gpw, grouped_rows(rows), rows, k, layers, workspace,       \
-                          ws_layer, sf)
-#define IDX_LAUNCH_SPLIT_LAYERS(PW_)                                                               \
-    do {                                                                                           \
-        if (s.sbk == 64) IDX_LAUNCH_SPLIT_LAYERS_G(PW_, true);                                     \
-        else IDX_LAUNCH_SPLIT_LAYERS_G(PW_, false);                                                \
-    } while (0)
-    if (gpw == 8)
-        IDX_LAUNCH_SPLIT_LAYERS(2);
+#define IDX_LAUNCH_SPLIT_LAYERS_G(G64_)                                                            \
+    hipExtLaunchKernelGGL((score_split_layers_kernel<QF, kSplitGroupsPerWave, G64_>), sgrid,       \
+                          dim3(kScoreThreads), 0, stream, timing.start, timing.stop, 0,            \
+                          s.sparse_indices, s.pages, s.nsb, s.sbk, gpw, grouped_rows(rows), rows,  \
+                          k, layers, workspace, ws_layer, sf)
+    if (s.sbk == 64)
+        IDX_LAUNCH_SPLIT_LAYERS_G(true);
     else
-        IDX_LAUNCH_SPLIT_LAYERS(4);
-#undef IDX_LAUNCH_SPLIT_LAYERS
+        IDX_LAUNCH_SPLIT_LAYERS_G(false);
 #undef IDX_LAUNCH_SPLIT_LAYERS_G
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

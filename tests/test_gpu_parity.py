@@ -801,6 +801,46 @@ def test_separate_value_and_scale_pools(name):
     np.testing.assert_array_equal(got[1][1], got[0][1])
 
 
+# Launch forms that no other case reaches, each named by what it takes
+WIDE_FORMS = {
+    # the dense comparator's selection with 16 keys a thread (over 4096 candidate columns)
+    "dense_8192_columns": W.Spec(name="wf1", num_rows=24, page_size=64, cbs=64, nb=128,
+                                 topk=3000, ke_rule="uniform", ke_lo=8000, ke_hi=14000,
+                                 ks_rule="random", cand_rule="distinct", fill="all"),
+    # row groups for 8192-column rows: two layers in one launch, and bf16 scoring
+    "row_groups_8192_layers": W.Spec(name="wf2", num_rows=2048, page_size=64, cbs=64, nb=100,
+                                     topk=1000, layers=2, mode="prefill", ke_rule="uniform",
+                                     ke_lo=1, ke_hi=6400, ks_rule="random", context=6400,
+                                     cand_rule="messy", fill="all"),
+    "row_groups_8192_bf16": W.Spec(name="wf3", num_rows=2048, page_size=64, cbs=64, nb=100,
+                                   topk=1000, mode="prefill", ke_rule="uniform", ke_lo=1,
+                                   ke_hi=6400, context=6400, cand_rule="causal_all", fill="all"),
+    # two 8-wave rows a CU with 16 keys a thread on 32-token sparse blocks
+    "one_row_two_a_cu_sbk32_16_keys": W.Spec(name="wf4", num_rows=520, page_size=32, cbs=32,
+                                             nb=200, topk=1500, ke_rule="uniform", ke_lo=2000,
+                                             ke_hi=9000, ks_rule="random", cand_rule="messy",
+                                             fill="all"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(WIDE_FORMS))
+def test_wide_launch_forms_all_rows(name):
+    import sparse_attention_indexer_candidate_amd as idx
+
+    spec = WIDE_FORMS[name]
+    case = W.generate(spec, seed=23)
+    if name == "row_groups_8192_layers":
+        _check_layers_call(case, name, "mxfp4")
+        return
+    sf = "bf16" if name.endswith("bf16") else "fp32"
+    g, res = run_and_compare(case, tag=name, score_format=sf)
+    if name == "dense_8192_columns":
+        ctx = int(case.row_ke.max() + 63) // 64 * 64
+        assert idx.idx_num_sparse_blocks(g.cfg) * g.sbk > 4096
+        np.testing.assert_array_equal(_dense_indices(g, case, ctx), res["indices"],
+                                      err_msg="dense != sparse indices")
+
+
 LAYERED = {
     # >= 256 rows of one table row each: every layer in one launch
     "one_launch": W.Spec(name="ml1", num_rows=300, page_size=64, cbs=64, nb=24, topk=300,
