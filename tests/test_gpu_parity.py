@@ -574,8 +574,9 @@ def test_config5_sparse_equals_dense_masked(q_format):
     np.testing.assert_array_equal(dout.cpu().numpy(), res["indices"])
 
 
+@pytest.mark.parametrize("q_format", ["mxfp4", "fp8"])
 @pytest.mark.parametrize("page_size", [16, 32])
-def test_dense_comparator_on_small_pages(page_size):
+def test_dense_comparator_on_small_pages(page_size, q_format):
     """The dense comparator on pages shorter than a 64-token group (each group spans
     several pages, so tiles are resolved one by one): the same indices as the sparse path
     (checked against the oracle on every row) and logits bitwise equal at the candidate
@@ -584,16 +585,16 @@ def test_dense_comparator_on_small_pages(page_size):
 
     spec = W.Spec(name=f"dp{page_size}", num_rows=24, page_size=page_size, cbs=page_size,
                   nb=40, topk=100, ke_rule="uniform", ke_lo=100, ke_hi=2000, ks_rule="random",
-                  cand_rule="messy", fill="all")
+                  cand_rule="messy", fill="all", q_formats=("mxfp4", "fp8"))
     case = W.generate(spec, seed=13)
-    g, res = run_and_compare(case, tag=f"dense-p{page_size}")
+    g, res = run_and_compare(case, tag=f"dense-p{page_size}-{q_format}", q_format=q_format)
     R = case.num_rows
     ctx = int(case.row_ke.max())
     lstride = (ctx + 63) // 64 * 64
     dlog = torch.empty((R, lstride), dtype=torch.float32, device=DEV)
     dout = torch.full((R, spec.topk), -7, dtype=torch.int32, device=DEV)
     L = g.dcase.layers[0]
-    qv, qs = L.q("mxfp4")
+    qv, qs = L.q(q_format)
     idx.idx_dense_masked_logits_topk(g.cfg, g.rows, ctx, qv, qs, L.weights, g.kcaches[0],
                                      g.sched.struct, dout, dout.stride(0), dlog, dlog.stride(0))
     torch.cuda.synchronize()
@@ -841,6 +842,59 @@ def test_wide_launch_forms_all_rows(name):
                                       err_msg="dense != sparse indices")
 
 
+def _sweep_spec(name, rows, cbs, nb, layers=1, prefill=False, topk=None):
+    """A small case for one launch form: cbs sets the sparse block (64 for cbs 64, else
+    cbs) and nb the row width (nb * cbs columns)."""
+    common = dict(name=name, num_rows=rows, page_size=max(cbs, 32) if cbs < 64 else 64, cbs=cbs,
+                  nb=nb, topk=topk or min(500, nb * cbs), layers=layers,
+                  q_formats=("mxfp4", "fp8"), fill="all")
+    if prefill:
+        return W.Spec(mode="prefill", ke_rule="uniform", ke_lo=1, ke_hi=nb * cbs,
+                      context=nb * cbs, ks_rule="random", cand_rule="messy", **common)
+    return W.Spec(ke_rule="uniform", ke_lo=nb * cbs // 2, ke_hi=2 * nb * cbs, ks_rule="random",
+                  cand_rule="messy", **common)
+
+
+# (query format, score format, spec): every instantiation of the one-row, multi-layer and
+# row-group kernels that the other cases leave out, by row count (one or two rows a CU,
+# 8- or 4-wave fp8 rows), width (4 to 32 keys a thread) and sparse block (64, or 32: the
+# per-tile path)
+KERNEL_SWEEP = {
+    "mx_layers_two_a_cu_8keys_sbk32": ("mxfp4", "fp32", _sweep_spec("k1", 260, 32, 100, 2)),
+    "mx_rows_two_a_cu_8keys_sbk64": ("mxfp4", "fp32", _sweep_spec("k2", 520, 64, 50)),
+    "mx_rows_two_a_cu_8keys_sbk32": ("mxfp4", "fp32", _sweep_spec("k3", 520, 32, 100)),
+    "f8_layers_4wave_4keys_sbk32": ("fp8", "fp32", _sweep_spec("k4", 260, 32, 20, 2)),
+    "f8_layers_4wave_8keys_sbk32": ("fp8", "fp32", _sweep_spec("k5", 260, 32, 50, 2)),
+    "f8_layers_4wave_16keys_sbk32": ("fp8", "fp32", _sweep_spec("k6", 260, 32, 100, 2)),
+    "f8_layers_4wave_32keys_sbk32": ("fp8", "fp32", _sweep_spec("k7", 260, 32, 200, 2)),
+    "f8_layers_8wave_4keys_sbk32": ("fp8", "fp32", _sweep_spec("k8", 150, 32, 40, 2)),
+    "f8_layers_8wave_8keys_sbk32": ("fp8", "fp32", _sweep_spec("k9", 150, 32, 100, 2)),
+    "f8_layers_8wave_8keys_sbk64": ("fp8", "fp32", _sweep_spec("k10", 150, 64, 50, 2)),
+    "f8_layers_8wave_16keys_sbk64": ("fp8", "fp32", _sweep_spec("k11", 150, 64, 100, 2)),
+    "f8_rows_4wave_4keys_sbk32": ("fp8", "fp32", _sweep_spec("k12", 520, 32, 20)),
+    "f8_rows_4wave_8keys_sbk32": ("fp8", "fp32", _sweep_spec("k13", 520, 32, 50)),
+    "f8_rows_4wave_8keys_sbk64": ("fp8", "fp32", _sweep_spec("k14", 520, 64, 25)),
+    "f8_rows_4wave_16keys_sbk32": ("fp8", "fp32", _sweep_spec("k15", 520, 32, 100)),
+    "f8_rows_4wave_32keys_sbk32": ("fp8", "fp32", _sweep_spec("k16", 520, 32, 200)),
+    "f8_rows_8wave_8keys_sbk32": ("fp8", "fp32", _sweep_spec("k17", 300, 32, 100)),
+    "bf16_row_group_layers_4096": ("mxfp4", "bf16", _sweep_spec("k18", 2048, 64, 60, 2, True)),
+    "bf16_row_group_layers_8192": ("mxfp4", "bf16", _sweep_spec("k19", 2048, 64, 100, 2, True)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(KERNEL_SWEEP))
+def test_kernel_instantiation_sweep(name):
+    """One case per launch form: single-layer calls against the oracle on every row;
+    multi-layer calls also against one call per layer, bit for bit."""
+    q_format, score_format, spec = KERNEL_SWEEP[name]
+    case = W.generate(spec, seed=29)
+    _say(f"[sweep-{name}] rows={spec.num_rows} cbs={spec.cbs} nb={spec.nb} layers={spec.layers}")
+    if spec.layers > 1:
+        _check_layers_call(case, name, q_format, score_format)
+    else:
+        run_and_compare(case, tag=name, q_format=q_format, score_format=score_format)
+
+
 LAYERED = {
     # >= 256 rows of one table row each: every layer in one launch
     "one_launch": W.Spec(name="ml1", num_rows=300, page_size=64, cbs=64, nb=24, topk=300,
@@ -919,11 +973,11 @@ def test_random_layers_calls(i):
     _check_layers_call(W.generate(spec, seed=70 + i), f"rl{i}", q_format)
 
 
-def _check_layers_call(case, name, q_format):
+def _check_layers_call(case, name, q_format, score_format="fp32"):
     """One multi-layer call (and its full-workspace and all-logits forms) against one call
     per layer, bit for bit, and every layer against the oracle on every row."""
     nl = case.spec.layers
-    g = GpuRun(case, to_device(case, DEV), q_format=q_format)
+    g = GpuRun(case, to_device(case, DEV), q_format=q_format, score_format=score_format)
     g.expand()
     with_logits = [i % 2 == 0 for i in range(nl)]     # odd layers use the workspace
     _say(f"[layers-{name}-{q_format}] one call, {nl} layers")
@@ -962,9 +1016,11 @@ def _check_layers_call(case, name, q_format):
                                           res["logits"].view(np.uint32),
                                           err_msg=f"{name} layer {layer}: logits")
         pool = case.layers[layer].host_pool(case.spec.page_bytes)
-        ora = oracle.indexer_rows(case, layer, None, q_format, pool=pool, threads=THREADS)
+        ora = oracle.indexer_rows(case, layer, None, q_format, pool=pool, threads=THREADS,
+                                  score_format=score_format)
         res["indices"] = outs[layer].cpu().numpy()
-        compare_rows(case, res, ora, case.spec.topk, g.sbk, f"layers-{name} layer {layer}")
+        compare_rows(case, res, ora, case.spec.topk, g.sbk, f"layers-{name} layer {layer}",
+                     score_format=score_format)
 
 
 def test_layers_call_on_long_decode_matches_per_layer_calls():

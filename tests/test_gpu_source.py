@@ -116,6 +116,18 @@ SOURCE_CASES = {
 }
 
 
+@pytest.mark.parametrize("page_size", [16, 32])
+def test_publication_fp8_queries_on_small_pages(page_size):
+    """fp8 queries on pages shorter than a 64-token scoring group (tiles resolved one by
+    one), every row against the oracle."""
+    spec = W.Spec(name=f"pf{page_size}", num_rows=24, page_size=page_size, cbs=page_size, nb=30,
+                  topk=100, ke_rule="uniform", ke_lo=10, ke_hi=3000, ks_rule="random",
+                  cand_rule="distinct", fill="all", q_formats=("mxfp4", "fp8"))
+    case = W.generate(spec, seed=47)
+    cand, logits = publish(case, to_device(case, DEV), q_format="fp8")
+    compare_publication(case, cand, logits, spec.nb, f"source-fp8-p{page_size}", "fp8")
+
+
 @pytest.mark.parametrize("name", sorted(SOURCE_CASES))
 def test_publication_matches_oracle_all_rows(name):
     spec, nb = SOURCE_CASES[name]
