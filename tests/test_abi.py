@@ -68,6 +68,25 @@ def test_header_is_c99_and_struct_layouts_match_the_binding(tmp_path):
             assert int(got[f"{name}.{f}"]) == getattr(st, f).offset, f"{name}.{f}"
 
 
+def test_readme_c_example_compiles_against_the_header(tmp_path):
+    """The README's C call sequence stays valid C99 against include/idx.h."""
+    import subprocess
+
+    text = open(os.path.join(ROOT, "README.md")).read()
+    code = re.search(r"```c\n(.*?)```", text, re.S).group(1)
+    decls = ("int32_t max_rows = 64, n = 64; int64_t page_bytes = 4352, num_pages = 100;\n"
+             "int64_t table_stride = 128; int32_t num_tables = 64, pages_per_table = 128;\n"
+             "void *d_ks = 0, *d_ke = 0, *d_table = 0, *d_values = 0, *d_scales = 0,\n"
+             "     *d_block_table = 0, *d_sparse_indices = 0, *d_end = 0, *d_work = 0,\n"
+             "     *d_candidates = 0, *d_q_values = 0, *d_q_scales = 0, *d_weights = 0,\n"
+             "     *d_topk = 0, *d_ws = 0, *stream = 0;\n")
+    src = tmp_path / "readme.c"
+    src.write_text('#include <stddef.h>\n#include <stdint.h>\n#include "idx.h"\nint main(void) {\n'
+                   + decls + code + "(void)nsb;\nreturn 0;\n}\n")
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-Wno-unused-variable",
+                    "-fsyntax-only", "-I", os.path.join(ROOT, "include"), str(src)], check=True)
+
+
 def cfg(**kw):
     base = dict(num_heads=64, head_dim=128, q_format=0, page_size=64, candidate_block_size=64,
                 sparse_block_kv=0, num_candidate_blocks=64, topk=2048, score_format=0)
