@@ -1,9 +1,10 @@
 """Throughput of the candidate-consuming sparse MQA-logits indexer on one MI355X.
 
-One step = the whole hot path over one batch: idx_expand_candidates (the shared
-sparse-column schedule) followed by the consuming layers (paged gather, MX-scaled
-MFMA, ReLU + fp32 head reduce, per-row top-k): one idx_sparse_mqa_logits_topk_layers
-call for a step's layers.  The default workload is the largest one that fits one GPU,
+One step = the whole hot path over one batch: the candidate expansion (the shared
+sparse-column schedule) and the consuming layers (paged gather, MX-scaled MFMA, ReLU +
+fp32 head reduce, per-row top-k) in one idx_expand_and_score_layers call for a step's
+layers (--separate-expansion: idx_expand_candidates, then one
+idx_sparse_mqa_logits_topk_layers call).  The default workload is the largest one that fits one GPU,
 the long-context decode batch (256 rows, contexts 32k-128k, 128 candidate blocks of
 64 tokens, top-2048, 4 consuming layers sharing one schedule).  Inputs are seeded and
 synthetic and already resident in HBM when the timed region starts; the step rotates
@@ -435,7 +436,7 @@ def traffic_for(kernel_name: str, workload: str, q_format: str, score_format: st
 
 def run_workload(idx, W, config: int, args, dev, stream, steps: int, warmup: int,
                  layers: int = 0, per_layer_calls: bool = False, graph: bool = False,
-                 rows: int = 0):
+                 rows: int = 0, separate_expansion: bool = False):
     """Generates one workload, times `steps` steps (after `warmup`) with nothing attached,
     then an event pass of EVENT_STEPS steps whose scoring launches carry dispatch events.
     Returns the measurements and the accounting the report needs.  layers / rows (> 0)
@@ -478,14 +479,17 @@ def run_workload(idx, W, config: int, args, dev, stream, steps: int, warmup: int
     # The step's consuming layers go to the library in one call; the library reports
     # which kernels that call launches (one rule for the launch and this accounting).
     dense = args.path == "dense"
-    layers_call = not dense and spec.layers > 1 and not per_layer_calls
+    # The step's expansion goes into the same call (idx_expand_and_score_layers) unless
+    # asked to keep its own launch (idx_expand_candidates first).
+    expand_in_call = not dense and not per_layer_calls and not separate_expansion
+    layers_call = not dense and (spec.layers > 1 or expand_in_call) and not per_layer_calls
     ncols = idx.idx_num_sparse_blocks(cfg) * cfg.sparse_block_kv
     ws_rows_all = R * spec.layers
     plan = idx.idx_sparse_plan(cfg, R, spec.layers if layers_call else 1, logits_home=True)
     if dense:
         kernel_name, fused, launch_layers = "score_dense_kernel", False, 1
     else:
-        kernel_name = plan["scoring_kernel"]
+        kernel_name = plan["expand_and_score_kernel" if expand_in_call else "scoring_kernel"]
         fused = plan["selects_in_scoring_kernel"]
         launch_layers = plan["layers_per_scoring_launch"]
     calls_per_step = 1 if layers_call else spec.layers
@@ -547,16 +551,21 @@ def run_workload(idx, W, config: int, args, dev, stream, steps: int, warmup: int
     # steps are not bound by Python.
     for p in plans:
         d = p["d"]
-        p["expand"] = idx.bind_expand_candidates(cfg, p["rows"], p["kc"][0], d.candidate_blocks,
-                                                 d.candidate_blocks.stride(0), p["sched"].struct,
-                                                 stream=sh)
+        p["expand"] = None if expand_in_call else idx.bind_expand_candidates(
+            cfg, p["rows"], p["kc"][0], d.candidate_blocks, d.candidate_blocks.stride(0),
+            p["sched"].struct, stream=sh)
         p["layers"] = []
         if layers_call:
             entries = [(*L.q(args.q_format), L.w(sfmt), p["kc"][layer], p["out_l"][layer], None)
                        for layer, L in enumerate(d.layers)]
-            p["layers"].append(idx.bind_sparse_mqa_logits_topk_layers(
-                cfg, p["rows"], p["sched"].struct, entries, spec.topk, p["ws"], p["ws"].numel(),
-                stream=sh))
+            if expand_in_call:
+                p["layers"].append(idx.bind_expand_and_score_layers(
+                    cfg, p["rows"], d.candidate_blocks, d.candidate_blocks.stride(0),
+                    p["sched"].struct, entries, spec.topk, p["ws"], p["ws"].numel(), stream=sh))
+            else:
+                p["layers"].append(idx.bind_sparse_mqa_logits_topk_layers(
+                    cfg, p["rows"], p["sched"].struct, entries, spec.topk, p["ws"],
+                    p["ws"].numel(), stream=sh))
         for layer, L in enumerate([] if layers_call else d.layers):
             qv, qs = L.q(args.q_format)
             if dense:
@@ -571,7 +580,8 @@ def run_workload(idx, W, config: int, args, dev, stream, steps: int, warmup: int
     set_events = idx.lib.idx_set_timing_events
 
     def launch(p, events=None):
-        p["expand"]()
+        if p["expand"] is not None:
+            p["expand"]()
         for c, call in enumerate(p["layers"]):
             if events is not None:
                 set_events(*events[c])
@@ -608,7 +618,8 @@ def run_workload(idx, W, config: int, args, dev, stream, steps: int, warmup: int
     kernel_ms = [a.elapsed_time(b) for a, b in ev]
     return dict(spec=spec, case=case, cfg=cfg, ends=ends, ctx=ctx, max_ctx=max_ctx, R=R,
                 gen_s=gen_s, kernel_name=kernel_name, fused=fused, launch_layers=launch_layers,
-                layers_call=layers_call, plan=plan, kernel_bytes=kernel_bytes,
+                layers_call=layers_call, expand_in_call=expand_in_call, plan=plan,
+                kernel_bytes=kernel_bytes,
                 step_bytes=step_bytes, nrep=nrep, elapsed=elapsed, steps=steps,
                 kernel_ms=kernel_ms)
 
@@ -707,6 +718,9 @@ def main():
                          "e.g. --config 6 --rows 512 for 256 requests of two decode rows")
     ap.add_argument("--per-layer-calls", action="store_true",
                     help="one sparse call per layer instead of one multi-layer call")
+    ap.add_argument("--separate-expansion", action="store_true",
+                    help="the expansion in its own call (idx_expand_candidates) before the "
+                         "scoring call, instead of idx_expand_and_score_layers")
     ap.add_argument("--graph", action="store_true",
                     help="replay each timed step as a captured HIP graph (measured slower than "
                          "direct launches on this stack: 21.7 vs 14.8 us a decode-batch step)")
@@ -758,7 +772,7 @@ def main():
     dense = args.path == "dense"
     m = run_workload(idx, W, args.config, args, dev, stream, args.steps, args.warmup,
                      layers=args.layers, per_layer_calls=args.per_layer_calls, graph=args.graph,
-                     rows=args.rows)
+                     rows=args.rows, separate_expansion=args.separate_expansion)
     spec, R = m["spec"], m["R"]
     peaks = measured_peaks(stream)
     roof = roofline(m, args.config, args.q_format, peaks, dense, args.score_format)
@@ -786,6 +800,9 @@ def main():
                    "score_format": args.score_format,
                    "path": args.path,
                    "calls": "one call for all layers" if m["layers_call"] else "one call per layer",
+                   "expansion": ("in the scoring kernel" if m["plan"]["expansion_in_scoring_kernel"]
+                                 else "own launch, in the same call") if m["expand_in_call"]
+                                else "own call",
                    "launch": "HIP graph per step" if args.graph else "direct",
                    "input_copies": m["nrep"], "seed": args.seed},
         "roofline": roof,

@@ -195,6 +195,9 @@ typedef struct {
     int32_t selects_in_scoring_kernel;  /* 1: no logits leave the scoring kernel */
     const char *scoring_kernel;         /* the kernel that streams K (static string) */
     const char *selection_kernel;       /* the separate selection kernel, or "" */
+    int32_t expansion_in_scoring_kernel; /* 1: idx_expand_and_score_layers expands each row
+                                            inside its scoring kernel (no expansion launch) */
+    const char *expand_and_score_kernel; /* the kernel that streams K in that call */
 } idx_plan_info;
 
 /* Fills *out for a call on num_rows rows and num_layers layers (1..IDX_MAX_LAYERS).
@@ -208,7 +211,8 @@ int idx_sparse_plan(const idx_config *cfg, int32_t num_rows, int32_t num_layers,
 
 /* Optional timing hook for benchmarks (not a step of the method: the pages publish no
  * timings).  While set, every idx_sparse_mqa_logits_topk,
- * idx_sparse_mqa_logits_topk_layers, idx_dense_masked_logits_topk and
+ * idx_sparse_mqa_logits_topk_layers, idx_expand_and_score_layers,
+ * idx_dense_masked_logits_topk and
  * idx_gather_k_workspace call made on this thread launches its scoring kernel (the one
  * that streams the K cache; for the gather, its one kernel) with start_event and
  * stop_event attached
@@ -318,6 +322,29 @@ int idx_sparse_mqa_logits_topk_layers(const idx_config *cfg, const idx_rows *row
                                       const idx_schedule *sched, int32_t num_layers,
                                       const idx_layer *layers, int64_t out_stride,
                                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* Step a1 and steps a2-a6 for the consuming layers of one step in one call: the same
+ * results (every layer's topk_indices and logits_out) and the same schedule in sched as
+ * idx_expand_candidates(cfg, rows, &layers[0].k, candidate_blocks, cand_stride, sched)
+ * followed by idx_sparse_mqa_logits_topk_layers(cfg, rows, sched, num_layers, layers,
+ * ...), so a later call of the step can still reuse the schedule (the backend source
+ * page: the step's first consuming layer builds the expansion and schedule that later
+ * ones reuse).  Where the rows take the one-row-per-workgroup kernel (num_rows >= the
+ * device's CUs, or num_rows * num_layers >= CUs with two or more layers; not the prefill
+ * row-group case) in one round (num_rows * num_layers <= 2 x CUs) with MXFP4 queries and
+ * sparse_block_kv 64 (so NB <= 128), each scoring workgroup expands its row in LDS and
+ * layer 0's workgroups write the schedule: one launch, no expansion launch and no
+ * schedule round trip through memory before the K stream starts
+ * (idx_sparse_plan's expansion_in_scoring_kernel says which).  Otherwise the two calls'
+ * launches.  Arguments and errors: those of the two calls (candidate_blocks
+ * and cand_stride as in idx_expand_candidates; the workspace rule as in
+ * idx_sparse_mqa_logits_topk_layers, also when the one launch needs none).  The timing
+ * events time the scoring launch as in idx_sparse_mqa_logits_topk_layers. */
+int idx_expand_and_score_layers(const idx_config *cfg, const idx_rows *rows,
+                                const int32_t *candidate_blocks, int64_t cand_stride,
+                                const idx_schedule *sched, int32_t num_layers,
+                                const idx_layer *layers, int64_t out_stride, void *workspace,
+                                size_t workspace_bytes, void *stream);
 
 /* Step a9, the comparator the sparse path replaces (the dense indexer scores the
  * whole context and masks to the candidates: module summary of the

@@ -31,7 +31,8 @@ IDX_MAX_TOPK = 8192
 EXPORTED = ("idx_check_config", "idx_num_sparse_blocks", "idx_schedule_work_bytes",
             "idx_workspace_bytes", "idx_last_error", "idx_set_timing_events",
             "idx_expand_candidates", "idx_sparse_mqa_logits_topk",
-            "idx_sparse_mqa_logits_topk_layers", "idx_dense_masked_logits_topk",
+            "idx_sparse_mqa_logits_topk_layers", "idx_expand_and_score_layers",
+            "idx_dense_masked_logits_topk",
             "idx_gather_k_workspace", "idx_sparse_plan", "idx_sparse_mqa_logits_topk_noalloc",
             "idx_publish_workspace_bytes", "idx_publish_candidates",
             "idx_measure_read", "idx_measure_mfma", "idx_measure_mfma_relu",
@@ -92,7 +93,9 @@ IDX_PLAN_ROW_GROUP_LAYERS = 6
 class idx_plan_info(ctypes.Structure):
     _fields_ = [("plan", ctypes.c_int32), ("layers_per_scoring_launch", ctypes.c_int32),
                 ("selects_in_scoring_kernel", ctypes.c_int32),
-                ("scoring_kernel", ctypes.c_char_p), ("selection_kernel", ctypes.c_char_p)]
+                ("scoring_kernel", ctypes.c_char_p), ("selection_kernel", ctypes.c_char_p),
+                ("expansion_in_scoring_kernel", ctypes.c_int32),
+                ("expand_and_score_kernel", ctypes.c_char_p)]
 
 
 def _load():
@@ -135,6 +138,9 @@ def _load():
     L.idx_sparse_mqa_logits_topk_layers.argtypes = [P(idx_config), P(idx_rows), P(idx_schedule),
                                                     i32, P(idx_layer), i64, vp, sz, vp]
     L.idx_sparse_mqa_logits_topk_layers.restype = ctypes.c_int
+    L.idx_expand_and_score_layers.argtypes = [P(idx_config), P(idx_rows), vp, i64,
+                                              P(idx_schedule), i32, P(idx_layer), i64, vp, sz, vp]
+    L.idx_expand_and_score_layers.restype = ctypes.c_int
     L.idx_dense_masked_logits_topk.argtypes = [P(idx_config), P(idx_rows), i32, vp, vp, vp,
                                                P(idx_kcache), P(idx_schedule), vp, i64, vp, i64,
                                                vp, sz, vp]
@@ -218,7 +224,9 @@ def idx_sparse_plan(cfg: idx_config, num_rows: int, num_layers: int = 1,
     return dict(plan=info.plan, layers_per_scoring_launch=info.layers_per_scoring_launch,
                 selects_in_scoring_kernel=bool(info.selects_in_scoring_kernel),
                 scoring_kernel=info.scoring_kernel.decode(),
-                selection_kernel=info.selection_kernel.decode())
+                selection_kernel=info.selection_kernel.decode(),
+                expansion_in_scoring_kernel=bool(info.expansion_in_scoring_kernel),
+                expand_and_score_kernel=info.expand_and_score_kernel.decode())
 
 
 def idx_expand_candidates(cfg, rows, k, candidate_blocks, cand_stride, sched, stream=None):
@@ -262,6 +270,17 @@ def idx_sparse_mqa_logits_topk_layers(cfg, rows, sched, layers, out_stride, work
     return _check(lib.idx_sparse_mqa_logits_topk_layers(
         ctypes.byref(cfg), ctypes.byref(rows), ctypes.byref(sched), len(arr), arr, out_stride,
         _p(workspace), workspace_bytes, _p(stream)))
+
+
+def idx_expand_and_score_layers(cfg, rows, candidate_blocks, cand_stride, sched, layers,
+                                out_stride, workspace=None, workspace_bytes=0, stream=None):
+    """idx_expand_candidates (with layers[0]'s cache) then idx_sparse_mqa_logits_topk_layers
+    in one call; layers as for the latter."""
+    arr = layers if isinstance(layers, ctypes.Array) else make_layers(layers)
+    return _check(lib.idx_expand_and_score_layers(
+        ctypes.byref(cfg), ctypes.byref(rows), _p(candidate_blocks), cand_stride,
+        ctypes.byref(sched), len(arr), arr, out_stride, _p(workspace), workspace_bytes,
+        _p(stream)))
 
 
 def idx_dense_masked_logits_topk(cfg, rows, max_ctx, q_values, q_scales, weights, k, sched,
@@ -412,6 +431,17 @@ def bind_sparse_mqa_logits_topk_layers(cfg, rows, sched, layers, out_stride, wor
     return BoundCall(lib.idx_sparse_mqa_logits_topk_layers,
                      (ctypes.byref(cfg), ctypes.byref(rows), ctypes.byref(sched), len(arr), arr,
                       out_stride, vp(workspace), workspace_bytes, vp(stream)),
+                     (cfg, rows, sched, arr))
+
+
+def bind_expand_and_score_layers(cfg, rows, candidate_blocks, cand_stride, sched, layers,
+                                 out_stride, workspace=None, workspace_bytes=0, stream=None):
+    arr = layers if isinstance(layers, ctypes.Array) else make_layers(layers)
+    vp = lambda x: ctypes.c_void_p(_p(x))
+    return BoundCall(lib.idx_expand_and_score_layers,
+                     (ctypes.byref(cfg), ctypes.byref(rows), vp(candidate_blocks), cand_stride,
+                      ctypes.byref(sched), len(arr), arr, out_stride, vp(workspace),
+                      workspace_bytes, vp(stream)),
                      (cfg, rows, sched, arr))
 
 

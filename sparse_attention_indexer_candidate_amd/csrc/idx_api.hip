@@ -251,7 +251,7 @@ int idx_sparse_plan(const idx_config *cfg, int32_t num_rows, int32_t num_layers,
                                          idx::device_cus(), logits_home != 0);
     static_assert(IDX_PLAN_ROW_GROUP_LAYERS == idx::kPlanRowGroupLayers &&
                   IDX_PLAN_SPLIT == idx::kPlanSplit, "one numbering of the plans");
-    idx_plan_info info = {p, 1, 0, "", ""};
+    idx_plan_info info = {p, 1, 0, "", "", 0, ""};
     switch (p) {
     case idx::kPlanNone: break;
     case idx::kPlanSplit:
@@ -283,6 +283,13 @@ int idx_sparse_plan(const idx_config *cfg, int32_t num_rows, int32_t num_layers,
         break;
     }
     if (p == idx::kPlanNone) info.layers_per_scoring_launch = 0;
+    info.expand_and_score_kernel = info.scoring_kernel;
+    if (idx::expansion_fuses(cfg->q_format, sbk, cfg->num_candidate_blocks, ncols, num_rows,
+                             num_layers, idx::device_cus())) {
+        info.expansion_in_scoring_kernel = 1;
+        info.expand_and_score_kernel =
+            p == idx::kPlanOneRow ? "expand_fused_row_kernel" : "expand_fused_layers_kernel";
+    }
     *out = info;
     return ok();
 }
@@ -395,15 +402,14 @@ int idx_sparse_mqa_logits_topk_noalloc(const idx_config *cfg, const idx_rows *ro
     return ok();
 }
 
-int idx_sparse_mqa_logits_topk_layers(const idx_config *cfg, const idx_rows *rows,
-                                      const idx_schedule *sched, int32_t num_layers,
-                                      const idx_layer *layers, int64_t out_stride,
-                                      void *workspace, size_t workspace_bytes, void *stream) {
-    int32_t sbk = 0;
+// The checks of a multi-layer call after those of its config, rows and schedule: the
+// layer count, every layer's pool, query and outputs (one cache geometry: only values
+// and scales may differ from layer 0's), and the workspace when some layer has no
+// logits_out.  Fills ls.
+static int check_layers(const idx_config *cfg, const idx_rows *rows, int32_t num_layers,
+                        const idx_layer *layers, int64_t out_stride, const idx::Schedule &s,
+                        void *workspace, size_t workspace_bytes, idx::LayerSet &ls) {
     int rc;
-    if ((rc = check_filled(cfg, &sbk)) || (rc = check_rows(rows)) ||
-        (rc = check_schedule(cfg, rows, sched)))
-        return rc;
     if (num_layers < 1 || num_layers > IDX_MAX_LAYERS)
         return fail(IDX_EINVAL, "num_layers %d must be in [1, %d]", num_layers, IDX_MAX_LAYERS);
     if (!layers) return fail(IDX_EINVAL, "layers is NULL");
@@ -411,7 +417,7 @@ int idx_sparse_mqa_logits_topk_layers(const idx_config *cfg, const idx_rows *row
         return fail(IDX_EINVAL, "out_stride %lld < topk %d", (long long)out_stride, cfg->topk);
     const idx_kcache &k0 = layers[0].k;
     bool need_ws = false;
-    idx::LayerSet ls = {};
+    ls = {};
     for (int l = 0; l < num_layers; ++l) {
         const idx_layer &L = layers[l];
         if ((rc = check_kcache(cfg, &L.k)) || (rc = check_q(cfg, L.q_values, L.q_scales, L.weights))) {
@@ -439,7 +445,6 @@ int idx_sparse_mqa_logits_topk_layers(const idx_config *cfg, const idx_rows *row
         ls.logits_out[l] = L.logits_out;
         ls.out[l] = L.topk_indices;
     }
-    const idx::Schedule s = to_schedule(cfg, sbk, sched);
     if (need_ws) {
         const size_t need = (size_t)rows->num_rows * s.nsb * s.sbk * sizeof(float);
         if (!workspace && need) return fail(IDX_EWORKSPACE, "workspace is NULL (needs %zu bytes)", need);
@@ -447,14 +452,63 @@ int idx_sparse_mqa_logits_topk_layers(const idx_config *cfg, const idx_rows *row
             return fail(IDX_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
         if (!aligned(workspace, 16)) return fail(IDX_EINVAL, "workspace must be 16-byte aligned");
     }
-    static_assert(idx::kMaxLayers == IDX_MAX_LAYERS, "one layer limit for the launch and the ABI");
+    return IDX_OK;
+}
+
+static_assert(idx::kMaxLayers == IDX_MAX_LAYERS, "one layer limit for the launch and the ABI");
+
+int idx_sparse_mqa_logits_topk_layers(const idx_config *cfg, const idx_rows *rows,
+                                      const idx_schedule *sched, int32_t num_layers,
+                                      const idx_layer *layers, int64_t out_stride,
+                                      void *workspace, size_t workspace_bytes, void *stream) {
+    int32_t sbk = 0;
+    int rc;
+    if ((rc = check_filled(cfg, &sbk)) || (rc = check_rows(rows)) ||
+        (rc = check_schedule(cfg, rows, sched)))
+        return rc;
+    const idx::Schedule s = to_schedule(cfg, sbk, sched);
+    idx::LayerSet ls;
+    if ((rc = check_layers(cfg, rows, num_layers, layers, out_stride, s, workspace,
+                           workspace_bytes, ls)))
+        return rc;
     if ((rc = hip_status(idx::launch_sparse_layers(cfg->q_format, cfg->score_format,
                                                    to_rows(rows), num_layers, ls,
-                                                   to_kcache(cfg, &k0), s, (float *)workspace,
+                                                   to_kcache(cfg, &layers[0].k), s,
+                                                   (float *)workspace,
                                                    workspace ? workspace_bytes : 0, cfg->topk,
                                                    out_stride, g_timing,
                                                    (hipStream_t)stream),
                          "sparse layers launch")))
+        return rc;
+    return ok();
+}
+
+int idx_expand_and_score_layers(const idx_config *cfg, const idx_rows *rows,
+                                const int32_t *candidate_blocks, int64_t cand_stride,
+                                const idx_schedule *sched, int32_t num_layers,
+                                const idx_layer *layers, int64_t out_stride, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+    int32_t sbk = 0;
+    int rc;
+    if ((rc = check_filled(cfg, &sbk)) || (rc = check_rows(rows)) ||
+        (rc = check_schedule(cfg, rows, sched)))
+        return rc;
+    if (rows->num_rows > 0 && !candidate_blocks) return fail(IDX_EINVAL, "candidate_blocks is NULL");
+    if (cand_stride < cfg->num_candidate_blocks)
+        return fail(IDX_EINVAL, "cand_stride %lld < num_candidate_blocks %d",
+                    (long long)cand_stride, cfg->num_candidate_blocks);
+    const idx::Schedule s = to_schedule(cfg, sbk, sched);
+    idx::LayerSet ls;
+    if ((rc = check_layers(cfg, rows, num_layers, layers, out_stride, s, workspace,
+                           workspace_bytes, ls)))
+        return rc;
+    if ((rc = hip_status(idx::launch_expand_sparse_layers(
+                             cfg->q_format, cfg->score_format, to_rows(rows), num_layers, ls,
+                             to_kcache(cfg, &layers[0].k), s, candidate_blocks, cand_stride,
+                             cfg->num_candidate_blocks, cfg->candidate_block_size,
+                             (float *)workspace, workspace ? workspace_bytes : 0, cfg->topk,
+                             out_stride, g_timing, (hipStream_t)stream),
+                         "expand and score launch")))
         return rc;
     return ok();
 }

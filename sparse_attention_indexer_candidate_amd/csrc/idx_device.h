@@ -196,6 +196,116 @@ __device__ int block_excl_scan(int x, int *total, int *wsum) {
     return before + incl - x;
 }
 
+// ---------------------------------------------------------------- expansion ----
+
+// Candidate expansion of one row by one wave.  craw: the row's candidate ids, lane l
+// holding ids l, l + 64, ... (E a lane; -1 past NB).  Ids that are negative or hold no
+// token of [ks, ke) become INT_MAX; a bitonic sort over the 64*E register slots
+// (shuffles across lanes, swaps within a lane) orders them; an id is kept if it differs
+// from its predecessor (so repeats count once); kept blocks split into cbs/sbk sparse
+// blocks, of which those holding a token of [ks, ke) and mapped by the block table
+// inside the pool are listed in order with their page: out_si / out_pg [0, nlist), then
+// -1 up to nsb (global or LDS memory).  stage: the wave's scratch of 64*E ints (LDS).
+// Returns nlist; ntok gets the row's valid token count (the same in every lane).
+template <int E>
+__device__ __forceinline__ int expand_row(const int (&craw)[E], int64_t ks, int64_t ke,
+                                          bool tbl_ok, int tbl, int32_t cbs, int32_t sbk,
+                                          int32_t nsb, const KCache &k, int32_t *stage,
+                                          int32_t *out_si, int32_t *out_pg, int &ntok) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int per = cbs / sbk;
+    int v[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int b = craw[e];
+        const bool ok = b >= 0 && (int64_t)b * cbs < ke && ((int64_t)b + 1) * cbs > ks;
+        v[e] = ok ? b : INT_MAX;
+    }
+#pragma unroll
+    for (int kk = 2; kk <= kWave * E; kk <<= 1) {
+#pragma unroll
+        for (int j = kk >> 1; j > 0; j >>= 1) {
+            if (j >= kWave) {
+                const int je = j / kWave;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    if (e & je) continue;
+                    const int e2 = e | je;
+                    const bool asc = ((e * kWave + lane) & kk) == 0;
+                    const int a = v[e], b = v[e2];
+                    const bool sw = asc ? (a > b) : (a < b);
+                    v[e] = sw ? b : a;
+                    v[e2] = sw ? a : b;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const int x = e * kWave + lane;
+                    const int p = lane_xor(v[e], j);
+                    const bool lower = (x & j) == 0, asc = (x & kk) == 0;
+                    v[e] = (lower == asc) ? min(v[e], p) : max(v[e], p);
+                }
+            }
+        }
+    }
+    int nkept = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        int prev = __builtin_amdgcn_update_dpp(0, v[e], 0x138, 0xF, 0xF, false);   // wave_shr:1
+        if (lane == 0) prev = (e == 0) ? -1 : __builtin_amdgcn_readlane(v[e > 0 ? e - 1 : 0], kWave - 1);
+        const bool keep = v[e] != INT_MAX && v[e] != prev;
+        const uint64_t m = __ballot(keep);
+        if (keep) stage[nkept + __popcll(m & lanemask_lt())] = v[e];
+        nkept += __popcll(m);
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // E sparse blocks a lane per pass, every block-table load of the pass issued before
+    // the first is used: one memory round trip per pass (one in all when each candidate
+    // block is one sparse block).
+    const int total = nkept * per;
+    int nlist = 0;
+    ntok = 0;
+    for (int base = 0; base < total; base += E * kWave) {
+        int32_t sb[E], page[E], cnt[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int i = base + e * kWave + lane;
+            sb[e] = 0;
+            page[e] = -1;
+            cnt[e] = 0;
+            if (i < total) {
+                const int64_t sb64 = (int64_t)stage[i / per] * per + i % per;
+                const int64_t lo = max(sb64 * sbk, ks), hi = min(sb64 * sbk + sbk, ke);
+                const int64_t lp = sb64 * sbk / k.page_size;
+                if (hi > lo && tbl_ok && lp < k.pages_per_table) {
+                    page[e] = k.block_table[(int64_t)tbl * k.block_table_stride + lp];
+                    cnt[e] = (int)(hi - lo);
+                }
+                sb[e] = (int32_t)sb64;
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const bool ok = page[e] >= 0 && page[e] < k.num_pages;
+            if (ok) ntok += cnt[e];
+            const uint64_t m = __ballot(ok);
+            if (ok) {
+                const int pos = nlist + __popcll(m & lanemask_lt());
+                out_si[pos] = sb[e];
+                out_pg[pos] = page[e];
+            }
+            nlist += __popcll(m);
+        }
+    }
+    for (int i = nlist + lane; i < nsb; i += kWave) {
+        out_si[i] = -1;
+        out_pg[i] = -1;
+    }
+    ntok = wave_sum(ntok);
+    return nlist;
+}
+
 // ---------------------------------------------------------------- scoring ------
 
 // Raw K data of one lane for a 16-token tile: 16 bytes of packed e2m1 (dimensions

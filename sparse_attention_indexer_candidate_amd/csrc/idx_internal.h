@@ -122,6 +122,21 @@ hipError_t launch_sparse_layers(int q_format, int score_format, const Rows &rows
                                 int32_t topk, int64_t out_stride, const Timing &timing,
                                 hipStream_t stream);
 
+// launch_expand then launch_sparse_layers, in one launch where the rows take the one-row
+// kernels (plan kPlanOneRow / kPlanOneRowLayers) in one round (rows x layers <= 2 x CUs)
+// with MXFP4 queries, sbk = 64 and nb <= 128 (expansion_fuses): each workgroup expands its
+// row in LDS and layer 0's workgroups write the schedule, the same values launch_expand
+// writes.  Otherwise the two launches.
+bool expansion_fuses(int q_format, int32_t sbk, int32_t nb, int32_t ncols, int32_t num_rows,
+                     int32_t num_layers, int cus);
+hipError_t launch_expand_sparse_layers(int q_format, int score_format, const Rows &rows,
+                                       int32_t num_layers, const LayerSet &layers,
+                                       const KCache &k, const Schedule &s, const int32_t *cand,
+                                       int64_t cand_stride, int32_t nb, int32_t cbs,
+                                       float *workspace, size_t workspace_bytes, int32_t topk,
+                                       int64_t out_stride, const Timing &timing,
+                                       hipStream_t stream);
+
 // Row groups (plan kPlanRowGroup / kPlanRowGroupLayers; MXFP4 queries, sbk = 64, NB*cbs <=
 // 8192): two rows a workgroup share K tiles, logits in LDS, selected in turn.  Called by
 // launch_sparse / launch_sparse_layers when their plan says so; the events ride on the

@@ -136,16 +136,34 @@ struct FusedLds {
     int32_t si[kMaxNSB];
     int32_t pg[kMaxNSB];
     int unit;
+    int kept;                                 // the row's kept count when expanded here
     SelectLds<NT, 5> sel;
 };
 
-// U: 64-column groups a wave takes per unit (two units in flight).
-template <int QF, int NT, int KPT, int U, bool G64>
+// A row's candidate expansion inside the one-row kernels (fused_row with E > 0): the
+// published candidate blocks, and the schedule arrays that the workgroup writes when
+// kept is set (layer 0's workgroups), so the schedule is the expansion launch's.
+struct FusedExpand {
+    const int32_t *cand;
+    int64_t cand_stride;
+    int32_t nb;
+    int32_t cbs;
+    int32_t *si;
+    int32_t *pg;
+    int32_t *end;
+    int32_t *kept;   // null: this workgroup writes no schedule
+};
+
+// U: 64-column groups a wave takes per unit (two units in flight).  E = 0: the row's
+// schedule comes from the expansion launch (si_base, pg_base, p_kept); E > 0: wave 0
+// expands the row's candidates (ex, E ids a lane, nb <= 64 E) into LDS while the other
+// waves load the query, and si_base, pg_base and p_kept are not read.
+template <int QF, int NT, int KPT, int U, bool G64, int E = 0>
 __device__ __forceinline__ void fused_row(
     FusedLds<NT> &L, int row, const int32_t *si_base, const int32_t *pg_base, const void *qv,
     const void *qs, const void *weights, const int32_t *p_kept, int32_t nsb, int32_t lsbk,
     const Rows &rows, const KCache &k, float *logits_out, int32_t topk, int32_t *out,
-    int64_t ostride, int sf) {
+    int64_t ostride, int sf, const FusedExpand &ex = {}) {
     uint32_t *s_word = L.word;
     int32_t *s_si = L.si;
     int32_t *s_pg = L.pg;
@@ -154,30 +172,74 @@ __device__ __forceinline__ void fused_row(
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int sbk = 1 << lsbk;
     RowInfo ri;
-    ri.si = si_base + (int64_t)row * nsb;
-    ri.pg = pg_base + (int64_t)row * nsb;
-    ri.kept = max(0, min(uniform(p_kept[row]), nsb));
-    ri.valid_cols = ri.kept * sbk;
     ri.ncols = nsb * sbk;
     ri.tbl_ok = true;
     QFrag<QF> f;
-    load_q<QF>(f, qv, qs, weights, sf, row, lane);   // overlaps the schedule copy
-    // Every slot [0, nsb) is written by the expansion (-1 past the kept count), so the
-    // copy is not bound by the kept load: the schedule, the kept count and the query
-    // are one memory round trip, not two.
-    for (int i = tid; i < nsb; i += NT) {
-        s_si[i] = ri.si[i];
-        s_pg[i] = ri.pg[i];
+    if constexpr (E == 0) {
+        ri.si = si_base + (int64_t)row * nsb;
+        ri.pg = pg_base + (int64_t)row * nsb;
+        ri.kept = max(0, min(uniform(p_kept[row]), nsb));
+        load_q<QF>(f, qv, qs, weights, sf, row, lane);   // overlaps the schedule copy
+        // Every slot [0, nsb) is written by the expansion (-1 past the kept count), so
+        // the copy is not bound by the kept load: the schedule, the kept count and the
+        // query are one memory round trip, not two.
+        for (int i = tid; i < nsb; i += NT) {
+            s_si[i] = ri.si[i];
+            s_pg[i] = ri.pg[i];
+        }
+        // ks / ke (their pointers are not preloaded) are needed only for the validity of
+        // the scored columns; loaded after the first loads so no wait for them comes first
+        const int vrow = row + opaque_zero();
+        const int32_t ks_raw = (rows.ks ? rows.ks : rows.ke)[vrow];   // no load behind a branch
+        ri.ks = rows.ks ? ks_raw : 0;
+        ri.ke = rows.ke[vrow];
+    } else {
+        // the row's metadata and candidate ids, then the query: one round trip (a null
+        // ks or table pointer reads ke's slot, then the value is replaced)
+        const int vrow = row + opaque_zero();
+        const int32_t ks_raw = (rows.ks ? rows.ks : rows.ke)[vrow];
+        const int32_t ke_raw = rows.ke[vrow];
+        const int32_t tbl_raw = (rows.table ? rows.table : rows.ke)[vrow];
+        int craw[E];
+        if (tid < kWave) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int i = e * kWave + lane;
+                craw[e] = ex.cand[(int64_t)row * ex.cand_stride + min(i, ex.nb - 1)];
+                if (i >= ex.nb) craw[e] = -1;
+            }
+        }
+        load_q<QF>(f, qv, qs, weights, sf, row, lane);
+        ri.ks = rows.ks ? ks_raw : 0;
+        ri.ke = ke_raw;
+        if (tid < kWave) {
+            const int tbl = rows.table ? tbl_raw : row;
+            int ntok;
+            const int nlist = expand_row<E>(craw, ri.ks, ri.ke, tbl >= 0 && tbl < k.num_tables,
+                                            tbl, ex.cbs, sbk, nsb, k,
+                                            reinterpret_cast<int32_t *>(s_word), s_si, s_pg,
+                                            ntok);
+            if (lane == 0) {
+                L.kept = nlist;
+                if (ex.kept) {
+                    ex.end[row] = ntok;
+                    ex.kept[row] = nlist;
+                }
+            }
+        }
     }
-    // ks / ke (their pointers are not preloaded) are needed only for the validity of the
-    // scored columns; loaded after the first loads so no wait for them comes first
-    const int vrow = row + opaque_zero();
-    const int32_t ks_raw = (rows.ks ? rows.ks : rows.ke)[vrow];   // no load behind a branch
-    ri.ks = rows.ks ? ks_raw : 0;
-    ri.ke = rows.ke[vrow];
     if (tid == 0) s_unit = 0;
     select_clear(s_sel);
     __syncthreads();
+    if constexpr (E > 0) {
+        ri.kept = uniform(L.kept);
+        if (ex.kept)
+            for (int i = tid; i < nsb; i += NT) {
+                ex.si[(int64_t)row * nsb + i] = s_si[i];
+                ex.pg[(int64_t)row * nsb + i] = s_pg[i];
+            }
+    }
+    ri.valid_cols = ri.kept * sbk;
     // The selection's first digit is counted while scoring (the scoring waits on
     // memory, so the extra instructions are free): valid keys per key >> 23.
     int nv = 0;
@@ -277,6 +339,47 @@ __global__ __launch_bounds__(NT, WPE) void fused_layers_kernel(
                                    pg_base, ls.q_values[layer], ls.q_scales[layer],
                                    ls.weights[layer], p_kept, nsb, lsbk, rows, kl,
                                    ls.logits_out[layer], topk, ls.out[layer], ostride, sf);
+}
+
+// The one-row kernels with each row's candidate expansion inside (MXFP4 queries, 64-token
+// sparse blocks, up to 128 candidate blocks a row: two ids a lane): wave 0 expands the
+// row into LDS while the other waves load the query, and the workgroups of layer 0 also
+// write the schedule, so a later call can reuse it.  The expansion launch and the
+// schedule round trip between it and the scoring launch are gone; every workgroup of a
+// row (one a layer) expands it again, which costs a candidate load, a sort in registers
+// and a block-table load.  The leading scalar arguments are the candidate row's address
+// terms (kernarg preload).
+constexpr int kFusedExpandIds = 2;
+
+template <int NT, int KPT, int WPE>
+__global__ __launch_bounds__(NT, WPE) void expand_fused_row_kernel(
+    const int32_t *cand, int64_t cand_stride, const void *qv, const void *qs,
+    const void *weights, int32_t nb, int32_t cbs, int32_t nsb, int32_t lsbk, int32_t group_rows,
+    Rows rows, KCache k, Schedule s, float *logits_out, int32_t topk, int32_t *out,
+    int64_t ostride, int32_t sf) {
+    __shared__ FusedLds<NT> lds;
+    const FusedExpand ex = {cand, cand_stride, nb, cbs, s.sparse_indices, s.pages, s.end, s.kept};
+    fused_row<0, NT, KPT, 1, true, kFusedExpandIds>(
+        lds, xcd_grouped_row(blockIdx.x, group_rows), nullptr, nullptr, qv, qs, weights,
+        nullptr, nsb, lsbk, rows, k, logits_out, topk, out, ostride, sf, ex);
+}
+
+template <int KPT>
+__global__ __launch_bounds__(512, 4) void expand_fused_layers_kernel(
+    const int32_t *cand, int64_t cand_stride, int32_t nb, int32_t cbs, int32_t nsb,
+    int32_t lsbk, int32_t topk, int32_t group_rows, Rows rows, KCache k, LayerSet ls,
+    Schedule s, int64_t ostride, int32_t sf) {
+    __shared__ FusedLds<512> lds;
+    const int layer = blockIdx.y;
+    KCache kl = k;
+    kl.values = ls.k_values[layer];
+    kl.scales = ls.k_scales[layer];
+    const FusedExpand ex = {cand, cand_stride, nb, cbs, s.sparse_indices, s.pages, s.end,
+                            layer == 0 ? s.kept : nullptr};
+    fused_row<0, 512, KPT, 1, true, kFusedExpandIds>(
+        lds, xcd_grouped_row(blockIdx.x, group_rows), nullptr, nullptr, ls.q_values[layer],
+        ls.q_scales[layer], ls.weights[layer], nullptr, nsb, lsbk, rows, kl,
+        ls.logits_out[layer], topk, ls.out[layer], ostride, sf, ex);
 }
 
 }  // namespace
@@ -517,6 +620,66 @@ hipError_t launch_sparse_layers(int q_format, int score_format, const Rows &rows
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+bool expansion_fuses(int q_format, int32_t sbk, int32_t nb, int32_t ncols, int32_t num_rows,
+                     int32_t num_layers, int cus) {
+    const Plan plan = plan_sparse(q_format, sbk, ncols, num_rows, num_layers, cus, true);
+    // Only when every row-layer's workgroup is resident at once (at most two a CU): then
+    // the expansion overlaps the other workgroups' K streams and the expansion launch is
+    // saved (measured 6 % faster steps on the 64-row, 4-layer decode batch).  With more
+    // rounds each workgroup's expansion, repeated for every layer, delays its own K
+    // stream by what the expansion launch costs (256 rows, 4 layers, 8192 columns: steps
+    // within noise of the two launches, the scoring launch ~3 us longer).
+    return q_format == 0 && sbk == 64 && nb <= kFusedExpandIds * kWave &&
+           (int64_t)num_rows * num_layers <= 2 * (int64_t)cus &&
+           (plan == kPlanOneRow || plan == kPlanOneRowLayers);
+}
+
+hipError_t launch_expand_sparse_layers(int q_format, int score_format, const Rows &rows,
+                                       int32_t num_layers, const LayerSet &layers,
+                                       const KCache &k, const Schedule &s, const int32_t *cand,
+                                       int64_t cand_stride, int32_t nb, int32_t cbs,
+                                       float *workspace, size_t workspace_bytes, int32_t topk,
+                                       int64_t out_stride, const Timing &timing,
+                                       hipStream_t stream) {
+    if (rows.num_rows == 0 || num_layers == 0) return hipSuccess;
+    const int ncols = s.nsb * s.sbk;
+    const int sf = score_format;
+    const int cus = device_cus();
+    if (!expansion_fuses(q_format, s.sbk, nb, ncols, rows.num_rows, num_layers, cus)) {
+        const hipError_t e = launch_expand(rows, k, cand, cand_stride, nb, cbs, s, stream);
+        if (e != hipSuccess) return e;
+        return launch_sparse_layers(q_format, score_format, rows, num_layers, layers, k, s,
+                                    workspace, workspace_bytes, topk, out_stride, timing, stream);
+    }
+    if (num_layers == 1) {
+        // the launch shapes of launch_sparse_q's one-row MXFP4 plan
+#define IDX_LAUNCH_EXPAND_ROW(NT_, KPT_, WPE_)                                                    \
+    hipExtLaunchKernelGGL((expand_fused_row_kernel<NT_, KPT_, WPE_>), dim3(rows.num_rows),         \
+                          dim3(NT_), 0, stream, timing.start, timing.stop, 0, cand, cand_stride,   \
+                          layers.q_values[0], layers.q_scales[0], layers.weights[0], nb, cbs,      \
+                          s.nsb, s.lsbk, grouped_rows(rows), rows, k, s, layers.logits_out[0],     \
+                          topk, layers.out[0], out_stride, sf)
+        if (rows.num_rows < 2 * cus) {
+            if (ncols <= 1024 * 4) IDX_LAUNCH_EXPAND_ROW(1024, 4, 1);
+            else IDX_LAUNCH_EXPAND_ROW(1024, 8, 1);
+        } else if (ncols <= 512 * 4) IDX_LAUNCH_EXPAND_ROW(512, 4, 4);   // 2 x CUs rows
+        else if (ncols <= 512 * 8) IDX_LAUNCH_EXPAND_ROW(512, 8, 4);
+        else IDX_LAUNCH_EXPAND_ROW(512, 16, 4);
+#undef IDX_LAUNCH_EXPAND_ROW
+        return hipGetLastError();
+    }
+    const dim3 grid(rows.num_rows, num_layers);
+#define IDX_LAUNCH_EXPAND_LAYERS(KPT_)                                                            \
+    hipExtLaunchKernelGGL((expand_fused_layers_kernel<KPT_>), grid, dim3(512), 0, stream,          \
+                          timing.start, timing.stop, 0, cand, cand_stride, nb, cbs, s.nsb, s.lsbk,  \
+                          topk, grouped_rows(rows), rows, k, layers, s, out_stride, sf)
+    if (ncols <= 512 * 4) IDX_LAUNCH_EXPAND_LAYERS(4);
+    else if (ncols <= 512 * 8) IDX_LAUNCH_EXPAND_LAYERS(8);
+    else IDX_LAUNCH_EXPAND_LAYERS(16);
+#undef IDX_LAUNCH_EXPAND_LAYERS
+    return hipGetLastError();
 }
 
 }  // namespace idx

@@ -175,14 +175,16 @@ class GpuRun:
             None if with_logits else self.workspace,
             0 if with_logits else self.workspace.numel())
 
-    def score_layers(self, layers, with_logits, workspace_layers=1, out_pad=0):
+    def score_layers(self, layers, with_logits, workspace_layers=1, out_pad=0,
+                     expand_in_call=False):
         """One idx_sparse_mqa_logits_topk_layers call over the given layers; returns
         per-layer (indices, logits or None) device tensors.  with_logits[i] False: that
         layer writes no logits (the workspace serves it).  workspace_layers: the
         workspace holds that many layers' logits (all of them lets fewer rows than CUs
         run every layer in one split launch).  out_pad: each layer's indices are a view
         of a [rows][topk + out_pad] buffer filled with -7 (out_stride topk + out_pad),
-        whose extra columns padded_tail reads."""
+        whose extra columns padded_tail reads.  expand_in_call: one
+        idx_expand_and_score_layers call instead, which also builds the schedule."""
         import torch
 
         R, s = self.case.num_rows, self.spec
@@ -201,8 +203,14 @@ class GpuRun:
         if workspace_layers > 1:
             ws = torch.empty(self.idx.idx_workspace_bytes(self.cfg, R * workspace_layers, 0),
                              dtype=torch.uint8, device=dev)
-        self.idx.idx_sparse_mqa_logits_topk_layers(self.cfg, self.rows, self.sched.struct,
-                                                   entries, s.topk + out_pad, ws, ws.numel())
+        if expand_in_call:
+            cand = self.dcase.candidate_blocks
+            self.idx.idx_expand_and_score_layers(self.cfg, self.rows, cand, cand.stride(0),
+                                                 self.sched.struct, entries, s.topk + out_pad,
+                                                 ws, ws.numel())
+        else:
+            self.idx.idx_sparse_mqa_logits_topk_layers(self.cfg, self.rows, self.sched.struct,
+                                                       entries, s.topk + out_pad, ws, ws.numel())
         return outs, logs
 
 

@@ -306,6 +306,41 @@ def test_layers_call_rejects_bad_arguments():
     assert layers_call([layer(), layer(logits=None)], ws=FAKE, wsb=100) == idx.IDX_EWORKSPACE
 
 
+def expand_score_call(layers, cand=FAKE, stride=64, n=None, r=None, ws=None, wsb=0,
+                      ostride=2048, s=None):
+    c = idx.idx_check_config(cfg())
+    arr = (idx.idx_layer * max(1, len(layers)))(*layers)
+    return idx.lib.idx_expand_and_score_layers(
+        ctypes.byref(c), ctypes.byref(r or rows()), cand, stride, ctypes.byref(s or sched()),
+        len(layers) if n is None else n, arr, ostride, ws, wsb, None)
+
+
+def test_expand_and_score_rejects_what_either_call_rejects():
+    """idx_expand_and_score_layers applies the checks of idx_expand_candidates (candidate
+    ids, their stride, the schedule) and of idx_sparse_mqa_logits_topk_layers (layers,
+    outputs, one cache geometry, the workspace), on the host before any launch."""
+    two = [layer(), layer(kcache(values=FAKE + 0x10000, scales=FAKE + 0x11000))]
+    assert expand_score_call(two, r=rows(0)) == idx.IDX_OK        # zero rows: nothing launched
+    assert expand_score_call(two, r=rows(0), cand=None) == idx.IDX_OK
+    assert expand_score_call(two, cand=None) == idx.IDX_EINVAL
+    assert "candidate_blocks" in idx.idx_last_error()
+    assert expand_score_call(two, stride=10) == idx.IDX_EINVAL    # stride < NB
+    assert "cand_stride" in idx.idx_last_error()
+    assert expand_score_call(two, s=sched(sparse_indices=None)) == idx.IDX_EINVAL
+    assert expand_score_call(two, n=0) == idx.IDX_EINVAL
+    assert expand_score_call([layer()] * 9) == idx.IDX_EINVAL    # > IDX_MAX_LAYERS
+    assert expand_score_call(two, ostride=100) == idx.IDX_EINVAL
+    assert expand_score_call([layer(), layer(qv=FAKE + 4)]) == idx.IDX_EINVAL
+    assert "layer 1" in idx.idx_last_error()
+    assert expand_score_call([layer(), layer(k=kcache(num_pages=11))]) == idx.IDX_EINVAL
+    assert "geometry" in idx.idx_last_error()
+    assert expand_score_call([layer(), layer(logits=None)]) == idx.IDX_EWORKSPACE
+    c = idx.idx_check_config(cfg())
+    assert idx.lib.idx_expand_and_score_layers(
+        ctypes.byref(c), ctypes.byref(rows()), FAKE, 64, ctypes.byref(sched()), 2, None, 2048,
+        None, 0, None) == idx.IDX_EINVAL
+
+
 def test_gather_rejects_bad_arguments():
     c = idx.idx_check_config(cfg())
     def call(k=None, n=2, cu=FAKE, seq=100, tokens=500, vo=FAKE, so=FAKE):
@@ -453,11 +488,29 @@ def test_sparse_plan_rule_on_the_host():
                          idx.IDX_PLAN_ROW_GROUP_LAYERS)
         assert p["layers_per_scoring_launch"] == (0 if plan == idx.IDX_PLAN_NONE else
                                                   layers if multi else 1)
+        # idx_expand_and_score_layers expands inside the one-row kernels (MXFP4, sbk 64,
+        # NB <= 128) when they take every row-layer in one round (at most two a CU), else
+        # keeps the expansion launch and the same scoring kernel
+        inside = (plan in (idx.IDX_PLAN_ONE_ROW, idx.IDX_PLAN_ONE_ROW_LAYERS)
+                  and rows * layers <= 2 * cus)
+        assert p["expansion_in_scoring_kernel"] == inside, p
+        assert p["expand_and_score_kernel"] == (
+            "expand_" + kernel if inside else kernel), p
     # fp8 queries and 32-token sparse blocks never take row groups
     c8 = idx.make_config(q_format=idx.IDX_Q_FP8_E4M3_ROWSCALE)
     assert idx.idx_sparse_plan(c8, 4096)["plan"] == idx.IDX_PLAN_ONE_ROW
     c32 = idx.make_config(candidate_block_size=32, num_candidate_blocks=64)
     assert idx.idx_sparse_plan(c32, 4096)["plan"] == idx.IDX_PLAN_ONE_ROW
+    # ... nor expand inside the scoring kernel (64-token sparse blocks with at most 8192
+    # columns a row mean at most 128 candidate blocks: two ids a lane)
+    for cx in (c8, c32):
+        p = idx.idx_sparse_plan(cx, 200, 2)
+        assert p["plan"] == idx.IDX_PLAN_ONE_ROW_LAYERS and not p["expansion_in_scoring_kernel"]
+        assert p["expand_and_score_kernel"] == p["scoring_kernel"]
+    assert idx.idx_sparse_plan(c, 200, 2)["expansion_in_scoring_kernel"]
+    assert idx.idx_sparse_plan(c, 2 * cus, 1)["expand_and_score_kernel"] == "expand_fused_row_kernel"
+    assert not idx.idx_sparse_plan(c, 2 * cus + 1, 1)["expansion_in_scoring_kernel"]
+    assert not idx.idx_sparse_plan(c, cus, 3)["expansion_in_scoring_kernel"]
     for bad in [(c, -1, 1), (c, 4, 0), (c, 4, idx.IDX_MAX_LAYERS + 1)]:
         with pytest.raises(idx.IdxError):
             idx.idx_sparse_plan(*bad)
