@@ -284,11 +284,19 @@ int idx_sparse_plan(const idx_config *cfg, int32_t num_rows, int32_t num_layers,
     }
     if (p == idx::kPlanNone) info.layers_per_scoring_launch = 0;
     info.expand_and_score_kernel = info.scoring_kernel;
-    if (idx::expansion_fuses(cfg->q_format, sbk, cfg->num_candidate_blocks, ncols, num_rows,
-                             num_layers, idx::device_cus())) {
+    switch (idx::expansion_place(cfg->q_format, sbk, cfg->num_candidate_blocks, ncols, num_rows,
+                                 num_layers, idx::device_cus(), logits_home != 0)) {
+    case idx::kExpandLaunch: break;
+    case idx::kExpandOneRow:
         info.expansion_in_scoring_kernel = 1;
         info.expand_and_score_kernel =
             p == idx::kPlanOneRow ? "expand_fused_row_kernel" : "expand_fused_layers_kernel";
+        break;
+    case idx::kExpandSplit:
+        info.expansion_in_scoring_kernel = 1;
+        info.expand_and_score_kernel = p == idx::kPlanSplit ? "score_split_expand_kernel"
+                                                            : "score_split_expand_layers_kernel";
+        break;
     }
     *out = info;
     return ok();

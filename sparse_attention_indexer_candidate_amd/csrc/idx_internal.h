@@ -122,13 +122,19 @@ hipError_t launch_sparse_layers(int q_format, int score_format, const Rows &rows
                                 int32_t topk, int64_t out_stride, const Timing &timing,
                                 hipStream_t stream);
 
-// launch_expand then launch_sparse_layers, in one launch where the rows take the one-row
-// kernels (plan kPlanOneRow / kPlanOneRowLayers) in one round (rows x layers <= 2 x CUs)
-// with MXFP4 queries, sbk = 64 and nb <= 128 (expansion_fuses): each workgroup expands its
-// row in LDS and layer 0's workgroups write the schedule, the same values launch_expand
-// writes.  Otherwise the two launches.
-bool expansion_fuses(int q_format, int32_t sbk, int32_t nb, int32_t ncols, int32_t num_rows,
-                     int32_t num_layers, int cus);
+// launch_expand then launch_sparse_layers, with the expansion inside the scoring launch
+// where expansion_place says so (MXFP4 queries, nb <= 128): the one-row kernels in one
+// round (plan kPlanOneRow / kPlanOneRowLayers, rows x layers <= 2 x CUs, sbk = 64), or the
+// split scoring launch (plan kPlanSplit with one layer, kPlanSplitLayers).  Each workgroup
+// expands its row in LDS and one workgroup a row writes the schedule, the same values
+// launch_expand writes.  Otherwise the expansion launch, then launch_sparse_layers.
+enum ExpandPlace : int {
+    kExpandLaunch = 0,   // launch_expand, then the scoring launches
+    kExpandOneRow = 1,   // expand_fused_row_kernel / expand_fused_layers_kernel
+    kExpandSplit = 2,    // score_split_expand_kernel / score_split_expand_layers_kernel
+};
+ExpandPlace expansion_place(int q_format, int32_t sbk, int32_t nb, int32_t ncols,
+                            int32_t num_rows, int32_t num_layers, int cus, bool logits_home);
 hipError_t launch_expand_sparse_layers(int q_format, int score_format, const Rows &rows,
                                        int32_t num_layers, const LayerSet &layers,
                                        const KCache &k, const Schedule &s, const int32_t *cand,

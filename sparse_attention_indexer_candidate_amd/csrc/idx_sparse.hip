@@ -113,6 +113,123 @@ __global__ __launch_bounds__(kScoreThreads, (split_waves_per_simd<QF>())) void s
                                  layer_logits(ls, l, ws, ws_layer), sf);
 }
 
+// A row's candidate expansion inside a scoring kernel: the published candidate blocks,
+// and the schedule arrays that the workgroup writes when kept is set (one workgroup a
+// row), so the schedule is the expansion launch's.
+struct FusedExpand {
+    const int32_t *cand;
+    int64_t cand_stride;
+    int32_t nb;
+    int32_t cbs;
+    int32_t *si;
+    int32_t *pg;
+    int32_t *end;
+    int32_t *kept;   // null: this workgroup writes no schedule
+};
+
+// Candidate ids a lane of the expansions inside the scoring kernels: up to 128
+// candidate blocks a row.
+constexpr int kFusedExpandIds = 2;
+
+struct SplitExpandLds {
+    int32_t stage[kFusedExpandIds * kWave];
+    int32_t si[kMaxNSB];
+    int32_t pg[kMaxNSB];
+};
+
+// score_split_row with the row's expansion inside: wave 0 loads the row's metadata and
+// candidate ids and lists its kept sparse blocks and pages in LDS while the other waves
+// load the query; then the workgroup scores its chunk from the LDS schedule.  Every chunk
+// of a row expands the row again (a candidate load, a sort in registers and a block-table
+// load, all on-chip after the first); the workgroup with ex.kept set also writes the
+// row's schedule, which the selection launch reads.
+template <int QF, int PW, bool G64>
+__device__ __forceinline__ void score_split_row_expand(
+    SplitExpandLds &L, const FusedExpand &ex, const void *qv, const void *qs,
+    const void *weights, int32_t nsb, int32_t sbk, int32_t groups_per_wg, int32_t group_rows,
+    const Rows &rows, const KCache &k, float *logits, int sf) {
+    const int row = xcd_grouped_row(blockIdx.x, group_rows);
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wave = uniform(tid / kWave);
+    const int ncols = nsb * sbk;
+    const int ngroups = (ncols + 63) / 64;
+    const int g0 = min(blockIdx.y * groups_per_wg + wave * PW, ngroups);
+    const int g1 = min(g0 + PW, ngroups);
+    // the row's metadata and candidate ids, then the query: one round trip (a null ks or
+    // table pointer reads ke's slot, then the value is replaced)
+    const int32_t ks_raw = (rows.ks ? rows.ks : rows.ke)[row];
+    const int32_t ke_raw = rows.ke[row];
+    const int32_t tbl_raw = (rows.table ? rows.table : rows.ke)[row];
+    int craw[kFusedExpandIds];
+    if (wave == 0) {
+#pragma unroll
+        for (int e = 0; e < kFusedExpandIds; ++e) {
+            const int i = e * kWave + lane;
+            craw[e] = ex.cand[(int64_t)row * ex.cand_stride + min(i, ex.nb - 1)];
+            if (i >= ex.nb) craw[e] = -1;
+        }
+    }
+    QFrag<QF> f;
+    load_q<QF>(f, qv, qs, weights, sf, row, lane);
+    const int ks = rows.ks ? ks_raw : 0, ke = ke_raw;
+    if (wave == 0) {
+        const int tbl = rows.table ? tbl_raw : row;
+        int ntok;
+        const int nlist = expand_row<kFusedExpandIds>(craw, ks, ke, tbl >= 0 && tbl < k.num_tables,
+                                                      tbl, ex.cbs, sbk, nsb, k, L.stage, L.si,
+                                                      L.pg, ntok);
+        if (lane == 0 && ex.kept) {
+            ex.end[row] = ntok;
+            ex.kept[row] = nlist;
+        }
+    }
+    __syncthreads();
+    if (ex.kept)
+        for (int i = tid; i < nsb; i += kScoreThreads) {
+            ex.si[(int64_t)row * nsb + i] = L.si[i];
+            ex.pg[(int64_t)row * nsb + i] = L.pg[i];
+        }
+    float *lrow = logits + (int64_t)row * ncols;
+    score_groups<QF, PW, PW, G64>(k, f, ks, ke, g0, g1, sf, SparseDesc{L.si, L.pg, nsb, sbk},
+                             [&](int c, float v, bool ok) {
+                                 if (c < ncols) lrow[c] = ok ? v : -INFINITY;
+                             });
+}
+
+// The split scoring launches with the expansion inside (MXFP4 queries); chunk 0 of each
+// row (of layer 0) writes the schedule.  The leading scalar arguments are the candidate
+// row's address terms (kernarg preload).
+template <bool G64>
+__global__ __launch_bounds__(kScoreThreads) void score_split_expand_kernel(
+    const int32_t *cand, int64_t cand_stride, const void *qv, const void *qs,
+    const void *weights, int32_t nb, int32_t cbs, int32_t nsb, int32_t sbk,
+    int32_t groups_per_wg, int32_t group_rows, Rows rows, KCache k, Schedule s, float *logits,
+    int32_t sf) {
+    __shared__ SplitExpandLds lds;
+    const FusedExpand ex = {cand, cand_stride, nb, cbs, s.sparse_indices, s.pages, s.end,
+                            blockIdx.y == 0 ? s.kept : nullptr};
+    score_split_row_expand<0, kSplitGroupsPerWave, G64>(lds, ex, qv, qs, weights, nsb, sbk,
+                                                        groups_per_wg, group_rows, rows, k,
+                                                        logits, sf);
+}
+
+template <bool G64>
+__global__ __launch_bounds__(kScoreThreads) void score_split_expand_layers_kernel(
+    const int32_t *cand, int64_t cand_stride, int32_t nb, int32_t cbs, int32_t nsb,
+    int32_t sbk, int32_t groups_per_wg, int32_t group_rows, Rows rows, KCache k, LayerSet ls,
+    Schedule s, float *ws, int64_t ws_layer, int32_t sf) {
+    __shared__ SplitExpandLds lds;
+    const int l = blockIdx.z;
+    KCache kl = k;
+    kl.values = ls.k_values[l];
+    kl.scales = ls.k_scales[l];
+    const FusedExpand ex = {cand, cand_stride, nb, cbs, s.sparse_indices, s.pages, s.end,
+                            blockIdx.y == 0 && l == 0 ? s.kept : nullptr};
+    score_split_row_expand<0, kSplitGroupsPerWave, G64>(
+        lds, ex, ls.q_values[l], ls.q_scales[l], ls.weights[l], nsb, sbk, groups_per_wg,
+        group_rows, rows, kl, layer_logits(ls, l, ws, ws_layer), sf);
+}
+
 // The selection of a multi-layer split launch: grid.y = layer.
 template <int KPT>
 __global__ __launch_bounds__(kTopkThreads) void topk_split_layers_kernel(
@@ -138,20 +255,6 @@ struct FusedLds {
     int unit;
     int kept;                                 // the row's kept count when expanded here
     SelectLds<NT, 5> sel;
-};
-
-// A row's candidate expansion inside the one-row kernels (fused_row with E > 0): the
-// published candidate blocks, and the schedule arrays that the workgroup writes when
-// kept is set (layer 0's workgroups), so the schedule is the expansion launch's.
-struct FusedExpand {
-    const int32_t *cand;
-    int64_t cand_stride;
-    int32_t nb;
-    int32_t cbs;
-    int32_t *si;
-    int32_t *pg;
-    int32_t *end;
-    int32_t *kept;   // null: this workgroup writes no schedule
 };
 
 // U: 64-column groups a wave takes per unit (two units in flight).  E = 0: the row's
@@ -349,7 +452,6 @@ __global__ __launch_bounds__(NT, WPE) void fused_layers_kernel(
 // row (one a layer) expands it again, which costs a candidate load, a sort in registers
 // and a block-table load.  The leading scalar arguments are the candidate row's address
 // terms (kernarg preload).
-constexpr int kFusedExpandIds = 2;
 
 template <int NT, int KPT, int WPE>
 __global__ __launch_bounds__(NT, WPE) void expand_fused_row_kernel(
@@ -622,18 +724,86 @@ hipError_t launch_sparse_layers(int q_format, int score_format, const Rows &rows
     return hipSuccess;
 }
 
-bool expansion_fuses(int q_format, int32_t sbk, int32_t nb, int32_t ncols, int32_t num_rows,
-                     int32_t num_layers, int cus) {
-    const Plan plan = plan_sparse(q_format, sbk, ncols, num_rows, num_layers, cus, true);
-    // Only when every row-layer's workgroup is resident at once (at most two a CU): then
-    // the expansion overlaps the other workgroups' K streams and the expansion launch is
-    // saved (measured 6 % faster steps on the 64-row, 4-layer decode batch).  With more
-    // rounds each workgroup's expansion, repeated for every layer, delays its own K
-    // stream by what the expansion launch costs (256 rows, 4 layers, 8192 columns: steps
-    // within noise of the two launches, the scoring launch ~3 us longer).
-    return q_format == 0 && sbk == 64 && nb <= kFusedExpandIds * kWave &&
-           (int64_t)num_rows * num_layers <= 2 * (int64_t)cus &&
-           (plan == kPlanOneRow || plan == kPlanOneRowLayers);
+ExpandPlace expansion_place(int q_format, int32_t sbk, int32_t nb, int32_t ncols,
+                            int32_t num_rows, int32_t num_layers, int cus, bool logits_home) {
+    const Plan plan = plan_sparse(q_format, sbk, ncols, num_rows, num_layers, cus, logits_home);
+    if (q_format != 0 || nb > kFusedExpandIds * kWave) return kExpandLaunch;
+    // One-row kernels: only when every row-layer's workgroup is resident at once (at most
+    // two a CU): then the expansion overlaps the other workgroups' K streams and the
+    // expansion launch is saved (measured 6 % faster steps on the 64-row, 4-layer decode
+    // batch).  With more rounds each workgroup's expansion, repeated for every layer,
+    // delays its own K stream by what the expansion launch costs (256 rows, 4 layers, 8192
+    // columns: steps within noise of the two launches, the scoring launch ~3 us longer).
+    if (sbk == 64 && (int64_t)num_rows * num_layers <= 2 * (int64_t)cus &&
+        (plan == kPlanOneRow || plan == kPlanOneRowLayers))
+        return kExpandOneRow;
+    // Split launches (fewer rows, or row-layers, than CUs: one round of short workgroups,
+    // bound by latency): the expansion launch and its schedule round trip are saved
+    if ((plan == kPlanSplit && num_layers == 1) || plan == kPlanSplitLayers) return kExpandSplit;
+    return kExpandLaunch;
+}
+
+// The split pair with the expansion inside the scoring launch (one layer, or every layer
+// in one launch pair): the selection launch as in launch_sparse_q / launch_split_layers.
+static hipError_t launch_split_expand(const Rows &rows, int32_t num_layers,
+                                      const LayerSet &layers, int sf, const KCache &k,
+                                      const Schedule &s, const int32_t *cand,
+                                      int64_t cand_stride, int32_t nb, int32_t cbs,
+                                      float *workspace, int32_t topk, int64_t out_stride,
+                                      const Timing &timing, hipStream_t stream) {
+    const int ncols = s.nsb * s.sbk;
+    const int ngroups = (ncols + 63) / 64;
+    const int gpw = kSplitGroupsPerWg;
+    hipError_t e;
+    if (num_layers == 1) {
+        float *logits = layers.logits_out[0] ? layers.logits_out[0] : workspace;
+        const dim3 sgrid(rows.num_rows, (ngroups + gpw - 1) / gpw);
+#define IDX_LAUNCH_SPLIT_EXPAND_G(G64_)                                                            \
+    hipExtLaunchKernelGGL((score_split_expand_kernel<G64_>), sgrid, dim3(kScoreThreads), 0,        \
+                          stream, timing.start, timing.stop, 0, cand, cand_stride,                 \
+                          layers.q_values[0], layers.q_scales[0], layers.weights[0], nb, cbs,      \
+                          s.nsb, s.sbk, gpw, grouped_rows(rows), rows, k, s, logits, sf)
+        if (s.sbk == 64)
+            IDX_LAUNCH_SPLIT_EXPAND_G(true);
+        else
+            IDX_LAUNCH_SPLIT_EXPAND_G(false);
+#undef IDX_LAUNCH_SPLIT_EXPAND_G
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (ncols <= 8 * kTopkThreads)
+            hipLaunchKernelGGL((topk_split_kernel<false, 8>), dim3(rows.num_rows),
+                               dim3(kTopkThreads), 0, stream, logits, s.sparse_indices, rows.ks,
+                               rows.ke, s.kept, s.nsb, s.lsbk, (int64_t)0, 0, topk,
+                               layers.out[0], out_stride);
+        else
+            hipLaunchKernelGGL((topk_split_kernel<false, 16>), dim3(rows.num_rows),
+                               dim3(kTopkThreads), 0, stream, logits, s.sparse_indices, rows.ks,
+                               rows.ke, s.kept, s.nsb, s.lsbk, (int64_t)0, 0, topk,
+                               layers.out[0], out_stride);
+        return hipGetLastError();
+    }
+    const int64_t ws_layer = (int64_t)rows.num_rows * ncols;
+    const dim3 sgrid(rows.num_rows, (ngroups + gpw - 1) / gpw, num_layers);
+#define IDX_LAUNCH_SPLIT_EXPAND_LAYERS_G(G64_)                                                     \
+    hipExtLaunchKernelGGL((score_split_expand_layers_kernel<G64_>), sgrid, dim3(kScoreThreads), 0, \
+                          stream, timing.start, timing.stop, 0, cand, cand_stride, nb, cbs, s.nsb, \
+                          s.sbk, gpw, grouped_rows(rows), rows, k, layers, s, workspace, ws_layer, \
+                          sf)
+    if (s.sbk == 64)
+        IDX_LAUNCH_SPLIT_EXPAND_LAYERS_G(true);
+    else
+        IDX_LAUNCH_SPLIT_EXPAND_LAYERS_G(false);
+#undef IDX_LAUNCH_SPLIT_EXPAND_LAYERS_G
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const dim3 tgrid(rows.num_rows, num_layers);
+    if (ncols <= 8 * kTopkThreads)
+        hipLaunchKernelGGL((topk_split_layers_kernel<8>), tgrid, dim3(kTopkThreads), 0, stream,
+                           s.sparse_indices, rows.ks, rows.ke, s.kept, s.nsb, s.lsbk, topk, layers,
+                           workspace, ws_layer, out_stride);
+    else
+        hipLaunchKernelGGL((topk_split_layers_kernel<16>), tgrid, dim3(kTopkThreads), 0, stream,
+                           s.sparse_indices, rows.ks, rows.ke, s.kept, s.nsb, s.lsbk, topk, layers,
+                           workspace, ws_layer, out_stride);
+    return hipGetLastError();
 }
 
 hipError_t launch_expand_sparse_layers(int q_format, int score_format, const Rows &rows,
@@ -647,12 +817,22 @@ hipError_t launch_expand_sparse_layers(int q_format, int score_format, const Row
     const int ncols = s.nsb * s.sbk;
     const int sf = score_format;
     const int cus = device_cus();
-    if (!expansion_fuses(q_format, s.sbk, nb, ncols, rows.num_rows, num_layers, cus)) {
+    // as launch_sparse_layers: every layer's logits need a home for the batched split pair
+    bool all_out = true;
+    for (int l = 0; l < num_layers; ++l) all_out = all_out && layers.logits_out[l];
+    const size_t need = (size_t)num_layers * rows.num_rows * ncols * sizeof(float);
+    const bool home = all_out || (workspace && workspace_bytes >= need);
+    const ExpandPlace place = expansion_place(q_format, s.sbk, nb, ncols, rows.num_rows,
+                                              num_layers, cus, home);
+    if (place == kExpandLaunch) {
         const hipError_t e = launch_expand(rows, k, cand, cand_stride, nb, cbs, s, stream);
         if (e != hipSuccess) return e;
         return launch_sparse_layers(q_format, score_format, rows, num_layers, layers, k, s,
                                     workspace, workspace_bytes, topk, out_stride, timing, stream);
     }
+    if (place == kExpandSplit)
+        return launch_split_expand(rows, num_layers, layers, sf, k, s, cand, cand_stride, nb, cbs,
+                                   workspace, topk, out_stride, timing, stream);
     if (num_layers == 1) {
         // the launch shapes of launch_sparse_q's one-row MXFP4 plan
 #define IDX_LAUNCH_EXPAND_ROW(NT_, KPT_, WPE_)                                                    \

@@ -489,13 +489,17 @@ def test_sparse_plan_rule_on_the_host():
         assert p["layers_per_scoring_launch"] == (0 if plan == idx.IDX_PLAN_NONE else
                                                   layers if multi else 1)
         # idx_expand_and_score_layers expands inside the one-row kernels (MXFP4, sbk 64,
-        # NB <= 128) when they take every row-layer in one round (at most two a CU), else
-        # keeps the expansion launch and the same scoring kernel
-        inside = (plan in (idx.IDX_PLAN_ONE_ROW, idx.IDX_PLAN_ONE_ROW_LAYERS)
-                  and rows * layers <= 2 * cus)
-        assert p["expansion_in_scoring_kernel"] == inside, p
-        assert p["expand_and_score_kernel"] == (
-            "expand_" + kernel if inside else kernel), p
+        # NB <= 128) when they take every row-layer in one round (at most two a CU), and
+        # inside the split scoring launch (one layer, or all layers in one launch pair);
+        # else it keeps the expansion launch and the same scoring kernel
+        if plan in (idx.IDX_PLAN_ONE_ROW, idx.IDX_PLAN_ONE_ROW_LAYERS) and rows * layers <= 2 * cus:
+            want_kernel = "expand_" + kernel
+        elif (plan == idx.IDX_PLAN_SPLIT and layers == 1) or plan == idx.IDX_PLAN_SPLIT_LAYERS:
+            want_kernel = kernel.replace("score_split_", "score_split_expand_")
+        else:
+            want_kernel = kernel
+        assert p["expand_and_score_kernel"] == want_kernel, p
+        assert p["expansion_in_scoring_kernel"] == (want_kernel != kernel), p
     # fp8 queries and 32-token sparse blocks never take row groups
     c8 = idx.make_config(q_format=idx.IDX_Q_FP8_E4M3_ROWSCALE)
     assert idx.idx_sparse_plan(c8, 4096)["plan"] == idx.IDX_PLAN_ONE_ROW

@@ -26,34 +26,49 @@ def _spec(name, rows, nb, layers, cbs=64, page=64, topk=300, cand="messy", ks="r
                   cand_rule=cand, fill="all", q_formats=("mxfp4", "fp8"))
 
 
-# name -> (spec, expansion inside the scoring kernel with MXFP4 queries on a 256-CU device)
+# name -> (spec, the kernel that streams K in the one call with MXFP4 queries on a 256-CU
+# device, workspace for every layer's logits)
 CASES = {
     # one layer, fewer than two rows a CU: 1024-thread rows (4 and 8 keys a thread)
-    "row_1024_k4": (_spec("es1", 260, 48, 1), True),
-    "row_1024_k8": (_spec("es2", 300, 128, 1, topk=2048, cand="distinct", ks="zero"), True),
+    "row_1024_k4": (_spec("es1", 260, 48, 1), "expand_fused_row_kernel", False),
+    "row_1024_k8": (_spec("es2", 300, 128, 1, topk=2048, cand="distinct", ks="zero"),
+                    "expand_fused_row_kernel", False),
     # one layer, two rows a CU: 512-thread rows, two a CU (4, 8, 16 keys a thread)
-    "row_512_k4": (_spec("es3", 512, 24, 1), True),
-    "row_512_k8": (_spec("es4", 512, 64, 1, topk=1000), True),
-    "row_512_k16": (_spec("es5", 512, 128, 1, topk=2048), True),
+    "row_512_k4": (_spec("es3", 512, 24, 1), "expand_fused_row_kernel", False),
+    "row_512_k8": (_spec("es4", 512, 64, 1, topk=1000), "expand_fused_row_kernel", False),
+    "row_512_k16": (_spec("es5", 512, 128, 1, topk=2048), "expand_fused_row_kernel", False),
     # several layers, one launch, at most two row-layers a CU: >= CUs rows, or fewer rows
     # but >= CUs row-layers
-    "layers_rows": (_spec("es6", 170, 24, 3), True),
-    "layers_row_layers": (_spec("es7", 40, 16, 8), True),
-    "layers_k8": (_spec("es8", 130, 64, 2, topk=2048), True),
-    "layers_k16": (_spec("es9", 256, 128, 2, topk=2048, cand="distinct"), True),
-    # more than two rows, or row-layers, a CU: the two launches
-    "two_launches_rows": (_spec("es14", 600, 24, 1), False),
-    "two_launches_row_layers": (_spec("es15", 300, 24, 3), False),
-    # the two launches: 32- and 16-token sparse blocks, fewer
-    # row-layers than CUs (split), a prefill chunk's row groups
-    "two_launches_nb": (_spec("es10", 260, 160, 2, cbs=32, page=64, topk=1000), False),
-    "two_launches_sbk16": (_spec("es11", 260, 40, 2, cbs=16, page=32), False),
-    "two_launches_split": (_spec("es12", 40, 30, 2), False),
+    "layers_rows": (_spec("es6", 170, 24, 3), "expand_fused_layers_kernel", False),
+    "layers_row_layers": (_spec("es7", 40, 16, 8), "expand_fused_layers_kernel", False),
+    "layers_k8": (_spec("es8", 130, 64, 2, topk=2048), "expand_fused_layers_kernel", False),
+    "layers_k16": (_spec("es9", 256, 128, 2, topk=2048, cand="distinct"),
+                   "expand_fused_layers_kernel", False),
+    # fewer rows (or row-layers) than CUs: the split scoring launch expands (64-, 32- and
+    # 16-token sparse blocks), one layer or every layer in one launch pair
+    "split_one_layer": (_spec("es16", 64, 64, 1, topk=1000), "score_split_expand_kernel", False),
+    "split_one_layer_sbk32": (_spec("es17", 100, 100, 1, cbs=32, page=64),
+                              "score_split_expand_kernel", False),
+    "split_one_layer_sbk16": (_spec("es19", 30, 120, 1, cbs=16, page=32),
+                              "score_split_expand_kernel", False),
+    "split_layers": (_spec("es12", 40, 30, 2), "score_split_expand_layers_kernel", True),
+    "split_layers_wide": (_spec("es22", 24, 128, 2, topk=7000, cand="distinct"),
+                          "score_split_expand_layers_kernel", True),
+    # the two launches: more than two row-layers a CU, more than 128 candidate blocks,
+    # 16-token sparse blocks in the one-row kernels, split layers without a home for every
+    # layer's logits (layer by layer), a prefill chunk's row groups
+    "two_launches_rows": (_spec("es14", 600, 24, 1), "fused_row_kernel", False),
+    "two_launches_row_layers": (_spec("es15", 300, 24, 3), "fused_layers_kernel", False),
+    "two_launches_nb": (_spec("es10", 200, 160, 2, cbs=32, page=64, topk=1000),
+                        "fused_layers_kernel", False),
+    "two_launches_sbk16": (_spec("es11", 200, 40, 2, cbs=16, page=32), "fused_layers_kernel",
+                           False),
+    "two_launches_split_no_home": (_spec("es18", 40, 30, 2), "score_split_kernel", False),
     "two_launches_groups": (W.Spec(name="es13", num_rows=2050, page_size=128, cbs=64, nb=8,
                                    topk=100, layers=2, mode="prefill", ke_rule="uniform",
                                    ke_lo=1, ke_hi=1500, ks_rule="random", context=1600,
-                                   cand_rule="messy", fill="all",
-                                   q_formats=("mxfp4", "fp8")), False),
+                                   cand_rule="messy", fill="all", q_formats=("mxfp4", "fp8")),
+                            "row_group_layers_kernel", False),
 }
 
 
@@ -69,23 +84,31 @@ def _poison(g):
     g.sched.work.fill_(0xAB)
 
 
-def _check(case, tag, q_format, expect_fused=None):
+def _check(case, tag, q_format, kernel=None, ws_all=False):
+    """kernel: the kernel the one call's plan must name with MXFP4 queries on 256 CUs (fp8
+    queries: no expansion inside).  ws_all: a workspace for every layer's logits."""
     import sparse_attention_indexer_candidate_amd as idx
 
     nl = case.spec.layers
     g = GpuRun(case, to_device(case, DEV), q_format=q_format)
-    plan = idx.idx_sparse_plan(g.cfg, case.num_rows, nl, logits_home=True)
-    if expect_fused is not None and torch.cuda.get_device_properties(0).multi_processor_count == 256:
-        assert plan["expansion_in_scoring_kernel"] == (expect_fused and q_format == "mxfp4"), plan
     with_logits = [i % 2 == 0 for i in range(nl)]
+    home = all(with_logits) or ws_all
+    plan = idx.idx_sparse_plan(g.cfg, case.num_rows, nl, logits_home=home)
+    if kernel is not None and torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        if q_format == "mxfp4":
+            assert plan["expand_and_score_kernel"] == kernel, plan
+        else:
+            assert not plan["expansion_in_scoring_kernel"], plan
+    wsl = nl if ws_all else 1
     _say(f"[{tag}] two calls ({plan['scoring_kernel']})")
     _poison(g)
     g.expand()
-    ref_out, ref_log = g.score_layers(range(nl), with_logits)
+    ref_out, ref_log = g.score_layers(range(nl), with_logits, workspace_layers=wsl)
     ref_sched = _schedule(g)
     _say(f"[{tag}] one call ({plan['expand_and_score_kernel']})")
     _poison(g)
-    outs, logs = g.score_layers(range(nl), with_logits, out_pad=3, expand_in_call=True)
+    outs, logs = g.score_layers(range(nl), with_logits, workspace_layers=wsl, out_pad=3,
+                                expand_in_call=True)
     sched = _schedule(g)
     for a, b, what in zip(sched, ref_sched, ("sparse_indices", "end", "work")):
         np.testing.assert_array_equal(a, b, err_msg=f"{tag}: schedule {what}")
@@ -103,9 +126,9 @@ def _check(case, tag, q_format, expect_fused=None):
 @pytest.mark.parametrize("q_format", ["mxfp4", "fp8"])
 @pytest.mark.parametrize("name", sorted(CASES))
 def test_expand_and_score_matches_two_calls(name, q_format):
-    spec, fused = CASES[name]
+    spec, kernel, ws_all = CASES[name]
     case = W.generate(spec, seed=31)
-    g, outs, logs = _check(case, f"es-{name}-{q_format}", q_format, fused)
+    g, outs, logs = _check(case, f"es-{name}-{q_format}", q_format, kernel, ws_all)
     if q_format != "mxfp4":
         return
     # layer 0 against the oracle, from the one call's own schedule and outputs
@@ -116,16 +139,18 @@ def test_expand_and_score_matches_two_calls(name, q_format):
     compare_rows(case, res, ora, case.spec.topk, g.sbk, f"es-{name} layer 0")
 
 
-@pytest.mark.parametrize("layers", [1, 2])
-def test_expand_and_score_drops_pages_outside_the_pool(layers):
+@pytest.mark.parametrize("rows,layers,kernel", [
+    (256, 1, "expand_fused_row_kernel"), (256, 2, "expand_fused_layers_kernel"),
+    (64, 1, "score_split_expand_kernel")])
+def test_expand_and_score_drops_pages_outside_the_pool(rows, layers, kernel):
     """Table entries outside the pool and table rows outside the tables, expanded inside the
     scoring kernel: the schedule leaves them out as the expansion launch does, and layer 0
     equals the oracle on the clean tables with those blocks removed."""
-    spec = dataclasses.replace(_spec("es20", 256, 32, layers), fill="candidates")
+    spec = dataclasses.replace(_spec("es20", rows, 32, layers), fill="candidates")
     case = W.generate(spec, seed=22)
     bad, clean, bad_rows, _ = corrupt_tables(case, seed=6)
-    tag = f"es-drop-l{layers}"
-    g, outs, logs = _check(bad, tag, "mxfp4", True)
+    tag = f"es-drop-r{rows}-l{layers}"
+    g, outs, logs = _check(bad, tag, "mxfp4", kernel)
     si_o, end_o = oracle.expand(clean, g.sbk)
     res = g.fetch()
     np.testing.assert_array_equal(res["sparse_indices"], si_o, err_msg=f"{tag}: schedule")
@@ -137,11 +162,13 @@ def test_expand_and_score_drops_pages_outside_the_pool(layers):
     compare_rows(clean, res, ora, spec.topk, g.sbk, tag)
 
 
-def test_expand_and_score_empty_rows_and_short_candidate_lists():
+@pytest.mark.parametrize("rows,kernel", [(250, "expand_fused_layers_kernel"),
+                                         (60, "score_split_expand_layers_kernel")])
+def test_expand_and_score_empty_rows_and_short_candidate_lists(rows, kernel):
     """Rows with no candidate at all, or only negative ids, and NB below the two ids a lane
     of the in-kernel expansion (one id a lane)."""
-    spec = _spec("es21", 250, 5, 2, topk=200)
+    spec = _spec("es21", rows, 5, 2, topk=200)
     case = W.generate(spec, seed=23)
     case.candidate_blocks[::7] = -1
     case.candidate_blocks[3::11, :2] = -5
-    _check(case, "es-empty", "mxfp4", True)
+    _check(case, f"es-empty-r{rows}", "mxfp4", kernel, ws_all=True)
