@@ -54,6 +54,8 @@ CASES = {
     "split_layers": (_spec("es12", 40, 30, 2), "score_split_expand_layers_kernel", True),
     "split_layers_wide": (_spec("es22", 24, 128, 2, topk=7000, cand="distinct"),
                           "score_split_expand_layers_kernel", True),
+    "split_layers_sbk32": (_spec("es23", 40, 60, 3, cbs=32, page=64),
+                           "score_split_expand_layers_kernel", True),
     # the two launches: more than two row-layers a CU, more than 128 candidate blocks,
     # 16-token sparse blocks in the one-row kernels, split layers without a home for every
     # layer's logits (layer by layer), a prefill chunk's row groups
