@@ -13,6 +13,10 @@
 //                       global scratch, selection in a second launch (and the
 //                       multi-layer pair, grid.z / grid.y = layer)
 //  row groups           >= 8 rows a CU with MXFP4 queries: idx_row_groups.hip
+//
+// and, for the call that also expands the candidates (launch_expand_sparse_layers), the
+// same scoring with each row's expansion inside: expand_fused_row_kernel,
+// expand_fused_layers_kernel, score_split_expand_kernel, score_split_expand_layers_kernel.
 
 #include "idx_device.h"
 
@@ -452,7 +456,6 @@ __global__ __launch_bounds__(NT, WPE) void fused_layers_kernel(
 // row (one a layer) expands it again, which costs a candidate load, a sort in registers
 // and a block-table load.  The leading scalar arguments are the candidate row's address
 // terms (kernarg preload).
-
 template <int NT, int KPT, int WPE>
 __global__ __launch_bounds__(NT, WPE) void expand_fused_row_kernel(
     const int32_t *cand, int64_t cand_stride, const void *qv, const void *qs,
@@ -730,8 +733,8 @@ ExpandPlace expansion_place(int q_format, int32_t sbk, int32_t nb, int32_t ncols
     if (q_format != 0 || nb > kFusedExpandIds * kWave) return kExpandLaunch;
     // One-row kernels: only when every row-layer's workgroup is resident at once (at most
     // two a CU): then the expansion overlaps the other workgroups' K streams and the
-    // expansion launch is saved (measured 6 % faster steps on the 64-row, 4-layer decode
-    // batch).  With more rounds each workgroup's expansion, repeated for every layer,
+    // expansion launch is saved (measured 4-6 % faster steps on the 64-row, 4-layer decode
+    // batch, 10 % on 256 rows of one layer).  With more rounds each workgroup's expansion, repeated for every layer,
     // delays its own K stream by what the expansion launch costs (256 rows, 4 layers, 8192
     // columns: steps within noise of the two launches, the scoring launch ~3 us longer).
     if (sbk == 64 && (int64_t)num_rows * num_layers <= 2 * (int64_t)cus &&
@@ -739,6 +742,7 @@ ExpandPlace expansion_place(int q_format, int32_t sbk, int32_t nb, int32_t ncols
         return kExpandOneRow;
     // Split launches (fewer rows, or row-layers, than CUs: one round of short workgroups,
     // bound by latency): the expansion launch and its schedule round trip are saved
+    // (measured 7-11 % faster steps on 64- and 128-row decode batches)
     if ((plan == kPlanSplit && num_layers == 1) || plan == kPlanSplitLayers) return kExpandSplit;
     return kExpandLaunch;
 }
