@@ -173,8 +173,11 @@ __device__ __forceinline__ void score_split_row_expand(
             if (i >= ex.nb) craw[e] = -1;
         }
     }
+    // MXFP4 queries load while wave 0 expands; fp8 queries (bf16 fragments, held to 168
+    // VGPRs) load after it, so their registers are not live across the sort (they still
+    // fly with the first K loads)
     QFrag<QF> f;
-    load_q<QF>(f, qv, qs, weights, sf, row, lane);
+    if constexpr (QF == 0) load_q<QF>(f, qv, qs, weights, sf, row, lane);
     const int ks = rows.ks ? ks_raw : 0, ke = ke_raw;
     if (wave == 0) {
         const int tbl = rows.table ? tbl_raw : row;
@@ -188,6 +191,7 @@ __device__ __forceinline__ void score_split_row_expand(
         }
     }
     __syncthreads();
+    if constexpr (QF == 1) load_q<QF>(f, qv, qs, weights, sf, row, lane);
     if (ex.kept)
         for (int i = tid; i < nsb; i += kScoreThreads) {
             ex.si[(int64_t)row * nsb + i] = L.si[i];
@@ -200,11 +204,12 @@ __device__ __forceinline__ void score_split_row_expand(
                              });
 }
 
-// The split scoring launches with the expansion inside (MXFP4 queries); chunk 0 of each
-// row (of layer 0) writes the schedule.  The leading scalar arguments are the candidate
-// row's address terms (kernarg preload).
-template <bool G64>
-__global__ __launch_bounds__(kScoreThreads) void score_split_expand_kernel(
+// The split scoring launches with the expansion inside (both query formats, fp8 held to
+// the same 168 VGPRs as score_split_kernel); chunk 0 of each row (of layer 0) writes the
+// schedule.  The leading scalar arguments are the candidate row's address terms (kernarg
+// preload).
+template <int QF, bool G64>
+__global__ __launch_bounds__(kScoreThreads, (split_waves_per_simd<QF>())) void score_split_expand_kernel(
     const int32_t *cand, int64_t cand_stride, const void *qv, const void *qs,
     const void *weights, int32_t nb, int32_t cbs, int32_t nsb, int32_t sbk,
     int32_t groups_per_wg, int32_t group_rows, Rows rows, KCache k, Schedule s, float *logits,
@@ -212,13 +217,13 @@ __global__ __launch_bounds__(kScoreThreads) void score_split_expand_kernel(
     __shared__ SplitExpandLds lds;
     const FusedExpand ex = {cand, cand_stride, nb, cbs, s.sparse_indices, s.pages, s.end,
                             blockIdx.y == 0 ? s.kept : nullptr};
-    score_split_row_expand<0, kSplitGroupsPerWave, G64>(lds, ex, qv, qs, weights, nsb, sbk,
-                                                        groups_per_wg, group_rows, rows, k,
-                                                        logits, sf);
+    score_split_row_expand<QF, kSplitGroupsPerWave, G64>(lds, ex, qv, qs, weights, nsb, sbk,
+                                                         groups_per_wg, group_rows, rows, k,
+                                                         logits, sf);
 }
 
-template <bool G64>
-__global__ __launch_bounds__(kScoreThreads) void score_split_expand_layers_kernel(
+template <int QF, bool G64>
+__global__ __launch_bounds__(kScoreThreads, (split_waves_per_simd<QF>())) void score_split_expand_layers_kernel(
     const int32_t *cand, int64_t cand_stride, int32_t nb, int32_t cbs, int32_t nsb,
     int32_t sbk, int32_t groups_per_wg, int32_t group_rows, Rows rows, KCache k, LayerSet ls,
     Schedule s, float *ws, int64_t ws_layer, int32_t sf) {
@@ -229,7 +234,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_split_expand_layers_kerne
     kl.scales = ls.k_scales[l];
     const FusedExpand ex = {cand, cand_stride, nb, cbs, s.sparse_indices, s.pages, s.end,
                             blockIdx.y == 0 && l == 0 ? s.kept : nullptr};
-    score_split_row_expand<0, kSplitGroupsPerWave, G64>(
+    score_split_row_expand<QF, kSplitGroupsPerWave, G64>(
         lds, ex, ls.q_values[l], ls.q_scales[l], ls.weights[l], nsb, sbk, groups_per_wg,
         group_rows, rows, kl, layer_logits(ls, l, ws, ws_layer), sf);
 }
@@ -730,25 +735,34 @@ hipError_t launch_sparse_layers(int q_format, int score_format, const Rows &rows
 ExpandPlace expansion_place(int q_format, int32_t sbk, int32_t nb, int32_t ncols,
                             int32_t num_rows, int32_t num_layers, int cus, bool logits_home) {
     const Plan plan = plan_sparse(q_format, sbk, ncols, num_rows, num_layers, cus, logits_home);
-    if (q_format != 0 || nb > kFusedExpandIds * kWave) return kExpandLaunch;
+    if (nb > kFusedExpandIds * kWave) return kExpandLaunch;
     // One-row kernels: only when every row-layer's workgroup is resident at once (at most
     // two a CU): then the expansion overlaps the other workgroups' K streams and the
     // expansion launch is saved (measured 4-6 % faster steps on the 64-row, 4-layer decode
     // batch, 10 % on 256 rows of one layer).  With more rounds each workgroup's expansion, repeated for every layer,
     // delays its own K stream by what the expansion launch costs (256 rows, 4 layers, 8192
     // columns: steps within noise of the two launches, the scoring launch ~3 us longer).
-    if (sbk == 64 && (int64_t)num_rows * num_layers <= 2 * (int64_t)cus &&
+    if (q_format == 0 && sbk == 64 && (int64_t)num_rows * num_layers <= 2 * (int64_t)cus &&
         (plan == kPlanOneRow || plan == kPlanOneRowLayers))
         return kExpandOneRow;
-    // Split launches (fewer rows, or row-layers, than CUs: one round of short workgroups,
-    // bound by latency): the expansion launch and its schedule round trip are saved
-    // (measured 7-11 % faster steps on 64- and 128-row decode batches)
-    if ((plan == kPlanSplit && num_layers == 1) || plan == kPlanSplitLayers) return kExpandSplit;
+    // Split launches (fewer rows, or row-layers, than CUs; short workgroups bound by
+    // latency) whose workgroups are all resident at once (MXFP4: 80 VGPRs, six a CU; fp8:
+    // 168, three a CU): the expansion launch and its schedule round trip are saved
+    // (measured 7-11 % faster steps on 64- and 128-row decode batches).  A second round
+    // waits on its own expansions (fp8 on 128 rows, 1024 workgroups: 1.6 % slower steps).
+    // fp8 queries only with 64-token sparse blocks: the generic tile path does not fit
+    // their 168 VGPRs with the expansion's state.
+    const int64_t wgs = (int64_t)num_rows * num_layers *
+                        ((((ncols + 63) / 64) + kSplitGroupsPerWg - 1) / kSplitGroupsPerWg);
+    if ((q_format == 0 || sbk == 64) && wgs <= (q_format == 0 ? 6 : 3) * (int64_t)cus &&
+        ((plan == kPlanSplit && num_layers == 1) || plan == kPlanSplitLayers))
+        return kExpandSplit;
     return kExpandLaunch;
 }
 
 // The split pair with the expansion inside the scoring launch (one layer, or every layer
 // in one launch pair): the selection launch as in launch_sparse_q / launch_split_layers.
+template <int QF>
 static hipError_t launch_split_expand(const Rows &rows, int32_t num_layers,
                                       const LayerSet &layers, int sf, const KCache &k,
                                       const Schedule &s, const int32_t *cand,
@@ -763,14 +777,16 @@ static hipError_t launch_split_expand(const Rows &rows, int32_t num_layers,
         float *logits = layers.logits_out[0] ? layers.logits_out[0] : workspace;
         const dim3 sgrid(rows.num_rows, (ngroups + gpw - 1) / gpw);
 #define IDX_LAUNCH_SPLIT_EXPAND_G(G64_)                                                            \
-    hipExtLaunchKernelGGL((score_split_expand_kernel<G64_>), sgrid, dim3(kScoreThreads), 0,        \
+    hipExtLaunchKernelGGL((score_split_expand_kernel<QF, G64_>), sgrid, dim3(kScoreThreads), 0,    \
                           stream, timing.start, timing.stop, 0, cand, cand_stride,                 \
                           layers.q_values[0], layers.q_scales[0], layers.weights[0], nb, cbs,      \
                           s.nsb, s.sbk, gpw, grouped_rows(rows), rows, k, s, logits, sf)
         if (s.sbk == 64)
             IDX_LAUNCH_SPLIT_EXPAND_G(true);
-        else
+        else if constexpr (QF == 0)
             IDX_LAUNCH_SPLIT_EXPAND_G(false);
+        else
+            return hipErrorInvalidValue;   // fp8 with sbk < 64: not placed here
 #undef IDX_LAUNCH_SPLIT_EXPAND_G
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (ncols <= 8 * kTopkThreads)
@@ -788,14 +804,17 @@ static hipError_t launch_split_expand(const Rows &rows, int32_t num_layers,
     const int64_t ws_layer = (int64_t)rows.num_rows * ncols;
     const dim3 sgrid(rows.num_rows, (ngroups + gpw - 1) / gpw, num_layers);
 #define IDX_LAUNCH_SPLIT_EXPAND_LAYERS_G(G64_)                                                     \
-    hipExtLaunchKernelGGL((score_split_expand_layers_kernel<G64_>), sgrid, dim3(kScoreThreads), 0, \
+    hipExtLaunchKernelGGL((score_split_expand_layers_kernel<QF, G64_>), sgrid,                     \
+                          dim3(kScoreThreads), 0,                                                  \
                           stream, timing.start, timing.stop, 0, cand, cand_stride, nb, cbs, s.nsb, \
                           s.sbk, gpw, grouped_rows(rows), rows, k, layers, s, workspace, ws_layer, \
                           sf)
     if (s.sbk == 64)
         IDX_LAUNCH_SPLIT_EXPAND_LAYERS_G(true);
-    else
+    else if constexpr (QF == 0)
         IDX_LAUNCH_SPLIT_EXPAND_LAYERS_G(false);
+    else
+        return hipErrorInvalidValue;   // fp8 with sbk < 64: not placed here
 #undef IDX_LAUNCH_SPLIT_EXPAND_LAYERS_G
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const dim3 tgrid(rows.num_rows, num_layers);
@@ -834,9 +853,13 @@ hipError_t launch_expand_sparse_layers(int q_format, int score_format, const Row
         return launch_sparse_layers(q_format, score_format, rows, num_layers, layers, k, s,
                                     workspace, workspace_bytes, topk, out_stride, timing, stream);
     }
-    if (place == kExpandSplit)
-        return launch_split_expand(rows, num_layers, layers, sf, k, s, cand, cand_stride, nb, cbs,
-                                   workspace, topk, out_stride, timing, stream);
+    if (place == kExpandSplit) {
+        if (q_format == 0)
+            return launch_split_expand<0>(rows, num_layers, layers, sf, k, s, cand, cand_stride,
+                                          nb, cbs, workspace, topk, out_stride, timing, stream);
+        return launch_split_expand<1>(rows, num_layers, layers, sf, k, s, cand, cand_stride, nb,
+                                      cbs, workspace, topk, out_stride, timing, stream);
+    }
     if (num_layers == 1) {
         // the launch shapes of launch_sparse_q's one-row MXFP4 plan
 #define IDX_LAUNCH_EXPAND_ROW(NT_, KPT_, WPE_)                                                    \

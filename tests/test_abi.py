@@ -494,7 +494,8 @@ def test_sparse_plan_rule_on_the_host():
         # else it keeps the expansion launch and the same scoring kernel
         if plan in (idx.IDX_PLAN_ONE_ROW, idx.IDX_PLAN_ONE_ROW_LAYERS) and rows * layers <= 2 * cus:
             want_kernel = "expand_" + kernel
-        elif (plan == idx.IDX_PLAN_SPLIT and layers == 1) or plan == idx.IDX_PLAN_SPLIT_LAYERS:
+        elif ((plan == idx.IDX_PLAN_SPLIT and layers == 1) or plan == idx.IDX_PLAN_SPLIT_LAYERS) \
+                and rows * layers * 8 <= 6 * cus:   # 4096 columns: 8 workgroups a row
             want_kernel = kernel.replace("score_split_", "score_split_expand_")
         else:
             want_kernel = kernel
@@ -512,6 +513,16 @@ def test_sparse_plan_rule_on_the_host():
         assert p["plan"] == idx.IDX_PLAN_ONE_ROW_LAYERS and not p["expansion_in_scoring_kernel"]
         assert p["expand_and_score_kernel"] == p["scoring_kernel"]
     assert idx.idx_sparse_plan(c, 200, 2)["expansion_in_scoring_kernel"]
+    # fp8 queries: inside the split launches with 64-token sparse blocks only
+    assert idx.idx_sparse_plan(c8, 64, 1)["expand_and_score_kernel"] == "score_split_expand_kernel"
+    c8_32 = idx.make_config(q_format=idx.IDX_Q_FP8_E4M3_ROWSCALE, candidate_block_size=32)
+    assert not idx.idx_sparse_plan(c8_32, 64, 1)["expansion_in_scoring_kernel"]
+    # ... and only when every split workgroup is resident at once (three a CU for fp8, six
+    # for MXFP4; 4096 columns are 8 workgroups a row)
+    assert idx.idx_sparse_plan(c8, 96, 1)["expansion_in_scoring_kernel"]
+    assert not idx.idx_sparse_plan(c8, 97, 1)["expansion_in_scoring_kernel"]
+    assert idx.idx_sparse_plan(c, 192, 1)["expansion_in_scoring_kernel"]
+    assert not idx.idx_sparse_plan(c, 193, 1)["expansion_in_scoring_kernel"]
     assert idx.idx_sparse_plan(c, 2 * cus, 1)["expand_and_score_kernel"] == "expand_fused_row_kernel"
     assert not idx.idx_sparse_plan(c, 2 * cus + 1, 1)["expansion_in_scoring_kernel"]
     assert not idx.idx_sparse_plan(c, cus, 3)["expansion_in_scoring_kernel"]

@@ -66,6 +66,9 @@ CASES = {
     "two_launches_sbk16": (_spec("es11", 200, 40, 2, cbs=16, page=32), "fused_layers_kernel",
                            False),
     "two_launches_split_no_home": (_spec("es18", 40, 30, 2), "score_split_kernel", False),
+    # more split workgroups than are resident at once (200 rows x 16 of 512 columns)
+    "two_launches_split_rounds": (_spec("es24", 200, 128, 1, topk=2048, cand="distinct"),
+                                  "score_split_kernel", False),
     "two_launches_groups": (W.Spec(name="es13", num_rows=2050, page_size=128, cbs=64, nb=8,
                                    topk=100, layers=2, mode="prefill", ke_rule="uniform",
                                    ke_lo=1, ke_hi=1500, ks_rule="random", context=1600,
@@ -88,7 +91,8 @@ def _poison(g):
 
 def _check(case, tag, q_format, kernel=None, ws_all=False):
     """kernel: the kernel the one call's plan must name with MXFP4 queries on 256 CUs (fp8
-    queries: no expansion inside).  ws_all: a workspace for every layer's logits."""
+    queries: the same split kernels with 64-token sparse blocks, else no expansion inside).
+    ws_all: a workspace for every layer's logits."""
     import sparse_attention_indexer_candidate_amd as idx
 
     nl = case.spec.layers
@@ -97,10 +101,10 @@ def _check(case, tag, q_format, kernel=None, ws_all=False):
     home = all(with_logits) or ws_all
     plan = idx.idx_sparse_plan(g.cfg, case.num_rows, nl, logits_home=home)
     if kernel is not None and torch.cuda.get_device_properties(0).multi_processor_count == 256:
-        if q_format == "mxfp4":
-            assert plan["expand_and_score_kernel"] == kernel, plan
-        else:
-            assert not plan["expansion_in_scoring_kernel"], plan
+        # fp8 queries expand inside the split launches with 64-token sparse blocks only
+        fp8_inside = kernel.startswith("score_split_expand") and g.sbk == 64
+        want = kernel if q_format == "mxfp4" or fp8_inside else plan["scoring_kernel"]
+        assert plan["expand_and_score_kernel"] == want, plan
     wsl = nl if ws_all else 1
     _say(f"[{tag}] two calls ({plan['scoring_kernel']})")
     _poison(g)
