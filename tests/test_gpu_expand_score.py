@@ -56,6 +56,14 @@ CASES = {
                           "score_split_expand_layers_kernel", True),
     "split_layers_sbk32": (_spec("es23", 40, 60, 3, cbs=32, page=64),
                            "score_split_expand_layers_kernel", True),
+    # two rows a request (rows_per_request 2: a request's rows placed on one XCD), in the
+    # split launch and in the one-row kernel
+    "split_rows_per_request": (W.config(6, name="es25", fill="all",
+                                        q_formats=("mxfp4", "fp8")),
+                               "score_split_expand_kernel", False),
+    "row_rows_per_request": (W.config(6, name="es26", num_rows=512, ke_lo=2000, ke_hi=6000,
+                                      fill="all", q_formats=("mxfp4", "fp8")),
+                             "expand_fused_row_kernel", False),
     # the two launches: more than two row-layers a CU, more than 128 candidate blocks,
     # 16-token sparse blocks in the one-row kernels, split layers without a home for every
     # layer's logits (layer by layer), a prefill chunk's row groups
@@ -101,8 +109,11 @@ def _check(case, tag, q_format, kernel=None, ws_all=False):
     home = all(with_logits) or ws_all
     plan = idx.idx_sparse_plan(g.cfg, case.num_rows, nl, logits_home=home)
     if kernel is not None and torch.cuda.get_device_properties(0).multi_processor_count == 256:
-        # fp8 queries expand inside the split launches with 64-token sparse blocks only
-        fp8_inside = kernel.startswith("score_split_expand") and g.sbk == 64
+        # fp8 queries expand inside the split launches with 64-token sparse blocks only,
+        # when their workgroups (8 groups of 64 columns each) fit three a CU
+        ngroups = -(-case.spec.nb * case.spec.cbs // 64)
+        wgs = case.num_rows * nl * -(-ngroups // 8)
+        fp8_inside = kernel.startswith("score_split_expand") and g.sbk == 64 and wgs <= 3 * 256
         want = kernel if q_format == "mxfp4" or fp8_inside else plan["scoring_kernel"]
         assert plan["expand_and_score_kernel"] == want, plan
     wsl = nl if ws_all else 1
