@@ -312,10 +312,11 @@ def test_invariances_page_permutation_scale_and_weights():
 
 @pytest.mark.parametrize("which", ["decode_batch", "rows_per_cu"])
 def test_step_graph_replays_match_eager(which):
-    """A step (expansion, sparse scoring and the dense comparator) captured as one HIP
-    graph on its own stream and replayed several times, with eager steps of other
-    inputs on the same stream between the replays: every replay gives the eager
-    result, bit for bit (the library records no memset and allocates nothing)."""
+    """A step (expansion, sparse scoring, the dense comparator, and the expansion and
+    scoring in one call) captured as one HIP graph on its own stream and replayed several
+    times, with eager steps of other inputs on the same stream between the replays: every
+    replay gives the eager result, bit for bit (the library records no memset and
+    allocates nothing)."""
     import sparse_attention_indexer_candidate_amd as idx
 
     spec = W.config(2) if which == "decode_batch" else WEIGHT_PATHS["fused"]
@@ -336,6 +337,7 @@ def test_step_graph_replays_match_eager(which):
             sched = idx.Schedule(cfg, R, DEV)
             out = torch.full((R, s.topk), -7, dtype=torch.int32, device=DEV)
             dout = torch.full((R, s.topk), -7, dtype=torch.int32, device=DEV)
+            out1 = torch.full((R, s.topk), -7, dtype=torch.int32, device=DEV)
             ws = torch.empty(idx.idx_workspace_bytes(cfg, R, ctx), dtype=torch.uint8, device=DEV)
             qv, qs = d.layers[0].q("mxfp4")
             calls = [idx.bind_expand_candidates(cfg, rows, kc, d.candidate_blocks,
@@ -347,8 +349,13 @@ def test_step_graph_replays_match_eager(which):
                      idx.bind_dense_masked_logits_topk(cfg, rows, ctx, qv, qs,
                                                        d.layers[0].weights, kc, sched.struct, dout,
                                                        dout.stride(0), None, 0, ws, ws.numel(),
-                                                       stream=sh)]
-            runs.append(dict(keep=(d, rows, kc, sched, ws), calls=calls, out=out, dout=dout))
+                                                       stream=sh),
+                     idx.bind_expand_and_score_layers(
+                         cfg, rows, d.candidate_blocks, d.candidate_blocks.stride(0),
+                         sched.struct, [(qv, qs, d.layers[0].weights, kc, out1, None)],
+                         out1.stride(0), ws, ws.numel(), stream=sh)]
+            runs.append(dict(keep=(d, rows, kc, sched, ws), calls=calls, out=out, dout=dout,
+                             out1=out1))
         for r in runs:                                   # eager results
             for c in r["calls"]:
                 c()
@@ -356,6 +363,8 @@ def test_step_graph_replays_match_eager(which):
         for r in runs:
             r["ref"], r["dref"] = r["out"].clone(), r["dout"].clone()
         np.testing.assert_array_equal(runs[0]["ref"].cpu().numpy(), runs[0]["dref"].cpu().numpy())
+        for r in runs:
+            assert torch.equal(r["out1"], r["ref"]), "one call != expansion + scoring calls"
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             for c in runs[0]["calls"]:
@@ -364,6 +373,7 @@ def test_step_graph_replays_match_eager(which):
         for rep in range(3):
             runs[0]["out"].fill_(-7)
             runs[0]["dout"].fill_(-7)
+            runs[0]["out1"].fill_(-7)
             other["out"].fill_(-7)
             for c in other["calls"]:                     # eager work between replays
                 c()
@@ -372,6 +382,7 @@ def test_step_graph_replays_match_eager(which):
             _say(f"[graph {which}] replay {rep}")
             assert torch.equal(runs[0]["out"], runs[0]["ref"]), f"replay {rep}: sparse indices"
             assert torch.equal(runs[0]["dout"], runs[0]["dref"]), f"replay {rep}: dense indices"
+            assert torch.equal(runs[0]["out1"], runs[0]["ref"]), f"replay {rep}: one call"
             assert torch.equal(other["out"], other["ref"]), f"replay {rep}: eager step"
 
 
