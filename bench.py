@@ -4,9 +4,9 @@ One step = the whole hot path over one batch: the candidate expansion (the share
 sparse-column schedule) and the consuming layers (paged gather, MX-scaled MFMA, ReLU +
 fp32 head reduce, per-row top-k) in one idx_expand_and_score_layers call for a step's
 layers (--separate-expansion: idx_expand_candidates, then one
-idx_sparse_mqa_logits_topk_layers call).  The default workload is the largest one that fits one GPU,
-the long-context decode batch (256 rows, contexts 32k-128k, 128 candidate blocks of
-64 tokens, top-2048, 4 consuming layers sharing one schedule).  Inputs are seeded and
+idx_sparse_mqa_logits_topk_layers call).  The default workload is the largest one that
+fits one GPU, the long-context decode batch (256 rows, contexts 32k-128k, 128 candidate
+blocks of 64 tokens, top-2048, 4 consuming layers sharing one schedule).  Inputs are seeded and
 synthetic and already resident in HBM when the timed region starts; the step rotates
 through enough copies of them (distinct device buffers) that no step finds its K
 pages in the 256 MB Infinity Cache.
