@@ -97,14 +97,21 @@ def _poison(g):
     g.sched.work.fill_(0xAB)
 
 
-def _check(case, tag, q_format, kernel=None, ws_all=False):
+def _check(case, tag, q_format, kernel=None, ws_all=False, cand_pad=0):
     """kernel: the kernel the one call's plan must name with MXFP4 queries on 256 CUs (fp8
     queries: the same split kernels with 64-token sparse blocks, else no expansion inside).
-    ws_all: a workspace for every layer's logits."""
+    ws_all: a workspace for every layer's logits.  cand_pad: candidate rows that many ids
+    wider than NB (a strided view), the padding holding valid-looking ids."""
     import sparse_attention_indexer_candidate_amd as idx
 
     nl = case.spec.layers
     g = GpuRun(case, to_device(case, DEV), q_format=q_format)
+    if cand_pad:
+        nb = case.spec.nb
+        padded = torch.arange(case.num_rows * (nb + cand_pad), dtype=torch.int32,
+                              device=DEV).reshape(case.num_rows, nb + cand_pad) % 7
+        padded[:, :nb] = g.dcase.candidate_blocks
+        g.dcase.candidate_blocks = padded[:, :nb]
     with_logits = [i % 2 == 0 for i in range(nl)]
     home = all(with_logits) or ws_all
     plan = idx.idx_sparse_plan(g.cfg, case.num_rows, nl, logits_home=home)
@@ -189,3 +196,12 @@ def test_expand_and_score_empty_rows_and_short_candidate_lists(rows, kernel):
     case.candidate_blocks[::7] = -1
     case.candidate_blocks[3::11, :2] = -5
     _check(case, f"es-empty-r{rows}", "mxfp4", kernel, ws_all=True)
+
+
+@pytest.mark.parametrize("rows,layers,kernel", [(64, 1, "score_split_expand_kernel"),
+                                                (256, 2, "expand_fused_layers_kernel")])
+def test_expand_and_score_wide_candidate_stride(rows, layers, kernel):
+    """Candidate rows wider than NB (stride NB + 5) whose padding holds valid-looking ids:
+    the one call reads the first NB ids of each row, as the expansion launch does."""
+    case = W.generate(_spec("es31", rows, 40, layers), seed=24)
+    _check(case, f"es-stride-r{rows}-l{layers}", "mxfp4", kernel, cand_pad=5)
