@@ -123,8 +123,9 @@ hipError_t launch_sparse_layers(int q_format, int score_format, const Rows &rows
                                 hipStream_t stream);
 
 // launch_expand then launch_sparse_layers, with the expansion inside the scoring launch
-// where expansion_place says so (nb <= 128): the one-row kernels in one round (MXFP4
-// queries, plan kPlanOneRow / kPlanOneRowLayers, rows x layers <= 2 x CUs, sbk = 64), or
+// where expansion_place says so (nb <= 128): the one-row kernels in one round (plan
+// kPlanOneRow / kPlanOneRowLayers, sbk = 64, rows x layers <= 2 x CUs for MXFP4 queries,
+// < 2 x CUs for fp8: their 8-wave shapes), or
 // the split scoring launch in one round (plan kPlanSplit with one layer, kPlanSplitLayers;
 // fp8 queries only with sbk = 64).  Each workgroup
 // expands its row in LDS and one workgroup a row writes the schedule, the same values

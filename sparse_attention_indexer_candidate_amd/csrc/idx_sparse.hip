@@ -321,7 +321,9 @@ __device__ __forceinline__ void fused_row(
                 if (i >= ex.nb) craw[e] = -1;
             }
         }
-        load_q<QF>(f, qv, qs, weights, sf, row, lane);
+        // fp8 queries (bf16 fragments) load after the expansion, so their registers are not
+        // live across its sort
+        if constexpr (QF == 0) load_q<QF>(f, qv, qs, weights, sf, row, lane);
         ri.ks = rows.ks ? ks_raw : 0;
         ri.ke = ke_raw;
         if (tid < kWave) {
@@ -344,6 +346,7 @@ __device__ __forceinline__ void fused_row(
     select_clear(s_sel);
     __syncthreads();
     if constexpr (E > 0) {
+        if constexpr (QF == 1) load_q<QF>(f, qv, qs, weights, sf, row, lane);
         ri.kept = uniform(L.kept);
         if (ex.kept)
             for (int i = tid; i < nsb; i += NT) {
@@ -453,15 +456,15 @@ __global__ __launch_bounds__(NT, WPE) void fused_layers_kernel(
                                    ls.logits_out[layer], topk, ls.out[layer], ostride, sf);
 }
 
-// The one-row kernels with each row's candidate expansion inside (MXFP4 queries, 64-token
-// sparse blocks, up to 128 candidate blocks a row: two ids a lane): wave 0 expands the
-// row into LDS while the other waves load the query, and the workgroups of layer 0 also
+// The one-row kernels with each row's candidate expansion inside (64-token sparse blocks,
+// up to 128 candidate blocks a row: two ids a lane; MXFP4 queries, or fp8 in the 8-wave
+// shapes): wave 0 expands the row into LDS while the other waves load an MXFP4 query, and the workgroups of layer 0 also
 // write the schedule, so a later call can reuse it.  The expansion launch and the
 // schedule round trip between it and the scoring launch are gone; every workgroup of a
 // row (one a layer) expands it again, which costs a candidate load, a sort in registers
 // and a block-table load.  The leading scalar arguments are the candidate row's address
 // terms (kernarg preload).
-template <int NT, int KPT, int WPE>
+template <int QF, int NT, int KPT, int U, int WPE>
 __global__ __launch_bounds__(NT, WPE) void expand_fused_row_kernel(
     const int32_t *cand, int64_t cand_stride, const void *qv, const void *qs,
     const void *weights, int32_t nb, int32_t cbs, int32_t nsb, int32_t lsbk, int32_t group_rows,
@@ -469,13 +472,13 @@ __global__ __launch_bounds__(NT, WPE) void expand_fused_row_kernel(
     int64_t ostride, int32_t sf) {
     __shared__ FusedLds<NT> lds;
     const FusedExpand ex = {cand, cand_stride, nb, cbs, s.sparse_indices, s.pages, s.end, s.kept};
-    fused_row<0, NT, KPT, 1, true, kFusedExpandIds>(
+    fused_row<QF, NT, KPT, U, true, kFusedExpandIds>(
         lds, xcd_grouped_row(blockIdx.x, group_rows), nullptr, nullptr, qv, qs, weights,
         nullptr, nsb, lsbk, rows, k, logits_out, topk, out, ostride, sf, ex);
 }
 
-template <int KPT>
-__global__ __launch_bounds__(512, 4) void expand_fused_layers_kernel(
+template <int QF, int KPT, int U, int WPE>
+__global__ __launch_bounds__(512, WPE) void expand_fused_layers_kernel(
     const int32_t *cand, int64_t cand_stride, int32_t nb, int32_t cbs, int32_t nsb,
     int32_t lsbk, int32_t topk, int32_t group_rows, Rows rows, KCache k, LayerSet ls,
     Schedule s, int64_t ostride, int32_t sf) {
@@ -486,7 +489,7 @@ __global__ __launch_bounds__(512, 4) void expand_fused_layers_kernel(
     kl.scales = ls.k_scales[layer];
     const FusedExpand ex = {cand, cand_stride, nb, cbs, s.sparse_indices, s.pages, s.end,
                             layer == 0 ? s.kept : nullptr};
-    fused_row<0, 512, KPT, 1, true, kFusedExpandIds>(
+    fused_row<QF, 512, KPT, U, true, kFusedExpandIds>(
         lds, xcd_grouped_row(blockIdx.x, group_rows), nullptr, nullptr, ls.q_values[layer],
         ls.q_scales[layer], ls.weights[layer], nullptr, nsb, lsbk, rows, kl,
         ls.logits_out[layer], topk, ls.out[layer], ostride, sf, ex);
@@ -742,8 +745,11 @@ ExpandPlace expansion_place(int q_format, int32_t sbk, int32_t nb, int32_t ncols
     // batch, 10 % on 256 rows of one layer).  With more rounds each workgroup's expansion, repeated for every layer,
     // delays its own K stream by what the expansion launch costs (256 rows, 4 layers, 8192
     // columns: steps within noise of the two launches, the scoring launch ~3 us longer).
-    if (q_format == 0 && sbk == 64 && (int64_t)num_rows * num_layers <= 2 * (int64_t)cus &&
-        (plan == kPlanOneRow || plan == kPlanOneRowLayers))
+    // fp8 queries: the 8-wave one-row shapes only (fewer than 2 x CUs row-layers; at 2 x CUs
+    // their launches take 4-wave rows)
+    const int64_t row_layers = (int64_t)num_rows * num_layers;
+    if (sbk == 64 && (plan == kPlanOneRow || plan == kPlanOneRowLayers) &&
+        (q_format == 0 ? row_layers <= 2 * (int64_t)cus : row_layers < 2 * (int64_t)cus))
         return kExpandOneRow;
     // Split launches (fewer rows, or row-layers, than CUs; short workgroups bound by
     // latency) whose workgroups are all resident at once (MXFP4: 80 VGPRs, six a CU; fp8:
@@ -861,30 +867,38 @@ hipError_t launch_expand_sparse_layers(int q_format, int score_format, const Row
                                       cbs, workspace, topk, out_stride, timing, stream);
     }
     if (num_layers == 1) {
-        // the launch shapes of launch_sparse_q's one-row MXFP4 plan
-#define IDX_LAUNCH_EXPAND_ROW(NT_, KPT_, WPE_)                                                    \
-    hipExtLaunchKernelGGL((expand_fused_row_kernel<NT_, KPT_, WPE_>), dim3(rows.num_rows),         \
+        // the launch shapes of launch_sparse_q's one-row plan
+#define IDX_LAUNCH_EXPAND_ROW(QF_, NT_, KPT_, U_, WPE_)                                           \
+    hipExtLaunchKernelGGL((expand_fused_row_kernel<QF_, NT_, KPT_, U_, WPE_>), dim3(rows.num_rows), \
                           dim3(NT_), 0, stream, timing.start, timing.stop, 0, cand, cand_stride,   \
                           layers.q_values[0], layers.q_scales[0], layers.weights[0], nb, cbs,      \
                           s.nsb, s.lsbk, grouped_rows(rows), rows, k, s, layers.logits_out[0],     \
                           topk, layers.out[0], out_stride, sf)
-        if (rows.num_rows < 2 * cus) {
-            if (ncols <= 1024 * 4) IDX_LAUNCH_EXPAND_ROW(1024, 4, 1);
-            else IDX_LAUNCH_EXPAND_ROW(1024, 8, 1);
-        } else if (ncols <= 512 * 4) IDX_LAUNCH_EXPAND_ROW(512, 4, 4);   // 2 x CUs rows
-        else if (ncols <= 512 * 8) IDX_LAUNCH_EXPAND_ROW(512, 8, 4);
-        else IDX_LAUNCH_EXPAND_ROW(512, 16, 4);
+        if (q_format == 1) {   // fewer than 2 x CUs rows (expansion_place): 8-wave rows
+            if (ncols <= 512 * 4) IDX_LAUNCH_EXPAND_ROW(1, 512, 4, 2, 1);
+            else if (ncols <= 512 * 8) IDX_LAUNCH_EXPAND_ROW(1, 512, 8, 2, 1);
+            else IDX_LAUNCH_EXPAND_ROW(1, 512, 16, 2, 1);
+        } else if (rows.num_rows < 2 * cus) {
+            if (ncols <= 1024 * 4) IDX_LAUNCH_EXPAND_ROW(0, 1024, 4, 1, 1);
+            else IDX_LAUNCH_EXPAND_ROW(0, 1024, 8, 1, 1);
+        } else if (ncols <= 512 * 4) IDX_LAUNCH_EXPAND_ROW(0, 512, 4, 1, 4);   // 2 x CUs rows
+        else if (ncols <= 512 * 8) IDX_LAUNCH_EXPAND_ROW(0, 512, 8, 1, 4);
+        else IDX_LAUNCH_EXPAND_ROW(0, 512, 16, 1, 4);
 #undef IDX_LAUNCH_EXPAND_ROW
         return hipGetLastError();
     }
     const dim3 grid(rows.num_rows, num_layers);
-#define IDX_LAUNCH_EXPAND_LAYERS(KPT_)                                                            \
-    hipExtLaunchKernelGGL((expand_fused_layers_kernel<KPT_>), grid, dim3(512), 0, stream,          \
-                          timing.start, timing.stop, 0, cand, cand_stride, nb, cbs, s.nsb, s.lsbk,  \
-                          topk, grouped_rows(rows), rows, k, layers, s, out_stride, sf)
-    if (ncols <= 512 * 4) IDX_LAUNCH_EXPAND_LAYERS(4);
-    else if (ncols <= 512 * 8) IDX_LAUNCH_EXPAND_LAYERS(8);
-    else IDX_LAUNCH_EXPAND_LAYERS(16);
+#define IDX_LAUNCH_EXPAND_LAYERS(QF_, KPT_, U_, WPE_)                                             \
+    hipExtLaunchKernelGGL((expand_fused_layers_kernel<QF_, KPT_, U_, WPE_>), grid, dim3(512), 0,   \
+                          stream, timing.start, timing.stop, 0, cand, cand_stride, nb, cbs, s.nsb,  \
+                          s.lsbk, topk, grouped_rows(rows), rows, k, layers, s, out_stride, sf)
+    if (q_format == 1) {   // fewer than 2 x CUs row-layers (expansion_place): 8-wave rows
+        if (ncols <= 512 * 4) IDX_LAUNCH_EXPAND_LAYERS(1, 4, 2, 1);
+        else if (ncols <= 512 * 8) IDX_LAUNCH_EXPAND_LAYERS(1, 8, 2, 1);
+        else IDX_LAUNCH_EXPAND_LAYERS(1, 16, 2, 1);
+    } else if (ncols <= 512 * 4) IDX_LAUNCH_EXPAND_LAYERS(0, 4, 1, 4);
+    else if (ncols <= 512 * 8) IDX_LAUNCH_EXPAND_LAYERS(0, 8, 1, 4);
+    else IDX_LAUNCH_EXPAND_LAYERS(0, 16, 1, 4);
 #undef IDX_LAUNCH_EXPAND_LAYERS
     return hipGetLastError();
 }

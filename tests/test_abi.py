@@ -508,10 +508,14 @@ def test_sparse_plan_rule_on_the_host():
     assert idx.idx_sparse_plan(c32, 4096)["plan"] == idx.IDX_PLAN_ONE_ROW
     # ... nor expand inside the scoring kernel (64-token sparse blocks with at most 8192
     # columns a row mean at most 128 candidate blocks: two ids a lane)
-    for cx in (c8, c32):
-        p = idx.idx_sparse_plan(cx, 200, 2)
-        assert p["plan"] == idx.IDX_PLAN_ONE_ROW_LAYERS and not p["expansion_in_scoring_kernel"]
-        assert p["expand_and_score_kernel"] == p["scoring_kernel"]
+    p = idx.idx_sparse_plan(c32, 200, 2)
+    assert p["plan"] == idx.IDX_PLAN_ONE_ROW_LAYERS and not p["expansion_in_scoring_kernel"]
+    assert p["expand_and_score_kernel"] == p["scoring_kernel"]
+    # fp8 queries: inside the 8-wave one-row shapes (fewer than two row-layers a CU)
+    assert idx.idx_sparse_plan(c8, 200, 2)["expand_and_score_kernel"] == "expand_fused_layers_kernel"
+    assert idx.idx_sparse_plan(c8, 300, 1)["expand_and_score_kernel"] == "expand_fused_row_kernel"
+    assert not idx.idx_sparse_plan(c8, 2 * cus, 1)["expansion_in_scoring_kernel"]
+    assert not idx.idx_sparse_plan(c8, cus, 2)["expansion_in_scoring_kernel"]
     assert idx.idx_sparse_plan(c, 200, 2)["expansion_in_scoring_kernel"]
     # fp8 queries: inside the split launches with 64-token sparse blocks only
     assert idx.idx_sparse_plan(c8, 64, 1)["expand_and_score_kernel"] == "score_split_expand_kernel"

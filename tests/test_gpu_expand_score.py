@@ -99,7 +99,7 @@ def _poison(g):
 
 def _check(case, tag, q_format, kernel=None, ws_all=False, cand_pad=0):
     """kernel: the kernel the one call's plan must name with MXFP4 queries on 256 CUs (fp8
-    queries: the same split kernels with 64-token sparse blocks, else no expansion inside).
+    queries: the same kernel where fp8 expands inside, else no expansion inside).
     ws_all: a workspace for every layer's logits.  cand_pad: candidate rows that many ids
     wider than NB (a strided view), the padding holding valid-looking ids."""
     import sparse_attention_indexer_candidate_amd as idx
@@ -116,11 +116,14 @@ def _check(case, tag, q_format, kernel=None, ws_all=False, cand_pad=0):
     home = all(with_logits) or ws_all
     plan = idx.idx_sparse_plan(g.cfg, case.num_rows, nl, logits_home=home)
     if kernel is not None and torch.cuda.get_device_properties(0).multi_processor_count == 256:
-        # fp8 queries expand inside the split launches with 64-token sparse blocks only,
-        # when their workgroups (8 groups of 64 columns each) fit three a CU
+        # fp8 queries expand inside with 64-token sparse blocks only: in the split launches
+        # when their workgroups (8 groups of 64 columns each) fit three a CU, in the
+        # one-row kernels with fewer than two row-layers a CU (8-wave rows)
         ngroups = -(-case.spec.nb * case.spec.cbs // 64)
         wgs = case.num_rows * nl * -(-ngroups // 8)
-        fp8_inside = kernel.startswith("score_split_expand") and g.sbk == 64 and wgs <= 3 * 256
+        fp8_inside = g.sbk == 64 and (
+            (kernel.startswith("score_split_expand") and wgs <= 3 * 256)
+            or (kernel.startswith("expand_fused") and case.num_rows * nl < 2 * 256))
         want = kernel if q_format == "mxfp4" or fp8_inside else plan["scoring_kernel"]
         assert plan["expand_and_score_kernel"] == want, plan
     wsl = nl if ws_all else 1
