@@ -335,11 +335,12 @@ int idx_sparse_mqa_logits_topk_layers(const idx_config *cfg, const idx_rows *row
  * stream starts.  That holds where the rows take the one-row-per-workgroup kernel
  * (num_rows >= the device's CUs, or num_rows * num_layers >= CUs with two or more layers;
  * not the prefill row-group case) in one round (num_rows * num_layers <= 2 x CUs; fp8
- * queries: fewer than 2 x CUs) with sparse_block_kv 64, and where they take the split scoring launch
- * (fewer rows, or row-layers, than CUs: one layer, or every layer in one launch pair;
- * fp8 queries with sparse_block_kv 64 only) when all its workgroups (rows x layers x one
- * per 512 columns) are resident at once (MXFP4: 6 x CUs, fp8: 3 x CUs).  idx_sparse_plan's expansion_in_scoring_kernel says which.  Otherwise the two
- * calls' launches.  Arguments and errors: those of the two calls (candidate_blocks
+ * queries: fewer than 2 x CUs) with sparse_block_kv 64, and where they take the split
+ * scoring launch (fewer rows, or row-layers, than CUs: one layer, or every layer in one
+ * launch pair; fp8 queries with sparse_block_kv 64 only) when all its workgroups (rows x
+ * layers x one per 512 columns) are resident at once (MXFP4: 6 x CUs, fp8: 3 x CUs).
+ * idx_sparse_plan's expansion_in_scoring_kernel says which.  Otherwise the two calls'
+ * launches.  Arguments and errors: those of the two calls (candidate_blocks
  * and cand_stride as in idx_expand_candidates; the workspace rule as in
  * idx_sparse_mqa_logits_topk_layers, also when the one launch needs none).  The timing
  * events time the scoring launch as in idx_sparse_mqa_logits_topk_layers. */
