@@ -44,6 +44,10 @@ CASES = {
     "layers_k8": (_spec("es8", 130, 64, 2, topk=2048), "expand_fused_layers_kernel", False),
     "layers_k16": (_spec("es9", 256, 128, 2, topk=2048, cand="distinct"),
                    "expand_fused_layers_kernel", False),
+    # fp8 queries in their 8-wave shapes too: 8192-column layers, short single-layer rows
+    "layers_k16_below_two_a_cu": (_spec("es32", 200, 128, 2, topk=2048, cand="distinct"),
+                                  "expand_fused_layers_kernel", False),
+    "row_short": (_spec("es33", 270, 24, 1), "expand_fused_row_kernel", False),
     # fewer rows (or row-layers) than CUs: the split scoring launch expands (64-, 32- and
     # 16-token sparse blocks), one layer or every layer in one launch pair
     "split_one_layer": (_spec("es16", 64, 64, 1, topk=1000), "score_split_expand_kernel", False),
