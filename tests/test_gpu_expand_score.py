@@ -101,7 +101,7 @@ def _poison(g):
     g.sched.work.fill_(0xAB)
 
 
-def _check(case, tag, q_format, kernel=None, ws_all=False, cand_pad=0):
+def _check(case, tag, q_format, kernel=None, ws_all=False, cand_pad=0, score_format="fp32"):
     """kernel: the kernel the one call's plan must name with MXFP4 queries on 256 CUs (fp8
     queries: the same kernel where fp8 expands inside, else no expansion inside).
     ws_all: a workspace for every layer's logits.  cand_pad: candidate rows that many ids
@@ -109,7 +109,7 @@ def _check(case, tag, q_format, kernel=None, ws_all=False, cand_pad=0):
     import sparse_attention_indexer_candidate_amd as idx
 
     nl = case.spec.layers
-    g = GpuRun(case, to_device(case, DEV), q_format=q_format)
+    g = GpuRun(case, to_device(case, DEV), q_format=q_format, score_format=score_format)
     if cand_pad:
         nb = case.spec.nb
         padded = torch.arange(case.num_rows * (nb + cand_pad), dtype=torch.int32,
@@ -212,3 +212,20 @@ def test_expand_and_score_wide_candidate_stride(rows, layers, kernel):
     the one call reads the first NB ids of each row, as the expansion launch does."""
     case = W.generate(_spec("es31", rows, 40, layers), seed=24)
     _check(case, f"es-stride-r{rows}-l{layers}", "mxfp4", kernel, cand_pad=5)
+
+
+@pytest.mark.parametrize("name", ["split_one_layer", "row_1024_k4", "layers_row_layers"])
+def test_expand_and_score_bf16_scoring(name):
+    """bf16 weights and bf16-rounded logits through the one call (split, one-row and
+    multi-layer forms): the same schedule, indices and logits as the two calls, and layer 0
+    against the oracle's bf16 scoring."""
+    spec, kernel, ws_all = CASES[name]
+    case = W.generate(spec, seed=33)
+    g, outs, logs = _check(case, f"es-bf16-{name}", "mxfp4", kernel, ws_all,
+                           score_format="bf16")
+    res = g.fetch()
+    res["indices"] = outs[0].cpu().numpy()
+    res["logits"] = logs[0].cpu().numpy()
+    ora = oracle.indexer_rows(case, 0, None, "mxfp4", threads=THREADS, score_format="bf16")
+    compare_rows(case, res, ora, case.spec.topk, g.sbk, f"es-bf16-{name} layer 0",
+                 score_format="bf16")
