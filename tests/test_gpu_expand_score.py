@@ -14,7 +14,7 @@ import oracle
 import workloads as W
 from parity import GpuRun, compare_rows, corrupt_tables, padded_tail
 from workloads.device import to_device
-from gpu_cases import DEV, THREADS, _say
+from gpu_cases import DEV, THREADS, _random_spec, _say
 
 pytestmark = pytest.mark.gpu
 
@@ -229,3 +229,26 @@ def test_expand_and_score_bf16_scoring(name):
     ora = oracle.indexer_rows(case, 0, None, "mxfp4", threads=THREADS, score_format="bf16")
     compare_rows(case, res, ora, case.spec.topk, g.sbk, f"es-bf16-{name} layer 0",
                  score_format="bf16")
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_expand_and_score_calls(i):
+    """Seeded random one calls against the two calls, bit for bit: 1-8 layers, row counts
+    that take each placement (split launches, one-row kernels in one round, more rounds,
+    row groups), random block and page sizes, k, ranges and candidate mess, both query
+    formats; the plan names no expectation here (the fixed cases pin it)."""
+    rng = np.random.default_rng(9000 + i)
+    spec, _ = _random_spec(400 + i)
+    layers = int(rng.integers(1, 9))
+    form = i % 4
+    rows = [int(rng.integers(4, 120)), int(rng.integers(256 // layers + 1, 2 * 256 // layers)),
+            int(rng.integers(256, 420)), spec.num_rows][form]
+    if form == 3 and spec.mode != "prefill":
+        spec = dataclasses.replace(spec, mode="prefill", ke_lo=1, context=spec.ke_hi)
+        rows = 2048 + int(rng.integers(0, 40))
+    spec = dataclasses.replace(spec, name=f"re{i}", num_rows=max(rows, 1), layers=layers,
+                               q_formats=("mxfp4", "fp8"))
+    q_format = ("mxfp4", "fp8")[(i + i // 4) % 2]
+    _say(f"[re{i}] rows={spec.num_rows} layers={layers} cbs={spec.cbs} page={spec.page_size} "
+         f"nb={spec.nb} k={spec.topk} {spec.mode} {q_format}")
+    _check(W.generate(spec, seed=90 + i), f"re{i}", q_format, ws_all=bool(i % 2))
